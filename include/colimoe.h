@@ -1,0 +1,201 @@
+/*
+ * colimoe.h - C ABI of the MI355X (gfx950) int4 routed-expert MoE layer.
+ *
+ * The layer (sources cited by page title and section):
+ *   [A] "Colibrì: running a 744B MoE model on a laptop with 2400 lines of pure C"
+ *       (kechuai.cn article)
+ *   [P] "colibrì" project profile (gh.puless.com)
+ *   [D] "colibrì: 1300 lines of C, a 25 GB laptop, a 744-billion-parameter model"
+ *       (SSP GitHub Daily #091, jsqmd.com)
+ *
+ *   - a router picks k of E experts per token, 8 of 256 at the pages' scale
+ *     ([A] §1 background; [D] §3);
+ *   - each routed expert is an int4 container with one scale per 64 weights
+ *     ([P] "aggressive optimisation, conservative correctness"), its three
+ *     matrices stored side by side ([A] §2 technical mechanism);
+ *   - at batch 1 the weights are dequantised and multiplied in floating point
+ *     ([D] §4, highlight 4);
+ *   - a shared expert runs for every token ([D] §3);
+ *   - batched positions read each unique expert once ([A] §2, batch-union);
+ *   - precision and routing never change silently ([A] §4): every call
+ *     validates its arguments and returns a status; there is no fallback.
+ *
+ * Computed per token t with activations x[t] (fp32, length d):
+ *   l[e]  = sum_c R[e][c] x[c] + b[e]                       (fp32 logits)
+ *   idx   = the k largest l[e], larger first, exact ties to the lower e
+ *   w_j   = exp(l[idx_j] - l[idx_0]) / sum_i exp(l[idx_i] - l[idx_0])
+ *   y_e   = Wd_e (SiLU(Wg_e x) * (Wu_e x)),  W[r][c] = q[r][c] * s[r][c/64]
+ *   r[t] += sum_j w_j y_{idx_j}  (ascending expert id)  + y_shared
+ *
+ * Conventions
+ *   - Status: 0 = COLIMOE_OK, negative = error (colimoe_status_str()).
+ *     Arguments are checked on the host before anything is enqueued; a
+ *     rejected call has no effect.  A fault inside a kernel surfaces as
+ *     COLIMOE_E_HIP at the next call that synchronises.
+ *   - Ownership: the caller owns every device buffer (layer weights,
+ *     workspace, inputs, outputs).  The library owns only its host context.
+ *   - route/forward/rmsnorm enqueue on the context's HIP stream, allocate
+ *     nothing and do not synchronise the host.
+ *   - A context is not thread-safe: use one per stream.
+ *   - Device pointers must be 16-byte aligned, layer buffers 256-byte aligned.
+ *   - A call with T == 0 does nothing and may pass NULL data pointers.
+ */
+#ifndef COLIMOE_H
+#define COLIMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum colimoe_status {
+  COLIMOE_OK = 0,
+  COLIMOE_E_ARG = -1,        /* null / misaligned pointer, bad flag or index */
+  COLIMOE_E_SHAPE = -2,      /* invalid shape, or T outside [0, max_tokens] */
+  COLIMOE_E_NOT_LOADED = -3, /* layer has no weights loaded */
+  COLIMOE_E_WORKSPACE = -4,  /* workspace missing or too small */
+  COLIMOE_E_HIP = -5,        /* a HIP runtime call failed */
+  COLIMOE_E_STATE = -6,      /* call out of order (e.g. load before create) */
+};
+
+/* Forward path selection. */
+enum colimoe_forward_flags {
+  COLIMOE_FWD_AUTO = 0,      /* fp32 dequant-GEMV for decode/verify calls,
+                                bf16 MFMA grouped GEMM for prefill-shaped calls
+                                (T*k >= 64*E, i.e. >= 64 tokens per expert) */
+  COLIMOE_FWD_FP32 = 1,      /* always the fp32 dequant-GEMV path */
+  COLIMOE_FWD_BF16_MFMA = 2, /* always the bf16 MFMA grouped-GEMM path */
+};
+
+typedef struct colimoe_config {
+  int32_t d;          /* hidden size, multiple of 64 */
+  int32_t f;          /* expert intermediate size, multiple of 64 */
+  int32_t n_experts;  /* E, 1..1024 */
+  int32_t top_k;      /* k, 1..min(E, 16) */
+  int32_t n_layers;   /* layers the context can hold, >= 1 */
+  int32_t n_shared;   /* always-on shared experts: 0 or 1 */
+  int32_t group_size; /* must be 64 */
+  int32_t max_tokens; /* largest T of any call, 1..65536 */
+  uint32_t flags;     /* reserved, must be 0 */
+} colimoe_config;
+
+/* One layer's weights in host memory, canonical format.
+ * A canonical expert blob (colimoe_expert_bytes() bytes) is
+ *   [gate q: f*d/2 B][gate s: f*(d/64) fp16][up q: f*d/2 B][up s: f*(d/64) fp16]
+ *   [down q: d*f/2 B][down s: d*(f/64) fp16]
+ * with gate/up row-major [f][d] and down row-major [d][f] (rows = outputs);
+ * byte i of a row holds element 2i in bits 0-3 and element 2i+1 in bits 4-7,
+ * each a two's-complement int4; scale g of a row covers elements 64g..64g+63. */
+typedef struct colimoe_layer_src {
+  const float *router;    /* [E][d] fp32, required */
+  const float *bias;      /* [E] fp32 additive logit bias, or NULL (= 0) */
+  const uint8_t *experts; /* E canonical blobs back to back, required */
+  const uint8_t *shared;  /* one canonical blob; required iff n_shared == 1 */
+} colimoe_layer_src;
+
+/* Batch-union lists (device int32 arrays), for a call with T tokens:
+ *   n_unique[1]                 number of distinct experts U
+ *   ids[min(E, T*k)]            the distinct experts, ascending
+ *   offsets[min(E, T*k) + 1]    pairs of ids[u] are offsets[u] .. offsets[u+1]-1
+ *   pair_token[T*k], pair_slot[T*k]  the (token, slot j) of each pair, ordered
+ *                               by (expert, token)
+ *   pair_of[T*k]                position of pair (t, j) at index t*k + j */
+typedef struct colimoe_union {
+  int32_t *n_unique;
+  int32_t *ids;
+  int32_t *offsets;
+  int32_t *pair_token;
+  int32_t *pair_slot;
+  int32_t *pair_of;
+} colimoe_union;
+
+typedef struct colimoe_ctx colimoe_ctx;
+
+/* Validate cfg and create a context bound to a HIP stream (NULL = default
+ * stream).  Selects the current HIP device.  Errors: E_ARG, E_SHAPE, E_HIP. */
+int colimoe_create(const colimoe_config *cfg, void *hip_stream, colimoe_ctx **out);
+
+/* Free the host context.  Device buffers stay the caller's. */
+void colimoe_destroy(colimoe_ctx *ctx);
+
+/* Change the stream later calls enqueue on. */
+int colimoe_set_stream(colimoe_ctx *ctx, void *hip_stream);
+
+/* Sizes, for the caller to allocate.  Return 0 for an invalid cfg.
+ *   expert_bytes    bytes of one expert blob (same canonical and on device)
+ *   layer_bytes     device bytes one loaded layer needs (router, bias, experts)
+ *   workspace_bytes device scratch route/forward need at max_tokens */
+size_t colimoe_expert_bytes(const colimoe_config *cfg);
+size_t colimoe_layer_bytes(const colimoe_config *cfg);
+size_t colimoe_workspace_bytes(const colimoe_config *cfg);
+
+/* Hand the context a caller-owned device workspace of >= workspace_bytes.
+ * Errors: E_ARG (null/misaligned), E_WORKSPACE (too small). */
+int colimoe_set_workspace(colimoe_ctx *ctx, void *dev, size_t bytes);
+
+/* Load one layer ([A] §2: an expert's three matrices are adjacent and read
+ * as one unit): copies router, bias and the E (+ shared) canonical blobs
+ * from host memory into the caller-owned device buffer dev_dst (>=
+ * layer_bytes, 256-byte aligned), repacked into the kernels' layout, and
+ * records them for `layer`.  Synchronous: host buffers may be reused on
+ * return.  Errors: E_ARG, E_SHAPE (layer out of range), E_HIP. */
+int colimoe_load_experts(colimoe_ctx *ctx, int32_t layer, const colimoe_layer_src *src, void *dev_dst,
+                         size_t dev_bytes);
+
+/* Route T tokens (device pointers).  x [T][d] fp32 -> idx [T][k] int32,
+ * w [T][k] fp32.  If u is non-NULL its arrays receive the batch-union lists.
+ * logits [T][E] fp32 may be NULL.  Errors: E_ARG, E_SHAPE, E_NOT_LOADED,
+ * E_WORKSPACE, E_HIP. */
+int colimoe_route(colimoe_ctx *ctx, int32_t layer, const float *x, int32_t T, int32_t *idx, float *w,
+                  const colimoe_union *u, float *logits);
+
+/* Batch-union scheduler on its own ([A] §2, batch-union): builds the union
+ * lists of a routing idx [T][k] (device) into u.  A routing with an expert
+ * id outside [0, E) or an expert twice in one token yields n_unique = 0 and
+ * makes the next colimoe_sync return E_ARG.  Errors: E_ARG, E_SHAPE,
+ * E_WORKSPACE, E_HIP. */
+int colimoe_union_build(colimoe_ctx *ctx, const int32_t *idx, int32_t T, const colimoe_union *u);
+
+/* residual[T][d] += MoE(x) under the given routing (idx, w are inputs, so a
+ * caller may force a routing).  u: union lists for this idx, as written by
+ * colimoe_route, or NULL to rebuild them in the workspace.  flags: one of
+ * colimoe_forward_flags.  The fp32 path gives each token bit-identical
+ * results whether it runs alone or batched with others.  Errors: E_ARG,
+ * E_SHAPE, E_NOT_LOADED, E_WORKSPACE, E_HIP. */
+int colimoe_forward(colimoe_ctx *ctx, int32_t layer, const float *x, int32_t T, const int32_t *idx,
+                    const float *w, const colimoe_union *u, float *residual, uint32_t flags);
+
+/* x_out[t] = r[t] / sqrt(mean(r[t]^2) + eps), unit weight, fp32 (device
+ * pointers, [T][d]); lets a stack of layers run without leaving the GPU. */
+int colimoe_rmsnorm(colimoe_ctx *ctx, const float *r, int32_t T, float eps, float *x_out);
+
+/* One expert on one token through the fp32 path, every stage exposed
+ * (device pointers, any of g/u/h may be NULL): x [d] -> g, u, h [f], y [d].
+ * e = -1 selects the shared expert.  Debug and parity only. */
+int colimoe_debug_expert(colimoe_ctx *ctx, int32_t layer, int32_t e, const float *x, float *g, float *u,
+                         float *h, float *y);
+
+/* Per-kernel timing for measurement.  While enabled, every kernel launch of
+ * the context is bracketed by a pair of HIP events on its stream (this adds
+ * two event records per launch).  Kernel names: "router", "topk", "union",
+ * "gateup", "down", "combine", "rmsnorm". */
+int colimoe_timing_enable(colimoe_ctx *ctx, int enable);
+
+/* Synchronises the stream, then reports the summed duration (ms) and the
+ * number of launches of kernel `name` recorded since the last reset; clears
+ * the records if reset != 0.  Errors: E_ARG (unknown name), E_HIP. */
+int colimoe_timing_read(colimoe_ctx *ctx, const char *name, double *total_ms, int64_t *count, int reset);
+
+/* Wait for the context's stream; reports a kernel fault as E_HIP. */
+int colimoe_sync(colimoe_ctx *ctx);
+
+/* Static text for a status code. */
+const char *colimoe_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* COLIMOE_H */

@@ -1,0 +1,567 @@
+// host.cpp - C ABI of the int4 routed-expert MoE layer (include/colimoe.h):
+// argument validation, workspace carve-up, the layer loader (canonical blobs
+// -> device layout) and kernel sequencing.  Sources are cited by page title
+// and section:
+//   [A] "Colibrì: running a 744B MoE model on a laptop with 2400 lines of pure C"
+//       (kechuai.cn article)
+//   [P] "colibrì" project profile (gh.puless.com)
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <algorithm>
+#include <thread>
+#include <vector>
+
+#include "../../include/colimoe.h"
+#include "internal.h"
+
+using namespace colimoe;
+
+struct colimoe_ctx {
+  colimoe_config cfg;
+  hipStream_t stream;
+  int device;
+  std::vector<LayerDev> layers;
+  std::vector<char> loaded;
+  uint8_t *ws;
+  size_t ws_bytes;
+  Workspace wl;
+  ExpertLayout el;
+  uint8_t *staging[2];  // pinned host buffers for the loader
+  size_t staging_bytes;
+  // kernel timing
+  bool timing;
+  std::vector<hipEvent_t> ev_pool;
+  size_t ev_used;
+  struct Rec {
+    int kid;
+    hipEvent_t a, b;
+  };
+  std::vector<Rec> recs;
+  double tot_ms[8];
+  long long cnt[8];
+};
+
+namespace {
+const char *const kKernelNames[] = {"router", "topk", "union", "gateup", "down", "combine", "rmsnorm"};
+enum { K_ROUTER, K_TOPK, K_UNION, K_GATEUP, K_DOWN, K_COMBINE, K_RMSNORM, K_COUNT };
+
+hipEvent_t take_event(colimoe_ctx *c) {
+  if (c->ev_used == c->ev_pool.size()) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    c->ev_pool.push_back(e);
+  }
+  return c->ev_pool[c->ev_used++];
+}
+
+// Brackets one kernel launch with events when timing is on.
+struct KTimer {
+  colimoe_ctx *c;
+  int kid;
+  hipEvent_t a = nullptr;
+  KTimer(colimoe_ctx *c_, int kid_) : c(c_), kid(kid_) {
+    if (c->timing && (a = take_event(c))) (void)hipEventRecord(a, c->stream);
+  }
+  ~KTimer() {
+    if (!a) return;
+    hipEvent_t b = take_event(c);
+    if (!b) return;
+    (void)hipEventRecord(b, c->stream);
+    c->recs.push_back({kid, a, b});
+  }
+};
+
+int drain_timing(colimoe_ctx *c) {
+  if (c->recs.empty()) return COLIMOE_OK;
+  if (hipStreamSynchronize(c->stream) != hipSuccess) return COLIMOE_E_HIP;
+  for (auto &r : c->recs) {
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) return COLIMOE_E_HIP;
+    c->tot_ms[r.kid] += ms;
+    c->cnt[r.kid] += 1;
+  }
+  c->recs.clear();
+  c->ev_used = 0;
+  return COLIMOE_OK;
+}
+}  // namespace
+
+namespace {
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+bool cfg_ok(const colimoe_config *c) {
+  if (!c) return false;
+  if (c->d <= 0 || c->f <= 0 || c->d % kGroup || c->f % kGroup) return false;
+  if (c->d > 16384 || c->f > 16384) return false;  // <= 8 chunks of 32 per lane
+  if (c->n_experts < 1 || c->n_experts > 1024) return false;
+  if (c->top_k < 1 || c->top_k > 16 || c->top_k > c->n_experts) return false;
+  if (c->n_layers < 1 || c->n_shared < 0 || c->n_shared > 1) return false;
+  if (c->group_size != kGroup) return false;
+  if (c->max_tokens < 1 || c->max_tokens > 65536) return false;
+  if ((long long)c->max_tokens * c->top_k > (1LL << 24)) return false;
+  if (c->flags != 0) return false;
+  return true;
+}
+
+size_t router_bytes(const colimoe_config *c) {
+  return align_up((size_t)c->n_experts * c->d * 4, kAlign) + align_up((size_t)c->n_experts * 4, kAlign);
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? COLIMOE_OK : COLIMOE_E_HIP; }
+
+LayerDev layer_of(colimoe_ctx *ctx, int layer) { return ctx->layers[layer]; }
+
+Dims dims_of(const colimoe_ctx *ctx, int T) {
+  Dims D;
+  D.d = ctx->cfg.d;
+  D.f = ctx->cfg.f;
+  D.E = ctx->cfg.n_experts;
+  D.k = ctx->cfg.top_k;
+  D.T = T;
+  D.n_shared = ctx->cfg.n_shared;
+  return D;
+}
+
+UnionDev ws_union(colimoe_ctx *ctx) {
+  UnionDev U;
+  U.n_unique = (int32_t *)(ctx->ws + ctx->wl.n_unique);
+  U.ids = (int32_t *)(ctx->ws + ctx->wl.ids);
+  U.offsets = (int32_t *)(ctx->ws + ctx->wl.offsets);
+  U.pair_token = (int32_t *)(ctx->ws + ctx->wl.pair_token);
+  U.pair_slot = (int32_t *)(ctx->ws + ctx->wl.pair_slot);
+  U.pair_of = (int32_t *)(ctx->ws + ctx->wl.pair_of);
+  return U;
+}
+
+bool union_ok(const colimoe_union *u) {
+  return u && u->n_unique && u->ids && u->offsets && u->pair_token && u->pair_slot && u->pair_of &&
+         aligned(u->n_unique, 4) && aligned(u->ids, 4) && aligned(u->offsets, 4) && aligned(u->pair_token, 4) &&
+         aligned(u->pair_slot, 4) && aligned(u->pair_of, 4);
+}
+
+UnionDev to_dev(const colimoe_union *u) {
+  UnionDev U;
+  U.n_unique = u->n_unique;
+  U.ids = u->ids;
+  U.offsets = u->offsets;
+  U.pair_token = u->pair_token;
+  U.pair_slot = u->pair_slot;
+  U.pair_of = u->pair_of;
+  return U;
+}
+
+// Common checks of route/forward/debug: context, layer, workspace, T.
+int check_call(colimoe_ctx *ctx, int32_t layer, int32_t T) {
+  if (!ctx) return COLIMOE_E_ARG;
+  if (layer < 0 || layer >= ctx->cfg.n_layers) return COLIMOE_E_SHAPE;
+  if (T < 0 || T > ctx->cfg.max_tokens) return COLIMOE_E_SHAPE;
+  if (!ctx->loaded[layer]) return COLIMOE_E_NOT_LOADED;
+  if (!ctx->ws) return COLIMOE_E_WORKSPACE;
+  return COLIMOE_OK;
+}
+
+// ---------------------------------------------------------------- repacking
+// Canonical blob -> device layout (internal.h): gate/up rows interleaved in
+// tiles of 4+4, scales regrouped per (tile, group) so one 16-byte load gives
+// a tile's 8 rows their scale, nibbles turned offset-binary (XOR 0x88).
+
+inline void copy_xor88(uint8_t *dst, const uint8_t *src, size_t n) {
+  size_t i = 0;
+  for (; i + 8 <= n; i += 8) {
+    uint64_t v;
+    memcpy(&v, src + i, 8);
+    v ^= 0x8888888888888888ULL;
+    memcpy(dst + i, &v, 8);
+  }
+  for (; i < n; ++i) dst[i] = src[i] ^ 0x88;
+}
+
+void repack_expert(const uint8_t *src, uint8_t *dst, int d, int f) {
+  const size_t w = (size_t)d * f, nb = w / 2, ns = w / kGroup;  // bytes of nibbles, number of scales
+  const uint8_t *gn = src;
+  const uint16_t *gs = (const uint16_t *)(gn + nb);
+  const uint8_t *un = gn + nb + 2 * ns;
+  const uint16_t *us = (const uint16_t *)(un + nb);
+  const uint8_t *dn = un + nb + 2 * ns;
+  const uint16_t *ds = (const uint16_t *)(dn + nb);
+  const ExpertLayout L = expert_layout(d, f);
+  const size_t rowd = (size_t)d / 2, rowf = (size_t)f / 2;
+  const int Gd = d / kGroup, Gf = f / kGroup;
+  uint16_t *gus = (uint16_t *)(dst + L.gu_sc);
+  for (int ti = 0; ti < f / 4; ++ti) {
+    for (int r = 0; r < 8; ++r) {
+      const int srow = 4 * ti + (r & 3);
+      const uint8_t *s = (r < 4 ? gn : un) + (size_t)srow * rowd;
+      copy_xor88(dst + L.gu_nib + ((size_t)ti * 8 + r) * rowd, s, rowd);
+      const uint16_t *sc = (r < 4 ? gs : us) + (size_t)srow * Gd;
+      for (int g = 0; g < Gd; ++g) gus[((size_t)ti * Gd + g) * 8 + r] = sc[g];
+    }
+  }
+  copy_xor88(dst + L.dn_nib, dn, (size_t)d * rowf);
+  uint16_t *dss = (uint16_t *)(dst + L.dn_sc);
+  for (int ti = 0; ti < d / 8; ++ti)
+    for (int r = 0; r < 8; ++r)
+      for (int g = 0; g < Gf; ++g) dss[((size_t)ti * Gf + g) * 8 + r] = ds[((size_t)ti * 8 + r) * Gf + g];
+}
+
+void repack_many(const uint8_t *const *srcs, uint8_t *dst, int n, size_t be, int d, int f) {
+  unsigned hw = std::thread::hardware_concurrency();
+  int nt = (int)std::min<unsigned>(hw ? hw : 4, 16);
+  nt = std::min(nt, n);
+  if (nt <= 1) {
+    for (int i = 0; i < n; ++i) repack_expert(srcs[i], dst + (size_t)i * be, d, f);
+    return;
+  }
+  std::vector<std::thread> th;
+  for (int t = 0; t < nt; ++t)
+    th.emplace_back([=]() {
+      for (int i = t; i < n; i += nt) repack_expert(srcs[i], dst + (size_t)i * be, d, f);
+    });
+  for (auto &x : th) x.join();
+}
+
+}  // namespace
+
+namespace colimoe {
+
+Workspace workspace_layout(int d, int f, int E, int k, int n_shared, int max_tokens) {
+  Workspace W;
+  size_t o = 0;
+  const size_t tk = (size_t)max_tokens * k;
+  const size_t ue = std::min<size_t>((size_t)E, tk);
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = align_up(o + bytes, kAlign);
+    return at;
+  };
+  W.err = take(4);
+  W.n_unique = take(4);
+  W.ids = take(ue * 4);
+  W.offsets = take((ue + 1) * 4);
+  W.pair_token = take(tk * 4);
+  W.pair_slot = take(tk * 4);
+  W.pair_of = take(tk * 4);
+  W.logits = take((size_t)max_tokens * E * 4);
+  const size_t rows = tk + (size_t)max_tokens * n_shared;
+  W.h = take(rows * f * 4);
+  W.y = take(rows * d * 4);
+  W.bytes = o;
+  return W;
+}
+
+}  // namespace colimoe
+
+extern "C" {
+
+const char *colimoe_status_str(int s) {
+  switch (s) {
+    case COLIMOE_OK: return "ok";
+    case COLIMOE_E_ARG: return "invalid argument (null or misaligned pointer, bad flag, index or routing)";
+    case COLIMOE_E_SHAPE: return "invalid shape (config, layer index or token count)";
+    case COLIMOE_E_NOT_LOADED: return "layer not loaded";
+    case COLIMOE_E_WORKSPACE: return "workspace missing or too small";
+    case COLIMOE_E_HIP: return "HIP runtime error";
+    case COLIMOE_E_STATE: return "call out of order";
+    default: return "unknown status";
+  }
+}
+
+size_t colimoe_expert_bytes(const colimoe_config *cfg) {
+  if (!cfg_ok(cfg)) return 0;
+  return expert_layout(cfg->d, cfg->f).bytes;
+}
+
+size_t colimoe_layer_bytes(const colimoe_config *cfg) {
+  if (!cfg_ok(cfg)) return 0;
+  return router_bytes(cfg) + (size_t)(cfg->n_experts + cfg->n_shared) * expert_layout(cfg->d, cfg->f).bytes;
+}
+
+size_t colimoe_workspace_bytes(const colimoe_config *cfg) {
+  if (!cfg_ok(cfg)) return 0;
+  return workspace_layout(cfg->d, cfg->f, cfg->n_experts, cfg->top_k, cfg->n_shared, cfg->max_tokens).bytes;
+}
+
+int colimoe_create(const colimoe_config *cfg, void *hip_stream, colimoe_ctx **out) {
+  if (!out) return COLIMOE_E_ARG;
+  *out = nullptr;
+  if (!cfg) return COLIMOE_E_ARG;
+  if (!cfg_ok(cfg)) return COLIMOE_E_SHAPE;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return COLIMOE_E_HIP;
+  colimoe_ctx *c = new colimoe_ctx();
+  c->cfg = *cfg;
+  c->stream = (hipStream_t)hip_stream;
+  c->device = dev;
+  c->layers.assign(cfg->n_layers, LayerDev{nullptr, nullptr, nullptr, 0});
+  c->loaded.assign(cfg->n_layers, 0);
+  c->ws = nullptr;
+  c->ws_bytes = 0;
+  c->wl = workspace_layout(cfg->d, cfg->f, cfg->n_experts, cfg->top_k, cfg->n_shared, cfg->max_tokens);
+  c->el = expert_layout(cfg->d, cfg->f);
+  c->staging[0] = c->staging[1] = nullptr;
+  c->staging_bytes = 0;
+  c->timing = false;
+  c->ev_used = 0;
+  for (int i = 0; i < 8; ++i) {
+    c->tot_ms[i] = 0.0;
+    c->cnt[i] = 0;
+  }
+  *out = c;
+  return COLIMOE_OK;
+}
+
+void colimoe_destroy(colimoe_ctx *ctx) {
+  if (!ctx) return;
+  for (int i = 0; i < 2; ++i)
+    if (ctx->staging[i]) (void)hipHostFree(ctx->staging[i]);
+  for (hipEvent_t e : ctx->ev_pool) (void)hipEventDestroy(e);
+  delete ctx;
+}
+
+int colimoe_set_stream(colimoe_ctx *ctx, void *hip_stream) {
+  if (!ctx) return COLIMOE_E_ARG;
+  ctx->stream = (hipStream_t)hip_stream;
+  return COLIMOE_OK;
+}
+
+int colimoe_set_workspace(colimoe_ctx *ctx, void *dev, size_t bytes) {
+  if (!ctx || !dev || !aligned(dev, kAlign)) return COLIMOE_E_ARG;
+  if (bytes < ctx->wl.bytes) return COLIMOE_E_WORKSPACE;
+  ctx->ws = (uint8_t *)dev;
+  ctx->ws_bytes = bytes;
+  return hip_status(hipMemsetAsync(ctx->ws + ctx->wl.err, 0, 4, ctx->stream));
+}
+
+int colimoe_load_experts(colimoe_ctx *ctx, int32_t layer, const colimoe_layer_src *src, void *dev_dst,
+                         size_t dev_bytes) {
+  if (!ctx || !src || !dev_dst || !src->router || !src->experts) return COLIMOE_E_ARG;
+  const colimoe_config *c = &ctx->cfg;
+  if (layer < 0 || layer >= c->n_layers) return COLIMOE_E_SHAPE;
+  if ((c->n_shared == 1) != (src->shared != nullptr)) return COLIMOE_E_ARG;
+  if (!aligned(dev_dst, kAlign)) return COLIMOE_E_ARG;
+  if (dev_bytes < colimoe_layer_bytes(c)) return COLIMOE_E_SHAPE;
+  const size_t be = ctx->el.bytes;
+  uint8_t *dst = (uint8_t *)dev_dst;
+  hipStream_t s = ctx->stream;
+  const size_t rb = (size_t)c->n_experts * c->d * 4;
+  float *router = (float *)dst;
+  float *bias = (float *)(dst + align_up(rb, kAlign));
+  uint8_t *experts = dst + router_bytes(c);
+  ctx->loaded[layer] = 0;
+  if (hipMemcpyAsync(router, src->router, rb, hipMemcpyHostToDevice, s) != hipSuccess) return COLIMOE_E_HIP;
+  if (src->bias) {
+    if (hipMemcpyAsync(bias, src->bias, (size_t)c->n_experts * 4, hipMemcpyHostToDevice, s) != hipSuccess)
+      return COLIMOE_E_HIP;
+  } else if (hipMemsetAsync(bias, 0, (size_t)c->n_experts * 4, s) != hipSuccess) {
+    return COLIMOE_E_HIP;
+  }
+  // Repack batches of experts into pinned staging buffers, double-buffered
+  // against the host-to-device copies.
+  const int total = c->n_experts + c->n_shared;
+  const int per = (int)std::max<size_t>(1, std::min<size_t>((size_t)total, ((size_t)256 << 20) / be));
+  if (ctx->staging_bytes < (size_t)per * be) {
+    for (int i = 0; i < 2; ++i) {
+      if (ctx->staging[i]) (void)hipHostFree(ctx->staging[i]);
+      ctx->staging[i] = nullptr;
+    }
+    ctx->staging_bytes = 0;
+    for (int i = 0; i < 2; ++i)
+      if (hipHostMalloc((void **)&ctx->staging[i], (size_t)per * be, hipHostMallocDefault) != hipSuccess)
+        return COLIMOE_E_HIP;
+    ctx->staging_bytes = (size_t)per * be;
+  }
+  hipEvent_t done[2];
+  if (hipEventCreateWithFlags(&done[0], hipEventDisableTiming) != hipSuccess) return COLIMOE_E_HIP;
+  if (hipEventCreateWithFlags(&done[1], hipEventDisableTiming) != hipSuccess) return COLIMOE_E_HIP;
+  bool used[2] = {false, false};
+  int rc = COLIMOE_OK;
+  std::vector<const uint8_t *> srcs(per);
+  for (int e0 = 0, b = 0; e0 < total && rc == COLIMOE_OK; e0 += per, b ^= 1) {
+    const int n = std::min(per, total - e0);
+    if (used[b] && hipEventSynchronize(done[b]) != hipSuccess) {
+      rc = COLIMOE_E_HIP;
+      break;
+    }
+    for (int i = 0; i < n; ++i) {
+      const int e = e0 + i;
+      srcs[i] = e < c->n_experts ? src->experts + (size_t)e * be : src->shared;
+    }
+    repack_many(srcs.data(), ctx->staging[b], n, be, c->d, c->f);
+    if (hipMemcpyAsync(experts + (size_t)e0 * be, ctx->staging[b], (size_t)n * be, hipMemcpyHostToDevice, s) !=
+            hipSuccess ||
+        hipEventRecord(done[b], s) != hipSuccess)
+      rc = COLIMOE_E_HIP;
+    used[b] = true;
+  }
+  if (hipStreamSynchronize(s) != hipSuccess) rc = COLIMOE_E_HIP;
+  (void)hipEventDestroy(done[0]);
+  (void)hipEventDestroy(done[1]);
+  if (rc != COLIMOE_OK) return rc;
+  ctx->layers[layer] = LayerDev{router, bias, experts, be};
+  ctx->loaded[layer] = 1;
+  return COLIMOE_OK;
+}
+
+int colimoe_route(colimoe_ctx *ctx, int32_t layer, const float *x, int32_t T, int32_t *idx, float *w,
+                  const colimoe_union *u, float *logits) {
+  int rc = check_call(ctx, layer, T);
+  if (rc) return rc;
+  if (T == 0) return COLIMOE_OK;  // nothing to read or write; pointers may be NULL
+  if (!x || !idx || !w || !aligned(x, 16) || !aligned(idx, 4) || !aligned(w, 4)) return COLIMOE_E_ARG;
+  if (logits && !aligned(logits, 4)) return COLIMOE_E_ARG;
+  if (u && !union_ok(u)) return COLIMOE_E_ARG;
+  const Dims D = dims_of(ctx, T);
+  const LayerDev L = layer_of(ctx, layer);
+  float *lg = logits ? logits : (float *)(ctx->ws + ctx->wl.logits);
+  hipStream_t s = ctx->stream;
+  {
+    KTimer kt(ctx, K_ROUTER);
+    if (launch_router(L, D, x, lg, s) != hipSuccess) return COLIMOE_E_HIP;
+  }
+  {
+    KTimer kt(ctx, K_TOPK);
+    if (launch_topk(lg, D, idx, w, s) != hipSuccess) return COLIMOE_E_HIP;
+  }
+  if (u) {
+    KTimer kt(ctx, K_UNION);
+    if (launch_union(idx, D, to_dev(u), (int32_t *)(ctx->ws + ctx->wl.err), s) != hipSuccess)
+      return COLIMOE_E_HIP;
+  }
+  return COLIMOE_OK;
+}
+
+int colimoe_union_build(colimoe_ctx *ctx, const int32_t *idx, int32_t T, const colimoe_union *u) {
+  if (!ctx) return COLIMOE_E_ARG;
+  if (T < 0 || T > ctx->cfg.max_tokens) return COLIMOE_E_SHAPE;
+  if (!ctx->ws) return COLIMOE_E_WORKSPACE;
+  if (T == 0) return COLIMOE_OK;
+  if (!idx || !aligned(idx, 4) || !union_ok(u)) return COLIMOE_E_ARG;
+  const Dims D = dims_of(ctx, T);
+  return hip_status(launch_union(idx, D, to_dev(u), (int32_t *)(ctx->ws + ctx->wl.err), ctx->stream));
+}
+
+int colimoe_forward(colimoe_ctx *ctx, int32_t layer, const float *x, int32_t T, const int32_t *idx, const float *w,
+                    const colimoe_union *u, float *residual, uint32_t flags) {
+  int rc = check_call(ctx, layer, T);
+  if (rc) return rc;
+  if (flags != COLIMOE_FWD_AUTO && flags != COLIMOE_FWD_FP32 && flags != COLIMOE_FWD_BF16_MFMA)
+    return COLIMOE_E_ARG;
+  if (flags == COLIMOE_FWD_BF16_MFMA) return COLIMOE_E_ARG;  // prefill path not built yet
+  if (T == 0) return COLIMOE_OK;  // nothing to read or write; pointers may be NULL
+  if (!x || !idx || !w || !residual || !aligned(x, 16) || !aligned(idx, 4) || !aligned(w, 4) ||
+      !aligned(residual, 4))
+    return COLIMOE_E_ARG;
+  if (u && !union_ok(u)) return COLIMOE_E_ARG;
+  const Dims D = dims_of(ctx, T);
+  const LayerDev L = layer_of(ctx, layer);
+  hipStream_t s = ctx->stream;
+  UnionDev U;
+  if (u) {
+    U = to_dev(u);
+  } else {
+    U = ws_union(ctx);
+    KTimer kt(ctx, K_UNION);
+    if (launch_union(idx, D, U, (int32_t *)(ctx->ws + ctx->wl.err), s) != hipSuccess) return COLIMOE_E_HIP;
+  }
+  float *h = (float *)(ctx->ws + ctx->wl.h);
+  float *y = (float *)(ctx->ws + ctx->wl.y);
+  {
+    KTimer kt(ctx, K_GATEUP);
+    if (launch_gateup(L, D, x, U, h, s) != hipSuccess) return COLIMOE_E_HIP;
+  }
+  {
+    KTimer kt(ctx, K_DOWN);
+    if (launch_down(L, D, h, U, y, s) != hipSuccess) return COLIMOE_E_HIP;
+  }
+  {
+    KTimer kt(ctx, K_COMBINE);
+    if (launch_combine(D, idx, w, U, y, residual, s) != hipSuccess) return COLIMOE_E_HIP;
+  }
+  return COLIMOE_OK;
+}
+
+int colimoe_rmsnorm(colimoe_ctx *ctx, const float *r, int32_t T, float eps, float *x_out) {
+  if (!ctx) return COLIMOE_E_ARG;
+  if (T < 0 || T > ctx->cfg.max_tokens) return COLIMOE_E_SHAPE;
+  if (!(eps >= 0.0f)) return COLIMOE_E_ARG;
+  if (T == 0) return COLIMOE_OK;
+  if (!r || !x_out || !aligned(r, 4) || !aligned(x_out, 4)) return COLIMOE_E_ARG;
+  KTimer kt(ctx, K_RMSNORM);
+  return hip_status(launch_rmsnorm(r, T, ctx->cfg.d, eps, x_out, ctx->stream));
+}
+
+int colimoe_debug_expert(colimoe_ctx *ctx, int32_t layer, int32_t e, const float *x, float *g, float *u, float *h,
+                         float *y) {
+  int rc = check_call(ctx, layer, 1);
+  if (rc) return rc;
+  if (!x || !y || !aligned(x, 16) || !aligned(y, 4)) return COLIMOE_E_ARG;
+  if ((g == nullptr) != (u == nullptr)) return COLIMOE_E_ARG;
+  if (e < -1 || e >= ctx->cfg.n_experts) return COLIMOE_E_ARG;
+  if (e == -1 && ctx->cfg.n_shared == 0) return COLIMOE_E_ARG;
+  const int slot = e < 0 ? ctx->cfg.n_experts : e;
+  // a one-slot union in the workspace: expert `slot`, one pair (token 0)
+  Dims D = dims_of(ctx, 1);
+  D.k = 1;
+  D.n_shared = 0;
+  D.E = ctx->cfg.n_experts + 1;  // admits the shared expert's storage index
+  UnionDev U = ws_union(ctx);
+  const int32_t host[7] = {1, slot, 0, 1, 0, 0, 0};
+  hipStream_t s = ctx->stream;
+  if (hipMemcpyAsync(U.n_unique, &host[0], 4, hipMemcpyHostToDevice, s) != hipSuccess ||
+      hipMemcpyAsync(U.ids, &host[1], 4, hipMemcpyHostToDevice, s) != hipSuccess ||
+      hipMemcpyAsync(U.offsets, &host[2], 8, hipMemcpyHostToDevice, s) != hipSuccess ||
+      hipMemcpyAsync(U.pair_token, &host[4], 4, hipMemcpyHostToDevice, s) != hipSuccess ||
+      hipMemcpyAsync(U.pair_slot, &host[5], 4, hipMemcpyHostToDevice, s) != hipSuccess ||
+      hipMemcpyAsync(U.pair_of, &host[6], 4, hipMemcpyHostToDevice, s) != hipSuccess)
+    return COLIMOE_E_HIP;
+  float *hh = h ? h : (float *)(ctx->ws + ctx->wl.h);
+  const LayerDev L = layer_of(ctx, layer);
+  if (launch_debug_gateup(L, D, x, U, hh, g, u, s) != hipSuccess) return COLIMOE_E_HIP;
+  if (launch_down(L, D, hh, U, y, s) != hipSuccess) return COLIMOE_E_HIP;
+  return hip_status(hipStreamSynchronize(s));  // keeps `host` alive for the copies
+}
+
+int colimoe_timing_enable(colimoe_ctx *ctx, int enable) {
+  if (!ctx) return COLIMOE_E_ARG;
+  ctx->timing = enable != 0;
+  return COLIMOE_OK;
+}
+
+int colimoe_timing_read(colimoe_ctx *ctx, const char *name, double *total_ms, int64_t *count, int reset) {
+  if (!ctx || !name || !total_ms || !count) return COLIMOE_E_ARG;
+  int kid = -1;
+  for (int i = 0; i < K_COUNT; ++i)
+    if (strcmp(name, kKernelNames[i]) == 0) kid = i;
+  if (kid < 0) return COLIMOE_E_ARG;
+  int rc = drain_timing(ctx);
+  if (rc) return rc;
+  *total_ms = ctx->tot_ms[kid];
+  *count = ctx->cnt[kid];
+  if (reset)
+    for (int i = 0; i < 8; ++i) {
+      ctx->tot_ms[i] = 0.0;
+      ctx->cnt[i] = 0;
+    }
+  return COLIMOE_OK;
+}
+
+int colimoe_sync(colimoe_ctx *ctx) {
+  if (!ctx) return COLIMOE_E_ARG;
+  if (hipStreamSynchronize(ctx->stream) != hipSuccess) return COLIMOE_E_HIP;
+  if (!ctx->ws) return COLIMOE_OK;
+  int32_t err = 0;
+  if (hipMemcpy(&err, ctx->ws + ctx->wl.err, 4, hipMemcpyDeviceToHost) != hipSuccess) return COLIMOE_E_HIP;
+  if (err) {
+    if (hipMemset(ctx->ws + ctx->wl.err, 0, 4) != hipSuccess) return COLIMOE_E_HIP;
+    return COLIMOE_E_ARG;
+  }
+  return COLIMOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,192 @@
+"""GPU parity of the HIP path against the CPU oracle (fp32 path).
+
+Bound per output: |gpu - oracle| <= 1e-3 * (1 + |oracle|).  Routing ids equal
+the oracle's except on near-ties (gap < 1e-5 between the k-th and (k+1)-th
+fp64 logits); union lists are compared exactly; batched results must be
+bit-identical to one-at-a-time results.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests import _parity as P
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TINY = synth.WORKLOADS["tiny"]
+DECODE = synth.WORKLOADS["decode"]
+UNION16 = synth.WORKLOADS["union16"]
+# odd shapes: partial lane groups (d/32 = 10, f/32 = 6), E not a multiple of 64
+RAGGED = synth.Workload(name="ragged", d=320, f=192, E=37, k=3, T=5, n_shared=1, zipf=1.1, rho=0.3,
+                        seed=synth.BASE_SEED + 101)
+# d/32 = 66: two chunks per lane, the second one partial
+RAGGED2 = synth.Workload(name="ragged2", d=2112, f=128, E=20, k=4, T=3, n_shared=0, seed=synth.BASE_SEED + 102)
+
+
+def _ctx(w, n_layers=1, max_tokens=None):
+    from int4_routed_expert_fp32_amd.runtime import MoeContext
+    print("context", w.name, w.d, w.f, w.E, w.k, w.T, flush=True)
+    return MoeContext(w.d, w.f, w.E, w.k, n_layers=n_layers, n_shared=w.n_shared,
+                      max_tokens=max_tokens or max(w.T, 1))
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _builds():
+    oracle.build(force=False)
+    synth.build(force=False)
+
+
+def test_native_library_is_the_path():
+    import int4_routed_expert_fp32_amd as cm
+    L = cm.lib()
+    assert L._name.endswith("libcolimoe.so")
+    assert torch.cuda.is_available()
+
+
+@pytest.mark.parametrize("w", [TINY, RAGGED, RAGGED2, DECODE], ids=lambda w: w.name)
+def test_debug_expert_onehot_is_exact(w):
+    """x = e_c makes g and u single dequantised weights q*s, exact in fp32."""
+    ctx = _ctx(w)
+    P.load_layer(ctx, w, 0)
+    blob = synth.expert_blobs(w, 0, 3, 4)[0]
+    Wg = oracle.dequant(*oracle.blob_sections(blob, w.d, w.f)[0], w.f, w.d)
+    Wu = oracle.dequant(*oracle.blob_sections(blob, w.d, w.f)[1], w.f, w.d)
+    for c in (0, 1, 33, w.d - 1):
+        x = torch.zeros(w.d, dtype=torch.float32, device="cuda")
+        x[c] = 1.0
+        g, u, h, y = ctx.debug_expert(0, 3, x)
+        assert np.array_equal(g.cpu().numpy().astype(np.float64), Wg[:, c])
+        assert np.array_equal(u.cpu().numpy().astype(np.float64), Wu[:, c])
+
+
+@pytest.mark.parametrize("w", [TINY, RAGGED, RAGGED2, DECODE], ids=lambda w: w.name)
+def test_debug_expert_stages(w):
+    ctx = _ctx(w)
+    P.load_layer(ctx, w, 0)
+    x = synth.activations(w, stream=7, T=1)[0]
+    xt = torch.from_numpy(x).cuda()
+    for e in ([0, w.E - 1] + ([-1] if w.n_shared else [])):
+        blob = synth.expert_blobs(w, 0, e if e >= 0 else w.E, (e if e >= 0 else w.E) + 1)[0]
+        o = oracle.expert(blob, w.d, w.f, x.astype(np.float64))
+        g, u, h, y = (t.cpu().numpy() for t in ctx.debug_expert(0, e, xt))
+        P.assert_close(g, o["g"], what="g")
+        P.assert_close(u, o["u"], what="u")
+        P.assert_close(h, o["h"], what="h")
+        P.assert_close(y, o["y"], what="y")
+
+
+def _rand_routing(rng, T, E, k):
+    return np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+
+
+@pytest.mark.parametrize("T,E,k", [(1, 256, 8), (16, 256, 8), (7, 37, 3), (2048, 256, 8), (100, 16, 16),
+                                   (64, 1000, 1), (65, 64, 2)])
+def test_union_lists_exact(T, E, k):
+    w = synth.Workload(name="u", d=256, f=128, E=E, k=k, T=T, n_shared=0)
+    ctx = _ctx(w)
+    rng = np.random.default_rng(T * 1000 + E + k)
+    for trial in range(3):
+        idx = _rand_routing(rng, T, E, k)
+        if trial == 1:
+            idx[:] = idx[0]  # identical tokens: U = k
+        U = ctx.new_union(T)
+        ctx.union_build(torch.from_numpy(idx).cuda(), U)
+        ctx.sync()
+        g = U.to_host()
+        o = oracle.union(idx, E)
+        assert g["n_unique"] == o["n_unique"]
+        for key in ("ids", "offsets", "pair_token", "pair_slot", "pair_of"):
+            assert np.array_equal(g[key], o[key]), key
+
+
+def test_invalid_routing_is_reported():
+    w = TINY
+    ctx = _ctx(w, max_tokens=2)
+    U = ctx.new_union(2)
+    for bad in (np.array([[0, 16], [1, 2]], np.int32), np.array([[3, 3], [1, 2]], np.int32),
+                np.array([[-1, 2], [1, 2]], np.int32)):
+        ctx.union_build(torch.from_numpy(bad).cuda(), U)
+        assert ctx.sync(check=False) == -1
+        assert int(U.n_unique.item()) == 0
+    assert ctx.sync(check=False) == 0
+
+
+@pytest.mark.parametrize("w", [TINY, RAGGED, RAGGED2], ids=lambda w: w.name)
+def test_layer_parity_small(w):
+    ctx = _ctx(w)
+    P.load_layer(ctx, w, 0)
+    ora = P.OracleLayer(w, 0)
+    X = synth.activations(w, stream=0)
+    r = P.layer_parity(ctx, w, 0, X, ora)
+    print(w.name, "worst ratio", r["ratio"], "near-tie tokens", r["differ"])
+    # union lists from route equal the oracle's union of the GPU routing
+    o = oracle.union(r["idx"], w.E)
+    for key in ("ids", "offsets"):
+        assert np.array_equal(r["union"][key], o[key])
+
+
+def test_layer_parity_decode():
+    w = DECODE
+    ctx = _ctx(w)
+    P.load_layer(ctx, w, 0)
+    ora = P.OracleLayer(w, 0)
+    for stream in (0, 1, 2):
+        X = synth.activations(w, stream=stream)
+        r = P.layer_parity(ctx, w, 0, X, ora)
+        print("decode stream", stream, "worst ratio", r["ratio"], "near-ties", r["differ"])
+
+
+def test_zero_tokens_is_a_noop():
+    w = TINY
+    ctx = _ctx(w)
+    P.load_layer(ctx, w, 0)
+    x = torch.zeros((0, w.d), dtype=torch.float32, device="cuda")
+    idx, wts, _ = ctx.route(0, x)
+    res = torch.zeros((0, w.d), dtype=torch.float32, device="cuda")
+    ctx.forward(0, x, idx, wts, None, res)
+    ctx.sync()
+
+
+def test_union16_parity_and_batch_identity():
+    """16 correlated positions: batched == one at a time, bit for bit; each
+    unique expert appears once in the union; outputs match the oracle."""
+    w = UNION16
+    ctx = _ctx(w)
+    P.load_layer(ctx, w, 0)
+    ora = P.OracleLayer(w, 0)
+    X = synth.activations(w, stream=0)
+    r = P.layer_parity(ctx, w, 0, X, ora)
+    nu = r["union"]["n_unique"]
+    print("union16: unique experts", nu, "of", w.T * w.k, "pairs; worst ratio", r["ratio"])
+    assert nu < w.T * w.k
+    xt = torch.from_numpy(X).cuda()
+    for t in range(w.T):
+        x1 = xt[t:t + 1].contiguous()
+        U1 = ctx.new_union(1)
+        idx1, w1, _ = ctx.route(0, x1, U1)
+        res1 = x1.clone()
+        ctx.forward(0, x1, idx1, w1, U1, res1)
+        ctx.sync()
+        assert np.array_equal(idx1.cpu().numpy()[0], r["idx"][t])
+        assert np.array_equal(w1.cpu().numpy()[0].view(np.uint32), r["w"][t].view(np.uint32))
+        assert np.array_equal(res1.cpu().numpy()[0].view(np.uint32), r["out"][t].view(np.uint32)), t
+
+
+def test_forced_routing_onehot_gate():
+    """Caller-forced routing with gate weights (1, 0, ...) and a zero residual
+    yields exactly one expert's output (plus the shared expert)."""
+    w = RAGGED
+    ctx = _ctx(w, max_tokens=1)
+    P.load_layer(ctx, w, 0)
+    x = synth.activations(w, stream=3, T=1)
+    xt = torch.from_numpy(x).cuda()
+    idx = torch.tensor([[5, 0, 9]], dtype=torch.int32, device="cuda")
+    wts = torch.tensor([[1.0, 0.0, 0.0]], dtype=torch.float32, device="cuda")
+    res = torch.zeros_like(xt)
+    ctx.forward(0, xt, idx, wts, None, res)
+    ctx.sync()
+    ora = P.OracleLayer(w, 0)
+    out, _ = ora.forward(x, np.array([[5, 0, 9]]), np.array([[1.0, 0.0, 0.0]]), residual=np.zeros_like(x))
+    P.assert_close(res.cpu().numpy(), out, what="one-hot gate")
