@@ -34,6 +34,9 @@ def parse():
     ap.add_argument("--ring", type=int, default=8, help="independent layer instances cycled over")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--path", choices=("auto", "fp32", "fxp"), default="auto",
+                    help="arithmetic path of the headline (auto: fixed-point activations at these shapes)")
+    ap.add_argument("--no-compare", action="store_true", help="skip timing the other arithmetic path")
     return ap.parse_args()
 
 
@@ -73,43 +76,57 @@ def main():
     unions = [ctx.new_union(1) for _ in range(args.ring)]
     stream = torch.cuda.current_stream(dev)
 
-    def step(i):
+    flag_of = {"auto": cm.COLIMOE_FWD_AUTO, "fp32": cm.COLIMOE_FWD_FP32, "fxp": cm.COLIMOE_FWD_FXP}
+
+    def step(i, flags):
         layer = i % args.ring
         x = X[i:i + 1]
         U = unions[layer]
-        cm.colimoe_route(ctx.ctx, layer, x.data_ptr(), 1, idx[i].data_ptr(), wts[i].data_ptr(), U.abi(), None)
-        cm.colimoe_forward(ctx.ctx, layer, x.data_ptr(), 1, idx[i].data_ptr(), wts[i].data_ptr(), U.abi(),
-                           res[i].data_ptr(), cm.COLIMOE_FWD_AUTO)
+        cm.colimoe_route_forward(ctx.ctx, layer, x.data_ptr(), 1, idx[i].data_ptr(), wts[i].data_ptr(), U.abi(),
+                                 res[i].data_ptr(), flags)
 
+    def timed(flags):
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for i in range(args.warmup, n):
+            step(i, flags)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        ctx.sync()
+        return ev0.elapsed_time(ev1) / args.steps
+
+    def per_kernel(flags):
+        names = ("route", "topk", "union", "encode", "gateup", "down", "combine")
+        cm.colimoe_timing_enable(ctx.ctx, True)
+        cm.colimoe_timing_read(ctx.ctx, "route", reset=True)
+        for i in range(args.warmup, n):
+            step(i, flags)
+        kern = {}
+        for k in names:
+            tot, cnt = cm.colimoe_timing_read(ctx.ctx, k)
+            if cnt:
+                kern[k] = dict(avg_us=1000.0 * tot / cnt, launches=cnt)
+        cm.colimoe_timing_enable(ctx.ctx, False)
+        ctx.sync()
+        return kern
+
+    head = flag_of[args.path]
     for i in range(args.warmup):
-        step(i)
+        step(i, head)
     ctx.sync()
     torch.cuda.synchronize()
-
-    # headline pass: plain launches
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    ev0.record(stream)
-    for i in range(args.warmup, n):
-        step(i)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    ms_total = ev0.elapsed_time(ev1)
-    ctx.sync()
-    ms_step = ms_total / args.steps
-
-    # per-kernel pass: the same steps with HIP events around each kernel
-    cm.colimoe_timing_enable(ctx.ctx, True)
-    for k in ("router", "topk", "union", "gateup", "down", "combine"):
-        cm.colimoe_timing_read(ctx.ctx, k, reset=True)
-    for i in range(args.warmup, n):
-        step(i)
-    kern = {}
-    for k in ("router", "topk", "union", "gateup", "down", "combine"):
-        tot, cnt = cm.colimoe_timing_read(ctx.ctx, k)
-        kern[k] = dict(avg_us=1000.0 * tot / max(cnt, 1), launches=cnt)
-    cm.colimoe_timing_enable(ctx.ctx, False)
-    ctx.sync()
+    ms_step = timed(head)          # headline pass: plain launches
+    kern = per_kernel(head)        # the same steps with HIP events around each kernel
+    other = None
+    if not args.no_compare:
+        oflags = cm.COLIMOE_FWD_FP32 if args.path != "fp32" else cm.COLIMOE_FWD_FXP
+        for i in range(args.warmup):
+            step(i, oflags)
+        oms = timed(oflags)
+        okern = per_kernel(oflags)
+        other = {"path": "fp32" if oflags == cm.COLIMOE_FWD_FP32 else "fxp", "us_per_token": round(1000 * oms, 3),
+                 "kernels": {k: round(v["avg_us"], 3) for k, v in okern.items()}}
 
     be = w.expert_bytes
     gu_bytes = 2 * (w.d * w.f // 2 + 2 * w.d * w.f // 64)     # gate+up int4 + fp16 scales of one expert
@@ -139,7 +156,8 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int4 weights, fp32 compute",
+        "dtype": "int4 weights; fp32 accumulation" + (" (fixed-point activations, exact int4 dot)"
+                                                        if args.path != "fp32" else " (fp32 dequant)"),
         "data": "synthetic (seeded int4 gs64 experts, fp16 scales, N(0,1) activations)",
         "config": {"workload": "decode MoE layer d=6144 f=2048 E=256 top-8 + 1 shared, 1 token",
                    "layer_ring": args.ring},
@@ -149,6 +167,8 @@ def main():
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "kernels": {k: {"avg_us": round(v["avg_us"], 3), "launches": v["launches"]} for k, v in kern.items()},
         "down_gbs": round(dn_gbs, 1),
+        "path": args.path,
+        "compare": other,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

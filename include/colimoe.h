@@ -50,6 +50,8 @@
 extern "C" {
 #endif
 
+#define COLIMOE_API __attribute__((visibility("default")))
+
 enum colimoe_status {
   COLIMOE_OK = 0,
   COLIMOE_E_ARG = -1,        /* null / misaligned pointer, bad flag or index */
@@ -62,11 +64,19 @@ enum colimoe_status {
 
 /* Forward path selection. */
 enum colimoe_forward_flags {
-  COLIMOE_FWD_AUTO = 0,      /* fp32 dequant-GEMV for decode/verify calls,
-                                bf16 MFMA grouped GEMM for prefill-shaped calls
-                                (T*k >= 64*E, i.e. >= 64 tokens per expert) */
-  COLIMOE_FWD_FP32 = 1,      /* always the fp32 dequant-GEMV path */
-  COLIMOE_FWD_BF16_MFMA = 2, /* always the bf16 MFMA grouped-GEMM path */
+  COLIMOE_FWD_AUTO = 0,      /* the fixed-point activation path when d >= 2048 and
+                                f >= 2048, else the fp32 dequant path */
+  COLIMOE_FWD_FP32 = 1,      /* int4 weights dequantised to fp32, fp32 FMA, fp32
+                                accumulation ([D] §4, highlight 4) */
+  COLIMOE_FWD_BF16_MFMA = 2, /* bf16 MFMA grouped GEMM (not built: E_ARG) */
+  COLIMOE_FWD_FXP = 3,       /* fixed-point activations: every 16 activations are
+                                encoded as 23-bit integers with one power-of-two
+                                scale (error <= 2^-22 of the group's largest
+                                magnitude) and multiplied with the int4 weights
+                                exactly by integer dot products; per 16 columns
+                                the exact sum is rounded once to fp32, scaled by
+                                the fp16 weight scale and accumulated in fp32.
+                                Needs d >= 2048 and f >= 2048 (else E_SHAPE) */
 };
 
 typedef struct colimoe_config {
@@ -115,25 +125,25 @@ typedef struct colimoe_ctx colimoe_ctx;
 
 /* Validate cfg and create a context bound to a HIP stream (NULL = default
  * stream).  Selects the current HIP device.  Errors: E_ARG, E_SHAPE, E_HIP. */
-int colimoe_create(const colimoe_config *cfg, void *hip_stream, colimoe_ctx **out);
+COLIMOE_API int colimoe_create(const colimoe_config *cfg, void *hip_stream, colimoe_ctx **out);
 
 /* Free the host context.  Device buffers stay the caller's. */
-void colimoe_destroy(colimoe_ctx *ctx);
+COLIMOE_API void colimoe_destroy(colimoe_ctx *ctx);
 
 /* Change the stream later calls enqueue on. */
-int colimoe_set_stream(colimoe_ctx *ctx, void *hip_stream);
+COLIMOE_API int colimoe_set_stream(colimoe_ctx *ctx, void *hip_stream);
 
 /* Sizes, for the caller to allocate.  Return 0 for an invalid cfg.
  *   expert_bytes    bytes of one expert blob (same canonical and on device)
  *   layer_bytes     device bytes one loaded layer needs (router, bias, experts)
  *   workspace_bytes device scratch route/forward need at max_tokens */
-size_t colimoe_expert_bytes(const colimoe_config *cfg);
-size_t colimoe_layer_bytes(const colimoe_config *cfg);
-size_t colimoe_workspace_bytes(const colimoe_config *cfg);
+COLIMOE_API size_t colimoe_expert_bytes(const colimoe_config *cfg);
+COLIMOE_API size_t colimoe_layer_bytes(const colimoe_config *cfg);
+COLIMOE_API size_t colimoe_workspace_bytes(const colimoe_config *cfg);
 
 /* Hand the context a caller-owned device workspace of >= workspace_bytes.
  * Errors: E_ARG (null/misaligned), E_WORKSPACE (too small). */
-int colimoe_set_workspace(colimoe_ctx *ctx, void *dev, size_t bytes);
+COLIMOE_API int colimoe_set_workspace(colimoe_ctx *ctx, void *dev, size_t bytes);
 
 /* Load one layer ([A] §2: an expert's three matrices are adjacent and read
  * as one unit): copies router, bias and the E (+ shared) canonical blobs
@@ -141,14 +151,14 @@ int colimoe_set_workspace(colimoe_ctx *ctx, void *dev, size_t bytes);
  * layer_bytes, 256-byte aligned), repacked into the kernels' layout, and
  * records them for `layer`.  Synchronous: host buffers may be reused on
  * return.  Errors: E_ARG, E_SHAPE (layer out of range), E_HIP. */
-int colimoe_load_experts(colimoe_ctx *ctx, int32_t layer, const colimoe_layer_src *src, void *dev_dst,
+COLIMOE_API int colimoe_load_experts(colimoe_ctx *ctx, int32_t layer, const colimoe_layer_src *src, void *dev_dst,
                          size_t dev_bytes);
 
 /* Route T tokens (device pointers).  x [T][d] fp32 -> idx [T][k] int32,
  * w [T][k] fp32.  If u is non-NULL its arrays receive the batch-union lists.
  * logits [T][E] fp32 may be NULL.  Errors: E_ARG, E_SHAPE, E_NOT_LOADED,
  * E_WORKSPACE, E_HIP. */
-int colimoe_route(colimoe_ctx *ctx, int32_t layer, const float *x, int32_t T, int32_t *idx, float *w,
+COLIMOE_API int colimoe_route(colimoe_ctx *ctx, int32_t layer, const float *x, int32_t T, int32_t *idx, float *w,
                   const colimoe_union *u, float *logits);
 
 /* Batch-union scheduler on its own ([A] §2, batch-union): builds the union
@@ -156,7 +166,7 @@ int colimoe_route(colimoe_ctx *ctx, int32_t layer, const float *x, int32_t T, in
  * id outside [0, E) or an expert twice in one token yields n_unique = 0 and
  * makes the next colimoe_sync return E_ARG.  Errors: E_ARG, E_SHAPE,
  * E_WORKSPACE, E_HIP. */
-int colimoe_union_build(colimoe_ctx *ctx, const int32_t *idx, int32_t T, const colimoe_union *u);
+COLIMOE_API int colimoe_union_build(colimoe_ctx *ctx, const int32_t *idx, int32_t T, const colimoe_union *u);
 
 /* residual[T][d] += MoE(x) under the given routing (idx, w are inputs, so a
  * caller may force a routing).  u: union lists for this idx, as written by
@@ -164,35 +174,44 @@ int colimoe_union_build(colimoe_ctx *ctx, const int32_t *idx, int32_t T, const c
  * colimoe_forward_flags.  The fp32 path gives each token bit-identical
  * results whether it runs alone or batched with others.  Errors: E_ARG,
  * E_SHAPE, E_NOT_LOADED, E_WORKSPACE, E_HIP. */
-int colimoe_forward(colimoe_ctx *ctx, int32_t layer, const float *x, int32_t T, const int32_t *idx,
+COLIMOE_API int colimoe_forward(colimoe_ctx *ctx, int32_t layer, const float *x, int32_t T, const int32_t *idx,
                     const float *w, const colimoe_union *u, float *residual, uint32_t flags);
+
+/* colimoe_route followed by colimoe_forward on the same x, as one call: the
+ * route kernel also encodes x for the fixed-point path, saving a launch.
+ * idx, w (outputs) and u (NULL: the workspace's lists) are written as by
+ * colimoe_route.  Errors: as colimoe_route and colimoe_forward. */
+COLIMOE_API int colimoe_route_forward(colimoe_ctx *ctx, int32_t layer, const float *x, int32_t T, int32_t *idx, float *w,
+                          const colimoe_union *u, float *residual, uint32_t flags);
 
 /* x_out[t] = r[t] / sqrt(mean(r[t]^2) + eps), unit weight, fp32 (device
  * pointers, [T][d]); lets a stack of layers run without leaving the GPU. */
-int colimoe_rmsnorm(colimoe_ctx *ctx, const float *r, int32_t T, float eps, float *x_out);
+COLIMOE_API int colimoe_rmsnorm(colimoe_ctx *ctx, const float *r, int32_t T, float eps, float *x_out);
 
 /* One expert on one token through the fp32 path, every stage exposed
  * (device pointers, any of g/u/h may be NULL): x [d] -> g, u, h [f], y [d].
  * e = -1 selects the shared expert.  Debug and parity only. */
-int colimoe_debug_expert(colimoe_ctx *ctx, int32_t layer, int32_t e, const float *x, float *g, float *u,
+COLIMOE_API int colimoe_debug_expert(colimoe_ctx *ctx, int32_t layer, int32_t e, const float *x, float *g, float *u,
                          float *h, float *y);
 
 /* Per-kernel timing for measurement.  While enabled, every kernel launch of
  * the context is bracketed by a pair of HIP events on its stream (this adds
- * two event records per launch).  Kernel names: "router", "topk", "union",
- * "gateup", "down", "combine", "rmsnorm". */
-int colimoe_timing_enable(colimoe_ctx *ctx, int enable);
+ * two event records per launch).  Kernel names: "route" (router, fused with
+ * top-k and union when T <= 16), "topk", "union", "encode" (fixed-point
+ * encoding of x), "gateup", "down" (with the combine when it fits in LDS),
+ * "combine", "rmsnorm". */
+COLIMOE_API int colimoe_timing_enable(colimoe_ctx *ctx, int enable);
 
 /* Synchronises the stream, then reports the summed duration (ms) and the
  * number of launches of kernel `name` recorded since the last reset; clears
  * the records if reset != 0.  Errors: E_ARG (unknown name), E_HIP. */
-int colimoe_timing_read(colimoe_ctx *ctx, const char *name, double *total_ms, int64_t *count, int reset);
+COLIMOE_API int colimoe_timing_read(colimoe_ctx *ctx, const char *name, double *total_ms, int64_t *count, int reset);
 
 /* Wait for the context's stream; reports a kernel fault as E_HIP. */
-int colimoe_sync(colimoe_ctx *ctx);
+COLIMOE_API int colimoe_sync(colimoe_ctx *ctx);
 
 /* Static text for a status code. */
-const char *colimoe_status_str(int status);
+COLIMOE_API const char *colimoe_status_str(int status);
 
 #ifdef __cplusplus
 }

@@ -11,7 +11,7 @@ SOURCES = [os.path.join(CSRC, "host.cpp"), os.path.join(CSRC, "kernels.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-fvisibility=hidden",
     # every float operation is written out; no implicit contraction
     "-ffp-contract=off",
     # no packed-fp32 instructions in device code

@@ -39,13 +39,14 @@ struct colimoe_ctx {
     hipEvent_t a, b;
   };
   std::vector<Rec> recs;
-  double tot_ms[8];
-  long long cnt[8];
+  double tot_ms[16];
+  long long cnt[16];
 };
 
 namespace {
-const char *const kKernelNames[] = {"router", "topk", "union", "gateup", "down", "combine", "rmsnorm"};
-enum { K_ROUTER, K_TOPK, K_UNION, K_GATEUP, K_DOWN, K_COMBINE, K_RMSNORM, K_COUNT };
+// "route": the fused route kernel, or the router GEMV/GEMM when top-k runs apart.
+const char *const kKernelNames[] = {"route", "topk", "union", "encode", "gateup", "down", "combine", "rmsnorm"};
+enum { K_ROUTE, K_TOPK, K_UNION, K_ENCODE, K_GATEUP, K_DOWN, K_COMBINE, K_RMSNORM, K_COUNT };
 
 hipEvent_t take_event(colimoe_ctx *c) {
   if (c->ev_used == c->ev_pool.size()) {
@@ -96,7 +97,7 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 bool cfg_ok(const colimoe_config *c) {
   if (!c) return false;
   if (c->d <= 0 || c->f <= 0 || c->d % kGroup || c->f % kGroup) return false;
-  if (c->d > 16384 || c->f > 16384) return false;  // <= 8 chunks of 32 per lane
+  if (c->d > 16384 || c->f > 16384) return false;  // gate/up: at most 8 waves of 64 chunks per tile
   if (c->n_experts < 1 || c->n_experts > 1024) return false;
   if (c->top_k < 1 || c->top_k > 16 || c->top_k > c->n_experts) return false;
   if (c->n_layers < 1 || c->n_shared < 0 || c->n_shared > 1) return false;
@@ -168,18 +169,17 @@ int check_call(colimoe_ctx *ctx, int32_t layer, int32_t T) {
 
 // ---------------------------------------------------------------- repacking
 // Canonical blob -> device layout (internal.h): gate/up rows interleaved in
-// tiles of 4+4, scales regrouped per (tile, group) so one 16-byte load gives
-// a tile's 8 rows their scale, nibbles turned offset-binary (XOR 0x88).
+// tiles of 4+4, nibbles of a tile stored step-major, scales regrouped per
+// (tile, group) so one 16-byte load gives a tile's 8 rows their scale.
 
-inline void copy_xor88(uint8_t *dst, const uint8_t *src, size_t n) {
-  size_t i = 0;
-  for (; i + 8 <= n; i += 8) {
-    uint64_t v;
-    memcpy(&v, src + i, 8);
-    v ^= 0x8888888888888888ULL;
-    memcpy(dst + i, &v, 8);
+// Copies one canonical row of K nibbles into tile row r of tile `tile` of a
+// device matrix (step-major tiles).
+inline void put_row(uint8_t *dst_nib, const uint8_t *src_row, int tile, int r, int K) {
+  const int C = K / kChunk;
+  for (int c0 = 0; c0 < C; c0 += 64) {
+    const int width = std::min(64, C - c0);
+    memcpy(dst_nib + chunk_offset(tile, K, c0, r), src_row + (size_t)c0 * 16, (size_t)width * 16);
   }
-  for (; i < n; ++i) dst[i] = src[i] ^ 0x88;
 }
 
 void repack_expert(const uint8_t *src, uint8_t *dst, int d, int f) {
@@ -197,17 +197,17 @@ void repack_expert(const uint8_t *src, uint8_t *dst, int d, int f) {
   for (int ti = 0; ti < f / 4; ++ti) {
     for (int r = 0; r < 8; ++r) {
       const int srow = 4 * ti + (r & 3);
-      const uint8_t *s = (r < 4 ? gn : un) + (size_t)srow * rowd;
-      copy_xor88(dst + L.gu_nib + ((size_t)ti * 8 + r) * rowd, s, rowd);
+      put_row(dst + L.gu_nib, (r < 4 ? gn : un) + (size_t)srow * rowd, ti, r, d);
       const uint16_t *sc = (r < 4 ? gs : us) + (size_t)srow * Gd;
       for (int g = 0; g < Gd; ++g) gus[((size_t)ti * Gd + g) * 8 + r] = sc[g];
     }
   }
-  copy_xor88(dst + L.dn_nib, dn, (size_t)d * rowf);
   uint16_t *dss = (uint16_t *)(dst + L.dn_sc);
   for (int ti = 0; ti < d / 8; ++ti)
-    for (int r = 0; r < 8; ++r)
+    for (int r = 0; r < 8; ++r) {
+      put_row(dst + L.dn_nib, dn + ((size_t)ti * 8 + r) * rowf, ti, r, f);
       for (int g = 0; g < Gf; ++g) dss[((size_t)ti * Gf + g) * 8 + r] = ds[((size_t)ti * 8 + r) * Gf + g];
+    }
 }
 
 void repack_many(const uint8_t *const *srcs, uint8_t *dst, int n, size_t be, int d, int f) {
@@ -251,11 +251,133 @@ Workspace workspace_layout(int d, int f, int E, int k, int n_shared, int max_tok
   const size_t rows = tk + (size_t)max_tokens * n_shared;
   W.h = take(rows * f * 4);
   W.y = take(rows * d * 4);
+  W.xq = take((size_t)max_tokens * (d / kChunk) * kDigitWords * 4);
+  W.xs = take((size_t)max_tokens * (d / 16) * 4);
+  W.hq = take(rows * (f / kChunk) * kDigitWords * 4);
+  W.hs = take(rows * (f / 16) * 4);
   W.bytes = o;
   return W;
 }
 
 }  // namespace colimoe
+
+enum { PATH_FP32 = 0, PATH_FXP = 1 };
+
+// Arithmetic path of a forward call: the fixed-point activation path when the
+// shapes allow it (both d and f at least 2048) unless fp32 is asked for.
+static int select_path(colimoe_ctx *ctx, int T, uint32_t flags) {
+  const Dims D = dims_of(ctx, T);
+  if (flags == COLIMOE_FWD_BF16_MFMA) return COLIMOE_E_ARG;  // prefill path not built yet
+  if (flags == COLIMOE_FWD_FP32) return PATH_FP32;
+  if (flags == COLIMOE_FWD_FXP) return fxp_supported(D) ? PATH_FXP : COLIMOE_E_SHAPE;
+  return fxp_supported(D) ? PATH_FXP : PATH_FP32;
+}
+
+static colimoe_union ws_union_abi(colimoe_ctx *ctx) {
+  const UnionDev U = ws_union(ctx);
+  colimoe_union u;
+  u.n_unique = U.n_unique;
+  u.ids = U.ids;
+  u.offsets = U.offsets;
+  u.pair_token = U.pair_token;
+  u.pair_slot = U.pair_slot;
+  u.pair_of = U.pair_of;
+  return u;
+}
+
+// Router, top-k and (if u) union lists; `encode` also writes the fixed-point
+// encoding of x into the workspace when the route runs as one kernel.
+static int route_impl(colimoe_ctx *ctx, int32_t layer, const float *x, int32_t T, int32_t *idx, float *w,
+               const colimoe_union *u, float *logits, bool encode) {
+  const Dims D = dims_of(ctx, T);
+  const LayerDev L = layer_of(ctx, layer);
+  float *lg = logits ? logits : (float *)(ctx->ws + ctx->wl.logits);
+  hipStream_t s = ctx->stream;
+  int32_t *err = (int32_t *)(ctx->ws + ctx->wl.err);
+  if (D.T <= kRouteSplitMaxT) {
+    {
+      KTimer kt(ctx, K_ROUTE);
+      uint32_t *xq = encode ? (uint32_t *)(ctx->ws + ctx->wl.xq) : nullptr;
+      float *xs = encode ? (float *)(ctx->ws + ctx->wl.xs) : nullptr;
+      if (launch_router_split(L, D, x, lg, xq, xs, s) != hipSuccess) return COLIMOE_E_HIP;
+    }
+    if (D.T == 1) {
+      KTimer kt(ctx, K_TOPK);
+      const UnionDev U = u ? to_dev(u) : UnionDev{};
+      if (launch_topk_union1(lg, D, idx, w, u ? &U : nullptr, s) != hipSuccess) return COLIMOE_E_HIP;
+      return COLIMOE_OK;
+    }
+  } else {
+    KTimer kt(ctx, K_ROUTE);
+    if (launch_router(L, D, x, lg, s) != hipSuccess) return COLIMOE_E_HIP;
+  }
+  {
+    KTimer kt(ctx, K_TOPK);
+    if (launch_topk(lg, D, idx, w, s) != hipSuccess) return COLIMOE_E_HIP;
+  }
+  if (u) {
+    KTimer kt(ctx, K_UNION);
+    if (launch_union(idx, D, to_dev(u), err, s) != hipSuccess) return COLIMOE_E_HIP;
+  }
+  return COLIMOE_OK;
+}
+
+// Expert work and combine.  x_encoded: the workspace already holds the
+// fixed-point encoding of this x (written by the route kernel).
+static int forward_impl(colimoe_ctx *ctx, int32_t layer, const float *x, int32_t T, const int32_t *idx, const float *w,
+                 const colimoe_union *u, float *residual, int path, bool x_encoded) {
+  const Dims D = dims_of(ctx, T);
+  const LayerDev L = layer_of(ctx, layer);
+  hipStream_t s = ctx->stream;
+  UnionDev U;
+  if (u) {
+    U = to_dev(u);
+  } else {
+    U = ws_union(ctx);
+    KTimer kt(ctx, K_UNION);
+    if (launch_union(idx, D, U, (int32_t *)(ctx->ws + ctx->wl.err), s) != hipSuccess) return COLIMOE_E_HIP;
+  }
+  float *h = (float *)(ctx->ws + ctx->wl.h);
+  float *y = (float *)(ctx->ws + ctx->wl.y);
+  const bool fused = down_fusable(D);
+  if (path == PATH_FXP) {
+    uint32_t *xq = (uint32_t *)(ctx->ws + ctx->wl.xq);
+    float *xs = (float *)(ctx->ws + ctx->wl.xs);
+    uint32_t *hq = (uint32_t *)(ctx->ws + ctx->wl.hq);
+    float *hs = (float *)(ctx->ws + ctx->wl.hs);
+    if (!x_encoded) {
+      KTimer kt(ctx, K_ENCODE);
+      if (launch_xquant(x, T, D.d, xq, xs, s) != hipSuccess) return COLIMOE_E_HIP;
+    }
+    {
+      KTimer kt(ctx, K_GATEUP);
+      if (launch_gateup_fxp(L, D, xq, xs, U, h, hq, hs, nullptr, nullptr, s) != hipSuccess) return COLIMOE_E_HIP;
+    }
+    if (T == 1) {
+      KTimer kt(ctx, K_DOWN);
+      if (launch_down_dec(L, D, hq, hs, U, w, residual, s) != hipSuccess) return COLIMOE_E_HIP;
+      return COLIMOE_OK;  // combine done in the kernel
+    }
+    {
+      KTimer kt(ctx, K_DOWN);
+      if (launch_down_fxp(L, D, hq, hs, U, y, w, residual, fused, s) != hipSuccess) return COLIMOE_E_HIP;
+    }
+  } else {
+    {
+      KTimer kt(ctx, K_GATEUP);
+      if (launch_gateup(L, D, x, U, h, s) != hipSuccess) return COLIMOE_E_HIP;
+    }
+    {
+      KTimer kt(ctx, K_DOWN);
+      if (launch_down(L, D, h, U, y, w, residual, fused, s) != hipSuccess) return COLIMOE_E_HIP;
+    }
+  }
+  if (!fused) {
+    KTimer kt(ctx, K_COMBINE);
+    if (launch_combine(D, w, U, y, residual, s) != hipSuccess) return COLIMOE_E_HIP;
+  }
+  return COLIMOE_OK;
+}
 
 extern "C" {
 
@@ -308,7 +430,7 @@ int colimoe_create(const colimoe_config *cfg, void *hip_stream, colimoe_ctx **ou
   c->staging_bytes = 0;
   c->timing = false;
   c->ev_used = 0;
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < 16; ++i) {
     c->tot_ms[i] = 0.0;
     c->cnt[i] = 0;
   }
@@ -416,24 +538,7 @@ int colimoe_route(colimoe_ctx *ctx, int32_t layer, const float *x, int32_t T, in
   if (!x || !idx || !w || !aligned(x, 16) || !aligned(idx, 4) || !aligned(w, 4)) return COLIMOE_E_ARG;
   if (logits && !aligned(logits, 4)) return COLIMOE_E_ARG;
   if (u && !union_ok(u)) return COLIMOE_E_ARG;
-  const Dims D = dims_of(ctx, T);
-  const LayerDev L = layer_of(ctx, layer);
-  float *lg = logits ? logits : (float *)(ctx->ws + ctx->wl.logits);
-  hipStream_t s = ctx->stream;
-  {
-    KTimer kt(ctx, K_ROUTER);
-    if (launch_router(L, D, x, lg, s) != hipSuccess) return COLIMOE_E_HIP;
-  }
-  {
-    KTimer kt(ctx, K_TOPK);
-    if (launch_topk(lg, D, idx, w, s) != hipSuccess) return COLIMOE_E_HIP;
-  }
-  if (u) {
-    KTimer kt(ctx, K_UNION);
-    if (launch_union(idx, D, to_dev(u), (int32_t *)(ctx->ws + ctx->wl.err), s) != hipSuccess)
-      return COLIMOE_E_HIP;
-  }
-  return COLIMOE_OK;
+  return route_impl(ctx, layer, x, T, idx, w, u, logits, false);
 }
 
 int colimoe_union_build(colimoe_ctx *ctx, const int32_t *idx, int32_t T, const colimoe_union *u) {
@@ -450,40 +555,35 @@ int colimoe_forward(colimoe_ctx *ctx, int32_t layer, const float *x, int32_t T, 
                     const colimoe_union *u, float *residual, uint32_t flags) {
   int rc = check_call(ctx, layer, T);
   if (rc) return rc;
-  if (flags != COLIMOE_FWD_AUTO && flags != COLIMOE_FWD_FP32 && flags != COLIMOE_FWD_BF16_MFMA)
-    return COLIMOE_E_ARG;
-  if (flags == COLIMOE_FWD_BF16_MFMA) return COLIMOE_E_ARG;  // prefill path not built yet
+  if (flags > COLIMOE_FWD_FXP) return COLIMOE_E_ARG;
   if (T == 0) return COLIMOE_OK;  // nothing to read or write; pointers may be NULL
   if (!x || !idx || !w || !residual || !aligned(x, 16) || !aligned(idx, 4) || !aligned(w, 4) ||
       !aligned(residual, 4))
     return COLIMOE_E_ARG;
   if (u && !union_ok(u)) return COLIMOE_E_ARG;
-  const Dims D = dims_of(ctx, T);
-  const LayerDev L = layer_of(ctx, layer);
-  hipStream_t s = ctx->stream;
-  UnionDev U;
-  if (u) {
-    U = to_dev(u);
-  } else {
-    U = ws_union(ctx);
-    KTimer kt(ctx, K_UNION);
-    if (launch_union(idx, D, U, (int32_t *)(ctx->ws + ctx->wl.err), s) != hipSuccess) return COLIMOE_E_HIP;
-  }
-  float *h = (float *)(ctx->ws + ctx->wl.h);
-  float *y = (float *)(ctx->ws + ctx->wl.y);
-  {
-    KTimer kt(ctx, K_GATEUP);
-    if (launch_gateup(L, D, x, U, h, s) != hipSuccess) return COLIMOE_E_HIP;
-  }
-  {
-    KTimer kt(ctx, K_DOWN);
-    if (launch_down(L, D, h, U, y, s) != hipSuccess) return COLIMOE_E_HIP;
-  }
-  {
-    KTimer kt(ctx, K_COMBINE);
-    if (launch_combine(D, idx, w, U, y, residual, s) != hipSuccess) return COLIMOE_E_HIP;
-  }
-  return COLIMOE_OK;
+  int path = select_path(ctx, T, flags);
+  if (path < 0) return path;
+  return forward_impl(ctx, layer, x, T, idx, w, u, residual, path, false);
+}
+
+int colimoe_route_forward(colimoe_ctx *ctx, int32_t layer, const float *x, int32_t T, int32_t *idx, float *w,
+                          const colimoe_union *u, float *residual, uint32_t flags) {
+  int rc = check_call(ctx, layer, T);
+  if (rc) return rc;
+  if (flags > COLIMOE_FWD_FXP) return COLIMOE_E_ARG;
+  if (T == 0) return COLIMOE_OK;
+  if (!x || !idx || !w || !residual || !aligned(x, 16) || !aligned(idx, 4) || !aligned(w, 4) ||
+      !aligned(residual, 4))
+    return COLIMOE_E_ARG;
+  if (u && !union_ok(u)) return COLIMOE_E_ARG;
+  const int path = select_path(ctx, T, flags);
+  if (path < 0) return path;
+  const colimoe_union uw = ws_union_abi(ctx);
+  const colimoe_union *uu = u ? u : &uw;
+  const bool encode = path == PATH_FXP;
+  rc = route_impl(ctx, layer, x, T, idx, w, uu, nullptr, encode);
+  if (rc) return rc;
+  return forward_impl(ctx, layer, x, T, idx, w, uu, residual, path, encode && T <= kRouteSplitMaxT);
 }
 
 int colimoe_rmsnorm(colimoe_ctx *ctx, const float *r, int32_t T, float eps, float *x_out) {
@@ -523,7 +623,7 @@ int colimoe_debug_expert(colimoe_ctx *ctx, int32_t layer, int32_t e, const float
   float *hh = h ? h : (float *)(ctx->ws + ctx->wl.h);
   const LayerDev L = layer_of(ctx, layer);
   if (launch_debug_gateup(L, D, x, U, hh, g, u, s) != hipSuccess) return COLIMOE_E_HIP;
-  if (launch_down(L, D, hh, U, y, s) != hipSuccess) return COLIMOE_E_HIP;
+  if (launch_down(L, D, hh, U, y, nullptr, nullptr, false, s) != hipSuccess) return COLIMOE_E_HIP;
   return hip_status(hipStreamSynchronize(s));  // keeps `host` alive for the copies
 }
 
@@ -544,7 +644,7 @@ int colimoe_timing_read(colimoe_ctx *ctx, const char *name, double *total_ms, in
   *total_ms = ctx->tot_ms[kid];
   *count = ctx->cnt[kid];
   if (reset)
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 16; ++i) {
       ctx->tot_ms[i] = 0.0;
       ctx->cnt[i] = 0;
     }

@@ -15,17 +15,34 @@ constexpr int kTileRows = 8; // rows of one tile (one wave reduces 8 rows at onc
 // ---------------------------------------------------------------------------
 // Device layout of one expert (same byte count as the canonical blob).
 //
-//   gu_nib  [2f rows][d/2 B]  gate and up rows interleaved by tiles of 8:
-//           device row 8i+r is gate row 4i+r (r < 4) or up row 4i+r-4 (r >= 4)
+//   gu_nib  gate and up rows interleaved by tiles of 8: tile i holds gate rows
+//           4i..4i+3 (tile rows 0-3) and up rows 4i..4i+3 (tile rows 4-7)
 //   gu_sc   [f/4 tiles][d/64 groups][8 rows] fp16
-//   dn_nib  [d rows][f/2 B]   natural row order
+//   dn_nib  down rows in natural order, tiles of 8
 //   dn_sc   [d/8 tiles][f/64 groups][8 rows] fp16
 //
-// Nibbles are stored offset-binary (n + 8, i.e. the canonical byte XOR 0x88)
-// so a byte-to-float conversion yields n + 8 directly; the kernels fold the
-// -8 into each chunk's starting value.  A 16-byte load of scales gives the 8
-// rows of a tile their scale for one 64-wide group.
+// Nibble bytes of a tile (8 rows of K/2 bytes) are stored step-major: step j
+// covers 32-column chunks 64j..64j+63 of all 8 rows, row after row, so the
+// 8 rows x 1 KB one wave reads for a step are contiguous (rows shorter than
+// 64 chunks are simply row-major within the tile).
+// Nibbles keep the canonical two's-complement encoding.  A 16-byte load of
+// scales gives the 8 rows of a tile their scale for one 64-wide group.
 // ---------------------------------------------------------------------------
+
+// Byte offset of chunk c (32 columns, 16 bytes) of row r of tile `tile` in a
+// matrix whose rows have K columns.
+__host__ __device__ inline size_t chunk_offset(int tile, int K, int c, int r) {
+  const int C = K / kChunk;
+  const int j = c >> 6, cl = c & 63;
+  const int width = (C - 64 * j) < 64 ? (C - 64 * j) : 64;
+  return (size_t)tile * kTileRows * (size_t)(K / 2) + (size_t)j * (kTileRows * 64 * 16) + (size_t)r * width * 16 +
+         (size_t)cl * 16;
+}
+
+constexpr int kDigitWords = 24;               // fixed-point activations: words per 32-column chunk
+constexpr int kRouteSplitMaxT = 16;           // router with K split over waves up to this many tokens
+constexpr size_t kFusedLdsMax = 64 * 1024;    // LDS budget of the fused down + combine kernel
+
 struct ExpertLayout {
   size_t gu_nib, gu_sc, dn_nib, dn_sc, bytes;
 };
@@ -60,28 +77,51 @@ struct UnionDev {
 
 // Workspace carve-up (all offsets 256-byte aligned).
 struct Workspace {
-  size_t err;  // int32 error word set by kernels that reject a routing
+  size_t err;     // int32 error word set by kernels that reject a routing
   size_t n_unique, ids, offsets, pair_token, pair_slot, pair_of;  // union lists
   size_t logits;  // [Tmax][E] fp32
   size_t h;       // [(Tmax*k + Tmax*n_shared)][f] fp32
   size_t y;       // [(Tmax*k + Tmax*n_shared)][d] fp32
+  size_t xq, xs;  // fixed-point x: [Tmax][d/32][24] u32 digit words, [Tmax][d/16] fp32 scales
+  size_t hq, hs;  // fixed-point h: [rows][f/32][24] u32, [rows][f/16] fp32
   size_t bytes;
 };
 
 Workspace workspace_layout(int d, int f, int E, int k, int n_shared, int max_tokens);
 
 // Kernel launchers (kernels.hip).  All enqueue on `s`, return hipError_t.
+// Router with each expert row split over a block's 4 waves (T <= 16); xq/xs
+// non-null: also encodes x for the fixed-point gate/up kernel.
+hipError_t launch_router_split(const LayerDev &L, const Dims &D, const float *x, float *logits, uint32_t *xq,
+                               float *xs, hipStream_t s);
+// Top-k of one token and, if U, its union lists (T == 1).
+hipError_t launch_topk_union1(const float *logits, const Dims &D, int32_t *idx, float *w, const UnionDev *U,
+                              hipStream_t s);
 hipError_t launch_router(const LayerDev &L, const Dims &D, const float *x, float *logits, hipStream_t s);
 hipError_t launch_topk(const float *logits, const Dims &D, int32_t *idx, float *w, hipStream_t s);
 hipError_t launch_union(const int32_t *idx, const Dims &D, const UnionDev &U, int32_t *err, hipStream_t s);
 hipError_t launch_gateup(const LayerDev &L, const Dims &D, const float *x, const UnionDev &U, float *h,
                          hipStream_t s);
-hipError_t launch_down(const LayerDev &L, const Dims &D, const float *h, const UnionDev &U, float *y,
-                       hipStream_t s);
-hipError_t launch_combine(const Dims &D, const int32_t *idx, const float *w, const UnionDev &U, const float *y,
-                          float *residual, hipStream_t s);
-hipError_t launch_rmsnorm(const float *r, int T, int d, float eps, float *x, hipStream_t s);
 hipError_t launch_debug_gateup(const LayerDev &L, const Dims &D, const float *x, const UnionDev &U, float *h,
                                float *g, float *u, hipStream_t s);
+bool down_fusable(const Dims &D);
+// fused: y stays in LDS and the combine into `residual` happens in the same
+// kernel; otherwise y is written to global memory for launch_combine.
+hipError_t launch_down(const LayerDev &L, const Dims &D, const float *h, const UnionDev &U, float *y,
+                       const float *w, float *residual, bool fused, hipStream_t s);
+hipError_t launch_combine(const Dims &D, const float *w, const UnionDev &U, const float *y, float *residual,
+                          hipStream_t s);
+// Fixed-point activation path (d >= 2048 and f >= 2048).
+bool fxp_supported(const Dims &D);
+hipError_t launch_xquant(const float *x, int T, int K, uint32_t *xq, float *xs, hipStream_t s);
+hipError_t launch_gateup_fxp(const LayerDev &L, const Dims &D, const uint32_t *xq, const float *xs,
+                             const UnionDev &U, float *h, uint32_t *hq, float *hs, float *g, float *u,
+                             hipStream_t s);
+hipError_t launch_down_fxp(const LayerDev &L, const Dims &D, const uint32_t *hq, const float *hs, const UnionDev &U,
+                           float *y, const float *w, float *residual, bool fused, hipStream_t s);
+// Down + combine for one token, one wave per output tile (T == 1).
+hipError_t launch_down_dec(const LayerDev &L, const Dims &D, const uint32_t *hq, const float *hs, const UnionDev &U,
+                           const float *w, float *residual, hipStream_t s);
+hipError_t launch_rmsnorm(const float *r, int T, int d, float eps, float *x, hipStream_t s);
 
 }  // namespace colimoe

@@ -34,13 +34,15 @@ __device__ __forceinline__ float tile_scale(const uint4 &s, int r) {
   return (r & 1) ? half_hi(w) : half_lo(w);
 }
 
-// Dot product of 32 offset-binary nibbles (one 16-byte load) with 32 fp32
-// activations, minus 8 * (their sum), which the caller passes in as `nsx`:
-//   sum_i (n_i + 8 - 8) x_i = sum_i q_i x_i.
+// Dot product of 32 int4 weights (one 16-byte load of two's-complement
+// nibbles) with 32 fp32 activations.  Each word is flipped to offset binary
+// (n = q + 8, XOR 0x88888888), converted byte by byte, and the -8 * (sum of
+// the activations), which the caller passes in as `nsx`, starts the sum:
+//   sum_i (n_i - 8) x_i = sum_i q_i x_i.
 // Byte b of word i holds columns 8i+2b (low nibble) and 8i+2b+1 (high).
 // Even columns accumulate into alo, odd columns (read as 16 n) into ahi.
 __device__ __forceinline__ float chunk_dot(const uint4 &w, const float4 *xv, float nsx) {
-  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+  const uint32_t ws[4] = {w.x ^ 0x88888888u, w.y ^ 0x88888888u, w.z ^ 0x88888888u, w.w ^ 0x88888888u};
   float alo = nsx, ahi = 0.0f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -68,13 +70,50 @@ __device__ __forceinline__ float neg8_sum(const float4 *xv) {
   return -8.0f * t;
 }
 
-__device__ __forceinline__ float dpp_shr(float v, int n) {
-  // row_shr:n within 16-lane rows; lanes without a source read 0
-  switch (n) {
-    case 1: return bits_f(__builtin_amdgcn_update_dpp(0u, f_bits(v), 0x111, 0xF, 0xF, false));
-    case 2: return bits_f(__builtin_amdgcn_update_dpp(0u, f_bits(v), 0x112, 0xF, 0xF, false));
-    default: return bits_f(__builtin_amdgcn_update_dpp(0u, f_bits(v), 0x114, 0xF, 0xF, false));
-  }
+// DPP moves within 16-lane rows (lanes without a source read 0).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114;
+constexpr int kRowRor1 = 0x121, kRowRor2 = 0x122, kRowRor4 = 0x124, kRowRor8 = 0x128;
+
+// Value of lane l ^ 32 (one permlane32 swap).
+__device__ __forceinline__ uint32_t xor32(uint32_t v) {
+  auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return (threadIdx.x & 32) ? r[0] : r[1];
+}
+// Value of lane l ^ 16 (one permlane16 swap).
+__device__ __forceinline__ uint32_t xor16(uint32_t v) {
+  auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return (threadIdx.x & 16) ? r[0] : r[1];
+}
+
+// Sum over the 64 lanes of a wave, every lane receiving the same value.
+// Fixed tree: l^32, l^16, then rotations by 8, 4, 2, 1 inside 16-lane rows.
+__device__ __forceinline__ float wave_sum(float v) {
+  v = v + bits_f(xor32(f_bits(v)));
+  v = v + bits_f(xor16(f_bits(v)));
+  v = v + bits_f(dpp<kRowRor8>(f_bits(v)));
+  v = v + bits_f(dpp<kRowRor4>(f_bits(v)));
+  v = v + bits_f(dpp<kRowRor2>(f_bits(v)));
+  v = v + bits_f(dpp<kRowRor1>(f_bits(v)));
+  return v;
+}
+
+// Maximum over the 64 lanes of a wave (unsigned 64-bit), every lane receiving it.
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint32_t lo, uint32_t hi) {
+  const uint64_t b = ((uint64_t)hi << 32) | lo;
+  return b > a ? b : a;
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  v = max_u64(v, xor32((uint32_t)v), xor32((uint32_t)(v >> 32)));
+  v = max_u64(v, xor16((uint32_t)v), xor16((uint32_t)(v >> 32)));
+  v = max_u64(v, dpp<kRowRor8>((uint32_t)v), dpp<kRowRor8>((uint32_t)(v >> 32)));
+  v = max_u64(v, dpp<kRowRor4>((uint32_t)v), dpp<kRowRor4>((uint32_t)(v >> 32)));
+  v = max_u64(v, dpp<kRowRor2>((uint32_t)v), dpp<kRowRor2>((uint32_t)(v >> 32)));
+  v = max_u64(v, dpp<kRowRor1>((uint32_t)v), dpp<kRowRor1>((uint32_t)(v >> 32)));
+  return v;
 }
 
 // Transposed reduction of 8 per-lane partials (one per tile row) across the
@@ -93,14 +132,13 @@ __device__ __forceinline__ float reduce8_rows(const float *p) {
     auto r = __builtin_amdgcn_permlane16_swap(f_bits(q[i]), f_bits(q[i + 2]), false, false);
     t[i] = bits_f(r[0]) + bits_f(r[1]);  // 16-lane rows: i, i+2, i+4, i+6
   }
-  const int lane = threadIdx.x & 63;
-  const bool upper8 = (lane & 8) != 0;
-  float keep = upper8 ? t[1] : t[0];
-  float send = upper8 ? t[0] : t[1];
-  float v = keep + bits_f(__builtin_amdgcn_update_dpp(0u, f_bits(send), 0x128, 0xF, 0xF, false));  // row_ror:8
-  v = v + dpp_shr(v, 4);
-  v = v + dpp_shr(v, 2);
-  v = v + dpp_shr(v, 1);
+  const bool upper8 = (threadIdx.x & 8) != 0;
+  const float keep = upper8 ? t[1] : t[0];
+  const float send = upper8 ? t[0] : t[1];
+  float v = keep + bits_f(dpp<kRowRor8>(f_bits(send)));
+  v = v + bits_f(dpp<kRowShr4>(f_bits(v)));
+  v = v + bits_f(dpp<kRowShr2>(f_bits(v)));
+  v = v + bits_f(dpp<kRowShr1>(f_bits(v)));
   return v;
 }
 
@@ -139,23 +177,37 @@ __device__ __forceinline__ bool resolve_slot(const Dims &D, const UnionDev &U, i
   return D.n_shared > 0;
 }
 
+// Pair p of slot s: its token (activation row) and its output row; a token
+// outside [0, T) in caller-supplied lists yields orow = -1 (skipped).
+__device__ __forceinline__ void slot_token(const Dims &D, const UnionDev &U, int nu, int s, int p, int &t, int &orow) {
+  if (s < nu) {
+    t = U.pair_token[p];
+    orow = p;
+  } else {
+    t = p;
+    orow = D.T * D.k + p;
+  }
+  if (t < 0 || t >= D.T) {
+    t = 0;
+    orow = -1;
+  }
+}
+
 // ------------------------------------------------------------------- router
 // A1 ([A] §1: a router picks 8 of the 256 experts): logits l[t][e] =
 // sum_c R[e][c] x[t][c] + b[e] in fp32.  One wave per expert row; the row is
-// held in registers and applied to every token, each token's sum taken in
-// the same lane order and tree regardless of T.
+// held in registers and applied to every token; each token's sum runs in the
+// same lane order and tree whatever T is.
 
 template <int STEPS>
-__global__ __launch_bounds__(256) void k_router_gemv(LayerDev L, Dims D, const float *__restrict__ x,
-                                                     float *__restrict__ logits) {
+__device__ __forceinline__ void router_row(const LayerDev &L, const Dims &D, const float *__restrict__ x, int e,
+                                           float *__restrict__ logits) {
   const int lane = threadIdx.x & 63;
-  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (e >= D.E) return;
   const float *row = L.router + (size_t)e * D.d;
   float4 r[STEPS];
 #pragma unroll
   for (int i = 0; i < STEPS; ++i) {
-    int c = 4 * lane + 256 * i;
+    const int c = 4 * lane + 256 * i;
     r[i] = c < D.d ? *(const float4 *)(row + c) : make_float4(0.f, 0.f, 0.f, 0.f);
   }
   const float b = L.bias[e];
@@ -164,18 +216,25 @@ __global__ __launch_bounds__(256) void k_router_gemv(LayerDev L, Dims D, const f
     float acc = 0.0f;
 #pragma unroll
     for (int i = 0; i < STEPS; ++i) {
-      int c = 4 * lane + 256 * i;
+      const int c = 4 * lane + 256 * i;
       if (c < D.d) {
-        float4 xv = *(const float4 *)(xr + c);
+        const float4 xv = *(const float4 *)(xr + c);
         acc = __builtin_fmaf(r[i].x, xv.x, acc);
         acc = __builtin_fmaf(r[i].y, xv.y, acc);
         acc = __builtin_fmaf(r[i].z, xv.z, acc);
         acc = __builtin_fmaf(r[i].w, xv.w, acc);
       }
     }
-    acc = group_sum(acc, 64);
+    acc = wave_sum(acc);
     if (lane == 0) logits[(size_t)t * D.E + e] = acc + b;
   }
+}
+
+template <int STEPS>
+__global__ __launch_bounds__(256) void k_router_gemv(LayerDev L, Dims D, const float *__restrict__ x,
+                                                     float *__restrict__ logits) {
+  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (e < D.E) router_row<STEPS>(L, D, x, e, logits);
 }
 
 // Tiled variant for many tokens: a 64x64 block of (tokens, experts), K in
@@ -189,8 +248,8 @@ __global__ __launch_bounds__(256) void k_router_gemm(LayerDev L, Dims D, const f
   float acc[4][4] = {};
   for (int k0 = 0; k0 < D.d; k0 += 32) {
     for (int i = threadIdx.x; i < 64 * 32; i += 256) {
-      int rr = i >> 5, cc = i & 31;
-      int t = t0 + rr, e = e0 + rr;
+      const int rr = i >> 5, cc = i & 31;
+      const int t = t0 + rr, e = e0 + rr;
       xs[cc][rr] = t < D.T ? x[(size_t)t * D.d + k0 + cc] : 0.0f;
       rs[cc][rr] = e < D.E ? L.router[(size_t)e * D.d + k0 + cc] : 0.0f;
     }
@@ -212,30 +271,9 @@ __global__ __launch_bounds__(256) void k_router_gemm(LayerDev L, Dims D, const f
   }
   for (int i = 0; i < 4; ++i)
     for (int j = 0; j < 4; ++j) {
-      int t = t0 + ty * 4 + i, e = e0 + tx * 4 + j;
+      const int t = t0 + ty * 4 + i, e = e0 + tx * 4 + j;
       if (t < D.T && e < D.E) logits[(size_t)t * D.E + e] = acc[i][j] + L.bias[e];
     }
-}
-
-static bool launch_router_gemv(const LayerDev &L, const Dims &D, const float *x, float *logits, hipStream_t s) {
-  const int steps = (D.d + 255) / 256;
-  dim3 grid((D.E + 3) / 4), block(256);
-#define ROUTER_CASE(S) \
-  case S: k_router_gemv<S><<<grid, block, 0, s>>>(L, D, x, logits); return true;
-  switch (steps) {
-    ROUTER_CASE(1) ROUTER_CASE(2) ROUTER_CASE(3) ROUTER_CASE(4) ROUTER_CASE(6) ROUTER_CASE(8)
-    ROUTER_CASE(12) ROUTER_CASE(16) ROUTER_CASE(24) ROUTER_CASE(32) ROUTER_CASE(48) ROUTER_CASE(64)
-    default: return false;
-  }
-#undef ROUTER_CASE
-}
-
-hipError_t launch_router(const LayerDev &L, const Dims &D, const float *x, float *logits, hipStream_t s) {
-  if (D.T <= 0) return hipSuccess;
-  if (D.T <= 32 && launch_router_gemv(L, D, x, logits, s)) return hipGetLastError();
-  dim3 grid((D.T + 63) / 64, (D.E + 63) / 64), block(256);
-  k_router_gemm<<<grid, block, 0, s>>>(L, D, x, logits);
-  return hipGetLastError();
 }
 
 // -------------------------------------------------------------------- top-k
@@ -244,30 +282,21 @@ hipError_t launch_router(const LayerDev &L, const Dims &D, const float *x, float
 
 __device__ __forceinline__ uint64_t topk_key(float v, int e) {
   uint32_t b = f_bits(v);
-  if ((b & 0x7FFFFFFFu) == 0) b = 0;                       // +0 and -0 tie
-  uint32_t ord = (b & 0x80000000u) ? ~b : (b | 0x80000000u);  // monotone in v
+  if ((b & 0x7FFFFFFFu) == 0) b = 0;                                // +0 and -0 tie
+  const uint32_t ord = (b & 0x80000000u) ? ~b : (b | 0x80000000u);  // monotone in v
   return ((uint64_t)ord << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-  for (int o = 32; o > 0; o >>= 1) {
-    uint64_t w = __shfl_xor(v, o, 64);
-    v = w > v ? w : v;
-  }
-  return v;
-}
-
+// Selects for one token; lane 0 writes idx and w (and the ids to `lds_ids`
+// if given).  Every valid key is nonzero, so k <= E rounds always find one.
 template <int PER>
-__global__ __launch_bounds__(256) void k_topk(const float *__restrict__ logits, Dims D, int32_t *__restrict__ idx,
-                                              float *__restrict__ wout) {
+__device__ __forceinline__ void topk_token(const float *__restrict__ l, const Dims &D, int t,
+                                           int32_t *__restrict__ idx, float *__restrict__ wout, int32_t *lds_ids) {
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= D.T) return;
-  const float *l = logits + (size_t)t * D.E;
   uint64_t key[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
-    int e = lane + 64 * i;
+    const int e = lane + 64 * i;
     key[i] = e < D.E ? topk_key(l[e], e) : 0ull;
   }
   float vals[16];
@@ -279,7 +308,7 @@ __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ logits, 
 #pragma unroll
       for (int i = 0; i < PER; ++i) best = key[i] > best ? key[i] : best;
       best = wave_max_u64(best);
-      int e = (int)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFu));
+      const int e = (int)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFu));
       ids[j] = e;
       vals[j] = l[e];
 #pragma unroll
@@ -298,53 +327,50 @@ __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ logits, 
       if (j < D.k) {
         idx[(size_t)t * D.k + j] = ids[j];
         wout[(size_t)t * D.k + j] = expf(vals[j] - m) / sum;
+        if (lds_ids) lds_ids[t * D.k + j] = ids[j];
       }
   }
 }
 
-hipError_t launch_topk(const float *logits, const Dims &D, int32_t *idx, float *w, hipStream_t s) {
-  if (D.T <= 0) return hipSuccess;
-  dim3 grid((D.T + 3) / 4), block(256);
-  const int per = (D.E + 63) / 64;
-  if (per <= 1)
-    k_topk<1><<<grid, block, 0, s>>>(logits, D, idx, w);
-  else if (per <= 2)
-    k_topk<2><<<grid, block, 0, s>>>(logits, D, idx, w);
-  else if (per <= 4)
-    k_topk<4><<<grid, block, 0, s>>>(logits, D, idx, w);
-  else if (per <= 8)
-    k_topk<8><<<grid, block, 0, s>>>(logits, D, idx, w);
-  else
-    k_topk<16><<<grid, block, 0, s>>>(logits, D, idx, w);
-  return hipGetLastError();
+template <int PER>
+__global__ __launch_bounds__(256) void k_topk(const float *__restrict__ logits, Dims D, int32_t *__restrict__ idx,
+                                              float *__restrict__ wout) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t < D.T) topk_token<PER>(logits + (size_t)t * D.E, D, t, idx, wout, nullptr);
 }
 
 // -------------------------------------------------------------------- union
 // A3 ([A] §2, batch-union: batched positions read each unique expert once):
 // distinct experts ascending, and every (token, slot) pair grouped by expert
-// in token order.  One wave; ranks come from per-expert lane masks, so the
-// result is independent of timing.  Invalid routings (expert out of range,
-// or an expert twice in one token) produce an empty union and set *err.
+// in token order.  One wave; ranks come from per-expert lane masks in LDS, so
+// the result is independent of timing.  Invalid routings (expert out of
+// range, or an expert twice in one token) produce an empty union and set *err.
+// LDS: masks[E] u64 (8-byte aligned), counts[E], running[E], one flag.
 
-__global__ __launch_bounds__(64) void k_union(const int32_t *__restrict__ idx, Dims D, UnionDev U,
-                                              int32_t *__restrict__ err) {
-  // Dynamic LDS: masks[E] (8-byte aligned, first), counts[E], running[E], bad.
-  extern __shared__ __align__(16) unsigned long long union_lds[];
+__host__ __device__ inline size_t union_lds_bytes(int E) { return (size_t)E * 8 + (size_t)(2 * E + 1) * 4; }
+
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+__device__ void union_wave(const int32_t *__restrict__ idx, const Dims &D, const UnionDev &U,
+                           int32_t *__restrict__ err, unsigned long long *masks) {
   const int E = D.E, k = D.k, T = D.T;
-  unsigned long long *masks = union_lds;
-  int32_t *counts = (int32_t *)(union_lds + E);
+  int32_t *counts = (int32_t *)(masks + E);
   int32_t *running = counts + E;
   int32_t &bad = running[E];
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
   if (lane == 0) bad = 0;
   for (int e = lane; e < E; e += 64) {
     counts[e] = 0;
     masks[e] = 0ull;
   }
-  __syncthreads();
+  wave_lds_sync();
   for (int t = lane; t < T; t += 64) {
     for (int j = 0; j < k; ++j) {
-      int e = idx[(size_t)t * k + j];
+      const int e = idx[(size_t)t * k + j];
       bool ok = e >= 0 && e < E;
       for (int i = 0; i < j && ok; ++i) ok = idx[(size_t)t * k + i] != e;
       if (!ok)
@@ -353,7 +379,7 @@ __global__ __launch_bounds__(64) void k_union(const int32_t *__restrict__ idx, D
         atomicAdd(&counts[e], 1);
     }
   }
-  __syncthreads();
+  wave_lds_sync();
   if (bad) {
     if (lane == 0) {
       *U.n_unique = 0;
@@ -372,7 +398,7 @@ __global__ __launch_bounds__(64) void k_union(const int32_t *__restrict__ idx, D
   }
   int cinc = csum, ninc = nsum;
   for (int o = 1; o < 64; o <<= 1) {
-    int a = __shfl_up(cinc, o, 64), b = __shfl_up(ninc, o, 64);
+    const int a = __shfl_up(cinc, o, 64), b = __shfl_up(ninc, o, 64);
     if (lane >= o) {
       cinc += a;
       ninc += b;
@@ -392,7 +418,7 @@ __global__ __launch_bounds__(64) void k_union(const int32_t *__restrict__ idx, D
     *U.n_unique = ninc;
     U.offsets[ninc] = cinc;
   }
-  __syncthreads();
+  wave_lds_sync();
   for (int t0 = 0; t0 < T; t0 += 64) {
     const int t = t0 + lane;
     const bool act = t < T;
@@ -405,7 +431,7 @@ __global__ __launch_bounds__(64) void k_union(const int32_t *__restrict__ idx, D
         ee[j] = idx[(size_t)t * k + j];
         atomicOr(&masks[ee[j]], 1ull << lane);
       }
-    __syncthreads();
+    wave_lds_sync();
 #pragma unroll
     for (int j = 0; j < 16; ++j)
       if (act && j < k) {
@@ -416,149 +442,707 @@ __global__ __launch_bounds__(64) void k_union(const int32_t *__restrict__ idx, D
         U.pair_slot[p] = j;
         U.pair_of[(size_t)t * k + j] = p;
       }
-    __syncthreads();
+    wave_lds_sync();
 #pragma unroll
     for (int j = 0; j < 16; ++j)
       if (act && j < k && rr[j] == 0) {
         running[ee[j]] += __popcll(mm[j]);
         masks[ee[j]] = 0ull;
       }
-    __syncthreads();
+    wave_lds_sync();
   }
 }
 
-hipError_t launch_union(const int32_t *idx, const Dims &D, const UnionDev &U, int32_t *err, hipStream_t s) {
-  size_t lds = (size_t)D.E * 8 + (size_t)(2 * D.E + 1) * 4;
-  k_union<<<1, 64, lds, s>>>(idx, D, U, err);
-  return hipGetLastError();
+__global__ __launch_bounds__(64) void k_union(const int32_t *__restrict__ idx, Dims D, UnionDev U,
+                                              int32_t *__restrict__ err) {
+  extern __shared__ __align__(16) unsigned long long union_lds[];
+  union_wave(idx, D, U, err, union_lds);
 }
 
 // ----------------------------------------------------------- expert GEMVs
 // A4-A6: W[r][c] = q[r][c] * s[r][c/64] ([P] "conservative correctness":
 // int4, group size 64), dequantised to fp32 and multiplied in fp32 ([D] §4,
 // highlight 4: at batch 1, f32 rather than integer arithmetic), fp32
-// accumulation.  A wave owns one 8-row tile of one expert and streams it
-// chunk by chunk (LPR lanes per row, CPL 32-column chunks per lane); each
-// chunk's weights, once in registers, are applied to up to MT of the
-// expert's tokens, so for calls with at most MT tokens per expert every
-// weight is read from HBM once per call.  Per token and row the operations
-// (chunk dots, scale fmas in chunk order, reduction tree) do not depend on MT
-// or on the other tokens, which makes batched and one-at-a-time results
-// bit-identical.
+// accumulation.  Work is cut into 8-row tiles; each lane handles 32-column
+// chunks (one 16-byte load per row), each wave one 64-chunk step of a tile
+// (8 rows x 1 KB, contiguous in the device layout).  A step's weights, once
+// in registers, are applied to up to MT of the expert's tokens, so each
+// weight is read from HBM once per call when no expert has more than MT
+// tokens.  Per token and row the operations (chunk dots, scale fmas, lane
+// and wave reduction trees) do not depend on MT or on the other tokens:
+// batched and one-at-a-time results are bit-identical.
 
-template <int LPR>
-struct TileShape {
-  static constexpr int RG = 64 / LPR;                    // row groups per wave
-  static constexpr int RPG = (kTileRows + RG - 1) / RG;  // rows per lane
-};
-
-// One chunk (j) of a tile: weights + the 8 rows' scales for this lane.
-template <int LPR>
-__device__ __forceinline__ void load_chunk(const uint8_t *__restrict__ nib, const uint8_t *__restrict__ sc, int tile,
-                                           int K, int c, uint4 (&W)[TileShape<LPR>::RPG], uint4 &S) {
-  using TS = TileShape<LPR>;
-  const int gr = (threadIdx.x & 63) / LPR;
+__device__ __forceinline__ void load_step(const uint8_t *__restrict__ nib, const uint8_t *__restrict__ sc, int tile,
+                                          int K, int c, uint4 (&W)[kTileRows], uint4 &S) {
   const int G = K / kGroup;
-  const size_t rowb = (size_t)K / 2;
   S = *(const uint4 *)(sc + ((size_t)tile * G + (c >> 1)) * 16);
 #pragma unroll
-  for (int i = 0; i < TS::RPG; ++i) {
-    const int r = gr + TS::RG * i;
-    W[i] = r < kTileRows ? *(const uint4 *)(nib + ((size_t)tile * kTileRows + r) * rowb + (size_t)c * 16)
-                         : make_uint4(0u, 0u, 0u, 0u);
-  }
+  for (int r = 0; r < kTileRows; ++r) W[r] = *(const uint4 *)(nib + chunk_offset(tile, K, c, r));
 }
 
-// acc[i] += s_r * (sum over the chunk of q * x) for this lane's rows.
-template <int LPR>
-__device__ __forceinline__ void chunk_accumulate(const uint4 (&W)[TileShape<LPR>::RPG], const uint4 &S,
-                                                 const float *__restrict__ xrow, int c,
-                                                 float (&acc)[TileShape<LPR>::RPG]) {
-  using TS = TileShape<LPR>;
-  const int gr = (threadIdx.x & 63) / LPR;
+// acc[r] = fma(s_r, chunk dot, acc[r]) for the 8 rows of a step, one token.
+__device__ __forceinline__ void step_accumulate(const uint4 (&W)[kTileRows], const uint4 &S,
+                                                const float *__restrict__ xrow, int c, float (&acc)[kTileRows]) {
   float4 xv[8];
   const float4 *src = (const float4 *)(xrow + (size_t)kChunk * c);
 #pragma unroll
   for (int v = 0; v < 8; ++v) xv[v] = src[v];
   const float nsx = neg8_sum(xv);
 #pragma unroll
-  for (int i = 0; i < TS::RPG; ++i) {
-    const int r = gr + TS::RG * i;
-    if (r < kTileRows) acc[i] = __builtin_fmaf(tile_scale(S, r), chunk_dot(W[i], xv, nsx), acc[i]);
-  }
+  for (int r = 0; r < kTileRows; ++r) acc[r] = __builtin_fmaf(tile_scale(S, r), chunk_dot(W[r], xv, nsx), acc[r]);
 }
 
-// Reduce a tile for one token.  LPR == 64: lane 8r+7 returns row r's sum.
-// Otherwise the 8 row sums go to `rows` (wave-private LDS).
-template <int LPR>
-__device__ __forceinline__ float tile_reduce(const float *acc, float *rows) {
-  using TS = TileShape<LPR>;
-  if constexpr (LPR == 64) {
-    return reduce8_rows(acc);
-  } else {
-    const int lane = threadIdx.x & 63;
-    const int q = lane % LPR, gr = lane / LPR;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+// Gate/up for K = d >= 2048: a block of NW = ceil(d/2048) waves per work item
+// (unique expert slot, tile of 4 gate + 4 up rows); wave w handles chunks
+// 64w..64w+63 of the 8 rows, the block sums the waves' row totals in wave
+// order and writes h = SiLU(g) * u per pair.  Slot nu (after the routed
+// experts) is the shared expert with all T tokens ([D] §3).
+template <int MT>
+__global__ __launch_bounds__(512) void k_gateup_wide(LayerDev L, Dims D, const float *__restrict__ x, UnionDev U,
+                                                      float *__restrict__ h, float *__restrict__ gdbg,
+                                                      float *__restrict__ udbg) {
+  __shared__ float red[8][MT][kTileRows];
+  const int nw = blockDim.x >> 6, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int C = D.d / kChunk, tiles = D.f / 4;
+  const int nu = clamp_nu(U.n_unique, D);
+  const int items = (nu + D.n_shared) * tiles;
+  const ExpertLayout EL = expert_layout(D.d, D.f);
+  const int c = lane + 64 * wave;
+  const bool active = c < C;
+  for (int item = blockIdx.x; item < items; item += gridDim.x) {
+    const int s = item / tiles, ti = item - s * tiles;
+    int e, p0, p1;
+    if (!resolve_slot(D, U, nu, s, e, p0, p1)) continue;
+    const uint8_t *base = L.experts + (size_t)e * L.expert_stride;
+    uint4 W[kTileRows], S;
+    if (active) load_step(base + EL.gu_nib, base + EL.gu_sc, ti, D.d, c, W, S);
+    for (int pg = p0; pg < p1; pg += MT) {
+      const int mcount = min(MT, p1 - pg);
+      float acc[MT][kTileRows];
 #pragma unroll
-    for (int i = 0; i < TS::RPG; ++i) {
-      const float v = group_sum(acc[i], LPR);
-      const int r = gr + TS::RG * i;
-      if (q == 0 && r < kTileRows) rows[r] = v;
+      for (int m = 0; m < MT; ++m) {
+#pragma unroll
+        for (int r = 0; r < kTileRows; ++r) acc[m][r] = 0.0f;
+        if (m < mcount && active) {
+          int t, orow;
+          slot_token(D, U, nu, s, pg + m, t, orow);
+          step_accumulate(W, S, x + (size_t)t * D.d, c, acc[m]);
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+        if (m < mcount) {
+          const float v = reduce8_rows(acc[m]);
+          if ((lane & 7) == 7) red[wave][m][lane >> 3] = v;
+        }
+      __syncthreads();
+      if ((int)threadIdx.x < mcount * 4) {
+        const int m = threadIdx.x >> 2, r = threadIdx.x & 3;
+        float g = red[0][m][r], u = red[0][m][r + 4];
+        for (int w2 = 1; w2 < nw; ++w2) {
+          g = g + red[w2][m][r];
+          u = u + red[w2][m][r + 4];
+        }
+        int t, orow;
+        slot_token(D, U, nu, s, pg + m, t, orow);
+        if (orow >= 0) {
+          const size_t o = (size_t)orow * D.f + (size_t)ti * 4 + r;
+          h[o] = silu_f(g) * u;
+          if (gdbg) {
+            gdbg[o] = g;
+            udbg[o] = u;
+          }
+        }
+      }
+      __syncthreads();
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    return 0.0f;
   }
 }
 
-// Accumulate one tile over all K for up to MT tokens (token i of the group is
-// pair p0 + i of the slot).  acc[m][i]: lane partial of row i for token m.
-template <int LPR, int CPL, int MT>
-__device__ __forceinline__ void tile_pass(const uint8_t *__restrict__ nib, const uint8_t *__restrict__ sc, int tile,
-                                          int K, const float *__restrict__ xbase, size_t xstride,
-                                          const int (&xrow)[MT], int mcount, float (&acc)[MT][TileShape<LPR>::RPG]) {
-  using TS = TileShape<LPR>;
-  const int q = (threadIdx.x & 63) % LPR;
-  const int C = K / kChunk;
+// A7 for one 8-row output tile, y of every pair in LDS: per token and row,
+// the routed experts in ascending expert id (ascending pair index, since the
+// union lists are grouped by expert) weighted by w, then the shared expert.
+__device__ __forceinline__ void combine_tile(const Dims &D, const UnionDev &U, int nu, const float *__restrict__ w,
+                                             const float *ylds, float *__restrict__ residual, int ti) {
+  const int tk = D.T * D.k;
+  for (int q = threadIdx.x; q < D.T * kTileRows; q += blockDim.x) {
+    const int t = q >> 3, r = q & 7;
+    float *rp = residual + (size_t)t * D.d + (size_t)ti * kTileRows + r;
+    float acc = *rp;
+    if (nu > 0) {
+      int pj[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) pj[j] = j < D.k ? U.pair_of[(size_t)t * D.k + j] : 0x7FFFFFFF;
+      int prev = -1;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (i < D.k) {
+          int best = 0x7FFFFFFF, bj = 0;
+#pragma unroll
+          for (int j = 0; j < 16; ++j)
+            if (pj[j] > prev && pj[j] < best) {
+              best = pj[j];
+              bj = j;
+            }
+          if (best < tk) acc = __builtin_fmaf(w[(size_t)t * D.k + bj], ylds[(size_t)best * kTileRows + r], acc);
+          prev = best;
+        }
+      }
+    }
+    if (D.n_shared) acc = acc + ylds[((size_t)tk + t) * kTileRows + r];
+    *rp = acc;
+  }
+}
+
+// Down projection for K = f >= 2048 with the combine fused in: a block owns an
+// 8-row output tile; its waves take the call's slots round-robin, run all
+// chunk steps of their slot (y = Wd h for each of the slot's tokens) and
+// leave y in LDS; then the block adds, per token and row, the routed experts
+// in ascending expert id (ascending pair index) weighted by w, then the
+// shared expert, into the residual.  FUSED == false writes y to global
+// memory instead (k_combine finishes), for calls too large for LDS.
+template <int MT, bool FUSED, int NWMAX>
+__global__ __launch_bounds__(64 * NWMAX) void k_down_wide(LayerDev L, Dims D, const float *__restrict__ h, UnionDev U,
+                                                    float *__restrict__ y, const float *__restrict__ w,
+                                                    float *__restrict__ residual) {
+  extern __shared__ float ylds[];  // [T*k + T*n_shared][8] when FUSED
+  const int nw = blockDim.x >> 6, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int C = D.f / kChunk, tiles = D.d / kTileRows;
+  const int nu = clamp_nu(U.n_unique, D);
+  const int slots = nu + D.n_shared;
+  const int tk = D.T * D.k;
+  const ExpertLayout EL = expert_layout(D.d, D.f);
+  for (int ti = blockIdx.x; ti < tiles; ti += gridDim.x) {
+    for (int s = wave; s < slots; s += nw) {
+      int e, p0, p1;
+      if (!resolve_slot(D, U, nu, s, e, p0, p1)) continue;
+      const uint8_t *base = L.experts + (size_t)e * L.expert_stride;
+      for (int pg = p0; pg < p1; pg += MT) {
+        const int mcount = min(MT, p1 - pg);
+        float acc[MT][kTileRows];
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+          for (int r = 0; r < kTileRows; ++r) acc[m][r] = 0.0f;
+        for (int c = lane; c < ((C + 63) & ~63); c += 64) {
+          if (c < C) {
+            uint4 W[kTileRows], S;
+            load_step(base + EL.dn_nib, base + EL.dn_sc, ti, D.f, c, W, S);
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+              if (m < mcount) {
+                const int orow = (s < nu) ? pg + m : tk + pg + m;
+                step_accumulate(W, S, h + (size_t)orow * D.f, c, acc[m]);
+              }
+          }
+        }
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+          if (m < mcount) {
+            const float v = reduce8_rows(acc[m]);
+            if ((lane & 7) == 7) {
+              const int orow = (s < nu) ? pg + m : tk + pg + m;
+              if (FUSED)
+                ylds[(size_t)orow * kTileRows + (lane >> 3)] = v;
+              else
+                y[(size_t)orow * D.d + (size_t)ti * kTileRows + (lane >> 3)] = v;
+            }
+          }
+      }
+    }
+    if (FUSED) {
+      __syncthreads();
+      combine_tile(D, U, nu, w, ylds, residual, ti);
+      __syncthreads();
+    }
+  }
+}
+
+// ------------------------------------------------ fixed-point activations
+// A4-A6 on the decode path with exact int4 arithmetic.  Each group of 16
+// consecutive activations (x for gate/up, h for down) is encoded as signed
+// integers X_i = rint(v_i 2^(22-E)) with 2^E > max|v| over the group, so
+// |X_i| <= 2^22 and |v_i - X_i 2^(E-22)| <= 2^(E-23) <= 2^-22 max|v|.  X is
+// split into six signed base-16 digits (each in [-8, 7]) packed eight to a
+// word in the weights' nibble order, so one v_dot8_i32_i4 multiplies 8 int4
+// weights by 8 digits exactly.  Per 16 columns and row: six digit-plane
+// dot products (exact int32), recombined as sum_k 16^k a_k (exact in two
+// int32 halves, rounded once to fp32), scaled by s_row * 2^(E-22) and
+// accumulated in fp32 along the row.  The weights are the canonical
+// two's-complement nibbles, read as they are.
+
+// Encodes 16 values; words[2k + w] holds digit plane k of columns 8w..8w+7.
+__device__ __forceinline__ void quant16(const float *v, uint32_t *words, float &scale) {
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
+  int E = m > 0.0f ? ilogbf(m) + 1 : 0;  // m < 2^E
+  E = E < -100 ? -100 : E;
+  const float up = ldexpf(1.0f, 22 - E);
+  scale = ldexpf(1.0f, E - 22);
+#pragma unroll
+  for (int k = 0; k < 12; ++k) words[k] = 0u;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t B = (uint32_t)((int)__builtin_rintf(v[i] * up) + 0x888888);
+#pragma unroll
+    for (int k = 0; k < 6; ++k) words[2 * k + (i >> 3)] |= (((B >> (4 * k)) & 15u) ^ 8u) << (4 * (i & 7));
+  }
+}
+
+// acc += s * sum over a 32-column chunk of q_i * v_i, with the chunk's digit
+// words dg[24] ([half][plane][2]) and half-group scales xs[2].
+__device__ __forceinline__ float fxp_chunk(const uint4 &w, const uint32_t *dg, const float *xs, float s, float acc) {
+  const uint32_t wh[2][2] = {{w.x, w.y}, {w.z, w.w}};
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    int a[6];
+#pragma unroll
+    for (int k = 0; k < 6; ++k) {
+      a[k] = __builtin_amdgcn_sdot8((int)wh[hf][0], (int)dg[hf * 12 + 2 * k], 0, false);
+      a[k] = __builtin_amdgcn_sdot8((int)wh[hf][1], (int)dg[hf * 12 + 2 * k + 1], a[k], false);
+    }
+    const int lo = a[0] + (a[1] << 4) + (a[2] << 8);
+    const int hi = a[3] + (a[4] << 4) + (a[5] << 8);
+    const float V = __builtin_fmaf((float)hi, 4096.0f, (float)lo);
+    acc = __builtin_fmaf(s * xs[hf], V, acc);
+  }
+  return acc;
+}
+
+// Digit words and scales of chunk c of activation row `row` (K columns).
+__device__ __forceinline__ void load_digits(const uint32_t *__restrict__ q, const float *__restrict__ qs, int row, int K,
+                                            int c, uint32_t (&dg)[kDigitWords], float (&xs)[2]) {
+  const uint4 *src = (const uint4 *)(q + ((size_t)row * (K / kChunk) + c) * kDigitWords);
+#pragma unroll
+  for (int i = 0; i < kDigitWords / 4; ++i) {
+    const uint4 v = src[i];
+    dg[4 * i] = v.x;
+    dg[4 * i + 1] = v.y;
+    dg[4 * i + 2] = v.z;
+    dg[4 * i + 3] = v.w;
+  }
+  const float2 sv = *(const float2 *)(qs + (size_t)row * (K / 16) + 2 * c);
+  xs[0] = sv.x;
+  xs[1] = sv.y;
+}
+
+__device__ __forceinline__ void fxp_step(const uint4 (&W)[kTileRows], const uint4 &S, const uint32_t *__restrict__ q,
+                                         const float *__restrict__ qs, int row, int K, int c,
+                                         float (&acc)[kTileRows]) {
+  uint32_t dg[kDigitWords];
+  float xs[2];
+  load_digits(q, qs, row, K, c, dg, xs);
+#pragma unroll
+  for (int r = 0; r < kTileRows; ++r) acc[r] = fxp_chunk(W[r], dg, xs, tile_scale(S, r), acc[r]);
+}
+
+// Encodes T rows of x (K columns each) for the gate/up kernel; one lane per
+// 16-column group.
+__device__ __forceinline__ void xquant_group(const float *__restrict__ x, int K, int g, uint32_t *__restrict__ q,
+                                             float *__restrict__ qs) {
+  const int gpr = K / 16;
+  const int t = g / gpr, gi = g - t * gpr;
+  float v[16];
+  const float4 *src = (const float4 *)(x + (size_t)t * K + (size_t)gi * 16);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float4 f = src[i];
+    v[4 * i] = f.x;
+    v[4 * i + 1] = f.y;
+    v[4 * i + 2] = f.z;
+    v[4 * i + 3] = f.w;
+  }
+  uint32_t words[12];
+  float scale;
+  quant16(v, words, scale);
+  uint4 *dst = (uint4 *)(q + ((size_t)t * (K / kChunk) + (gi >> 1)) * kDigitWords + (gi & 1) * 12);
+  dst[0] = make_uint4(words[0], words[1], words[2], words[3]);
+  dst[1] = make_uint4(words[4], words[5], words[6], words[7]);
+  dst[2] = make_uint4(words[8], words[9], words[10], words[11]);
+  qs[(size_t)t * gpr + gi] = scale;
+}
+
+__global__ __launch_bounds__(256) void k_xquant(const float *__restrict__ x, int T, int K, uint32_t *__restrict__ q,
+                                                float *__restrict__ qs) {
+  const int groups = T * (K / 16);
+  for (int g = blockIdx.x * 256 + threadIdx.x; g < groups; g += gridDim.x * 256) xquant_group(x, K, g, q, qs);
+}
+
+// Gate/up on the fixed-point path.  A block of 4 waves owns 16 consecutive
+// h rows of one slot (4 tiles of 4 gate + 4 up rows); each wave runs all
+// chunk steps of its tile for up to MT tokens, then the block encodes its 16
+// h values per token for the down kernel (one 16-column group) and also
+// writes h in fp32.
+template <int MT>
+__global__ __launch_bounds__(256) void k_gateup_fxp(LayerDev L, Dims D, const uint32_t *__restrict__ xq,
+                                                    const float *__restrict__ xs, UnionDev U, float *__restrict__ h,
+                                                    uint32_t *__restrict__ hq, float *__restrict__ hs,
+                                                    float *__restrict__ gdbg, float *__restrict__ udbg) {
+  __shared__ float hv[MT][16];
+  __shared__ uint32_t hw[MT][12];
+  __shared__ float hsc[MT];
+  __shared__ int orow_s[MT];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int C = D.d / kChunk, quads = D.f / 16;
+  const int nsteps = (C + 63) / 64;
+  const int nu = clamp_nu(U.n_unique, D);
+  const int items = (nu + D.n_shared) * quads;
+  const ExpertLayout EL = expert_layout(D.d, D.f);
+  for (int item = blockIdx.x; item < items; item += gridDim.x) {
+    const int s = item / quads, qd = item - s * quads;
+    const int ti = qd * 4 + wave;
+    int e, p0, p1;
+    if (!resolve_slot(D, U, nu, s, e, p0, p1)) continue;
+    const uint8_t *base = L.experts + (size_t)e * L.expert_stride;
+    for (int pg = p0; pg < p1; pg += MT) {
+      const int mcount = min(MT, p1 - pg);
+      int trow[MT];
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        int t = 0, orow = -1;
+        if (m < mcount) slot_token(D, U, nu, s, pg + m, t, orow);
+        trow[m] = t;
+        if (threadIdx.x == 0) orow_s[m] = orow;
+      }
+      float acc[MT][kTileRows];
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int r = 0; r < kTileRows; ++r) acc[m][r] = 0.0f;
+      for (int j = 0; j < nsteps; ++j) {
+        const int c = lane + 64 * j;
+        if (c < C) {
+          uint4 W[kTileRows], S;
+          load_step(base + EL.gu_nib, base + EL.gu_sc, ti, D.d, c, W, S);
+#pragma unroll
+          for (int m = 0; m < MT; ++m)
+            if (m < mcount) fxp_step(W, S, xq, xs, trow[m], D.d, c, acc[m]);
+        }
+      }
+      if ((int)threadIdx.x < MT * 12) hw[threadIdx.x / 12][threadIdx.x % 12] = 0u;
+      __syncthreads();
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+        if (m < mcount) {
+          const float v = reduce8_rows(acc[m]);
+          const float u = bits_f(xor32(f_bits(v)));  // up rows sit 32 lanes above their gate rows
+          const int r = lane >> 3;
+          if ((lane & 7) == 7 && r < 4) {
+            const float hval = silu_f(v) * u;
+            hv[m][wave * 4 + r] = hval;
+            const int orow = orow_s[m];
+            if (orow >= 0) {
+              const size_t o = (size_t)orow * D.f + (size_t)ti * 4 + r;
+              h[o] = hval;
+              if (gdbg) {
+                gdbg[o] = v;
+                udbg[o] = u;
+              }
+            }
+          }
+        }
+      __syncthreads();
+      // encode the block's 16 h values of each token: one 16-lane row per token
+      {
+        const int m = threadIdx.x >> 4, i = threadIdx.x & 15;
+        const float v = (m < mcount) ? hv[m][i] : 0.0f;
+        uint32_t mb = f_bits(fabsf(v));
+        mb = max(mb, dpp<kRowRor8>(mb));
+        mb = max(mb, dpp<kRowRor4>(mb));
+        mb = max(mb, dpp<kRowRor2>(mb));
+        mb = max(mb, dpp<kRowRor1>(mb));
+        const float mx = bits_f(mb);
+        int E = mx > 0.0f ? ilogbf(mx) + 1 : 0;
+        E = E < -100 ? -100 : E;
+        if (m < mcount) {
+          const uint32_t B = (uint32_t)((int)__builtin_rintf(v * ldexpf(1.0f, 22 - E)) + 0x888888);
+#pragma unroll
+          for (int k = 0; k < 6; ++k) atomicOr(&hw[m][2 * k + (i >> 3)], (((B >> (4 * k)) & 15u) ^ 8u) << (4 * (i & 7)));
+          if (i == 0) hsc[m] = ldexpf(1.0f, E - 22);
+        }
+      }
+      __syncthreads();
+      if ((int)threadIdx.x < mcount * 12) {
+        const int m = threadIdx.x / 12, wd = threadIdx.x % 12;
+        const int orow = orow_s[m];
+        if (orow >= 0) {
+          hq[((size_t)orow * (D.f / kChunk) + (qd >> 1)) * kDigitWords + (qd & 1) * 12 + wd] = hw[m][wd];
+          if (wd == 0) hs[(size_t)orow * (D.f / 16) + qd] = hsc[m];
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// Down projection on the fixed-point path, combine fused as in k_down_wide.
+template <int MT, bool FUSED, int NWMAX>
+__global__ __launch_bounds__(64 * NWMAX) void k_down_fxp(LayerDev L, Dims D, const uint32_t *__restrict__ hq,
+                                                         const float *__restrict__ hs, UnionDev U,
+                                                         float *__restrict__ y, const float *__restrict__ w,
+                                                         float *__restrict__ residual) {
+  extern __shared__ float ylds[];  // [T*k + T*n_shared][8] when FUSED
+  const int nw = blockDim.x >> 6, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int C = D.f / kChunk, tiles = D.d / kTileRows;
+  const int nu = clamp_nu(U.n_unique, D);
+  const int slots = nu + D.n_shared;
+  const int tk = D.T * D.k;
+  const ExpertLayout EL = expert_layout(D.d, D.f);
+  for (int ti = blockIdx.x; ti < tiles; ti += gridDim.x) {
+    for (int s = wave; s < slots; s += nw) {
+      int e, p0, p1;
+      if (!resolve_slot(D, U, nu, s, e, p0, p1)) continue;
+      const uint8_t *base = L.experts + (size_t)e * L.expert_stride;
+      for (int pg = p0; pg < p1; pg += MT) {
+        const int mcount = min(MT, p1 - pg);
+        float acc[MT][kTileRows];
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+          for (int r = 0; r < kTileRows; ++r) acc[m][r] = 0.0f;
+        for (int c = lane; c < ((C + 63) & ~63); c += 64) {
+          if (c < C) {
+            uint4 W[kTileRows], S;
+            load_step(base + EL.dn_nib, base + EL.dn_sc, ti, D.f, c, W, S);
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+              if (m < mcount) fxp_step(W, S, hq, hs, (s < nu) ? pg + m : tk + pg + m, D.f, c, acc[m]);
+          }
+        }
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+          if (m < mcount) {
+            const float v = reduce8_rows(acc[m]);
+            if ((lane & 7) == 7) {
+              const int orow = (s < nu) ? pg + m : tk + pg + m;
+              if (FUSED)
+                ylds[(size_t)orow * kTileRows + (lane >> 3)] = v;
+              else
+                y[(size_t)orow * D.d + (size_t)ti * kTileRows + (lane >> 3)] = v;
+            }
+          }
+      }
+    }
+    if (FUSED) {
+      __syncthreads();
+      combine_tile(D, U, nu, w, ylds, residual, ti);
+      __syncthreads();
+    }
+  }
+}
+
+// ------------------------------------------------------ decode (T == 1) path
+// One token: every slot holds exactly one pair (pair index = slot for the
+// routed experts, T*k for the shared one).  The kernels below keep each wave
+// streaming with the next step's loads in flight while it computes the
+// current one; per row they perform exactly the operations of the general
+// fixed-point kernels above (same chunk order, same reduction trees, same
+// combine order), so their results are bit-identical to them.
+
+// Router with the d columns split over the 4 waves of a block, one block per
+// expert row; the 4 partial sums are added in wave order.
+__global__ __launch_bounds__(256) void k_router_split(LayerDev L, Dims D, const float *__restrict__ x,
+                                                      float *__restrict__ logits, uint32_t *__restrict__ xq,
+                                                      float *__restrict__ xs) {
+  __shared__ float part[16][4];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int e = blockIdx.x;
+  if (xq) {  // fixed-point encoding of x for the gate/up kernel, spread over the blocks
+    const int groups = D.T * (D.d / 16);
+    for (int g = blockIdx.x * 256 + threadIdx.x; g < groups; g += gridDim.x * 256) xquant_group(x, D.d, g, xq, xs);
+  }
+  const int q4 = D.d / 4;  // columns per wave (d is a multiple of 64)
+  const float *row = L.router + (size_t)e * D.d + (size_t)wave * q4;
+  for (int t = 0; t < D.T; ++t) {
+    const float *xr = x + (size_t)t * D.d + (size_t)wave * q4;
+    float acc = 0.0f;
+    for (int c = 4 * lane; c < q4; c += 256) {
+      const float4 r = *(const float4 *)(row + c);
+      const float4 xv = *(const float4 *)(xr + c);
+      acc = __builtin_fmaf(r.x, xv.x, acc);
+      acc = __builtin_fmaf(r.y, xv.y, acc);
+      acc = __builtin_fmaf(r.z, xv.z, acc);
+      acc = __builtin_fmaf(r.w, xv.w, acc);
+    }
+    acc = wave_sum(acc);
+    if (lane == 0) part[t & 15][wave] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) logits[(size_t)t * D.E + e] = ((part[t & 15][0] + part[t & 15][1]) + part[t & 15][2]) +
+                                                         part[t & 15][3] + L.bias[e];
+    __syncthreads();
+  }
+}
+
+// Top-k of one token plus its union lists (its ids sorted ascending).
+template <int PER>
+__global__ __launch_bounds__(64) void k_topk_union1(const float *__restrict__ logits, Dims D,
+                                                    int32_t *__restrict__ idx, float *__restrict__ wout, UnionDev U,
+                                                    int with_union) {
+  __shared__ int32_t ids[16];
+  topk_token<PER>(logits, D, 0, idx, wout, ids);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  const int j = threadIdx.x;
+  if (with_union && j < D.k) {
+    const int e = ids[j];
+    int rank = 0;
+    for (int i = 0; i < D.k; ++i) rank += ids[i] < e;
+    U.ids[rank] = e;
+    U.offsets[rank] = rank;
+    U.pair_token[rank] = 0;
+    U.pair_slot[rank] = j;
+    U.pair_of[j] = rank;
+    if (j == 0) {
+      *U.n_unique = D.k;
+      U.offsets[D.k] = D.k;
+    }
+  }
+}
+
+// Weights and activation digits of one (slot, step) of the down projection,
+// for the decode stream below.
+__device__ __forceinline__ void dec_down_slot(const LayerDev &L, const Dims &D, const UnionDev &U, int nu,
+                                              const ExpertLayout &EL, int s, int ti, int c, uint4 (&W)[kTileRows],
+                                              uint4 &S, uint32_t (&dg)[kDigitWords], float (&dsc)[2],
+                                              const uint32_t *__restrict__ hq, const float *__restrict__ hs) {
+  int e, p0, p1;
+  if (!resolve_slot(D, U, nu, s, e, p0, p1)) e = -1;
+  if (e < 0 || p1 <= p0 || c >= D.f / kChunk) return;
+  const uint8_t *base = L.experts + (size_t)e * L.expert_stride;
+  load_step(base + EL.dn_nib, base + EL.dn_sc, ti, D.f, c, W, S);
+  load_digits(hq, hs, s < nu ? p0 : D.T * D.k, D.f, c, dg, dsc);
+}
+
+// Down + combine, T == 1, one wave per 8-row output tile: the wave streams
+// every slot's steps (next step's weights and digits in flight) and folds
+// each slot's y into the residual in registers, routed experts in ascending
+// id (slot order) weighted by w, then the shared expert.
+template <int NSTEPS>
+__global__ __launch_bounds__(256) void k_down_wave(LayerDev L, Dims D, const uint32_t *__restrict__ hq,
+                                                   const float *__restrict__ hs, UnionDev U,
+                                                   const float *__restrict__ w, float *__restrict__ residual) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int tiles = D.d / kTileRows, C = D.f / kChunk;
+  const int nu = clamp_nu(U.n_unique, D);
+  const int slots = nu + D.n_shared;
+  const ExpertLayout EL = expert_layout(D.d, D.f);
+  const int nst = slots * NSTEPS;
+  const int wpb = blockDim.x >> 6;
+  for (int ti = blockIdx.x * wpb + wave; ti < tiles; ti += gridDim.x * wpb) {
+    const int r = lane >> 3;
+    float out = residual[(size_t)ti * kTileRows + r];
+    uint4 W[2][kTileRows], S[2];
+    uint32_t dg[2][kDigitWords];
+    float dsc[2][2];
+    float acc[kTileRows];
+#pragma unroll
+    for (int rr = 0; rr < kTileRows; ++rr) acc[rr] = 0.0f;
+    if (nst > 0) dec_down_slot(L, D, U, nu, EL, 0, ti, lane, W[0], S[0], dg[0], dsc[0], hq, hs);
+    for (int q0 = 0; q0 < nst; q0 += 2) {
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int q = q0 + half;
+        if (q < nst) {
+          if (q + 1 < nst)
+            dec_down_slot(L, D, U, nu, EL, (q + 1) / NSTEPS, ti, lane + 64 * ((q + 1) % NSTEPS), W[half ^ 1],
+                          S[half ^ 1], dg[half ^ 1], dsc[half ^ 1], hq, hs);
+          const int s = q / NSTEPS, j = q % NSTEPS;
+          const int c = lane + 64 * j;
+          int e, p0, p1;
+          const bool ok = resolve_slot(D, U, nu, s, e, p0, p1) && p1 > p0;
+          if (ok && c < C) {
+#pragma unroll
+            for (int rr = 0; rr < kTileRows; ++rr)
+              acc[rr] = fxp_chunk(W[half][rr], dg[half], dsc[half], tile_scale(S[half], rr), acc[rr]);
+          }
+          if (j == NSTEPS - 1) {
+            const float v = reduce8_rows(acc);
+            if (ok) {
+              if (s < nu)
+                out = __builtin_fmaf(w[U.pair_slot[p0]], v, out);
+              else
+                out = out + v;
+            }
+#pragma unroll
+            for (int rr = 0; rr < kTileRows; ++rr) acc[rr] = 0.0f;
+          }
+        }
+      }
+    }
+    if ((lane & 7) == 7) residual[(size_t)ti * kTileRows + r] = out;
+  }
+}
+
+// ------------------------------------------------- narrow shapes (K < 2048)
+// Rows shorter than 64 chunks: LPR lanes per row (a power of two >= K/32),
+// 64/LPR rows side by side in a wave, one wave per (slot, 8-row tile).  Same
+// arithmetic per chunk; reductions by a fixed butterfly within LPR lanes.
+
+template <int LPR>
+struct NarrowShape {
+  static constexpr int RG = 64 / LPR;                    // row groups per wave
+  static constexpr int RPG = (kTileRows + RG - 1) / RG;  // rows per lane
+};
+
+template <int LPR, int MT>
+__device__ __forceinline__ void narrow_tile(const uint8_t *__restrict__ nib, const uint8_t *__restrict__ sc, int tile,
+                                            int K, const float *__restrict__ xbase, size_t xstride,
+                                            const int (&xrow)[MT], int mcount,
+                                            float (&acc)[MT][NarrowShape<LPR>::RPG]) {
+  using NS = NarrowShape<LPR>;
+  const int lane = threadIdx.x & 63;
+  const int q = lane % LPR, gr = lane / LPR;
+  const int C = K / kChunk, G = K / kGroup;
 #pragma unroll
   for (int m = 0; m < MT; ++m)
 #pragma unroll
-    for (int i = 0; i < TS::RPG; ++i) acc[m][i] = 0.0f;
+    for (int i = 0; i < NS::RPG; ++i) acc[m][i] = 0.0f;
+  if (q >= C) return;
+  const uint4 S = *(const uint4 *)(sc + ((size_t)tile * G + (q >> 1)) * 16);
 #pragma unroll
-  for (int j = 0; j < CPL; ++j) {
-    const int c = q + LPR * j;
-    if (c < C) {
-      uint4 W[TS::RPG], S;
-      load_chunk<LPR>(nib, sc, tile, K, c, W, S);
+  for (int i = 0; i < NS::RPG; ++i) {
+    const int r = gr + NS::RG * i;
+    if (r < kTileRows) {
+      const uint4 Wr = *(const uint4 *)(nib + chunk_offset(tile, K, q, r));
 #pragma unroll
       for (int m = 0; m < MT; ++m)
-        if (m < mcount) chunk_accumulate<LPR>(W, S, xbase + (size_t)xrow[m] * xstride, c, acc[m]);
+        if (m < mcount) {
+          float4 xv[8];
+          const float4 *src = (const float4 *)(xbase + (size_t)xrow[m] * xstride + (size_t)kChunk * q);
+#pragma unroll
+          for (int v = 0; v < 8; ++v) xv[v] = src[v];
+          acc[m][i] = __builtin_fmaf(tile_scale(S, r), chunk_dot(Wr, xv, neg8_sum(xv)), acc[m][i]);
+        }
     }
   }
 }
 
-// Token p of slot s: its activation row and output row.
-__device__ __forceinline__ void slot_token(const Dims &D, const UnionDev &U, int nu, int s, int p, int &t, int &orow) {
-  if (s < nu) {
-    t = U.pair_token[p];
-    orow = p;
-  } else {
-    t = p;
-    orow = D.T * D.k + p;
+template <int LPR>
+__device__ __forceinline__ void narrow_reduce(const float *acc, float *rows) {
+  using NS = NarrowShape<LPR>;
+  const int lane = threadIdx.x & 63;
+  const int q = lane % LPR, gr = lane / LPR;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+  for (int i = 0; i < NS::RPG; ++i) {
+    const float v = group_sum(acc[i], LPR);
+    const int r = gr + NS::RG * i;
+    if (q == 0 && r < kTileRows) rows[r] = v;
   }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Gate/up for every (unique expert, tile of 4 gate + 4 up rows) item, applied
-// to each of the expert's tokens: h = SiLU(g) * u, written per pair.  Slot nu
-// (after the routed experts) is the shared expert with all T tokens ([D] §3).
-template <int LPR, int CPL, int MT>
-__global__ __launch_bounds__(256) void k_gateup(LayerDev L, Dims D, const float *__restrict__ x, UnionDev U,
-                                                float *__restrict__ h, float *__restrict__ gdbg,
-                                                float *__restrict__ udbg) {
-  using TS = TileShape<LPR>;
+template <int LPR, int MT>
+__global__ __launch_bounds__(256) void k_gateup_narrow(LayerDev L, Dims D, const float *__restrict__ x, UnionDev U,
+                                                       float *__restrict__ h, float *__restrict__ gdbg,
+                                                       float *__restrict__ udbg) {
+  using NS = NarrowShape<LPR>;
   __shared__ float rows_lds[4][kTileRows];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int tiles = D.f / 4;
@@ -577,36 +1161,18 @@ __global__ __launch_bounds__(256) void k_gateup(LayerDev L, Dims D, const float 
       for (int m = 0; m < MT; ++m) {
         int t = 0, orow = -1;
         if (m < mcount) slot_token(D, U, nu, s, pg + m, t, orow);
-        if (t < 0 || t >= D.T) {
-          t = 0;
-          orow = -1;
-        }
         xrow[m] = t;
         orows[m] = orow;
       }
-      float acc[MT][TS::RPG];
-      tile_pass<LPR, CPL, MT>(base + EL.gu_nib, base + EL.gu_sc, ti, D.d, x, (size_t)D.d, xrow, mcount, acc);
+      float acc[MT][NS::RPG];
+      narrow_tile<LPR, MT>(base + EL.gu_nib, base + EL.gu_sc, ti, D.d, x, (size_t)D.d, xrow, mcount, acc);
 #pragma unroll
-      for (int m = 0; m < MT; ++m) {
+      for (int m = 0; m < MT; ++m)
         if (m < mcount) {
-          const float v = tile_reduce<LPR>(acc[m], rows_lds[wave]);
-          float g, u;
-          int r;
-          bool writer;
-          if constexpr (LPR == 64) {
-            auto sw = __builtin_amdgcn_permlane32_swap(f_bits(v), f_bits(v), false, false);
-            u = bits_f(sw[1]);  // lanes < 32 receive lane + 32
-            g = v;
-            r = lane >> 3;
-            writer = (lane & 7) == 7 && r < 4;
-          } else {
-            r = lane & 3;
-            writer = lane < 4;
-            g = rows_lds[wave][r];
-            u = rows_lds[wave][r + 4];
-          }
-          if (writer && orows[m] >= 0) {
-            const size_t o = (size_t)orows[m] * D.f + (size_t)ti * 4 + r;
+          narrow_reduce<LPR>(acc[m], rows_lds[wave]);
+          if (lane < 4 && orows[m] >= 0) {
+            const float g = rows_lds[wave][lane], u = rows_lds[wave][lane + 4];
+            const size_t o = (size_t)orows[m] * D.f + (size_t)ti * 4 + lane;
             h[o] = silu_f(g) * u;
             if (gdbg) {
               gdbg[o] = g;
@@ -614,17 +1180,14 @@ __global__ __launch_bounds__(256) void k_gateup(LayerDev L, Dims D, const float 
             }
           }
         }
-      }
     }
   }
 }
 
-// Down projection y = Wd h for every (unique expert, 8-row tile) item and
-// each of the expert's tokens, written per pair (shared: row T*k + t).
-template <int LPR, int CPL, int MT>
-__global__ __launch_bounds__(256) void k_down(LayerDev L, Dims D, const float *__restrict__ h, UnionDev U,
-                                              float *__restrict__ y) {
-  using TS = TileShape<LPR>;
+template <int LPR, int MT>
+__global__ __launch_bounds__(256) void k_down_narrow(LayerDev L, Dims D, const float *__restrict__ h, UnionDev U,
+                                                     float *__restrict__ y) {
+  using NS = NarrowShape<LPR>;
   __shared__ float rows_lds[4][kTileRows];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int tiles = D.d / kTileRows;
@@ -641,110 +1204,24 @@ __global__ __launch_bounds__(256) void k_down(LayerDev L, Dims D, const float *_
       int orows[MT];
 #pragma unroll
       for (int m = 0; m < MT; ++m) orows[m] = m < mcount ? ((s < nu) ? pg + m : D.T * D.k + pg + m) : 0;
-      float acc[MT][TS::RPG];
-      tile_pass<LPR, CPL, MT>(base + EL.dn_nib, base + EL.dn_sc, ti, D.f, h, (size_t)D.f, orows, mcount, acc);
+      float acc[MT][NS::RPG];
+      narrow_tile<LPR, MT>(base + EL.dn_nib, base + EL.dn_sc, ti, D.f, h, (size_t)D.f, orows, mcount, acc);
 #pragma unroll
-      for (int m = 0; m < MT; ++m) {
+      for (int m = 0; m < MT; ++m)
         if (m < mcount) {
-          float v = tile_reduce<LPR>(acc[m], rows_lds[wave]);
-          int r;
-          bool writer;
-          if constexpr (LPR == 64) {
-            r = lane >> 3;
-            writer = (lane & 7) == 7;
-          } else {
-            r = lane & 7;
-            writer = lane < kTileRows;
-            v = rows_lds[wave][r];
-          }
-          if (writer) y[(size_t)orows[m] * D.d + (size_t)ti * kTileRows + r] = v;
+          narrow_reduce<LPR>(acc[m], rows_lds[wave]);
+          if (lane < kTileRows) y[(size_t)orows[m] * D.d + (size_t)ti * kTileRows + lane] = rows_lds[wave][lane];
         }
-      }
     }
   }
-}
-
-struct GemvGrid {
-  dim3 grid, block;
-};
-
-static GemvGrid gemv_grid(int items_max) {
-  int blocks = (items_max + 3) / 4;
-  if (blocks > 8192) blocks = 8192;
-  if (blocks < 1) blocks = 1;
-  return {dim3(blocks), dim3(256)};
-}
-
-// Lane shape from K (the matrix's input length): 64 lanes per row with CPL
-// chunks each when K >= 2048, else one chunk per lane and 64/LPR rows side
-// by side.  MT: tokens per pass, 1 when no expert can have more than one
-// token (T == 1), else 16.
-#define GEMV_LAUNCH(KERNEL, LPR_, CPL_, ...)                                             \
-  do {                                                                                   \
-    if (mt1)                                                                             \
-      KERNEL<LPR_, CPL_, 1><<<G.grid, G.block, 0, s>>>(__VA_ARGS__);                     \
-    else                                                                                 \
-      KERNEL<LPR_, CPL_, 16><<<G.grid, G.block, 0, s>>>(__VA_ARGS__);                    \
-  } while (0)
-
-#define GEMV_DISPATCH(KERNEL, K, ...)                                          \
-  do {                                                                         \
-    const int C_ = (K) / kChunk;                                               \
-    if (C_ >= 64) {                                                            \
-      switch ((C_ + 63) / 64) {                                                \
-        case 1: GEMV_LAUNCH(KERNEL, 64, 1, __VA_ARGS__); break;                \
-        case 2: GEMV_LAUNCH(KERNEL, 64, 2, __VA_ARGS__); break;                \
-        case 3: GEMV_LAUNCH(KERNEL, 64, 3, __VA_ARGS__); break;                \
-        case 4: GEMV_LAUNCH(KERNEL, 64, 4, __VA_ARGS__); break;                \
-        case 5: GEMV_LAUNCH(KERNEL, 64, 5, __VA_ARGS__); break;                \
-        case 6: GEMV_LAUNCH(KERNEL, 64, 6, __VA_ARGS__); break;                \
-        case 7: GEMV_LAUNCH(KERNEL, 64, 7, __VA_ARGS__); break;                \
-        case 8: GEMV_LAUNCH(KERNEL, 64, 8, __VA_ARGS__); break;                \
-        default: return hipErrorInvalidValue;                                  \
-      }                                                                        \
-    } else if (C_ > 16) {                                                      \
-      GEMV_LAUNCH(KERNEL, 32, 1, __VA_ARGS__);                                 \
-    } else if (C_ > 8) {                                                       \
-      GEMV_LAUNCH(KERNEL, 16, 1, __VA_ARGS__);                                 \
-    } else if (C_ > 4) {                                                       \
-      GEMV_LAUNCH(KERNEL, 8, 1, __VA_ARGS__);                                  \
-    } else if (C_ > 2) {                                                       \
-      GEMV_LAUNCH(KERNEL, 4, 1, __VA_ARGS__);                                  \
-    } else {                                                                   \
-      GEMV_LAUNCH(KERNEL, 2, 1, __VA_ARGS__);                                  \
-    }                                                                          \
-  } while (0)
-
-static int slots_max(const Dims &D) {
-  long long tk = (long long)D.T * D.k;
-  return (int)(tk < D.E ? tk : D.E) + D.n_shared;
-}
-
-hipError_t launch_gateup(const LayerDev &L, const Dims &D, const float *x, const UnionDev &U, float *h,
-                         hipStream_t s) {
-  if (D.T <= 0) return hipSuccess;
-  const bool mt1 = D.T == 1;
-  GemvGrid G = gemv_grid(slots_max(D) * (D.f / 4));
-  GEMV_DISPATCH(k_gateup, D.d, L, D, x, U, h, nullptr, nullptr);
-  return hipGetLastError();
-}
-
-hipError_t launch_down(const LayerDev &L, const Dims &D, const float *h, const UnionDev &U, float *y,
-                       hipStream_t s) {
-  if (D.T <= 0) return hipSuccess;
-  const bool mt1 = D.T == 1;
-  GemvGrid G = gemv_grid(slots_max(D) * (D.d / kTileRows));
-  GEMV_DISPATCH(k_down, D.f, L, D, h, U, y);
-  return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ combine
 // A7: r[t] += sum over the token's experts in ascending id of w * y, then the
 // shared expert's y (weight 1).  Fixed order, no atomics: a token's result
-// is the same whether it runs alone or batched.
+// is the same whether it runs alone or batched, fused or not.
 
-__global__ __launch_bounds__(256) void k_combine(Dims D, const int32_t *__restrict__ idx,
-                                                 const float *__restrict__ w, UnionDev U,
+__global__ __launch_bounds__(256) void k_combine(Dims D, const float *__restrict__ w, UnionDev U,
                                                  const float *__restrict__ y, float *__restrict__ residual) {
   const int t = blockIdx.y;
   const int r = blockIdx.x * 256 + threadIdx.x;
@@ -774,16 +1251,8 @@ __global__ __launch_bounds__(256) void k_combine(Dims D, const int32_t *__restri
       }
     }
   }
-  if (D.n_shared) acc = acc + y[((size_t)D.T * D.k + t) * D.d + r];
+  if (D.n_shared) acc = acc + y[((size_t)tk + t) * D.d + r];
   residual[(size_t)t * D.d + r] = acc;
-}
-
-hipError_t launch_combine(const Dims &D, const int32_t *idx, const float *w, const UnionDev &U, const float *y,
-                          float *residual, hipStream_t s) {
-  if (D.T <= 0) return hipSuccess;
-  dim3 grid((D.d + 255) / 256, D.T), block(256);
-  k_combine<<<grid, block, 0, s>>>(D, idx, w, U, y, residual);
-  return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ rmsnorm
@@ -797,7 +1266,7 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float *__restrict__ r, in
   const float *rr = r + (size_t)t * d;
   float acc = 0.0f;
   for (int c = threadIdx.x; c < d; c += 256) acc = __builtin_fmaf(rr[c], rr[c], acc);
-  acc = group_sum(acc, 64);
+  acc = wave_sum(acc);
   if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
   __syncthreads();
   const float ss = (part[0] + part[1]) + (part[2] + part[3]);
@@ -805,21 +1274,275 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float *__restrict__ r, in
   for (int c = threadIdx.x; c < d; c += 256) x[(size_t)t * d + c] = rr[c] * inv;
 }
 
-hipError_t launch_rmsnorm(const float *r, int T, int d, float eps, float *x, hipStream_t s) {
-  if (T <= 0) return hipSuccess;
-  k_rmsnorm<<<T, 256, 0, s>>>(r, d, eps, x);
+// ---------------------------------------------------------------- launchers
+
+static int slots_max(const Dims &D) {
+  const long long tk = (long long)D.T * D.k;
+  return (int)(tk < D.E ? tk : D.E) + D.n_shared;
+}
+
+static int topk_per(int E) {
+  const int per = (E + 63) / 64;
+  return per <= 1 ? 1 : per <= 2 ? 2 : per <= 4 ? 4 : per <= 8 ? 8 : 16;
+}
+
+static bool steps_supported(int steps) {
+  return steps == 1 || steps == 2 || steps == 3 || steps == 4 || steps == 6 || steps == 8 || steps == 12 ||
+         steps == 16 || steps == 24 || steps == 32;
+}
+
+template <int S>
+static void router_gemv_launch(dim3 g, dim3 b, hipStream_t s, const LayerDev &L, const Dims &D, const float *x,
+                               float *logits) {
+  k_router_gemv<S><<<g, b, 0, s>>>(L, D, x, logits);
+}
+
+hipError_t launch_router_split(const LayerDev &L, const Dims &D, const float *x, float *logits, uint32_t *xq,
+                               float *xs, hipStream_t s) {
+  if (D.T <= 0) return hipSuccess;
+  k_router_split<<<D.E, 256, 0, s>>>(L, D, x, logits, xq, xs);
   return hipGetLastError();
 }
 
-// --------------------------------------------------------------- debug path
-// One expert, one token, through the same kernels (a one-slot union that the
-// caller wrote into the workspace).
+hipError_t launch_topk_union1(const float *logits, const Dims &D, int32_t *idx, float *w, const UnionDev *U,
+                              hipStream_t s) {
+  const UnionDev u = U ? *U : UnionDev{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
+  switch (topk_per(D.E)) {
+    case 1: k_topk_union1<1><<<1, 64, 0, s>>>(logits, D, idx, w, u, U ? 1 : 0); break;
+    case 2: k_topk_union1<2><<<1, 64, 0, s>>>(logits, D, idx, w, u, U ? 1 : 0); break;
+    case 4: k_topk_union1<4><<<1, 64, 0, s>>>(logits, D, idx, w, u, U ? 1 : 0); break;
+    case 8: k_topk_union1<8><<<1, 64, 0, s>>>(logits, D, idx, w, u, U ? 1 : 0); break;
+    default: k_topk_union1<16><<<1, 64, 0, s>>>(logits, D, idx, w, u, U ? 1 : 0); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_router(const LayerDev &L, const Dims &D, const float *x, float *logits, hipStream_t s) {
+  if (D.T <= 0) return hipSuccess;
+  const int steps = (D.d + 255) / 256;
+  if (D.T <= 32 && steps_supported(steps)) {
+    dim3 g((D.E + 3) / 4), b(256);
+    switch (steps) {
+      case 1: router_gemv_launch<1>(g, b, s, L, D, x, logits); break;
+      case 2: router_gemv_launch<2>(g, b, s, L, D, x, logits); break;
+      case 3: router_gemv_launch<3>(g, b, s, L, D, x, logits); break;
+      case 4: router_gemv_launch<4>(g, b, s, L, D, x, logits); break;
+      case 6: router_gemv_launch<6>(g, b, s, L, D, x, logits); break;
+      case 8: router_gemv_launch<8>(g, b, s, L, D, x, logits); break;
+      case 12: router_gemv_launch<12>(g, b, s, L, D, x, logits); break;
+      case 16: router_gemv_launch<16>(g, b, s, L, D, x, logits); break;
+      case 24: router_gemv_launch<24>(g, b, s, L, D, x, logits); break;
+      default: router_gemv_launch<32>(g, b, s, L, D, x, logits); break;
+    }
+    return hipGetLastError();
+  }
+  dim3 g((D.T + 63) / 64, (D.E + 63) / 64), b(256);
+  k_router_gemm<<<g, b, 0, s>>>(L, D, x, logits);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk(const float *logits, const Dims &D, int32_t *idx, float *w, hipStream_t s) {
+  if (D.T <= 0) return hipSuccess;
+  dim3 g((D.T + 3) / 4), b(256);
+  switch (topk_per(D.E)) {
+    case 1: k_topk<1><<<g, b, 0, s>>>(logits, D, idx, w); break;
+    case 2: k_topk<2><<<g, b, 0, s>>>(logits, D, idx, w); break;
+    case 4: k_topk<4><<<g, b, 0, s>>>(logits, D, idx, w); break;
+    case 8: k_topk<8><<<g, b, 0, s>>>(logits, D, idx, w); break;
+    default: k_topk<16><<<g, b, 0, s>>>(logits, D, idx, w); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_union(const int32_t *idx, const Dims &D, const UnionDev &U, int32_t *err, hipStream_t s) {
+  k_union<<<1, 64, union_lds_bytes(D.E), s>>>(idx, D, U, err);
+  return hipGetLastError();
+}
+
+static bool wide(int K) { return K / kChunk >= 64; }
+
+static int narrow_lpr(int K) {
+  const int C = K / kChunk;
+  return C > 16 ? 32 : C > 8 ? 16 : C > 4 ? 8 : C > 2 ? 4 : 2;
+}
+
+static int grid_cap(long long blocks, int cap) { return (int)(blocks < 1 ? 1 : blocks > cap ? cap : blocks); }
+
+template <int LPR>
+static void narrow_gateup(bool mt1, int grid, hipStream_t s, const LayerDev &L, const Dims &D, const float *x,
+                          const UnionDev &U, float *h, float *g, float *u) {
+  if (mt1)
+    k_gateup_narrow<LPR, 1><<<grid, 256, 0, s>>>(L, D, x, U, h, g, u);
+  else
+    k_gateup_narrow<LPR, 8><<<grid, 256, 0, s>>>(L, D, x, U, h, g, u);
+}
+
+template <int LPR>
+static void narrow_down(bool mt1, int grid, hipStream_t s, const LayerDev &L, const Dims &D, const float *h,
+                        const UnionDev &U, float *y) {
+  if (mt1)
+    k_down_narrow<LPR, 1><<<grid, 256, 0, s>>>(L, D, h, U, y);
+  else
+    k_down_narrow<LPR, 8><<<grid, 256, 0, s>>>(L, D, h, U, y);
+}
+
+static hipError_t gateup_impl(const LayerDev &L, const Dims &D, const float *x, const UnionDev &U, float *h, float *g,
+                              float *u, hipStream_t s) {
+  const bool mt1 = D.T == 1;
+  const long long items = (long long)slots_max(D) * (D.f / 4);
+  if (wide(D.d)) {
+    const int nw = (D.d / kChunk + 63) / 64;
+    dim3 grid(grid_cap(items, 16384)), block(64 * nw);
+    if (mt1)
+      k_gateup_wide<1><<<grid, block, 0, s>>>(L, D, x, U, h, g, u);
+    else
+      k_gateup_wide<8><<<grid, block, 0, s>>>(L, D, x, U, h, g, u);
+  } else {
+    const int grid = grid_cap((items + 3) / 4, 8192);
+    switch (narrow_lpr(D.d)) {
+      case 32: narrow_gateup<32>(mt1, grid, s, L, D, x, U, h, g, u); break;
+      case 16: narrow_gateup<16>(mt1, grid, s, L, D, x, U, h, g, u); break;
+      case 8: narrow_gateup<8>(mt1, grid, s, L, D, x, U, h, g, u); break;
+      case 4: narrow_gateup<4>(mt1, grid, s, L, D, x, U, h, g, u); break;
+      default: narrow_gateup<2>(mt1, grid, s, L, D, x, U, h, g, u); break;
+    }
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gateup(const LayerDev &L, const Dims &D, const float *x, const UnionDev &U, float *h,
+                         hipStream_t s) {
+  if (D.T <= 0) return hipSuccess;
+  return gateup_impl(L, D, x, U, h, nullptr, nullptr, s);
+}
 
 hipError_t launch_debug_gateup(const LayerDev &L, const Dims &D, const float *x, const UnionDev &U, float *h,
                                float *g, float *u, hipStream_t s) {
-  const bool mt1 = true;
-  GemvGrid G = gemv_grid(D.f / 4);
-  GEMV_DISPATCH(k_gateup, D.d, L, D, x, U, h, g, u);
+  return gateup_impl(L, D, x, U, h, g, u, s);
+}
+
+// Rows of y the fused down kernel keeps in LDS (pairs plus shared rows).
+static size_t fused_rows(const Dims &D) { return (size_t)D.T * D.k + (size_t)D.T * D.n_shared; }
+
+bool down_fusable(const Dims &D) { return wide(D.f) && fused_rows(D) * kTileRows * 4 <= kFusedLdsMax; }
+
+hipError_t launch_down(const LayerDev &L, const Dims &D, const float *h, const UnionDev &U, float *y,
+                       const float *w, float *residual, bool fused, hipStream_t s) {
+  if (D.T <= 0) return hipSuccess;
+  const bool mt1 = D.T == 1;
+  if (wide(D.f)) {
+    const int tiles = D.d / kTileRows;
+    const int nwmax = mt1 ? 9 : 8;  // decode: k = 8 routed + shared slots side by side
+    int nw = slots_max(D);
+    nw = nw < 1 ? 1 : nw > nwmax ? nwmax : nw;
+    dim3 grid(tiles), block(64 * nw);
+    const size_t lds = fused ? fused_rows(D) * kTileRows * 4 : 0;
+    if (fused) {
+      if (mt1)
+        k_down_wide<1, true, 9><<<grid, block, lds, s>>>(L, D, h, U, y, w, residual);
+      else
+        k_down_wide<8, true, 8><<<grid, block, lds, s>>>(L, D, h, U, y, w, residual);
+    } else {
+      if (mt1)
+        k_down_wide<1, false, 9><<<grid, block, 0, s>>>(L, D, h, U, y, w, residual);
+      else
+        k_down_wide<8, false, 8><<<grid, block, 0, s>>>(L, D, h, U, y, w, residual);
+    }
+  } else {
+    const long long items = (long long)slots_max(D) * (D.d / kTileRows);
+    const int grid = grid_cap((items + 3) / 4, 8192);
+    switch (narrow_lpr(D.f)) {
+      case 32: narrow_down<32>(mt1, grid, s, L, D, h, U, y); break;
+      case 16: narrow_down<16>(mt1, grid, s, L, D, h, U, y); break;
+      case 8: narrow_down<8>(mt1, grid, s, L, D, h, U, y); break;
+      case 4: narrow_down<4>(mt1, grid, s, L, D, h, U, y); break;
+      default: narrow_down<2>(mt1, grid, s, L, D, h, U, y); break;
+    }
+  }
+  return hipGetLastError();
+}
+
+bool fxp_supported(const Dims &D) { return wide(D.d) && wide(D.f); }
+
+hipError_t launch_xquant(const float *x, int T, int K, uint32_t *xq, float *xs, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  const long long groups = (long long)T * (K / 16);
+  k_xquant<<<grid_cap((groups + 255) / 256, 4096), 256, 0, s>>>(x, T, K, xq, xs);
+  return hipGetLastError();
+}
+
+static hipError_t gateup_fxp_impl(const LayerDev &L, const Dims &D, const uint32_t *xq, const float *xs,
+                                  const UnionDev &U, float *h, uint32_t *hq, float *hs, float *g, float *u,
+                                  hipStream_t s) {
+  const long long items = (long long)slots_max(D) * (D.f / 16);
+  dim3 grid(grid_cap(items, 16384)), block(256);
+  if (D.T == 1)
+    k_gateup_fxp<1><<<grid, block, 0, s>>>(L, D, xq, xs, U, h, hq, hs, g, u);
+  else
+    k_gateup_fxp<8><<<grid, block, 0, s>>>(L, D, xq, xs, U, h, hq, hs, g, u);
+  return hipGetLastError();
+}
+
+hipError_t launch_gateup_fxp(const LayerDev &L, const Dims &D, const uint32_t *xq, const float *xs,
+                             const UnionDev &U, float *h, uint32_t *hq, float *hs, float *g, float *u,
+                             hipStream_t s) {
+  if (D.T <= 0) return hipSuccess;
+  return gateup_fxp_impl(L, D, xq, xs, U, h, hq, hs, g, u, s);
+}
+
+hipError_t launch_down_fxp(const LayerDev &L, const Dims &D, const uint32_t *hq, const float *hs, const UnionDev &U,
+                           float *y, const float *w, float *residual, bool fused, hipStream_t s) {
+  if (D.T <= 0) return hipSuccess;
+  const bool mt1 = D.T == 1;
+  const int tiles = D.d / kTileRows;
+  const int nwmax = mt1 ? 9 : 8;
+  int nw = slots_max(D);
+  nw = nw < 1 ? 1 : nw > nwmax ? nwmax : nw;
+  dim3 grid(tiles), block(64 * nw);
+  const size_t lds = fused ? fused_rows(D) * kTileRows * 4 : 0;
+  if (fused) {
+    if (mt1)
+      k_down_fxp<1, true, 9><<<grid, block, lds, s>>>(L, D, hq, hs, U, y, w, residual);
+    else
+      k_down_fxp<8, true, 8><<<grid, block, lds, s>>>(L, D, hq, hs, U, y, w, residual);
+  } else {
+    if (mt1)
+      k_down_fxp<1, false, 9><<<grid, block, 0, s>>>(L, D, hq, hs, U, y, w, residual);
+    else
+      k_down_fxp<8, false, 8><<<grid, block, 0, s>>>(L, D, hq, hs, U, y, w, residual);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_down_dec(const LayerDev &L, const Dims &D, const uint32_t *hq, const float *hs, const UnionDev &U,
+                           const float *w, float *residual, hipStream_t s) {
+  if (D.T != 1) return hipErrorInvalidValue;
+  const int nsteps = (D.f / kChunk + 63) / 64;
+  const int tiles = D.d / kTileRows;
+  switch (nsteps) {
+    case 1: k_down_wave<1><<<tiles, 64, 0, s>>>(L, D, hq, hs, U, w, residual); break;
+    case 2: k_down_wave<2><<<tiles, 64, 0, s>>>(L, D, hq, hs, U, w, residual); break;
+    case 3: k_down_wave<3><<<tiles, 64, 0, s>>>(L, D, hq, hs, U, w, residual); break;
+    case 4: k_down_wave<4><<<tiles, 64, 0, s>>>(L, D, hq, hs, U, w, residual); break;
+    case 5: k_down_wave<5><<<tiles, 64, 0, s>>>(L, D, hq, hs, U, w, residual); break;
+    case 6: k_down_wave<6><<<tiles, 64, 0, s>>>(L, D, hq, hs, U, w, residual); break;
+    case 7: k_down_wave<7><<<tiles, 64, 0, s>>>(L, D, hq, hs, U, w, residual); break;
+    default: k_down_wave<8><<<tiles, 64, 0, s>>>(L, D, hq, hs, U, w, residual); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const Dims &D, const float *w, const UnionDev &U, const float *y, float *residual,
+                          hipStream_t s) {
+  if (D.T <= 0) return hipSuccess;
+  dim3 grid((D.d + 255) / 256, D.T), block(256);
+  k_combine<<<grid, block, 0, s>>>(D, w, U, y, residual);
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm(const float *r, int T, int d, float eps, float *x, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  k_rmsnorm<<<T, 256, 0, s>>>(r, d, eps, x);
   return hipGetLastError();
 }
 

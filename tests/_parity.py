@@ -96,8 +96,10 @@ class OracleLayer:
         return oracle.softmax_selected(L_row, np.asarray(idx_row, dtype=np.int32))
 
 
-def layer_parity(ctx, w: synth.Workload, layer: int, X: np.ndarray, ora: OracleLayer, residual=None):
-    """Route + forward on the GPU, then check routing, weights and outputs against the oracle.
+def layer_parity(ctx, w: synth.Workload, layer: int, X: np.ndarray, ora: OracleLayer, residual=None, flags=0,
+                 one_call=False):
+    """Route + forward on the GPU (or colimoe_route_forward if one_call), then
+    check routing, weights and outputs against the oracle.
 
     Returns dict with the GPU results and the worst error ratio."""
     import torch
@@ -105,17 +107,21 @@ def layer_parity(ctx, w: synth.Workload, layer: int, X: np.ndarray, ora: OracleL
     xt = torch.from_numpy(np.ascontiguousarray(X, dtype=np.float32)).to(dev)
     T = X.shape[0]
     U = ctx.new_union(T)
-    idx, wts, logits = ctx.route(layer, xt, U, want_logits=True)
     res = xt.clone() if residual is None else torch.from_numpy(np.ascontiguousarray(residual, np.float32)).to(dev)
-    ctx.forward(layer, xt, idx, wts, U, res)
+    if one_call:
+        idx, wts = ctx.route_forward(layer, xt, U, res, flags)
+        glog = None
+    else:
+        idx, wts, logits = ctx.route(layer, xt, U, want_logits=True)
+        ctx.forward(layer, xt, idx, wts, U, res, flags)
     ctx.sync()
     gidx = idx.cpu().numpy()
     gw = wts.cpu().numpy()
-    glog = logits.cpu().numpy()
     gout = res.cpu().numpy()
     L, oidx, ow = ora.route(X)
-    # logits: fp32 dot of 6144 terms vs fp64
-    assert_close(glog, L, rel=1e-4, what="logits")
+    if not one_call:
+        # logits: fp32 dot of d terms vs fp64
+        assert_close(logits.cpu().numpy(), L, rel=1e-4, what="logits")
     n_exact, differ = check_routing(L, gidx, w.k)
     # weights for the GPU's selection vs the oracle's softmax over the same selection
     wref = np.stack([ora.weights_for(L[t], gidx[t]) for t in range(T)])

@@ -21,8 +21,12 @@ UNION16 = synth.WORKLOADS["union16"]
 # odd shapes: partial lane groups (d/32 = 10, f/32 = 6), E not a multiple of 64
 RAGGED = synth.Workload(name="ragged", d=320, f=192, E=37, k=3, T=5, n_shared=1, zipf=1.1, rho=0.3,
                         seed=synth.BASE_SEED + 101)
-# d/32 = 66: two chunks per lane, the second one partial
+# d/32 = 66: two chunk steps per row, the second one partial
 RAGGED2 = synth.Workload(name="ragged2", d=2112, f=128, E=20, k=4, T=3, n_shared=0, seed=synth.BASE_SEED + 102)
+# wide in both d and f (fixed-point path) with partial steps in both GEMVs
+RAGGED3 = synth.Workload(name="ragged3", d=2112, f=2112, E=24, k=3, T=4, n_shared=1, zipf=1.1, rho=0.5,
+                         seed=synth.BASE_SEED + 103)
+FP32, FXP = 1, 3
 
 
 def _ctx(w, n_layers=1, max_tokens=None):
@@ -113,13 +117,18 @@ def test_invalid_routing_is_reported():
     assert ctx.sync(check=False) == 0
 
 
-@pytest.mark.parametrize("w", [TINY, RAGGED, RAGGED2], ids=lambda w: w.name)
+@pytest.mark.parametrize("w", [TINY, RAGGED, RAGGED2, RAGGED3], ids=lambda w: w.name)
 def test_layer_parity_small(w):
     ctx = _ctx(w)
     P.load_layer(ctx, w, 0)
     ora = P.OracleLayer(w, 0)
     X = synth.activations(w, stream=0)
     r = P.layer_parity(ctx, w, 0, X, ora)
+    if w is RAGGED3:  # both arithmetic paths, and the one-call entry point
+        r2 = P.layer_parity(ctx, w, 0, X, ora, flags=FP32)
+        r3 = P.layer_parity(ctx, w, 0, X, ora, one_call=True)
+        assert np.array_equal(r3["out"].view(np.uint32), r["out"].view(np.uint32))
+        print("ragged3 fp32 path worst ratio", r2["ratio"])
     print(w.name, "worst ratio", r["ratio"], "near-tie tokens", r["differ"])
     # union lists from route equal the oracle's union of the GPU routing
     o = oracle.union(r["idx"], w.E)
@@ -127,15 +136,18 @@ def test_layer_parity_small(w):
         assert np.array_equal(r["union"][key], o[key])
 
 
-def test_layer_parity_decode():
+@pytest.mark.parametrize("flags", [FXP, FP32], ids=["fxp", "fp32"])
+def test_layer_parity_decode(flags):
     w = DECODE
     ctx = _ctx(w)
     P.load_layer(ctx, w, 0)
     ora = P.OracleLayer(w, 0)
     for stream in (0, 1, 2):
         X = synth.activations(w, stream=stream)
-        r = P.layer_parity(ctx, w, 0, X, ora)
-        print("decode stream", stream, "worst ratio", r["ratio"], "near-ties", r["differ"])
+        r = P.layer_parity(ctx, w, 0, X, ora, flags=flags)
+        r1 = P.layer_parity(ctx, w, 0, X, ora, flags=flags, one_call=True)
+        assert np.array_equal(r1["out"].view(np.uint32), r["out"].view(np.uint32))
+        print("decode", flags, "stream", stream, "worst ratio", r["ratio"], "near-ties", r["differ"])
 
 
 def test_zero_tokens_is_a_noop():
@@ -149,7 +161,8 @@ def test_zero_tokens_is_a_noop():
     ctx.sync()
 
 
-def test_union16_parity_and_batch_identity():
+@pytest.mark.parametrize("flags", [FXP, FP32], ids=["fxp", "fp32"])
+def test_union16_parity_and_batch_identity(flags):
     """16 correlated positions: batched == one at a time, bit for bit; each
     unique expert appears once in the union; outputs match the oracle."""
     w = UNION16
@@ -157,7 +170,7 @@ def test_union16_parity_and_batch_identity():
     P.load_layer(ctx, w, 0)
     ora = P.OracleLayer(w, 0)
     X = synth.activations(w, stream=0)
-    r = P.layer_parity(ctx, w, 0, X, ora)
+    r = P.layer_parity(ctx, w, 0, X, ora, flags=flags)
     nu = r["union"]["n_unique"]
     print("union16: unique experts", nu, "of", w.T * w.k, "pairs; worst ratio", r["ratio"])
     assert nu < w.T * w.k
@@ -167,7 +180,7 @@ def test_union16_parity_and_batch_identity():
         U1 = ctx.new_union(1)
         idx1, w1, _ = ctx.route(0, x1, U1)
         res1 = x1.clone()
-        ctx.forward(0, x1, idx1, w1, U1, res1)
+        ctx.forward(0, x1, idx1, w1, U1, res1, flags)
         ctx.sync()
         assert np.array_equal(idx1.cpu().numpy()[0], r["idx"][t])
         assert np.array_equal(w1.cpu().numpy()[0].view(np.uint32), r["w"][t].view(np.uint32))
