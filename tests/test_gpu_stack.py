@@ -1,0 +1,102 @@
+"""32-layer decode stack (d=6144, f=2048, 256 experts, top-8 + shared, per-layer
+Zipf(1.1) router bias, RMSNorm with eps 1e-6 and unit weight between layers),
+all 32 layers resident on the GPU.
+
+The GPU runs the chain r_0 = x_0; x_l = RMSNorm(r_l) for l > 0 (x_0 raw);
+r_{l+1} = r_l + MoE_l(x_l) with colimoe_rmsnorm and colimoe_route_forward.  The
+oracle runs its own fp64 chain.  At every layer: the GPU's x_l and residual are
+checked against the oracle's with |gpu - oracle| <= 1e-3 (1 + |oracle|), the
+routing against the oracle's fp64 logits under the near-tie rule, and where a
+near-tie let the GPU pick a different (valid) set, the oracle follows the GPU's
+routing for that layer (teacher forcing only on near-ties).
+"""
+import time
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests._parity import OracleLayer, assert_close, check_routing, load_layer
+
+W = synth.WORKLOADS["stack32"]
+EPS = 1e-6
+FP32, FXP = 1, 3
+
+
+@pytest.fixture(scope="module")
+def stack_ctx():
+    import torch
+
+    from int4_routed_expert_fp32_amd.runtime import MoeContext
+    free, _ = torch.cuda.mem_get_info()
+    need = W.n_layers * (W.E + W.n_shared) * W.expert_bytes
+    if free < need * 1.05:
+        pytest.skip("stack of %d layers needs %.1f GB of device memory, %.1f GB free" % (W.n_layers, need / 1e9,
+                                                                                       free / 1e9))
+    ctx = MoeContext(W.d, W.f, W.E, W.k, n_layers=W.n_layers, n_shared=W.n_shared, max_tokens=1)
+    t0 = time.time()
+    for l in range(W.n_layers):
+        load_layer(ctx, W, l)
+        if l % 8 == 7:
+            print("stack: loaded %d/%d layers (%.1f s)" % (l + 1, W.n_layers, time.time() - t0), flush=True)
+    yield ctx
+    ctx.close()
+    del ctx
+    torch.cuda.empty_cache()
+
+
+def gpu_chain(ctx, x0, flags):
+    """Runs the stack on one token; returns per layer (x_l, idx_l, w_l, r_{l+1}) on the host."""
+    import torch
+    dev = ctx.device
+    r = torch.from_numpy(np.ascontiguousarray(x0, np.float32)).to(dev)
+    x = r.clone()
+    recs = []
+    for l in range(W.n_layers):
+        if l > 0:
+            ctx.rmsnorm(r, EPS, x)
+        U = ctx.new_union(1)
+        xin = x.cpu().numpy().copy()
+        idx, w = ctx.route_forward(l, x, U, r, flags)
+        ctx.sync()
+        recs.append((xin, idx.cpu().numpy(), w.cpu().numpy(), r.cpu().numpy().copy()))
+    return recs
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("flags", [FXP, FP32], ids=["fxp", "fp32"])
+def test_stack32_chain_matches_oracle(stack_ctx, flags):
+    x0 = synth.activations(W, stream=0, T=1)
+    recs = gpu_chain(stack_ctx, x0, flags)
+    ro = x0.astype(np.float64)
+    forced = []
+    worst = 0.0
+    for l in range(W.n_layers):
+        xo = ro if l == 0 else oracle.rmsnorm(ro[0], EPS)[None, :]
+        xg, gidx, gw, rg = recs[l]
+        if l > 0:
+            assert_close(xg, xo, what="layer %d RMSNorm output" % l)
+        ora = OracleLayer(W, l)
+        L, oidx, ow = ora.route(xo)
+        _, differ = check_routing(L, gidx, W.k)
+        if differ:
+            forced.append(l)
+        wref = ora.weights_for(L[0], gidx[0])[None, :]
+        assert_close(gw, wref, rel=1e-4, what="layer %d gate weights" % l)
+        out, _ = ora.forward(xo, gidx, wref, residual=ro)
+        worst = max(worst, assert_close(rg, out, what="layer %d residual" % l))
+        ro = out
+    print("stack32 %s: worst |gpu-oracle|/bound %.3g over 32 layers; near-tie layers followed: %s"
+          % ("fxp" if flags == FXP else "fp32", worst, forced))
+
+
+@pytest.mark.gpu
+def test_stack32_paths_route_identically(stack_ctx):
+    """Both arithmetic paths meet the bound; on this token they also pick the same experts at every layer
+    (the routes only see x, and x differs between the paths by far less than any logit gap here)."""
+    x0 = synth.activations(W, stream=1, T=1)
+    a = gpu_chain(stack_ctx, x0, FXP)
+    b = gpu_chain(stack_ctx, x0, FP32)
+    for l in range(W.n_layers):
+        assert np.array_equal(a[l][1], b[l][1]), "layer %d routed differently" % l
