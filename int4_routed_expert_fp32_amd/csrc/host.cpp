@@ -255,21 +255,30 @@ Workspace workspace_layout(int d, int f, int E, int k, int n_shared, int max_tok
   W.xs = take((size_t)max_tokens * (d / 16) * 4);
   W.hq = take(rows * (f / kChunk) * kDigitWords * 4);
   W.hs = take(rows * (f / 16) * 4);
+  W.xb = take(rows * d * 2);
+  W.hb = take(rows * f * 2);
+  W.mblk_max = mfma_max_entries(max_tokens, k, E, n_shared);
+  W.mblk = take((size_t)W.mblk_max * 16);
+  W.mcount = take(4);
   W.bytes = o;
   return W;
 }
 
 }  // namespace colimoe
 
-enum { PATH_FP32 = 0, PATH_FXP = 1 };
+enum { PATH_FP32 = 0, PATH_FXP = 1, PATH_MFMA = 2 };
 
-// Arithmetic path of a forward call: the fixed-point activation path when the
-// shapes allow it (both d and f at least 2048) unless fp32 is asked for.
+// Arithmetic path of a forward call.  AUTO: the bf16 MFMA path for
+// prefill-shaped calls (on average at least 64 tokens per expert, T*k >= 64*E),
+// else the fixed-point activation path when the shapes allow it (d and f at
+// least 2048), else fp32 dequantisation.
 static int select_path(colimoe_ctx *ctx, int T, uint32_t flags) {
   const Dims D = dims_of(ctx, T);
-  if (flags == COLIMOE_FWD_BF16_MFMA) return COLIMOE_E_ARG;  // prefill path not built yet
+  if (flags == COLIMOE_FWD_BF16_MFMA) return PATH_MFMA;
   if (flags == COLIMOE_FWD_FP32) return PATH_FP32;
   if (flags == COLIMOE_FWD_FXP) return fxp_supported(D) ? PATH_FXP : COLIMOE_E_SHAPE;
+  if (flags != COLIMOE_FWD_AUTO) return COLIMOE_E_ARG;
+  if ((long)T * D.k >= 64L * D.E) return PATH_MFMA;
   return fxp_supported(D) ? PATH_FXP : PATH_FP32;
 }
 
@@ -339,8 +348,27 @@ static int forward_impl(colimoe_ctx *ctx, int32_t layer, const float *x, int32_t
   }
   float *h = (float *)(ctx->ws + ctx->wl.h);
   float *y = (float *)(ctx->ws + ctx->wl.y);
-  const bool fused = down_fusable(D);
-  if (path == PATH_FXP) {
+  const bool fused = path != PATH_MFMA && down_fusable(D);
+  if (path == PATH_MFMA) {
+    int4 *list = (int4 *)(ctx->ws + ctx->wl.mblk);
+    int32_t *mcount = (int32_t *)(ctx->ws + ctx->wl.mcount);
+    uint16_t *xb = (uint16_t *)(ctx->ws + ctx->wl.xb);
+    uint16_t *hb = (uint16_t *)(ctx->ws + ctx->wl.hb);
+    const int me = mfma_max_entries(T, D.k, D.E, D.n_shared);
+    {
+      KTimer kt(ctx, K_ENCODE);
+      if (launch_mblocks(D, U, list, mcount, me, s) != hipSuccess) return COLIMOE_E_HIP;
+      if (launch_gather_bf16(x, D, U, xb, s) != hipSuccess) return COLIMOE_E_HIP;
+    }
+    {
+      KTimer kt(ctx, K_GATEUP);
+      if (launch_gateup_mfma(L, D, xb, list, mcount, me, hb, s) != hipSuccess) return COLIMOE_E_HIP;
+    }
+    {
+      KTimer kt(ctx, K_DOWN);
+      if (launch_down_mfma(L, D, hb, list, mcount, me, y, s) != hipSuccess) return COLIMOE_E_HIP;
+    }
+  } else if (path == PATH_FXP) {
     uint32_t *xq = (uint32_t *)(ctx->ws + ctx->wl.xq);
     float *xs = (float *)(ctx->ws + ctx->wl.xs);
     uint32_t *hq = (uint32_t *)(ctx->ws + ctx->wl.hq);

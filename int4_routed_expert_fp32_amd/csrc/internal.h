@@ -42,6 +42,8 @@ __host__ __device__ inline size_t chunk_offset(int tile, int K, int c, int r) {
 constexpr int kDigitWords = 24;               // fixed-point activations: words per 32-column chunk
 constexpr int kRouteSplitMaxT = 16;           // router with K split over waves up to this many tokens
 constexpr size_t kFusedLdsMax = 64 * 1024;    // LDS budget of the fused down + combine kernel
+constexpr int kMB = 128;                      // bf16 MFMA path: rows (pairs) per M-block
+constexpr int kNT = 128;                      // bf16 MFMA path: weight rows per work item
 
 struct ExpertLayout {
   size_t gu_nib, gu_sc, dn_nib, dn_sc, bytes;
@@ -84,6 +86,9 @@ struct Workspace {
   size_t y;       // [(Tmax*k + Tmax*n_shared)][d] fp32
   size_t xq, xs;  // fixed-point x: [Tmax][d/32][24] u32 digit words, [Tmax][d/16] fp32 scales
   size_t hq, hs;  // fixed-point h: [rows][f/32][24] u32, [rows][f/16] fp32
+  size_t xb, hb;  // bf16 MFMA path: x rows in pair order [rows][d], h [rows][f], bf16
+  size_t mblk, mcount;  // bf16 MFMA path: M-block list (int4 entries) and its length
+  int mblk_max;
   size_t bytes;
 };
 
@@ -122,6 +127,15 @@ hipError_t launch_down_fxp(const LayerDev &L, const Dims &D, const uint32_t *hq,
 // Down + combine for one token, one wave per output tile (T == 1).
 hipError_t launch_down_dec(const LayerDev &L, const Dims &D, const uint32_t *hq, const float *hs, const UnionDev &U,
                            const float *w, float *residual, hipStream_t s);
+// bf16 MFMA path (prefill-shaped calls).
+int mfma_max_entries(int T, int k, int E, int n_shared);
+hipError_t launch_mblocks(const Dims &D, const UnionDev &U, int4 *list, int32_t *count, int max_entries,
+                          hipStream_t s);
+hipError_t launch_gather_bf16(const float *x, const Dims &D, const UnionDev &U, uint16_t *xb, hipStream_t s);
+hipError_t launch_gateup_mfma(const LayerDev &L, const Dims &D, const uint16_t *xb, const int4 *list,
+                              const int32_t *count, int max_entries, uint16_t *hb, hipStream_t s);
+hipError_t launch_down_mfma(const LayerDev &L, const Dims &D, const uint16_t *hb, const int4 *list,
+                            const int32_t *count, int max_entries, float *y, hipStream_t s);
 hipError_t launch_rmsnorm(const float *r, int T, int d, float eps, float *x, hipStream_t s);
 
 }  // namespace colimoe
