@@ -1,20 +1,23 @@
 #!/usr/bin/env python3
 """Benchmark of the int4 routed-expert MoE layer on one MI355X.
 
-A step is one decode token through one MoE layer: route (router GEMV, top-k,
-batch-union) and forward (fused gate/up dequant-GEMV + SiLU*mul, down
-dequant-GEMV, gate-weighted combine into the residual), d=6144, f=2048,
-256 experts, top-8, plus one shared expert.  Inputs are seeded synthetic
-tensors resident in HBM before timing starts.  Consecutive steps cycle over a
-ring of independently generated layer instances (default 8, 41 GB), so the
-expert weights come from HBM rather than from the 256 MB Infinity Cache.
+Headline: one decode token through one MoE layer (d=6144, f=2048, 256 experts,
+top-8, plus one shared expert): route (router GEMV, top-k, union lists) and
+forward (gate/up dequant-GEMV + SiLU*mul, down dequant-GEMV, gate-weighted
+combine into the residual) in one colimoe_route_forward call.  Inputs are
+seeded synthetic tensors resident in HBM before timing starts.  Consecutive
+steps cycle over a ring of independently generated layer instances (default
+8, 41 GB) so the expert weights come from HBM rather than from the 256 MB
+Infinity Cache.  `value` is microseconds per token per MoE layer.
 
-Prints one JSON line.  `value` is microseconds per token per MoE layer (lower
-is better); the line also carries tokens/s, int4 expert-weight GB/s and its
-fraction of the 8 TB/s HBM peak, the roofline of the dominant kernel and the
-CPU oracle's time on a bounded sample of the same workload.
+The same JSON line also carries the other workloads of the layer, each timed on
+its own loaded layers: the 32-layer decode stack (RMSNorm between layers),
+the 16-position batch-union call and the 2048-token prefill call (bf16 MFMA
+path, with its matrix-core utilisation), plus the roofline of the dominant
+decode kernel and the CPU oracle's time on a bounded sample.
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -24,6 +27,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix-core peak of MI355X
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_gateup_traffic.json")
+KERNEL_SOURCES = ("kernels.hip", "device_common.h", "internal.h")
 
 
 def parse():
@@ -37,7 +43,240 @@ def parse():
     ap.add_argument("--path", choices=("auto", "fp32", "fxp"), default="auto",
                     help="arithmetic path of the headline (auto: fixed-point activations at these shapes)")
     ap.add_argument("--no-compare", action="store_true", help="skip timing the other arithmetic path")
+    ap.add_argument("--only", choices=("all", "decode", "stack32", "union16", "prefill2048"), default="all",
+                    help="run one workload only (the headline line needs decode)")
     return ap.parse_args()
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_sha():
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "int4_routed_expert_fp32_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or
+    None when the kernel sources changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    if not k or rec.get("source_sha256") != kernel_source_sha():
+        return None
+    return int(k["fetch_bytes"] + k["write_bytes"])
+
+
+def calibration_copy(torch, dev):
+    """A plain device copy of known size (256 MiB read + 256 MiB written): the
+    reference point that scales FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    a = torch.empty(64 << 20, dtype=torch.float32, device=dev).fill_(1.0)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    del a, b
+
+
+def per_kernel(cm, ctx, run, names=("route", "topk", "union", "encode", "gateup", "down", "combine", "rmsnorm")):
+    cm.colimoe_timing_enable(ctx.ctx, True)
+    for k in names:
+        cm.colimoe_timing_read(ctx.ctx, k, reset=True)
+    run()
+    kern = {}
+    for k in names:
+        tot, cnt = cm.colimoe_timing_read(ctx.ctx, k)
+        if cnt:
+            kern[k] = dict(avg_us=1000.0 * tot / cnt, launches=cnt)
+    cm.colimoe_timing_enable(ctx.ctx, False)
+    ctx.sync()
+    return kern
+
+
+def event_time(torch, stream, run):
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    run()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1)  # ms
+
+
+def load_ring(ctx, synth, w, n, tag):
+    t0 = time.time()
+    for i in range(n):
+        ex = synth.expert_blobs(w, i, 0, w.E)
+        ctx.load_layer(i, synth.router(w, i), synth.bias(w, i), ex, synth.shared_blob(w, i))
+        del ex
+        if i % 8 == 7 or i == n - 1:
+            log("%s: loaded layer %d/%d (%.1f s)" % (tag, i + 1, n, time.time() - t0))
+
+
+def bench_decode(args, torch, np, synth, cm, MoeContext, dev, stream):
+    w = synth.WORKLOADS["decode"]
+    ctx = MoeContext(w.d, w.f, w.E, w.k, n_layers=args.ring, n_shared=w.n_shared, max_tokens=1)
+    load_ring(ctx, synth, w, args.ring, "decode")
+    n = args.warmup + args.steps
+    X = torch.from_numpy(synth.activations(w.with_(T=n), stream=11)).to(dev)
+    res = X.clone()
+    idx = torch.empty((n, w.k), dtype=torch.int32, device=dev)
+    wts = torch.empty((n, w.k), dtype=torch.float32, device=dev)
+    unions = [ctx.new_union(1) for _ in range(args.ring)]
+    flag_of = {"auto": cm.COLIMOE_FWD_AUTO, "fp32": cm.COLIMOE_FWD_FP32, "fxp": cm.COLIMOE_FWD_FXP}
+
+    def step(i, flags):
+        layer = i % args.ring
+        cm.colimoe_route_forward(ctx.ctx, layer, X[i].data_ptr(), 1, idx[i].data_ptr(), wts[i].data_ptr(),
+                                 unions[layer].abi(), res[i].data_ptr(), flags)
+
+    def steps(flags, lo, hi):
+        return lambda: [step(i, flags) for i in range(lo, hi)]
+
+    head = flag_of[args.path]
+    steps(head, 0, args.warmup)()
+    ctx.sync()
+    ms = event_time(torch, stream, steps(head, args.warmup, n)) / args.steps
+    ctx.sync()
+    kern = per_kernel(cm, ctx, steps(head, args.warmup, n))
+    other = None
+    if not args.no_compare:
+        oflags = cm.COLIMOE_FWD_FP32 if args.path != "fp32" else cm.COLIMOE_FWD_FXP
+        steps(oflags, 0, args.warmup)()
+        oms = event_time(torch, stream, steps(oflags, args.warmup, n)) / args.steps
+        okern = per_kernel(cm, ctx, steps(oflags, args.warmup, n))
+        other = {"path": "fp32" if oflags == cm.COLIMOE_FWD_FP32 else "fxp", "us_per_token": round(1000 * oms, 3),
+                 "kernels": {k: round(v["avg_us"], 3) for k, v in okern.items()}}
+    ctx.close()
+    del ctx, X, res
+    torch.cuda.empty_cache()
+    return w, ms, kern, other
+
+
+def bench_stack32(args, torch, np, synth, cm, MoeContext, dev, stream):
+    w = synth.WORKLOADS["stack32"]
+    need = w.n_layers * (w.E + w.n_shared) * w.expert_bytes
+    free, _ = torch.cuda.mem_get_info()
+    if free < need * 1.05:
+        return {"skipped": "needs %.1f GB of device memory, %.1f GB free" % (need / 1e9, free / 1e9)}
+    ctx = MoeContext(w.d, w.f, w.E, w.k, n_layers=w.n_layers, n_shared=w.n_shared, max_tokens=1)
+    load_ring(ctx, synth, w, w.n_layers, "stack32")
+    ntok, warm = 24, 4
+    X0 = torch.from_numpy(synth.activations(w.with_(T=ntok + warm), stream=5)).to(dev)
+    r = X0.clone()
+    x = torch.empty_like(X0)
+    idx = torch.empty((w.n_layers, w.k), dtype=torch.int32, device=dev)
+    wts = torch.empty((w.n_layers, w.k), dtype=torch.float32, device=dev)
+    U = ctx.new_union(1)
+    nu_total = []
+
+    def token(i):
+        for l in range(w.n_layers):
+            src = X0[i] if l == 0 else x[i]
+            if l > 0:
+                cm.colimoe_rmsnorm(ctx.ctx, r[i].data_ptr(), 1, 1e-6, x[i].data_ptr())
+            cm.colimoe_route_forward(ctx.ctx, l, src.data_ptr(), 1, idx[l].data_ptr(), wts[l].data_ptr(), U.abi(),
+                                     r[i].data_ptr(), cm.COLIMOE_FWD_AUTO)
+
+    for i in range(warm):
+        token(i)
+    ctx.sync()
+    ms = event_time(torch, stream, lambda: [token(i) for i in range(warm, warm + ntok)]) / ntok
+    ctx.sync()
+    kern = per_kernel(cm, ctx, lambda: [token(i) for i in range(warm, warm + 4)])
+    ctx.close()
+    del ctx, X0, r, x
+    torch.cuda.empty_cache()
+    bytes_tok = w.n_layers * (w.k + w.n_shared) * w.expert_bytes
+    gbs = bytes_tok / (ms * 1e-3) / 1e9
+    return {"workload": "32-layer decode stack, d=6144 f=2048 E=256 top-8 + shared, Zipf(1.1) bias, RMSNorm "
+                        "eps 1e-6 between layers, 1 token; all 32 layers resident (%.1f GB)" % (need / 1e9),
+            "us_per_token": round(1000 * ms, 2), "tokens_per_s": round(1000.0 / ms, 1),
+            "us_per_layer": round(1000 * ms / w.n_layers, 3), "int4_bytes_per_token": bytes_tok,
+            "int4_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "tokens_timed": ntok,
+            "kernels": {k: round(v["avg_us"], 3) for k, v in kern.items()}}
+
+
+def bench_union16(args, torch, np, synth, cm, MoeContext, dev, stream):
+    w = synth.WORKLOADS["union16"]
+    ring = 4
+    ctx = MoeContext(w.d, w.f, w.E, w.k, n_layers=ring, n_shared=w.n_shared, max_tokens=w.T)
+    load_ring(ctx, synth, w, ring, "union16")
+    nb, warm = 32, 4
+    Xs = [torch.from_numpy(synth.activations(w, stream=100 + b)).to(dev) for b in range(nb + warm)]
+    res = [x.clone() for x in Xs]
+    idx = torch.empty((w.T, w.k), dtype=torch.int32, device=dev)
+    wts = torch.empty((w.T, w.k), dtype=torch.float32, device=dev)
+    unions = [ctx.new_union(w.T) for _ in range(nb + warm)]
+
+    def call(b):
+        cm.colimoe_route_forward(ctx.ctx, b % ring, Xs[b].data_ptr(), w.T, idx.data_ptr(), wts.data_ptr(),
+                                 unions[b].abi(), res[b].data_ptr(), cm.COLIMOE_FWD_AUTO)
+
+    for b in range(warm):
+        call(b)
+    ctx.sync()
+    ms = event_time(torch, stream, lambda: [call(b) for b in range(warm, warm + nb)]) / nb
+    ctx.sync()
+    kern = per_kernel(cm, ctx, lambda: [call(b) for b in range(warm, warm + nb)])
+    nus = [int(unions[b].n_unique.item()) for b in range(warm, warm + nb)]
+    ctx.close()
+    del ctx
+    torch.cuda.empty_cache()
+    bytes_call = (float(np.mean(nus)) + w.n_shared) * w.expert_bytes
+    gbs = bytes_call / (ms * 1e-3) / 1e9
+    return {"workload": "batch-union call, 16 positions (pairwise correlation 0.6, Zipf(1.1) bias), d=6144 f=2048 "
+                        "E=256 top-8 + shared", "us_per_call": round(1000 * ms, 2),
+            "tokens_per_s": round(w.T * 1000.0 / ms, 1), "unique_experts_mean": round(float(np.mean(nus)), 2),
+            "int4_bytes_per_call": int(bytes_call), "int4_gbs": round(gbs, 1),
+            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "calls_timed": nb,
+            "kernels": {k: round(v["avg_us"], 3) for k, v in kern.items()}}
+
+
+def bench_prefill(args, torch, np, synth, cm, MoeContext, dev, stream):
+    w = synth.WORKLOADS["prefill2048"]
+    ring = 2
+    ctx = MoeContext(w.d, w.f, w.E, w.k, n_layers=ring, n_shared=w.n_shared, max_tokens=w.T)
+    load_ring(ctx, synth, w, ring, "prefill2048")
+    nb, warm = 8, 2
+    X = torch.from_numpy(synth.activations(w, stream=0)).to(dev)
+    res = X.clone()
+    idx = torch.empty((w.T, w.k), dtype=torch.int32, device=dev)
+    wts = torch.empty((w.T, w.k), dtype=torch.float32, device=dev)
+    U = ctx.new_union(w.T)
+
+    def call(b):
+        cm.colimoe_route_forward(ctx.ctx, b % ring, X.data_ptr(), w.T, idx.data_ptr(), wts.data_ptr(), U.abi(),
+                                 res.data_ptr(), cm.COLIMOE_FWD_AUTO)
+
+    for b in range(warm):
+        call(b)
+    ctx.sync()
+    ms = event_time(torch, stream, lambda: [call(b) for b in range(warm, warm + nb)]) / nb
+    ctx.sync()
+    kern = per_kernel(cm, ctx, lambda: [call(b) for b in range(warm, warm + nb)])
+    nu = int(U.n_unique.item())
+    ctx.close()
+    del ctx, X, res
+    torch.cuda.empty_cache()
+    pairs = w.T * w.k
+    flops = 2.0 * 3 * w.d * w.f * (pairs + w.T * w.n_shared)
+    gemm_us = kern.get("gateup", {}).get("avg_us", 0.0) + kern.get("down", {}).get("avg_us", 0.0)
+    bytes_call = (nu + w.n_shared) * w.expert_bytes
+    gbs = bytes_call / (ms * 1e-3) / 1e9
+    return {"workload": "prefill call, 2048 tokens, Zipf(1.1) bias, d=6144 f=2048 E=256 top-8 + shared, bf16 MFMA "
+                        "grouped GEMM", "ms_per_call": round(ms, 4), "tokens_per_s": round(w.T * 1000.0 / ms, 1),
+            "unique_experts": nu, "expert_flops": flops,
+            "mfma_util": round(flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "mfma_util_gemm_kernels": round(flops / (gemm_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4) if gemm_us else None,
+            "int4_bytes_per_call": bytes_call, "int4_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "calls_timed": nb, "kernels": {k: round(v["avg_us"], 3) for k, v in kern.items()}}
 
 
 def main():
@@ -54,80 +293,22 @@ def main():
     import int4_routed_expert_fp32_amd as cm
     from int4_routed_expert_fp32_amd.runtime import MoeContext
 
-    w = synth.WORKLOADS["decode"]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    ctx = MoeContext(w.d, w.f, w.E, w.k, n_layers=args.ring, n_shared=w.n_shared, max_tokens=1)
-    t0 = time.time()
-    for i in range(args.ring):
-        R = synth.router(w, i)
-        ex = synth.expert_blobs(w, i, 0, w.E)
-        sh = synth.shared_blob(w, i)
-        ctx.load_layer(i, R, None, ex, sh)
-        del ex
-        print("loaded layer instance %d/%d (%.1f s)" % (i + 1, args.ring, time.time() - t0), file=sys.stderr,
-              flush=True)
-
-    n = args.warmup + args.steps
-    X = torch.from_numpy(synth.activations(w.with_(T=n), stream=11)).to(dev)
-    res = X.clone()
-    idx = torch.empty((n, w.k), dtype=torch.int32, device=dev)
-    wts = torch.empty((n, w.k), dtype=torch.float32, device=dev)
-    unions = [ctx.new_union(1) for _ in range(args.ring)]
     stream = torch.cuda.current_stream(dev)
+    calibration_copy(torch, dev)
+    common = (args, torch, np, synth, cm, MoeContext, dev, stream)
 
-    flag_of = {"auto": cm.COLIMOE_FWD_AUTO, "fp32": cm.COLIMOE_FWD_FP32, "fxp": cm.COLIMOE_FWD_FXP}
+    extra = {}
+    for name, fn in (("stack32", bench_stack32), ("union16", bench_union16), ("prefill2048", bench_prefill)):
+        if args.only in ("all", name):
+            extra[name] = fn(*common)
+            log("%s: %s" % (name, json.dumps({k: v for k, v in extra[name].items() if k != "kernels"})))
+    if args.only not in ("all", "decode"):
+        print(json.dumps(extra), flush=True)
+        return
 
-    def step(i, flags):
-        layer = i % args.ring
-        x = X[i:i + 1]
-        U = unions[layer]
-        cm.colimoe_route_forward(ctx.ctx, layer, x.data_ptr(), 1, idx[i].data_ptr(), wts[i].data_ptr(), U.abi(),
-                                 res[i].data_ptr(), flags)
-
-    def timed(flags):
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        ev0.record(stream)
-        for i in range(args.warmup, n):
-            step(i, flags)
-        ev1.record(stream)
-        torch.cuda.synchronize()
-        ctx.sync()
-        return ev0.elapsed_time(ev1) / args.steps
-
-    def per_kernel(flags):
-        names = ("route", "topk", "union", "encode", "gateup", "down", "combine")
-        cm.colimoe_timing_enable(ctx.ctx, True)
-        cm.colimoe_timing_read(ctx.ctx, "route", reset=True)
-        for i in range(args.warmup, n):
-            step(i, flags)
-        kern = {}
-        for k in names:
-            tot, cnt = cm.colimoe_timing_read(ctx.ctx, k)
-            if cnt:
-                kern[k] = dict(avg_us=1000.0 * tot / cnt, launches=cnt)
-        cm.colimoe_timing_enable(ctx.ctx, False)
-        ctx.sync()
-        return kern
-
-    head = flag_of[args.path]
-    for i in range(args.warmup):
-        step(i, head)
-    ctx.sync()
-    torch.cuda.synchronize()
-    ms_step = timed(head)          # headline pass: plain launches
-    kern = per_kernel(head)        # the same steps with HIP events around each kernel
-    other = None
-    if not args.no_compare:
-        oflags = cm.COLIMOE_FWD_FP32 if args.path != "fp32" else cm.COLIMOE_FWD_FXP
-        for i in range(args.warmup):
-            step(i, oflags)
-        oms = timed(oflags)
-        okern = per_kernel(oflags)
-        other = {"path": "fp32" if oflags == cm.COLIMOE_FWD_FP32 else "fxp", "us_per_token": round(1000 * oms, 3),
-                 "kernels": {k: round(v["avg_us"], 3) for k, v in okern.items()}}
-
+    w, ms_step, kern, other = bench_decode(*common)
     be = w.expert_bytes
     gu_bytes = 2 * (w.d * w.f // 2 + 2 * w.d * w.f // 64)     # gate+up int4 + fp16 scales of one expert
     dn_bytes = be - gu_bytes
@@ -137,8 +318,8 @@ def main():
     gbs = int4_bytes / (ms_step * 1e-3) / 1e9
     gu_gbs = experts_touched * gu_bytes / (kern["gateup"]["avg_us"] * 1e-6) / 1e9
     dn_gbs = experts_touched * dn_bytes / (kern["down"]["avg_us"] * 1e-6) / 1e9
-    roofline = dict(bound="hbm", kernel="gateup", achieved=round(gu_gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(gu_gbs / HBM_PEAK_GBS, 4), traffic=None,
+    roofline = dict(bound="hbm", kernel="k_gateup_fxp<1>", achieved=round(gu_gbs, 1), peak=HBM_PEAK_GBS,
+                    unit="GB/s", frac=round(gu_gbs / HBM_PEAK_GBS, 4), traffic=measured_traffic("k_gateup_fxp<1>"),
                     bytes_per_launch=experts_touched * gu_bytes, avg_launch_us=round(kern["gateup"]["avg_us"], 3))
 
     cpu = None
@@ -156,7 +337,7 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int4 weights; fp32 accumulation" + (" (fixed-point activations, exact int4 dot)"
+        "dtype": "int4 weights, fp32 accumulation" + (" (fixed-point activations, exact int4 dot)"
                                                         if args.path != "fp32" else " (fp32 dequant)"),
         "data": "synthetic (seeded int4 gs64 experts, fp16 scales, N(0,1) activations)",
         "config": {"workload": "decode MoE layer d=6144 f=2048 E=256 top-8 + 1 shared, 1 token",
@@ -171,6 +352,7 @@ def main():
         "compare": other,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "workloads": extra,
     }
     print(json.dumps(out), flush=True)
 
