@@ -248,6 +248,7 @@ Workspace workspace_layout(int d, int f, int E, int k, int n_shared, int max_tok
   W.pair_slot = take(tk * 4);
   W.pair_of = take(tk * 4);
   W.logits = take((size_t)max_tokens * E * 4);
+  W.rpart = take((size_t)router_splits(d) * max_tokens * E * 4);
   const size_t rows = tk + (size_t)max_tokens * n_shared;
   W.h = take(rows * f * 4);
   W.y = take(rows * d * 4);
@@ -318,7 +319,7 @@ static int route_impl(colimoe_ctx *ctx, int32_t layer, const float *x, int32_t T
     }
   } else {
     KTimer kt(ctx, K_ROUTE);
-    if (launch_router(L, D, x, lg, s) != hipSuccess) return COLIMOE_E_HIP;
+    if (launch_router_mfma(L, D, x, (float *)(ctx->ws + ctx->wl.rpart), lg, s) != hipSuccess) return COLIMOE_E_HIP;
   }
   {
     KTimer kt(ctx, K_TOPK);

@@ -43,7 +43,7 @@ constexpr int kDigitWords = 24;               // fixed-point activations: words 
 constexpr int kRouteSplitMaxT = 16;           // router with K split over waves up to this many tokens
 constexpr size_t kFusedLdsMax = 64 * 1024;    // LDS budget of the fused down + combine kernel
 constexpr int kMB = 128;                      // bf16 MFMA path: rows (pairs) per M-block
-constexpr int kNT = 128;                      // bf16 MFMA path: weight rows per work item
+constexpr int kNT = 256;                      // bf16 MFMA path: weight rows per work item
 
 struct ExpertLayout {
   size_t gu_nib, gu_sc, dn_nib, dn_sc, bytes;
@@ -82,6 +82,7 @@ struct Workspace {
   size_t err;     // int32 error word set by kernels that reject a routing
   size_t n_unique, ids, offsets, pair_token, pair_slot, pair_of;  // union lists
   size_t logits;  // [Tmax][E] fp32
+  size_t rpart;   // router partial sums for many tokens: [S][Tmax][E] fp32
   size_t h;       // [(Tmax*k + Tmax*n_shared)][f] fp32
   size_t y;       // [(Tmax*k + Tmax*n_shared)][d] fp32
   size_t xq, xs;  // fixed-point x: [Tmax][d/32][24] u32 digit words, [Tmax][d/16] fp32 scales
@@ -102,7 +103,6 @@ hipError_t launch_router_split(const LayerDev &L, const Dims &D, const float *x,
 // Top-k of one token and, if U, its union lists (T == 1).
 hipError_t launch_topk_union1(const float *logits, const Dims &D, int32_t *idx, float *w, const UnionDev *U,
                               hipStream_t s);
-hipError_t launch_router(const LayerDev &L, const Dims &D, const float *x, float *logits, hipStream_t s);
 hipError_t launch_topk(const float *logits, const Dims &D, int32_t *idx, float *w, hipStream_t s);
 hipError_t launch_union(const int32_t *idx, const Dims &D, const UnionDev &U, int32_t *err, hipStream_t s);
 hipError_t launch_gateup(const LayerDev &L, const Dims &D, const float *x, const UnionDev &U, float *h,
@@ -127,6 +127,11 @@ hipError_t launch_down_fxp(const LayerDev &L, const Dims &D, const uint32_t *hq,
 // Down + combine for one token, one wave per output tile (T == 1).
 hipError_t launch_down_dec(const LayerDev &L, const Dims &D, const uint32_t *hq, const float *hs, const UnionDev &U,
                            const float *w, float *residual, hipStream_t s);
+// Router for many tokens on the matrix cores (fp32), with S = router_splits(d)
+// K-slices whose partials (part: [S][T][E]) are summed in slice order.
+int router_splits(int d);
+hipError_t launch_router_mfma(const LayerDev &L, const Dims &D, const float *x, float *part, float *logits,
+                              hipStream_t s);
 // bf16 MFMA path (prefill-shaped calls).
 int mfma_max_entries(int T, int k, int E, int n_shared);
 hipError_t launch_mblocks(const Dims &D, const UnionDev &U, int4 *list, int32_t *count, int max_entries,

@@ -142,86 +142,9 @@ __device__ __forceinline__ float group_sum(float v, int width) {
 
 // ------------------------------------------------------------------- router
 // A1 ([A] §1: a router picks 8 of the 256 experts): logits l[t][e] =
-// sum_c R[e][c] x[t][c] + b[e] in fp32.  One wave per expert row; the row is
-// held in registers and applied to every token; each token's sum runs in the
-// same lane order and tree whatever T is.
-
-template <int STEPS>
-__device__ __forceinline__ void router_row(const LayerDev &L, const Dims &D, const float *__restrict__ x, int e,
-                                           float *__restrict__ logits) {
-  const int lane = threadIdx.x & 63;
-  const float *row = L.router + (size_t)e * D.d;
-  float4 r[STEPS];
-#pragma unroll
-  for (int i = 0; i < STEPS; ++i) {
-    const int c = 4 * lane + 256 * i;
-    r[i] = c < D.d ? *(const float4 *)(row + c) : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
-  const float b = L.bias[e];
-  for (int t = 0; t < D.T; ++t) {
-    const float *xr = x + (size_t)t * D.d;
-    float acc = 0.0f;
-#pragma unroll
-    for (int i = 0; i < STEPS; ++i) {
-      const int c = 4 * lane + 256 * i;
-      if (c < D.d) {
-        const float4 xv = *(const float4 *)(xr + c);
-        acc = __builtin_fmaf(r[i].x, xv.x, acc);
-        acc = __builtin_fmaf(r[i].y, xv.y, acc);
-        acc = __builtin_fmaf(r[i].z, xv.z, acc);
-        acc = __builtin_fmaf(r[i].w, xv.w, acc);
-      }
-    }
-    acc = wave_sum(acc);
-    if (lane == 0) logits[(size_t)t * D.E + e] = acc + b;
-  }
-}
-
-template <int STEPS>
-__global__ __launch_bounds__(256) void k_router_gemv(LayerDev L, Dims D, const float *__restrict__ x,
-                                                     float *__restrict__ logits) {
-  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (e < D.E) router_row<STEPS>(L, D, x, e, logits);
-}
-
-// Tiled variant for many tokens: a 64x64 block of (tokens, experts), K in
-// steps of 32 through LDS; each output's sum runs over c in ascending order.
-__global__ __launch_bounds__(256) void k_router_gemm(LayerDev L, Dims D, const float *__restrict__ x,
-                                                     float *__restrict__ logits) {
-  __shared__ float xs[32][65];
-  __shared__ float rs[32][65];
-  const int t0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
-  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-  float acc[4][4] = {};
-  for (int k0 = 0; k0 < D.d; k0 += 32) {
-    for (int i = threadIdx.x; i < 64 * 32; i += 256) {
-      const int rr = i >> 5, cc = i & 31;
-      const int t = t0 + rr, e = e0 + rr;
-      xs[cc][rr] = t < D.T ? x[(size_t)t * D.d + k0 + cc] : 0.0f;
-      rs[cc][rr] = e < D.E ? L.router[(size_t)e * D.d + k0 + cc] : 0.0f;
-    }
-    __syncthreads();
-#pragma unroll 8
-    for (int kk = 0; kk < 32; ++kk) {
-      float a[4], bb[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        a[i] = xs[kk][ty * 4 + i];
-        bb[i] = rs[kk][tx * 4 + i];
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(a[i], bb[j], acc[i][j]);
-    }
-    __syncthreads();
-  }
-  for (int i = 0; i < 4; ++i)
-    for (int j = 0; j < 4; ++j) {
-      const int t = t0 + ty * 4 + i, e = e0 + tx * 4 + j;
-      if (t < D.T && e < D.E) logits[(size_t)t * D.E + e] = acc[i][j] + L.bias[e];
-    }
-}
+// sum_c R[e][c] x[t][c] + b[e] in fp32.  Up to 16 tokens: k_router_split
+// below (one block per expert row); more tokens: the matrix-core kernel in
+// kernels_mfma.hip.
 
 // -------------------------------------------------------------------- top-k
 // A2: the k largest logits, larger first, exact ties to the lower expert;
@@ -404,6 +327,137 @@ __global__ __launch_bounds__(64) void k_union(const int32_t *__restrict__ idx, D
                                               int32_t *__restrict__ err) {
   extern __shared__ __align__(16) unsigned long long union_lds[];
   union_wave(idx, D, U, err, union_lds);
+}
+
+// Union for many tokens: the W waves of one block each take a contiguous
+// segment of tokens.  Per-(segment, expert) counts, prefixed over segments in
+// wave order and offset by each expert's start, give every wave the position
+// of its first pair of each expert, so the scatter (one wave per segment,
+// 64-token chunks ranked with lane masks as above) keeps token order inside
+// every expert.  Same lists as the one-wave kernel.
+// LDS: masks[W][E] u64, segc[W][E], counts[E], start[E], one flag.
+__host__ __device__ inline size_t union_multi_lds_bytes(int E, int W) {
+  return (size_t)W * E * 8 + ((size_t)W * E + 2 * (size_t)E + 1) * 4;
+}
+
+__global__ __launch_bounds__(1024) void k_union_multi(const int32_t *__restrict__ idx, Dims D, UnionDev U,
+                                                      int32_t *__restrict__ err) {
+  extern __shared__ __align__(16) unsigned long long union_lds[];
+  const int E = D.E, k = D.k, T = D.T;
+  const int W = blockDim.x >> 6, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  unsigned long long *masks = union_lds;
+  int32_t *segc = (int32_t *)(masks + (size_t)W * E);
+  int32_t *counts = segc + (size_t)W * E;
+  int32_t *start = counts + E;
+  int32_t &bad = start[E];
+  for (int i = threadIdx.x; i < W * E; i += blockDim.x) {
+    masks[i] = 0ull;
+    segc[i] = 0;
+  }
+  if (threadIdx.x == 0) bad = 0;
+  __syncthreads();
+  const int seg = (T + W - 1) / W;
+  const int t_lo = min(T, wave * seg), t_hi = min(T, t_lo + seg);
+  int32_t *mycount = segc + (size_t)wave * E;
+  for (int t = t_lo + lane; t < t_hi; t += 64) {
+    for (int j = 0; j < k; ++j) {
+      const int e = idx[(size_t)t * k + j];
+      bool ok = e >= 0 && e < E;
+      for (int i = 0; i < j && ok; ++i) ok = idx[(size_t)t * k + i] != e;
+      if (!ok)
+        bad = 1;
+      else
+        atomicAdd(&mycount[e], 1);
+    }
+  }
+  __syncthreads();
+  if (bad) {
+    if (threadIdx.x == 0) {
+      *U.n_unique = 0;
+      U.offsets[0] = 0;
+      atomicOr(err, 1);
+    }
+    return;
+  }
+  // per expert: exclusive prefix over segments (wave order) and the total
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    int run = 0;
+    for (int w = 0; w < W; ++w) {
+      const int c = segc[(size_t)w * E + e];
+      segc[(size_t)w * E + e] = run;
+      run += c;
+    }
+    counts[e] = run;
+  }
+  __syncthreads();
+  if (wave == 0) {  // exclusive scans of counts and of (counts > 0), lane-blocked
+    const int per = (E + 63) / 64;
+    const int e0 = lane * per, e1 = min(E, e0 + per);
+    int csum = 0, nsum = 0;
+    for (int e = e0; e < e1; ++e) {
+      csum += counts[e];
+      nsum += counts[e] > 0;
+    }
+    int cinc = csum, ninc = nsum;
+    for (int o = 1; o < 64; o <<= 1) {
+      const int a = __shfl_up(cinc, o, 64), b = __shfl_up(ninc, o, 64);
+      if (lane >= o) {
+        cinc += a;
+        ninc += b;
+      }
+    }
+    int cb = cinc - csum, nb = ninc - nsum;
+    for (int e = e0; e < e1; ++e) {
+      start[e] = cb;
+      if (counts[e] > 0) {
+        U.ids[nb] = e;
+        U.offsets[nb] = cb;
+        ++nb;
+      }
+      cb += counts[e];
+    }
+    if (lane == 63) {
+      *U.n_unique = ninc;
+      U.offsets[ninc] = cinc;
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < W * E; i += blockDim.x) segc[i] += start[i % E];
+  __syncthreads();
+  // scatter: wave w over its segment, running positions in segc[w][*]
+  unsigned long long *mymask = masks + (size_t)wave * E;
+  for (int c0 = t_lo; c0 < t_hi; c0 += 64) {
+    const int t = c0 + lane;
+    const bool act = t < t_hi;
+    int ee[16];
+    unsigned long long mm[16];
+    int rr[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (act && j < k) {
+        ee[j] = idx[(size_t)t * k + j];
+        atomicOr(&mymask[ee[j]], 1ull << lane);
+      }
+    wave_lds_sync();
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (act && j < k) {
+        mm[j] = mymask[ee[j]];
+        rr[j] = __popcll(mm[j] & ((1ull << lane) - 1ull));
+        const int p = mycount[ee[j]] + rr[j];
+        U.pair_token[p] = t;
+        U.pair_slot[p] = j;
+        U.pair_of[(size_t)t * k + j] = p;
+      }
+    wave_lds_sync();
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (act && j < k && rr[j] == 0) {
+        mycount[ee[j]] += __popcll(mm[j]);
+        mymask[ee[j]] = 0ull;
+      }
+    wave_lds_sync();
+  }
 }
 
 // ----------------------------------------------------------- expert GEMVs
@@ -888,37 +942,48 @@ __global__ __launch_bounds__(64 * NWMAX) void k_down_fxp(LayerDev L, Dims D, con
 // combine order), so their results are bit-identical to them.
 
 // Router with the d columns split over the 4 waves of a block, one block per
-// expert row; the 4 partial sums are added in wave order.
+// expert row, up to 16 tokens.  Each wave keeps its quarter of the row in
+// registers and applies it to every token; the 4 partial sums of a token are
+// added in wave order.  A token's logit does not depend on T.
 __global__ __launch_bounds__(256) void k_router_split(LayerDev L, Dims D, const float *__restrict__ x,
                                                       float *__restrict__ logits, uint32_t *__restrict__ xq,
                                                       float *__restrict__ xs) {
-  __shared__ float part[16][4];
+  __shared__ float part[kRouteSplitMaxT][4];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int e = blockIdx.x;
   if (xq) {  // fixed-point encoding of x for the gate/up kernel, spread over the blocks
     const int groups = D.T * (D.d / 16);
     for (int g = blockIdx.x * 256 + threadIdx.x; g < groups; g += gridDim.x * 256) xquant_group(x, D.d, g, xq, xs);
   }
-  const int q4 = D.d / 4;  // columns per wave (d is a multiple of 64)
+  const int q4 = D.d / 4;  // columns per wave (d is a multiple of 64, at most 16384)
   const float *row = L.router + (size_t)e * D.d + (size_t)wave * q4;
+  float4 r[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int c = 4 * lane + 256 * i;
+    r[i] = c < q4 ? *(const float4 *)(row + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
   for (int t = 0; t < D.T; ++t) {
     const float *xr = x + (size_t)t * D.d + (size_t)wave * q4;
     float acc = 0.0f;
-    for (int c = 4 * lane; c < q4; c += 256) {
-      const float4 r = *(const float4 *)(row + c);
-      const float4 xv = *(const float4 *)(xr + c);
-      acc = __builtin_fmaf(r.x, xv.x, acc);
-      acc = __builtin_fmaf(r.y, xv.y, acc);
-      acc = __builtin_fmaf(r.z, xv.z, acc);
-      acc = __builtin_fmaf(r.w, xv.w, acc);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int c = 4 * lane + 256 * i;
+      if (c < q4) {
+        const float4 xv = *(const float4 *)(xr + c);
+        acc = __builtin_fmaf(r[i].x, xv.x, acc);
+        acc = __builtin_fmaf(r[i].y, xv.y, acc);
+        acc = __builtin_fmaf(r[i].z, xv.z, acc);
+        acc = __builtin_fmaf(r[i].w, xv.w, acc);
+      }
     }
     acc = wave_sum(acc);
-    if (lane == 0) part[t & 15][wave] = acc;
-    __syncthreads();
-    if (threadIdx.x == 0) logits[(size_t)t * D.E + e] = ((part[t & 15][0] + part[t & 15][1]) + part[t & 15][2]) +
-                                                         part[t & 15][3] + L.bias[e];
-    __syncthreads();
+    if (lane == 0) part[t][wave] = acc;
   }
+  __syncthreads();
+  if (threadIdx.x < D.T)
+    logits[(size_t)threadIdx.x * D.E + e] =
+        ((part[threadIdx.x][0] + part[threadIdx.x][1]) + part[threadIdx.x][2]) + part[threadIdx.x][3] + L.bias[e];
 }
 
 // Top-k of one token plus its union lists (its ids sorted ascending).
@@ -1170,36 +1235,43 @@ __global__ __launch_bounds__(256) void k_down_narrow(LayerDev L, Dims D, const f
 
 __global__ __launch_bounds__(256) void k_combine(Dims D, const float *__restrict__ w, UnionDev U,
                                                  const float *__restrict__ y, float *__restrict__ residual) {
-  const int t = blockIdx.y;
-  const int r = blockIdx.x * 256 + threadIdx.x;
-  if (t >= D.T || r >= D.d) return;
-  // A token's pairs sit in ascending expert order in the union lists, so
-  // visiting its slots by increasing pair index visits experts ascending.
+  // One block per token.  A token's pairs sit in ascending expert order in the
+  // union lists, so visiting its slots by increasing pair index visits experts
+  // ascending; the order is ranked once into LDS.
+  __shared__ int order[16];
+  __shared__ float wt[16];
+  __shared__ int nsel;
+  const int t = blockIdx.x;
+  if (t >= D.T) return;
   const int nu = clamp_nu(U.n_unique, D);
   const int tk = D.T * D.k;
-  float acc = residual[(size_t)t * D.d + r];
-  if (nu > 0) {
-    int pj[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) pj[j] = j < D.k ? U.pair_of[(size_t)t * D.k + j] : 0x7FFFFFFF;
-    int prev = -1;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      if (i < D.k) {
-        int best = 0x7FFFFFFF, bj = 0;
-#pragma unroll
-        for (int j = 0; j < 16; ++j)
-          if (pj[j] > prev && pj[j] < best) {
-            best = pj[j];
-            bj = j;
-          }
-        if (best < tk) acc = __builtin_fmaf(w[(size_t)t * D.k + bj], y[(size_t)best * D.d + r], acc);
-        prev = best;
-      }
+  if (threadIdx.x < 64) {
+    const int j = threadIdx.x;
+    int p = 0x7FFFFFFF;
+    if (nu > 0 && j < D.k) {
+      p = U.pair_of[(size_t)t * D.k + j];
+      if (p < 0 || p >= tk) p = 0x7FFFFFFF;
     }
+    int rank = 0, valid = 0;
+    for (int i = 0; i < D.k; ++i) {
+      const int q = __shfl(p, i, 64);
+      rank += (q < p) || (q == p && i < j);
+      valid += q < tk;
+    }
+    if (j < D.k && p < tk) {
+      order[rank] = p;
+      wt[rank] = w[(size_t)t * D.k + j];
+    }
+    if (j == 0) nsel = valid;
   }
-  if (D.n_shared) acc = acc + y[((size_t)tk + t) * D.d + r];
-  residual[(size_t)t * D.d + r] = acc;
+  __syncthreads();
+  const int n = nsel;
+  for (int r = threadIdx.x; r < D.d; r += blockDim.x) {
+    float acc = residual[(size_t)t * D.d + r];
+    for (int i = 0; i < n; ++i) acc = __builtin_fmaf(wt[i], y[(size_t)order[i] * D.d + r], acc);
+    if (D.n_shared) acc = acc + y[((size_t)tk + t) * D.d + r];
+    residual[(size_t)t * D.d + r] = acc;
+  }
 }
 
 // ------------------------------------------------------------------ rmsnorm
@@ -1233,17 +1305,6 @@ static int topk_per(int E) {
   return per <= 1 ? 1 : per <= 2 ? 2 : per <= 4 ? 4 : per <= 8 ? 8 : 16;
 }
 
-static bool steps_supported(int steps) {
-  return steps == 1 || steps == 2 || steps == 3 || steps == 4 || steps == 6 || steps == 8 || steps == 12 ||
-         steps == 16 || steps == 24 || steps == 32;
-}
-
-template <int S>
-static void router_gemv_launch(dim3 g, dim3 b, hipStream_t s, const LayerDev &L, const Dims &D, const float *x,
-                               float *logits) {
-  k_router_gemv<S><<<g, b, 0, s>>>(L, D, x, logits);
-}
-
 hipError_t launch_router_split(const LayerDev &L, const Dims &D, const float *x, float *logits, uint32_t *xq,
                                float *xs, hipStream_t s) {
   if (D.T <= 0) return hipSuccess;
@@ -1264,30 +1325,6 @@ hipError_t launch_topk_union1(const float *logits, const Dims &D, int32_t *idx, 
   return hipGetLastError();
 }
 
-hipError_t launch_router(const LayerDev &L, const Dims &D, const float *x, float *logits, hipStream_t s) {
-  if (D.T <= 0) return hipSuccess;
-  const int steps = (D.d + 255) / 256;
-  if (D.T <= 32 && steps_supported(steps)) {
-    dim3 g((D.E + 3) / 4), b(256);
-    switch (steps) {
-      case 1: router_gemv_launch<1>(g, b, s, L, D, x, logits); break;
-      case 2: router_gemv_launch<2>(g, b, s, L, D, x, logits); break;
-      case 3: router_gemv_launch<3>(g, b, s, L, D, x, logits); break;
-      case 4: router_gemv_launch<4>(g, b, s, L, D, x, logits); break;
-      case 6: router_gemv_launch<6>(g, b, s, L, D, x, logits); break;
-      case 8: router_gemv_launch<8>(g, b, s, L, D, x, logits); break;
-      case 12: router_gemv_launch<12>(g, b, s, L, D, x, logits); break;
-      case 16: router_gemv_launch<16>(g, b, s, L, D, x, logits); break;
-      case 24: router_gemv_launch<24>(g, b, s, L, D, x, logits); break;
-      default: router_gemv_launch<32>(g, b, s, L, D, x, logits); break;
-    }
-    return hipGetLastError();
-  }
-  dim3 g((D.T + 63) / 64, (D.E + 63) / 64), b(256);
-  k_router_gemm<<<g, b, 0, s>>>(L, D, x, logits);
-  return hipGetLastError();
-}
-
 hipError_t launch_topk(const float *logits, const Dims &D, int32_t *idx, float *w, hipStream_t s) {
   if (D.T <= 0) return hipSuccess;
   dim3 g((D.T + 3) / 4), b(256);
@@ -1302,7 +1339,14 @@ hipError_t launch_topk(const float *logits, const Dims &D, int32_t *idx, float *
 }
 
 hipError_t launch_union(const int32_t *idx, const Dims &D, const UnionDev &U, int32_t *err, hipStream_t s) {
-  k_union<<<1, 64, union_lds_bytes(D.E), s>>>(idx, D, U, err);
+  if (D.T > 256) {
+    // one wave per segment; LDS stays under 64 KB
+    int W = 16;
+    while (W > 1 && union_multi_lds_bytes(D.E, W) > 64 * 1024) W >>= 1;
+    k_union_multi<<<1, 64 * W, union_multi_lds_bytes(D.E, W), s>>>(idx, D, U, err);
+  } else {
+    k_union<<<1, 64, union_lds_bytes(D.E), s>>>(idx, D, U, err);
+  }
   return hipGetLastError();
 }
 
@@ -1482,8 +1526,7 @@ hipError_t launch_down_dec(const LayerDev &L, const Dims &D, const uint32_t *hq,
 hipError_t launch_combine(const Dims &D, const float *w, const UnionDev &U, const float *y, float *residual,
                           hipStream_t s) {
   if (D.T <= 0) return hipSuccess;
-  dim3 grid((D.d + 255) / 256, D.T), block(256);
-  k_combine<<<grid, block, 0, s>>>(D, w, U, y, residual);
+  k_combine<<<D.T, 256, 0, s>>>(D, w, U, y, residual);
   return hipGetLastError();
 }
 

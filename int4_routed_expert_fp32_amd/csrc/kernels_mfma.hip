@@ -17,13 +17,12 @@
 // feeds the down product, whose fp32 rows go to the combine kernel.
 //
 // Work decomposition.  An M-block is up to kMB = 128 consecutive rows (pairs)
-// of one expert; an item is (M-block, 128 weight rows).  A block of 4 waves
-// takes an item; wave w owns 32 weight rows and all M-tiles (32 rows each) of
-// the M-block that hold rows, with v_mfma_f32_32x32x16_bf16.  Lane (j, hh)
-// (j = lane % 32, hh = lane / 32) dequantises chunk 2g + hh of weight row j for
-// group g: its 4 words are the B operands of the 4 MFMAs of the group, the K
-// order inside a group permuted the same way for A, which reads 16 bytes of
-// activation row j at column 64g + 32hh + 8q for MFMA q.  Items are taken in
+// of one expert; an item is (M-block, kNT = 256 weight rows), taken by a block
+// of 4 waves with v_mfma_f32_32x32x16_bf16 (32 x 32 outputs, K = 16).  Lane
+// (j, hh) (j = lane % 32, hh = lane / 32) dequantises chunk 2g + hh of its
+// weight row for group g: the 4 words are the B operands of the group's 4
+// MFMAs, and A is read with the same K order inside the group (16 bytes of an
+// activation row at column 64g + 32hh + 8q for MFMA q).  Items are taken in
 // rounds; inside a round the 8 XCDs get contiguous ranges so that the weight
 // tiles of one M-block run on one XCD and share its L2 for the activation rows.
 #include <hip/hip_runtime.h>
@@ -36,6 +35,10 @@ namespace colimoe {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+// Plain LLVM vector for 16-byte loads: copies of it stay in registers (the
+// uint4 class type is copied through memory, which keeps staged data off
+// registers).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // bf16 of an fp32 value, round to nearest even (hardware conversion).
 __device__ __forceinline__ uint16_t bf16_bits(float v) {
@@ -61,7 +64,7 @@ __device__ __forceinline__ bf16x8 dequant8(uint32_t w, float s, float m8s) {
   return r;
 }
 
-__device__ __forceinline__ bf16x8 as_bf16x8(const uint4 &v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4 &v) { return __builtin_bit_cast(bf16x8, v); }
 
 // ------------------------------------------------------------- M-block list
 // One wave: for each slot (unique routed expert in union order, then the
@@ -129,11 +132,97 @@ __global__ __launch_bounds__(256) void k_gather_bf16(const float *__restrict__ x
 //         output hb [rows][f] = bf16(SiLU(g) * u).
 // down:   A = hb [rows][f], weights = down rows (d of them), output y [rows][d]
 //         fp32.
+// Block: 4 waves, item = (M-block of up to 128 rows, 256 weight rows); wave w
+// owns weight rows 64w..64w+63 of the item as two 32-column MFMA tiles, so
+// each A operand read from LDS feeds two MFMAs.  Per 64-wide K group the
+// block stages the M-block's A tile (128 rows x 128 bytes, rows padded to 144
+// bytes so the 16-byte reads of 16 consecutive lanes hit distinct banks) in
+// one of two LDS buffers while the other is consumed.  Loads run two groups
+// ahead (A into one of two register sets, weights and scales likewise), and
+// the barrier between groups waits only for LDS traffic, so loads stay in
+// flight across it.
+constexpr int kArowBytes = 144;
+constexpr int kAbuf = kMB * kArowBytes;  // bytes of one A stage
+
+// Barrier for the LDS ring: LDS writes of this wave complete, then s_barrier;
+// vector-memory loads issued earlier stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt left at their maximum
+  __builtin_amdgcn_s_barrier();
+}
+
+// 64 bytes of one A row staged in registers between its load and its LDS
+// store.  Loader threads past the M-block's last row read the block's first
+// row instead: output row i of an MFMA depends only on A row i, and rows past
+// the block are never stored.
+struct AStage {
+  u32x4 a0, a1, a2, a3;
+  __device__ __forceinline__ void load(const u32x4 *src) {
+    a0 = src[0];
+    a1 = src[1];
+    a2 = src[2];
+    a3 = src[3];
+  }
+  __device__ __forceinline__ void store(unsigned char *dst) const {
+    *(u32x4 *)(dst) = a0;
+    *(u32x4 *)(dst + 16) = a1;
+    *(u32x4 *)(dst + 32) = a2;
+    *(u32x4 *)(dst + 48) = a3;
+  }
+};
+
+struct WStage {
+  u32x4 w0, w1;  // chunk of weight rows gr0 and gr0 + 32
+  float s0, s1;  // their group scales
+};
+
 template <bool GATEUP>
-__global__ __launch_bounds__(256) void k_gemm_mfma(LayerDev L, Dims D, const uint16_t *__restrict__ A,
-                                                   const int4 *__restrict__ list, const int32_t *__restrict__ count,
-                                                   int max_entries, uint16_t *__restrict__ hb,
-                                                   float *__restrict__ y) {
+struct GemmItem {
+  const uint8_t *nib;
+  const uint16_t *sc0, *sc1;
+  int tile0, tile1, r, K;
+  bool wact;
+  __device__ __forceinline__ void load(int g, WStage &st) const {
+    st.w0 = *(const u32x4 *)(nib + chunk_offset(tile0, K, 2 * g + (threadIdx.x >> 5 & 1), r));
+    st.w1 = *(const u32x4 *)(nib + chunk_offset(tile1, K, 2 * g + (threadIdx.x >> 5 & 1), r));
+    st.s0 = (float)__builtin_bit_cast(_Float16, sc0[(size_t)g * 8]);
+    st.s1 = (float)__builtin_bit_cast(_Float16, sc1[(size_t)g * 8]);
+  }
+};
+
+// One K group: dequantise the lane's two weight chunks and run the MFMAs of
+// the M-tiles that hold rows.  Done in two halves of K (MFMAs 0-1, then 2-3)
+// so only half of the B and A operands are live at a time.
+template <int NMT_MAX>
+__device__ __forceinline__ void gemm_group(const unsigned char *cur, const WStage &st, int nmt, int j, int hh,
+                                           f32x16 (&acc)[4][2]) {
+  const float m0 = -8.0f * st.s0, m1 = -8.0f * st.s1;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const bf16x8 b00 = dequant8(st.w0[2 * half], st.s0, m0);
+    const bf16x8 b01 = dequant8(st.w0[2 * half + 1], st.s0, m0);
+    const bf16x8 b10 = dequant8(st.w1[2 * half], st.s1, m1);
+    const bf16x8 b11 = dequant8(st.w1[2 * half + 1], st.s1, m1);
+#pragma unroll
+    for (int mt = 0; mt < NMT_MAX; ++mt) {
+      if (mt < nmt) {
+        const unsigned char *ar = cur + (32 * mt + j) * kArowBytes + 64 * hh + 32 * half;
+        const u32x4 a0 = *(const u32x4 *)(ar), a1 = *(const u32x4 *)(ar + 16);
+        acc[mt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a0), b00, acc[mt][0], 0, 0, 0);
+        acc[mt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a0), b10, acc[mt][1], 0, 0, 0);
+        acc[mt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a1), b01, acc[mt][0], 0, 0, 0);
+        acc[mt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a1), b11, acc[mt][1], 0, 0, 0);
+      }
+    }
+  }
+}
+
+template <bool GATEUP>
+__global__ __launch_bounds__(256, 2) void k_gemm_mfma(LayerDev L, Dims D, const uint16_t *__restrict__ A,
+                                                      const int4 *__restrict__ list,
+                                                      const int32_t *__restrict__ count, int max_entries,
+                                                      uint16_t *__restrict__ hb, float *__restrict__ y) {
+  __shared__ __align__(16) unsigned char As[2 * kAbuf];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int j = lane & 31, hh = lane >> 5;
   const int K = GATEUP ? D.d : D.f;
@@ -146,78 +235,95 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(LayerDev L, Dims D, const uin
   const int items = nmb * ntiles;
   const int per_xcd = gridDim.x >> 3;  // gridDim.x is a multiple of 8
   const int slot_in_round = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  // A loader role of this thread: row t/2, bytes 64*(t%2) .. +64 of the group
+  const int lrow = threadIdx.x >> 1, lhalf = threadIdx.x & 1;
   for (int base = 0; base < items; base += gridDim.x) {
     const int item = base + slot_in_round;
-    if (item >= items) continue;
+    if (item >= items) continue;  // block-uniform
     const int mb = item / ntiles, nt = item - mb * ntiles;
     const int4 ent = list[mb];
     const int e = ent.x, row0 = ent.y, rc = ent.z;
-    if (32 * wave + nt * kNT >= nrows) continue;  // whole wave past the last weight row
-    const int gr = nt * kNT + 32 * wave + j;        // weight row of this lane
-    const int tile = gr >> 3, r = gr & 7;
-    const uint8_t *base_e = L.experts + (size_t)e * L.expert_stride;
-    const uint8_t *nib = base_e + (GATEUP ? EL.gu_nib : EL.dn_nib);
-    const uint16_t *sc = (const uint16_t *)(base_e + (GATEUP ? EL.gu_sc : EL.dn_sc)) + (size_t)tile * G * 8 + r;
     const int nmt = (rc + 31) >> 5;  // M-tiles holding rows (1..4)
-    const uint16_t *arow[4];
-    bool aok[4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      const int rr = 32 * mt + j;
-      aok[mt] = rr < rc;
-      arow[mt] = A + (size_t)(row0 + (aok[mt] ? rr : 0)) * K + 32 * hh;
-    }
-    f32x16 acc[4];
+    GemmItem<GATEUP> it;
+    // weight rows come in multiples of 64; a wave past the last one computes
+    // on row 0's weights (valid memory) and stores nothing
+    it.wact = nt * kNT + 64 * wave < nrows;
+    const int gr0 = it.wact ? nt * kNT + 64 * wave + j : j;
+    it.tile0 = gr0 >> 3;
+    it.tile1 = (gr0 + 32) >> 3;
+    it.r = gr0 & 7;
+    it.K = K;
+    const uint8_t *base_e = L.experts + (size_t)e * L.expert_stride;
+    it.nib = base_e + (GATEUP ? EL.gu_nib : EL.dn_nib);
+    const uint16_t *scb = (const uint16_t *)(base_e + (GATEUP ? EL.gu_sc : EL.dn_sc));
+    it.sc0 = scb + (size_t)it.tile0 * G * 8 + it.r;
+    it.sc1 = scb + (size_t)it.tile1 * G * 8 + it.r;
+    const bool lok = lrow < rc;
+    const u32x4 *asrc = (const u32x4 *)(A + (size_t)(row0 + (lok ? lrow : 0)) * K + 32 * lhalf);
+    unsigned char *adst = As + lrow * kArowBytes + 64 * lhalf;
+
+    f32x16 acc[4][2];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[mt][v] = 0.0f;
+      for (int n = 0; n < 2; ++n)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[mt][n][v] = 0.0f;
 
-    uint4 Wn = *(const uint4 *)(nib + chunk_offset(tile, K, hh, r));
-    float sn = (float)__builtin_bit_cast(_Float16, sc[0]);
-    for (int g = 0; g < G; ++g) {
-      const uint4 W = Wn;
-      const float s = sn;
-      if (g + 1 < G) {
-        Wn = *(const uint4 *)(nib + chunk_offset(tile, K, 2 * (g + 1) + hh, r));
-        sn = (float)__builtin_bit_cast(_Float16, sc[(size_t)(g + 1) * 8]);
-      }
-      const float m8s = -8.0f * s;
-      const bf16x8 b0 = dequant8(W.x, s, m8s), b1 = dequant8(W.y, s, m8s);
-      const bf16x8 b2 = dequant8(W.z, s, m8s), b3 = dequant8(W.w, s, m8s);
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        if (mt < nmt) {
-          uint4 a[4];
-          const uint4 *ap = (const uint4 *)(arow[mt] + 64 * g);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) a[q] = aok[mt] ? ap[q] : make_uint4(0u, 0u, 0u, 0u);
-          acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[0]), b0, acc[mt], 0, 0, 0);
-          acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[1]), b1, acc[mt], 0, 0, 0);
-          acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[2]), b2, acc[mt], 0, 0, 0);
-          acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[3]), b3, acc[mt], 0, 0, 0);
-        }
-      }
+    // Prologue: A(0) into LDS buffer 0; A(1), W(0) and W(1) in flight.  The
+    // loop below loads unconditionally (group indices clamped to G - 1, a
+    // redundant but valid load at the tail) so the compiler can count
+    // outstanding loads exactly and wait only for the ones it consumes.
+    const int G1 = G - 1;
+    AStage rA, rB;
+    rA.load(asrc);
+    rA.store(adst);
+    rB.load(asrc + 8 * min(1, G1));
+    WStage sE, sO;
+    it.load(0, sE);
+    it.load(min(1, G1), sO);
+    lds_barrier();
+    // groups in pairs: even groups use LDS buffer 0 and register sets rA / sE
+    for (int g = 0; g < G; g += 2) {
+      // ---- even group g: A(g+1) is in rB, A(g+2) goes to rA
+      rA.load(asrc + 8 * min(g + 2, G1));
+      gemm_group<4>(As, sE, nmt, j, hh, acc);
+      it.load(min(g + 2, G1), sE);
+      rB.store(adst + kAbuf);
+      lds_barrier();
+      if (g + 1 >= G) break;
+      // ---- odd group g+1: A(g+2) is in rA, A(g+3) goes to rB
+      rB.load(asrc + 8 * min(g + 3, G1));
+      gemm_group<4>(As + kAbuf, sO, nmt, j, hh, acc);
+      it.load(min(g + 3, G1), sO);
+      rA.store(adst);
+      lds_barrier();
     }
 
     // Epilogue.  Accumulator element v of lane (j, hh) is row 8(v/4) + 4hh + v%4
-    // of the M-tile, column j (weight row gr).
+    // of the M-tile, column j of the 32-column tile.
+    if (it.wact) {
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      if (mt < nmt) {
+      for (int mt = 0; mt < 4; ++mt) {
+        if (mt < nmt) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int rr = 32 * mt + 8 * (v >> 2) + 4 * hh + (v & 3);
-          const float val = acc[mt][v];
-          if (GATEUP) {
-            // tile rows 0-3 are gate rows, 4-7 the up rows of the same features
-            const float up = __shfl_down(val, 4, 64);
-            if ((j & 7) < 4 && rr < rc) {
-              const int feat = 4 * tile + (j & 3);
-              hb[(size_t)(row0 + rr) * D.f + feat] = bf16_bits(silu_f(val) * up);
+          for (int n = 0; n < 2; ++n) {
+            const int gr = gr0 + 32 * n;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const int rr = 32 * mt + 8 * (v >> 2) + 4 * hh + (v & 3);
+              const float val = acc[mt][n][v];
+              if (GATEUP) {
+                // tile rows 0-3 are gate rows, 4-7 the up rows of the same features
+                const float up = __shfl_down(val, 4, 64);
+                if ((j & 7) < 4 && rr < rc) {
+                  const int feat = 4 * (gr >> 3) + (j & 3);
+                  hb[(size_t)(row0 + rr) * D.f + feat] = bf16_bits(silu_f(val) * up);
+                }
+              } else {
+                if (rr < rc) y[(size_t)(row0 + rr) * D.d + gr] = val;
+              }
             }
-          } else {
-            if (rr < rc) y[(size_t)(row0 + rr) * D.d + gr] = val;
           }
         }
       }
@@ -225,7 +331,89 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(LayerDev L, Dims D, const uin
   }
 }
 
+// ----------------------------------------------------- router, many tokens
+// A1 for many tokens: logits = x R^T + b in fp32 on the matrix cores
+// (v_mfma_f32_32x32x2_f32).  Block: 64 tokens x 64 experts over one of S
+// K-slices of d (4 waves, 32 x 32 each), K staged in LDS 32 columns at a
+// time; slices write fp32 partials that k_router_reduce sums in slice order
+// and adds the bias to.  A logit depends only on its token's row, so the
+// result does not depend on which other tokens share the call.
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+__global__ __launch_bounds__(256) void k_router_mfma(LayerDev L, Dims D, const float *__restrict__ x,
+                                                     float *__restrict__ part, int S) {
+  __shared__ float xs[64][33];
+  __shared__ float rs[64][33];
+  const int t0 = blockIdx.x * 64, e0 = blockIdx.y * 64, ks = blockIdx.z;
+  const int Kc = D.d / S, kbeg = ks * Kc;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wt = wave >> 1, we = wave & 1, i = lane & 31, kh = lane >> 5;
+  const int lr = threadIdx.x >> 2, lc = (threadIdx.x & 3) * 8;  // loader: row, first of 8 columns
+  const int lt = t0 + lr, le = e0 + lr;
+  const float *xrow = x + (size_t)(lt < D.T ? lt : 0) * D.d;
+  const float *rrow = L.router + (size_t)(le < D.E ? le : 0) * D.d;
+  f32x16_t acc;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
+  for (int k0 = kbeg; k0 < kbeg + Kc; k0 += 32) {
+    float4 x0 = make_float4(0.f, 0.f, 0.f, 0.f), x1 = x0, r0 = x0, r1 = x0;
+    if (lt < D.T) {
+      x0 = *(const float4 *)(xrow + k0 + lc);
+      x1 = *(const float4 *)(xrow + k0 + lc + 4);
+    }
+    if (le < D.E) {
+      r0 = *(const float4 *)(rrow + k0 + lc);
+      r1 = *(const float4 *)(rrow + k0 + lc + 4);
+    }
+    float *xd = &xs[lr][lc], *rd = &rs[lr][lc];
+    xd[0] = x0.x; xd[1] = x0.y; xd[2] = x0.z; xd[3] = x0.w;
+    xd[4] = x1.x; xd[5] = x1.y; xd[6] = x1.z; xd[7] = x1.w;
+    rd[0] = r0.x; rd[1] = r0.y; rd[2] = r0.z; rd[3] = r0.w;
+    rd[4] = r1.x; rd[5] = r1.y; rd[6] = r1.z; rd[7] = r1.w;
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk)
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(xs[32 * wt + i][2 * kk + kh], rs[32 * we + i][2 * kk + kh], acc, 0, 0,
+                                                0);
+    __syncthreads();
+  }
+  // element v of lane (i, kh): token row 8(v/4) + 4kh + v%4 of the wave tile, expert column i
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int tt = t0 + 32 * wt + 8 * (v >> 2) + 4 * kh + (v & 3), ee = e0 + 32 * we + i;
+    if (tt < D.T && ee < D.E) part[((size_t)ks * D.T + tt) * D.E + ee] = acc[v];
+  }
+}
+
+__global__ __launch_bounds__(256) void k_router_reduce(const float *__restrict__ part, int S, LayerDev L, Dims D,
+                                                       float *__restrict__ logits) {
+  const size_t n = (size_t)D.T * D.E;
+  for (size_t o = (size_t)blockIdx.x * 256 + threadIdx.x; o < n; o += (size_t)gridDim.x * 256) {
+    float sum = part[o];
+    for (int ks = 1; ks < S; ++ks) sum = sum + part[(size_t)ks * n + o];
+    logits[o] = sum + L.bias[o % D.E];
+  }
+}
+
 // ---------------------------------------------------------------- launchers
+
+int router_splits(int d) {
+  for (int S = 8; S > 1; S >>= 1)
+    if (d % (32 * S) == 0) return S;
+  return 1;
+}
+
+hipError_t launch_router_mfma(const LayerDev &L, const Dims &D, const float *x, float *part, float *logits,
+                              hipStream_t s) {
+  if (D.T <= 0) return hipSuccess;
+  const int S = router_splits(D.d);
+  dim3 g((D.T + 63) / 64, (D.E + 63) / 64, S);
+  k_router_mfma<<<g, 256, 0, s>>>(L, D, x, part, S);
+  const size_t n = (size_t)D.T * D.E;
+  k_router_reduce<<<(int)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096), 256, 0, s>>>(part, S, L, D, logits);
+  return hipGetLastError();
+}
+
 
 int mfma_max_entries(int T, int k, int E, int n_shared) {
   const int tk = T * k;
@@ -250,7 +438,7 @@ hipError_t launch_gather_bf16(const float *x, const Dims &D, const UnionDev &U, 
 // Blocks of the persistent grid: a multiple of 8 (one share per XCD).
 static int mfma_grid(int max_entries, int ntiles) {
   const long items = (long)max_entries * ntiles;
-  long g = 1024;
+  long g = 512;  // two blocks per CU
   if (items < g) g = (items + 7) / 8 * 8;
   return (int)(g < 8 ? 8 : g);
 }
