@@ -64,11 +64,18 @@ enum colimoe_status {
 
 /* Forward path selection. */
 enum colimoe_forward_flags {
-  COLIMOE_FWD_AUTO = 0,      /* the fixed-point activation path when d >= 2048 and
-                                f >= 2048, else the fp32 dequant path */
+  COLIMOE_FWD_AUTO = 0,      /* BF16_MFMA for prefill-shaped calls (T*k >= 64*E,
+                                on average 64 tokens per expert); otherwise FXP
+                                when d >= 2048 and f >= 2048, else FP32 */
   COLIMOE_FWD_FP32 = 1,      /* int4 weights dequantised to fp32, fp32 FMA, fp32
                                 accumulation ([D] §4, highlight 4) */
-  COLIMOE_FWD_BF16_MFMA = 2, /* bf16 MFMA grouped GEMM (not built: E_ARG) */
+  COLIMOE_FWD_BF16_MFMA = 2, /* grouped GEMM on the matrix cores for many tokens
+                                per expert ([D] §4, highlight 4: the int4 kernel
+                                pays off on batches): tokens grouped by expert
+                                through the union lists; weights dequantised to
+                                bf16 as bf16(q*s), x and SiLU(g)*u rounded to
+                                bf16 (round to nearest even), fp32 accumulation;
+                                down outputs combined in fp32.  Any shape */
   COLIMOE_FWD_FXP = 3,       /* fixed-point activations: every 16 activations are
                                 encoded as 23-bit integers with one power-of-two
                                 scale (error <= 2^-22 of the group's largest
@@ -185,7 +192,8 @@ COLIMOE_API int colimoe_route_forward(colimoe_ctx *ctx, int32_t layer, const flo
                           const colimoe_union *u, float *residual, uint32_t flags);
 
 /* x_out[t] = r[t] / sqrt(mean(r[t]^2) + eps), unit weight, fp32 (device
- * pointers, [T][d]); lets a stack of layers run without leaving the GPU. */
+ * pointers, [T][d], 16-byte aligned); lets a stack of layers run without
+ * leaving the GPU.  Errors: E_ARG, E_SHAPE, E_HIP. */
 COLIMOE_API int colimoe_rmsnorm(colimoe_ctx *ctx, const float *r, int32_t T, float eps, float *x_out);
 
 /* One expert on one token through the fp32 path, every stage exposed
@@ -196,10 +204,12 @@ COLIMOE_API int colimoe_debug_expert(colimoe_ctx *ctx, int32_t layer, int32_t e,
 
 /* Per-kernel timing for measurement.  While enabled, every kernel launch of
  * the context is bracketed by a pair of HIP events on its stream (this adds
- * two event records per launch).  Kernel names: "route" (router, fused with
- * top-k and union when T <= 16), "topk", "union", "encode" (fixed-point
- * encoding of x), "gateup", "down" (with the combine when it fits in LDS),
- * "combine", "rmsnorm". */
+ * two event records per launch).  Kernel names: "route" (router; in
+ * colimoe_route_forward with T <= 16 it also encodes x), "topk" (top-k; with
+ * the union lists when T == 1), "union", "encode" (fixed-point encoding of x,
+ * or the M-block list and bf16 gather of the MFMA path), "gateup", "down"
+ * (with the combine when T == 1 or when it fits in LDS), "combine",
+ * "rmsnorm". */
 COLIMOE_API int colimoe_timing_enable(colimoe_ctx *ctx, int enable);
 
 /* Synchronises the stream, then reports the summed duration (ms) and the

@@ -378,14 +378,19 @@ static int forward_impl(colimoe_ctx *ctx, int32_t layer, const float *x, int32_t
       KTimer kt(ctx, K_ENCODE);
       if (launch_xquant(x, T, D.d, xq, xs, s) != hipSuccess) return COLIMOE_E_HIP;
     }
-    {
-      KTimer kt(ctx, K_GATEUP);
-      if (launch_gateup_fxp(L, D, xq, xs, U, h, hq, hs, nullptr, nullptr, s) != hipSuccess) return COLIMOE_E_HIP;
-    }
-    if (T == 1) {
+    if (T == 1 && dec_supported(D)) {
+      {
+        KTimer kt(ctx, K_GATEUP);
+        if (launch_gateup_dec(L, D, nullptr, nullptr, nullptr, U, xq, xs, hq, hs, s) != hipSuccess)
+          return COLIMOE_E_HIP;
+      }
       KTimer kt(ctx, K_DOWN);
       if (launch_down_dec(L, D, hq, hs, U, w, residual, s) != hipSuccess) return COLIMOE_E_HIP;
       return COLIMOE_OK;  // combine done in the kernel
+    }
+    {
+      KTimer kt(ctx, K_GATEUP);
+      if (launch_gateup_fxp(L, D, xq, xs, U, h, hq, hs, nullptr, nullptr, s) != hipSuccess) return COLIMOE_E_HIP;
     }
     {
       KTimer kt(ctx, K_DOWN);
@@ -610,6 +615,29 @@ int colimoe_route_forward(colimoe_ctx *ctx, int32_t layer, const float *x, int32
   const colimoe_union uw = ws_union_abi(ctx);
   const colimoe_union *uu = u ? u : &uw;
   const bool encode = path == PATH_FXP;
+  const Dims D = dims_of(ctx, T);
+  if (T == 1 && encode && dec_supported(D)) {
+    // one token: router (+ encoding of x), gate/up with the top-k and union
+    // lists folded in, down with the combine folded in
+    const LayerDev L = layer_of(ctx, layer);
+    hipStream_t s = ctx->stream;
+    float *lg = (float *)(ctx->ws + ctx->wl.logits);
+    uint32_t *xq = (uint32_t *)(ctx->ws + ctx->wl.xq);
+    float *xs = (float *)(ctx->ws + ctx->wl.xs);
+    uint32_t *hq = (uint32_t *)(ctx->ws + ctx->wl.hq);
+    float *hs = (float *)(ctx->ws + ctx->wl.hs);
+    const UnionDev U = to_dev(uu);
+    {
+      KTimer kt(ctx, K_ROUTE);
+      if (launch_router_split(L, D, x, lg, xq, xs, s) != hipSuccess) return COLIMOE_E_HIP;
+    }
+    {
+      KTimer kt(ctx, K_GATEUP);
+      if (launch_gateup_dec(L, D, lg, idx, w, U, xq, xs, hq, hs, s) != hipSuccess) return COLIMOE_E_HIP;
+    }
+    KTimer kt(ctx, K_DOWN);
+    return hip_status(launch_down_dec(L, D, hq, hs, U, w, residual, s));
+  }
   rc = route_impl(ctx, layer, x, T, idx, w, uu, nullptr, encode);
   if (rc) return rc;
   return forward_impl(ctx, layer, x, T, idx, w, uu, residual, path, encode && T <= kRouteSplitMaxT);
@@ -620,7 +648,7 @@ int colimoe_rmsnorm(colimoe_ctx *ctx, const float *r, int32_t T, float eps, floa
   if (T < 0 || T > ctx->cfg.max_tokens) return COLIMOE_E_SHAPE;
   if (!(eps >= 0.0f)) return COLIMOE_E_ARG;
   if (T == 0) return COLIMOE_OK;
-  if (!r || !x_out || !aligned(r, 4) || !aligned(x_out, 4)) return COLIMOE_E_ARG;
+  if (!r || !x_out || !aligned(r, 16) || !aligned(x_out, 16)) return COLIMOE_E_ARG;
   KTimer kt(ctx, K_RMSNORM);
   return hip_status(launch_rmsnorm(r, T, ctx->cfg.d, eps, x_out, ctx->stream));
 }

@@ -124,7 +124,16 @@ hipError_t launch_gateup_fxp(const LayerDev &L, const Dims &D, const uint32_t *x
                              hipStream_t s);
 hipError_t launch_down_fxp(const LayerDev &L, const Dims &D, const uint32_t *hq, const float *hs, const UnionDev &U,
                            float *y, const float *w, float *residual, bool fused, hipStream_t s);
-// Down + combine for one token, one wave per output tile (T == 1).
+// The one-token kernels below need f % 32 == 0 (always true: f % 64 == 0) and
+// at most 17 slots (k + shared).
+inline bool dec_supported(const Dims &D) { return D.T == 1 && D.k + D.n_shared <= 17 && D.f % 32 == 0; }
+// Gate/up for one token with x's fixed-point encoding staged in LDS.  With
+// logits non-null the kernel also selects the top-k (writing idx, w and the
+// union lists U); otherwise it reads the routing from U.
+hipError_t launch_gateup_dec(const LayerDev &L, const Dims &D, const float *logits, int32_t *idx, float *w,
+                             const UnionDev &U, const uint32_t *xq, const float *xs, uint32_t *hq, float *hs,
+                             hipStream_t s);
+// Down + combine for one token, three waves per output tile (T == 1).
 hipError_t launch_down_dec(const LayerDev &L, const Dims &D, const uint32_t *hq, const float *hs, const UnionDev &U,
                            const float *w, float *residual, hipStream_t s);
 // Router for many tokens on the matrix cores (fp32), with S = router_splits(d)

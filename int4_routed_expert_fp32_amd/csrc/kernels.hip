@@ -157,8 +157,8 @@ __device__ __forceinline__ uint64_t topk_key(float v, int e) {
   return ((uint64_t)ord << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
 }
 
-// Selects for one token; lane 0 writes idx and w (and the ids to `lds_ids`
-// if given).  Every valid key is nonzero, so k <= E rounds always find one.
+// Selects for one token; lane 0 writes idx and w (each if non-null) and the
+// ids to `lds_ids` (if given).  Every valid key is nonzero, so k <= E rounds always find one.
 template <int PER>
 __device__ __forceinline__ void topk_token(const float *__restrict__ l, const Dims &D, int t,
                                            int32_t *__restrict__ idx, float *__restrict__ wout, int32_t *lds_ids) {
@@ -195,8 +195,8 @@ __device__ __forceinline__ void topk_token(const float *__restrict__ l, const Di
 #pragma unroll
     for (int j = 0; j < 16; ++j)
       if (j < D.k) {
-        idx[(size_t)t * D.k + j] = ids[j];
-        wout[(size_t)t * D.k + j] = expf(vals[j] - m) / sum;
+        if (idx) idx[(size_t)t * D.k + j] = ids[j];
+        if (wout) wout[(size_t)t * D.k + j] = expf(vals[j] - m) / sum;
         if (lds_ids) lds_ids[t * D.k + j] = ids[j];
       }
   }
@@ -986,18 +986,11 @@ __global__ __launch_bounds__(256) void k_router_split(LayerDev L, Dims D, const 
         ((part[threadIdx.x][0] + part[threadIdx.x][1]) + part[threadIdx.x][2]) + part[threadIdx.x][3] + L.bias[e];
 }
 
-// Top-k of one token plus its union lists (its ids sorted ascending).
-template <int PER>
-__global__ __launch_bounds__(64) void k_topk_union1(const float *__restrict__ logits, Dims D,
-                                                    int32_t *__restrict__ idx, float *__restrict__ wout, UnionDev U,
-                                                    int with_union) {
-  __shared__ int32_t ids[16];
-  topk_token<PER>(logits, D, 0, idx, wout, ids);
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-  const int j = threadIdx.x;
-  if (with_union && j < D.k) {
+// Union lists of one token from its k distinct expert ids (in LDS): the ids
+// ascending, one pair each, pair_slot = the id's position in the top-k.
+__device__ __forceinline__ void union_one_token(const int32_t *ids, const Dims &D, const UnionDev &U) {
+  const int j = threadIdx.x & 63;
+  if (j < D.k) {
     const int e = ids[j];
     int rank = 0;
     for (int i = 0; i < D.k; ++i) rank += ids[i] < e;
@@ -1010,6 +1003,147 @@ __global__ __launch_bounds__(64) void k_topk_union1(const float *__restrict__ lo
       *U.n_unique = D.k;
       U.offsets[D.k] = D.k;
     }
+  }
+}
+
+// Top-k of one token plus its union lists.
+template <int PER>
+__global__ __launch_bounds__(64) void k_topk_union1(const float *__restrict__ logits, Dims D,
+                                                    int32_t *__restrict__ idx, float *__restrict__ wout, UnionDev U,
+                                                    int with_union) {
+  __shared__ int32_t ids[16];
+  topk_token<PER>(logits, D, 0, idx, wout, ids);
+  wave_lds_sync();
+  if (with_union) union_one_token(ids, D, U);
+}
+
+// Gate/up for one token.  A block owns 32 consecutive h rows (8 tiles, two
+// 16-row encoding groups) of one slot; wave w streams tiles 2w and 2w+1 with
+// the next step's weights in flight; the block's copy of x's digit words
+// sits in LDS.  With TOPK the block first finds its expert from the logits
+// (top-k in wave 0; slot s < k is the s-th smallest selected id, slot k the
+// shared expert) and block 0 writes idx, w and the union lists.  Per row the
+// operations are those of k_gateup_fxp, so h and its encoding are identical.
+template <bool TOPK, int PER>
+__global__ __launch_bounds__(256) void k_gateup_dec(LayerDev L, Dims D, const float *__restrict__ logits,
+                                                    int32_t *__restrict__ idx, float *__restrict__ wout, UnionDev U,
+                                                    const uint32_t *__restrict__ xq, const float *__restrict__ xs,
+                                                    uint32_t *__restrict__ hq, float *__restrict__ hs) {
+  extern __shared__ __align__(16) uint32_t xlds[];  // [C][24] digit words, then [C][2] fp32 scales
+  __shared__ int32_t ids_s[16];
+  __shared__ int slot_s[2];  // expert, output row
+  __shared__ float hv[32];
+  __shared__ uint32_t hw[2][12];
+  __shared__ float hsc[2];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int C = D.d / kChunk, nsteps = (C + 63) / 64;
+  const int bps = D.f / 32;
+  const int s = blockIdx.x / bps, qb = blockIdx.x - s * bps;
+  float *xsl = (float *)(xlds + (size_t)C * kDigitWords);
+  for (int i = threadIdx.x; i < C * kDigitWords / 4; i += 256) ((uint4 *)xlds)[i] = ((const uint4 *)xq)[i];
+  for (int i = threadIdx.x; i < 2 * C; i += 256) xsl[i] = xs[i];
+  if (threadIdx.x < 24) hw[threadIdx.x / 12][threadIdx.x % 12] = 0u;
+  if (TOPK) {
+    if (s < D.k) {
+      if (wave == 0) {
+        topk_token<PER>(logits, D, 0, blockIdx.x == 0 ? idx : nullptr, blockIdx.x == 0 ? wout : nullptr, ids_s);
+        wave_lds_sync();
+        if (blockIdx.x == 0) union_one_token(ids_s, D, U);
+        if (lane < D.k) {
+          const int e = ids_s[lane];
+          int rank = 0;
+          for (int i = 0; i < D.k; ++i) rank += ids_s[i] < e;
+          if (rank == s) {
+            slot_s[0] = e;
+            slot_s[1] = s;
+          }
+        }
+      }
+    } else if (threadIdx.x == 0) {
+      slot_s[0] = (s == D.k && D.n_shared) ? D.E : -1;
+      slot_s[1] = D.k;
+    }
+  } else if (threadIdx.x == 0) {
+    const int nu = clamp_nu(U.n_unique, D);
+    int e = -1, p0 = 0, p1 = 0;
+    if (s < nu || (s == nu && D.n_shared)) {
+      if (!resolve_slot(D, U, nu, s, e, p0, p1) || p1 <= p0) e = -1;
+    }
+    slot_s[0] = e;
+    slot_s[1] = s < nu ? p0 : D.k;
+  }
+  __syncthreads();
+  const int e = slot_s[0], orow = slot_s[1];
+  if (e < 0) return;  // block-uniform
+  const ExpertLayout EL = expert_layout(D.d, D.f);
+  const uint8_t *base = L.experts + (size_t)e * L.expert_stride;
+  const uint8_t *nib = base + EL.gu_nib, *scp = base + EL.gu_sc;
+  const int ti0 = qb * 8 + 2 * wave;
+  const int nunits = 2 * nsteps;
+  uint4 W[2][kTileRows], S[2];
+  float acc[kTileRows];
+#pragma unroll
+  for (int r = 0; r < kTileRows; ++r) acc[r] = 0.0f;
+  if (lane < C) load_step(nib, scp, ti0, D.d, lane, W[0], S[0]);
+  for (int u0 = 0; u0 < nunits; u0 += 2) {
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int u = u0 + half;
+      if (u + 1 < nunits) {
+        const int c1 = lane + 64 * ((u + 1) % nsteps);
+        if (c1 < C) load_step(nib, scp, ti0 + (u + 1) / nsteps, D.d, c1, W[half ^ 1], S[half ^ 1]);
+      }
+      const int j = u % nsteps, c = lane + 64 * j;
+      if (c < C) {
+        uint32_t dg[kDigitWords];
+        const uint4 *src = (const uint4 *)(xlds + (size_t)c * kDigitWords);
+#pragma unroll
+        for (int i = 0; i < kDigitWords / 4; ++i) {
+          const uint4 v = src[i];
+          dg[4 * i] = v.x;
+          dg[4 * i + 1] = v.y;
+          dg[4 * i + 2] = v.z;
+          dg[4 * i + 3] = v.w;
+        }
+        const float xsc[2] = {xsl[2 * c], xsl[2 * c + 1]};
+#pragma unroll
+        for (int r = 0; r < kTileRows; ++r)
+          acc[r] = fxp_chunk(W[half][r], dg, xsc, tile_scale(S[half], r), acc[r]);
+      }
+      if (j == nsteps - 1) {
+        const float v = reduce8_rows(acc);
+        const float up = bits_f(xor32(f_bits(v)));  // up rows sit 32 lanes above their gate rows
+        const int r = lane >> 3;
+        if ((lane & 7) == 7 && r < 4) hv[(2 * wave + u / nsteps) * 4 + r] = silu_f(v) * up;
+#pragma unroll
+        for (int rr = 0; rr < kTileRows; ++rr) acc[rr] = 0.0f;
+      }
+    }
+  }
+  __syncthreads();
+  // encode the two 16-row groups (one 16-lane row each), as k_gateup_fxp does
+  if (threadIdx.x < 32) {
+    const int g = threadIdx.x >> 4, i = threadIdx.x & 15;
+    const float v = hv[16 * g + i];
+    uint32_t mb = f_bits(fabsf(v));
+    mb = max(mb, dpp<kRowRor8>(mb));
+    mb = max(mb, dpp<kRowRor4>(mb));
+    mb = max(mb, dpp<kRowRor2>(mb));
+    mb = max(mb, dpp<kRowRor1>(mb));
+    const float mx = bits_f(mb);
+    int E = mx > 0.0f ? ilogbf(mx) + 1 : 0;
+    E = E < -100 ? -100 : E;
+    const uint32_t B = (uint32_t)((int)__builtin_rintf(v * ldexpf(1.0f, 22 - E)) + 0x888888);
+#pragma unroll
+    for (int k = 0; k < 6; ++k) atomicOr(&hw[g][2 * k + (i >> 3)], (((B >> (4 * k)) & 15u) ^ 8u) << (4 * (i & 7)));
+    if (i == 0) hsc[g] = ldexpf(1.0f, E - 22);
+  }
+  __syncthreads();
+  if (threadIdx.x < 24) {
+    const int g = threadIdx.x / 12, wd = threadIdx.x % 12;
+    const int qd = 2 * qb + g;
+    hq[((size_t)orow * (D.f / kChunk) + (qd >> 1)) * kDigitWords + (qd & 1) * 12 + wd] = hw[g][wd];
+    if (wd == 0) hs[(size_t)orow * (D.f / 16) + qd] = hsc[g];
   }
 }
 
@@ -1027,63 +1161,74 @@ __device__ __forceinline__ void dec_down_slot(const LayerDev &L, const Dims &D, 
   load_digits(hq, hs, s < nu ? p0 : D.T * D.k, D.f, c, dg, dsc);
 }
 
-// Down + combine, T == 1, one wave per 8-row output tile: the wave streams
-// every slot's steps (next step's weights and digits in flight) and folds
-// each slot's y into the residual in registers, routed experts in ascending
-// id (slot order) weighted by w, then the shared expert.
+// Down + combine for one token.  A block of 3 waves owns one 8-row output
+// tile; wave w streams slots w, w+3, ... (next step's weights and digits in
+// flight) and leaves each slot's 8 outputs in LDS; wave 0 then folds them
+// into the residual in slot order: routed experts by ascending id weighted by
+// w, then the shared expert, as the general kernels do.
+constexpr int kDecMaxSlots = 17;
+
 template <int NSTEPS>
-__global__ __launch_bounds__(256) void k_down_wave(LayerDev L, Dims D, const uint32_t *__restrict__ hq,
-                                                   const float *__restrict__ hs, UnionDev U,
-                                                   const float *__restrict__ w, float *__restrict__ residual) {
+__global__ __launch_bounds__(192) void k_down_dec(LayerDev L, Dims D, const uint32_t *__restrict__ hq,
+                                                  const float *__restrict__ hs, UnionDev U,
+                                                  const float *__restrict__ w, float *__restrict__ residual) {
+  __shared__ float vb[kDecMaxSlots][kTileRows];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int tiles = D.d / kTileRows, C = D.f / kChunk;
+  const int ti = blockIdx.x, C = D.f / kChunk;
   const int nu = clamp_nu(U.n_unique, D);
   const int slots = nu + D.n_shared;
   const ExpertLayout EL = expert_layout(D.d, D.f);
-  const int nst = slots * NSTEPS;
-  const int wpb = blockDim.x >> 6;
-  for (int ti = blockIdx.x * wpb + wave; ti < tiles; ti += gridDim.x * wpb) {
-    const int r = lane >> 3;
-    float out = residual[(size_t)ti * kTileRows + r];
-    uint4 W[2][kTileRows], S[2];
-    uint32_t dg[2][kDigitWords];
-    float dsc[2][2];
-    float acc[kTileRows];
+  const int mine = slots > wave ? (slots - wave + 2) / 3 : 0;  // slots wave, wave+3, ...
+  const int nst = mine * NSTEPS;
+  uint4 W[2][kTileRows], S[2];
+  uint32_t dg[2][kDigitWords];
+  float dsc[2][2];
+  float acc[kTileRows];
 #pragma unroll
-    for (int rr = 0; rr < kTileRows; ++rr) acc[rr] = 0.0f;
-    if (nst > 0) dec_down_slot(L, D, U, nu, EL, 0, ti, lane, W[0], S[0], dg[0], dsc[0], hq, hs);
-    for (int q0 = 0; q0 < nst; q0 += 2) {
+  for (int rr = 0; rr < kTileRows; ++rr) acc[rr] = 0.0f;
+  if (nst > 0) dec_down_slot(L, D, U, nu, EL, wave, ti, lane, W[0], S[0], dg[0], dsc[0], hq, hs);
+  for (int q0 = 0; q0 < nst; q0 += 2) {
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int q = q0 + half;
-        if (q < nst) {
-          if (q + 1 < nst)
-            dec_down_slot(L, D, U, nu, EL, (q + 1) / NSTEPS, ti, lane + 64 * ((q + 1) % NSTEPS), W[half ^ 1],
-                          S[half ^ 1], dg[half ^ 1], dsc[half ^ 1], hq, hs);
-          const int s = q / NSTEPS, j = q % NSTEPS;
-          const int c = lane + 64 * j;
-          int e, p0, p1;
-          const bool ok = resolve_slot(D, U, nu, s, e, p0, p1) && p1 > p0;
-          if (ok && c < C) {
+    for (int half = 0; half < 2; ++half) {
+      const int q = q0 + half;
+      if (q < nst) {
+        if (q + 1 < nst)
+          dec_down_slot(L, D, U, nu, EL, wave + 3 * ((q + 1) / NSTEPS), ti, lane + 64 * ((q + 1) % NSTEPS),
+                        W[half ^ 1], S[half ^ 1], dg[half ^ 1], dsc[half ^ 1], hq, hs);
+        const int sl = wave + 3 * (q / NSTEPS), j = q % NSTEPS;
+        const int c = lane + 64 * j;
+        int e, p0, p1;
+        const bool ok = resolve_slot(D, U, nu, sl, e, p0, p1) && p1 > p0;
+        if (ok && c < C) {
 #pragma unroll
-            for (int rr = 0; rr < kTileRows; ++rr)
-              acc[rr] = fxp_chunk(W[half][rr], dg[half], dsc[half], tile_scale(S[half], rr), acc[rr]);
-          }
-          if (j == NSTEPS - 1) {
-            const float v = reduce8_rows(acc);
-            if (ok) {
-              if (s < nu)
-                out = __builtin_fmaf(w[U.pair_slot[p0]], v, out);
-              else
-                out = out + v;
-            }
+          for (int rr = 0; rr < kTileRows; ++rr)
+            acc[rr] = fxp_chunk(W[half][rr], dg[half], dsc[half], tile_scale(S[half], rr), acc[rr]);
+        }
+        if (j == NSTEPS - 1) {
+          const float v = reduce8_rows(acc);
+          if ((lane & 7) == 7) vb[sl][lane >> 3] = v;
 #pragma unroll
-            for (int rr = 0; rr < kTileRows; ++rr) acc[rr] = 0.0f;
-          }
+          for (int rr = 0; rr < kTileRows; ++rr) acc[rr] = 0.0f;
         }
       }
     }
-    if ((lane & 7) == 7) residual[(size_t)ti * kTileRows + r] = out;
+  }
+  __syncthreads();
+  if (wave == 0 && lane < kTileRows) {
+    float out = residual[(size_t)ti * kTileRows + lane];
+    for (int sl = 0; sl < slots; ++sl) {
+      int e, p0, p1;
+      if (!(resolve_slot(D, U, nu, sl, e, p0, p1) && p1 > p0)) continue;
+      const float v = vb[sl][lane];
+      if (sl < nu) {
+        int js = U.pair_slot[p0];
+        js = js < 0 ? 0 : (js >= D.k ? D.k - 1 : js);  // caller-supplied lists stay in bounds
+        out = __builtin_fmaf(w[js], v, out);
+      } else {
+        out = out + v;
+      }
+    }
+    residual[(size_t)ti * kTileRows + lane] = out;
   }
 }
 
@@ -1275,22 +1420,41 @@ __global__ __launch_bounds__(256) void k_combine(Dims D, const float *__restrict
 }
 
 // ------------------------------------------------------------------ rmsnorm
-// x = r / sqrt(mean(r^2) + eps), unit weight; one block per token, fixed
-// reduction order.
+// x = r / sqrt(mean(r^2) + eps), unit weight; one block of 512 threads per
+// token, 16-byte loads, fixed reduction order (per thread in column order,
+// then the wave tree, then the 8 waves in order).
 
-__global__ __launch_bounds__(256) void k_rmsnorm(const float *__restrict__ r, int d, float eps,
+__global__ __launch_bounds__(512) void k_rmsnorm(const float *__restrict__ r, int d, float eps,
                                                  float *__restrict__ x) {
-  __shared__ float part[4];
+  __shared__ float part[8];
   const int t = blockIdx.x;
-  const float *rr = r + (size_t)t * d;
+  const float4 *rr = (const float4 *)(r + (size_t)t * d);
+  float4 *xx = (float4 *)(x + (size_t)t * d);
+  const int n4 = d / 4;
+  float4 v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int c = threadIdx.x + 512 * i;
+    v[i] = c < n4 ? rr[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
   float acc = 0.0f;
-  for (int c = threadIdx.x; c < d; c += 256) acc = __builtin_fmaf(rr[c], rr[c], acc);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    acc = __builtin_fmaf(v[i].x, v[i].x, acc);
+    acc = __builtin_fmaf(v[i].y, v[i].y, acc);
+    acc = __builtin_fmaf(v[i].z, v[i].z, acc);
+    acc = __builtin_fmaf(v[i].w, v[i].w, acc);
+  }
   acc = wave_sum(acc);
   if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
   __syncthreads();
-  const float ss = (part[0] + part[1]) + (part[2] + part[3]);
+  const float ss = ((part[0] + part[1]) + (part[2] + part[3])) + ((part[4] + part[5]) + (part[6] + part[7]));
   const float inv = 1.0f / sqrtf(ss / (float)d + eps);
-  for (int c = threadIdx.x; c < d; c += 256) x[(size_t)t * d + c] = rr[c] * inv;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int c = threadIdx.x + 512 * i;
+    if (c < n4) xx[c] = make_float4(v[i].x * inv, v[i].y * inv, v[i].z * inv, v[i].w * inv);
+  }
 }
 
 // ---------------------------------------------------------------- launchers
@@ -1507,18 +1671,39 @@ hipError_t launch_down_fxp(const LayerDev &L, const Dims &D, const uint32_t *hq,
 
 hipError_t launch_down_dec(const LayerDev &L, const Dims &D, const uint32_t *hq, const float *hs, const UnionDev &U,
                            const float *w, float *residual, hipStream_t s) {
-  if (D.T != 1) return hipErrorInvalidValue;
+  if (D.T != 1 || D.k + D.n_shared > kDecMaxSlots) return hipErrorInvalidValue;
   const int nsteps = (D.f / kChunk + 63) / 64;
   const int tiles = D.d / kTileRows;
   switch (nsteps) {
-    case 1: k_down_wave<1><<<tiles, 64, 0, s>>>(L, D, hq, hs, U, w, residual); break;
-    case 2: k_down_wave<2><<<tiles, 64, 0, s>>>(L, D, hq, hs, U, w, residual); break;
-    case 3: k_down_wave<3><<<tiles, 64, 0, s>>>(L, D, hq, hs, U, w, residual); break;
-    case 4: k_down_wave<4><<<tiles, 64, 0, s>>>(L, D, hq, hs, U, w, residual); break;
-    case 5: k_down_wave<5><<<tiles, 64, 0, s>>>(L, D, hq, hs, U, w, residual); break;
-    case 6: k_down_wave<6><<<tiles, 64, 0, s>>>(L, D, hq, hs, U, w, residual); break;
-    case 7: k_down_wave<7><<<tiles, 64, 0, s>>>(L, D, hq, hs, U, w, residual); break;
-    default: k_down_wave<8><<<tiles, 64, 0, s>>>(L, D, hq, hs, U, w, residual); break;
+    case 1: k_down_dec<1><<<tiles, 192, 0, s>>>(L, D, hq, hs, U, w, residual); break;
+    case 2: k_down_dec<2><<<tiles, 192, 0, s>>>(L, D, hq, hs, U, w, residual); break;
+    case 3: k_down_dec<3><<<tiles, 192, 0, s>>>(L, D, hq, hs, U, w, residual); break;
+    case 4: k_down_dec<4><<<tiles, 192, 0, s>>>(L, D, hq, hs, U, w, residual); break;
+    case 5: k_down_dec<5><<<tiles, 192, 0, s>>>(L, D, hq, hs, U, w, residual); break;
+    case 6: k_down_dec<6><<<tiles, 192, 0, s>>>(L, D, hq, hs, U, w, residual); break;
+    case 7: k_down_dec<7><<<tiles, 192, 0, s>>>(L, D, hq, hs, U, w, residual); break;
+    default: k_down_dec<8><<<tiles, 192, 0, s>>>(L, D, hq, hs, U, w, residual); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gateup_dec(const LayerDev &L, const Dims &D, const float *logits, int32_t *idx, float *w,
+                             const UnionDev &U, const uint32_t *xq, const float *xs, uint32_t *hq, float *hs,
+                             hipStream_t s) {
+  if (D.T != 1 || D.f % 32 != 0) return hipErrorInvalidValue;
+  const int C = D.d / kChunk;
+  const size_t lds = (size_t)C * kDigitWords * 4 + (size_t)C * 2 * 4;
+  const int grid = (D.k + D.n_shared) * (D.f / 32);
+  if (!logits) {
+    k_gateup_dec<false, 1><<<grid, 256, lds, s>>>(L, D, nullptr, idx, w, U, xq, xs, hq, hs);
+    return hipGetLastError();
+  }
+  switch (topk_per(D.E)) {
+    case 1: k_gateup_dec<true, 1><<<grid, 256, lds, s>>>(L, D, logits, idx, w, U, xq, xs, hq, hs); break;
+    case 2: k_gateup_dec<true, 2><<<grid, 256, lds, s>>>(L, D, logits, idx, w, U, xq, xs, hq, hs); break;
+    case 4: k_gateup_dec<true, 4><<<grid, 256, lds, s>>>(L, D, logits, idx, w, U, xq, xs, hq, hs); break;
+    case 8: k_gateup_dec<true, 8><<<grid, 256, lds, s>>>(L, D, logits, idx, w, U, xq, xs, hq, hs); break;
+    default: k_gateup_dec<true, 16><<<grid, 256, lds, s>>>(L, D, logits, idx, w, U, xq, xs, hq, hs); break;
   }
   return hipGetLastError();
 }
@@ -1532,7 +1717,7 @@ hipError_t launch_combine(const Dims &D, const float *w, const UnionDev &U, cons
 
 hipError_t launch_rmsnorm(const float *r, int T, int d, float eps, float *x, hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  k_rmsnorm<<<T, 256, 0, s>>>(r, d, eps, x);
+  k_rmsnorm<<<T, 512, 0, s>>>(r, d, eps, x);
   return hipGetLastError();
 }
 
