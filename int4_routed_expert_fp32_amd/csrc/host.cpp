@@ -261,6 +261,7 @@ Workspace workspace_layout(int d, int f, int E, int k, int n_shared, int max_tok
   W.mblk_max = mfma_max_entries(max_tokens, k, E, n_shared);
   W.mblk = take((size_t)W.mblk_max * 16);
   W.mcount = take(4);
+  W.wslot = take(32 * 4);
   W.bytes = o;
   return W;
 }
@@ -381,11 +382,12 @@ static int forward_impl(colimoe_ctx *ctx, int32_t layer, const float *x, int32_t
     if (T == 1 && dec_supported(D)) {
       {
         KTimer kt(ctx, K_GATEUP);
-        if (launch_gateup_dec(L, D, nullptr, nullptr, nullptr, U, xq, xs, hq, hs, s) != hipSuccess)
+        if (launch_gateup_dec(L, D, U, w, xq, xs, hq, hs, (float *)(ctx->ws + ctx->wl.wslot), s) != hipSuccess)
           return COLIMOE_E_HIP;
       }
       KTimer kt(ctx, K_DOWN);
-      if (launch_down_dec(L, D, hq, hs, U, w, residual, s) != hipSuccess) return COLIMOE_E_HIP;
+      if (launch_down_dec(L, D, hq, hs, U, (const float *)(ctx->ws + ctx->wl.wslot), residual, s) != hipSuccess)
+        return COLIMOE_E_HIP;
       return COLIMOE_OK;  // combine done in the kernel
     }
     {
@@ -617,8 +619,8 @@ int colimoe_route_forward(colimoe_ctx *ctx, int32_t layer, const float *x, int32
   const bool encode = path == PATH_FXP;
   const Dims D = dims_of(ctx, T);
   if (T == 1 && encode && dec_supported(D)) {
-    // one token: router (+ encoding of x), gate/up with the top-k and union
-    // lists folded in, down with the combine folded in
+    // one token: router (+ encoding of x), top-k with the union lists,
+    // gate/up, down with the combine folded in
     const LayerDev L = layer_of(ctx, layer);
     hipStream_t s = ctx->stream;
     float *lg = (float *)(ctx->ws + ctx->wl.logits);
@@ -632,11 +634,16 @@ int colimoe_route_forward(colimoe_ctx *ctx, int32_t layer, const float *x, int32
       if (launch_router_split(L, D, x, lg, xq, xs, s) != hipSuccess) return COLIMOE_E_HIP;
     }
     {
+      KTimer kt(ctx, K_TOPK);
+      if (launch_topk_union1(lg, D, idx, w, &U, s) != hipSuccess) return COLIMOE_E_HIP;
+    }
+    {
       KTimer kt(ctx, K_GATEUP);
-      if (launch_gateup_dec(L, D, lg, idx, w, U, xq, xs, hq, hs, s) != hipSuccess) return COLIMOE_E_HIP;
+      if (launch_gateup_dec(L, D, U, w, xq, xs, hq, hs, (float *)(ctx->ws + ctx->wl.wslot), s) != hipSuccess)
+        return COLIMOE_E_HIP;
     }
     KTimer kt(ctx, K_DOWN);
-    return hip_status(launch_down_dec(L, D, hq, hs, U, w, residual, s));
+    return hip_status(launch_down_dec(L, D, hq, hs, U, (const float *)(ctx->ws + ctx->wl.wslot), residual, s));
   }
   rc = route_impl(ctx, layer, x, T, idx, w, uu, nullptr, encode);
   if (rc) return rc;

@@ -89,6 +89,7 @@ struct Workspace {
   size_t hq, hs;  // fixed-point h: [rows][f/32][24] u32, [rows][f/16] fp32
   size_t xb, hb;  // bf16 MFMA path: x rows in pair order [rows][d], h [rows][f], bf16
   size_t mblk, mcount;  // bf16 MFMA path: M-block list (int4 entries) and its length
+  size_t wslot;         // one-token path: gate weight of each slot in slot order
   int mblk_max;
   size_t bytes;
 };
@@ -124,18 +125,20 @@ hipError_t launch_gateup_fxp(const LayerDev &L, const Dims &D, const uint32_t *x
                              hipStream_t s);
 hipError_t launch_down_fxp(const LayerDev &L, const Dims &D, const uint32_t *hq, const float *hs, const UnionDev &U,
                            float *y, const float *w, float *residual, bool fused, hipStream_t s);
-// The one-token kernels below need f % 32 == 0 (always true: f % 64 == 0) and
-// at most 17 slots (k + shared).
-inline bool dec_supported(const Dims &D) { return D.T == 1 && D.k + D.n_shared <= 17 && D.f % 32 == 0; }
-// Gate/up for one token with x's fixed-point encoding staged in LDS.  With
-// logits non-null the kernel also selects the top-k (writing idx, w and the
-// union lists U); otherwise it reads the routing from U.
-hipError_t launch_gateup_dec(const LayerDev &L, const Dims &D, const float *logits, int32_t *idx, float *w,
-                             const UnionDev &U, const uint32_t *xq, const float *xs, uint32_t *hq, float *hs,
+// The one-token gate/up kernel covers d <= 8192 (at most 4 steps of 64
+// chunks per row); down needs at most 17 slots (k + shared).
+bool gateup_dec_supported(const Dims &D);
+inline bool dec_supported(const Dims &D) {
+  return D.T == 1 && D.k + D.n_shared <= 17 && D.f % 16 == 0 && gateup_dec_supported(D);
+}
+// Gate/up for one token, one wave per (tile, step), routing from U; records
+// each slot's gate weight (from w) in wslot[k + shared] for launch_down_dec.
+hipError_t launch_gateup_dec(const LayerDev &L, const Dims &D, const UnionDev &U, const float *w,
+                             const uint32_t *xq, const float *xs, uint32_t *hq, float *hs, float *wslot,
                              hipStream_t s);
-// Down + combine for one token, three waves per output tile (T == 1).
+// Down + combine for one token (T == 1), slot factors from wslot.
 hipError_t launch_down_dec(const LayerDev &L, const Dims &D, const uint32_t *hq, const float *hs, const UnionDev &U,
-                           const float *w, float *residual, hipStream_t s);
+                           const float *wslot, float *residual, hipStream_t s);
 // Router for many tokens on the matrix cores (fp32), with S = router_splits(d)
 // K-slices whose partials (part: [S][T][E]) are summed in slice order.
 int router_splits(int d);

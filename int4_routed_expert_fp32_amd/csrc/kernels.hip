@@ -772,9 +772,10 @@ __global__ __launch_bounds__(256) void k_xquant(const float *__restrict__ x, int
 
 // Gate/up on the fixed-point path.  A block of 4 waves owns 16 consecutive
 // h rows of one slot (4 tiles of 4 gate + 4 up rows); each wave runs all
-// chunk steps of its tile for up to MT tokens, then the block encodes its 16
-// h values per token for the down kernel (one 16-column group) and also
-// writes h in fp32.
+// chunk steps of its tile for up to MT tokens (per lane, each step's
+// contribution is formed from zero and the steps are added in order), then
+// the block encodes its 16 h values per token for the down kernel (one
+// 16-column group) and also writes h in fp32.
 template <int MT>
 __global__ __launch_bounds__(256) void k_gateup_fxp(LayerDev L, Dims D, const uint32_t *__restrict__ xq,
                                                     const float *__restrict__ xs, UnionDev U, float *__restrict__ h,
@@ -811,15 +812,25 @@ __global__ __launch_bounds__(256) void k_gateup_fxp(LayerDev L, Dims D, const ui
       for (int m = 0; m < MT; ++m)
 #pragma unroll
         for (int r = 0; r < kTileRows; ++r) acc[m][r] = 0.0f;
+      // per lane: each step's contribution from zero, the steps added in order
       for (int j = 0; j < nsteps; ++j) {
         const int c = lane + 64 * j;
+        float part[MT][kTileRows];
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+          for (int r = 0; r < kTileRows; ++r) part[m][r] = 0.0f;
         if (c < C) {
           uint4 W[kTileRows], S;
           load_step(base + EL.gu_nib, base + EL.gu_sc, ti, D.d, c, W, S);
 #pragma unroll
           for (int m = 0; m < MT; ++m)
-            if (m < mcount) fxp_step(W, S, xq, xs, trow[m], D.d, c, acc[m]);
+            if (m < mcount) fxp_step(W, S, xq, xs, trow[m], D.d, c, part[m]);
         }
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+          for (int r = 0; r < kTileRows; ++r) acc[m][r] = j == 0 ? part[m][r] : acc[m][r] + part[m][r];
       }
       if ((int)threadIdx.x < MT * 12) hw[threadIdx.x / 12][threadIdx.x % 12] = 0u;
       __syncthreads();
@@ -1017,53 +1028,31 @@ __global__ __launch_bounds__(64) void k_topk_union1(const float *__restrict__ lo
   if (with_union) union_one_token(ids, D, U);
 }
 
-// Gate/up for one token.  A block owns 32 consecutive h rows (8 tiles, two
-// 16-row encoding groups) of one slot; wave w streams tiles 2w and 2w+1 with
-// the next step's weights in flight; the block's copy of x's digit words
-// sits in LDS.  With TOPK the block first finds its expert from the logits
-// (top-k in wave 0; slot s < k is the s-th smallest selected id, slot k the
-// shared expert) and block 0 writes idx, w and the union lists.  Per row the
-// operations are those of k_gateup_fxp, so h and its encoding are identical.
-template <bool TOPK, int PER>
-__global__ __launch_bounds__(256) void k_gateup_dec(LayerDev L, Dims D, const float *__restrict__ logits,
-                                                    int32_t *__restrict__ idx, float *__restrict__ wout, UnionDev U,
-                                                    const uint32_t *__restrict__ xq, const float *__restrict__ xs,
-                                                    uint32_t *__restrict__ hq, float *__restrict__ hs) {
-  extern __shared__ __align__(16) uint32_t xlds[];  // [C][24] digit words, then [C][2] fp32 scales
-  __shared__ int32_t ids_s[16];
+// Gate/up for one token.  A block owns one 16-row encoding group of one slot
+// (4 tiles) and has one wave per (tile, step): every wave issues its step's
+// 8 x 1 KB of weights at once, so the whole kernel keeps many loads in flight
+// while earlier waves compute.  Step contributions meet in LDS and are added
+// in step order, then each tile is reduced, SiLU(g) * u formed and the group
+// encoded for the down kernel — per row the operations of k_gateup_fxp.  The
+// first block of each slot also records the slot's gate weight in wslot
+// (slot order; 1 for the shared expert) for the down kernel's combine.
+template <int NS>
+__global__ __launch_bounds__(256 * NS) void k_gateup_dec(LayerDev L, Dims D, UnionDev U, const float *__restrict__ w,
+                                                         const uint32_t *__restrict__ xq,
+                                                         const float *__restrict__ xs, uint32_t *__restrict__ hq,
+                                                         float *__restrict__ hs, float *__restrict__ wslot) {
+  __shared__ float part[4 * NS][kTileRows][64];
   __shared__ int slot_s[2];  // expert, output row
-  __shared__ float hv[32];
-  __shared__ uint32_t hw[2][12];
-  __shared__ float hsc[2];
+  __shared__ float hv[16];
+  __shared__ uint32_t hw[12];
+  __shared__ float hsc;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int C = D.d / kChunk, nsteps = (C + 63) / 64;
-  const int bps = D.f / 32;
-  const int s = blockIdx.x / bps, qb = blockIdx.x - s * bps;
-  float *xsl = (float *)(xlds + (size_t)C * kDigitWords);
-  for (int i = threadIdx.x; i < C * kDigitWords / 4; i += 256) ((uint4 *)xlds)[i] = ((const uint4 *)xq)[i];
-  for (int i = threadIdx.x; i < 2 * C; i += 256) xsl[i] = xs[i];
-  if (threadIdx.x < 24) hw[threadIdx.x / 12][threadIdx.x % 12] = 0u;
-  if (TOPK) {
-    if (s < D.k) {
-      if (wave == 0) {
-        topk_token<PER>(logits, D, 0, blockIdx.x == 0 ? idx : nullptr, blockIdx.x == 0 ? wout : nullptr, ids_s);
-        wave_lds_sync();
-        if (blockIdx.x == 0) union_one_token(ids_s, D, U);
-        if (lane < D.k) {
-          const int e = ids_s[lane];
-          int rank = 0;
-          for (int i = 0; i < D.k; ++i) rank += ids_s[i] < e;
-          if (rank == s) {
-            slot_s[0] = e;
-            slot_s[1] = s;
-          }
-        }
-      }
-    } else if (threadIdx.x == 0) {
-      slot_s[0] = (s == D.k && D.n_shared) ? D.E : -1;
-      slot_s[1] = D.k;
-    }
-  } else if (threadIdx.x == 0) {
+  const int C = D.d / kChunk, quads = D.f / 16;
+  const int s = blockIdx.x / quads, qd = blockIdx.x - s * quads;
+  const int tt = wave / NS, st = wave - tt * NS;
+  const int ti = qd * 4 + tt, c = lane + 64 * st;
+  if (threadIdx.x < 12) hw[threadIdx.x] = 0u;
+  if (threadIdx.x == 0) {
     const int nu = clamp_nu(U.n_unique, D);
     int e = -1, p0 = 0, p1 = 0;
     if (s < nu || (s == nu && D.n_shared)) {
@@ -1071,60 +1060,50 @@ __global__ __launch_bounds__(256) void k_gateup_dec(LayerDev L, Dims D, const fl
     }
     slot_s[0] = e;
     slot_s[1] = s < nu ? p0 : D.k;
+    if (qd == 0 && e >= 0) {
+      float f = 1.0f;
+      if (s < nu) {
+        int js = U.pair_slot[p0];
+        js = js < 0 ? 0 : (js >= D.k ? D.k - 1 : js);  // caller-supplied lists stay in bounds
+        f = w[js];
+      }
+      wslot[s] = f;
+    }
   }
   __syncthreads();
   const int e = slot_s[0], orow = slot_s[1];
   if (e < 0) return;  // block-uniform
   const ExpertLayout EL = expert_layout(D.d, D.f);
   const uint8_t *base = L.experts + (size_t)e * L.expert_stride;
-  const uint8_t *nib = base + EL.gu_nib, *scp = base + EL.gu_sc;
-  const int ti0 = qb * 8 + 2 * wave;
-  const int nunits = 2 * nsteps;
-  uint4 W[2][kTileRows], S[2];
   float acc[kTileRows];
 #pragma unroll
   for (int r = 0; r < kTileRows; ++r) acc[r] = 0.0f;
-  if (lane < C) load_step(nib, scp, ti0, D.d, lane, W[0], S[0]);
-  for (int u0 = 0; u0 < nunits; u0 += 2) {
+  if (c < C) {
+    uint4 W[kTileRows], S;
+    load_step(base + EL.gu_nib, base + EL.gu_sc, ti, D.d, c, W, S);
+    fxp_step(W, S, xq, xs, 0, D.d, c, acc);
+  }
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int u = u0 + half;
-      if (u + 1 < nunits) {
-        const int c1 = lane + 64 * ((u + 1) % nsteps);
-        if (c1 < C) load_step(nib, scp, ti0 + (u + 1) / nsteps, D.d, c1, W[half ^ 1], S[half ^ 1]);
-      }
-      const int j = u % nsteps, c = lane + 64 * j;
-      if (c < C) {
-        uint32_t dg[kDigitWords];
-        const uint4 *src = (const uint4 *)(xlds + (size_t)c * kDigitWords);
+  for (int r = 0; r < kTileRows; ++r) part[wave][r][lane] = acc[r];
+  __syncthreads();
+  if (st == 0) {
+    float tot[kTileRows];
 #pragma unroll
-        for (int i = 0; i < kDigitWords / 4; ++i) {
-          const uint4 v = src[i];
-          dg[4 * i] = v.x;
-          dg[4 * i + 1] = v.y;
-          dg[4 * i + 2] = v.z;
-          dg[4 * i + 3] = v.w;
-        }
-        const float xsc[2] = {xsl[2 * c], xsl[2 * c + 1]};
+    for (int r = 0; r < kTileRows; ++r) {
+      tot[r] = part[wave][r][lane];
 #pragma unroll
-        for (int r = 0; r < kTileRows; ++r)
-          acc[r] = fxp_chunk(W[half][r], dg, xsc, tile_scale(S[half], r), acc[r]);
-      }
-      if (j == nsteps - 1) {
-        const float v = reduce8_rows(acc);
-        const float up = bits_f(xor32(f_bits(v)));  // up rows sit 32 lanes above their gate rows
-        const int r = lane >> 3;
-        if ((lane & 7) == 7 && r < 4) hv[(2 * wave + u / nsteps) * 4 + r] = silu_f(v) * up;
-#pragma unroll
-        for (int rr = 0; rr < kTileRows; ++rr) acc[rr] = 0.0f;
-      }
+      for (int j = 1; j < NS; ++j) tot[r] = tot[r] + part[wave + j][r][lane];
     }
+    const float v = reduce8_rows(tot);
+    const float up = bits_f(xor32(f_bits(v)));  // up rows sit 32 lanes above their gate rows
+    const int r = lane >> 3;
+    if ((lane & 7) == 7 && r < 4) hv[tt * 4 + r] = silu_f(v) * up;
   }
   __syncthreads();
-  // encode the two 16-row groups (one 16-lane row each), as k_gateup_fxp does
-  if (threadIdx.x < 32) {
-    const int g = threadIdx.x >> 4, i = threadIdx.x & 15;
-    const float v = hv[16 * g + i];
+  // encode the block's 16 h values (one 16-lane row), as k_gateup_fxp does
+  if (threadIdx.x < 16) {
+    const int i = threadIdx.x;
+    const float v = hv[i];
     uint32_t mb = f_bits(fabsf(v));
     mb = max(mb, dpp<kRowRor8>(mb));
     mb = max(mb, dpp<kRowRor4>(mb));
@@ -1135,15 +1114,13 @@ __global__ __launch_bounds__(256) void k_gateup_dec(LayerDev L, Dims D, const fl
     E = E < -100 ? -100 : E;
     const uint32_t B = (uint32_t)((int)__builtin_rintf(v * ldexpf(1.0f, 22 - E)) + 0x888888);
 #pragma unroll
-    for (int k = 0; k < 6; ++k) atomicOr(&hw[g][2 * k + (i >> 3)], (((B >> (4 * k)) & 15u) ^ 8u) << (4 * (i & 7)));
-    if (i == 0) hsc[g] = ldexpf(1.0f, E - 22);
+    for (int k = 0; k < 6; ++k) atomicOr(&hw[2 * k + (i >> 3)], (((B >> (4 * k)) & 15u) ^ 8u) << (4 * (i & 7)));
+    if (i == 0) hsc = ldexpf(1.0f, E - 22);
   }
   __syncthreads();
-  if (threadIdx.x < 24) {
-    const int g = threadIdx.x / 12, wd = threadIdx.x % 12;
-    const int qd = 2 * qb + g;
-    hq[((size_t)orow * (D.f / kChunk) + (qd >> 1)) * kDigitWords + (qd & 1) * 12 + wd] = hw[g][wd];
-    if (wd == 0) hs[(size_t)orow * (D.f / 16) + qd] = hsc[g];
+  if (threadIdx.x < 12) {
+    hq[((size_t)orow * (D.f / kChunk) + (qd >> 1)) * kDigitWords + (qd & 1) * 12 + threadIdx.x] = hw[threadIdx.x];
+    if (threadIdx.x == 0) hs[(size_t)orow * (D.f / 16) + qd] = hsc;
   }
 }
 
@@ -1161,18 +1138,64 @@ __device__ __forceinline__ void dec_down_slot(const LayerDev &L, const Dims &D, 
   load_digits(hq, hs, s < nu ? p0 : D.T * D.k, D.f, c, dg, dsc);
 }
 
-// Down + combine for one token.  A block of 3 waves owns one 8-row output
-// tile; wave w streams slots w, w+3, ... (next step's weights and digits in
-// flight) and leaves each slot's 8 outputs in LDS; wave 0 then folds them
-// into the residual in slot order: routed experts by ascending id weighted by
-// w, then the shared expert, as the general kernels do.
+// Down + combine for one token when a down row is one step (f <= 2048): a
+// block of one wave per slot owns one 8-row output tile; every wave issues its
+// slot's weights and digits at once and leaves the slot's 8 outputs in LDS;
+// wave 0 folds them into the residual in slot order (routed experts by
+// ascending id weighted by their gate weight, taken from wslot as recorded by
+// the gate/up kernel, then the shared expert), as the general kernels do.
+__global__ __launch_bounds__(1024) void k_down_dec1(LayerDev L, Dims D, const uint32_t *__restrict__ hq,
+                                                    const float *__restrict__ hs, UnionDev U,
+                                                    const float *__restrict__ wslot, float *__restrict__ residual) {
+  __shared__ float vb[16][kTileRows];
+  __shared__ int ok_s[16];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int ti = blockIdx.x, C = D.f / kChunk;
+  const int nu = clamp_nu(U.n_unique, D);
+  const int slots = nu + D.n_shared;
+  const ExpertLayout EL = expert_layout(D.d, D.f);
+  if (wave < slots) {
+    uint4 W[kTileRows], S;
+    uint32_t dg[kDigitWords];
+    float dsc[2];
+    dec_down_slot(L, D, U, nu, EL, wave, ti, lane, W, S, dg, dsc, hq, hs);
+    int e, p0, p1;
+    const bool ok = resolve_slot(D, U, nu, wave, e, p0, p1) && p1 > p0;
+    float acc[kTileRows];
+#pragma unroll
+    for (int rr = 0; rr < kTileRows; ++rr) acc[rr] = 0.0f;
+    if (ok && lane < C) {
+#pragma unroll
+      for (int rr = 0; rr < kTileRows; ++rr) acc[rr] = fxp_chunk(W[rr], dg, dsc, tile_scale(S, rr), acc[rr]);
+    }
+    const float v = reduce8_rows(acc);
+    if ((lane & 7) == 7) vb[wave][lane >> 3] = v;
+    if (lane == 0) ok_s[wave] = ok;
+  }
+  __syncthreads();
+  if (wave == 0 && lane < kTileRows) {
+    float out = residual[(size_t)ti * kTileRows + lane];
+    for (int sl = 0; sl < slots; ++sl) {
+      if (!ok_s[sl]) continue;
+      const float v = vb[sl][lane];
+      out = sl < nu ? __builtin_fmaf(wslot[sl], v, out) : out + v;
+    }
+    residual[(size_t)ti * kTileRows + lane] = out;
+  }
+}
+
+// Down + combine for one token, longer down rows: a block of 3 waves owns one
+// 8-row output tile; wave w streams slots w, w+3, ... (next step's weights and
+// digits in flight) and leaves each slot's 8 outputs in LDS; wave 0 combines
+// as above.
 constexpr int kDecMaxSlots = 17;
 
 template <int NSTEPS>
 __global__ __launch_bounds__(192) void k_down_dec(LayerDev L, Dims D, const uint32_t *__restrict__ hq,
                                                   const float *__restrict__ hs, UnionDev U,
-                                                  const float *__restrict__ w, float *__restrict__ residual) {
+                                                  const float *__restrict__ wslot, float *__restrict__ residual) {
   __shared__ float vb[kDecMaxSlots][kTileRows];
+  __shared__ int ok_s[kDecMaxSlots];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int ti = blockIdx.x, C = D.f / kChunk;
   const int nu = clamp_nu(U.n_unique, D);
@@ -1207,6 +1230,7 @@ __global__ __launch_bounds__(192) void k_down_dec(LayerDev L, Dims D, const uint
         if (j == NSTEPS - 1) {
           const float v = reduce8_rows(acc);
           if ((lane & 7) == 7) vb[sl][lane >> 3] = v;
+          if (lane == 0) ok_s[sl] = ok;
 #pragma unroll
           for (int rr = 0; rr < kTileRows; ++rr) acc[rr] = 0.0f;
         }
@@ -1217,16 +1241,9 @@ __global__ __launch_bounds__(192) void k_down_dec(LayerDev L, Dims D, const uint
   if (wave == 0 && lane < kTileRows) {
     float out = residual[(size_t)ti * kTileRows + lane];
     for (int sl = 0; sl < slots; ++sl) {
-      int e, p0, p1;
-      if (!(resolve_slot(D, U, nu, sl, e, p0, p1) && p1 > p0)) continue;
+      if (!ok_s[sl]) continue;
       const float v = vb[sl][lane];
-      if (sl < nu) {
-        int js = U.pair_slot[p0];
-        js = js < 0 ? 0 : (js >= D.k ? D.k - 1 : js);  // caller-supplied lists stay in bounds
-        out = __builtin_fmaf(w[js], v, out);
-      } else {
-        out = out + v;
-      }
+      out = sl < nu ? __builtin_fmaf(wslot[sl], v, out) : out + v;
     }
     residual[(size_t)ti * kTileRows + lane] = out;
   }
@@ -1670,40 +1687,41 @@ hipError_t launch_down_fxp(const LayerDev &L, const Dims &D, const uint32_t *hq,
 }
 
 hipError_t launch_down_dec(const LayerDev &L, const Dims &D, const uint32_t *hq, const float *hs, const UnionDev &U,
-                           const float *w, float *residual, hipStream_t s) {
+                           const float *wslot, float *residual, hipStream_t s) {
   if (D.T != 1 || D.k + D.n_shared > kDecMaxSlots) return hipErrorInvalidValue;
   const int nsteps = (D.f / kChunk + 63) / 64;
   const int tiles = D.d / kTileRows;
+  const int slots = D.k + D.n_shared;
+  if (nsteps == 1 && slots <= 16) {
+    k_down_dec1<<<tiles, 64 * slots, 0, s>>>(L, D, hq, hs, U, wslot, residual);
+    return hipGetLastError();
+  }
   switch (nsteps) {
-    case 1: k_down_dec<1><<<tiles, 192, 0, s>>>(L, D, hq, hs, U, w, residual); break;
-    case 2: k_down_dec<2><<<tiles, 192, 0, s>>>(L, D, hq, hs, U, w, residual); break;
-    case 3: k_down_dec<3><<<tiles, 192, 0, s>>>(L, D, hq, hs, U, w, residual); break;
-    case 4: k_down_dec<4><<<tiles, 192, 0, s>>>(L, D, hq, hs, U, w, residual); break;
-    case 5: k_down_dec<5><<<tiles, 192, 0, s>>>(L, D, hq, hs, U, w, residual); break;
-    case 6: k_down_dec<6><<<tiles, 192, 0, s>>>(L, D, hq, hs, U, w, residual); break;
-    case 7: k_down_dec<7><<<tiles, 192, 0, s>>>(L, D, hq, hs, U, w, residual); break;
-    default: k_down_dec<8><<<tiles, 192, 0, s>>>(L, D, hq, hs, U, w, residual); break;
+    case 1: k_down_dec<1><<<tiles, 192, 0, s>>>(L, D, hq, hs, U, wslot, residual); break;
+    case 2: k_down_dec<2><<<tiles, 192, 0, s>>>(L, D, hq, hs, U, wslot, residual); break;
+    case 3: k_down_dec<3><<<tiles, 192, 0, s>>>(L, D, hq, hs, U, wslot, residual); break;
+    case 4: k_down_dec<4><<<tiles, 192, 0, s>>>(L, D, hq, hs, U, wslot, residual); break;
+    case 5: k_down_dec<5><<<tiles, 192, 0, s>>>(L, D, hq, hs, U, wslot, residual); break;
+    case 6: k_down_dec<6><<<tiles, 192, 0, s>>>(L, D, hq, hs, U, wslot, residual); break;
+    case 7: k_down_dec<7><<<tiles, 192, 0, s>>>(L, D, hq, hs, U, wslot, residual); break;
+    default: k_down_dec<8><<<tiles, 192, 0, s>>>(L, D, hq, hs, U, wslot, residual); break;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_gateup_dec(const LayerDev &L, const Dims &D, const float *logits, int32_t *idx, float *w,
-                             const UnionDev &U, const uint32_t *xq, const float *xs, uint32_t *hq, float *hs,
+bool gateup_dec_supported(const Dims &D) { return (D.d / kChunk + 63) / 64 <= 4; }
+
+hipError_t launch_gateup_dec(const LayerDev &L, const Dims &D, const UnionDev &U, const float *w,
+                             const uint32_t *xq, const float *xs, uint32_t *hq, float *hs, float *wslot,
                              hipStream_t s) {
-  if (D.T != 1 || D.f % 32 != 0) return hipErrorInvalidValue;
-  const int C = D.d / kChunk;
-  const size_t lds = (size_t)C * kDigitWords * 4 + (size_t)C * 2 * 4;
-  const int grid = (D.k + D.n_shared) * (D.f / 32);
-  if (!logits) {
-    k_gateup_dec<false, 1><<<grid, 256, lds, s>>>(L, D, nullptr, idx, w, U, xq, xs, hq, hs);
-    return hipGetLastError();
-  }
-  switch (topk_per(D.E)) {
-    case 1: k_gateup_dec<true, 1><<<grid, 256, lds, s>>>(L, D, logits, idx, w, U, xq, xs, hq, hs); break;
-    case 2: k_gateup_dec<true, 2><<<grid, 256, lds, s>>>(L, D, logits, idx, w, U, xq, xs, hq, hs); break;
-    case 4: k_gateup_dec<true, 4><<<grid, 256, lds, s>>>(L, D, logits, idx, w, U, xq, xs, hq, hs); break;
-    case 8: k_gateup_dec<true, 8><<<grid, 256, lds, s>>>(L, D, logits, idx, w, U, xq, xs, hq, hs); break;
-    default: k_gateup_dec<true, 16><<<grid, 256, lds, s>>>(L, D, logits, idx, w, U, xq, xs, hq, hs); break;
+  if (D.T != 1 || D.f % 16 != 0 || !gateup_dec_supported(D)) return hipErrorInvalidValue;
+  const int ns = (D.d / kChunk + 63) / 64;
+  const int grid = (D.k + D.n_shared) * (D.f / 16);
+  switch (ns) {
+    case 1: k_gateup_dec<1><<<grid, 256, 0, s>>>(L, D, U, w, xq, xs, hq, hs, wslot); break;
+    case 2: k_gateup_dec<2><<<grid, 512, 0, s>>>(L, D, U, w, xq, xs, hq, hs, wslot); break;
+    case 3: k_gateup_dec<3><<<grid, 768, 0, s>>>(L, D, U, w, xq, xs, hq, hs, wslot); break;
+    default: k_gateup_dec<4><<<grid, 1024, 0, s>>>(L, D, U, w, xq, xs, hq, hs, wslot); break;
   }
   return hipGetLastError();
 }
