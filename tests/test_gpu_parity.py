@@ -203,3 +203,34 @@ def test_forced_routing_onehot_gate():
     ora = P.OracleLayer(w, 0)
     out, _ = ora.forward(x, np.array([[5, 0, 9]]), np.array([[1.0, 0.0, 0.0]]), residual=np.zeros_like(x))
     P.assert_close(res.cpu().numpy(), out, what="one-hot gate")
+
+
+# One-token shapes that reach the other kernel variants: two steps per row with
+# a partial second one (d = f = 2112: the streaming down kernel), 17 slots
+# (k = 16 + shared: more slots than one block of slot-waves holds), and
+# d > 8192 (the general fixed-point kernels).
+DEC_SHAPES = [
+    synth.Workload(name="dec_2step", d=2112, f=2112, E=40, k=3, T=3, n_shared=1, zipf=1.1,
+                   seed=synth.BASE_SEED + 104),
+    synth.Workload(name="dec_k16", d=2048, f=2048, E=64, k=16, T=3, n_shared=1, seed=synth.BASE_SEED + 105),
+    synth.Workload(name="dec_wide", d=8256, f=2048, E=16, k=2, T=3, n_shared=1, seed=synth.BASE_SEED + 106),
+]
+
+
+@pytest.mark.parametrize("w", DEC_SHAPES, ids=lambda w: w.name)
+def test_one_token_kernel_variants(w):
+    """Each token alone (one call and route + forward) matches the oracle, the
+    two call forms agree bit for bit, and both equal the batched call."""
+    ctx = _ctx(w)
+    P.load_layer(ctx, w, 0)
+    ora = P.OracleLayer(w, 0)
+    X = synth.activations(w, stream=4)
+    batch = P.layer_parity(ctx, w, 0, X, ora, flags=FXP)
+    for t in range(w.T):
+        x1 = X[t:t + 1]
+        a = P.layer_parity(ctx, w, 0, x1, ora, flags=FXP, one_call=True)
+        b = P.layer_parity(ctx, w, 0, x1, ora, flags=FXP)
+        assert np.array_equal(a["out"].view(np.uint32), b["out"].view(np.uint32)), t
+        assert np.array_equal(a["out"][0].view(np.uint32), batch["out"][t].view(np.uint32)), t
+        assert np.array_equal(a["idx"][0], batch["idx"][t])
+    print(w.name, "worst ratio", batch["ratio"])
