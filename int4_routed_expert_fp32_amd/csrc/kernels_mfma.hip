@@ -45,22 +45,49 @@ __device__ __forceinline__ uint16_t bf16_bits(float v) {
   return __builtin_bit_cast(uint16_t, (__bf16)v);
 }
 
+// v_and_or_b32 (x & mask) | magic, mask in a scalar register (one constant
+// per VOP3 instruction on gfx9).
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t magic) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(mask), "v"(magic));
+  return r;
+}
+
+__device__ __forceinline__ float half_lo_f(uint32_t h) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(h & 0xFFFFu));
+}
+__device__ __forceinline__ float half_hi_f(uint32_t h) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(h >> 16)); }
+
+// Scale constants of one weight group for dequant8.
+struct GroupScale {
+  float s, m1032, s16, m72;
+  __device__ __forceinline__ explicit GroupScale(float sc)
+      : s(sc), m1032(-1032.0f * sc), s16(0.0625f * sc), m72(-72.0f * sc) {}
+};
+
 // 8 int4 weights (one word of two's-complement nibbles, element 2b in the low
-// nibble of byte b) times their group scale s, each product exact in fp32
-// ((n - 8) * s with n = q + 8), rounded to bf16.
-__device__ __forceinline__ bf16x8 dequant8(uint32_t w, float s, float m8s) {
-  uint32_t x = w ^ 0x88888888u;
-  uint32_t lo = x & 0x0F0F0F0Fu, hi = (x >> 4) & 0x0F0F0F0Fu;
-  asm("" : "+v"(lo), "+v"(hi));  // byte conversions stay single instructions
+// nibble of byte b) times their group scale s, rounded to bf16.  Each word is
+// flipped to offset binary n = q + 8; nibbles are dropped into the mantissas of
+// fp16 halves with exponent 10 (0x6400 = 1024): bits 0-3 give 1024 + n, bits
+// 4-7 give 1024 + 16 n.  One v_fma_mix_f32 per weight then forms
+// (1024 + n) s - 1032 s, or (1024 + 16 n) (s/16) - 72 s, both exactly
+// (n - 8) s = q s in fp32 (at most 15 significant bits), and v_cvt_pk_bf16_f32
+// rounds pairs to bf16, to nearest even.
+__device__ __forceinline__ bf16x8 dequant8(uint32_t w, const GroupScale &g, uint32_t magic) {
+  const uint32_t x = w ^ 0x88888888u, y = x >> 8;
+  const uint32_t h0 = and_or(x, 0x000F000Fu, magic);  // elements 0, 4
+  const uint32_t h1 = and_or(x, 0x00F000F0u, magic);  // elements 1, 5 (times 16)
+  const uint32_t h2 = and_or(y, 0x000F000Fu, magic);  // elements 2, 6
+  const uint32_t h3 = and_or(y, 0x00F000F0u, magic);  // elements 3, 7 (times 16)
   bf16x8 r;
-  r[0] = (__bf16)__builtin_fmaf((float)(lo & 0xFFu), s, m8s);
-  r[1] = (__bf16)__builtin_fmaf((float)(hi & 0xFFu), s, m8s);
-  r[2] = (__bf16)__builtin_fmaf((float)((lo >> 8) & 0xFFu), s, m8s);
-  r[3] = (__bf16)__builtin_fmaf((float)((hi >> 8) & 0xFFu), s, m8s);
-  r[4] = (__bf16)__builtin_fmaf((float)((lo >> 16) & 0xFFu), s, m8s);
-  r[5] = (__bf16)__builtin_fmaf((float)((hi >> 16) & 0xFFu), s, m8s);
-  r[6] = (__bf16)__builtin_fmaf((float)(lo >> 24), s, m8s);
-  r[7] = (__bf16)__builtin_fmaf((float)(hi >> 24), s, m8s);
+  r[0] = (__bf16)__builtin_fmaf(half_lo_f(h0), g.s, g.m1032);
+  r[1] = (__bf16)__builtin_fmaf(half_lo_f(h1), g.s16, g.m72);
+  r[2] = (__bf16)__builtin_fmaf(half_lo_f(h2), g.s, g.m1032);
+  r[3] = (__bf16)__builtin_fmaf(half_lo_f(h3), g.s16, g.m72);
+  r[4] = (__bf16)__builtin_fmaf(half_hi_f(h0), g.s, g.m1032);
+  r[5] = (__bf16)__builtin_fmaf(half_hi_f(h1), g.s16, g.m72);
+  r[6] = (__bf16)__builtin_fmaf(half_hi_f(h2), g.s, g.m1032);
+  r[7] = (__bf16)__builtin_fmaf(half_hi_f(h3), g.s16, g.m72);
   return r;
 }
 
@@ -196,13 +223,14 @@ struct GemmItem {
 template <int NMT_MAX>
 __device__ __forceinline__ void gemm_group(const unsigned char *cur, const WStage &st, int nmt, int j, int hh,
                                            f32x16 (&acc)[4][2]) {
-  const float m0 = -8.0f * st.s0, m1 = -8.0f * st.s1;
+  const GroupScale g0(st.s0), g1(st.s1);
+  const uint32_t magic = 0x64006400u;
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
-    const bf16x8 b00 = dequant8(st.w0[2 * half], st.s0, m0);
-    const bf16x8 b01 = dequant8(st.w0[2 * half + 1], st.s0, m0);
-    const bf16x8 b10 = dequant8(st.w1[2 * half], st.s1, m1);
-    const bf16x8 b11 = dequant8(st.w1[2 * half + 1], st.s1, m1);
+    const bf16x8 b00 = dequant8(st.w0[2 * half], g0, magic);
+    const bf16x8 b01 = dequant8(st.w0[2 * half + 1], g0, magic);
+    const bf16x8 b10 = dequant8(st.w1[2 * half], g1, magic);
+    const bf16x8 b11 = dequant8(st.w1[2 * half + 1], g1, magic);
 #pragma unroll
     for (int mt = 0; mt < NMT_MAX; ++mt) {
       if (mt < nmt) {
