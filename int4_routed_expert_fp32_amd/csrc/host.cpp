@@ -350,7 +350,7 @@ static int forward_impl(colimoe_ctx *ctx, int32_t layer, const float *x, int32_t
   }
   float *h = (float *)(ctx->ws + ctx->wl.h);
   float *y = (float *)(ctx->ws + ctx->wl.y);
-  const bool fused = path != PATH_MFMA && down_fusable(D);
+  const bool fused = path == PATH_FP32 && down_fusable(D);
   if (path == PATH_MFMA) {
     int4 *list = (int4 *)(ctx->ws + ctx->wl.mblk);
     int32_t *mcount = (int32_t *)(ctx->ws + ctx->wl.mcount);
@@ -375,28 +375,23 @@ static int forward_impl(colimoe_ctx *ctx, int32_t layer, const float *x, int32_t
     float *xs = (float *)(ctx->ws + ctx->wl.xs);
     uint32_t *hq = (uint32_t *)(ctx->ws + ctx->wl.hq);
     float *hs = (float *)(ctx->ws + ctx->wl.hs);
+    float *wslot = (float *)(ctx->ws + ctx->wl.wslot);
     if (!x_encoded) {
       KTimer kt(ctx, K_ENCODE);
       if (launch_xquant(x, T, D.d, xq, xs, s) != hipSuccess) return COLIMOE_E_HIP;
     }
-    if (T == 1 && dec_supported(D)) {
-      {
-        KTimer kt(ctx, K_GATEUP);
-        if (launch_gateup_dec(L, D, U, w, xq, xs, hq, hs, (float *)(ctx->ws + ctx->wl.wslot), s) != hipSuccess)
-          return COLIMOE_E_HIP;
-      }
+    {
+      KTimer kt(ctx, K_GATEUP);
+      if (launch_gateup_tok(L, D, U, w, xq, xs, hq, hs, wslot, s) != hipSuccess) return COLIMOE_E_HIP;
+    }
+    if (down_dec_supported(D)) {
       KTimer kt(ctx, K_DOWN);
-      if (launch_down_dec(L, D, hq, hs, U, (const float *)(ctx->ws + ctx->wl.wslot), residual, s) != hipSuccess)
-        return COLIMOE_E_HIP;
+      if (launch_down_dec(L, D, hq, hs, U, wslot, residual, s) != hipSuccess) return COLIMOE_E_HIP;
       return COLIMOE_OK;  // combine done in the kernel
     }
     {
-      KTimer kt(ctx, K_GATEUP);
-      if (launch_gateup_fxp(L, D, xq, xs, U, h, hq, hs, nullptr, nullptr, s) != hipSuccess) return COLIMOE_E_HIP;
-    }
-    {
       KTimer kt(ctx, K_DOWN);
-      if (launch_down_fxp(L, D, hq, hs, U, y, w, residual, fused, s) != hipSuccess) return COLIMOE_E_HIP;
+      if (launch_down_tok(L, D, U, hq, hs, y, s) != hipSuccess) return COLIMOE_E_HIP;
     }
   } else {
     {
@@ -618,33 +613,6 @@ int colimoe_route_forward(colimoe_ctx *ctx, int32_t layer, const float *x, int32
   const colimoe_union *uu = u ? u : &uw;
   const bool encode = path == PATH_FXP;
   const Dims D = dims_of(ctx, T);
-  if (T == 1 && encode && dec_supported(D)) {
-    // one token: router (+ encoding of x), top-k with the union lists,
-    // gate/up, down with the combine folded in
-    const LayerDev L = layer_of(ctx, layer);
-    hipStream_t s = ctx->stream;
-    float *lg = (float *)(ctx->ws + ctx->wl.logits);
-    uint32_t *xq = (uint32_t *)(ctx->ws + ctx->wl.xq);
-    float *xs = (float *)(ctx->ws + ctx->wl.xs);
-    uint32_t *hq = (uint32_t *)(ctx->ws + ctx->wl.hq);
-    float *hs = (float *)(ctx->ws + ctx->wl.hs);
-    const UnionDev U = to_dev(uu);
-    {
-      KTimer kt(ctx, K_ROUTE);
-      if (launch_router_split(L, D, x, lg, xq, xs, s) != hipSuccess) return COLIMOE_E_HIP;
-    }
-    {
-      KTimer kt(ctx, K_TOPK);
-      if (launch_topk_union1(lg, D, idx, w, &U, s) != hipSuccess) return COLIMOE_E_HIP;
-    }
-    {
-      KTimer kt(ctx, K_GATEUP);
-      if (launch_gateup_dec(L, D, U, w, xq, xs, hq, hs, (float *)(ctx->ws + ctx->wl.wslot), s) != hipSuccess)
-        return COLIMOE_E_HIP;
-    }
-    KTimer kt(ctx, K_DOWN);
-    return hip_status(launch_down_dec(L, D, hq, hs, U, (const float *)(ctx->ws + ctx->wl.wslot), residual, s));
-  }
   rc = route_impl(ctx, layer, x, T, idx, w, uu, nullptr, encode);
   if (rc) return rc;
   return forward_impl(ctx, layer, x, T, idx, w, uu, residual, path, encode && T <= kRouteSplitMaxT);

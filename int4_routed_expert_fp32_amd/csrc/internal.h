@@ -120,23 +120,17 @@ hipError_t launch_combine(const Dims &D, const float *w, const UnionDev &U, cons
 // Fixed-point activation path (d >= 2048 and f >= 2048).
 bool fxp_supported(const Dims &D);
 hipError_t launch_xquant(const float *x, int T, int K, uint32_t *xq, float *xs, hipStream_t s);
-hipError_t launch_gateup_fxp(const LayerDev &L, const Dims &D, const uint32_t *xq, const float *xs,
-                             const UnionDev &U, float *h, uint32_t *hq, float *hs, float *g, float *u,
-                             hipStream_t s);
-hipError_t launch_down_fxp(const LayerDev &L, const Dims &D, const uint32_t *hq, const float *hs, const UnionDev &U,
-                           float *y, const float *w, float *residual, bool fused, hipStream_t s);
-// The one-token gate/up kernel covers d <= 8192 (at most 4 steps of 64
-// chunks per row); down needs at most 17 slots (k + shared).
-bool gateup_dec_supported(const Dims &D);
-inline bool dec_supported(const Dims &D) {
-  return D.T == 1 && D.k + D.n_shared <= 17 && D.f % 16 == 0 && gateup_dec_supported(D);
-}
-// Gate/up for one token, one wave per (tile, step), routing from U; records
-// each slot's gate weight (from w) in wslot[k + shared] for launch_down_dec.
-hipError_t launch_gateup_dec(const LayerDev &L, const Dims &D, const UnionDev &U, const float *w,
-                             const uint32_t *xq, const float *xs, uint32_t *hq, float *hs, float *wslot,
-                             hipStream_t s);
-// Down + combine for one token (T == 1), slot factors from wslot.
+// Fixed-point gate/up for any T (one wave per tile and step, weights loaded
+// once per call, tokens in chunks of 16); writes h's encoding to hq/hs and, for
+// T == 1, each slot's gate weight (from w) to wslot[k + shared].
+hipError_t launch_gateup_tok(const LayerDev &L, const Dims &D, const UnionDev &U, const float *w, const uint32_t *xq,
+                             const float *xs, uint32_t *hq, float *hs, float *wslot, hipStream_t s);
+// Fixed-point down for any T: y [T*k + T*shared][d] fp32 (combine in k_combine).
+hipError_t launch_down_tok(const LayerDev &L, const Dims &D, const UnionDev &U, const uint32_t *hq, const float *hs,
+                           float *y, hipStream_t s);
+// Down + combine for one token when a down row is one step (f <= 2048) and
+// k + shared <= 16 slots; slot gate weights from wslot.
+bool down_dec_supported(const Dims &D);
 hipError_t launch_down_dec(const LayerDev &L, const Dims &D, const uint32_t *hq, const float *hs, const UnionDev &U,
                            const float *wslot, float *residual, hipStream_t s);
 // Router for many tokens on the matrix cores (fp32), with S = router_splits(d)

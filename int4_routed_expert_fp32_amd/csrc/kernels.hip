@@ -770,177 +770,278 @@ __global__ __launch_bounds__(256) void k_xquant(const float *__restrict__ x, int
   for (int g = blockIdx.x * 256 + threadIdx.x; g < groups; g += gridDim.x * 256) xquant_group(x, K, g, q, qs);
 }
 
-// Gate/up on the fixed-point path.  A block of 4 waves owns 16 consecutive
-// h rows of one slot (4 tiles of 4 gate + 4 up rows); each wave runs all
-// chunk steps of its tile for up to MT tokens (per lane, each step's
-// contribution is formed from zero and the steps are added in order), then
-// the block encodes its 16 h values per token for the down kernel (one
-// 16-column group) and also writes h in fp32.
-template <int MT>
-__global__ __launch_bounds__(256) void k_gateup_fxp(LayerDev L, Dims D, const uint32_t *__restrict__ xq,
-                                                    const float *__restrict__ xs, UnionDev U, float *__restrict__ h,
-                                                    uint32_t *__restrict__ hq, float *__restrict__ hs,
-                                                    float *__restrict__ gdbg, float *__restrict__ udbg) {
-  __shared__ float hv[MT][16];
-  __shared__ uint32_t hw[MT][12];
-  __shared__ float hsc[MT];
-  __shared__ int orow_s[MT];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int C = D.d / kChunk, quads = D.f / 16;
-  const int nsteps = (C + 63) / 64;
-  const int nu = clamp_nu(U.n_unique, D);
-  const int items = (nu + D.n_shared) * quads;
-  const ExpertLayout EL = expert_layout(D.d, D.f);
-  for (int item = blockIdx.x; item < items; item += gridDim.x) {
-    const int s = item / quads, qd = item - s * quads;
-    const int ti = qd * 4 + wave;
-    int e, p0, p1;
-    if (!resolve_slot(D, U, nu, s, e, p0, p1)) continue;
-    const uint8_t *base = L.experts + (size_t)e * L.expert_stride;
-    for (int pg = p0; pg < p1; pg += MT) {
-      const int mcount = min(MT, p1 - pg);
-      int trow[MT];
+// Fixed-point GEMVs for any number of tokens.  A block owns 4 tiles (32
+// weight rows) of one slot and has, per tile, up to 4 waves that split the
+// row's steps (64 chunks each; wave sg takes steps sg, sg + 4, ...).  Each
+// wave loads its weights once and applies them to every token of the slot
+// (16 at a time, token rows staged in LDS).  Per token and step a lane's
+// contribution is formed from zero, reduced across the wave by the fixed
+// tree of reduce8_rows, and the per-step row values are added in step order:
+// v = ((R_0 + R_1) + R_2) + ...  This order is the same whatever T is, so a
+// token gives bit-identical results alone or batched.
+constexpr int kTokChunk = 16;
+
+template <int SPW, bool ONE>
+__device__ __forceinline__ void tile_tokens(const uint8_t *__restrict__ nib, const uint8_t *__restrict__ scp, int ti,
+                                            int K, int sg, int wpt, const int *tok, int mc,
+                                            const uint32_t *__restrict__ q, const float *__restrict__ qs,
+                                            float *red /* [NS][kTokChunk][8] of this tile */) {
+  const int lane = threadIdx.x & 63;
+  const int C = K / kChunk, NS = (C + 63) / 64;
+  uint4 W[SPW][kTileRows], S[SPW];
 #pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        int t = 0, orow = -1;
-        if (m < mcount) slot_token(D, U, nu, s, pg + m, t, orow);
-        trow[m] = t;
-        if (threadIdx.x == 0) orow_s[m] = orow;
+  for (int k = 0; k < SPW; ++k) {
+    const int j = sg + wpt * k, c = lane + 64 * j;
+    if (j < NS && c < C) load_step(nib, scp, ti, K, c, W[k], S[k]);
+  }
+  for (int m = 0; m < (ONE ? 1 : mc); ++m) {
+    const int row = tok[m];
+#pragma unroll
+    for (int k = 0; k < SPW; ++k) {
+      const int j = sg + wpt * k, c = lane + 64 * j;
+      if (j < NS) {
+        float acc[kTileRows];
+#pragma unroll
+        for (int r = 0; r < kTileRows; ++r) acc[r] = 0.0f;
+        if (c < C) fxp_step(W[k], S[k], q, qs, row, K, c, acc);
+        const float v = reduce8_rows(acc);
+        if ((lane & 7) == 7) red[((size_t)j * kTokChunk + m) * kTileRows + (lane >> 3)] = v;
       }
-      float acc[MT][kTileRows];
-#pragma unroll
-      for (int m = 0; m < MT; ++m)
-#pragma unroll
-        for (int r = 0; r < kTileRows; ++r) acc[m][r] = 0.0f;
-      // per lane: each step's contribution from zero, the steps added in order
-      for (int j = 0; j < nsteps; ++j) {
-        const int c = lane + 64 * j;
-        float part[MT][kTileRows];
-#pragma unroll
-        for (int m = 0; m < MT; ++m)
-#pragma unroll
-          for (int r = 0; r < kTileRows; ++r) part[m][r] = 0.0f;
-        if (c < C) {
-          uint4 W[kTileRows], S;
-          load_step(base + EL.gu_nib, base + EL.gu_sc, ti, D.d, c, W, S);
-#pragma unroll
-          for (int m = 0; m < MT; ++m)
-            if (m < mcount) fxp_step(W, S, xq, xs, trow[m], D.d, c, part[m]);
-        }
-#pragma unroll
-        for (int m = 0; m < MT; ++m)
-#pragma unroll
-          for (int r = 0; r < kTileRows; ++r) acc[m][r] = j == 0 ? part[m][r] : acc[m][r] + part[m][r];
-      }
-      if ((int)threadIdx.x < MT * 12) hw[threadIdx.x / 12][threadIdx.x % 12] = 0u;
-      __syncthreads();
-#pragma unroll
-      for (int m = 0; m < MT; ++m)
-        if (m < mcount) {
-          const float v = reduce8_rows(acc[m]);
-          const float u = bits_f(xor32(f_bits(v)));  // up rows sit 32 lanes above their gate rows
-          const int r = lane >> 3;
-          if ((lane & 7) == 7 && r < 4) {
-            const float hval = silu_f(v) * u;
-            hv[m][wave * 4 + r] = hval;
-            const int orow = orow_s[m];
-            if (orow >= 0) {
-              const size_t o = (size_t)orow * D.f + (size_t)ti * 4 + r;
-              h[o] = hval;
-              if (gdbg) {
-                gdbg[o] = v;
-                udbg[o] = u;
-              }
-            }
-          }
-        }
-      __syncthreads();
-      // encode the block's 16 h values of each token: one 16-lane row per token
-      {
-        const int m = threadIdx.x >> 4, i = threadIdx.x & 15;
-        const float v = (m < mcount) ? hv[m][i] : 0.0f;
-        uint32_t mb = f_bits(fabsf(v));
-        mb = max(mb, dpp<kRowRor8>(mb));
-        mb = max(mb, dpp<kRowRor4>(mb));
-        mb = max(mb, dpp<kRowRor2>(mb));
-        mb = max(mb, dpp<kRowRor1>(mb));
-        const float mx = bits_f(mb);
-        int E = mx > 0.0f ? ilogbf(mx) + 1 : 0;
-        E = E < -100 ? -100 : E;
-        if (m < mcount) {
-          const uint32_t B = (uint32_t)((int)__builtin_rintf(v * ldexpf(1.0f, 22 - E)) + 0x888888);
-#pragma unroll
-          for (int k = 0; k < 6; ++k) atomicOr(&hw[m][2 * k + (i >> 3)], (((B >> (4 * k)) & 15u) ^ 8u) << (4 * (i & 7)));
-          if (i == 0) hsc[m] = ldexpf(1.0f, E - 22);
-        }
-      }
-      __syncthreads();
-      if ((int)threadIdx.x < mcount * 12) {
-        const int m = threadIdx.x / 12, wd = threadIdx.x % 12;
-        const int orow = orow_s[m];
-        if (orow >= 0) {
-          hq[((size_t)orow * (D.f / kChunk) + (qd >> 1)) * kDigitWords + (qd & 1) * 12 + wd] = hw[m][wd];
-          if (wd == 0) hs[(size_t)orow * (D.f / 16) + qd] = hsc[m];
-        }
-      }
-      __syncthreads();
     }
   }
 }
 
-// Down projection on the fixed-point path, combine fused as in k_down_wide.
-template <int MT, bool FUSED, int NWMAX>
-__global__ __launch_bounds__(64 * NWMAX) void k_down_fxp(LayerDev L, Dims D, const uint32_t *__restrict__ hq,
-                                                         const float *__restrict__ hs, UnionDev U,
-                                                         float *__restrict__ y, const float *__restrict__ w,
-                                                         float *__restrict__ residual) {
-  extern __shared__ float ylds[];  // [T*k + T*n_shared][8] when FUSED
-  const int nw = blockDim.x >> 6, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int C = D.f / kChunk, tiles = D.d / kTileRows;
-  const int nu = clamp_nu(U.n_unique, D);
-  const int slots = nu + D.n_shared;
-  const int tk = D.T * D.k;
+// Gate/up: block = (slot, 16 h rows = 4 tiles); after each chunk of tokens the
+// block forms h = SiLU(g) * u per token and encodes its 16 values for the down
+// kernel.  For T == 1 the first block of each slot also records the slot's
+// gate weight in wslot (slot order, 1 for the shared expert).
+// WPT waves per tile (block = 4 * WPT waves).
+template <int SPW, bool ONE, int WPT>
+__global__ __launch_bounds__(256 * WPT) void k_gateup_tok(LayerDev L, Dims D, UnionDev U, const float *__restrict__ w,
+                                                     const uint32_t *__restrict__ xq, const float *__restrict__ xs,
+                                                     uint32_t *__restrict__ hq, float *__restrict__ hs,
+                                                     float *__restrict__ wslot) {
+  extern __shared__ float red[];  // [4 tiles][NS][kTokChunk][8]
+  __shared__ int slot_s[4];       // expert, p0, p1, nu
+  __shared__ int tok_s[kTokChunk], orow_s[kTokChunk];
+  __shared__ float hv[kTokChunk][16];
+  __shared__ uint32_t hw[kTokChunk][12];
+  __shared__ float hsc[kTokChunk];
+  const int wave = threadIdx.x >> 6;
+  const int C = D.d / kChunk, NS = (C + 63) / 64, wpt = WPT;
+  const int quads = D.f / 16;
+  const int s = blockIdx.x / quads, qd = blockIdx.x - s * quads;
+  const int tt = wave / wpt, sg = wave - tt * wpt, ti = qd * 4 + tt;
+  if (threadIdx.x == 0) {
+    const int nu = clamp_nu(U.n_unique, D);
+    int e = -1, p0 = 0, p1 = 0;
+    if (s < nu || (s == nu && D.n_shared)) {
+      if (!resolve_slot(D, U, nu, s, e, p0, p1) || p1 <= p0) e = -1;
+    }
+    slot_s[0] = e;
+    slot_s[1] = p0;
+    slot_s[2] = p1;
+    slot_s[3] = nu;
+    if (D.T == 1 && qd == 0 && e >= 0) {
+      float f = 1.0f;
+      if (s < nu) {
+        int js = U.pair_slot[p0];
+        js = js < 0 ? 0 : (js >= D.k ? D.k - 1 : js);  // caller-supplied lists stay in bounds
+        f = w[js];
+      }
+      wslot[s] = f;
+    }
+  }
+  __syncthreads();
+  const int e = slot_s[0], p0 = slot_s[1], p1 = slot_s[2], nu = slot_s[3];
+  if (e < 0) return;  // block-uniform
   const ExpertLayout EL = expert_layout(D.d, D.f);
-  for (int ti = blockIdx.x; ti < tiles; ti += gridDim.x) {
-    for (int s = wave; s < slots; s += nw) {
-      int e, p0, p1;
-      if (!resolve_slot(D, U, nu, s, e, p0, p1)) continue;
-      const uint8_t *base = L.experts + (size_t)e * L.expert_stride;
-      for (int pg = p0; pg < p1; pg += MT) {
-        const int mcount = min(MT, p1 - pg);
-        float acc[MT][kTileRows];
+  const uint8_t *base = L.experts + (size_t)e * L.expert_stride;
+  for (int pg = p0; pg < p1; pg += kTokChunk) {
+    const int mc = min(kTokChunk, p1 - pg);
+    if ((int)threadIdx.x < mc) {
+      int t, orow;
+      slot_token(D, U, nu, s, pg + threadIdx.x, t, orow);
+      tok_s[threadIdx.x] = t;
+      orow_s[threadIdx.x] = orow;
+    }
+    if ((int)threadIdx.x < kTokChunk * 12) hw[threadIdx.x / 12][threadIdx.x % 12] = 0u;
+    __syncthreads();
+    tile_tokens<SPW, ONE>(base + EL.gu_nib, base + EL.gu_sc, ti, D.d, sg, wpt, tok_s, mc, xq, xs,
+                     red + (size_t)tt * NS * kTokChunk * kTileRows);
+    __syncthreads();
+    // h for (token m, h row i): tile i/4, gate row i%4, up row i%4 + 4
+    if ((int)threadIdx.x < mc * 16) {
+      const int m = threadIdx.x >> 4, i = threadIdx.x & 15;
+      const float *rt = red + (size_t)(i >> 2) * NS * kTokChunk * kTileRows + (size_t)m * kTileRows;
+      float g = rt[i & 3], u = rt[(i & 3) + 4];
+      for (int j = 1; j < NS; ++j) {
+        g = g + rt[(size_t)j * kTokChunk * kTileRows + (i & 3)];
+        u = u + rt[(size_t)j * kTokChunk * kTileRows + (i & 3) + 4];
+      }
+      hv[m][i] = silu_f(g) * u;
+    }
+    __syncthreads();
+    // encode each token's 16 h values (one 16-lane row per token)
+    if ((int)threadIdx.x < kTokChunk * 16) {
+      const int m = threadIdx.x >> 4, i = threadIdx.x & 15;
+      const float v = m < mc ? hv[m][i] : 0.0f;
+      uint32_t mb = f_bits(fabsf(v));
+      mb = max(mb, dpp<kRowRor8>(mb));
+      mb = max(mb, dpp<kRowRor4>(mb));
+      mb = max(mb, dpp<kRowRor2>(mb));
+      mb = max(mb, dpp<kRowRor1>(mb));
+      const float mx = bits_f(mb);
+      int E = mx > 0.0f ? ilogbf(mx) + 1 : 0;
+      E = E < -100 ? -100 : E;
+      if (m < mc) {
+        const uint32_t B = (uint32_t)((int)__builtin_rintf(v * ldexpf(1.0f, 22 - E)) + 0x888888);
 #pragma unroll
-        for (int m = 0; m < MT; ++m)
-#pragma unroll
-          for (int r = 0; r < kTileRows; ++r) acc[m][r] = 0.0f;
-        for (int c = lane; c < ((C + 63) & ~63); c += 64) {
-          if (c < C) {
-            uint4 W[kTileRows], S;
-            load_step(base + EL.dn_nib, base + EL.dn_sc, ti, D.f, c, W, S);
-#pragma unroll
-            for (int m = 0; m < MT; ++m)
-              if (m < mcount) fxp_step(W, S, hq, hs, (s < nu) ? pg + m : tk + pg + m, D.f, c, acc[m]);
-          }
-        }
-#pragma unroll
-        for (int m = 0; m < MT; ++m)
-          if (m < mcount) {
-            const float v = reduce8_rows(acc[m]);
-            if ((lane & 7) == 7) {
-              const int orow = (s < nu) ? pg + m : tk + pg + m;
-              if (FUSED)
-                ylds[(size_t)orow * kTileRows + (lane >> 3)] = v;
-              else
-                y[(size_t)orow * D.d + (size_t)ti * kTileRows + (lane >> 3)] = v;
-            }
-          }
+        for (int k = 0; k < 6; ++k) atomicOr(&hw[m][2 * k + (i >> 3)], (((B >> (4 * k)) & 15u) ^ 8u) << (4 * (i & 7)));
+        if (i == 0) hsc[m] = ldexpf(1.0f, E - 22);
       }
     }
-    if (FUSED) {
-      __syncthreads();
-      combine_tile(D, U, nu, w, ylds, residual, ti);
-      __syncthreads();
+    __syncthreads();
+    if ((int)threadIdx.x < mc * 12) {
+      const int m = threadIdx.x / 12, wd = threadIdx.x % 12;
+      const int orow = orow_s[m];
+      if (orow >= 0) {
+        hq[((size_t)orow * (D.f / kChunk) + (qd >> 1)) * kDigitWords + (qd & 1) * 12 + wd] = hw[m][wd];
+        if (wd == 0) hs[(size_t)orow * (D.f / 16) + qd] = hsc[m];
+      }
     }
+    __syncthreads();
+  }
+}
+
+// Gate/up for one token, up to 4 steps per row (d <= 8192): one wave per
+// (tile, step), the same operations as k_gateup_tok with a single token, in
+// a lean form that keeps two blocks resident per CU.
+template <int NS>
+__global__ __launch_bounds__(256 * NS) void k_gateup_one(LayerDev L, Dims D, UnionDev U, const float *__restrict__ w,
+                                                         const uint32_t *__restrict__ xq,
+                                                         const float *__restrict__ xs, uint32_t *__restrict__ hq,
+                                                         float *__restrict__ hs, float *__restrict__ wslot) {
+  __shared__ float red[4][NS][kTileRows];
+  __shared__ int slot_s[2];  // expert, output row
+  __shared__ float hv[16];
+  __shared__ uint32_t hw[12];
+  __shared__ float hsc;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int C = D.d / kChunk, quads = D.f / 16;
+  const int s = blockIdx.x / quads, qd = blockIdx.x - s * quads;
+  const int tt = wave / NS, st = wave - tt * NS;
+  const int ti = qd * 4 + tt, c = lane + 64 * st;
+  if (threadIdx.x < 12) hw[threadIdx.x] = 0u;
+  if (threadIdx.x == 0) {
+    const int nu = clamp_nu(U.n_unique, D);
+    int e = -1, p0 = 0, p1 = 0;
+    if (s < nu || (s == nu && D.n_shared)) {
+      if (!resolve_slot(D, U, nu, s, e, p0, p1) || p1 <= p0) e = -1;
+    }
+    slot_s[0] = e;
+    slot_s[1] = s < nu ? p0 : D.k;
+    if (qd == 0 && e >= 0) {
+      float f = 1.0f;
+      if (s < nu) {
+        int js = U.pair_slot[p0];
+        js = js < 0 ? 0 : (js >= D.k ? D.k - 1 : js);  // caller-supplied lists stay in bounds
+        f = w[js];
+      }
+      wslot[s] = f;
+    }
+  }
+  __syncthreads();
+  const int e = slot_s[0], orow = slot_s[1];
+  if (e < 0) return;  // block-uniform
+  const ExpertLayout EL = expert_layout(D.d, D.f);
+  const uint8_t *base = L.experts + (size_t)e * L.expert_stride;
+  float acc[kTileRows];
+#pragma unroll
+  for (int r = 0; r < kTileRows; ++r) acc[r] = 0.0f;
+  if (c < C) {
+    uint4 W[kTileRows], S;
+    load_step(base + EL.gu_nib, base + EL.gu_sc, ti, D.d, c, W, S);
+    fxp_step(W, S, xq, xs, 0, D.d, c, acc);
+  }
+  const float v = reduce8_rows(acc);
+  if ((lane & 7) == 7) red[tt][st][lane >> 3] = v;
+  __syncthreads();
+  if (threadIdx.x < 16) {
+    const int i = threadIdx.x, t4 = i >> 2, r = i & 3;
+    float g = red[t4][0][r], u = red[t4][0][r + 4];
+#pragma unroll
+    for (int j = 1; j < NS; ++j) {
+      g = g + red[t4][j][r];
+      u = u + red[t4][j][r + 4];
+    }
+    const float hval = silu_f(g) * u;
+    uint32_t mb = f_bits(fabsf(hval));
+    mb = max(mb, dpp<kRowRor8>(mb));
+    mb = max(mb, dpp<kRowRor4>(mb));
+    mb = max(mb, dpp<kRowRor2>(mb));
+    mb = max(mb, dpp<kRowRor1>(mb));
+    const float mx = bits_f(mb);
+    int E = mx > 0.0f ? ilogbf(mx) + 1 : 0;
+    E = E < -100 ? -100 : E;
+    const uint32_t B = (uint32_t)((int)__builtin_rintf(hval * ldexpf(1.0f, 22 - E)) + 0x888888);
+#pragma unroll
+    for (int k = 0; k < 6; ++k) atomicOr(&hw[2 * k + (i >> 3)], (((B >> (4 * k)) & 15u) ^ 8u) << (4 * (i & 7)));
+    if (i == 0) hsc = ldexpf(1.0f, E - 22);
+  }
+  __syncthreads();
+  if (threadIdx.x < 12) {
+    hq[((size_t)orow * (D.f / kChunk) + (qd >> 1)) * kDigitWords + (qd & 1) * 12 + threadIdx.x] = hw[threadIdx.x];
+    if (threadIdx.x == 0) hs[(size_t)orow * (D.f / 16) + qd] = hsc;
+  }
+}
+
+// Down: block = (slot, 4 output tiles = 32 rows); y[output row of the pair]
+// for each of the slot's pairs (the shared expert: rows T*k + t).  The
+// combine runs afterwards in k_combine (or, for one token, in k_down_dec1).
+template <int SPW, bool ONE, int WPT>
+__global__ __launch_bounds__(256 * WPT) void k_down_tok(LayerDev L, Dims D, UnionDev U, const uint32_t *__restrict__ hq,
+                                                   const float *__restrict__ hs, float *__restrict__ y) {
+  extern __shared__ float red[];  // [4 tiles][NS][kTokChunk][8]
+  __shared__ int slot_s[4];
+  __shared__ int row_s[kTokChunk];
+  const int wave = threadIdx.x >> 6;
+  const int C = D.f / kChunk, NS = (C + 63) / 64, wpt = WPT;
+  const int groups = D.d / 32;
+  const int s = blockIdx.x / groups, qd = blockIdx.x - s * groups;
+  const int tt = wave / wpt, sg = wave - tt * wpt, ti = qd * 4 + tt;
+  if (threadIdx.x == 0) {
+    const int nu = clamp_nu(U.n_unique, D);
+    int e = -1, p0 = 0, p1 = 0;
+    if (s < nu || (s == nu && D.n_shared)) {
+      if (!resolve_slot(D, U, nu, s, e, p0, p1) || p1 <= p0) e = -1;
+    }
+    slot_s[0] = e;
+    slot_s[1] = p0;
+    slot_s[2] = p1;
+    slot_s[3] = nu;
+  }
+  __syncthreads();
+  const int e = slot_s[0], p0 = slot_s[1], p1 = slot_s[2], nu = slot_s[3];
+  if (e < 0) return;  // block-uniform
+  const ExpertLayout EL = expert_layout(D.d, D.f);
+  const uint8_t *base = L.experts + (size_t)e * L.expert_stride;
+  const int tk = D.T * D.k;
+  for (int pg = p0; pg < p1; pg += kTokChunk) {
+    const int mc = min(kTokChunk, p1 - pg);
+    if ((int)threadIdx.x < mc) row_s[threadIdx.x] = s < nu ? pg + threadIdx.x : tk + pg + threadIdx.x;
+    __syncthreads();
+    tile_tokens<SPW, ONE>(base + EL.dn_nib, base + EL.dn_sc, ti, D.f, sg, wpt, row_s, mc, hq, hs,
+                     red + (size_t)tt * NS * kTokChunk * kTileRows);
+    __syncthreads();
+    for (int q = threadIdx.x; q < mc * 32; q += blockDim.x) {
+      const int m = q >> 5, i = q & 31;  // output row 32*qd + i
+      const float *rt = red + (size_t)(i >> 3) * NS * kTokChunk * kTileRows + (size_t)m * kTileRows + (i & 7);
+      float v = rt[0];
+      for (int j = 1; j < NS; ++j) v = v + rt[(size_t)j * kTokChunk * kTileRows];
+      y[(size_t)row_s[m] * D.d + (size_t)qd * 32 + i] = v;
+    }
+    __syncthreads();
   }
 }
 
@@ -1028,102 +1129,6 @@ __global__ __launch_bounds__(64) void k_topk_union1(const float *__restrict__ lo
   if (with_union) union_one_token(ids, D, U);
 }
 
-// Gate/up for one token.  A block owns one 16-row encoding group of one slot
-// (4 tiles) and has one wave per (tile, step): every wave issues its step's
-// 8 x 1 KB of weights at once, so the whole kernel keeps many loads in flight
-// while earlier waves compute.  Step contributions meet in LDS and are added
-// in step order, then each tile is reduced, SiLU(g) * u formed and the group
-// encoded for the down kernel — per row the operations of k_gateup_fxp.  The
-// first block of each slot also records the slot's gate weight in wslot
-// (slot order; 1 for the shared expert) for the down kernel's combine.
-template <int NS>
-__global__ __launch_bounds__(256 * NS) void k_gateup_dec(LayerDev L, Dims D, UnionDev U, const float *__restrict__ w,
-                                                         const uint32_t *__restrict__ xq,
-                                                         const float *__restrict__ xs, uint32_t *__restrict__ hq,
-                                                         float *__restrict__ hs, float *__restrict__ wslot) {
-  __shared__ float part[4 * NS][kTileRows][64];
-  __shared__ int slot_s[2];  // expert, output row
-  __shared__ float hv[16];
-  __shared__ uint32_t hw[12];
-  __shared__ float hsc;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int C = D.d / kChunk, quads = D.f / 16;
-  const int s = blockIdx.x / quads, qd = blockIdx.x - s * quads;
-  const int tt = wave / NS, st = wave - tt * NS;
-  const int ti = qd * 4 + tt, c = lane + 64 * st;
-  if (threadIdx.x < 12) hw[threadIdx.x] = 0u;
-  if (threadIdx.x == 0) {
-    const int nu = clamp_nu(U.n_unique, D);
-    int e = -1, p0 = 0, p1 = 0;
-    if (s < nu || (s == nu && D.n_shared)) {
-      if (!resolve_slot(D, U, nu, s, e, p0, p1) || p1 <= p0) e = -1;
-    }
-    slot_s[0] = e;
-    slot_s[1] = s < nu ? p0 : D.k;
-    if (qd == 0 && e >= 0) {
-      float f = 1.0f;
-      if (s < nu) {
-        int js = U.pair_slot[p0];
-        js = js < 0 ? 0 : (js >= D.k ? D.k - 1 : js);  // caller-supplied lists stay in bounds
-        f = w[js];
-      }
-      wslot[s] = f;
-    }
-  }
-  __syncthreads();
-  const int e = slot_s[0], orow = slot_s[1];
-  if (e < 0) return;  // block-uniform
-  const ExpertLayout EL = expert_layout(D.d, D.f);
-  const uint8_t *base = L.experts + (size_t)e * L.expert_stride;
-  float acc[kTileRows];
-#pragma unroll
-  for (int r = 0; r < kTileRows; ++r) acc[r] = 0.0f;
-  if (c < C) {
-    uint4 W[kTileRows], S;
-    load_step(base + EL.gu_nib, base + EL.gu_sc, ti, D.d, c, W, S);
-    fxp_step(W, S, xq, xs, 0, D.d, c, acc);
-  }
-#pragma unroll
-  for (int r = 0; r < kTileRows; ++r) part[wave][r][lane] = acc[r];
-  __syncthreads();
-  if (st == 0) {
-    float tot[kTileRows];
-#pragma unroll
-    for (int r = 0; r < kTileRows; ++r) {
-      tot[r] = part[wave][r][lane];
-#pragma unroll
-      for (int j = 1; j < NS; ++j) tot[r] = tot[r] + part[wave + j][r][lane];
-    }
-    const float v = reduce8_rows(tot);
-    const float up = bits_f(xor32(f_bits(v)));  // up rows sit 32 lanes above their gate rows
-    const int r = lane >> 3;
-    if ((lane & 7) == 7 && r < 4) hv[tt * 4 + r] = silu_f(v) * up;
-  }
-  __syncthreads();
-  // encode the block's 16 h values (one 16-lane row), as k_gateup_fxp does
-  if (threadIdx.x < 16) {
-    const int i = threadIdx.x;
-    const float v = hv[i];
-    uint32_t mb = f_bits(fabsf(v));
-    mb = max(mb, dpp<kRowRor8>(mb));
-    mb = max(mb, dpp<kRowRor4>(mb));
-    mb = max(mb, dpp<kRowRor2>(mb));
-    mb = max(mb, dpp<kRowRor1>(mb));
-    const float mx = bits_f(mb);
-    int E = mx > 0.0f ? ilogbf(mx) + 1 : 0;
-    E = E < -100 ? -100 : E;
-    const uint32_t B = (uint32_t)((int)__builtin_rintf(v * ldexpf(1.0f, 22 - E)) + 0x888888);
-#pragma unroll
-    for (int k = 0; k < 6; ++k) atomicOr(&hw[2 * k + (i >> 3)], (((B >> (4 * k)) & 15u) ^ 8u) << (4 * (i & 7)));
-    if (i == 0) hsc = ldexpf(1.0f, E - 22);
-  }
-  __syncthreads();
-  if (threadIdx.x < 12) {
-    hq[((size_t)orow * (D.f / kChunk) + (qd >> 1)) * kDigitWords + (qd & 1) * 12 + threadIdx.x] = hw[threadIdx.x];
-    if (threadIdx.x == 0) hs[(size_t)orow * (D.f / 16) + qd] = hsc;
-  }
-}
-
 // Weights and activation digits of one (slot, step) of the down projection,
 // for the decode stream below.
 __device__ __forceinline__ void dec_down_slot(const LayerDev &L, const Dims &D, const UnionDev &U, int nu,
@@ -1184,70 +1189,7 @@ __global__ __launch_bounds__(1024) void k_down_dec1(LayerDev L, Dims D, const ui
   }
 }
 
-// Down + combine for one token, longer down rows: a block of 3 waves owns one
-// 8-row output tile; wave w streams slots w, w+3, ... (next step's weights and
-// digits in flight) and leaves each slot's 8 outputs in LDS; wave 0 combines
-// as above.
-constexpr int kDecMaxSlots = 17;
-
-template <int NSTEPS>
-__global__ __launch_bounds__(192) void k_down_dec(LayerDev L, Dims D, const uint32_t *__restrict__ hq,
-                                                  const float *__restrict__ hs, UnionDev U,
-                                                  const float *__restrict__ wslot, float *__restrict__ residual) {
-  __shared__ float vb[kDecMaxSlots][kTileRows];
-  __shared__ int ok_s[kDecMaxSlots];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int ti = blockIdx.x, C = D.f / kChunk;
-  const int nu = clamp_nu(U.n_unique, D);
-  const int slots = nu + D.n_shared;
-  const ExpertLayout EL = expert_layout(D.d, D.f);
-  const int mine = slots > wave ? (slots - wave + 2) / 3 : 0;  // slots wave, wave+3, ...
-  const int nst = mine * NSTEPS;
-  uint4 W[2][kTileRows], S[2];
-  uint32_t dg[2][kDigitWords];
-  float dsc[2][2];
-  float acc[kTileRows];
-#pragma unroll
-  for (int rr = 0; rr < kTileRows; ++rr) acc[rr] = 0.0f;
-  if (nst > 0) dec_down_slot(L, D, U, nu, EL, wave, ti, lane, W[0], S[0], dg[0], dsc[0], hq, hs);
-  for (int q0 = 0; q0 < nst; q0 += 2) {
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int q = q0 + half;
-      if (q < nst) {
-        if (q + 1 < nst)
-          dec_down_slot(L, D, U, nu, EL, wave + 3 * ((q + 1) / NSTEPS), ti, lane + 64 * ((q + 1) % NSTEPS),
-                        W[half ^ 1], S[half ^ 1], dg[half ^ 1], dsc[half ^ 1], hq, hs);
-        const int sl = wave + 3 * (q / NSTEPS), j = q % NSTEPS;
-        const int c = lane + 64 * j;
-        int e, p0, p1;
-        const bool ok = resolve_slot(D, U, nu, sl, e, p0, p1) && p1 > p0;
-        if (ok && c < C) {
-#pragma unroll
-          for (int rr = 0; rr < kTileRows; ++rr)
-            acc[rr] = fxp_chunk(W[half][rr], dg[half], dsc[half], tile_scale(S[half], rr), acc[rr]);
-        }
-        if (j == NSTEPS - 1) {
-          const float v = reduce8_rows(acc);
-          if ((lane & 7) == 7) vb[sl][lane >> 3] = v;
-          if (lane == 0) ok_s[sl] = ok;
-#pragma unroll
-          for (int rr = 0; rr < kTileRows; ++rr) acc[rr] = 0.0f;
-        }
-      }
-    }
-  }
-  __syncthreads();
-  if (wave == 0 && lane < kTileRows) {
-    float out = residual[(size_t)ti * kTileRows + lane];
-    for (int sl = 0; sl < slots; ++sl) {
-      if (!ok_s[sl]) continue;
-      const float v = vb[sl][lane];
-      out = sl < nu ? __builtin_fmaf(wslot[sl], v, out) : out + v;
-    }
-    residual[(size_t)ti * kTileRows + lane] = out;
-  }
-}
+constexpr int kDecMaxSlots = 16;
 
 // ------------------------------------------------- narrow shapes (K < 2048)
 // Rows shorter than 64 chunks: LPR lanes per row (a power of two >= K/32),
@@ -1643,86 +1585,89 @@ hipError_t launch_xquant(const float *x, int T, int K, uint32_t *xq, float *xs, 
   return hipGetLastError();
 }
 
-static hipError_t gateup_fxp_impl(const LayerDev &L, const Dims &D, const uint32_t *xq, const float *xs,
-                                  const UnionDev &U, float *h, uint32_t *hq, float *hs, float *g, float *u,
-                                  hipStream_t s) {
-  const long long items = (long long)slots_max(D) * (D.f / 16);
-  dim3 grid(grid_cap(items, 16384)), block(256);
-  if (D.T == 1)
-    k_gateup_fxp<1><<<grid, block, 0, s>>>(L, D, xq, xs, U, h, hq, hs, g, u);
-  else
-    k_gateup_fxp<8><<<grid, block, 0, s>>>(L, D, xq, xs, U, h, hq, hs, g, u);
-  return hipGetLastError();
+static size_t tok_lds(int K) {
+  const int NS = (K / kChunk + 63) / 64;
+  return (size_t)4 * NS * kTokChunk * kTileRows * 4;
 }
 
-hipError_t launch_gateup_fxp(const LayerDev &L, const Dims &D, const uint32_t *xq, const float *xs,
-                             const UnionDev &U, float *h, uint32_t *hq, float *hs, float *g, float *u,
-                             hipStream_t s) {
-  if (D.T <= 0) return hipSuccess;
-  return gateup_fxp_impl(L, D, xq, xs, U, h, hq, hs, g, u, s);
+template <int SPW, bool ONE>
+static void gateup_tok_launch(int wpt, int grid, size_t lds, hipStream_t s, const LayerDev &L, const Dims &D,
+                              const UnionDev &U, const float *w, const uint32_t *xq, const float *xs, uint32_t *hq,
+                              float *hs, float *wslot) {
+  switch (wpt) {
+    case 1: k_gateup_tok<SPW, ONE, 1><<<grid, 256, lds, s>>>(L, D, U, w, xq, xs, hq, hs, wslot); break;
+    case 2: k_gateup_tok<SPW, ONE, 2><<<grid, 512, lds, s>>>(L, D, U, w, xq, xs, hq, hs, wslot); break;
+    case 3: k_gateup_tok<SPW, ONE, 3><<<grid, 768, lds, s>>>(L, D, U, w, xq, xs, hq, hs, wslot); break;
+    default: k_gateup_tok<SPW, ONE, 4><<<grid, 1024, lds, s>>>(L, D, U, w, xq, xs, hq, hs, wslot); break;
+  }
 }
 
-hipError_t launch_down_fxp(const LayerDev &L, const Dims &D, const uint32_t *hq, const float *hs, const UnionDev &U,
-                           float *y, const float *w, float *residual, bool fused, hipStream_t s) {
+template <int SPW, bool ONE>
+static void down_tok_launch(int wpt, int grid, size_t lds, hipStream_t s, const LayerDev &L, const Dims &D,
+                            const UnionDev &U, const uint32_t *hq, const float *hs, float *y) {
+  switch (wpt) {
+    case 1: k_down_tok<SPW, ONE, 1><<<grid, 256, lds, s>>>(L, D, U, hq, hs, y); break;
+    case 2: k_down_tok<SPW, ONE, 2><<<grid, 512, lds, s>>>(L, D, U, hq, hs, y); break;
+    case 3: k_down_tok<SPW, ONE, 3><<<grid, 768, lds, s>>>(L, D, U, hq, hs, y); break;
+    default: k_down_tok<SPW, ONE, 4><<<grid, 1024, lds, s>>>(L, D, U, hq, hs, y); break;
+  }
+}
+
+hipError_t launch_gateup_tok(const LayerDev &L, const Dims &D, const UnionDev &U, const float *w, const uint32_t *xq,
+                             const float *xs, uint32_t *hq, float *hs, float *wslot, hipStream_t s) {
   if (D.T <= 0) return hipSuccess;
-  const bool mt1 = D.T == 1;
-  const int tiles = D.d / kTileRows;
-  const int nwmax = mt1 ? 9 : 8;
-  int nw = slots_max(D);
-  nw = nw < 1 ? 1 : nw > nwmax ? nwmax : nw;
-  dim3 grid(tiles), block(64 * nw);
-  const size_t lds = fused ? fused_rows(D) * kTileRows * 4 : 0;
-  if (fused) {
-    if (mt1)
-      k_down_fxp<1, true, 9><<<grid, block, lds, s>>>(L, D, hq, hs, U, y, w, residual);
-    else
-      k_down_fxp<8, true, 8><<<grid, block, lds, s>>>(L, D, hq, hs, U, y, w, residual);
+  const int NS = (D.d / kChunk + 63) / 64, wpt = NS < 4 ? NS : 4;
+  const int slots = (D.T * D.k < D.E ? D.T * D.k : D.E) + D.n_shared;
+  const int grid = slots * (D.f / 16);
+  const size_t lds = tok_lds(D.d);
+  if (D.T == 1) {
+    if (NS <= 4) {
+      switch (NS) {
+        case 1: k_gateup_one<1><<<grid, 256, 0, s>>>(L, D, U, w, xq, xs, hq, hs, wslot); break;
+        case 2: k_gateup_one<2><<<grid, 512, 0, s>>>(L, D, U, w, xq, xs, hq, hs, wslot); break;
+        case 3: k_gateup_one<3><<<grid, 768, 0, s>>>(L, D, U, w, xq, xs, hq, hs, wslot); break;
+        default: k_gateup_one<4><<<grid, 1024, 0, s>>>(L, D, U, w, xq, xs, hq, hs, wslot); break;
+      }
+    } else
+      gateup_tok_launch<2, true>(wpt, grid, lds, s, L, D, U, w, xq, xs, hq, hs, wslot);
   } else {
-    if (mt1)
-      k_down_fxp<1, false, 9><<<grid, block, 0, s>>>(L, D, hq, hs, U, y, w, residual);
+    if (NS <= 4)
+      gateup_tok_launch<1, false>(wpt, grid, lds, s, L, D, U, w, xq, xs, hq, hs, wslot);
     else
-      k_down_fxp<8, false, 8><<<grid, block, 0, s>>>(L, D, hq, hs, U, y, w, residual);
+      gateup_tok_launch<2, false>(wpt, grid, lds, s, L, D, U, w, xq, xs, hq, hs, wslot);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_down_tok(const LayerDev &L, const Dims &D, const UnionDev &U, const uint32_t *hq, const float *hs,
+                           float *y, hipStream_t s) {
+  if (D.T <= 0) return hipSuccess;
+  const int NS = (D.f / kChunk + 63) / 64, wpt = NS < 4 ? NS : 4;
+  const int slots = (D.T * D.k < D.E ? D.T * D.k : D.E) + D.n_shared;
+  const int grid = slots * (D.d / 32);
+  const size_t lds = tok_lds(D.f);
+  if (D.T == 1) {
+    if (NS <= 4)
+      down_tok_launch<1, true>(wpt, grid, lds, s, L, D, U, hq, hs, y);
+    else
+      down_tok_launch<2, true>(wpt, grid, lds, s, L, D, U, hq, hs, y);
+  } else {
+    if (NS <= 4)
+      down_tok_launch<1, false>(wpt, grid, lds, s, L, D, U, hq, hs, y);
+    else
+      down_tok_launch<2, false>(wpt, grid, lds, s, L, D, U, hq, hs, y);
+  }
+  return hipGetLastError();
+}
+
+bool down_dec_supported(const Dims &D) {
+  return D.T == 1 && (D.f / kChunk + 63) / 64 == 1 && D.k + D.n_shared <= kDecMaxSlots;
 }
 
 hipError_t launch_down_dec(const LayerDev &L, const Dims &D, const uint32_t *hq, const float *hs, const UnionDev &U,
                            const float *wslot, float *residual, hipStream_t s) {
-  if (D.T != 1 || D.k + D.n_shared > kDecMaxSlots) return hipErrorInvalidValue;
-  const int nsteps = (D.f / kChunk + 63) / 64;
-  const int tiles = D.d / kTileRows;
-  const int slots = D.k + D.n_shared;
-  if (nsteps == 1 && slots <= 16) {
-    k_down_dec1<<<tiles, 64 * slots, 0, s>>>(L, D, hq, hs, U, wslot, residual);
-    return hipGetLastError();
-  }
-  switch (nsteps) {
-    case 1: k_down_dec<1><<<tiles, 192, 0, s>>>(L, D, hq, hs, U, wslot, residual); break;
-    case 2: k_down_dec<2><<<tiles, 192, 0, s>>>(L, D, hq, hs, U, wslot, residual); break;
-    case 3: k_down_dec<3><<<tiles, 192, 0, s>>>(L, D, hq, hs, U, wslot, residual); break;
-    case 4: k_down_dec<4><<<tiles, 192, 0, s>>>(L, D, hq, hs, U, wslot, residual); break;
-    case 5: k_down_dec<5><<<tiles, 192, 0, s>>>(L, D, hq, hs, U, wslot, residual); break;
-    case 6: k_down_dec<6><<<tiles, 192, 0, s>>>(L, D, hq, hs, U, wslot, residual); break;
-    case 7: k_down_dec<7><<<tiles, 192, 0, s>>>(L, D, hq, hs, U, wslot, residual); break;
-    default: k_down_dec<8><<<tiles, 192, 0, s>>>(L, D, hq, hs, U, wslot, residual); break;
-  }
-  return hipGetLastError();
-}
-
-bool gateup_dec_supported(const Dims &D) { return (D.d / kChunk + 63) / 64 <= 4; }
-
-hipError_t launch_gateup_dec(const LayerDev &L, const Dims &D, const UnionDev &U, const float *w,
-                             const uint32_t *xq, const float *xs, uint32_t *hq, float *hs, float *wslot,
-                             hipStream_t s) {
-  if (D.T != 1 || D.f % 16 != 0 || !gateup_dec_supported(D)) return hipErrorInvalidValue;
-  const int ns = (D.d / kChunk + 63) / 64;
-  const int grid = (D.k + D.n_shared) * (D.f / 16);
-  switch (ns) {
-    case 1: k_gateup_dec<1><<<grid, 256, 0, s>>>(L, D, U, w, xq, xs, hq, hs, wslot); break;
-    case 2: k_gateup_dec<2><<<grid, 512, 0, s>>>(L, D, U, w, xq, xs, hq, hs, wslot); break;
-    case 3: k_gateup_dec<3><<<grid, 768, 0, s>>>(L, D, U, w, xq, xs, hq, hs, wslot); break;
-    default: k_gateup_dec<4><<<grid, 1024, 0, s>>>(L, D, U, w, xq, xs, hq, hs, wslot); break;
-  }
+  if (!down_dec_supported(D)) return hipErrorInvalidValue;
+  k_down_dec1<<<D.d / kTileRows, 64 * (D.k + D.n_shared), 0, s>>>(L, D, hq, hs, U, wslot, residual);
   return hipGetLastError();
 }
 
