@@ -60,6 +60,10 @@ def kernel_source_sha():
     return h.hexdigest()
 
 
+# the gate/up kernel of a one-token call (d = 6144: three 64-chunk steps per row)
+DECODE_GATEUP_KERNEL = "k_gateup_one<3>"
+
+
 def measured_traffic(kernel):
     """HBM bytes per launch of `kernel` from the committed counter summary, or
     None when the kernel sources changed since the counters were taken."""
@@ -318,8 +322,8 @@ def main():
     gbs = int4_bytes / (ms_step * 1e-3) / 1e9
     gu_gbs = experts_touched * gu_bytes / (kern["gateup"]["avg_us"] * 1e-6) / 1e9
     dn_gbs = experts_touched * dn_bytes / (kern["down"]["avg_us"] * 1e-6) / 1e9
-    roofline = dict(bound="hbm", kernel="k_gateup_dec<3>", achieved=round(gu_gbs, 1), peak=HBM_PEAK_GBS,
-                    unit="GB/s", frac=round(gu_gbs / HBM_PEAK_GBS, 4), traffic=measured_traffic("k_gateup_dec<3>"),
+    roofline = dict(bound="hbm", kernel=DECODE_GATEUP_KERNEL, achieved=round(gu_gbs, 1), peak=HBM_PEAK_GBS,
+                    unit="GB/s", frac=round(gu_gbs / HBM_PEAK_GBS, 4), traffic=measured_traffic(DECODE_GATEUP_KERNEL),
                     bytes_per_launch=experts_touched * gu_bytes, avg_launch_us=round(kern["gateup"]["avg_us"], 3))
 
     cpu = None
