@@ -8,6 +8,20 @@
 
 namespace colimoe {
 
+// Plain LLVM vector for 16-byte loads: copies of it stay in registers (the
+// uint4 class type is copied through memory, which keeps staged data off
+// registers).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer resource over `bytes` bytes at p (p wave-uniform): loads through it
+// take a per-lane offset plus a scalar offset, and loads past the end read 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t wave_rsrc(const void *p, uint32_t bytes) {
+  const uint64_t a = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc((void *)(((uint64_t)hi << 32) | lo), (short)0, (int)bytes, 0x00020000);
+}
+
 __device__ __forceinline__ float bits_f(uint32_t v) { return __uint_as_float(v); }
 __device__ __forceinline__ uint32_t f_bits(float v) { return __float_as_uint(v); }
 

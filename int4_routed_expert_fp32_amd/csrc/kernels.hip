@@ -1129,49 +1129,49 @@ __global__ __launch_bounds__(64) void k_topk_union1(const float *__restrict__ lo
   if (with_union) union_one_token(ids, D, U);
 }
 
-// Weights and activation digits of one (slot, step) of the down projection,
-// for the decode stream below.
-__device__ __forceinline__ void dec_down_slot(const LayerDev &L, const Dims &D, const UnionDev &U, int nu,
-                                              const ExpertLayout &EL, int s, int ti, int c, uint4 (&W)[kTileRows],
-                                              uint4 &S, uint32_t (&dg)[kDigitWords], float (&dsc)[2],
-                                              const uint32_t *__restrict__ hq, const float *__restrict__ hs) {
-  int e, p0, p1;
-  if (!resolve_slot(D, U, nu, s, e, p0, p1)) e = -1;
-  if (e < 0 || p1 <= p0 || c >= D.f / kChunk) return;
-  const uint8_t *base = L.experts + (size_t)e * L.expert_stride;
-  load_step(base + EL.dn_nib, base + EL.dn_sc, ti, D.f, c, W, S);
-  load_digits(hq, hs, s < nu ? p0 : D.T * D.k, D.f, c, dg, dsc);
-}
-
 // Down + combine for one token when a down row is one step (f <= 2048): a
 // block of one wave per slot owns one 8-row output tile; every wave issues its
 // slot's weights and digits at once and leaves the slot's 8 outputs in LDS;
 // wave 0 folds them into the residual in slot order (routed experts by
 // ascending id weighted by their gate weight, taken from wslot as recorded by
 // the gate/up kernel, then the shared expert), as the general kernels do.
-__global__ __launch_bounds__(1024) void k_down_dec1(LayerDev L, Dims D, const uint32_t *__restrict__ hq,
-                                                    const float *__restrict__ hs, UnionDev U,
-                                                    const float *__restrict__ wslot, float *__restrict__ residual) {
+// The weights come through buffer loads (one lane offset, the row in the
+// scalar offset), which keeps the kernel small enough in registers for three
+// blocks per CU: the whole grid of d/8 blocks is resident at once.  Every
+// lane computes (a lane past the row end reads a valid chunk and its result
+// is replaced by 0), so no load sits behind a branch.
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(6))) void k_down_dec1(
+    LayerDev L, Dims D, const uint32_t *__restrict__ hq, const float *__restrict__ hs, UnionDev U,
+    const float *__restrict__ wslot, float *__restrict__ residual) {
   __shared__ float vb[16][kTileRows];
   __shared__ int ok_s[16];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int ti = blockIdx.x, C = D.f / kChunk;
   const int nu = clamp_nu(U.n_unique, D);
   const int slots = nu + D.n_shared;
   const ExpertLayout EL = expert_layout(D.d, D.f);
   if (wave < slots) {
-    uint4 W[kTileRows], S;
-    uint32_t dg[kDigitWords];
-    float dsc[2];
-    dec_down_slot(L, D, U, nu, EL, wave, ti, lane, W, S, dg, dsc, hq, hs);
     int e, p0, p1;
     const bool ok = resolve_slot(D, U, nu, wave, e, p0, p1) && p1 > p0;
+    const uint8_t *base = L.experts + (size_t)(ok ? e : 0) * L.expert_stride;
+    const __amdgpu_buffer_rsrc_t rn = wave_rsrc(base + EL.dn_nib, (uint32_t)(EL.dn_sc - EL.dn_nib));
+    const __amdgpu_buffer_rsrc_t rs = wave_rsrc(base + EL.dn_sc, (uint32_t)(EL.bytes - EL.dn_sc));
+    const int cl = lane < C ? lane : C - 1;
+    // chunk_offset with one step per row: tile, then row r at r * C * 16 bytes
+    const int tb = ti * kTileRows * (D.f / 2);
+    u32x4 W[kTileRows];
+#pragma unroll
+    for (int r = 0; r < kTileRows; ++r) W[r] = __builtin_amdgcn_raw_buffer_load_b128(rn, cl * 16, tb + r * C * 16, 0);
+    const u32x4 Sv = __builtin_amdgcn_raw_buffer_load_b128(rs, (cl >> 1) * 16, ti * (D.f / kGroup) * 16, 0);
+    uint32_t dg[kDigitWords];
+    float dsc[2];
+    load_digits(hq, hs, wave < nu ? p0 : D.T * D.k, D.f, cl, dg, dsc);
+    const uint4 S = make_uint4(Sv.x, Sv.y, Sv.z, Sv.w);
     float acc[kTileRows];
 #pragma unroll
-    for (int rr = 0; rr < kTileRows; ++rr) acc[rr] = 0.0f;
-    if (ok && lane < C) {
-#pragma unroll
-      for (int rr = 0; rr < kTileRows; ++rr) acc[rr] = fxp_chunk(W[rr], dg, dsc, tile_scale(S, rr), acc[rr]);
+    for (int rr = 0; rr < kTileRows; ++rr) {
+      const float a = fxp_chunk(make_uint4(W[rr].x, W[rr].y, W[rr].z, W[rr].w), dg, dsc, tile_scale(S, rr), 0.0f);
+      acc[rr] = (ok && lane < C) ? a : 0.0f;
     }
     const float v = reduce8_rows(acc);
     if ((lane & 7) == 7) vb[wave][lane >> 3] = v;

@@ -35,10 +35,6 @@ namespace colimoe {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-// Plain LLVM vector for 16-byte loads: copies of it stay in registers (the
-// uint4 class type is copied through memory, which keeps staged data off
-// registers).
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // bf16 of an fp32 value, round to nearest even (hardware conversion).
 __device__ __forceinline__ uint16_t bf16_bits(float v) {
