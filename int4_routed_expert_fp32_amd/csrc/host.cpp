@@ -589,7 +589,7 @@ int colimoe_forward(colimoe_ctx *ctx, int32_t layer, const float *x, int32_t T, 
   if (flags > COLIMOE_FWD_FXP) return COLIMOE_E_ARG;
   if (T == 0) return COLIMOE_OK;  // nothing to read or write; pointers may be NULL
   if (!x || !idx || !w || !residual || !aligned(x, 16) || !aligned(idx, 4) || !aligned(w, 4) ||
-      !aligned(residual, 4))
+      !aligned(residual, 16))
     return COLIMOE_E_ARG;
   if (u && !union_ok(u)) return COLIMOE_E_ARG;
   int path = select_path(ctx, T, flags);
@@ -604,7 +604,7 @@ int colimoe_route_forward(colimoe_ctx *ctx, int32_t layer, const float *x, int32
   if (flags > COLIMOE_FWD_FXP) return COLIMOE_E_ARG;
   if (T == 0) return COLIMOE_OK;
   if (!x || !idx || !w || !residual || !aligned(x, 16) || !aligned(idx, 4) || !aligned(w, 4) ||
-      !aligned(residual, 4))
+      !aligned(residual, 16))
     return COLIMOE_E_ARG;
   if (u && !union_ok(u)) return COLIMOE_E_ARG;
   const int path = select_path(ctx, T, flags);

@@ -1075,22 +1075,30 @@ __global__ __launch_bounds__(256) void k_router_split(LayerDev L, Dims D, const 
     const int c = 4 * lane + 256 * i;
     r[i] = c < q4 ? *(const float4 *)(row + c) : make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  for (int t = 0; t < D.T; ++t) {
-    const float *xr = x + (size_t)t * D.d + (size_t)wave * q4;
-    float acc = 0.0f;
+  // tokens four at a time, so their loads and reductions overlap; per token
+  // the operations and their order do not depend on the grouping
+  for (int t0 = 0; t0 < D.T; t0 += 4) {
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int c = 4 * lane + 256 * i;
       if (c < q4) {
-        const float4 xv = *(const float4 *)(xr + c);
-        acc = __builtin_fmaf(r[i].x, xv.x, acc);
-        acc = __builtin_fmaf(r[i].y, xv.y, acc);
-        acc = __builtin_fmaf(r[i].z, xv.z, acc);
-        acc = __builtin_fmaf(r[i].w, xv.w, acc);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int t = t0 + u < D.T ? t0 + u : D.T - 1;  // a clamped row is computed and dropped
+          const float4 xv = *(const float4 *)(x + (size_t)t * D.d + (size_t)wave * q4 + c);
+          acc[u] = __builtin_fmaf(r[i].x, xv.x, acc[u]);
+          acc[u] = __builtin_fmaf(r[i].y, xv.y, acc[u]);
+          acc[u] = __builtin_fmaf(r[i].z, xv.z, acc[u]);
+          acc[u] = __builtin_fmaf(r[i].w, xv.w, acc[u]);
+        }
       }
     }
-    acc = wave_sum(acc);
-    if (lane == 0) part[t][wave] = acc;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float v = wave_sum(acc[u]);
+      if (lane == 0 && t0 + u < D.T) part[t0 + u][wave] = v;
+    }
   }
   __syncthreads();
   if (threadIdx.x < D.T)
@@ -1339,13 +1347,14 @@ __global__ __launch_bounds__(256) void k_down_narrow(LayerDev L, Dims D, const f
 
 __global__ __launch_bounds__(256) void k_combine(Dims D, const float *__restrict__ w, UnionDev U,
                                                  const float *__restrict__ y, float *__restrict__ residual) {
-  // One block per token.  A token's pairs sit in ascending expert order in the
-  // union lists, so visiting its slots by increasing pair index visits experts
-  // ascending; the order is ranked once into LDS.
+  // Block (column slice, token): 256 threads x 4 columns.  A token's pairs sit
+  // in ascending expert order in the union lists, so visiting its slots by
+  // increasing pair index visits experts ascending; the order is ranked into
+  // LDS by every block of the token.
   __shared__ int order[16];
   __shared__ float wt[16];
   __shared__ int nsel;
-  const int t = blockIdx.x;
+  const int t = blockIdx.y;
   if (t >= D.T) return;
   const int nu = clamp_nu(U.n_unique, D);
   const int tk = D.T * D.k;
@@ -1370,12 +1379,36 @@ __global__ __launch_bounds__(256) void k_combine(Dims D, const float *__restrict
   }
   __syncthreads();
   const int n = nsel;
-  for (int r = threadIdx.x; r < D.d; r += blockDim.x) {
-    float acc = residual[(size_t)t * D.d + r];
-    for (int i = 0; i < n; ++i) acc = __builtin_fmaf(wt[i], y[(size_t)order[i] * D.d + r], acc);
-    if (D.n_shared) acc = acc + y[((size_t)tk + t) * D.d + r];
-    residual[(size_t)t * D.d + r] = acc;
+  const int d4 = D.d / 4, c4 = blockIdx.x * 256 + threadIdx.x;
+  if (c4 >= d4) return;
+  float4 *rp = (float4 *)residual + (size_t)t * d4 + c4;
+  const float4 *y4 = (const float4 *)y;
+  float4 acc = *rp;
+  if (n > 0) {
+    // every load first (a slot past n reads the last valid row again), then
+    // the fmas in slot order
+    float4 v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (i < D.k) v[i] = y4[(size_t)order[i < n ? i : n - 1] * d4 + c4];
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (i < n) {
+        const float a = wt[i];
+        acc.x = __builtin_fmaf(a, v[i].x, acc.x);
+        acc.y = __builtin_fmaf(a, v[i].y, acc.y);
+        acc.z = __builtin_fmaf(a, v[i].z, acc.z);
+        acc.w = __builtin_fmaf(a, v[i].w, acc.w);
+      }
   }
+  if (D.n_shared) {
+    const float4 sh = y4[((size_t)tk + t) * d4 + c4];
+    acc.x = acc.x + sh.x;
+    acc.y = acc.y + sh.y;
+    acc.z = acc.z + sh.z;
+    acc.w = acc.w + sh.w;
+  }
+  *rp = acc;
 }
 
 // ------------------------------------------------------------------ rmsnorm
@@ -1674,7 +1707,7 @@ hipError_t launch_down_dec(const LayerDev &L, const Dims &D, const uint32_t *hq,
 hipError_t launch_combine(const Dims &D, const float *w, const UnionDev &U, const float *y, float *residual,
                           hipStream_t s) {
   if (D.T <= 0) return hipSuccess;
-  k_combine<<<D.T, 256, 0, s>>>(D, w, U, y, residual);
+  k_combine<<<dim3((D.d / 4 + 255) / 256, D.T), 256, 0, s>>>(D, w, U, y, residual);
   return hipGetLastError();
 }
 
