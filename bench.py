@@ -43,7 +43,7 @@ def parse():
     ap.add_argument("--path", choices=("auto", "fp32", "fxp"), default="auto",
                     help="arithmetic path of the headline (auto: fixed-point activations at these shapes)")
     ap.add_argument("--no-compare", action="store_true", help="skip timing the other arithmetic path")
-    ap.add_argument("--only", choices=("all", "decode", "stack32", "union16", "prefill2048"), default="all",
+    ap.add_argument("--only", choices=("all", "decode", "stack32", "union16", "verify", "prefill2048"), default="all",
                     help="run one workload only (the headline line needs decode)")
     return ap.parse_args()
 
@@ -243,6 +243,44 @@ def bench_union16(args, torch, np, synth, cm, MoeContext, dev, stream):
             "kernels": {k: round(v["avg_us"], 3) for k, v in kern.items()}}
 
 
+def bench_verify(args, torch, np, synth, cm, MoeContext, dev, stream):
+    """T = 1..4 draft positions per call (batch-union recipe): the cost of each
+    extra position in time and in expert bytes."""
+    w4 = synth.WORKLOADS["verify4"]
+    ring = 4
+    ctx = MoeContext(w4.d, w4.f, w4.E, w4.k, n_layers=ring, n_shared=w4.n_shared, max_tokens=w4.T)
+    load_ring(ctx, synth, w4, ring, "verify")
+    nb, warm = 48, 4
+    out = {"workload": "multi-position verify: T = 1..4 positions per call (pairwise correlation 0.6, Zipf(1.1) "
+                       "bias), d=6144 f=2048 E=256 top-8 + shared", "per_T": {}}
+    for T in (1, 2, 3, 4):
+        w = w4.with_(T=T)
+        Xs = [torch.from_numpy(synth.activations(w, stream=300 + b)).to(dev) for b in range(nb + warm)]
+        res = [x.clone() for x in Xs]
+        idx = torch.empty((T, w.k), dtype=torch.int32, device=dev)
+        wts = torch.empty((T, w.k), dtype=torch.float32, device=dev)
+        unions = [ctx.new_union(T) for _ in range(nb + warm)]
+
+        def call(b):
+            cm.colimoe_route_forward(ctx.ctx, b % ring, Xs[b].data_ptr(), T, idx.data_ptr(), wts.data_ptr(),
+                                     unions[b].abi(), res[b].data_ptr(), cm.COLIMOE_FWD_AUTO)
+
+        for b in range(warm):
+            call(b)
+        ctx.sync()
+        ms = event_time(torch, stream, lambda: [call(b) for b in range(warm, warm + nb)]) / nb
+        nus = [int(unions[b].n_unique.item()) for b in range(warm, warm + nb)]
+        bytes_call = (float(np.mean(nus)) + w.n_shared) * w.expert_bytes
+        out["per_T"][T] = {"us_per_call": round(1000 * ms, 2), "us_per_position": round(1000 * ms / T, 2),
+                           "unique_experts_mean": round(float(np.mean(nus)), 2), "int4_bytes_per_call": int(bytes_call),
+                           "int4_gbs": round(bytes_call / (ms * 1e-3) / 1e9, 1)}
+        del Xs, res, unions
+    ctx.close()
+    del ctx
+    torch.cuda.empty_cache()
+    return out
+
+
 def bench_prefill(args, torch, np, synth, cm, MoeContext, dev, stream):
     w = synth.WORKLOADS["prefill2048"]
     ring = 2
@@ -304,7 +342,8 @@ def main():
     common = (args, torch, np, synth, cm, MoeContext, dev, stream)
 
     extra = {}
-    for name, fn in (("stack32", bench_stack32), ("union16", bench_union16), ("prefill2048", bench_prefill)):
+    for name, fn in (("stack32", bench_stack32), ("union16", bench_union16), ("verify", bench_verify),
+                     ("prefill2048", bench_prefill)):
         if args.only in ("all", name):
             extra[name] = fn(*common)
             log("%s: %s" % (name, json.dumps({k: v for k, v in extra[name].items() if k != "kernels"})))

@@ -1053,6 +1053,38 @@ __global__ __launch_bounds__(256 * WPT) void k_down_tok(LayerDev L, Dims D, Unio
 // fixed-point kernels above (same chunk order, same reduction trees, same
 // combine order), so their results are bit-identical to them.
 
+// Dot products of one wave's quarter row r with tokens t0..t0+G-1 (rows past T
+// are clamped to T-1, computed and dropped); part[t][wave] = the wave's sum.
+template <int G>
+__device__ __forceinline__ void router_tokens(const float4 (&r)[16], const float *__restrict__ x, const Dims &D,
+                                              int wave, int lane, int q4, float (*part)[4]) {
+  for (int t0 = 0; t0 < D.T; t0 += G) {
+    float acc[G];
+#pragma unroll
+    for (int u = 0; u < G; ++u) acc[u] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int c = 4 * lane + 256 * i;
+      if (c < q4) {
+#pragma unroll
+        for (int u = 0; u < G; ++u) {
+          const int t = t0 + u < D.T ? t0 + u : D.T - 1;
+          const float4 xv = *(const float4 *)(x + (size_t)t * D.d + (size_t)wave * q4 + c);
+          acc[u] = __builtin_fmaf(r[i].x, xv.x, acc[u]);
+          acc[u] = __builtin_fmaf(r[i].y, xv.y, acc[u]);
+          acc[u] = __builtin_fmaf(r[i].z, xv.z, acc[u]);
+          acc[u] = __builtin_fmaf(r[i].w, xv.w, acc[u]);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+      const float v = wave_sum(acc[u]);
+      if (lane == 0 && t0 + u < D.T) part[t0 + u][wave] = v;
+    }
+  }
+}
+
 // Router with the d columns split over the 4 waves of a block, one block per
 // expert row, up to 16 tokens.  Each wave keeps its quarter of the row in
 // registers and applies it to every token; the 4 partial sums of a token are
@@ -1063,10 +1095,6 @@ __global__ __launch_bounds__(256) void k_router_split(LayerDev L, Dims D, const 
   __shared__ float part[kRouteSplitMaxT][4];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int e = blockIdx.x;
-  if (xq) {  // fixed-point encoding of x for the gate/up kernel, spread over the blocks
-    const int groups = D.T * (D.d / 16);
-    for (int g = blockIdx.x * 256 + threadIdx.x; g < groups; g += gridDim.x * 256) xquant_group(x, D.d, g, xq, xs);
-  }
   const int q4 = D.d / 4;  // columns per wave (d is a multiple of 64, at most 16384)
   const float *row = L.router + (size_t)e * D.d + (size_t)wave * q4;
   float4 r[16];
@@ -1075,31 +1103,16 @@ __global__ __launch_bounds__(256) void k_router_split(LayerDev L, Dims D, const 
     const int c = 4 * lane + 256 * i;
     r[i] = c < q4 ? *(const float4 *)(row + c) : make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  // tokens four at a time, so their loads and reductions overlap; per token
-  // the operations and their order do not depend on the grouping
-  for (int t0 = 0; t0 < D.T; t0 += 4) {
-    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int c = 4 * lane + 256 * i;
-      if (c < q4) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int t = t0 + u < D.T ? t0 + u : D.T - 1;  // a clamped row is computed and dropped
-          const float4 xv = *(const float4 *)(x + (size_t)t * D.d + (size_t)wave * q4 + c);
-          acc[u] = __builtin_fmaf(r[i].x, xv.x, acc[u]);
-          acc[u] = __builtin_fmaf(r[i].y, xv.y, acc[u]);
-          acc[u] = __builtin_fmaf(r[i].z, xv.z, acc[u]);
-          acc[u] = __builtin_fmaf(r[i].w, xv.w, acc[u]);
-        }
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float v = wave_sum(acc[u]);
-      if (lane == 0 && t0 + u < D.T) part[t0 + u][wave] = v;
-    }
+  if (xq) {  // fixed-point encoding of x for the gate/up kernel, while the row is in flight
+    const int groups = D.T * (D.d / 16);
+    for (int g = blockIdx.x * 256 + threadIdx.x; g < groups; g += gridDim.x * 256) xquant_group(x, D.d, g, xq, xs);
   }
+  // one token alone, or tokens four at a time so their loads and reductions
+  // overlap; per token the operations and their order are the same
+  if (D.T == 1)
+    router_tokens<1>(r, x, D, wave, lane, q4, part);
+  else
+    router_tokens<4>(r, x, D, wave, lane, q4, part);
   __syncthreads();
   if (threadIdx.x < D.T)
     logits[(size_t)threadIdx.x * D.E + e] =

@@ -98,6 +98,8 @@ WORKLOADS = {
     "stack32": _wl(2, name="stack32", d=6144, f=2048, E=256, k=8, T=1, n_shared=1, n_layers=32, zipf=1.1),
     "union16": _wl(3, name="union16", d=6144, f=2048, E=256, k=8, T=16, n_shared=1, zipf=1.1, rho=0.6),
     "prefill2048": _wl(4, name="prefill2048", d=6144, f=2048, E=256, k=8, T=2048, n_shared=1, zipf=1.1),
+    # multi-position verify: a few draft positions of the batch-union recipe
+    "verify4": _wl(5, name="verify4", d=6144, f=2048, E=256, k=8, T=4, n_shared=1, zipf=1.1, rho=0.6),
 }
 
 

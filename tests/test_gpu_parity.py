@@ -187,6 +187,24 @@ def test_union16_parity_and_batch_identity(flags):
         assert np.array_equal(res1.cpu().numpy()[0].view(np.uint32), r["out"][t].view(np.uint32)), t
 
 
+@pytest.mark.parametrize("T", [2, 3, 4])
+def test_verify_positions_match_single_token_calls(T):
+    """A few draft positions in one call (the batch-union path) give each
+    position the bits of a one-token call (the one-token kernels), through
+    colimoe_route_forward both times, and match the oracle."""
+    w = synth.WORKLOADS["verify4"].with_(T=T)
+    ctx = _ctx(w)
+    P.load_layer(ctx, w, 0)
+    ora = P.OracleLayer(w, 0)
+    X = synth.activations(w, stream=7)
+    r = P.layer_parity(ctx, w, 0, X, ora, one_call=True)
+    for t in range(T):
+        a = P.layer_parity(ctx, w, 0, X[t:t + 1], ora, one_call=True)
+        assert np.array_equal(a["idx"][0], r["idx"][t])
+        assert np.array_equal(a["out"][0].view(np.uint32), r["out"][t].view(np.uint32)), t
+    print("verify T=%d: unique experts %d, worst ratio %.3g" % (T, r["union"]["n_unique"], r["ratio"]))
+
+
 def test_forced_routing_onehot_gate():
     """Caller-forced routing with gate weights (1, 0, ...) and a zero residual
     yields exactly one expert's output (plus the shared expert)."""
