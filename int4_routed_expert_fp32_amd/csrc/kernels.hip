@@ -157,8 +157,18 @@ __device__ __forceinline__ uint64_t topk_key(float v, int e) {
   return ((uint64_t)ord << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
 }
 
-// Selects for one token; lane 0 writes idx and w (each if non-null) and the
-// ids to `lds_ids` (if given).  Every valid key is nonzero, so k <= E rounds always find one.
+// Selects for one token: k rounds of a wave-wide maximum over the keys; the
+// selected logit is read back from its key (no memory access in the loop).
+// Lane j keeps the j-th selected logit; gate weights are exp(v_j - v_0)
+// divided by their sum, the sum taken by a fixed tree over lanes 0..15 and
+// broadcast from lane 0.  Lane j writes entry j of idx and w (each if
+// non-null) and the id to `lds_ids` (if given).  Every valid key is nonzero,
+// so k <= E rounds always find one.
+__device__ __forceinline__ float key_value(uint64_t key) {
+  const uint32_t ord = (uint32_t)(key >> 32);
+  return bits_f((ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord);
+}
+
 template <int PER>
 __device__ __forceinline__ void topk_token(const float *__restrict__ l, const Dims &D, int t,
                                            int32_t *__restrict__ idx, float *__restrict__ wout, int32_t *lds_ids) {
@@ -169,8 +179,8 @@ __device__ __forceinline__ void topk_token(const float *__restrict__ l, const Di
     const int e = lane + 64 * i;
     key[i] = e < D.E ? topk_key(l[e], e) : 0ull;
   }
-  float vals[16];
-  int ids[16];
+  float m = 0.0f, myv = 0.0f;
+  int myid = 0;
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     if (j < D.k) {
@@ -178,27 +188,27 @@ __device__ __forceinline__ void topk_token(const float *__restrict__ l, const Di
 #pragma unroll
       for (int i = 0; i < PER; ++i) best = key[i] > best ? key[i] : best;
       best = wave_max_u64(best);
-      const int e = (int)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFu));
-      ids[j] = e;
-      vals[j] = l[e];
+      const float v = key_value(best);
+      if (j == 0) m = v;
+      if (lane == j) {
+        myv = v;
+        myid = (int)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFu));
+      }
 #pragma unroll
       for (int i = 0; i < PER; ++i)
         if (key[i] == best) key[i] = 0ull;
     }
   }
-  if (lane == 0) {
-    const float m = vals[0];
-    float sum = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 16; ++j)
-      if (j < D.k) sum += expf(vals[j] - m);
-#pragma unroll
-    for (int j = 0; j < 16; ++j)
-      if (j < D.k) {
-        if (idx) idx[(size_t)t * D.k + j] = ids[j];
-        if (wout) wout[(size_t)t * D.k + j] = expf(vals[j] - m) / sum;
-        if (lds_ids) lds_ids[t * D.k + j] = ids[j];
-      }
+  const float ex = lane < D.k ? expf(myv - m) : 0.0f;
+  float sum = ex + __shfl_xor(ex, 8, 64);
+  sum = sum + __shfl_xor(sum, 4, 64);
+  sum = sum + __shfl_xor(sum, 2, 64);
+  sum = sum + __shfl_xor(sum, 1, 64);
+  sum = bits_f(__builtin_amdgcn_readfirstlane(f_bits(sum)));
+  if (lane < D.k) {
+    if (idx) idx[(size_t)t * D.k + lane] = myid;
+    if (wout) wout[(size_t)t * D.k + lane] = ex / sum;
+    if (lds_ids) lds_ids[t * D.k + lane] = myid;
   }
 }
 
