@@ -1171,16 +1171,26 @@ __global__ __launch_bounds__(64) void k_topk_union1(const float *__restrict__ lo
 // blocks per CU: the whole grid of d/8 blocks is resident at once.  Every
 // lane computes (a lane past the row end reads a valid chunk and its result
 // is replaced by 0), so no load sits behind a branch.
+constexpr int kDecMaxSlots = 16;  // slots of the one-token down kernel (one wave each)
+
 __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(6))) void k_down_dec1(
     LayerDev L, Dims D, const uint32_t *__restrict__ hq, const float *__restrict__ hs, UnionDev U,
     const float *__restrict__ wslot, float *__restrict__ residual) {
   __shared__ float vb[16][kTileRows];
   __shared__ int ok_s[16];
+  __shared__ float wsl_s[16];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int ti = blockIdx.x, C = D.f / kChunk;
   const int nu = clamp_nu(U.n_unique, D);
   const int slots = nu + D.n_shared;
   const ExpertLayout EL = expert_layout(D.d, D.f);
+  // the combine's inputs (slot gate weights, the residual tile) are fetched
+  // by wave 0 before its weights, so they are in hand after the barrier
+  float wl = 0.0f, rin = 0.0f;
+  if (wave == 0) {
+    wl = wslot[lane < kDecMaxSlots ? lane : kDecMaxSlots - 1];
+    rin = residual[(size_t)ti * kTileRows + (lane & 7)];
+  }
   if (wave < slots) {
     int e, p0, p1;
     const bool ok = resolve_slot(D, U, nu, wave, e, p0, p1) && p1 > p0;
@@ -1208,19 +1218,19 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(6))) void 
     if ((lane & 7) == 7) vb[wave][lane >> 3] = v;
     if (lane == 0) ok_s[wave] = ok;
   }
+  if (wave == 0 && lane < kDecMaxSlots) wsl_s[lane] = wl;
   __syncthreads();
   if (wave == 0 && lane < kTileRows) {
-    float out = residual[(size_t)ti * kTileRows + lane];
+    float out = rin;
     for (int sl = 0; sl < slots; ++sl) {
       if (!ok_s[sl]) continue;
       const float v = vb[sl][lane];
-      out = sl < nu ? __builtin_fmaf(wslot[sl], v, out) : out + v;
+      out = sl < nu ? __builtin_fmaf(wsl_s[sl], v, out) : out + v;
     }
     residual[(size_t)ti * kTileRows + lane] = out;
   }
 }
 
-constexpr int kDecMaxSlots = 16;
 
 // ------------------------------------------------- narrow shapes (K < 2048)
 // Rows shorter than 64 chunks: LPR lanes per row (a power of two >= K/32),
