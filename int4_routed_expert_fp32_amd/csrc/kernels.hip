@@ -677,8 +677,8 @@ __global__ __launch_bounds__(64 * NWMAX) void k_down_wide(LayerDev L, Dims D, co
 // split into six signed base-16 digits (each in [-8, 7]) packed eight to a
 // word in the weights' nibble order, so one v_dot8_i32_i4 multiplies 8 int4
 // weights by 8 digits exactly.  Per 16 columns and row: six digit-plane
-// dot products (exact int32), recombined as sum_k 16^k a_k (exact in two
-// int32 halves, rounded once to fp32), scaled by s_row * 2^(E-22) and
+// dot products (exact int32), recombined as sum_k 16^k a_k (exact in
+// int32, rounded once to fp32), scaled by s_row * 2^(E-22) and
 // accumulated in fp32 along the row.  The weights are the canonical
 // two's-complement nibbles, read as they are.
 
@@ -707,15 +707,16 @@ __device__ __forceinline__ float fxp_chunk(const uint4 &w, const uint32_t *dg, c
   const uint32_t wh[2][2] = {{w.x, w.y}, {w.z, w.w}};
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf) {
-    int a[6];
+    // V = sum_k 16^k a_k by Horner from the top plane down, each plane's two
+    // dot8s accumulating into 16 * (the planes above): exact in int32, since
+    // |V| = |sum_i q_i X_i| <= 16 * 8 * 2^22 = 2^29; rounded once to fp32
+    int t = 0;
 #pragma unroll
-    for (int k = 0; k < 6; ++k) {
-      a[k] = __builtin_amdgcn_sdot8((int)wh[hf][0], (int)dg[hf * 12 + 2 * k], 0, false);
-      a[k] = __builtin_amdgcn_sdot8((int)wh[hf][1], (int)dg[hf * 12 + 2 * k + 1], a[k], false);
+    for (int k = 5; k >= 0; --k) {
+      t = __builtin_amdgcn_sdot8((int)wh[hf][0], (int)dg[hf * 12 + 2 * k], t * 16, false);
+      t = __builtin_amdgcn_sdot8((int)wh[hf][1], (int)dg[hf * 12 + 2 * k + 1], t, false);
     }
-    const int lo = a[0] + (a[1] << 4) + (a[2] << 8);
-    const int hi = a[3] + (a[4] << 4) + (a[5] << 8);
-    const float V = __builtin_fmaf((float)hi, 4096.0f, (float)lo);
+    const float V = (float)t;
     acc = __builtin_fmaf(s * xs[hf], V, acc);
   }
   return acc;
