@@ -181,12 +181,13 @@ def bench_stack32(args, torch, np, synth, cm, MoeContext, dev, stream):
     nu_total = []
 
     def token(i):
-        for l in range(w.n_layers):
-            src = X0[i] if l == 0 else x[i]
-            if l > 0:
-                cm.colimoe_rmsnorm(ctx.ctx, r[i].data_ptr(), 1, 1e-6, x[i].data_ptr())
-            cm.colimoe_route_forward(ctx.ctx, l, src.data_ptr(), 1, idx[l].data_ptr(), wts[l].data_ptr(), U.abi(),
-                                     r[i].data_ptr(), cm.COLIMOE_FWD_AUTO)
+        # layer 0 takes x_0 itself; every later layer is one call: RMSNorm of
+        # the residual, route, experts, combine
+        cm.colimoe_route_forward(ctx.ctx, 0, X0[i].data_ptr(), 1, idx[0].data_ptr(), wts[0].data_ptr(), U.abi(),
+                                 r[i].data_ptr(), cm.COLIMOE_FWD_AUTO)
+        for l in range(1, w.n_layers):
+            cm.colimoe_rmsnorm_route_forward(ctx.ctx, l, r[i].data_ptr(), 1, 1e-6, x[i].data_ptr(), idx[l].data_ptr(),
+                                             wts[l].data_ptr(), U.abi(), cm.COLIMOE_FWD_AUTO)
 
     for i in range(warm):
         token(i)

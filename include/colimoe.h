@@ -196,6 +196,17 @@ COLIMOE_API int colimoe_route_forward(colimoe_ctx *ctx, int32_t layer, const flo
  * leaving the GPU.  Errors: E_ARG, E_SHAPE, E_HIP. */
 COLIMOE_API int colimoe_rmsnorm(colimoe_ctx *ctx, const float *r, int32_t T, float eps, float *x_out);
 
+/* colimoe_rmsnorm(r -> x_out) followed by colimoe_route_forward(x_out, with
+ * residual r), as one call: the step of a stack of layers.  r [T][d] is the
+ * residual (read, then updated in place: r += MoE(x_out)); x_out [T][d]
+ * receives RMSNorm(r) (eps, unit weight); idx, w, u as colimoe_route_forward.
+ * For one token on the fixed-point path the router forms x_out on the fly
+ * (one launch fewer); the results are those of the two calls bit for bit.
+ * Device pointers; r and x_out 16-byte aligned.  Errors: as colimoe_rmsnorm
+ * and colimoe_route_forward. */
+COLIMOE_API int colimoe_rmsnorm_route_forward(colimoe_ctx *ctx, int32_t layer, float *r, int32_t T, float eps,
+                                  float *x_out, int32_t *idx, float *w, const colimoe_union *u, uint32_t flags);
+
 /* One expert on one token through the fp32 path, every stage exposed
  * (device pointers, any of g/u/h may be NULL): x [d] -> g, u, h [f], y [d].
  * e = -1 selects the shared expert.  Debug and parity only. */

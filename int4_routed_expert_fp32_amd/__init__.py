@@ -31,7 +31,7 @@ COLIMOE_FWD_FXP = 3
 EXPORTED = [
     "colimoe_create", "colimoe_destroy", "colimoe_set_stream", "colimoe_expert_bytes", "colimoe_layer_bytes",
     "colimoe_workspace_bytes", "colimoe_set_workspace", "colimoe_load_experts", "colimoe_route",
-    "colimoe_union_build", "colimoe_forward", "colimoe_route_forward", "colimoe_rmsnorm", "colimoe_debug_expert", "colimoe_sync", "colimoe_status_str",
+    "colimoe_union_build", "colimoe_forward", "colimoe_route_forward", "colimoe_rmsnorm_route_forward", "colimoe_rmsnorm", "colimoe_debug_expert", "colimoe_sync", "colimoe_status_str",
     "colimoe_timing_enable", "colimoe_timing_read",
 ]
 
@@ -92,6 +92,9 @@ def lib() -> ctypes.CDLL:
         L.colimoe_forward.restype = ctypes.c_int
         L.colimoe_route_forward.argtypes = [vp, i32, vp, i32, vp, vp, ctypes.POINTER(colimoe_union), vp, u32]
         L.colimoe_route_forward.restype = ctypes.c_int
+        L.colimoe_rmsnorm_route_forward.argtypes = [vp, i32, vp, i32, ctypes.c_float, vp, vp, vp,
+                                                    ctypes.POINTER(colimoe_union), u32]
+        L.colimoe_rmsnorm_route_forward.restype = ctypes.c_int
         L.colimoe_rmsnorm.argtypes = [vp, vp, i32, ctypes.c_float, vp]
         L.colimoe_rmsnorm.restype = ctypes.c_int
         L.colimoe_debug_expert.argtypes = [vp, i32, i32, vp, vp, vp, vp, vp]
@@ -195,6 +198,13 @@ def colimoe_route_forward(ctx, layer: int, x: int, T: int, idx: int, w: int, uni
     rc = lib().colimoe_route_forward(ctx, layer, x, T, idx, w, ctypes.byref(union) if union is not None else None,
                                      residual, flags)
     return _check("colimoe_route_forward", rc) if check else rc
+
+
+def colimoe_rmsnorm_route_forward(ctx, layer: int, r: int, T: int, eps: float, x_out: int, idx: int, w: int,
+                                  union: Optional[colimoe_union], flags: int = 0, check: bool = True) -> int:
+    rc = lib().colimoe_rmsnorm_route_forward(ctx, layer, r, T, eps, x_out, idx, w,
+                                             ctypes.byref(union) if union is not None else None, flags)
+    return _check("colimoe_rmsnorm_route_forward", rc) if check else rc
 
 
 def colimoe_rmsnorm(ctx, r: int, T: int, eps: float, x_out: int, check: bool = True) -> int:

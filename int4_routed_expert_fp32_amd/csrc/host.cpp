@@ -618,6 +618,45 @@ int colimoe_route_forward(colimoe_ctx *ctx, int32_t layer, const float *x, int32
   return forward_impl(ctx, layer, x, T, idx, w, uu, residual, path, encode && T <= kRouteSplitMaxT);
 }
 
+int colimoe_rmsnorm_route_forward(colimoe_ctx *ctx, int32_t layer, float *r, int32_t T, float eps, float *x_out,
+                                  int32_t *idx, float *w, const colimoe_union *u, uint32_t flags) {
+  int rc = check_call(ctx, layer, T);
+  if (rc) return rc;
+  if (flags > COLIMOE_FWD_FXP) return COLIMOE_E_ARG;
+  if (!(eps >= 0.0f)) return COLIMOE_E_ARG;
+  if (T == 0) return COLIMOE_OK;
+  if (!r || !x_out || !idx || !w || !aligned(r, 16) || !aligned(x_out, 16) || !aligned(idx, 4) || !aligned(w, 4))
+    return COLIMOE_E_ARG;
+  if (u && !union_ok(u)) return COLIMOE_E_ARG;
+  const int path = select_path(ctx, T, flags);
+  if (path < 0) return path;
+  const Dims D = dims_of(ctx, T);
+  if (T != 1 || path != PATH_FXP) {  // the two calls it stands for
+    {
+      KTimer kt(ctx, K_RMSNORM);
+      rc = hip_status(launch_rmsnorm(r, T, ctx->cfg.d, eps, x_out, ctx->stream));
+    }
+    if (rc) return rc;
+    return colimoe_route_forward(ctx, layer, x_out, T, idx, w, u, r, flags);
+  }
+  const colimoe_union uw = ws_union_abi(ctx);
+  const colimoe_union *uu = u ? u : &uw;
+  const LayerDev L = layer_of(ctx, layer);
+  {
+    KTimer kt(ctx, K_ROUTE);
+    if (launch_router_norm(L, D, r, eps, x_out, (float *)(ctx->ws + ctx->wl.logits), (uint32_t *)(ctx->ws + ctx->wl.xq),
+                           (float *)(ctx->ws + ctx->wl.xs), ctx->stream) != hipSuccess)
+      return COLIMOE_E_HIP;
+  }
+  {
+    KTimer kt(ctx, K_TOPK);
+    const UnionDev U = to_dev(uu);
+    if (launch_topk_union1((float *)(ctx->ws + ctx->wl.logits), D, idx, w, &U, ctx->stream) != hipSuccess)
+      return COLIMOE_E_HIP;
+  }
+  return forward_impl(ctx, layer, x_out, T, idx, w, uu, r, path, true);
+}
+
 int colimoe_rmsnorm(colimoe_ctx *ctx, const float *r, int32_t T, float eps, float *x_out) {
   if (!ctx) return COLIMOE_E_ARG;
   if (T < 0 || T > ctx->cfg.max_tokens) return COLIMOE_E_SHAPE;

@@ -101,6 +101,11 @@ Workspace workspace_layout(int d, int f, int E, int k, int n_shared, int max_tok
 // non-null: also encodes x for the fixed-point gate/up kernel.
 hipError_t launch_router_split(const LayerDev &L, const Dims &D, const float *x, float *logits, uint32_t *xq,
                                float *xs, hipStream_t s);
+// One token: the router applied to x = RMSNorm(r) (eps, unit weight) formed
+// on the fly, with x written to xout and encoded into xq/xs; every value
+// equals that of launch_rmsnorm followed by launch_router_split.
+hipError_t launch_router_norm(const LayerDev &L, const Dims &D, const float *r, float eps, float *xout, float *logits,
+                              uint32_t *xq, float *xs, hipStream_t s);
 // Top-k of one token and, if U, its union lists (T == 1).
 hipError_t launch_topk_union1(const float *logits, const Dims &D, int32_t *idx, float *w, const UnionDev *U,
                               hipStream_t s);

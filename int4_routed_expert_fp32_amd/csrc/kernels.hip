@@ -775,6 +775,31 @@ __device__ __forceinline__ void xquant_group(const float *__restrict__ x, int K,
   qs[(size_t)t * gpr + gi] = scale;
 }
 
+// As xquant_group for one row whose values are x * inv.
+__device__ __forceinline__ void xquant_group_scaled(const float *__restrict__ x, int K, int g, float inv, uint32_t *__restrict__ q,
+                                             float *__restrict__ qs) {
+  const int gpr = K / 16;
+  const int t = g / gpr, gi = g - t * gpr;
+  float v[16];
+  const float4 *src = (const float4 *)(x + (size_t)t * K + (size_t)gi * 16);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float4 f = src[i];
+    v[4 * i] = f.x * inv;
+    v[4 * i + 1] = f.y * inv;
+    v[4 * i + 2] = f.z * inv;
+    v[4 * i + 3] = f.w * inv;
+  }
+  uint32_t words[12];
+  float scale;
+  quant16(v, words, scale);
+  uint4 *dst = (uint4 *)(q + ((size_t)t * (K / kChunk) + (gi >> 1)) * kDigitWords + (gi & 1) * 12);
+  dst[0] = make_uint4(words[0], words[1], words[2], words[3]);
+  dst[1] = make_uint4(words[4], words[5], words[6], words[7]);
+  dst[2] = make_uint4(words[8], words[9], words[10], words[11]);
+  qs[(size_t)t * gpr + gi] = scale;
+}
+
 __global__ __launch_bounds__(256) void k_xquant(const float *__restrict__ x, int T, int K, uint32_t *__restrict__ q,
                                                 float *__restrict__ qs) {
   const int groups = T * (K / 16);
@@ -1096,14 +1121,74 @@ __device__ __forceinline__ void router_tokens(const float4 (&r)[16], const float
   }
 }
 
+// One token whose x is r * inv (formed per element as it is read), with the
+// operations and order of router_tokens<1>.
+__device__ __forceinline__ void router_tokens_scaled(const float4 (&rw)[16], const float *__restrict__ rres,
+                                                     const Dims &D, int wave, int lane, int q4, float inv,
+                                                     float (*part)[4]) {
+  float acc = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int c = 4 * lane + 256 * i;
+    if (c < q4) {
+      const float4 rv = *(const float4 *)(rres + (size_t)wave * q4 + c);
+      const float4 xv = make_float4(rv.x * inv, rv.y * inv, rv.z * inv, rv.w * inv);
+      acc = __builtin_fmaf(rw[i].x, xv.x, acc);
+      acc = __builtin_fmaf(rw[i].y, xv.y, acc);
+      acc = __builtin_fmaf(rw[i].z, xv.z, acc);
+      acc = __builtin_fmaf(rw[i].w, xv.w, acc);
+    }
+  }
+  const float v = wave_sum(acc);
+  if (lane == 0) part[0][wave] = v;
+}
+
+// x = r * inv of one token with inv = 1 / sqrt(mean(r^2) + eps): the sum of
+// squares in exactly the order of k_rmsnorm's 512 threads (thread t sums the
+// float4 columns t, t + 512, ... in order; each wave's tree; the 8 wave sums
+// by a fixed tree), emulated by a block of 256 threads (thread t plays t and
+// t + 256, whose waves are w and w + 4), so inv is the same bits.
+__device__ __forceinline__ float rms_inv_256(const float *__restrict__ r, int d, float eps, float *part8) {
+  const float4 *rr = (const float4 *)r;
+  const int n4 = d / 4, t = threadIdx.x;
+  float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int c0 = t + 512 * i, c1 = t + 256 + 512 * i;
+    const float4 v0 = c0 < n4 ? rr[c0] : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float4 v1 = c1 < n4 ? rr[c1] : make_float4(0.f, 0.f, 0.f, 0.f);
+    a0 = __builtin_fmaf(v0.x, v0.x, a0);
+    a0 = __builtin_fmaf(v0.y, v0.y, a0);
+    a0 = __builtin_fmaf(v0.z, v0.z, a0);
+    a0 = __builtin_fmaf(v0.w, v0.w, a0);
+    a1 = __builtin_fmaf(v1.x, v1.x, a1);
+    a1 = __builtin_fmaf(v1.y, v1.y, a1);
+    a1 = __builtin_fmaf(v1.z, v1.z, a1);
+    a1 = __builtin_fmaf(v1.w, v1.w, a1);
+  }
+  a0 = wave_sum(a0);
+  a1 = wave_sum(a1);
+  if ((t & 63) == 0) {
+    part8[t >> 6] = a0;
+    part8[(t >> 6) + 4] = a1;
+  }
+  __syncthreads();
+  const float ss = ((part8[0] + part8[1]) + (part8[2] + part8[3])) + ((part8[4] + part8[5]) + (part8[6] + part8[7]));
+  return 1.0f / sqrtf(ss / (float)d + eps);
+}
+
 // Router with the d columns split over the 4 waves of a block, one block per
 // expert row, up to 16 tokens.  Each wave keeps its quarter of the row in
 // registers and applies it to every token; the 4 partial sums of a token are
-// added in wave order.  A token's logit does not depend on T.
+// added in wave order.  A token's logit does not depend on T.  NORM (one
+// token): x is RMSNorm(r) formed on the fly (every block computes the same
+// inv; x = r * inv wherever x is read), and x_out receives it.
+template <bool NORM>
 __global__ __launch_bounds__(256) void k_router_split(LayerDev L, Dims D, const float *__restrict__ x,
                                                       float *__restrict__ logits, uint32_t *__restrict__ xq,
-                                                      float *__restrict__ xs) {
+                                                      float *__restrict__ xs, float eps, float *__restrict__ xout) {
   __shared__ float part[kRouteSplitMaxT][4];
+  __shared__ float part8[8];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int e = blockIdx.x;
   const int q4 = D.d / 4;  // columns per wave (d is a multiple of 64, at most 16384)
@@ -1114,16 +1199,27 @@ __global__ __launch_bounds__(256) void k_router_split(LayerDev L, Dims D, const 
     const int c = 4 * lane + 256 * i;
     r[i] = c < q4 ? *(const float4 *)(row + c) : make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  if (xq) {  // fixed-point encoding of x for the gate/up kernel, while the row is in flight
-    const int groups = D.T * (D.d / 16);
-    for (int g = blockIdx.x * 256 + threadIdx.x; g < groups; g += gridDim.x * 256) xquant_group(x, D.d, g, xq, xs);
+  if (NORM) {
+    const float inv = rms_inv_256(x, D.d, eps, part8);
+    for (int c = blockIdx.x * 256 + threadIdx.x; c < D.d / 4; c += gridDim.x * 256) {
+      const float4 v = ((const float4 *)x)[c];
+      ((float4 *)xout)[c] = make_float4(v.x * inv, v.y * inv, v.z * inv, v.w * inv);
+    }
+    const int groups = D.d / 16;
+    for (int g = blockIdx.x * 256 + threadIdx.x; g < groups; g += gridDim.x * 256) xquant_group_scaled(x, D.d, g, inv, xq, xs);
+    router_tokens_scaled(r, x, D, wave, lane, q4, inv, part);
+  } else {
+    if (xq) {  // fixed-point encoding of x for the gate/up kernel, while the row is in flight
+      const int groups = D.T * (D.d / 16);
+      for (int g = blockIdx.x * 256 + threadIdx.x; g < groups; g += gridDim.x * 256) xquant_group(x, D.d, g, xq, xs);
+    }
+    // one token alone, or tokens four at a time so their loads and reductions
+    // overlap; per token the operations and their order are the same
+    if (D.T == 1)
+      router_tokens<1>(r, x, D, wave, lane, q4, part);
+    else
+      router_tokens<4>(r, x, D, wave, lane, q4, part);
   }
-  // one token alone, or tokens four at a time so their loads and reductions
-  // overlap; per token the operations and their order are the same
-  if (D.T == 1)
-    router_tokens<1>(r, x, D, wave, lane, q4, part);
-  else
-    router_tokens<4>(r, x, D, wave, lane, q4, part);
   __syncthreads();
   if (threadIdx.x < D.T)
     logits[(size_t)threadIdx.x * D.E + e] =
@@ -1498,7 +1594,14 @@ static int topk_per(int E) {
 hipError_t launch_router_split(const LayerDev &L, const Dims &D, const float *x, float *logits, uint32_t *xq,
                                float *xs, hipStream_t s) {
   if (D.T <= 0) return hipSuccess;
-  k_router_split<<<D.E, 256, 0, s>>>(L, D, x, logits, xq, xs);
+  k_router_split<false><<<D.E, 256, 0, s>>>(L, D, x, logits, xq, xs, 0.0f, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_norm(const LayerDev &L, const Dims &D, const float *r, float eps, float *xout, float *logits,
+                              uint32_t *xq, float *xs, hipStream_t s) {
+  if (D.T != 1 || D.d > 8 * 512 * 4) return hipErrorInvalidValue;
+  k_router_split<true><<<D.E, 256, 0, s>>>(L, D, r, logits, xq, xs, eps, xout);
   return hipGetLastError();
 }
 

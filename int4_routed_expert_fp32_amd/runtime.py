@@ -14,7 +14,8 @@ import numpy as np
 import torch
 
 from . import (COLIMOE_FWD_AUTO, colimoe_create, colimoe_debug_expert, colimoe_destroy, colimoe_forward,
-               colimoe_layer_bytes, colimoe_load_experts, colimoe_rmsnorm, colimoe_route, colimoe_route_forward,
+               colimoe_layer_bytes, colimoe_load_experts, colimoe_rmsnorm, colimoe_rmsnorm_route_forward, colimoe_route,
+               colimoe_route_forward,
                colimoe_set_stream,
                colimoe_set_workspace, colimoe_sync, colimoe_union_build, colimoe_workspace_bytes, colimoe_expert_bytes, make_config,
                make_union)
@@ -128,6 +129,16 @@ class MoeContext:
         w = torch.empty((T, self.k), dtype=torch.float32, device=self.device)
         colimoe_route_forward(self.ctx, layer, x.data_ptr(), T, idx.data_ptr(), w.data_ptr(),
                               union.abi() if union is not None else None, residual.data_ptr(), flags)
+        return idx, w
+
+    def rmsnorm_route_forward(self, layer: int, r: torch.Tensor, eps: float, x_out: torch.Tensor,
+                              union: Optional[UnionTensors], flags: int = COLIMOE_FWD_AUTO):
+        """x_out = RMSNorm(r); r += MoE_layer(x_out); returns (idx, w)."""
+        T = r.shape[0]
+        idx = torch.empty((T, self.k), dtype=torch.int32, device=self.device)
+        w = torch.empty((T, self.k), dtype=torch.float32, device=self.device)
+        colimoe_rmsnorm_route_forward(self.ctx, layer, r.data_ptr(), T, eps, x_out.data_ptr(), idx.data_ptr(),
+                                      w.data_ptr(), union.abi() if union is not None else None, flags)
         return idx, w
 
     def rmsnorm(self, r: torch.Tensor, eps: float, out: torch.Tensor) -> None:

@@ -100,3 +100,37 @@ def test_stack32_paths_route_identically(stack_ctx):
     b = gpu_chain(stack_ctx, x0, FP32)
     for l in range(W.n_layers):
         assert np.array_equal(a[l][1], b[l][1]), "layer %d routed differently" % l
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("flags", [0, FP32], ids=["auto", "fp32"])
+def test_stack32_one_call_per_layer_is_bit_identical(stack_ctx, flags):
+    """colimoe_rmsnorm_route_forward (RMSNorm formed inside the router for one
+    token on the fixed-point path; the two calls it stands for otherwise) gives
+    the bits of colimoe_rmsnorm + colimoe_route_forward at every layer: the
+    residual, the normalised x, the routing and the gate weights."""
+    import torch
+    x0 = synth.activations(W, stream=2, T=1)
+    dev = stack_ctx.device
+    r1 = torch.from_numpy(np.ascontiguousarray(x0, np.float32)).to(dev)
+    r2 = r1.clone()
+    x1 = torch.empty_like(r1)
+    x2 = torch.empty_like(r1)
+    for l in range(W.n_layers):
+        U1, U2 = stack_ctx.new_union(1), stack_ctx.new_union(1)
+        if l == 0:
+            i1, w1 = stack_ctx.route_forward(l, r1.clone(), U1, r1, flags)
+            i2, w2 = stack_ctx.route_forward(l, r2.clone(), U2, r2, flags)
+            stack_ctx.sync()
+            continue
+        stack_ctx.rmsnorm(r1, EPS, x1)
+        i1, w1 = stack_ctx.route_forward(l, x1, U1, r1, flags)
+        i2, w2 = stack_ctx.rmsnorm_route_forward(l, r2, EPS, x2, U2, flags)
+        stack_ctx.sync()
+        assert np.array_equal(x1.cpu().numpy().view(np.uint32), x2.cpu().numpy().view(np.uint32)), l
+        assert np.array_equal(i1.cpu().numpy(), i2.cpu().numpy()), l
+        assert np.array_equal(w1.cpu().numpy().view(np.uint32), w2.cpu().numpy().view(np.uint32)), l
+        assert np.array_equal(r1.cpu().numpy().view(np.uint32), r2.cpu().numpy().view(np.uint32)), l
+        assert U1.to_host()["n_unique"] == U2.to_host()["n_unique"]
+    print("stack32 one call per layer (%s): bit-identical over %d layers" % ("auto" if flags == 0 else "fp32",
+                                                                            W.n_layers))
