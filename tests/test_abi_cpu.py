@@ -62,5 +62,8 @@ def test_null_arguments_rejected():
     assert L.colimoe_load_experts(None, 0, None, None, 0) == cm.COLIMOE_E_ARG
     assert L.colimoe_union_build(None, None, 1, None) == cm.COLIMOE_E_ARG
     assert L.colimoe_sync(None) == cm.COLIMOE_E_ARG
+    assert L.colimoe_route_forward(None, 0, None, 1, None, None, None, None, 0) == cm.COLIMOE_E_ARG
+    assert L.colimoe_rmsnorm_route_forward(None, 0, None, 1, 1e-6, None, None, None, None, 0) == cm.COLIMOE_E_ARG
+    assert L.colimoe_rmsnorm(None, None, 1, 1e-6, None) == cm.COLIMOE_E_ARG
     for s in (0, -1, -2, -3, -4, -5, -6, -99):
         assert cm.status_str(s)
