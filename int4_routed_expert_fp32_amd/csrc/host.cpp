@@ -318,6 +318,11 @@ static int route_impl(colimoe_ctx *ctx, int32_t layer, const float *x, int32_t T
       if (launch_topk_union1(lg, D, idx, w, u ? &U : nullptr, s) != hipSuccess) return COLIMOE_E_HIP;
       return COLIMOE_OK;
     }
+    if (u) {  // up to 16 tokens: top-k and the union lists in one launch
+      KTimer kt(ctx, K_TOPK);
+      if (launch_topk_union(lg, D, idx, w, to_dev(u), err, s) != hipSuccess) return COLIMOE_E_HIP;
+      return COLIMOE_OK;
+    }
   } else {
     KTimer kt(ctx, K_ROUTE);
     if (launch_router_mfma(L, D, x, (float *)(ctx->ws + ctx->wl.rpart), lg, s) != hipSuccess) return COLIMOE_E_HIP;

@@ -111,6 +111,10 @@ hipError_t launch_topk_union1(const float *logits, const Dims &D, int32_t *idx, 
                               hipStream_t s);
 hipError_t launch_topk(const float *logits, const Dims &D, int32_t *idx, float *w, hipStream_t s);
 hipError_t launch_union(const int32_t *idx, const Dims &D, const UnionDev &U, int32_t *err, hipStream_t s);
+// Top-k of 1..16 tokens and their union lists in one launch (the results of
+// launch_topk followed by launch_union).
+hipError_t launch_topk_union(const float *logits, const Dims &D, int32_t *idx, float *w, const UnionDev &U,
+                             int32_t *err, hipStream_t s);
 hipError_t launch_gateup(const LayerDev &L, const Dims &D, const float *x, const UnionDev &U, float *h,
                          hipStream_t s);
 hipError_t launch_debug_gateup(const LayerDev &L, const Dims &D, const float *x, const UnionDev &U, float *h,

@@ -1631,6 +1631,35 @@ hipError_t launch_topk(const float *logits, const Dims &D, int32_t *idx, float *
   return hipGetLastError();
 }
 
+// Top-k of up to 16 tokens (one wave each) and their union lists (wave 0,
+// after the block barrier) in one launch; the same functions as k_topk and
+// k_union, so the same results.
+template <int PER>
+__global__ __launch_bounds__(1024) void k_topk_union(const float *__restrict__ logits, Dims D,
+                                                     int32_t *__restrict__ idx, float *__restrict__ wout, UnionDev U,
+                                                     int32_t *__restrict__ err) {
+  extern __shared__ unsigned long long masks[];
+  const int t = threadIdx.x >> 6;
+  if (t < D.T) topk_token<PER>(logits + (size_t)t * D.E, D, t, idx, wout, nullptr);
+  __syncthreads();
+  if (threadIdx.x < 64) union_wave(idx, D, U, err, masks);
+}
+
+hipError_t launch_topk_union(const float *logits, const Dims &D, int32_t *idx, float *w, const UnionDev &U,
+                             int32_t *err, hipStream_t s) {
+  if (D.T < 1 || D.T > kRouteSplitMaxT) return hipErrorInvalidValue;
+  const int b = 64 * D.T;
+  const size_t lds = union_lds_bytes(D.E);
+  switch (topk_per(D.E)) {
+    case 1: k_topk_union<1><<<1, b, lds, s>>>(logits, D, idx, w, U, err); break;
+    case 2: k_topk_union<2><<<1, b, lds, s>>>(logits, D, idx, w, U, err); break;
+    case 4: k_topk_union<4><<<1, b, lds, s>>>(logits, D, idx, w, U, err); break;
+    case 8: k_topk_union<8><<<1, b, lds, s>>>(logits, D, idx, w, U, err); break;
+    default: k_topk_union<16><<<1, b, lds, s>>>(logits, D, idx, w, U, err); break;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_union(const int32_t *idx, const Dims &D, const UnionDev &U, int32_t *err, hipStream_t s) {
   if (D.T > 256) {
     // one wave per segment; LDS stays under 64 KB
