@@ -270,11 +270,14 @@ def bench_verify(args, torch, np, synth, cm, MoeContext, dev, stream):
             call(b)
         ctx.sync()
         ms = event_time(torch, stream, lambda: [call(b) for b in range(warm, warm + nb)]) / nb
+        ctx.sync()
+        kern = per_kernel(cm, ctx, lambda: [call(b) for b in range(warm, warm + nb)])
         nus = [int(unions[b].n_unique.item()) for b in range(warm, warm + nb)]
         bytes_call = (float(np.mean(nus)) + w.n_shared) * w.expert_bytes
         out["per_T"][T] = {"us_per_call": round(1000 * ms, 2), "us_per_position": round(1000 * ms / T, 2),
                            "unique_experts_mean": round(float(np.mean(nus)), 2), "int4_bytes_per_call": int(bytes_call),
-                           "int4_gbs": round(bytes_call / (ms * 1e-3) / 1e9, 1)}
+                           "int4_gbs": round(bytes_call / (ms * 1e-3) / 1e9, 1),
+                           "kernels": {k: round(v["avg_us"], 3) for k, v in kern.items()}}
         del Xs, res, unions
     ctx.close()
     del ctx
