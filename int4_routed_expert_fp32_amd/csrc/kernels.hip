@@ -1727,6 +1727,53 @@ hipError_t launch_topk(const float *logits, const Dims &D, int32_t *idx, float *
   return hipGetLastError();
 }
 
+// Union lists of a call with at most 64 (token, slot) pairs, one wave: lane p
+// holds pair p and ranks it by (expert, token) among all pairs with a plain
+// count; the lists (and the handling of an invalid routing) are those of
+// union_wave.
+__device__ void union_small(const int32_t *__restrict__ idx, const Dims &D, const UnionDev &U,
+                            int32_t *__restrict__ err) {
+  const int P = D.T * D.k, lane = threadIdx.x & 63;
+  const bool act = lane < P;
+  const int e = act ? idx[lane] : 0;
+  const int t = act ? lane / D.k : 0, j = act ? lane - t * D.k : 0;
+  bool ok = !act || (e >= 0 && e < D.E);
+  for (int q = 0; q < j; ++q) ok = ok && idx[t * D.k + q] != e;
+  if (__ballot(!ok)) {
+    if (lane == 0) {
+      *U.n_unique = 0;
+      U.offsets[0] = 0;
+      atomicOr(err, 1);
+    }
+    return;
+  }
+  const int key = act ? e * D.T + t : 0x7FFFFFFF;  // (expert, token), unique per pair
+  int rank = 0;
+  bool first = act;
+  for (int q = 0; q < P; ++q) {
+    const int kq = __shfl(key, q, 64), eq = __shfl(e, q, 64);
+    rank += kq < key;
+    first = first && !(eq == e && kq < key);
+  }
+  const unsigned long long fm = __ballot(first);
+  int below = 0;  // distinct experts smaller than e
+  for (int q = 0; q < P; ++q) below += ((fm >> q) & 1ull) && __shfl(e, q, 64) < e;
+  if (act) {
+    U.pair_token[rank] = t;
+    U.pair_slot[rank] = j;
+    U.pair_of[lane] = rank;
+    if (first) {
+      U.ids[below] = e;
+      U.offsets[below] = rank;
+    }
+  }
+  if (lane == 0) {
+    const int n = __popcll(fm);
+    *U.n_unique = n;
+    U.offsets[n] = P;
+  }
+}
+
 // Top-k of up to 16 tokens (one wave each) and their union lists (wave 0,
 // after the block barrier) in one launch; the same functions as k_topk and
 // k_union, so the same results.
@@ -1738,7 +1785,12 @@ __global__ __launch_bounds__(1024) void k_topk_union(const float *__restrict__ l
   const int t = threadIdx.x >> 6;
   if (t < D.T) topk_token<PER>(logits + (size_t)t * D.E, D, t, idx, wout, nullptr);
   __syncthreads();
-  if (threadIdx.x < 64) union_wave(idx, D, U, err, masks);
+  if (threadIdx.x < 64) {
+    if (D.T * D.k <= 64)
+      union_small(idx, D, U, err);
+    else
+      union_wave(idx, D, U, err, masks);
+  }
 }
 
 hipError_t launch_topk_union(const float *logits, const Dims &D, int32_t *idx, float *w, const UnionDev &U,

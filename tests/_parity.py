@@ -129,4 +129,10 @@ def layer_parity(ctx, w: synth.Workload, layer: int, X: np.ndarray, ora: OracleL
     # outputs: the oracle under the GPU's routing (identical to its own where the sets agree)
     out, l1 = ora.forward(X, gidx, wref, residual)
     ratio = assert_close(gout, out, what="layer output")
-    return dict(idx=gidx, w=gw, out=gout, ratio=ratio, differ=differ, union=U.to_host(), oracle_out=out)
+    # the union lists of the GPU's routing, exactly as the oracle builds them
+    union = U.to_host()
+    ou = oracle.union(gidx, w.E)
+    assert union["n_unique"] == ou["n_unique"], "union: unique count"
+    for key in ("ids", "offsets", "pair_token", "pair_slot", "pair_of"):
+        assert np.array_equal(union[key], ou[key]), "union list " + key
+    return dict(idx=gidx, w=gw, out=gout, ratio=ratio, differ=differ, union=union, oracle_out=out)
