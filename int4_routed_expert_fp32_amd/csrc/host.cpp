@@ -259,8 +259,8 @@ Workspace workspace_layout(int d, int f, int E, int k, int n_shared, int max_tok
   W.xb = take(rows * d * 2);
   W.hb = take(rows * f * 2);
   W.mblk_max = mfma_max_entries(max_tokens, k, E, n_shared);
-  W.mblk = take((size_t)W.mblk_max * 16);
-  W.mcount = take(4);
+  W.mblk = take((size_t)W.mblk_max * 2 * 16);  // one-M-tile blocks, then the larger ones
+  W.mcount = take(8);
   W.wslot = take(32 * 4);
   W.bytes = o;
   return W;

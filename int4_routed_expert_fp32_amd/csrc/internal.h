@@ -88,7 +88,7 @@ struct Workspace {
   size_t xq, xs;  // fixed-point x: [Tmax][d/32][24] u32 digit words, [Tmax][d/16] fp32 scales
   size_t hq, hs;  // fixed-point h: [rows][f/32][24] u32, [rows][f/16] fp32
   size_t xb, hb;  // bf16 MFMA path: x rows in pair order [rows][d], h [rows][f], bf16
-  size_t mblk, mcount;  // bf16 MFMA path: M-block list (int4 entries) and its length
+  size_t mblk, mcount;  // bf16 MFMA path: M-block lists (int4 entries, two classes of mblk_max) and their lengths
   size_t wslot;         // one-token path: gate weight of each slot in slot order
   int mblk_max;
   size_t bytes;

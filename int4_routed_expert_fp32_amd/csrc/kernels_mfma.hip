@@ -93,13 +93,16 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4 &v) { return __builtin_b
 // One wave: for each slot (unique routed expert in union order, then the
 // shared expert) its rows split into M-blocks of kMB; entries (expert, first
 // row, rows).  Rows of routed slots are pair positions, those of the shared
-// expert are T*k + token.
+// expert are T*k + token.  M-blocks of at most 32 rows (one M-tile: most
+// experts of a prefill call, and the last block of a large one) go to
+// list[0..count[0]), the others to list[max_entries..max_entries+count[1]):
+// each class runs in a GEMM kernel sized for it.
 __global__ __launch_bounds__(64) void k_mblocks(Dims D, UnionDev U, int4 *__restrict__ list,
                                                 int32_t *__restrict__ count, int max_entries) {
   const int lane = threadIdx.x;
   const int nu = clamp_nu(U.n_unique, D);
   const int slots = nu + (D.n_shared > 0 ? 1 : 0);
-  int running = 0;
+  int run_s = 0, run_l = 0;
   for (int base = 0; base < slots; base += 64) {
     const int s = base + lane;
     int e = 0, p0 = 0, p1 = 0, cnt = 0, row0 = 0;
@@ -107,18 +110,30 @@ __global__ __launch_bounds__(64) void k_mblocks(Dims D, UnionDev U, int4 *__rest
       row0 = s < nu ? p0 : D.T * D.k;
       cnt = (p1 - p0 + kMB - 1) / kMB;
     }
-    int inc = cnt;
+    // only the last M-block of a slot can hold 32 rows or fewer
+    const int last_rows = cnt > 0 ? p1 - p0 - (cnt - 1) * kMB : 0;
+    const int ns = (cnt > 0 && last_rows <= 32) ? 1 : 0, nl = cnt - ns;
+    int is = ns, il = nl;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-      const int v = __shfl_up(inc, o, 64);
-      if (lane >= o) inc += v;
+      const int vs = __shfl_up(is, o, 64), vl = __shfl_up(il, o, 64);
+      if (lane >= o) {
+        is += vs;
+        il += vl;
+      }
     }
-    const int pos = running + inc - cnt;
-    for (int b = 0; b < cnt; ++b)
-      if (pos + b < max_entries) list[pos + b] = make_int4(e, row0 + b * kMB, min(kMB, p1 - p0 - b * kMB), 0);
-    running += __shfl(inc, 63, 64);
+    const int ps = run_s + is - ns, pl = run_l + il - nl;
+    for (int b = 0; b < nl; ++b)
+      if (pl + b < max_entries)
+        list[max_entries + pl + b] = make_int4(e, row0 + b * kMB, min(kMB, p1 - p0 - b * kMB), 0);
+    if (ns && ps < max_entries) list[ps] = make_int4(e, row0 + nl * kMB, last_rows, 0);
+    run_s += __shfl(is, 63, 64);
+    run_l += __shfl(il, 63, 64);
   }
-  if (lane == 0) *count = running < max_entries ? running : max_entries;
+  if (lane == 0) {
+    count[0] = run_s < max_entries ? run_s : max_entries;
+    count[1] = run_l < max_entries ? run_l : max_entries;
+  }
 }
 
 // ------------------------------------------------------- activation gather
@@ -165,7 +180,6 @@ __global__ __launch_bounds__(256) void k_gather_bf16(const float *__restrict__ x
 // the barrier between groups waits only for LDS traffic, so loads stay in
 // flight across it.
 constexpr int kArowBytes = 144;
-constexpr int kAbuf = kMB * kArowBytes;  // bytes of one A stage
 
 // Barrier for the LDS ring: LDS writes of this wave complete, then s_barrier;
 // vector-memory loads issued earlier stay in flight.
@@ -174,23 +188,20 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_barrier();
 }
 
-// 64 bytes of one A row staged in registers between its load and its LDS
+// 16 NP bytes of one A row staged in registers between its load and its LDS
 // store.  Loader threads past the M-block's last row read the block's first
 // row instead: output row i of an MFMA depends only on A row i, and rows past
 // the block are never stored.
+template <int NP>  // 16-byte pieces per thread: NMT (rows 32 NMT x 128 bytes over 256 threads)
 struct AStage {
-  u32x4 a0, a1, a2, a3;
+  u32x4 a[NP];
   __device__ __forceinline__ void load(const u32x4 *src) {
-    a0 = src[0];
-    a1 = src[1];
-    a2 = src[2];
-    a3 = src[3];
+#pragma unroll
+    for (int i = 0; i < NP; ++i) a[i] = src[i];
   }
   __device__ __forceinline__ void store(unsigned char *dst) const {
-    *(u32x4 *)(dst) = a0;
-    *(u32x4 *)(dst + 16) = a1;
-    *(u32x4 *)(dst + 32) = a2;
-    *(u32x4 *)(dst + 48) = a3;
+#pragma unroll
+    for (int i = 0; i < NP; ++i) *(u32x4 *)(dst + 16 * i) = a[i];
   }
 };
 
@@ -218,7 +229,7 @@ struct GemmItem {
 // so only half of the B and A operands are live at a time.
 template <int NMT_MAX>
 __device__ __forceinline__ void gemm_group(const unsigned char *cur, const WStage &st, int nmt, int j, int hh,
-                                           f32x16 (&acc)[4][2]) {
+                                           f32x16 (&acc)[NMT_MAX][2]) {
   const GroupScale g0(st.s0), g1(st.s1);
   const uint32_t magic = 0x64006400u;
 #pragma unroll
@@ -241,12 +252,15 @@ __device__ __forceinline__ void gemm_group(const unsigned char *cur, const WStag
   }
 }
 
-template <bool GATEUP>
-__global__ __launch_bounds__(256, 2) void k_gemm_mfma(LayerDev L, Dims D, const uint16_t *__restrict__ A,
+template <bool GATEUP, int NMT>
+__global__ __launch_bounds__(256, NMT == 1 ? 3 : 2) void k_gemm_mfma(LayerDev L, Dims D, const uint16_t *__restrict__ A,
                                                       const int4 *__restrict__ list,
                                                       const int32_t *__restrict__ count, int max_entries,
                                                       uint16_t *__restrict__ hb, float *__restrict__ y) {
-  __shared__ __align__(16) unsigned char As[2 * kAbuf];
+  constexpr int kRows = 32 * NMT;              // rows of an M-block this kernel takes
+  constexpr int kBuf = kRows * kArowBytes;     // bytes of one A stage
+  constexpr int kTPR = 8 / NMT;                // loader threads per A row (16 NMT bytes each)
+  __shared__ __align__(16) unsigned char As[2 * kBuf];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int j = lane & 31, hh = lane >> 5;
   const int K = GATEUP ? D.d : D.f;
@@ -259,15 +273,15 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mfma(LayerDev L, Dims D, const 
   const int items = nmb * ntiles;
   const int per_xcd = gridDim.x >> 3;  // gridDim.x is a multiple of 8
   const int slot_in_round = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-  // A loader role of this thread: row t/2, bytes 64*(t%2) .. +64 of the group
-  const int lrow = threadIdx.x >> 1, lhalf = threadIdx.x & 1;
+  // A loader role of this thread: row t/kTPR, bytes 16 NMT (t % kTPR) .. of the group
+  const int lrow = threadIdx.x / kTPR, lpart = threadIdx.x % kTPR;
   for (int base = 0; base < items; base += gridDim.x) {
     const int item = base + slot_in_round;
     if (item >= items) continue;  // block-uniform
     const int mb = item / ntiles, nt = item - mb * ntiles;
     const int4 ent = list[mb];
     const int e = ent.x, row0 = ent.y, rc = ent.z;
-    const int nmt = (rc + 31) >> 5;  // M-tiles holding rows (1..4)
+    const int nmt = (rc + 31) >> 5;  // M-tiles holding rows (1..NMT)
     GemmItem<GATEUP> it;
     // weight rows come in multiples of 64; a wave past the last one computes
     // on row 0's weights (valid memory) and stores nothing
@@ -283,12 +297,12 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mfma(LayerDev L, Dims D, const 
     it.sc0 = scb + (size_t)it.tile0 * G * 8 + it.r;
     it.sc1 = scb + (size_t)it.tile1 * G * 8 + it.r;
     const bool lok = lrow < rc;
-    const u32x4 *asrc = (const u32x4 *)(A + (size_t)(row0 + (lok ? lrow : 0)) * K + 32 * lhalf);
-    unsigned char *adst = As + lrow * kArowBytes + 64 * lhalf;
+    const u32x4 *asrc = (const u32x4 *)(A + (size_t)(row0 + (lok ? lrow : 0)) * K + 8 * NMT * lpart);
+    unsigned char *adst = As + lrow * kArowBytes + 16 * NMT * lpart;
 
-    f32x16 acc[4][2];
+    f32x16 acc[NMT][2];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
       for (int n = 0; n < 2; ++n)
 #pragma unroll
@@ -299,7 +313,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mfma(LayerDev L, Dims D, const 
     // redundant but valid load at the tail) so the compiler can count
     // outstanding loads exactly and wait only for the ones it consumes.
     const int G1 = G - 1;
-    AStage rA, rB;
+    AStage<NMT> rA, rB;
     rA.load(asrc);
     rA.store(adst);
     rB.load(asrc + 8 * min(1, G1));
@@ -311,14 +325,14 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mfma(LayerDev L, Dims D, const 
     for (int g = 0; g < G; g += 2) {
       // ---- even group g: A(g+1) is in rB, A(g+2) goes to rA
       rA.load(asrc + 8 * min(g + 2, G1));
-      gemm_group<4>(As, sE, nmt, j, hh, acc);
+      gemm_group<NMT>(As, sE, nmt, j, hh, acc);
       it.load(min(g + 2, G1), sE);
-      rB.store(adst + kAbuf);
+      rB.store(adst + kBuf);
       lds_barrier();
       if (g + 1 >= G) break;
       // ---- odd group g+1: A(g+2) is in rA, A(g+3) goes to rB
       rB.load(asrc + 8 * min(g + 3, G1));
-      gemm_group<4>(As + kAbuf, sO, nmt, j, hh, acc);
+      gemm_group<NMT>(As + kBuf, sO, nmt, j, hh, acc);
       it.load(min(g + 3, G1), sO);
       rA.store(adst);
       lds_barrier();
@@ -328,7 +342,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mfma(LayerDev L, Dims D, const 
     // of the M-tile, column j of the 32-column tile.
     if (it.wact) {
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
+      for (int mt = 0; mt < NMT; ++mt) {
         if (mt < nmt) {
 #pragma unroll
           for (int n = 0; n < 2; ++n) {
@@ -459,19 +473,25 @@ hipError_t launch_gather_bf16(const float *x, const Dims &D, const UnionDev &U, 
   return hipGetLastError();
 }
 
-// Blocks of the persistent grid: a multiple of 8 (one share per XCD).
-static int mfma_grid(int max_entries, int ntiles) {
+// Blocks of the persistent grid: a multiple of 8 (one share per XCD), `per_cu`
+// blocks per CU.
+static int mfma_grid(int max_entries, int ntiles, int per_cu) {
   const long items = (long)max_entries * ntiles;
-  long g = 512;  // two blocks per CU
+  long g = 256L * per_cu;
   if (items < g) g = (items + 7) / 8 * 8;
   return (int)(g < 8 ? 8 : g);
 }
 
+// M-blocks of one M-tile (list[0..count[0])) and of up to four
+// (list[max_entries..], count[1]), one kernel each.
 hipError_t launch_gateup_mfma(const LayerDev &L, const Dims &D, const uint16_t *xb, const int4 *list,
                               const int32_t *count, int max_entries, uint16_t *hb, hipStream_t s) {
   if (D.T <= 0) return hipSuccess;
   const int ntiles = (2 * D.f + kNT - 1) / kNT;
-  k_gemm_mfma<true><<<mfma_grid(max_entries, ntiles), 256, 0, s>>>(L, D, xb, list, count, max_entries, hb, nullptr);
+  k_gemm_mfma<true, 1><<<mfma_grid(max_entries, ntiles, 3), 256, 0, s>>>(L, D, xb, list, count, max_entries, hb,
+                                                                          nullptr);
+  k_gemm_mfma<true, 4><<<mfma_grid(max_entries, ntiles, 2), 256, 0, s>>>(L, D, xb, list + max_entries, count + 1,
+                                                                          max_entries, hb, nullptr);
   return hipGetLastError();
 }
 
@@ -479,7 +499,10 @@ hipError_t launch_down_mfma(const LayerDev &L, const Dims &D, const uint16_t *hb
                             const int32_t *count, int max_entries, float *y, hipStream_t s) {
   if (D.T <= 0) return hipSuccess;
   const int ntiles = (D.d + kNT - 1) / kNT;
-  k_gemm_mfma<false><<<mfma_grid(max_entries, ntiles), 256, 0, s>>>(L, D, hb, list, count, max_entries, nullptr, y);
+  k_gemm_mfma<false, 1><<<mfma_grid(max_entries, ntiles, 3), 256, 0, s>>>(L, D, hb, list, count, max_entries,
+                                                                           nullptr, y);
+  k_gemm_mfma<false, 4><<<mfma_grid(max_entries, ntiles, 2), 256, 0, s>>>(L, D, hb, list + max_entries, count + 1,
+                                                                           max_entries, nullptr, y);
   return hipGetLastError();
 }
 
