@@ -66,6 +66,8 @@ def lib():
         L.oracle_moe_token.argtypes = [_vp, i32, i32, i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
         L.oracle_route_token.restype = i32
         L.oracle_route_token.argtypes = [_vp, _vp, _vp, i32, i32, i32, _vp, _vp, _vp]
+        L.oracle_expert_top_p.argtypes = [_vp, i32, i32, ctypes.c_double, _vp, _vp]
+        L.oracle_expert_top_p.restype = i32
         _lib = L
     return _lib
 
@@ -189,8 +191,21 @@ def route_token(R, bias, x, k: int):
     return l, idx, w
 
 
-def route(R, bias, X, k: int):
-    """Route T tokens: logits [T][E], idx [T][k] int32, w [T][k] fp64."""
+def expert_top_p(l, idx, w, p: float):
+    """Adaptive expert top-p of one token's top-k routing (idx, w in top-k
+    order): the shortest prefix whose weight sum reaches p, re-weighted by the
+    softmax over the kept logits; dropped entries idx -1, w 0.  Returns
+    (idx, w, kept)."""
+    l, pl = _c(l, np.float64)
+    idx = np.array(idx, dtype=np.int32)
+    w = np.array(w, dtype=np.float64)
+    m = lib().oracle_expert_top_p(pl, l.size, idx.size, float(p), idx.ctypes.data, w.ctypes.data)
+    return idx, w, int(m)
+
+
+def route(R, bias, X, k: int, top_p: float = 1.0):
+    """Route T tokens: logits [T][E], idx [T][k] int32, w [T][k] fp64 (with
+    expert top-p when top_p < 1)."""
     X = np.atleast_2d(X)
     T = X.shape[0]
     L = np.empty((T, R.shape[0]))
@@ -198,6 +213,8 @@ def route(R, bias, X, k: int):
     W = np.empty((T, k))
     for t in range(T):
         L[t], I[t], W[t] = route_token(R, bias, X[t].astype(np.float64), k)
+        if top_p < 1.0:
+            I[t], W[t], _ = expert_top_p(L[t], I[t], W[t], top_p)
     return L, I, W
 
 

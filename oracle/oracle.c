@@ -225,14 +225,48 @@ void oracle_softmax_selected(const double *l, int E, const int32_t *idx, int k, 
   for (int j = 0; j < k; ++j) w[j] = exp(l[idx[j]] - m) / s;
 }
 
+/* Adaptive expert top-p ([D] key tuning parameters: "topp=0.7", an adaptive
+ * expert top-p that reads 30-40% fewer experts; [D] §4: top-p changes which
+ * experts are read).  Reading: take the k experts in top-k order with their
+ * gate weights w (softmax over the k selected), keep the shortest prefix
+ * whose weight sum reaches p (at least the first expert), and give the kept
+ * experts the softmax over their own logits.  Dropped entries become idx -1,
+ * w 0.  p >= 1 keeps all k.  Returns the number kept. */
+int oracle_expert_top_p(const double *l, int E, int k, double p, int32_t *idx, double *w) {
+  int m = k;
+  if (p < 1.0) {
+    double cum = 0.0;
+    m = 0;
+    while (m < k && (m == 0 || cum < p)) {
+      cum += w[m];
+      ++m;
+    }
+  }
+  if (g_mutation == 9) { /* kept weights left as they were (no softmax over the kept) */
+    for (int j = m; j < k; ++j) {
+      idx[j] = -1;
+      w[j] = 0.0;
+    }
+    return m;
+  }
+  oracle_softmax_selected(l, E, idx, m, w);
+  for (int j = m; j < k; ++j) {
+    idx[j] = -1;
+    w[j] = 0.0;
+  }
+  return m;
+}
+
 /* O6: batch-union ([A] §2: batched positions read each unique expert once).
  * ids: distinct experts, ascending; offsets[u]..offsets[u+1]: that expert's
  * (token, slot) pairs, ordered by token; pair_of[t*k + j]: position of the
- * pair (t, j).  Returns the number of distinct experts. */
+ * pair (t, j), -1 for a slot dropped by expert top-p (idx -1).  Returns the
+ * number of distinct experts. */
 int oracle_union(const int32_t *idx, int T, int k, int E, int32_t *ids, int32_t *offsets, int32_t *pair_token,
                  int32_t *pair_slot, int32_t *pair_of) {
   int n = 0, p = 0;
   offsets[0] = 0;
+  for (size_t i = 0; i < (size_t)T * k; ++i) pair_of[i] = -1;
   for (int e = 0; e < E; ++e) {
     int cnt = 0;
     for (int t = 0; t < T; ++t)
@@ -265,7 +299,7 @@ void oracle_rmsnorm(const double *r, int d, double eps, double *x) {
  *   x        [d]   fp64 activations the router and the experts see
  *   experts  E pointers to canonical blobs (only selected ones are read)
  *   shared   blob of the always-on shared expert or NULL ([D] §3)
- *   idx, w   the routing to apply (k entries)
+ *   idx, w   the routing to apply (k entries; idx -1 is a dropped slot)
  *   residual [d]   the stream the combine adds into
  * out = residual + sum_j w_j y_j + y_shared, and
  * l1[r] = |residual_r| + sum_j |w_j| sum_c |Wd_j[r][c] h_j[c]| + sum_c |Wd_sh[r][c] h_sh[c]|
@@ -279,6 +313,7 @@ int oracle_moe_token(const double *x, int d, int f, int k, const uint8_t *const 
     if (l1) l1[r] = fabs(residual[r]);
   }
   for (int j = 0; j < k; ++j) {
+    if (idx[j] < 0) continue; /* dropped by expert top-p: contributes nothing */
     const uint8_t *b = experts[idx[j]];
     if (!b) {
       free(y);

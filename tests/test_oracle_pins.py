@@ -408,6 +408,92 @@ def test_rmsnorm():
     pin_rmsnorm()
 
 
+# ------------------------------------------------------ expert top-p
+
+def _topp_reference(l, idx, p):
+    """The rule written out with scipy's softmax and numpy sums: the shortest
+    prefix of the top-k whose gate weights reach p, then the softmax over it."""
+    w = softmax(l[idx])
+    m = len(idx)
+    if p < 1.0:
+        m = 1
+        while m < len(idx) and w[:m].sum() < p:
+            m += 1
+    return m, softmax(l[idx[:m]])
+
+
+def pin_expert_top_p():
+    rng = np.random.default_rng(17)
+    E, k = 64, 8
+    seen = set()
+    for trial in range(40):
+        l = rng.standard_normal(E) * (0.5 + trial % 4)
+        idx = np.lexsort((np.arange(E), -l))[:k].astype(np.int32)
+        w = softmax(l[idx])
+        for p in (0.3, 0.5, 0.7, 0.9):
+            cums = np.cumsum(w)
+            if np.min(np.abs(cums - p)) < 1e-9:
+                continue  # a prefix sum at p itself: either side is a valid reading of the boundary
+            m, wk = _topp_reference(l, idx, p)
+            oi, ow, om = oracle.expert_top_p(l, idx, w, p)
+            assert om == m, (trial, p, om, m)
+            assert np.array_equal(oi[:m], idx[:m]) and np.all(oi[m:] == -1)
+            assert np.allclose(ow[:m], wk, rtol=1e-13, atol=0) and np.all(ow[m:] == 0.0)
+            assert abs(ow.sum() - 1.0) < 1e-14
+            # the kept mass before the last kept expert is below p, with it at or above
+            assert (m == 1 or w[:m - 1].sum() < p) and (m == k or w[:m].sum() >= p)
+            seen.add(m)
+    assert len(seen) >= 3  # the cases exercise several kept counts
+    # p = 1 keeps the whole routing; a tiny p keeps the first expert with weight 1
+    l = rng.standard_normal(E)
+    idx = np.lexsort((np.arange(E), -l))[:k].astype(np.int32)
+    w = softmax(l[idx])
+    oi, ow, om = oracle.expert_top_p(l, idx, w, 1.0)
+    assert om == k and np.array_equal(oi, idx) and np.allclose(ow, w, rtol=1e-14, atol=0)
+    oi, ow, om = oracle.expert_top_p(l, idx, w, 1e-12)
+    assert om == 1 and oi[0] == idx[0] and ow[0] == 1.0 and np.all(oi[1:] == -1)
+
+
+def pin_union_with_dropped_slots():
+    rng = np.random.default_rng(5)
+    T, E, k = 6, 12, 4
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    keep = rng.integers(1, k + 1, size=T)
+    for t in range(T):
+        idx[t, keep[t]:] = -1
+    u = oracle.union(idx, E)
+    # brute force over the kept (token, slot) pairs
+    pairs = sorted((int(idx[t, j]), t, j) for t in range(T) for j in range(k) if idx[t, j] >= 0)
+    assert u["n_unique"] == len(set(e for e, _, _ in pairs))
+    assert u["offsets"][-1] == len(pairs) == int(keep.sum())
+    for p, (e, t, j) in enumerate(pairs):
+        assert u["pair_token"][p] == t and u["pair_slot"][p] == j and u["pair_of"][t * k + j] == p
+    for t in range(T):
+        for j in range(k):
+            if idx[t, j] < 0:
+                assert u["pair_of"][t * k + j] == -1
+
+
+def test_expert_top_p():
+    pin_expert_top_p()
+
+
+def test_union_with_dropped_slots():
+    pin_union_with_dropped_slots()
+
+
+def test_dropped_slots_contribute_nothing():
+    """A routing with dropped slots gives the layer output of the kept slots alone."""
+    blobs, R, x = _tiny_inputs(1)
+    ex = {e: blobs[e] for e in range(TINY.E)}
+    x = x[0].astype(np.float64)
+    idx = np.array([3, 11], dtype=np.int32)
+    w = np.array([1.0, 0.0])
+    a, _ = oracle.moe_token(x, TINY.d, TINY.f, ex, None, np.array([3, -1], dtype=np.int32), w, x, TINY.E)
+    b, _ = oracle.moe_token(x, TINY.d, TINY.f, ex, None, idx[:1], w[:1], x, TINY.E)
+    assert np.array_equal(a, b)
+
+
 # -------------------------------------------------------------- page sizes
 
 def _golden_sizes():
@@ -445,10 +531,10 @@ def test_page_sizes():
 
 PINS = [pin_nibble_table, pin_dequant_matches_numpy, pin_matvec_closed_forms, pin_router, pin_topk,
         pin_softmax, pin_silu, pin_expert_dense, pin_onehot_gate, pin_dense_all_experts,
-        pin_tiny_layer_bruteforce]
+        pin_tiny_layer_bruteforce, pin_expert_top_p]
 MUTATIONS = {1: "nibble order swapped", 2: "offset-binary decode", 3: "scale groups along rows",
              4: "shared expert dropped", 5: "softmax over all experts", 6: "ties to the higher index",
-             7: "SiLU sign", 8: "router bias dropped"}
+             7: "SiLU sign", 8: "router bias dropped", 9: "top-p keeps the top-k weights of the kept experts"}
 
 
 @pytest.mark.parametrize("m", sorted(MUTATIONS))
