@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix-core peak of MI355X
+TOP_P = 0.7  # the adaptive expert top-p the pages run with
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_gateup_traffic.json")
 KERNEL_SOURCES = ("kernels.hip", "device_common.h", "internal.h")
 
@@ -149,6 +150,22 @@ def bench_decode(args, torch, np, synth, cm, MoeContext, dev, stream):
     ms = event_time(torch, stream, steps(head, args.warmup, n)) / args.steps
     ctx.sync()
     kern = per_kernel(cm, ctx, steps(head, args.warmup, n))
+    # adaptive expert top-p at the pages' value (p = 0.7): time per token and
+    # routed experts read (sampled outside the timed region)
+    cm.colimoe_set_expert_top_p(ctx.ctx, TOP_P)
+    steps(head, 0, args.warmup)()
+    tms = event_time(torch, stream, steps(head, args.warmup, n)) / args.steps
+    kept = []
+    for i in range(args.warmup, min(n, args.warmup + 64)):
+        step(i, head)
+        kept.append(int(unions[i % args.ring].n_unique.item()))
+    cm.colimoe_set_expert_top_p(ctx.ctx, 1.0)
+    ctx.sync()
+    km = float(np.mean(kept))
+    tb = (km + w.n_shared) * w.expert_bytes
+    topp = {"p": TOP_P, "us_per_token": round(1000 * tms, 3), "routed_experts_mean": round(km, 3),
+            "int4_bytes_per_token_mean": int(tb), "int4_gbs": round(tb / (tms * 1e-3) / 1e9, 1),
+            "sampled_tokens": len(kept)}
     other = None
     if not args.no_compare:
         oflags = cm.COLIMOE_FWD_FP32 if args.path != "fp32" else cm.COLIMOE_FWD_FXP
@@ -160,7 +177,7 @@ def bench_decode(args, torch, np, synth, cm, MoeContext, dev, stream):
     ctx.close()
     del ctx, X, res
     torch.cuda.empty_cache()
-    return w, ms, kern, other
+    return w, ms, kern, other, topp
 
 
 def bench_stack32(args, torch, np, synth, cm, MoeContext, dev, stream):
@@ -355,7 +372,7 @@ def main():
         print(json.dumps(extra), flush=True)
         return
 
-    w, ms_step, kern, other = bench_decode(*common)
+    w, ms_step, kern, other, topp = bench_decode(*common)
     be = w.expert_bytes
     gu_bytes = 2 * (w.d * w.f // 2 + 2 * w.d * w.f // 64)     # gate+up int4 + fp16 scales of one expert
     dn_bytes = be - gu_bytes
@@ -397,6 +414,7 @@ def main():
         "down_gbs": round(dn_gbs, 1),
         "path": args.path,
         "compare": other,
+        "expert_top_p": topp,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "workloads": extra,

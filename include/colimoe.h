@@ -184,6 +184,22 @@ COLIMOE_API int colimoe_union_build(colimoe_ctx *ctx, const int32_t *idx, int32_
 COLIMOE_API int colimoe_forward(colimoe_ctx *ctx, int32_t layer, const float *x, int32_t T, const int32_t *idx,
                     const float *w, const colimoe_union *u, float *residual, uint32_t flags);
 
+/* Adaptive expert top-p for one-token routing ([D] key tuning parameters,
+ * "topp=0.7": an adaptive expert top-p that reads 30-40% fewer experts; [D]
+ * §4: top-p decides which experts are read).  With p < 1, colimoe_route,
+ * colimoe_route_forward and colimoe_rmsnorm_route_forward with T == 1 keep,
+ * of the k selected experts in top-k order, the shortest prefix whose gate
+ * weights (softmax over the k) sum to at least p (at least the first one);
+ * the kept experts get the softmax over their own logits, and a dropped slot
+ * gets idx -1 and weight 0 (pair_of -1 in the union lists, which list the
+ * kept experts only), so the layer reads the kept experts and the shared
+ * expert only.  p = 1 (the default) is plain top-k.  The setting stays until
+ * changed.  A routing with dropped slots is passed to colimoe_forward with
+ * the union lists colimoe_route wrote (the lists cannot be rebuilt from an
+ * idx holding -1).  Calls with T > 1 while p < 1 return E_SHAPE.  Errors:
+ * E_ARG (null ctx, p not in (0, 1]). */
+COLIMOE_API int colimoe_set_expert_top_p(colimoe_ctx *ctx, float p);
+
 /* colimoe_route followed by colimoe_forward on the same x, as one call: the
  * route kernel also encodes x for the fixed-point path, saving a launch.
  * idx, w (outputs) and u (NULL: the workspace's lists) are written as by

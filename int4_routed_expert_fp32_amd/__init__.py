@@ -32,7 +32,7 @@ EXPORTED = [
     "colimoe_create", "colimoe_destroy", "colimoe_set_stream", "colimoe_expert_bytes", "colimoe_layer_bytes",
     "colimoe_workspace_bytes", "colimoe_set_workspace", "colimoe_load_experts", "colimoe_route",
     "colimoe_union_build", "colimoe_forward", "colimoe_route_forward", "colimoe_rmsnorm_route_forward", "colimoe_rmsnorm", "colimoe_debug_expert", "colimoe_sync", "colimoe_status_str",
-    "colimoe_timing_enable", "colimoe_timing_read",
+    "colimoe_timing_enable", "colimoe_timing_read", "colimoe_set_expert_top_p",
 ]
 
 
@@ -73,6 +73,8 @@ def lib() -> ctypes.CDLL:
         cfgp = ctypes.POINTER(colimoe_config)
         L.colimoe_create.argtypes = [cfgp, vp, ctypes.POINTER(vp)]
         L.colimoe_create.restype = ctypes.c_int
+        L.colimoe_set_expert_top_p.argtypes = [vp, ctypes.c_float]
+        L.colimoe_set_expert_top_p.restype = ctypes.c_int
         L.colimoe_destroy.argtypes = [vp]
         L.colimoe_destroy.restype = None
         L.colimoe_set_stream.argtypes = [vp, vp]
@@ -155,6 +157,11 @@ def colimoe_destroy(ctx) -> None:
 
 def colimoe_set_stream(ctx, stream: Optional[int]) -> int:
     return _check("colimoe_set_stream", lib().colimoe_set_stream(ctx, stream or None))
+
+
+def colimoe_set_expert_top_p(ctx, p: float, check: bool = True) -> int:
+    rc = lib().colimoe_set_expert_top_p(ctx, p)
+    return _check("colimoe_set_expert_top_p", rc) if check else rc
 
 
 def colimoe_set_workspace(ctx, dev_ptr: int, nbytes: int, check: bool = True) -> int:

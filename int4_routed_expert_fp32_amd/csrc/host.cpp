@@ -26,6 +26,7 @@ struct colimoe_ctx {
   std::vector<char> loaded;
   uint8_t *ws;
   size_t ws_bytes;
+  float top_p;  // adaptive expert top-p of one-token routing (1: off)
   Workspace wl;
   ExpertLayout el;
   uint8_t *staging[2];  // pinned host buffers for the loader
@@ -305,6 +306,7 @@ static int route_impl(colimoe_ctx *ctx, int32_t layer, const float *x, int32_t T
   float *lg = logits ? logits : (float *)(ctx->ws + ctx->wl.logits);
   hipStream_t s = ctx->stream;
   int32_t *err = (int32_t *)(ctx->ws + ctx->wl.err);
+  if (ctx->top_p < 1.0f && D.T != 1) return COLIMOE_E_SHAPE;  // expert top-p: one-token calls only
   if (D.T <= kRouteSplitMaxT) {
     {
       KTimer kt(ctx, K_ROUTE);
@@ -315,7 +317,7 @@ static int route_impl(colimoe_ctx *ctx, int32_t layer, const float *x, int32_t T
     if (D.T == 1) {
       KTimer kt(ctx, K_TOPK);
       const UnionDev U = u ? to_dev(u) : UnionDev{};
-      if (launch_topk_union1(lg, D, idx, w, u ? &U : nullptr, s) != hipSuccess) return COLIMOE_E_HIP;
+      if (launch_topk_union1(lg, D, idx, w, u ? &U : nullptr, ctx->top_p, s) != hipSuccess) return COLIMOE_E_HIP;
       return COLIMOE_OK;
     }
     if (u) {  // up to 16 tokens: top-k and the union lists in one launch
@@ -460,6 +462,7 @@ int colimoe_create(const colimoe_config *cfg, void *hip_stream, colimoe_ctx **ou
   c->loaded.assign(cfg->n_layers, 0);
   c->ws = nullptr;
   c->ws_bytes = 0;
+  c->top_p = 1.0f;
   c->wl = workspace_layout(cfg->d, cfg->f, cfg->n_experts, cfg->top_k, cfg->n_shared, cfg->max_tokens);
   c->el = expert_layout(cfg->d, cfg->f);
   c->staging[0] = c->staging[1] = nullptr;
@@ -480,6 +483,12 @@ void colimoe_destroy(colimoe_ctx *ctx) {
     if (ctx->staging[i]) (void)hipHostFree(ctx->staging[i]);
   for (hipEvent_t e : ctx->ev_pool) (void)hipEventDestroy(e);
   delete ctx;
+}
+
+int colimoe_set_expert_top_p(colimoe_ctx *ctx, float p) {
+  if (!ctx || !(p > 0.0f && p <= 1.0f)) return COLIMOE_E_ARG;
+  ctx->top_p = p;
+  return COLIMOE_OK;
 }
 
 int colimoe_set_stream(colimoe_ctx *ctx, void *hip_stream) {
@@ -632,6 +641,7 @@ int colimoe_rmsnorm_route_forward(colimoe_ctx *ctx, int32_t layer, float *r, int
   if (T == 0) return COLIMOE_OK;
   if (!r || !x_out || !idx || !w || !aligned(r, 16) || !aligned(x_out, 16) || !aligned(idx, 4) || !aligned(w, 4))
     return COLIMOE_E_ARG;
+  if (ctx->top_p < 1.0f && T != 1) return COLIMOE_E_SHAPE;  // expert top-p: one-token calls only
   if (u && !union_ok(u)) return COLIMOE_E_ARG;
   const int path = select_path(ctx, T, flags);
   if (path < 0) return path;
@@ -656,7 +666,7 @@ int colimoe_rmsnorm_route_forward(colimoe_ctx *ctx, int32_t layer, float *r, int
   {
     KTimer kt(ctx, K_TOPK);
     const UnionDev U = to_dev(uu);
-    if (launch_topk_union1((float *)(ctx->ws + ctx->wl.logits), D, idx, w, &U, ctx->stream) != hipSuccess)
+    if (launch_topk_union1((float *)(ctx->ws + ctx->wl.logits), D, idx, w, &U, ctx->top_p, ctx->stream) != hipSuccess)
       return COLIMOE_E_HIP;
   }
   return forward_impl(ctx, layer, x_out, T, idx, w, uu, r, path, true);

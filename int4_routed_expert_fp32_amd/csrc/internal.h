@@ -106,9 +106,10 @@ hipError_t launch_router_split(const LayerDev &L, const Dims &D, const float *x,
 // equals that of launch_rmsnorm followed by launch_router_split.
 hipError_t launch_router_norm(const LayerDev &L, const Dims &D, const float *r, float eps, float *xout, float *logits,
                               uint32_t *xq, float *xs, hipStream_t s);
-// Top-k of one token and, if U, its union lists (T == 1).
+// Top-k of one token and, if U, its union lists (T == 1); top_p < 1 applies
+// adaptive expert top-p (dropped slots: id -1, weight 0, pair_of -1).
 hipError_t launch_topk_union1(const float *logits, const Dims &D, int32_t *idx, float *w, const UnionDev *U,
-                              hipStream_t s);
+                              float top_p, hipStream_t s);
 hipError_t launch_topk(const float *logits, const Dims &D, int32_t *idx, float *w, hipStream_t s);
 hipError_t launch_union(const int32_t *idx, const Dims &D, const UnionDev &U, int32_t *err, hipStream_t s);
 // Top-k of 1..16 tokens and their union lists in one launch (the results of

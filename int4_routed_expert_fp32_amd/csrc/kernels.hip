@@ -164,6 +164,12 @@ __device__ __forceinline__ uint64_t topk_key(float v, int e) {
 // broadcast from lane 0.  Lane j writes entry j of idx and w (each if
 // non-null) and the id to `lds_ids` (if given).  Every valid key is nonzero,
 // so k <= E rounds always find one.
+// Adaptive expert top-p ([D] key tuning parameters, "topp=0.7": an adaptive
+// expert top-p that reads 30-40% fewer experts), for top_p < 1: lane j keeps
+// its expert while the gate weights of the lanes before it sum to less than
+// top_p (lane 0 always), the sum taken in lane order; kept lanes get the
+// softmax over the kept logits (the same tree over lanes 0..15 with the
+// dropped terms 0), dropped lanes write id -1 and weight 0.
 __device__ __forceinline__ float key_value(uint64_t key) {
   const uint32_t ord = (uint32_t)(key >> 32);
   return bits_f((ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord);
@@ -171,7 +177,8 @@ __device__ __forceinline__ float key_value(uint64_t key) {
 
 template <int PER>
 __device__ __forceinline__ void topk_token(const float *__restrict__ l, const Dims &D, int t,
-                                           int32_t *__restrict__ idx, float *__restrict__ wout, int32_t *lds_ids) {
+                                           int32_t *__restrict__ idx, float *__restrict__ wout, int32_t *lds_ids,
+                                           float top_p = 1.0f) {
   const int lane = threadIdx.x & 63;
   uint64_t key[PER];
 #pragma unroll
@@ -205,9 +212,27 @@ __device__ __forceinline__ void topk_token(const float *__restrict__ l, const Di
   sum = sum + __shfl_xor(sum, 2, 64);
   sum = sum + __shfl_xor(sum, 1, 64);
   sum = bits_f(__builtin_amdgcn_readfirstlane(f_bits(sum)));
+  float wj = ex / sum;
+  if (top_p < 1.0f) {
+    float before = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float wi = __shfl(wj, i, 64);
+      if (i < lane) before = before + wi;
+    }
+    const bool keep = lane < D.k && (lane == 0 || before < top_p);
+    const float exk = keep ? ex : 0.0f;
+    float sk = exk + __shfl_xor(exk, 8, 64);
+    sk = sk + __shfl_xor(sk, 4, 64);
+    sk = sk + __shfl_xor(sk, 2, 64);
+    sk = sk + __shfl_xor(sk, 1, 64);
+    sk = bits_f(__builtin_amdgcn_readfirstlane(f_bits(sk)));
+    wj = keep ? exk / sk : 0.0f;
+    if (!keep) myid = -1;
+  }
   if (lane < D.k) {
     if (idx) idx[(size_t)t * D.k + lane] = myid;
-    if (wout) wout[(size_t)t * D.k + lane] = ex / sum;
+    if (wout) wout[(size_t)t * D.k + lane] = wj;
     if (lds_ids) lds_ids[t * D.k + lane] = myid;
   }
 }
@@ -1322,22 +1347,29 @@ __global__ __launch_bounds__(256) void k_router_split(LayerDev L, Dims D, const 
         ((part[threadIdx.x][0] + part[threadIdx.x][1]) + part[threadIdx.x][2]) + part[threadIdx.x][3] + L.bias[e];
 }
 
-// Union lists of one token from its k distinct expert ids (in LDS): the ids
-// ascending, one pair each, pair_slot = the id's position in the top-k.
+// Union lists of one token from its k expert ids (in LDS; distinct, or -1 for
+// a slot dropped by expert top-p): the kept ids ascending, one pair each,
+// pair_slot = the id's position in the top-k, pair_of = -1 for a dropped slot.
 __device__ __forceinline__ void union_one_token(const int32_t *ids, const Dims &D, const UnionDev &U) {
   const int j = threadIdx.x & 63;
   if (j < D.k) {
+    int m = 0;
+    for (int i = 0; i < D.k; ++i) m += ids[i] >= 0;
     const int e = ids[j];
-    int rank = 0;
-    for (int i = 0; i < D.k; ++i) rank += ids[i] < e;
-    U.ids[rank] = e;
-    U.offsets[rank] = rank;
-    U.pair_token[rank] = 0;
-    U.pair_slot[rank] = j;
-    U.pair_of[j] = rank;
+    if (e >= 0) {
+      int rank = 0;
+      for (int i = 0; i < D.k; ++i) rank += ids[i] >= 0 && ids[i] < e;
+      U.ids[rank] = e;
+      U.offsets[rank] = rank;
+      U.pair_token[rank] = 0;
+      U.pair_slot[rank] = j;
+      U.pair_of[j] = rank;
+    } else {
+      U.pair_of[j] = -1;
+    }
     if (j == 0) {
-      *U.n_unique = D.k;
-      U.offsets[D.k] = D.k;
+      *U.n_unique = m;
+      U.offsets[m] = m;
     }
   }
 }
@@ -1346,9 +1378,9 @@ __device__ __forceinline__ void union_one_token(const int32_t *ids, const Dims &
 template <int PER>
 __global__ __launch_bounds__(64) void k_topk_union1(const float *__restrict__ logits, Dims D,
                                                     int32_t *__restrict__ idx, float *__restrict__ wout, UnionDev U,
-                                                    int with_union) {
+                                                    int with_union, float top_p) {
   __shared__ int32_t ids[16];
-  topk_token<PER>(logits, D, 0, idx, wout, ids);
+  topk_token<PER>(logits, D, 0, idx, wout, ids, top_p);
   wave_lds_sync();
   if (with_union) union_one_token(ids, D, U);
 }
@@ -1702,14 +1734,15 @@ hipError_t launch_router_norm(const LayerDev &L, const Dims &D, const float *r, 
 }
 
 hipError_t launch_topk_union1(const float *logits, const Dims &D, int32_t *idx, float *w, const UnionDev *U,
-                              hipStream_t s) {
+                              float top_p, hipStream_t s) {
   const UnionDev u = U ? *U : UnionDev{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
+  const int wu = U ? 1 : 0;
   switch (topk_per(D.E)) {
-    case 1: k_topk_union1<1><<<1, 64, 0, s>>>(logits, D, idx, w, u, U ? 1 : 0); break;
-    case 2: k_topk_union1<2><<<1, 64, 0, s>>>(logits, D, idx, w, u, U ? 1 : 0); break;
-    case 4: k_topk_union1<4><<<1, 64, 0, s>>>(logits, D, idx, w, u, U ? 1 : 0); break;
-    case 8: k_topk_union1<8><<<1, 64, 0, s>>>(logits, D, idx, w, u, U ? 1 : 0); break;
-    default: k_topk_union1<16><<<1, 64, 0, s>>>(logits, D, idx, w, u, U ? 1 : 0); break;
+    case 1: k_topk_union1<1><<<1, 64, 0, s>>>(logits, D, idx, w, u, wu, top_p); break;
+    case 2: k_topk_union1<2><<<1, 64, 0, s>>>(logits, D, idx, w, u, wu, top_p); break;
+    case 4: k_topk_union1<4><<<1, 64, 0, s>>>(logits, D, idx, w, u, wu, top_p); break;
+    case 8: k_topk_union1<8><<<1, 64, 0, s>>>(logits, D, idx, w, u, wu, top_p); break;
+    default: k_topk_union1<16><<<1, 64, 0, s>>>(logits, D, idx, w, u, wu, top_p); break;
   }
   return hipGetLastError();
 }

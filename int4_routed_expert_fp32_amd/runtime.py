@@ -14,6 +14,7 @@ import numpy as np
 import torch
 
 from . import (COLIMOE_FWD_AUTO, colimoe_create, colimoe_debug_expert, colimoe_destroy, colimoe_forward,
+               colimoe_set_expert_top_p,
                colimoe_layer_bytes, colimoe_load_experts, colimoe_rmsnorm, colimoe_rmsnorm_route_forward, colimoe_route,
                colimoe_route_forward,
                colimoe_set_stream,
@@ -69,6 +70,9 @@ class MoeContext:
     def _aligned(t: torch.Tensor, nbytes: int) -> torch.Tensor:
         off = (-t.data_ptr()) % 256
         return t[off:off + nbytes]
+
+    def set_expert_top_p(self, p: float) -> None:
+        colimoe_set_expert_top_p(self.ctx, p)
 
     def set_stream(self, stream: torch.cuda.Stream) -> None:
         self.stream = stream

@@ -79,10 +79,12 @@ class OracleLayer:
         self._blobs = {}
 
     def blobs(self, ids):
-        need = sorted(set(int(e) for e in ids) - set(self._blobs))
+        """Blobs of the experts in ids (an id of -1, a slot dropped by expert top-p, needs none)."""
+        ids = [int(e) for e in ids if int(e) >= 0]
+        need = sorted(set(ids) - set(self._blobs))
         for e in need:
             self._blobs[e] = synth.expert_blobs(self.w, self.layer, e, e + 1)[0].copy()
-        return {e: self._blobs[e] for e in set(int(i) for i in ids)}
+        return {e: self._blobs[e] for e in set(ids)}
 
     def route(self, X):
         return oracle.route(self.R, self.b, np.asarray(X, dtype=np.float64), self.w.k)

@@ -58,6 +58,7 @@ def test_null_arguments_rejected():
     L = cm.lib()
     assert L.colimoe_create(None, None, None) == cm.COLIMOE_E_ARG
     assert L.colimoe_route(None, 0, None, 1, None, None, None, None) == cm.COLIMOE_E_ARG
+    assert L.colimoe_set_expert_top_p(None, 0.7) == cm.COLIMOE_E_ARG
     assert L.colimoe_forward(None, 0, None, 1, None, None, None, None, 0) == cm.COLIMOE_E_ARG
     assert L.colimoe_load_experts(None, 0, None, None, 0) == cm.COLIMOE_E_ARG
     assert L.colimoe_union_build(None, None, 1, None) == cm.COLIMOE_E_ARG

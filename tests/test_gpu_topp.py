@@ -1,0 +1,153 @@
+"""Adaptive expert top-p on one-token calls, against the oracle.
+
+Rule (the oracle's): of the k experts in top-k order, keep the shortest prefix
+whose gate weights (softmax over the k) reach p, re-weighted by the softmax
+over the kept logits; dropped slots get id -1 and weight 0 and are not read.
+The GPU decides in fp32, the oracle in fp64: a token whose kept count differs
+is accepted only when the prefix mass at the boundary is within 1e-5 of p, and
+its outputs are then checked under the GPU's kept set.  Outputs: the fp32
+bound |gpu - oracle| <= 1e-3 (1 + |oracle|); union lists exactly.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests import _parity as P
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+FP32, FXP = 1, 3
+P_PAGES = 0.7  # the value the pages run with
+DECODE = synth.WORKLOADS["decode"]
+
+
+def _ctx(w, n_layers=1, max_tokens=1):
+    from int4_routed_expert_fp32_amd.runtime import MoeContext
+    print("context", w.name, w.d, w.f, w.E, w.k, flush=True)
+    return MoeContext(w.d, w.f, w.E, w.k, n_layers=n_layers, n_shared=w.n_shared, max_tokens=max_tokens)
+
+
+@pytest.fixture(scope="module")
+def dec():
+    oracle.build(force=False)
+    synth.build(force=False)
+    ctx = _ctx(DECODE)
+    P.load_layer(ctx, DECODE, 0)
+    yield ctx, P.OracleLayer(DECODE, 0)
+    ctx.close()
+
+
+def _one_call(ctx, x, flags):
+    U = ctx.new_union(1)
+    res = x.clone()
+    idx, w = ctx.route_forward(0, x, U, res, flags)
+    ctx.sync()
+    return idx.cpu().numpy()[0], w.cpu().numpy()[0], U.to_host(), res.cpu().numpy()[0]
+
+
+def check_topp_token(ora, x, gidx, gw, union, gout, k, p):
+    """Checks one token's top-p routing, weights, union lists and output; returns the kept count."""
+    l, oidx, ow = ora.route(x[None, :])
+    l, oidx, ow = l[0], oidx[0], ow[0]
+    m = int(np.sum(gidx >= 0))
+    assert m >= 1 and np.all(gidx[:m] >= 0) and np.all(gidx[m:] == -1), gidx
+    assert np.array_equal(gidx[:m], oidx[:m]), (gidx, oidx)  # a prefix of the top-k order
+    _, _, mo = oracle.expert_top_p(l, oidx, ow, p)
+    if m != mo:
+        cum = float(np.sum(ow[:min(m, mo)]))
+        assert abs(cum - p) < 1e-5, "kept %d, oracle %d, boundary mass %.9f" % (m, mo, cum)
+    wref = np.zeros(k)
+    wref[:m] = oracle.softmax_selected(l, gidx[:m])
+    P.assert_close(gw, wref, rel=1e-4, what="top-p gate weights")
+    assert np.all(gw[m:] == 0.0)
+    out, _ = ora.forward(x[None, :], gidx[None, :], wref[None, :])
+    P.assert_close(gout[None, :], out, what="top-p layer output")
+    ou = oracle.union(gidx[None, :], ora.w.E)
+    assert union["n_unique"] == ou["n_unique"] == m
+    for key in ("ids", "offsets", "pair_of"):
+        assert np.array_equal(union[key], ou[key]), key
+    for key in ("pair_token", "pair_slot"):
+        assert np.array_equal(union[key][:m], ou[key][:m]), key
+    return m
+
+
+@pytest.mark.parametrize("flags", [FXP, FP32], ids=["fxp", "fp32"])
+def test_topp_decode_parity(dec, flags):
+    ctx, ora = dec
+    ctx.set_expert_top_p(P_PAGES)
+    try:
+        X = synth.activations(DECODE.with_(T=12), stream=31)
+        kept = []
+        for t in range(X.shape[0]):
+            x = torch.from_numpy(X[t:t + 1]).cuda()
+            gidx, gw, union, gout = _one_call(ctx, x, flags)
+            kept.append(check_topp_token(ora, X[t].astype(np.float64), gidx, gw, union, gout, DECODE.k, P_PAGES))
+            # route, then forward with the lists route wrote: the same bits
+            U = ctx.new_union(1)
+            idx, w, _ = ctx.route(0, x, U)
+            res = x.clone()
+            ctx.forward(0, x, idx, w, U, res, flags)
+            ctx.sync()
+            assert np.array_equal(idx.cpu().numpy()[0], gidx)
+            assert np.array_equal(res.cpu().numpy()[0].view(np.uint32), gout.view(np.uint32))
+        print("top-p %.2f: experts kept per token" % P_PAGES, kept, "mean %.2f of %d" % (np.mean(kept), DECODE.k))
+        assert min(kept) < DECODE.k  # the workload does drop experts
+    finally:
+        ctx.set_expert_top_p(1.0)
+
+
+def test_topp_one_is_plain_topk(dec):
+    ctx, ora = dec
+    x = torch.from_numpy(synth.activations(DECODE.with_(T=1), stream=32)).cuda()
+    a = _one_call(ctx, x, FXP)
+    ctx.set_expert_top_p(0.5)
+    ctx.set_expert_top_p(1.0)
+    b = _one_call(ctx, x, FXP)
+    assert np.array_equal(a[0], b[0]) and np.all(a[0] >= 0)
+    assert np.array_equal(a[3].view(np.uint32), b[3].view(np.uint32))
+
+
+def test_topp_stack_step_matches_two_calls(dec):
+    """colimoe_rmsnorm_route_forward with top-p: the bits of colimoe_rmsnorm
+    followed by colimoe_route_forward."""
+    ctx, ora = dec
+    ctx.set_expert_top_p(P_PAGES)
+    try:
+        R = torch.from_numpy(synth.activations(DECODE.with_(T=3), stream=33) * 2.0).cuda()
+        for t in range(3):
+            r1, r2 = R[t:t + 1].clone(), R[t:t + 1].clone()
+            x1, x2 = torch.empty_like(r1), torch.empty_like(r2)
+            U1, U2 = ctx.new_union(1), ctx.new_union(1)
+            i1, w1 = ctx.rmsnorm_route_forward(0, r1, 1e-6, x1, U1, FXP)
+            ctx.rmsnorm(r2, 1e-6, x2)
+            i2, w2 = ctx.route_forward(0, x2, U2, r2, FXP)
+            ctx.sync()
+            assert torch.equal(i1, i2) and torch.equal(x1, x2)
+            assert np.array_equal(w1.cpu().numpy().view(np.uint32), w2.cpu().numpy().view(np.uint32))
+            assert np.array_equal(r1.cpu().numpy().view(np.uint32), r2.cpu().numpy().view(np.uint32))
+    finally:
+        ctx.set_expert_top_p(1.0)
+
+
+def test_topp_rejections():
+    import int4_routed_expert_fp32_amd as cm
+    w = synth.WORKLOADS["tiny"]
+    ctx = _ctx(w, max_tokens=2)
+    P.load_layer(ctx, w, 0)
+    for bad in (0.0, -0.5, 1.5, math.nan):
+        assert cm.colimoe_set_expert_top_p(ctx.ctx, bad, check=False) == cm.COLIMOE_E_ARG
+    ctx.set_expert_top_p(0.6)
+    x = torch.from_numpy(synth.activations(w.with_(T=2), stream=34)).cuda()
+    idx = torch.empty((2, w.k), dtype=torch.int32, device="cuda")
+    wt = torch.empty((2, w.k), dtype=torch.float32, device="cuda")
+    res = x.clone()
+    rc = cm.colimoe_route_forward(ctx.ctx, 0, x.data_ptr(), 2, idx.data_ptr(), wt.data_ptr(), None, res.data_ptr(),
+                                  0, check=False)
+    assert rc == cm.COLIMOE_E_SHAPE
+    ctx.sync()
+    assert torch.equal(res, x)  # a rejected call has no effect
+    ctx.close()
