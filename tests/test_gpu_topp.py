@@ -151,3 +151,30 @@ def test_topp_rejections():
     ctx.sync()
     assert torch.equal(res, x)  # a rejected call has no effect
     ctx.close()
+
+
+# odd shapes on the fp32 kernels: partial lane groups, E not a multiple of 64,
+# with and without a shared expert
+RAGGED = synth.Workload(name="ragged", d=320, f=192, E=37, k=3, T=6, n_shared=1, zipf=1.1, rho=0.3,
+                        seed=synth.BASE_SEED + 101)
+TINY6 = synth.WORKLOADS["tiny"].with_(T=6)
+
+
+@pytest.mark.parametrize("w", [RAGGED, TINY6], ids=lambda w: w.name)
+def test_topp_small_shapes(w):
+    ctx = _ctx(w)
+    P.load_layer(ctx, w, 0)
+    ora = P.OracleLayer(w, 0)
+    ctx.set_expert_top_p(0.5)
+    X = synth.activations(w, stream=35)
+    kept = []
+    for t in range(w.T):
+        x = torch.from_numpy(X[t:t + 1]).cuda()
+        U = ctx.new_union(1)
+        res = x.clone()
+        idx, wt = ctx.route_forward(0, x, U, res, FP32)
+        ctx.sync()
+        kept.append(check_topp_token(ora, X[t].astype(np.float64), idx.cpu().numpy()[0], wt.cpu().numpy()[0],
+                                     U.to_host(), res.cpu().numpy()[0], w.k, 0.5))
+    print(w.name, "experts kept per token", kept)
+    ctx.close()
