@@ -44,6 +44,7 @@ def parse():
     ap.add_argument("--path", choices=("auto", "fp32", "fxp"), default="auto",
                     help="arithmetic path of the headline (auto: fixed-point activations at these shapes)")
     ap.add_argument("--no-compare", action="store_true", help="skip timing the other arithmetic path")
+    ap.add_argument("--no-top-p", action="store_true", help="skip the adaptive expert top-p line of the decode workload")
     ap.add_argument("--only", choices=("all", "decode", "stack32", "union16", "verify", "prefill2048"), default="all",
                     help="run one workload only (the headline line needs decode)")
     return ap.parse_args()
@@ -150,22 +151,24 @@ def bench_decode(args, torch, np, synth, cm, MoeContext, dev, stream):
     ms = event_time(torch, stream, steps(head, args.warmup, n)) / args.steps
     ctx.sync()
     kern = per_kernel(cm, ctx, steps(head, args.warmup, n))
-    # adaptive expert top-p at the pages' value (p = 0.7): time per token and
-    # routed experts read (sampled outside the timed region)
-    cm.colimoe_set_expert_top_p(ctx.ctx, TOP_P)
-    steps(head, 0, args.warmup)()
-    tms = event_time(torch, stream, steps(head, args.warmup, n)) / args.steps
-    kept = []
-    for i in range(args.warmup, min(n, args.warmup + 64)):
-        step(i, head)
-        kept.append(int(unions[i % args.ring].n_unique.item()))
-    cm.colimoe_set_expert_top_p(ctx.ctx, 1.0)
-    ctx.sync()
-    km = float(np.mean(kept))
-    tb = (km + w.n_shared) * w.expert_bytes
-    topp = {"p": TOP_P, "us_per_token": round(1000 * tms, 3), "routed_experts_mean": round(km, 3),
-            "int4_bytes_per_token_mean": int(tb), "int4_gbs": round(tb / (tms * 1e-3) / 1e9, 1),
-            "sampled_tokens": len(kept)}
+    topp = None
+    if not args.no_top_p:
+        # adaptive expert top-p at the pages' value (p = 0.7): time per token and
+        # routed experts read (sampled outside the timed region)
+        cm.colimoe_set_expert_top_p(ctx.ctx, TOP_P)
+        steps(head, 0, args.warmup)()
+        tms = event_time(torch, stream, steps(head, args.warmup, n)) / args.steps
+        kept = []
+        for i in range(args.warmup, min(n, args.warmup + 64)):
+            step(i, head)
+            kept.append(int(unions[i % args.ring].n_unique.item()))
+        cm.colimoe_set_expert_top_p(ctx.ctx, 1.0)
+        ctx.sync()
+        km = float(np.mean(kept))
+        tb = (km + w.n_shared) * w.expert_bytes
+        topp = {"p": TOP_P, "us_per_token": round(1000 * tms, 3), "routed_experts_mean": round(km, 3),
+                "int4_bytes_per_token_mean": int(tb), "int4_gbs": round(tb / (tms * 1e-3) / 1e9, 1),
+                "sampled_tokens": len(kept)}
     other = None
     if not args.no_compare:
         oflags = cm.COLIMOE_FWD_FP32 if args.path != "fp32" else cm.COLIMOE_FWD_FXP
