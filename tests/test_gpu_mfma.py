@@ -124,3 +124,39 @@ def test_prefill2048_parity():
     print("prefill2048: %d unique experts, rows per expert max %d, >=64: %d; worst ratio %.3g over %d tokens; "
           "near-tie tokens %d" % (union["n_unique"], counts.max(), int((counts >= 64).sum()), ratio, sample.size,
                                   len(differ)))
+
+
+def test_mfma_block_class_boundaries():
+    """A forced routing that gives experts 1, 32, 33, 128, 129, 160 and 257
+    rows: M-blocks at both edges of the one-M-tile class (<= 32 rows) and of
+    the 128-row blocks, through the bf16 path, against the oracle under the
+    same routing."""
+    w = synth.Workload(name="mfma_edges", d=384, f=256, E=24, k=4, T=257, n_shared=1, seed=synth.BASE_SEED + 204)
+    counts = {0: 32, 1: 33, 2: 128, 3: 129, 4: 160, 5: 1, 6: 257}
+    rest = w.T * w.k - sum(counts.values())
+    others = list(range(7, w.E))
+    for i, e in enumerate(others):
+        counts[e] = rest // len(others) + (1 if i < rest % len(others) else 0)
+    pairs = [e for e in sorted(counts) for _ in range(counts[e])]
+    # pair i goes to token i mod T: an expert's pairs land on distinct tokens
+    idx = np.zeros((w.T, w.k), dtype=np.int32)
+    fill = np.zeros(w.T, dtype=np.int64)
+    for i, e in enumerate(pairs):
+        t = i % w.T
+        idx[t, fill[t]] = e
+        fill[t] += 1
+    assert np.all(fill == w.k) and all(len(set(r)) == w.k for r in idx.tolist())
+    rng = np.random.default_rng(204)
+    wts = rng.uniform(0.05, 1.0, size=(w.T, w.k))
+    wts = (wts / wts.sum(axis=1, keepdims=True)).astype(np.float32)
+    ctx = _ctx(w)
+    P.load_layer(ctx, w, 0)
+    X = synth.activations(w, stream=9)
+    xt = torch.from_numpy(X).cuda()
+    res = xt.clone()
+    ctx.forward(0, xt, torch.from_numpy(idx).cuda(), torch.from_numpy(wts).cuda(), None, res, MFMA)
+    ctx.sync()
+    ora = P.OracleLayer(w, 0)
+    out, l1 = ora.forward(X, idx, wts.astype(np.float64))
+    r = assert_bf16_bound(res.cpu().numpy(), out, l1, w.name)
+    print("%s: worst ratio %.3g" % (w.name, r))
