@@ -161,6 +161,44 @@ COLIMOE_API int colimoe_set_workspace(colimoe_ctx *ctx, void *dev, size_t bytes)
 COLIMOE_API int colimoe_load_experts(colimoe_ctx *ctx, int32_t layer, const colimoe_layer_src *src, void *dev_dst,
                          size_t dev_bytes);
 
+/* Tiered placement for models whose experts do not all fit in HBM ([A] §2:
+ * the routed experts stay on slower storage and are read on demand into a
+ * cache with least-recently-used eviction; [P]: the hot experts stay close;
+ * here host RAM over PCIe plays the disk and HBM the RAM).
+ *
+ * colimoe_expert_cache_bytes: device bytes of an expert cache of n_slots
+ * slots (slot maps of every layer, then the slots); 0 for a bad config or
+ * n_slots < 1.  colimoe_host_layer_bytes: device bytes of a host-resident
+ * layer (router and bias only).
+ *
+ * colimoe_set_expert_cache: the caller-owned device buffer (256-byte aligned)
+ * the cache lives in, before any host-resident layer is loaded (E_STATE once
+ * one is).  Errors: E_ARG, E_STATE, E_WORKSPACE (room for less than one
+ * slot), E_HIP.
+ *
+ * colimoe_load_experts_host: as colimoe_load_experts, but the routed experts
+ * are repacked into pinned host memory owned by the context (freed by
+ * colimoe_destroy or when the layer is loaded again); router and bias go to
+ * dev_dst (colimoe_host_layer_bytes); the shared expert takes a cache slot of
+ * its own for the layer's lifetime.  A forward on such a layer first copies
+ * the routing to the host (this synchronises the stream), brings each missing
+ * expert into the least recently used slot the call does not need, and then
+ * runs the same kernels, reading every expert from the cache: results are
+ * bit-identical to the layer loaded with colimoe_load_experts.  A call whose
+ * routing names more distinct experts than there are free slots returns
+ * E_WORKSPACE.  colimoe_debug_expert on such a layer returns E_STATE.
+ * Errors: E_ARG, E_SHAPE, E_STATE (no cache), E_WORKSPACE (cache too small for
+ * the shared expert and one token's experts), E_HIP.
+ *
+ * colimoe_cache_stats: experts found in the cache and brought in since the
+ * cache was set, and its number of slots.  Errors: E_ARG. */
+COLIMOE_API size_t colimoe_expert_cache_bytes(const colimoe_config *cfg, int32_t n_slots);
+COLIMOE_API size_t colimoe_host_layer_bytes(const colimoe_config *cfg);
+COLIMOE_API int colimoe_set_expert_cache(colimoe_ctx *ctx, void *dev, size_t bytes);
+COLIMOE_API int colimoe_load_experts_host(colimoe_ctx *ctx, int32_t layer, const colimoe_layer_src *src, void *dev_dst,
+                              size_t dev_bytes);
+COLIMOE_API int colimoe_cache_stats(colimoe_ctx *ctx, int64_t *hits, int64_t *misses, int32_t *slots);
+
 /* Route T tokens (device pointers).  x [T][d] fp32 -> idx [T][k] int32,
  * w [T][k] fp32.  If u is non-NULL its arrays receive the batch-union lists.
  * logits [T][E] fp32 may be NULL.  Errors: E_ARG, E_SHAPE, E_NOT_LOADED,

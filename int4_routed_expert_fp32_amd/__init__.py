@@ -32,7 +32,8 @@ EXPORTED = [
     "colimoe_create", "colimoe_destroy", "colimoe_set_stream", "colimoe_expert_bytes", "colimoe_layer_bytes",
     "colimoe_workspace_bytes", "colimoe_set_workspace", "colimoe_load_experts", "colimoe_route",
     "colimoe_union_build", "colimoe_forward", "colimoe_route_forward", "colimoe_rmsnorm_route_forward", "colimoe_rmsnorm", "colimoe_debug_expert", "colimoe_sync", "colimoe_status_str",
-    "colimoe_timing_enable", "colimoe_timing_read", "colimoe_set_expert_top_p",
+    "colimoe_timing_enable", "colimoe_timing_read", "colimoe_set_expert_top_p", "colimoe_expert_cache_bytes",
+    "colimoe_host_layer_bytes", "colimoe_set_expert_cache", "colimoe_load_experts_host", "colimoe_cache_stats",
 ]
 
 
@@ -86,6 +87,17 @@ def lib() -> ctypes.CDLL:
         L.colimoe_set_workspace.restype = ctypes.c_int
         L.colimoe_load_experts.argtypes = [vp, i32, ctypes.POINTER(colimoe_layer_src), vp, sz]
         L.colimoe_load_experts.restype = ctypes.c_int
+        L.colimoe_load_experts_host.argtypes = [vp, i32, ctypes.POINTER(colimoe_layer_src), vp, sz]
+        L.colimoe_load_experts_host.restype = ctypes.c_int
+        L.colimoe_expert_cache_bytes.argtypes = [cfgp, i32]
+        L.colimoe_expert_cache_bytes.restype = sz
+        L.colimoe_host_layer_bytes.argtypes = [cfgp]
+        L.colimoe_host_layer_bytes.restype = sz
+        L.colimoe_set_expert_cache.argtypes = [vp, vp, sz]
+        L.colimoe_set_expert_cache.restype = ctypes.c_int
+        L.colimoe_cache_stats.argtypes = [vp, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64),
+                                          ctypes.POINTER(i32)]
+        L.colimoe_cache_stats.restype = ctypes.c_int
         L.colimoe_route.argtypes = [vp, i32, vp, i32, vp, vp, ctypes.POINTER(colimoe_union), vp]
         L.colimoe_route.restype = ctypes.c_int
         L.colimoe_union_build.argtypes = [vp, vp, i32, ctypes.POINTER(colimoe_union)]
@@ -174,6 +186,33 @@ def colimoe_load_experts(ctx, layer: int, router_host: int, bias_host: Optional[
     src = colimoe_layer_src(router_host, bias_host or None, experts_host, shared_host or None)
     rc = lib().colimoe_load_experts(ctx, layer, ctypes.byref(src), dev_dst, dev_bytes)
     return _check("colimoe_load_experts", rc) if check else rc
+
+
+def colimoe_load_experts_host(ctx, layer: int, router_host: int, bias_host: Optional[int], experts_host: int,
+                              shared_host: Optional[int], dev_dst: int, dev_bytes: int, check: bool = True) -> int:
+    src = colimoe_layer_src(router_host, bias_host or None, experts_host, shared_host or None)
+    rc = lib().colimoe_load_experts_host(ctx, layer, ctypes.byref(src), dev_dst, dev_bytes)
+    return _check("colimoe_load_experts_host", rc) if check else rc
+
+
+def colimoe_expert_cache_bytes(cfg: colimoe_config, n_slots: int) -> int:
+    return int(lib().colimoe_expert_cache_bytes(ctypes.byref(cfg), n_slots))
+
+
+def colimoe_host_layer_bytes(cfg: colimoe_config) -> int:
+    return int(lib().colimoe_host_layer_bytes(ctypes.byref(cfg)))
+
+
+def colimoe_set_expert_cache(ctx, dev_ptr: int, nbytes: int, check: bool = True) -> int:
+    rc = lib().colimoe_set_expert_cache(ctx, dev_ptr, nbytes)
+    return _check("colimoe_set_expert_cache", rc) if check else rc
+
+
+def colimoe_cache_stats(ctx):
+    """(hits, misses, slots) of the expert cache."""
+    h, m, n = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int32()
+    _check("colimoe_cache_stats", lib().colimoe_cache_stats(ctx, ctypes.byref(h), ctypes.byref(m), ctypes.byref(n)))
+    return int(h.value), int(m.value), int(n.value)
 
 
 def make_union(n_unique: int, ids: int, offsets: int, pair_token: int, pair_slot: int,

@@ -24,6 +24,23 @@ struct colimoe_ctx {
   int device;
   std::vector<LayerDev> layers;
   std::vector<char> loaded;
+  // Tiered placement: routed experts of host-resident layers live in pinned
+  // host memory (device layout) and move into an HBM cache of fixed slots on
+  // demand, least recently used out.
+  std::vector<uint8_t *> host_store;  // per layer: E * expert bytes, or null
+  struct Cache {
+    uint8_t *slots = nullptr;      // device: n_slots * expert bytes
+    int32_t *dev_maps = nullptr;   // device: [n_layers][E + 1] slot of each expert
+    int32_t *stage = nullptr;      // pinned host copy of the maps as uploaded
+    int32_t *idx_host = nullptr;   // pinned host: a call's routing
+    int n_slots = 0;
+    std::vector<int32_t> slot_of;  // [n_layers][E + 1]: slot or -1
+    std::vector<int64_t> tag;      // per slot: layer * (E + 1) + expert, or -1
+    std::vector<uint64_t> used;    // per slot: call stamp of the last use
+    std::vector<char> fixed;       // per slot: holds a shared expert (never evicted)
+    uint64_t stamp = 0;
+    int64_t hits = 0, misses = 0;
+  } cache;
   uint8_t *ws;
   size_t ws_bytes;
   float top_p;  // adaptive expert top-p of one-token routing (1: off)
@@ -342,11 +359,90 @@ static int route_impl(colimoe_ctx *ctx, int32_t layer, const float *x, int32_t T
 
 // Expert work and combine.  x_encoded: the workspace already holds the
 // fixed-point encoding of this x (written by the route kernel).
+// Tiered placement: makes every expert of routing idx [T][k] (device) of a
+// host-resident layer present in the HBM cache.  Copies the routing to the
+// host (synchronising the stream, so no earlier kernel still reads a slot),
+// counts hits, brings each missing expert in over PCIe into the slot used
+// least recently (never one this call needs, never a shared expert's), and
+// uploads the layer's slot map.  A map entry of an expert not in the cache
+// points at the layer's shared-expert slot, so every address a kernel forms
+// stays inside the cache.  E_WORKSPACE if the call needs more experts than
+// the cache has slots for.
+static int ensure_resident(colimoe_ctx *ctx, int32_t layer, const int32_t *idx, int32_t T) {
+  colimoe_ctx::Cache &C = ctx->cache;
+  const int E = ctx->cfg.n_experts, k = ctx->cfg.top_k;
+  const size_t be = ctx->el.bytes;
+  hipStream_t s = ctx->stream;
+  if (hipMemcpyAsync(C.idx_host, idx, (size_t)T * k * 4, hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return COLIMOE_E_HIP;
+  std::vector<int> need;
+  for (int i = 0; i < T * k; ++i) {
+    const int e = C.idx_host[i];
+    if (e >= 0 && e < E) need.push_back(e);
+  }
+  std::sort(need.begin(), need.end());
+  need.erase(std::unique(need.begin(), need.end()), need.end());
+  int free_slots = 0;
+  for (int i = 0; i < C.n_slots; ++i) free_slots += !C.fixed[i];
+  if ((int)need.size() > free_slots) return COLIMOE_E_WORKSPACE;
+  const uint64_t now = ++C.stamp;
+  int32_t *map = &C.slot_of[(size_t)layer * (E + 1)];
+  for (int e : need)
+    if (map[e] >= 0) {
+      C.used[map[e]] = now;
+      ++C.hits;
+    }
+  for (int e : need) {
+    if (map[e] >= 0) continue;
+    int victim = -1;
+    for (int i = 0; i < C.n_slots; ++i)
+      if (!C.fixed[i] && C.used[i] != now && (victim < 0 || C.used[i] < C.used[victim])) victim = i;
+    if (victim < 0) return COLIMOE_E_WORKSPACE;
+    if (C.tag[victim] >= 0) C.slot_of[(size_t)C.tag[victim]] = -1;
+    if (hipMemcpyAsync(C.slots + (size_t)victim * be, ctx->host_store[layer] + (size_t)e * be, be,
+                       hipMemcpyHostToDevice, s) != hipSuccess)
+      return COLIMOE_E_HIP;
+    C.tag[victim] = (int64_t)layer * (E + 1) + e;
+    C.used[victim] = now;
+    map[e] = victim;
+    ++C.misses;
+  }
+  int32_t *st = C.stage + (size_t)layer * (E + 1);
+  const int dummy = map[E] >= 0 ? map[E] : 0;
+  for (int e = 0; e <= E; ++e) st[e] = map[e] >= 0 ? map[e] : dummy;
+  return hip_status(hipMemcpyAsync(C.dev_maps + (size_t)layer * (E + 1), st, (size_t)(E + 1) * 4,
+                                   hipMemcpyHostToDevice, s));
+}
+
+// Forgets a layer's place in the expert cache (its routed experts and its
+// shared-expert slot) and frees its host store.
+static void cache_drop_layer(colimoe_ctx *ctx, int32_t layer) {
+  colimoe_ctx::Cache &C = ctx->cache;
+  const int E = ctx->cfg.n_experts;
+  for (int i = 0; i < C.n_slots; ++i)
+    if (C.tag[i] >= 0 && C.tag[i] / (E + 1) == layer) {
+      C.tag[i] = -1;
+      C.used[i] = 0;
+      C.fixed[i] = 0;
+    }
+  if (!C.slot_of.empty())
+    for (int e = 0; e <= E; ++e) C.slot_of[(size_t)layer * (E + 1) + e] = -1;
+  if (ctx->host_store[layer]) {
+    (void)hipHostFree(ctx->host_store[layer]);
+    ctx->host_store[layer] = nullptr;
+  }
+}
+
 static int forward_impl(colimoe_ctx *ctx, int32_t layer, const float *x, int32_t T, const int32_t *idx, const float *w,
                  const colimoe_union *u, float *residual, int path, bool x_encoded) {
   const Dims D = dims_of(ctx, T);
   const LayerDev L = layer_of(ctx, layer);
   hipStream_t s = ctx->stream;
+  if (ctx->host_store[layer]) {
+    const int rc = ensure_resident(ctx, layer, idx, T);
+    if (rc) return rc;
+  }
   UnionDev U;
   if (u) {
     U = to_dev(u);
@@ -458,8 +554,9 @@ int colimoe_create(const colimoe_config *cfg, void *hip_stream, colimoe_ctx **ou
   c->cfg = *cfg;
   c->stream = (hipStream_t)hip_stream;
   c->device = dev;
-  c->layers.assign(cfg->n_layers, LayerDev{nullptr, nullptr, nullptr, 0});
+  c->layers.assign(cfg->n_layers, LayerDev{nullptr, nullptr, nullptr, 0, nullptr});
   c->loaded.assign(cfg->n_layers, 0);
+  c->host_store.assign(cfg->n_layers, nullptr);
   c->ws = nullptr;
   c->ws_bytes = 0;
   c->top_p = 1.0f;
@@ -479,6 +576,10 @@ int colimoe_create(const colimoe_config *cfg, void *hip_stream, colimoe_ctx **ou
 
 void colimoe_destroy(colimoe_ctx *ctx) {
   if (!ctx) return;
+  for (uint8_t *h : ctx->host_store)
+    if (h) (void)hipHostFree(h);
+  if (ctx->cache.stage) (void)hipHostFree(ctx->cache.stage);
+  if (ctx->cache.idx_host) (void)hipHostFree(ctx->cache.idx_host);
   for (int i = 0; i < 2; ++i)
     if (ctx->staging[i]) (void)hipHostFree(ctx->staging[i]);
   for (hipEvent_t e : ctx->ev_pool) (void)hipEventDestroy(e);
@@ -521,6 +622,7 @@ int colimoe_load_experts(colimoe_ctx *ctx, int32_t layer, const colimoe_layer_sr
   float *bias = (float *)(dst + align_up(rb, kAlign));
   uint8_t *experts = dst + router_bytes(c);
   ctx->loaded[layer] = 0;
+  cache_drop_layer(ctx, layer);
   if (hipMemcpyAsync(router, src->router, rb, hipMemcpyHostToDevice, s) != hipSuccess) return COLIMOE_E_HIP;
   if (src->bias) {
     if (hipMemcpyAsync(bias, src->bias, (size_t)c->n_experts * 4, hipMemcpyHostToDevice, s) != hipSuccess)
@@ -570,8 +672,132 @@ int colimoe_load_experts(colimoe_ctx *ctx, int32_t layer, const colimoe_layer_sr
   (void)hipEventDestroy(done[0]);
   (void)hipEventDestroy(done[1]);
   if (rc != COLIMOE_OK) return rc;
-  ctx->layers[layer] = LayerDev{router, bias, experts, be};
+  ctx->layers[layer] = LayerDev{router, bias, experts, be, nullptr};
   ctx->loaded[layer] = 1;
+  return COLIMOE_OK;
+}
+
+size_t colimoe_host_layer_bytes(const colimoe_config *cfg) {
+  if (!cfg_ok(cfg)) return 0;
+  return router_bytes(cfg);
+}
+
+size_t colimoe_expert_cache_bytes(const colimoe_config *cfg, int32_t n_slots) {
+  if (!cfg_ok(cfg) || n_slots < 1) return 0;
+  return align_up((size_t)cfg->n_layers * (cfg->n_experts + 1) * 4, kAlign) +
+         (size_t)n_slots * expert_layout(cfg->d, cfg->f).bytes;
+}
+
+int colimoe_set_expert_cache(colimoe_ctx *ctx, void *dev, size_t bytes) {
+  if (!ctx || !dev || !aligned(dev, kAlign)) return COLIMOE_E_ARG;
+  for (uint8_t *h : ctx->host_store)
+    if (h) return COLIMOE_E_STATE;  // the cache cannot move under host-resident layers
+  const colimoe_config *c = &ctx->cfg;
+  const size_t maps = align_up((size_t)c->n_layers * (c->n_experts + 1) * 4, kAlign);
+  const size_t be = ctx->el.bytes;
+  if (bytes < maps + be) return COLIMOE_E_WORKSPACE;
+  colimoe_ctx::Cache &C = ctx->cache;
+  if (!C.stage && hipHostMalloc((void **)&C.stage, (size_t)c->n_layers * (c->n_experts + 1) * 4,
+                                hipHostMallocDefault) != hipSuccess)
+    return COLIMOE_E_HIP;
+  if (!C.idx_host && hipHostMalloc((void **)&C.idx_host, (size_t)c->max_tokens * c->top_k * 4,
+                                   hipHostMallocDefault) != hipSuccess)
+    return COLIMOE_E_HIP;
+  C.dev_maps = (int32_t *)dev;
+  C.slots = (uint8_t *)dev + maps;
+  C.n_slots = (int)std::min<size_t>((bytes - maps) / be, (size_t)1 << 30);
+  C.slot_of.assign((size_t)c->n_layers * (c->n_experts + 1), -1);
+  C.tag.assign(C.n_slots, -1);
+  C.used.assign(C.n_slots, 0);
+  C.fixed.assign(C.n_slots, 0);
+  C.stamp = 0;
+  C.hits = C.misses = 0;
+  return COLIMOE_OK;
+}
+
+int colimoe_load_experts_host(colimoe_ctx *ctx, int32_t layer, const colimoe_layer_src *src, void *dev_dst,
+                              size_t dev_bytes) {
+  if (!ctx || !src || !dev_dst || !src->router || !src->experts) return COLIMOE_E_ARG;
+  const colimoe_config *c = &ctx->cfg;
+  if (layer < 0 || layer >= c->n_layers) return COLIMOE_E_SHAPE;
+  if ((c->n_shared == 1) != (src->shared != nullptr)) return COLIMOE_E_ARG;
+  if (!aligned(dev_dst, kAlign)) return COLIMOE_E_ARG;
+  if (dev_bytes < router_bytes(c)) return COLIMOE_E_SHAPE;
+  colimoe_ctx::Cache &C = ctx->cache;
+  if (!C.slots) return COLIMOE_E_STATE;  // colimoe_set_expert_cache first
+  const int E = c->n_experts;
+  const size_t be = ctx->el.bytes;
+  hipStream_t s = ctx->stream;
+  ctx->loaded[layer] = 0;
+  cache_drop_layer(ctx, layer);
+  // the shared expert takes a slot of its own for as long as the layer lives
+  int sslot = -1;
+  if (c->n_shared) {
+    for (int i = 0; i < C.n_slots && sslot < 0; ++i)
+      if (!C.fixed[i] && C.tag[i] < 0) sslot = i;  // an empty slot, else the least recently used
+    if (sslot < 0)
+      for (int i = 0; i < C.n_slots; ++i)
+        if (!C.fixed[i] && (sslot < 0 || C.used[i] < C.used[sslot])) sslot = i;
+    if (sslot < 0) return COLIMOE_E_WORKSPACE;
+    int free_after = 0;
+    for (int i = 0; i < C.n_slots; ++i) free_after += !C.fixed[i] && i != sslot;
+    if (free_after < c->top_k) return COLIMOE_E_WORKSPACE;  // room for one token's experts
+  }
+  float *router = (float *)dev_dst;
+  float *bias = (float *)((uint8_t *)dev_dst + align_up((size_t)E * c->d * 4, kAlign));
+  if (hipMemcpyAsync(router, src->router, (size_t)E * c->d * 4, hipMemcpyHostToDevice, s) != hipSuccess)
+    return COLIMOE_E_HIP;
+  if (src->bias) {
+    if (hipMemcpyAsync(bias, src->bias, (size_t)E * 4, hipMemcpyHostToDevice, s) != hipSuccess) return COLIMOE_E_HIP;
+  } else if (hipMemsetAsync(bias, 0, (size_t)E * 4, s) != hipSuccess) {
+    return COLIMOE_E_HIP;
+  }
+  uint8_t *store = nullptr;
+  if (hipHostMalloc((void **)&store, (size_t)E * be, hipHostMallocDefault) != hipSuccess) return COLIMOE_E_HIP;
+  std::vector<const uint8_t *> srcs(E);
+  for (int e = 0; e < E; ++e) srcs[e] = src->experts + (size_t)e * be;
+  repack_many(srcs.data(), store, E, be, c->d, c->f);
+  int32_t *map = &C.slot_of[(size_t)layer * (E + 1)];
+  if (c->n_shared) {
+    uint8_t *tmp = nullptr;
+    if (hipHostMalloc((void **)&tmp, be, hipHostMallocDefault) != hipSuccess) {
+      (void)hipHostFree(store);
+      return COLIMOE_E_HIP;
+    }
+    repack_expert(src->shared, tmp, c->d, c->f);
+    if (C.tag[sslot] >= 0) C.slot_of[(size_t)C.tag[sslot]] = -1;
+    const bool ok = hipMemcpyAsync(C.slots + (size_t)sslot * be, tmp, be, hipMemcpyHostToDevice, s) == hipSuccess &&
+                    hipStreamSynchronize(s) == hipSuccess;
+    (void)hipHostFree(tmp);
+    if (!ok) {
+      (void)hipHostFree(store);
+      return COLIMOE_E_HIP;
+    }
+    C.tag[sslot] = (int64_t)layer * (E + 1) + E;
+    C.fixed[sslot] = 1;
+    map[E] = sslot;
+  }
+  // until a call brings experts in, every entry points at a valid slot
+  int32_t *st = C.stage + (size_t)layer * (E + 1);
+  const int dummy = map[E] >= 0 ? map[E] : 0;
+  for (int e = 0; e <= E; ++e) st[e] = map[e] >= 0 ? map[e] : dummy;
+  if (hipMemcpyAsync(C.dev_maps + (size_t)layer * (E + 1), st, (size_t)(E + 1) * 4, hipMemcpyHostToDevice, s) !=
+          hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess) {
+    (void)hipHostFree(store);
+    return COLIMOE_E_HIP;
+  }
+  ctx->host_store[layer] = store;
+  ctx->layers[layer] = LayerDev{router, bias, C.slots, be, C.dev_maps + (size_t)layer * (E + 1)};
+  ctx->loaded[layer] = 1;
+  return COLIMOE_OK;
+}
+
+int colimoe_cache_stats(colimoe_ctx *ctx, int64_t *hits, int64_t *misses, int32_t *slots) {
+  if (!ctx || !hits || !misses || !slots) return COLIMOE_E_ARG;
+  *hits = ctx->cache.hits;
+  *misses = ctx->cache.misses;
+  *slots = ctx->cache.n_slots;
   return COLIMOE_OK;
 }
 
@@ -690,6 +916,7 @@ int colimoe_debug_expert(colimoe_ctx *ctx, int32_t layer, int32_t e, const float
   if ((g == nullptr) != (u == nullptr)) return COLIMOE_E_ARG;
   if (e < -1 || e >= ctx->cfg.n_experts) return COLIMOE_E_ARG;
   if (e == -1 && ctx->cfg.n_shared == 0) return COLIMOE_E_ARG;
+  if (ctx->host_store[layer]) return COLIMOE_E_STATE;  // experts of a host-resident layer are not all in HBM
   const int slot = e < 0 ? ctx->cfg.n_experts : e;
   // a one-slot union in the workspace: expert `slot`, one pair (token 0)
   Dims D = dims_of(ctx, 1);

@@ -67,7 +67,17 @@ struct LayerDev {
   const float *bias;
   const uint8_t *experts;
   size_t expert_stride;
+  // Host-resident layer (tiered placement): experts is the base of the HBM
+  // expert cache and slot_of[e] (device, E + 1 entries, the shared expert
+  // last) the slot holding expert e; null for a layer resident in HBM.
+  const int32_t *slot_of;
 };
+
+// Address of expert e (E: the shared expert) of a layer.
+__host__ __device__ inline const uint8_t *expert_base(const LayerDev &L, int e) {
+  const int s = L.slot_of ? L.slot_of[e] : e;
+  return L.experts + (size_t)s * L.expert_stride;
+}
 
 struct Dims {
   int d, f, E, k, T, n_shared;

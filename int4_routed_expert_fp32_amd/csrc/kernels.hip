@@ -549,7 +549,7 @@ __global__ __launch_bounds__(512) void k_gateup_wide(LayerDev L, Dims D, const f
     const int s = item / tiles, ti = item - s * tiles;
     int e, p0, p1;
     if (!resolve_slot(D, U, nu, s, e, p0, p1)) continue;
-    const uint8_t *base = L.experts + (size_t)e * L.expert_stride;
+    const uint8_t *base = expert_base(L, e);
     uint4 W[kTileRows], S;
     if (active) load_step(base + EL.gu_nib, base + EL.gu_sc, ti, D.d, c, W, S);
     for (int pg = p0; pg < p1; pg += MT) {
@@ -652,7 +652,7 @@ __global__ __launch_bounds__(64 * NWMAX) void k_down_wide(LayerDev L, Dims D, co
     for (int s = wave; s < slots; s += nw) {
       int e, p0, p1;
       if (!resolve_slot(D, U, nu, s, e, p0, p1)) continue;
-      const uint8_t *base = L.experts + (size_t)e * L.expert_stride;
+      const uint8_t *base = expert_base(L, e);
       for (int pg = p0; pg < p1; pg += MT) {
         const int mcount = min(MT, p1 - pg);
         float acc[MT][kTileRows];
@@ -917,7 +917,7 @@ __global__ __launch_bounds__(256 * WPT) void k_gateup_tok(LayerDev L, Dims D, Un
   const int e = slot_s[0], p0 = slot_s[1], p1 = slot_s[2], nu = slot_s[3];
   if (e < 0) return;  // block-uniform
   const ExpertLayout EL = expert_layout(D.d, D.f);
-  const uint8_t *base = L.experts + (size_t)e * L.expert_stride;
+  const uint8_t *base = expert_base(L, e);
   for (int pg = p0; pg < p1; pg += kTokChunk) {
     const int mc = min(kTokChunk, p1 - pg);
     if ((int)threadIdx.x < mc) {
@@ -1016,7 +1016,7 @@ __global__ __launch_bounds__(256 * NS) void k_gateup_one(LayerDev L, Dims D, Uni
   const int e = slot_s[0], orow = slot_s[1];
   if (e < 0) return;  // block-uniform
   const ExpertLayout EL = expert_layout(D.d, D.f);
-  const uint8_t *base = L.experts + (size_t)e * L.expert_stride;
+  const uint8_t *base = expert_base(L, e);
   float acc[kTileRows];
 #pragma unroll
   for (int r = 0; r < kTileRows; ++r) acc[r] = 0.0f;
@@ -1094,7 +1094,7 @@ __global__ __launch_bounds__(256 * NS) __attribute__((amdgpu_waves_per_eu(6))) v
   const int e = slot_s[0], p0 = slot_s[1], p1 = slot_s[2], nu = slot_s[3];
   if (e < 0) return;  // block-uniform
   const ExpertLayout EL = expert_layout(D.d, D.f);
-  const uint8_t *base = L.experts + (size_t)e * L.expert_stride;
+  const uint8_t *base = expert_base(L, e);
   uint4 W[kTileRows], S;
   if (c < C) load_step(base + EL.gu_nib, base + EL.gu_sc, ti, D.d, c, W, S);
   for (int pg = p0; pg < p1; pg += kFewT) {
@@ -1182,7 +1182,7 @@ __global__ __launch_bounds__(256 * WPT) void k_down_tok(LayerDev L, Dims D, Unio
   const int e = slot_s[0], p0 = slot_s[1], p1 = slot_s[2], nu = slot_s[3];
   if (e < 0) return;  // block-uniform
   const ExpertLayout EL = expert_layout(D.d, D.f);
-  const uint8_t *base = L.experts + (size_t)e * L.expert_stride;
+  const uint8_t *base = expert_base(L, e);
   const int tk = D.T * D.k;
   for (int pg = p0; pg < p1; pg += kTokChunk) {
     const int mc = min(kTokChunk, p1 - pg);
@@ -1419,7 +1419,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(6))) void 
   if (wave < slots) {
     int e, p0, p1;
     const bool ok = resolve_slot(D, U, nu, wave, e, p0, p1) && p1 > p0;
-    const uint8_t *base = L.experts + (size_t)(ok ? e : 0) * L.expert_stride;
+    const uint8_t *base = expert_base(L, ok ? e : 0);
     const __amdgpu_buffer_rsrc_t rn = wave_rsrc(base + EL.dn_nib, (uint32_t)(EL.dn_sc - EL.dn_nib));
     const __amdgpu_buffer_rsrc_t rs = wave_rsrc(base + EL.dn_sc, (uint32_t)(EL.bytes - EL.dn_sc));
     const int cl = lane < C ? lane : C - 1;
@@ -1535,7 +1535,7 @@ __global__ __launch_bounds__(256) void k_gateup_narrow(LayerDev L, Dims D, const
     const int s = item / tiles, ti = item - s * tiles;
     int e, p0, p1;
     if (!resolve_slot(D, U, nu, s, e, p0, p1)) continue;
-    const uint8_t *base = L.experts + (size_t)e * L.expert_stride;
+    const uint8_t *base = expert_base(L, e);
     for (int pg = p0; pg < p1; pg += MT) {
       const int mcount = min(MT, p1 - pg);
       int xrow[MT], orows[MT];
@@ -1580,7 +1580,7 @@ __global__ __launch_bounds__(256) void k_down_narrow(LayerDev L, Dims D, const f
     const int s = item / tiles, ti = item - s * tiles;
     int e, p0, p1;
     if (!resolve_slot(D, U, nu, s, e, p0, p1)) continue;
-    const uint8_t *base = L.experts + (size_t)e * L.expert_stride;
+    const uint8_t *base = expert_base(L, e);
     for (int pg = p0; pg < p1; pg += MT) {
       const int mcount = min(MT, p1 - pg);
       int orows[MT];

@@ -291,7 +291,7 @@ __global__ __launch_bounds__(256, NMT == 1 ? 3 : 2) void k_gemm_mfma(LayerDev L,
     it.tile1 = (gr0 + 32) >> 3;
     it.r = gr0 & 7;
     it.K = K;
-    const uint8_t *base_e = L.experts + (size_t)e * L.expert_stride;
+    const uint8_t *base_e = expert_base(L, e);
     it.nib = base_e + (GATEUP ? EL.gu_nib : EL.dn_nib);
     const uint16_t *scb = (const uint16_t *)(base_e + (GATEUP ? EL.gu_sc : EL.dn_sc));
     it.sc0 = scb + (size_t)it.tile0 * G * 8 + it.r;

@@ -13,8 +13,9 @@ from typing import Dict, Optional
 import numpy as np
 import torch
 
-from . import (COLIMOE_FWD_AUTO, colimoe_create, colimoe_debug_expert, colimoe_destroy, colimoe_forward,
-               colimoe_set_expert_top_p,
+from . import (COLIMOE_FWD_AUTO, colimoe_cache_stats, colimoe_create, colimoe_debug_expert, colimoe_destroy,
+               colimoe_expert_cache_bytes, colimoe_forward, colimoe_host_layer_bytes, colimoe_load_experts_host,
+               colimoe_set_expert_cache, colimoe_set_expert_top_p,
                colimoe_layer_bytes, colimoe_load_experts, colimoe_rmsnorm, colimoe_rmsnorm_route_forward, colimoe_route,
                colimoe_route_forward,
                colimoe_set_stream,
@@ -90,6 +91,9 @@ class MoeContext:
         if shared is not None:
             shared = np.ascontiguousarray(shared, dtype=np.uint8)
             assert shared.size == self.expert_bytes
+        if layer in getattr(self, "_host_layers", set()):
+            self._host_layers.discard(layer)
+            self.layers.pop(layer, None)  # a host-resident layer's buffer holds its router only
         buf = self.layers.get(layer)
         if buf is None:
             raw = torch.empty(self.layer_bytes + 256, dtype=torch.uint8, device=self.device)
@@ -99,6 +103,37 @@ class MoeContext:
             self._keep[layer] = raw
         colimoe_load_experts(self.ctx, layer, _ptr(router), _ptr(bias) if bias is not None else None, _ptr(experts),
                              _ptr(shared) if shared is not None else None, buf.data_ptr(), self.layer_bytes)
+
+    def set_expert_cache(self, n_slots: int) -> None:
+        """An HBM expert cache of n_slots experts for host-resident layers."""
+        nbytes = colimoe_expert_cache_bytes(self.cfg, n_slots)
+        raw = torch.empty(nbytes + 256, dtype=torch.uint8, device=self.device)
+        self._cache = raw
+        colimoe_set_expert_cache(self.ctx, self._aligned(raw, nbytes).data_ptr(), nbytes)
+
+    def load_layer_host(self, layer: int, router: np.ndarray, bias: Optional[np.ndarray], experts: np.ndarray,
+                        shared: Optional[np.ndarray]) -> None:
+        """Loads a layer whose routed experts stay in pinned host memory (tiered placement)."""
+        router = np.ascontiguousarray(router, dtype=np.float32)
+        experts = np.ascontiguousarray(experts, dtype=np.uint8)
+        assert router.shape == (self.E, self.d) and experts.size == self.E * self.expert_bytes
+        if bias is not None:
+            bias = np.ascontiguousarray(bias, dtype=np.float32)
+        if shared is not None:
+            shared = np.ascontiguousarray(shared, dtype=np.uint8)
+        nbytes = colimoe_host_layer_bytes(self.cfg)
+        raw = torch.empty(nbytes + 256, dtype=torch.uint8, device=self.device)
+        self._keep = getattr(self, "_keep", {})
+        self._keep[layer] = raw
+        self.layers[layer] = self._aligned(raw, nbytes)
+        self._host_layers = getattr(self, "_host_layers", set())
+        self._host_layers.add(layer)
+        colimoe_load_experts_host(self.ctx, layer, _ptr(router), _ptr(bias) if bias is not None else None,
+                                  _ptr(experts), _ptr(shared) if shared is not None else None,
+                                  self.layers[layer].data_ptr(), nbytes)
+
+    def cache_stats(self):
+        return colimoe_cache_stats(self.ctx)
 
     def new_union(self, T: int) -> UnionTensors:
         tk = T * self.k
