@@ -45,7 +45,8 @@ def parse():
                     help="arithmetic path of the headline (auto: fixed-point activations at these shapes)")
     ap.add_argument("--no-compare", action="store_true", help="skip timing the other arithmetic path")
     ap.add_argument("--no-top-p", action="store_true", help="skip the adaptive expert top-p line of the decode workload")
-    ap.add_argument("--only", choices=("all", "decode", "stack32", "union16", "verify", "prefill2048"), default="all",
+    ap.add_argument("--only", choices=("all", "decode", "stack32", "union16", "verify", "prefill2048", "tiered"),
+                    default="all",
                     help="run one workload only (the headline line needs decode)")
     return ap.parse_args()
 
@@ -305,6 +306,60 @@ def bench_verify(args, torch, np, synth, cm, MoeContext, dev, stream):
     return out
 
 
+def bench_tiered(args, torch, np, synth, cm, MoeContext, dev, stream):
+    """Tiered placement: the first 4 layers of the stacked-decode recipe kept in
+    pinned host memory, served through an HBM cache of 256 expert slots (a
+    quarter of their 1024 routed experts); one token at a time through the 4
+    layers.  Each layer call copies its routing to the host and streams the
+    missing experts over PCIe, so the time is wall-clock time."""
+    w = synth.WORKLOADS["stack32"].with_(n_layers=4)
+    slots = 256
+    ctx = MoeContext(w.d, w.f, w.E, w.k, n_layers=w.n_layers, n_shared=w.n_shared, max_tokens=1)
+    ctx.set_expert_cache(slots)
+    t0 = time.time()
+    for l in range(w.n_layers):
+        ctx.load_layer_host(l, synth.router(w, l), synth.bias(w, l), synth.expert_blobs(w, l, 0, w.E),
+                            synth.shared_blob(w, l))
+    log("tiered: loaded %d host-resident layers (%.1f s)" % (w.n_layers, time.time() - t0))
+    ntok, warm = 32, 8
+    X0 = torch.from_numpy(synth.activations(w.with_(T=ntok + warm), stream=5)).to(dev)
+    r = X0.clone()
+    x = torch.empty_like(X0)
+    idx = torch.empty((w.n_layers, w.k), dtype=torch.int32, device=dev)
+    wts = torch.empty((w.n_layers, w.k), dtype=torch.float32, device=dev)
+    U = ctx.new_union(1)
+
+    def token(i):
+        cm.colimoe_route_forward(ctx.ctx, 0, X0[i].data_ptr(), 1, idx[0].data_ptr(), wts[0].data_ptr(), U.abi(),
+                                 r[i].data_ptr(), cm.COLIMOE_FWD_AUTO)
+        for l in range(1, w.n_layers):
+            cm.colimoe_rmsnorm_route_forward(ctx.ctx, l, r[i].data_ptr(), 1, 1e-6, x[i].data_ptr(), idx[l].data_ptr(),
+                                             wts[l].data_ptr(), U.abi(), cm.COLIMOE_FWD_AUTO)
+
+    for i in range(warm):
+        token(i)
+    ctx.sync()
+    h0, m0, _ = ctx.cache_stats()
+    t = time.perf_counter()
+    for i in range(warm, warm + ntok):
+        token(i)
+    ctx.sync()
+    dt = time.perf_counter() - t
+    h1, m1, _ = ctx.cache_stats()
+    ctx.close()
+    del ctx, X0, r, x
+    torch.cuda.empty_cache()
+    hits, misses = h1 - h0, m1 - m0
+    return {"workload": "tiered placement: 4 layers of the stacked-decode recipe (d=6144 f=2048 E=256 top-8 + shared, "
+                        "Zipf(1.1) bias, RMSNorm between) with routed experts in pinned host memory (%.1f GB), an HBM "
+                        "cache of %d expert slots (%.1f GB), 1 token" % (w.n_layers * w.E * w.expert_bytes / 1e9, slots,
+                                                                         slots * w.expert_bytes / 1e9),
+            "us_per_token": round(1e6 * dt / ntok, 1), "us_per_layer": round(1e6 * dt / ntok / w.n_layers, 1),
+            "tokens_per_s": round(ntok / dt, 2), "hit_rate": round(hits / max(hits + misses, 1), 4),
+            "misses_per_token": round(misses / ntok, 2),
+            "pcie_gbs": round(misses * w.expert_bytes / dt / 1e9, 1), "tokens_timed": ntok}
+
+
 def bench_prefill(args, torch, np, synth, cm, MoeContext, dev, stream):
     w = synth.WORKLOADS["prefill2048"]
     ring = 2
@@ -367,7 +422,7 @@ def main():
 
     extra = {}
     for name, fn in (("stack32", bench_stack32), ("union16", bench_union16), ("verify", bench_verify),
-                     ("prefill2048", bench_prefill)):
+                     ("prefill2048", bench_prefill), ("tiered", bench_tiered)):
         if args.only in ("all", name):
             extra[name] = fn(*common)
             log("%s: %s" % (name, json.dumps({k: v for k, v in extra[name].items() if k != "kernels"})))

@@ -162,9 +162,10 @@ COLIMOE_API int colimoe_load_experts(colimoe_ctx *ctx, int32_t layer, const coli
                          size_t dev_bytes);
 
 /* Tiered placement for models whose experts do not all fit in HBM ([A] §2:
- * the routed experts stay on slower storage and are read on demand into a
- * cache with least-recently-used eviction; [P]: the hot experts stay close;
- * here host RAM over PCIe plays the disk and HBM the RAM).
+ * parameters are data moved between tiers by how often routing asks for them,
+ * with a per-layer LRU cache; [D] §3: the routed experts stay on disk and are
+ * read on demand into an LRU cache; here host RAM over PCIe plays the disk and
+ * HBM the RAM).
  *
  * colimoe_expert_cache_bytes: device bytes of an expert cache of n_slots
  * slots (slot maps of every layer, then the slots); 0 for a bad config or
