@@ -191,6 +191,15 @@ COLIMOE_API int colimoe_load_experts(colimoe_ctx *ctx, int32_t layer, const coli
  * Errors: E_ARG, E_SHAPE, E_STATE (no cache), E_WORKSPACE (cache too small for
  * the shared expert and one token's experts), E_HIP.
  *
+ * colimoe_cache_repin: learned pinning ([A] §2: the engine records which
+ * experts the workload routes to and pins the hottest; [D] key tuning
+ * parameters, --repin N: the hot experts are re-placed every N tokens).  The cache counts, per host-resident layer and
+ * expert, the calls that needed it; this call pins the n experts counted most
+ * often (ties to the lower layer, then the lower id) in the cache, loading
+ * the absent ones, and unpins the rest; pinned experts are never evicted.
+ * Synchronises the stream.  Errors: E_ARG, E_STATE (no cache), E_WORKSPACE
+ * (n leaves fewer free slots than one token's k experts), E_HIP.
+ *
  * colimoe_cache_stats: experts found in the cache and brought in since the
  * cache was set, and its number of slots.  Errors: E_ARG. */
 COLIMOE_API size_t colimoe_expert_cache_bytes(const colimoe_config *cfg, int32_t n_slots);
@@ -198,6 +207,7 @@ COLIMOE_API size_t colimoe_host_layer_bytes(const colimoe_config *cfg);
 COLIMOE_API int colimoe_set_expert_cache(colimoe_ctx *ctx, void *dev, size_t bytes);
 COLIMOE_API int colimoe_load_experts_host(colimoe_ctx *ctx, int32_t layer, const colimoe_layer_src *src, void *dev_dst,
                               size_t dev_bytes);
+COLIMOE_API int colimoe_cache_repin(colimoe_ctx *ctx, int32_t n);
 COLIMOE_API int colimoe_cache_stats(colimoe_ctx *ctx, int64_t *hits, int64_t *misses, int32_t *slots);
 
 /* Route T tokens (device pointers).  x [T][d] fp32 -> idx [T][k] int32,

@@ -34,6 +34,7 @@ EXPORTED = [
     "colimoe_union_build", "colimoe_forward", "colimoe_route_forward", "colimoe_rmsnorm_route_forward", "colimoe_rmsnorm", "colimoe_debug_expert", "colimoe_sync", "colimoe_status_str",
     "colimoe_timing_enable", "colimoe_timing_read", "colimoe_set_expert_top_p", "colimoe_expert_cache_bytes",
     "colimoe_host_layer_bytes", "colimoe_set_expert_cache", "colimoe_load_experts_host", "colimoe_cache_stats",
+    "colimoe_cache_repin",
 ]
 
 
@@ -98,6 +99,8 @@ def lib() -> ctypes.CDLL:
         L.colimoe_cache_stats.argtypes = [vp, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64),
                                           ctypes.POINTER(i32)]
         L.colimoe_cache_stats.restype = ctypes.c_int
+        L.colimoe_cache_repin.argtypes = [vp, i32]
+        L.colimoe_cache_repin.restype = ctypes.c_int
         L.colimoe_route.argtypes = [vp, i32, vp, i32, vp, vp, ctypes.POINTER(colimoe_union), vp]
         L.colimoe_route.restype = ctypes.c_int
         L.colimoe_union_build.argtypes = [vp, vp, i32, ctypes.POINTER(colimoe_union)]
@@ -206,6 +209,11 @@ def colimoe_host_layer_bytes(cfg: colimoe_config) -> int:
 def colimoe_set_expert_cache(ctx, dev_ptr: int, nbytes: int, check: bool = True) -> int:
     rc = lib().colimoe_set_expert_cache(ctx, dev_ptr, nbytes)
     return _check("colimoe_set_expert_cache", rc) if check else rc
+
+
+def colimoe_cache_repin(ctx, n: int, check: bool = True) -> int:
+    rc = lib().colimoe_cache_repin(ctx, n)
+    return _check("colimoe_cache_repin", rc) if check else rc
 
 
 def colimoe_cache_stats(ctx):

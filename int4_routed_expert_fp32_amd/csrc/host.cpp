@@ -37,7 +37,8 @@ struct colimoe_ctx {
     std::vector<int32_t> slot_of;  // [n_layers][E + 1]: slot or -1
     std::vector<int64_t> tag;      // per slot: layer * (E + 1) + expert, or -1
     std::vector<uint64_t> used;    // per slot: call stamp of the last use
-    std::vector<char> fixed;       // per slot: holds a shared expert (never evicted)
+    std::vector<char> fixed;       // per slot: 1 holds a shared expert, 2 a pinned expert (neither evicted)
+    std::vector<uint32_t> uses;    // [n_layers][E + 1]: calls that needed each expert
     uint64_t stamp = 0;
     int64_t hits = 0, misses = 0;
   } cache;
@@ -388,6 +389,7 @@ static int ensure_resident(colimoe_ctx *ctx, int32_t layer, const int32_t *idx, 
   if ((int)need.size() > free_slots) return COLIMOE_E_WORKSPACE;
   const uint64_t now = ++C.stamp;
   int32_t *map = &C.slot_of[(size_t)layer * (E + 1)];
+  for (int e : need) C.uses[(size_t)layer * (E + 1) + e] += 1;
   for (int e : need)
     if (map[e] >= 0) {
       C.used[map[e]] = now;
@@ -427,7 +429,10 @@ static void cache_drop_layer(colimoe_ctx *ctx, int32_t layer) {
       C.fixed[i] = 0;
     }
   if (!C.slot_of.empty())
-    for (int e = 0; e <= E; ++e) C.slot_of[(size_t)layer * (E + 1) + e] = -1;
+    for (int e = 0; e <= E; ++e) {
+      C.slot_of[(size_t)layer * (E + 1) + e] = -1;
+      C.uses[(size_t)layer * (E + 1) + e] = 0;
+    }
   if (ctx->host_store[layer]) {
     (void)hipHostFree(ctx->host_store[layer]);
     ctx->host_store[layer] = nullptr;
@@ -710,6 +715,7 @@ int colimoe_set_expert_cache(colimoe_ctx *ctx, void *dev, size_t bytes) {
   C.tag.assign(C.n_slots, -1);
   C.used.assign(C.n_slots, 0);
   C.fixed.assign(C.n_slots, 0);
+  C.uses.assign((size_t)c->n_layers * (c->n_experts + 1), 0);
   C.stamp = 0;
   C.hits = C.misses = 0;
   return COLIMOE_OK;
@@ -791,6 +797,65 @@ int colimoe_load_experts_host(colimoe_ctx *ctx, int32_t layer, const colimoe_lay
   ctx->layers[layer] = LayerDev{router, bias, C.slots, be, C.dev_maps + (size_t)layer * (E + 1)};
   ctx->loaded[layer] = 1;
   return COLIMOE_OK;
+}
+
+int colimoe_cache_repin(colimoe_ctx *ctx, int32_t n) {
+  if (!ctx || n < 0) return COLIMOE_E_ARG;
+  colimoe_ctx::Cache &C = ctx->cache;
+  if (!C.slots) return COLIMOE_E_STATE;
+  const int E = ctx->cfg.n_experts, k = ctx->cfg.top_k;
+  const size_t be = ctx->el.bytes;
+  hipStream_t s = ctx->stream;
+  int open_slots = 0;  // slots not holding a shared expert
+  for (int i = 0; i < C.n_slots; ++i) open_slots += C.fixed[i] != 1;
+  if (n > open_slots - k) return COLIMOE_E_WORKSPACE;  // one token's experts must still fit
+  // the n routed experts of host-resident layers used most often (ties: lower layer, lower id)
+  std::vector<int64_t> cand;
+  for (int l = 0; l < ctx->cfg.n_layers; ++l)
+    if (ctx->host_store[l])
+      for (int e = 0; e < E; ++e)
+        if (C.uses[(size_t)l * (E + 1) + e]) cand.push_back((int64_t)l * (E + 1) + e);
+  std::stable_sort(cand.begin(), cand.end(), [&](int64_t a, int64_t b) { return C.uses[a] > C.uses[b]; });
+  if ((int)cand.size() > n) cand.resize(n);
+  if (hipStreamSynchronize(s) != hipSuccess) return COLIMOE_E_HIP;  // no kernel still reads a slot
+  for (int i = 0; i < C.n_slots; ++i)
+    if (C.fixed[i] == 2) C.fixed[i] = 0;
+  std::vector<char> want(C.slot_of.size(), 0);
+  for (int64_t t : cand) want[t] = 1;
+  for (int64_t t : cand)  // those already present keep their slot
+    if (C.slot_of[t] >= 0) C.fixed[C.slot_of[t]] = 2;
+  std::vector<char> dirty(ctx->cfg.n_layers, 0);
+  for (int64_t t : cand) {
+    if (C.slot_of[t] >= 0) continue;
+    int victim = -1;
+    for (int i = 0; i < C.n_slots; ++i)
+      if (!C.fixed[i] && (victim < 0 || C.used[i] < C.used[victim])) victim = i;
+    if (victim < 0) return COLIMOE_E_WORKSPACE;
+    if (C.tag[victim] >= 0) {
+      C.slot_of[(size_t)C.tag[victim]] = -1;
+      dirty[C.tag[victim] / (E + 1)] = 1;
+    }
+    const int l = (int)(t / (E + 1)), e = (int)(t % (E + 1));
+    if (hipMemcpyAsync(C.slots + (size_t)victim * be, ctx->host_store[l] + (size_t)e * be, be,
+                       hipMemcpyHostToDevice, s) != hipSuccess)
+      return COLIMOE_E_HIP;
+    C.tag[victim] = t;
+    C.used[victim] = C.stamp;
+    C.fixed[victim] = 2;
+    C.slot_of[t] = victim;
+    dirty[l] = 1;
+  }
+  for (int l = 0; l < ctx->cfg.n_layers; ++l) {
+    if (!dirty[l]) continue;
+    const int32_t *map = &C.slot_of[(size_t)l * (E + 1)];
+    int32_t *st = C.stage + (size_t)l * (E + 1);
+    const int dummy = map[E] >= 0 ? map[E] : 0;
+    for (int e = 0; e <= E; ++e) st[e] = map[e] >= 0 ? map[e] : dummy;
+    if (hipMemcpyAsync(C.dev_maps + (size_t)l * (E + 1), st, (size_t)(E + 1) * 4, hipMemcpyHostToDevice, s) !=
+        hipSuccess)
+      return COLIMOE_E_HIP;
+  }
+  return hip_status(hipStreamSynchronize(s));
 }
 
 int colimoe_cache_stats(colimoe_ctx *ctx, int64_t *hits, int64_t *misses, int32_t *slots) {

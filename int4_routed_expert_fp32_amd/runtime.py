@@ -13,7 +13,7 @@ from typing import Dict, Optional
 import numpy as np
 import torch
 
-from . import (COLIMOE_FWD_AUTO, colimoe_cache_stats, colimoe_create, colimoe_debug_expert, colimoe_destroy,
+from . import (COLIMOE_FWD_AUTO, colimoe_cache_repin, colimoe_cache_stats, colimoe_create, colimoe_debug_expert, colimoe_destroy,
                colimoe_expert_cache_bytes, colimoe_forward, colimoe_host_layer_bytes, colimoe_load_experts_host,
                colimoe_set_expert_cache, colimoe_set_expert_top_p,
                colimoe_layer_bytes, colimoe_load_experts, colimoe_rmsnorm, colimoe_rmsnorm_route_forward, colimoe_route,
@@ -134,6 +134,9 @@ class MoeContext:
 
     def cache_stats(self):
         return colimoe_cache_stats(self.ctx)
+
+    def cache_repin(self, n: int) -> None:
+        colimoe_cache_repin(self.ctx, n)
 
     def new_union(self, T: int) -> UnionTensors:
         tk = T * self.k

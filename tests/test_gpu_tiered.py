@@ -117,3 +117,21 @@ def test_debug_expert_refused_on_host_layer(pair):
     rc = cm.lib().colimoe_debug_expert(host.ctx, 0, 3, x.data_ptr(), g.data_ptr(), g.data_ptr(), g.data_ptr(),
                                        y.data_ptr())
     assert rc == cm.COLIMOE_E_STATE
+
+
+def test_repin_keeps_results_and_pins(pair):
+    import int4_routed_expert_fp32_amd as cm
+    dev, host = pair
+    assert cm.colimoe_cache_repin(host.ctx, SLOTS, check=False) == cm.COLIMOE_E_WORKSPACE
+    host.cache_repin(2)  # the two experts the earlier calls needed most stay put
+    X = torch.from_numpy(synth.activations(W.with_(T=8), stream=44)).cuda()
+    h0, m0, _ = host.cache_stats()
+    for t in range(8):
+        x = X[t:t + 1].contiguous()
+        a = _call(dev, t % 2, x, FXP)
+        b = _call(host, t % 2, x, FXP)
+        for u, v in zip(a, b):
+            assert np.array_equal(u, v), t
+    h1, m1, _ = host.cache_stats()
+    print("after repin: hits %d misses %d" % (h1 - h0, m1 - m0))
+    host.cache_repin(0)
