@@ -91,6 +91,21 @@ def calibration_copy(torch, dev):
     del a, b
 
 
+def stream_ceiling(torch, dev, stream):
+    """Read-only HBM bandwidth on this machine: a sum over 4 GiB of fp32 (far
+    beyond the Infinity Cache), timed with events; the reference the decode
+    fractions are also quoted against."""
+    a = torch.ones(1 << 30, dtype=torch.float32, device=dev)
+    for _ in range(3):
+        a.sum()
+    torch.cuda.synchronize()
+    reps = 10
+    ms = event_time(torch, stream, lambda: [a.sum() for _ in range(reps)]) / reps
+    del a
+    torch.cuda.empty_cache()
+    return {"gbs": round((1 << 32) / (ms * 1e-3) / 1e9, 1), "how": "torch sum over 4 GiB fp32, read-only, 10 reps"}
+
+
 def per_kernel(cm, ctx, run, names=("route", "topk", "union", "encode", "gateup", "down", "combine", "rmsnorm")):
     cm.colimoe_timing_enable(ctx.ctx, True)
     for k in names:
@@ -441,6 +456,8 @@ def main():
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
     calibration_copy(torch, dev)
+    ceiling = stream_ceiling(torch, dev, stream)
+    log("read-only stream ceiling: %.1f GB/s" % ceiling["gbs"])
     common = (args, torch, np, synth, cm, MoeContext, dev, stream)
 
     extra = {}
@@ -491,6 +508,8 @@ def main():
         "int4_bytes_per_token": int4_bytes,
         "int4_gbs": round(gbs, 1),
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "stream_ceiling": ceiling,
+        "frac_of_stream_ceiling": round(gbs / ceiling["gbs"], 4),
         "kernels": {k: {"avg_us": round(v["avg_us"], 3), "launches": v["launches"]} for k, v in kern.items()},
         "down_gbs": round(dn_gbs, 1),
         "path": args.path,
