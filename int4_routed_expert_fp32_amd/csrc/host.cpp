@@ -67,10 +67,13 @@ namespace {
 const char *const kKernelNames[] = {"route", "topk", "union", "encode", "gateup", "down", "combine", "rmsnorm"};
 enum { K_ROUTE, K_TOPK, K_UNION, K_ENCODE, K_GATEUP, K_DOWN, K_COMBINE, K_RMSNORM, K_COUNT };
 
+// Timing events skip the system-scope fence (cache write-back and
+// invalidation) at each record: they only time, and their readout
+// synchronises the stream first.
 hipEvent_t take_event(colimoe_ctx *c) {
   if (c->ev_used == c->ev_pool.size()) {
     hipEvent_t e;
-    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
     c->ev_pool.push_back(e);
   }
   return c->ev_pool[c->ev_used++];
