@@ -41,6 +41,7 @@ def lib():
         L = ctypes.CDLL(_LIB)
         i32 = ctypes.c_int
         L.oracle_set_mutation.argtypes = [i32]
+        L.oracle_set_bits.argtypes = [i32]
         L.oracle_get_mutation.restype = i32
         L.oracle_nibble.restype = i32
         L.oracle_nibble.argtypes = [ctypes.c_uint8, i32]
@@ -77,6 +78,20 @@ def _c(a, dtype):
     return a, a.ctypes.data
 
 
+class container_bits:
+    """Context in which the oracle reads int8 (bits=8) or int4 (bits=4) expert containers."""
+
+    def __init__(self, bits: int):
+        self.bits = bits
+
+    def __enter__(self):
+        lib().oracle_set_bits(self.bits)
+        return self
+
+    def __exit__(self, *exc):
+        lib().oracle_set_bits(4)
+
+
 def set_mutation(m: int) -> None:
     lib().oracle_set_mutation(int(m))
 
@@ -95,10 +110,10 @@ def expert_bytes(d: int, f: int) -> int:
     return int(lib().oracle_expert_bytes(d, f))
 
 
-def blob_sections(blob: np.ndarray, d: int, f: int):
-    """(nibbles, scales) views of gate, up, down in a canonical blob."""
+def blob_sections(blob: np.ndarray, d: int, f: int, bits: int = 4):
+    """(weights, scales) views of gate, up, down in a canonical blob."""
     w = d * f
-    nb, ns = w // 2, (w // 64) * 2
+    nb, ns = (w if bits == 8 else w // 2), (w // 64) * 2
     out, o = [], 0
     for _ in range(3):
         out.append((blob[o:o + nb], blob[o + nb:o + nb + ns]))

@@ -40,6 +40,14 @@
 
 #define GS 64 /* elements per scale group ([P] "conservative correctness": gs64) */
 
+/* Container width: 4 (int4, the default) or 8 (int8 gs64: the pages keep the
+ * MTP head in int8 because int4 lost too much precision there, [P] lessons
+ * on record and [D] §4 highlight 2; here offered for expert weights).  Reading of the int8 container: the same blob layout
+ * with one two's-complement byte per weight, row-major, and the same fp16
+ * group scales. */
+static int g_bits = 4;
+void oracle_set_bits(int bits) { g_bits = bits == 8 ? 8 : 4; }
+
 /* Planted-mistake switch for the pin-sensitivity test (0 = the definition). */
 static int g_mutation = 0;
 void oracle_set_mutation(int m) { g_mutation = m; }
@@ -77,9 +85,15 @@ static inline uint16_t rd16(const uint8_t *p) { return (uint16_t)(p[0] | (p[1] <
  * [rows][cols] matrix (groups run along each row's input dimension). */
 double oracle_weight(const uint8_t *nib, const uint8_t *sc, int rows, int cols, int r, int c) {
   (void)rows;
-  size_t rowb = (size_t)cols / 2;
-  uint8_t b = nib[(size_t)r * rowb + (size_t)(c / 2)];
-  int q = oracle_nibble(b, c & 1);
+  int q;
+  if (g_bits == 8) {
+    const uint8_t b = nib[(size_t)r * (size_t)cols + (size_t)c];
+    q = b >= 128 ? (int)b - 256 : (int)b; /* two's complement byte */
+  } else {
+    size_t rowb = (size_t)cols / 2;
+    uint8_t b = nib[(size_t)r * rowb + (size_t)(c / 2)];
+    q = oracle_nibble(b, c & 1);
+  }
   int g = c / GS;
   if (g_mutation == 3) g = (r / GS) % (cols / GS); /* groups along the wrong axis */
   double s = oracle_half(rd16(sc + 2 * ((size_t)r * (size_t)(cols / GS) + (size_t)g)));
@@ -116,7 +130,7 @@ typedef struct {
 } blob_view;
 
 static blob_view view_blob(const uint8_t *blob, int d, int f) {
-  size_t w = (size_t)d * (size_t)f, nb = w / 2, ns = (w / GS) * 2;
+  size_t w = (size_t)d * (size_t)f, nb = g_bits == 8 ? w : w / 2, ns = (w / GS) * 2;
   blob_view v;
   v.gn = blob;
   v.gs = v.gn + nb;
@@ -129,7 +143,7 @@ static blob_view view_blob(const uint8_t *blob, int d, int f) {
 
 size_t oracle_expert_bytes(int d, int f) {
   size_t w = (size_t)d * (size_t)f;
-  return 3 * (w / 2 + (w / GS) * 2);
+  return 3 * ((g_bits == 8 ? w : w / 2) + (w / GS) * 2);
 }
 
 /* --------------------------------------------------------------- the layer */

@@ -58,6 +58,9 @@ def lib():
         L.synth_expert_bytes.argtypes = [i32, i32]
         L.synth_expert_blob.argtypes = [u64, i32, i32, i32, i32, f64, f64, vp]
         L.synth_expert_blobs.argtypes = [u64, i32, i32, i32, i32, i32, f64, f64, vp]
+        L.synth_expert_blobs_i8.argtypes = [u64, i32, i32, i32, i32, i32, f64, f64, vp]
+        L.synth_expert_bytes_i8.argtypes = [i32, i32]
+        L.synth_expert_bytes_i8.restype = ctypes.c_size_t
         L.synth_router.argtypes = [u64, i32, i32, i32, f64, vp]
         L.synth_zipf_bias.argtypes = [u64, i32, i32, f64, vp]
         L.synth_activations.argtypes = [u64, i32, i32, i32, f64, vp]
@@ -79,10 +82,11 @@ class Workload:
     zipf: float = 0.0  # Zipf exponent of the per-layer expert bias (0 = no bias)
     rho: float = 0.0   # pairwise correlation of the T activation rows
     seed: int = BASE_SEED
+    bits: int = 4      # expert container: int4 or int8 weights, gs64 fp16 scales
 
     @property
     def expert_bytes(self) -> int:
-        return expert_bytes(self.d, self.f)
+        return expert_bytes(self.d, self.f) if self.bits == 4 else int(lib().synth_expert_bytes_i8(self.d, self.f))
 
     def with_(self, **kw) -> "Workload":
         return replace(self, **kw)
@@ -114,7 +118,10 @@ def expert_blobs(w: Workload, layer: int, e0: int, e1: int, out: Optional[np.nda
     if out is None:
         out = np.empty(n, dtype=np.uint8)
     assert out.dtype == np.uint8 and out.size >= n and out.flags.c_contiguous
-    lib().synth_expert_blobs(w.seed, layer, e0, e1, w.d, w.f, SCALE_LO, SCALE_HI, out.ctypes.data)
+    if w.bits == 8:  # int8 weights are 16 times larger: scales 16 times smaller keep the same weight range
+        lib().synth_expert_blobs_i8(w.seed, layer, e0, e1, w.d, w.f, SCALE_LO / 16, SCALE_HI / 16, out.ctypes.data)
+    else:
+        lib().synth_expert_blobs(w.seed, layer, e0, e1, w.d, w.f, SCALE_LO, SCALE_HI, out.ctypes.data)
     return out[:n].reshape(e1 - e0, be) if e1 > e0 else out[:0].reshape(0, be)
 
 

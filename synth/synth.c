@@ -108,6 +108,35 @@ void synth_expert_blob(uint64_t seed, int layer, int expert, int d, int f, doubl
   }
 }
 
+/* int8 container: the same blob layout with one byte per weight, uniform
+ * over [-128, 127] (the hash bytes read as two's complement), scales
+ * U(lo, hi) rounded to fp16. */
+size_t synth_expert_bytes_i8(int d, int f) {
+  size_t w = (size_t)d * (size_t)f;
+  return 3 * (w + (w / 64) * 2);
+}
+
+void synth_expert_blob_i8(uint64_t seed, int layer, int expert, int d, int f, double sc_lo, double sc_hi,
+                          uint8_t *blob) {
+  size_t w = (size_t)d * (size_t)f, ns = w / 64;
+  uint8_t *p = blob;
+  static const int tq[3] = {T_GATE_NIB, T_UP_NIB, T_DOWN_NIB};
+  static const int tsc[3] = {T_GATE_SC, T_UP_SC, T_DOWN_SC};
+  for (int m = 0; m < 3; ++m) {
+    fill_nibbles(synth_key(seed ^ 0x1808ULL, synth_stream(layer, expert, tq[m])), p, w);
+    p += w;
+    fill_scales(synth_key(seed ^ 0x1808ULL, synth_stream(layer, expert, tsc[m])), p, ns, sc_lo, sc_hi);
+    p += ns * 2;
+  }
+}
+
+void synth_expert_blobs_i8(uint64_t seed, int layer, int e0, int e1, int d, int f, double sc_lo, double sc_hi,
+                           uint8_t *out) {
+  size_t be = synth_expert_bytes_i8(d, f);
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int e = e0; e < e1; ++e) synth_expert_blob_i8(seed, layer, e, d, f, sc_lo, sc_hi, out + (size_t)(e - e0) * be);
+}
+
 /* Experts [e0, e1) of one layer into consecutive blobs; OpenMP over experts. */
 void synth_expert_blobs(uint64_t seed, int layer, int e0, int e1, int d, int f, double sc_lo, double sc_hi,
                         uint8_t *out) {

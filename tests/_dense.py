@@ -48,6 +48,23 @@ def dense_expert(blob: np.ndarray, d: int, f: int):
     return dense_matrix(gn, gs, f, d), dense_matrix(un, us, f, d), dense_matrix(dn, ds, d, f)
 
 
+# int8 container: one two's-complement byte per weight (numpy's int8 view)
+def dense_matrix_i8(q8, sc, rows: int, cols: int) -> np.ndarray:
+    q = np.asarray(q8, dtype=np.uint8).view(np.int8).reshape(rows, cols).astype(np.float64)
+    return q * np.repeat(decode_scales(sc, rows, cols), GS, axis=1)
+
+
+def dense_expert_i8(blob: np.ndarray, d: int, f: int):
+    w = d * f
+    ns = (w // GS) * 2
+    b = np.asarray(blob, dtype=np.uint8)
+    mats, o = [], 0
+    for rows, cols in ((f, d), (f, d), (d, f)):
+        mats.append(dense_matrix_i8(b[o:o + w], b[o + w:o + w + ns], rows, cols))
+        o += w + ns
+    return mats
+
+
 def silu(z):
     from scipy.special import expit
     return z * expit(z)

@@ -494,6 +494,40 @@ def test_dropped_slots_contribute_nothing():
     assert np.array_equal(a, b)
 
 
+# ------------------------------------------------------ int8 container
+
+def pin_int8_container():
+    rng = np.random.default_rng(21)
+    rows, cols = 4, 256
+    q8 = np.arange(rows * cols, dtype=np.int64).astype(np.uint8)  # every byte value
+    sc = rng.uniform(0.0003, 0.0012, rows * cols // 64).astype(np.float16).view(np.uint8)
+    with oracle.container_bits(8):
+        W = oracle.dequant(q8, sc, rows, cols)
+        assert np.array_equal(W, _dense.dense_matrix_i8(q8, sc, rows, cols))
+        # byte 0x80 is -128 (column 128, group 2), 0x7F is 127 (group 1), 0xFF is -1 (group 3)
+        sg = sc.view(np.float16).astype(np.float64)
+        assert W[0, 128] == -128 * sg[2] and W[0, 127] == 127 * sg[1] and W[0, 255] == -1 * sg[3]
+        d, f = 256, 128
+        w8 = synth.WORKLOADS["tiny"].with_(bits=8)
+        assert oracle.expert_bytes(d, f) == w8.expert_bytes == 3 * (d * f + d * f // 32)
+        blob = synth.expert_blobs(w8, 0, 3, 4)[0]
+        x = rng.standard_normal(d).astype(np.float32).astype(np.float64)
+        Wg, Wu, Wd = _dense.dense_expert_i8(blob, d, f)
+        o = oracle.expert(blob, d, f, x)
+        h = _dense.silu(Wg @ x) * (Wu @ x)
+        assert np.allclose(o["h"], h, rtol=1e-12, atol=1e-12)
+        assert np.allclose(o["y"], Wd @ h, rtol=1e-11, atol=1e-11)
+        # a one-hot input picks a column of the gate matrix exactly
+        e = np.zeros(d)
+        e[37] = 1.0
+        assert np.array_equal(oracle.expert(blob, d, f, e)["g"], Wg[:, 37])
+    assert oracle.expert_bytes(d, f) == 3 * (d * f // 2 + d * f // 32)  # back to int4 outside
+
+
+def test_int8_container():
+    pin_int8_container()
+
+
 # -------------------------------------------------------------- page sizes
 
 def _golden_sizes():
