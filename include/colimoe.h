@@ -86,6 +86,19 @@ enum colimoe_forward_flags {
                                 Needs d >= 2048 and f >= 2048 (else E_SHAPE) */
 };
 
+/* Context options (colimoe_config.flags). */
+enum colimoe_config_flags {
+  COLIMOE_CFG_INT8 = 1, /* experts stored as int8 with one fp16 scale per 64
+                           weights ([P] lessons on record and [D] §4 highlight 2:
+                           the pages keep their MTP head in int8 because int4
+                           lost too much precision there): the canonical blob
+                           layout with one two's-complement byte per weight
+                           (colimoe_expert_bytes() = 3*d*f*(1 + 2/64)).
+                           Forward calls take T == 1 on the fp32 path (AUTO or
+                           FP32: dequantisation to fp32, fp32 accumulation);
+                           other T or paths return E_SHAPE */
+};
+
 typedef struct colimoe_config {
   int32_t d;          /* hidden size, multiple of 64 */
   int32_t f;          /* expert intermediate size, multiple of 64 */
@@ -95,7 +108,7 @@ typedef struct colimoe_config {
   int32_t n_shared;   /* always-on shared experts: 0 or 1 */
   int32_t group_size; /* must be 64 */
   int32_t max_tokens; /* largest T of any call, 1..65536 */
-  uint32_t flags;     /* reserved, must be 0 */
+  uint32_t flags;     /* colimoe_config_flags: 0, or COLIMOE_CFG_INT8 */
 } colimoe_config;
 
 /* One layer's weights in host memory, canonical format.

@@ -27,6 +27,7 @@ COLIMOE_FWD_AUTO = 0
 COLIMOE_FWD_FP32 = 1
 COLIMOE_FWD_BF16_MFMA = 2
 COLIMOE_FWD_FXP = 3
+COLIMOE_CFG_INT8 = 1
 
 EXPORTED = [
     "colimoe_create", "colimoe_destroy", "colimoe_set_stream", "colimoe_expert_bytes", "colimoe_layer_bytes",

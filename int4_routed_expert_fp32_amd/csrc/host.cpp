@@ -126,8 +126,14 @@ bool cfg_ok(const colimoe_config *c) {
   if (c->group_size != kGroup) return false;
   if (c->max_tokens < 1 || c->max_tokens > 65536) return false;
   if ((long long)c->max_tokens * c->top_k > (1LL << 24)) return false;
-  if (c->flags != 0) return false;
+  if (c->flags & ~(uint32_t)COLIMOE_CFG_INT8) return false;
   return true;
+}
+
+// Bytes of one expert in the context's container (int4 device layout, or the
+// int8 canonical layout).
+size_t cfg_expert_bytes(const colimoe_config *c) {
+  return (c->flags & COLIMOE_CFG_INT8) ? expert_bytes_i8(c->d, c->f) : expert_layout(c->d, c->f).bytes;
 }
 
 size_t router_bytes(const colimoe_config *c) {
@@ -232,6 +238,11 @@ void repack_expert(const uint8_t *src, uint8_t *dst, int d, int f) {
     }
 }
 
+// int8 container: the device layout is the canonical one.
+void copy_many(const uint8_t *const *srcs, uint8_t *dst, int n, size_t be) {
+  for (int i = 0; i < n; ++i) memcpy(dst + (size_t)i * be, srcs[i], be);
+}
+
 void repack_many(const uint8_t *const *srcs, uint8_t *dst, int n, size_t be, int d, int f) {
   unsigned hw = std::thread::hardware_concurrency();
   int nt = (int)std::min<unsigned>(hw ? hw : 4, 16);
@@ -290,7 +301,7 @@ Workspace workspace_layout(int d, int f, int E, int k, int n_shared, int max_tok
 
 }  // namespace colimoe
 
-enum { PATH_FP32 = 0, PATH_FXP = 1, PATH_MFMA = 2 };
+enum { PATH_FP32 = 0, PATH_FXP = 1, PATH_MFMA = 2, PATH_I8 = 3 };
 
 // Arithmetic path of a forward call.  AUTO: the bf16 MFMA path for
 // prefill-shaped calls (on average at least 64 tokens per expert, T*k >= 64*E),
@@ -298,6 +309,10 @@ enum { PATH_FP32 = 0, PATH_FXP = 1, PATH_MFMA = 2 };
 // least 2048), else fp32 dequantisation.
 static int select_path(colimoe_ctx *ctx, int T, uint32_t flags) {
   const Dims D = dims_of(ctx, T);
+  if (ctx->cfg.flags & COLIMOE_CFG_INT8) {  // int8 experts: one-token calls, fp32 dequantisation
+    if (T != 1 || (flags != COLIMOE_FWD_AUTO && flags != COLIMOE_FWD_FP32)) return COLIMOE_E_SHAPE;
+    return PATH_I8;
+  }
   if (flags == COLIMOE_FWD_BF16_MFMA) return PATH_MFMA;
   if (flags == COLIMOE_FWD_FP32) return PATH_FP32;
   if (flags == COLIMOE_FWD_FXP) return fxp_supported(D) ? PATH_FXP : COLIMOE_E_SHAPE;
@@ -462,7 +477,10 @@ static int forward_impl(colimoe_ctx *ctx, int32_t layer, const float *x, int32_t
   float *h = (float *)(ctx->ws + ctx->wl.h);
   float *y = (float *)(ctx->ws + ctx->wl.y);
   const bool fused = path == PATH_FP32 && down_fusable(D);
-  if (path == PATH_MFMA) {
+  if (path == PATH_I8) {
+    KTimer kt(ctx, K_GATEUP);
+    if (launch_forward_i8(L, D, x, U, h, y, s) != hipSuccess) return COLIMOE_E_HIP;
+  } else if (path == PATH_MFMA) {
     int4 *list = (int4 *)(ctx->ws + ctx->wl.mblk);
     int32_t *mcount = (int32_t *)(ctx->ws + ctx->wl.mcount);
     uint16_t *xb = (uint16_t *)(ctx->ws + ctx->wl.xb);
@@ -538,12 +556,12 @@ const char *colimoe_status_str(int s) {
 
 size_t colimoe_expert_bytes(const colimoe_config *cfg) {
   if (!cfg_ok(cfg)) return 0;
-  return expert_layout(cfg->d, cfg->f).bytes;
+  return cfg_expert_bytes(cfg);
 }
 
 size_t colimoe_layer_bytes(const colimoe_config *cfg) {
   if (!cfg_ok(cfg)) return 0;
-  return router_bytes(cfg) + (size_t)(cfg->n_experts + cfg->n_shared) * expert_layout(cfg->d, cfg->f).bytes;
+  return router_bytes(cfg) + (size_t)(cfg->n_experts + cfg->n_shared) * cfg_expert_bytes(cfg);
 }
 
 size_t colimoe_workspace_bytes(const colimoe_config *cfg) {
@@ -570,6 +588,7 @@ int colimoe_create(const colimoe_config *cfg, void *hip_stream, colimoe_ctx **ou
   c->top_p = 1.0f;
   c->wl = workspace_layout(cfg->d, cfg->f, cfg->n_experts, cfg->top_k, cfg->n_shared, cfg->max_tokens);
   c->el = expert_layout(cfg->d, cfg->f);
+  c->el.bytes = cfg_expert_bytes(cfg);  // the int8 container keeps the canonical layout
   c->staging[0] = c->staging[1] = nullptr;
   c->staging_bytes = 0;
   c->timing = false;
@@ -669,7 +688,10 @@ int colimoe_load_experts(colimoe_ctx *ctx, int32_t layer, const colimoe_layer_sr
       const int e = e0 + i;
       srcs[i] = e < c->n_experts ? src->experts + (size_t)e * be : src->shared;
     }
-    repack_many(srcs.data(), ctx->staging[b], n, be, c->d, c->f);
+    if (c->flags & COLIMOE_CFG_INT8)
+      copy_many(srcs.data(), ctx->staging[b], n, be);
+    else
+      repack_many(srcs.data(), ctx->staging[b], n, be, c->d, c->f);
     if (hipMemcpyAsync(experts + (size_t)e0 * be, ctx->staging[b], (size_t)n * be, hipMemcpyHostToDevice, s) !=
             hipSuccess ||
         hipEventRecord(done[b], s) != hipSuccess)
@@ -693,7 +715,7 @@ size_t colimoe_host_layer_bytes(const colimoe_config *cfg) {
 size_t colimoe_expert_cache_bytes(const colimoe_config *cfg, int32_t n_slots) {
   if (!cfg_ok(cfg) || n_slots < 1) return 0;
   return align_up((size_t)cfg->n_layers * (cfg->n_experts + 1) * 4, kAlign) +
-         (size_t)n_slots * expert_layout(cfg->d, cfg->f).bytes;
+         (size_t)n_slots * cfg_expert_bytes(cfg);
 }
 
 int colimoe_set_expert_cache(colimoe_ctx *ctx, void *dev, size_t bytes) {
@@ -765,7 +787,10 @@ int colimoe_load_experts_host(colimoe_ctx *ctx, int32_t layer, const colimoe_lay
   if (hipHostMalloc((void **)&store, (size_t)E * be, hipHostMallocDefault) != hipSuccess) return COLIMOE_E_HIP;
   std::vector<const uint8_t *> srcs(E);
   for (int e = 0; e < E; ++e) srcs[e] = src->experts + (size_t)e * be;
-  repack_many(srcs.data(), store, E, be, c->d, c->f);
+  if (c->flags & COLIMOE_CFG_INT8)
+    copy_many(srcs.data(), store, E, be);
+  else
+    repack_many(srcs.data(), store, E, be, c->d, c->f);
   int32_t *map = &C.slot_of[(size_t)layer * (E + 1)];
   if (c->n_shared) {
     uint8_t *tmp = nullptr;
@@ -773,7 +798,10 @@ int colimoe_load_experts_host(colimoe_ctx *ctx, int32_t layer, const colimoe_lay
       (void)hipHostFree(store);
       return COLIMOE_E_HIP;
     }
-    repack_expert(src->shared, tmp, c->d, c->f);
+    if (c->flags & COLIMOE_CFG_INT8)
+      memcpy(tmp, src->shared, be);
+    else
+      repack_expert(src->shared, tmp, c->d, c->f);
     if (C.tag[sslot] >= 0) C.slot_of[(size_t)C.tag[sslot]] = -1;
     const bool ok = hipMemcpyAsync(C.slots + (size_t)sslot * be, tmp, be, hipMemcpyHostToDevice, s) == hipSuccess &&
                     hipStreamSynchronize(s) == hipSuccess;
@@ -985,6 +1013,7 @@ int colimoe_debug_expert(colimoe_ctx *ctx, int32_t layer, int32_t e, const float
   if (e < -1 || e >= ctx->cfg.n_experts) return COLIMOE_E_ARG;
   if (e == -1 && ctx->cfg.n_shared == 0) return COLIMOE_E_ARG;
   if (ctx->host_store[layer]) return COLIMOE_E_STATE;  // experts of a host-resident layer are not all in HBM
+  if (ctx->cfg.flags & COLIMOE_CFG_INT8) return COLIMOE_E_SHAPE;  // the stage-by-stage path reads int4
   const int slot = e < 0 ? ctx->cfg.n_experts : e;
   // a one-slot union in the workspace: expert `slot`, one pair (token 0)
   Dims D = dims_of(ctx, 1);

@@ -168,5 +168,15 @@ hipError_t launch_gateup_mfma(const LayerDev &L, const Dims &D, const uint16_t *
 hipError_t launch_down_mfma(const LayerDev &L, const Dims &D, const uint16_t *hb, const int4 *list,
                             const int32_t *count, int max_entries, float *y, hipStream_t s);
 hipError_t launch_rmsnorm(const float *r, int T, int d, float eps, float *x, hipStream_t s);
+// int8 container, one token (fp32 dequantisation): h [rows][f] and y
+// [rows][d] fp32 in the rows of the fixed-point path; the combine follows in
+// launch_combine.
+hipError_t launch_forward_i8(const LayerDev &L, const Dims &D, const float *x, const UnionDev &U, float *h, float *y,
+                             hipStream_t s);
+// Bytes of one expert in the int8 container (the canonical layout).
+inline size_t expert_bytes_i8(int d, int f) {
+  const size_t w = (size_t)d * (size_t)f;
+  return 3 * (w + w / kGroup * 2);
+}
 
 }  // namespace colimoe

@@ -1457,6 +1457,97 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(6))) void 
 }
 
 
+// ------------------------------------------------------- int8 container
+// Experts stored as int8 gs64 (one two's-complement byte per weight, the
+// canonical blob layout [gate q][gate s][up q][up s][down q][down s], rows
+// row-major) for one-token calls: the pages keep the MTP head in int8
+// because int4 lost too much precision there ([P] lessons on record; [D] §4
+// highlight 2).  One wave per output row; a lane takes 16-column chunks
+// (one 16-byte load) lane, lane + 64, ...; each byte is flipped to offset
+// binary n = q + 128 (XOR 0x80) and converted, and -128 * (sum of the
+// chunk's activations) starts the chunk's sum, so sum n x - 128 sum x =
+// sum q x; times the group scale, accumulated in fp32; the wave's partials
+// are summed by the fixed tree of wave_sum.
+
+// Sum over 16 columns of (n_i - 128) x_i for the 16 bytes of w and x[0..15].
+__device__ __forceinline__ float chunk_dot_i8(const uint4 &w, const float4 (&xv)[4]) {
+  const uint32_t ws[4] = {w.x ^ 0x80808080u, w.y ^ 0x80808080u, w.z ^ 0x80808080u, w.w ^ 0x80808080u};
+  float sx = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) sx = sx + ((xv[i].x + xv[i].y) + (xv[i].z + xv[i].w));
+  float acc = -128.0f * sx;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    acc = __builtin_fmaf((float)(ws[i] & 0xFFu), xv[i].x, acc);
+    acc = __builtin_fmaf((float)((ws[i] >> 8) & 0xFFu), xv[i].y, acc);
+    acc = __builtin_fmaf((float)((ws[i] >> 16) & 0xFFu), xv[i].z, acc);
+    acc = __builtin_fmaf((float)(ws[i] >> 24), xv[i].w, acc);
+  }
+  return acc;
+}
+
+__device__ __forceinline__ float half_at(const uint8_t *p, size_t i) {
+  return (float)__builtin_bit_cast(_Float16, *(const uint16_t *)(p + 2 * i));
+}
+
+// Slot s of a one-token call: expert, output row and activation row; false
+// for a slot that holds nothing.
+__device__ __forceinline__ bool slot_i8(const Dims &D, const UnionDev &U, int s, int &e, int &orow) {
+  const int nu = clamp_nu(U.n_unique, D);
+  if (s > nu || (s == nu && !D.n_shared)) return false;
+  int p0, p1;
+  if (!resolve_slot(D, U, nu, s, e, p0, p1) || p1 <= p0) return false;
+  orow = s < nu ? p0 : D.T * D.k;
+  return true;
+}
+
+// h[orow][j] = SiLU(gate_j . x) * (up_j . x); grid (f/4, slots), 4 waves a block.
+__global__ __launch_bounds__(256) void k_gateup_i8(LayerDev L, Dims D, const float *__restrict__ x, UnionDev U,
+                                                   float *__restrict__ h) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int j = blockIdx.x * 4 + wave;
+  int e, orow;
+  if (j >= D.f || !slot_i8(D, U, blockIdx.y, e, orow)) return;
+  const size_t w = (size_t)D.d * D.f, ns = w / kGroup * 2;
+  const uint8_t *base = expert_base(L, e);
+  const uint8_t *gq = base + (size_t)j * D.d, *uq = base + w + ns + (size_t)j * D.d;
+  const uint8_t *gs = base + w + (size_t)j * (D.d / kGroup) * 2, *us = base + 2 * w + ns + (size_t)j * (D.d / kGroup) * 2;
+  float ag = 0.0f, au = 0.0f;
+  for (int c = lane; c < D.d / 16; c += 64) {
+    const uint4 wg = *(const uint4 *)(gq + 16 * (size_t)c), wu = *(const uint4 *)(uq + 16 * (size_t)c);
+    float4 xv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xv[i] = *(const float4 *)(x + 16 * (size_t)c + 4 * i);
+    ag = __builtin_fmaf(half_at(gs, c >> 2), chunk_dot_i8(wg, xv), ag);
+    au = __builtin_fmaf(half_at(us, c >> 2), chunk_dot_i8(wu, xv), au);
+  }
+  const float g = wave_sum(ag), u = wave_sum(au);
+  if (lane == 0) h[(size_t)orow * D.f + j] = silu_f(g) * u;
+}
+
+// y[orow][r] = down_r . h[orow]; grid (d/4, slots), 4 waves a block.
+__global__ __launch_bounds__(256) void k_down_i8(LayerDev L, Dims D, const float *__restrict__ h, UnionDev U,
+                                                 float *__restrict__ y) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + wave;
+  int e, orow;
+  if (r >= D.d || !slot_i8(D, U, blockIdx.y, e, orow)) return;
+  const size_t w = (size_t)D.d * D.f, ns = w / kGroup * 2;
+  const uint8_t *base = expert_base(L, e) + 2 * (w + ns);
+  const uint8_t *dq = base + (size_t)r * D.f, *ds = base + w + (size_t)r * (D.f / kGroup) * 2;
+  const float *hr = h + (size_t)orow * D.f;
+  float acc = 0.0f;
+  for (int c = lane; c < D.f / 16; c += 64) {
+    const uint4 wd = *(const uint4 *)(dq + 16 * (size_t)c);
+    float4 hv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hv[i] = *(const float4 *)(hr + 16 * (size_t)c + 4 * i);
+    acc = __builtin_fmaf(half_at(ds, c >> 2), chunk_dot_i8(wd, hv), acc);
+  }
+  const float v = wave_sum(acc);
+  if (lane == 0) y[(size_t)orow * D.d + r] = v;
+}
+
 // ------------------------------------------------- narrow shapes (K < 2048)
 // Rows shorter than 64 chunks: LPR lanes per row (a power of two >= K/32),
 // 64/LPR rows side by side in a wave, one wave per (slot, 8-row tile).  Same
@@ -2068,6 +2159,15 @@ hipError_t launch_combine(const Dims &D, const float *w, const UnionDev &U, cons
 hipError_t launch_rmsnorm(const float *r, int T, int d, float eps, float *x, hipStream_t s) {
   if (T <= 0) return hipSuccess;
   k_rmsnorm<<<T, 512, 0, s>>>(r, d, eps, x);
+  return hipGetLastError();
+}
+
+hipError_t launch_forward_i8(const LayerDev &L, const Dims &D, const float *x, const UnionDev &U, float *h, float *y,
+                             hipStream_t s) {
+  if (D.T != 1) return hipErrorInvalidValue;
+  const int slots = D.k + D.n_shared;
+  k_gateup_i8<<<dim3((D.f + 3) / 4, slots), 256, 0, s>>>(L, D, x, U, h);
+  k_down_i8<<<dim3((D.d + 3) / 4, slots), 256, 0, s>>>(L, D, h, U, y);
   return hipGetLastError();
 }
 

@@ -52,8 +52,9 @@ class MoeContext:
     """One library context with its own workspace and up to n_layers loaded layers."""
 
     def __init__(self, d: int, f: int, n_experts: int, top_k: int, n_layers: int = 1, n_shared: int = 0,
-                 max_tokens: int = 1, device: str = "cuda", stream: Optional[torch.cuda.Stream] = None):
-        self.cfg = make_config(d, f, n_experts, top_k, n_layers, n_shared, max_tokens)
+                 max_tokens: int = 1, device: str = "cuda", stream: Optional[torch.cuda.Stream] = None,
+                 cfg_flags: int = 0):
+        self.cfg = make_config(d, f, n_experts, top_k, n_layers, n_shared, max_tokens, flags=cfg_flags)
         self.d, self.f, self.E, self.k = d, f, n_experts, top_k
         self.n_layers, self.n_shared, self.max_tokens = n_layers, n_shared, max_tokens
         self.device = torch.device(device)

@@ -31,6 +31,8 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_sizes_match_the_container():
+    cfg8 = cm.make_config(6144, 2048, 256, 8, 1, 1, 1, flags=cm.COLIMOE_CFG_INT8)
+    assert cm.colimoe_expert_bytes(cfg8) == 3 * 6144 * 2048 * 33 // 32  # int8 weights + fp16 scales per 64
     cfg = cm.make_config(6144, 2048, 256, 8, 1, 1, 1)
     assert cm.colimoe_expert_bytes(cfg) == 20_054_016
     lb = cm.colimoe_layer_bytes(cfg)
@@ -40,7 +42,7 @@ def test_sizes_match_the_container():
 
 @pytest.mark.parametrize("bad", [
     dict(d=100), dict(f=96), dict(n_experts=0), dict(n_experts=2000), dict(top_k=0), dict(top_k=17),
-    dict(top_k=20, n_experts=16), dict(n_shared=2), dict(group_size=32), dict(max_tokens=0), dict(flags=1),
+    dict(top_k=20, n_experts=16), dict(n_shared=2), dict(group_size=32), dict(max_tokens=0), dict(flags=2),
     dict(n_layers=0), dict(d=32768),
 ])
 def test_invalid_configs_rejected_before_any_gpu_call(bad):

@@ -1,0 +1,77 @@
+"""int8 gs64 expert container (COLIMOE_CFG_INT8): one-token calls against the
+oracle reading the same int8 blobs.  Bound per output: the fp32 path's
+|gpu - oracle| <= 1e-3 (1 + |oracle|); routing, gate weights and union lists
+as on the int4 path.  Calls the int8 container does not serve are refused.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests import _parity as P
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TINY8 = synth.WORKLOADS["tiny"].with_(name="tiny8", bits=8, T=4)
+DEC8 = synth.Workload(name="dec8", d=6144, f=2048, E=32, k=8, T=3, n_shared=1, zipf=1.1, bits=8,
+                      seed=synth.BASE_SEED + 401)
+RAGGED8 = synth.Workload(name="ragged8", d=320, f=192, E=37, k=3, T=3, n_shared=1, bits=8,
+                         seed=synth.BASE_SEED + 402)
+
+
+def _ctx(w, max_tokens=2):
+    import int4_routed_expert_fp32_amd as cm
+    from int4_routed_expert_fp32_amd.runtime import MoeContext
+    print("context", w.name, w.d, w.f, w.E, w.k, "int8", flush=True)
+    return MoeContext(w.d, w.f, w.E, w.k, n_layers=1, n_shared=w.n_shared, max_tokens=max_tokens,
+                      cfg_flags=cm.COLIMOE_CFG_INT8)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _builds():
+    oracle.build(force=False)
+    synth.build(force=False)
+
+
+@pytest.mark.parametrize("w", [TINY8, RAGGED8, DEC8], ids=lambda w: w.name)
+def test_int8_layer_parity(w):
+    ctx = _ctx(w)
+    P.load_layer(ctx, w, 0)
+    ora = P.OracleLayer(w, 0)
+    X = synth.activations(w, stream=51)
+    worst = 0.0
+    with oracle.container_bits(8):
+        for t in range(w.T):
+            x1 = X[t:t + 1]
+            a = P.layer_parity(ctx, w, 0, x1, ora, one_call=True)
+            b = P.layer_parity(ctx, w, 0, x1, ora)
+            assert np.array_equal(a["out"].view(np.uint32), b["out"].view(np.uint32))
+            worst = max(worst, a["ratio"])
+    print("%s: worst ratio %.3g" % (w.name, worst))
+    ctx.close()
+
+
+def test_int8_refusals():
+    import int4_routed_expert_fp32_amd as cm
+    w = TINY8
+    ctx = _ctx(w)
+    P.load_layer(ctx, w, 0)
+    x = torch.from_numpy(synth.activations(w.with_(T=2), stream=52)).cuda()
+    idx = torch.zeros((2, w.k), dtype=torch.int32, device="cuda")
+    idx[:, 1] = 1
+    wt = torch.full((2, w.k), 0.5, dtype=torch.float32, device="cuda")
+    res = x.clone()
+    # more than one token, or a path other than the fp32 one
+    assert cm.colimoe_forward(ctx.ctx, 0, x.data_ptr(), 2, idx.data_ptr(), wt.data_ptr(), None, res.data_ptr(), 0,
+                              check=False) == cm.COLIMOE_E_SHAPE
+    for flags in (cm.COLIMOE_FWD_FXP, cm.COLIMOE_FWD_BF16_MFMA):
+        assert cm.colimoe_forward(ctx.ctx, 0, x.data_ptr(), 1, idx.data_ptr(), wt.data_ptr(), None, res.data_ptr(),
+                                  flags, check=False) == cm.COLIMOE_E_SHAPE
+    g = torch.empty(w.f, dtype=torch.float32, device="cuda")
+    y = torch.empty(w.d, dtype=torch.float32, device="cuda")
+    assert cm.lib().colimoe_debug_expert(ctx.ctx, 0, 1, x.data_ptr(), g.data_ptr(), g.data_ptr(), g.data_ptr(),
+                                         y.data_ptr()) == cm.COLIMOE_E_SHAPE
+    ctx.sync()
+    assert torch.equal(res, x)  # refused calls have no effect
+    ctx.close()
