@@ -45,7 +45,8 @@ def parse():
                     help="arithmetic path of the headline (auto: fixed-point activations at these shapes)")
     ap.add_argument("--no-compare", action="store_true", help="skip timing the other arithmetic path")
     ap.add_argument("--no-top-p", action="store_true", help="skip the adaptive expert top-p line of the decode workload")
-    ap.add_argument("--only", choices=("all", "decode", "stack32", "union16", "verify", "prefill2048", "tiered"),
+    ap.add_argument("--only", choices=("all", "decode", "stack32", "union16", "verify", "prefill2048", "tiered",
+                                       "int8"),
                     default="all",
                     help="run one workload only (the headline line needs decode)")
     return ap.parse_args()
@@ -400,6 +401,43 @@ def bench_tiered(args, torch, np, synth, cm, MoeContext, dev, stream):
             "after_repin": pinned}
 
 
+def bench_int8(args, torch, np, synth, cm, MoeContext, dev, stream):
+    """The decode layer with int8 gs64 experts (twice the int4 bytes), 1 token,
+    on a ring of 4 independently generated layers (each token reads 356 MB,
+    beyond the Infinity Cache)."""
+    w = synth.WORKLOADS["decode"].with_(bits=8)
+    ring = 4
+    ctx = MoeContext(w.d, w.f, w.E, w.k, n_layers=ring, n_shared=w.n_shared, max_tokens=1,
+                     cfg_flags=cm.COLIMOE_CFG_INT8)
+    load_ring(ctx, synth, w, ring, "int8")
+    nt, warm = 100, 10
+    X = torch.from_numpy(synth.activations(w.with_(T=nt + warm), stream=12)).to(dev)
+    res = X.clone()
+    idx = torch.empty((nt + warm, w.k), dtype=torch.int32, device=dev)
+    wts = torch.empty((nt + warm, w.k), dtype=torch.float32, device=dev)
+    U = ctx.new_union(1)
+
+    def step(i):
+        cm.colimoe_route_forward(ctx.ctx, i % ring, X[i].data_ptr(), 1, idx[i].data_ptr(), wts[i].data_ptr(), U.abi(),
+                                 res[i].data_ptr(), cm.COLIMOE_FWD_AUTO)
+
+    for i in range(warm):
+        step(i)
+    ctx.sync()
+    ms = event_time(torch, stream, lambda: [step(i) for i in range(warm, warm + nt)]) / nt
+    ctx.sync()
+    kern = per_kernel(cm, ctx, lambda: [step(i) for i in range(warm, warm + nt)])
+    ctx.close()
+    del ctx, X, res
+    torch.cuda.empty_cache()
+    bytes_tok = (w.k + w.n_shared) * w.expert_bytes
+    gbs = bytes_tok / (ms * 1e-3) / 1e9
+    return {"workload": "decode MoE layer with int8 gs64 experts, d=6144 f=2048 E=256 top-8 + shared, 1 token, ring "
+                        "of %d layers" % ring, "us_per_token": round(1000 * ms, 2),
+            "int8_bytes_per_token": bytes_tok, "int8_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "tokens_timed": nt, "kernels": {k: round(v["avg_us"], 3) for k, v in kern.items()}}
+
+
 def bench_prefill(args, torch, np, synth, cm, MoeContext, dev, stream):
     w = synth.WORKLOADS["prefill2048"]
     ring = 2
@@ -464,7 +502,7 @@ def main():
 
     extra = {}
     for name, fn in (("stack32", bench_stack32), ("union16", bench_union16), ("verify", bench_verify),
-                     ("prefill2048", bench_prefill), ("tiered", bench_tiered)):
+                     ("prefill2048", bench_prefill), ("tiered", bench_tiered), ("int8", bench_int8)):
         if args.only in ("all", name):
             extra[name] = fn(*common)
             log("%s: %s" % (name, json.dumps({k: v for k, v in extra[name].items() if k != "kernels"})))
