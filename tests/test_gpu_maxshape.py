@@ -144,3 +144,33 @@ def test_max_shape_rmsnorm_in_router(maxrun):
     assert np.array_equal(ra.cpu().numpy().view(np.uint32), rb.cpu().numpy().view(np.uint32))
     xo = oracle.rmsnorm(r0[0].astype(np.float64), EPS)
     P.assert_close(xb.cpu().numpy()[0], xo, what="RMSNorm at d = 16384")
+
+
+# The expert-count limit (1024 experts, top-16, Zipf bias): sixteen keys per
+# lane in the top-k, for one token (router + top-k + union in two launches),
+# up to 16 tokens (top-k and union in one launch) and beyond (matrix-core
+# router, separate top-k and union kernels).
+MAXE = synth.Workload(name="e1024", d=256, f=128, E=1024, k=16, T=40, n_shared=1, zipf=1.1, rho=0.3,
+                      seed=synth.BASE_SEED + 108)
+
+
+def test_max_experts_top16():
+    from int4_routed_expert_fp32_amd.runtime import MoeContext
+    oracle.build(force=False)
+    synth.build(force=False)
+    w = MAXE
+    print("context", w.name, w.d, w.f, w.E, w.k, w.T, flush=True)
+    ctx = MoeContext(w.d, w.f, w.E, w.k, n_layers=1, n_shared=w.n_shared, max_tokens=w.T)
+    P.load_layer(ctx, w, 0)
+    ora = P.OracleLayer(w, 0)
+    X = synth.activations(w, stream=0)
+    worst = 0.0
+    for T in (w.T, 16, 5, 1):
+        r = P.layer_parity(ctx, w, 0, X[:T], ora)
+        worst = max(worst, r["ratio"])
+        if T == 1:
+            r1 = P.layer_parity(ctx, w, 0, X[:1], ora, one_call=True)
+            assert np.array_equal(r1["out"].view(np.uint32), r["out"].view(np.uint32))
+        print("e1024 T=%d: %d unique experts, near-tie tokens %s" % (T, r["union"]["n_unique"], r["differ"]))
+    ctx.close()
+    print("e1024: worst |gpu-oracle|/bound %.3g" % worst)
