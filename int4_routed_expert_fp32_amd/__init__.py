@@ -69,8 +69,8 @@ def lib() -> ctypes.CDLL:
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
-            raise ImportError("libcolimoe.so not built: run __graft_entry__.build() (or python "
-                              "int4_routed_expert_fp32_amd/_build.py); there is no CPU fallback")
+            raise ImportError("libcolimoe.so not built: run python -m int4_routed_expert_fp32_amd._build; "
+                              "there is no CPU fallback")
         L = ctypes.CDLL(LIB_PATH)
         vp, i32, u32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_size_t
         cfgp = ctypes.POINTER(colimoe_config)
