@@ -1334,10 +1334,15 @@ __global__ __launch_bounds__(256) void k_router_split(LayerDev L, Dims D, const 
       const int groups = D.T * (D.d / 16);
       for (int g = blockIdx.x * 256 + threadIdx.x; g < groups; g += gridDim.x * 256) xquant_group(x, D.d, g, xq, xs);
     }
-    // one token alone, or tokens four at a time so their loads and reductions
-    // overlap; per token the operations and their order are the same
+    // one token alone, two or three together, or tokens four at a time so
+    // their loads and reductions overlap; per token the operations and their
+    // order are the same
     if (D.T == 1)
       router_tokens<1>(r, x, D, wave, lane, q4, part);
+    else if (D.T == 2)
+      router_tokens<2>(r, x, D, wave, lane, q4, part);
+    else if (D.T == 3)
+      router_tokens<3>(r, x, D, wave, lane, q4, part);
     else
       router_tokens<4>(r, x, D, wave, lane, q4, part);
   }
@@ -1854,7 +1859,7 @@ hipError_t launch_topk(const float *logits, const Dims &D, int32_t *idx, float *
 // Union lists of a call with at most 64 (token, slot) pairs, one wave: lane p
 // holds pair p and ranks it by (expert, token) among all pairs with a plain
 // count; the lists (and the handling of an invalid routing) are those of
-// union_wave.
+// union_wave.  idx may point to LDS (the top-k's copy of the routing).
 __device__ void union_small(const int32_t *__restrict__ idx, const Dims &D, const UnionDev &U,
                             int32_t *__restrict__ err) {
   const int P = D.T * D.k, lane = threadIdx.x & 63;
@@ -1862,7 +1867,12 @@ __device__ void union_small(const int32_t *__restrict__ idx, const Dims &D, cons
   const int e = act ? idx[lane] : 0;
   const int t = act ? lane / D.k : 0, j = act ? lane - t * D.k : 0;
   bool ok = !act || (e >= 0 && e < D.E);
-  for (int q = 0; q < j; ++q) ok = ok && idx[t * D.k + q] != e;
+  // distinct within the token: compare with the ids of slots 0..j-1 of the
+  // same token, taken from the lanes that hold them
+  for (int q = 0; q + 1 < D.k; ++q) {
+    const int eq = __shfl(e, t * D.k + q, 64);
+    if (q < j && eq == e) ok = false;
+  }
   if (__ballot(!ok)) {
     if (lane == 0) {
       *U.n_unique = 0;
@@ -1906,12 +1916,14 @@ __global__ __launch_bounds__(1024) void k_topk_union(const float *__restrict__ l
                                                      int32_t *__restrict__ idx, float *__restrict__ wout, UnionDev U,
                                                      int32_t *__restrict__ err) {
   extern __shared__ unsigned long long masks[];
+  __shared__ int32_t sids[64];  // the routing when T*k <= 64, for the one-wave union
   const int t = threadIdx.x >> 6;
-  if (t < D.T) topk_token<PER>(logits + (size_t)t * D.E, D, t, idx, wout, nullptr);
+  const bool small = D.T * D.k <= 64;
+  if (t < D.T) topk_token<PER>(logits + (size_t)t * D.E, D, t, idx, wout, small ? sids : nullptr);
   __syncthreads();
   if (threadIdx.x < 64) {
-    if (D.T * D.k <= 64)
-      union_small(idx, D, U, err);
+    if (small)
+      union_small(sids, D, U, err);
     else
       union_wave(idx, D, U, err, masks);
   }
