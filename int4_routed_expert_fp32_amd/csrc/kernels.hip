@@ -250,6 +250,7 @@ __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ logits, 
 // in token order.  One wave; ranks come from per-expert lane masks in LDS, so
 // the result is independent of timing.  Invalid routings (expert out of
 // range, or an expert twice in one token) produce an empty union and set *err.
+// idx may point to LDS (the top-k's copy of the routing, up to 16 tokens).
 // LDS: masks[E] u64 (8-byte aligned), counts[E], running[E], one flag.
 
 __host__ __device__ inline size_t union_lds_bytes(int E) { return (size_t)E * 8 + (size_t)(2 * E + 1) * 4; }
@@ -1916,16 +1917,15 @@ __global__ __launch_bounds__(1024) void k_topk_union(const float *__restrict__ l
                                                      int32_t *__restrict__ idx, float *__restrict__ wout, UnionDev U,
                                                      int32_t *__restrict__ err) {
   extern __shared__ unsigned long long masks[];
-  __shared__ int32_t sids[64];  // the routing when T*k <= 64, for the one-wave union
+  __shared__ int32_t sids[kRouteSplitMaxT * 16];  // the call's routing (T <= 16, k <= 16) for the union
   const int t = threadIdx.x >> 6;
-  const bool small = D.T * D.k <= 64;
-  if (t < D.T) topk_token<PER>(logits + (size_t)t * D.E, D, t, idx, wout, small ? sids : nullptr);
+  if (t < D.T) topk_token<PER>(logits + (size_t)t * D.E, D, t, idx, wout, sids);
   __syncthreads();
   if (threadIdx.x < 64) {
-    if (small)
+    if (D.T * D.k <= 64)
       union_small(sids, D, U, err);
     else
-      union_wave(idx, D, U, err, masks);
+      union_wave(sids, D, U, err, masks);
   }
 }
 
