@@ -1335,17 +1335,19 @@ __global__ __launch_bounds__(256) void k_router_split(LayerDev L, Dims D, const 
       const int groups = D.T * (D.d / 16);
       for (int g = blockIdx.x * 256 + threadIdx.x; g < groups; g += gridDim.x * 256) xquant_group(x, D.d, g, xq, xs);
     }
-    // one token alone, two or three together, or tokens four at a time so
-    // their loads and reductions overlap; per token the operations and their
-    // order are the same
+    // one token alone, two or three together, or tokens four or eight at a
+    // time so their loads and reductions overlap; per token the operations
+    // and their order are the same
     if (D.T == 1)
       router_tokens<1>(r, x, D, wave, lane, q4, part);
     else if (D.T == 2)
       router_tokens<2>(r, x, D, wave, lane, q4, part);
     else if (D.T == 3)
       router_tokens<3>(r, x, D, wave, lane, q4, part);
-    else
+    else if (D.T < 8)
       router_tokens<4>(r, x, D, wave, lane, q4, part);
+    else
+      router_tokens<8>(r, x, D, wave, lane, q4, part);
   }
   __syncthreads();
   if (threadIdx.x < D.T)
