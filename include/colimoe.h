@@ -35,7 +35,9 @@
  *   - Ownership: the caller owns every device buffer (layer weights,
  *     workspace, inputs, outputs).  The library owns only its host context.
  *   - route/forward/rmsnorm enqueue on the context's HIP stream, allocate
- *     nothing and do not synchronise the host.
+ *     nothing and do not synchronise the host; the one exception is a
+ *     forward on a layer loaded with colimoe_load_experts_host, which reads
+ *     the call's routing on the host to fill the HBM expert cache.
  *   - A context is not thread-safe: use one per stream.
  *   - Device pointers must be 16-byte aligned, layer buffers 256-byte aligned.
  *   - A call with T == 0 does nothing and may pass NULL data pointers.
