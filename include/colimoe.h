@@ -225,9 +225,15 @@ COLIMOE_API int colimoe_load_experts_host(colimoe_ctx *ctx, int32_t layer, const
 COLIMOE_API int colimoe_cache_repin(colimoe_ctx *ctx, int32_t n);
 COLIMOE_API int colimoe_cache_stats(colimoe_ctx *ctx, int64_t *hits, int64_t *misses, int32_t *slots);
 
-/* Route T tokens (device pointers).  x [T][d] fp32 -> idx [T][k] int32,
- * w [T][k] fp32.  If u is non-NULL its arrays receive the batch-union lists.
- * logits [T][E] fp32 may be NULL.  Errors: E_ARG, E_SHAPE, E_NOT_LOADED,
+/* Route T tokens ([A] §1 background: a router picks 8 of the 256 experts of
+ * a layer per token; [A] §4: routing is never changed silently, so the
+ * selection is deterministic).  Device pointers: x [T][d] fp32 ->
+ * logits l[t][e] = sum_c R[e][c] x[t][c] + b[e] in fp32; idx [T][k] int32,
+ * the k largest logits, larger first, exact ties to the lower expert id;
+ * w [T][k] fp32, the softmax over the k selected logits.  If u is non-NULL
+ * its arrays receive the batch-union lists of this routing ([A] §2,
+ * batch-union).  logits [T][E] fp32 may be NULL.  Enqueued on the context's
+ * stream; allocates nothing.  Errors: E_ARG, E_SHAPE, E_NOT_LOADED,
  * E_WORKSPACE, E_HIP. */
 COLIMOE_API int colimoe_route(colimoe_ctx *ctx, int32_t layer, const float *x, int32_t T, int32_t *idx, float *w,
                   const colimoe_union *u, float *logits);
@@ -239,12 +245,22 @@ COLIMOE_API int colimoe_route(colimoe_ctx *ctx, int32_t layer, const float *x, i
  * E_WORKSPACE, E_HIP. */
 COLIMOE_API int colimoe_union_build(colimoe_ctx *ctx, const int32_t *idx, int32_t T, const colimoe_union *u);
 
-/* residual[T][d] += MoE(x) under the given routing (idx, w are inputs, so a
- * caller may force a routing).  u: union lists for this idx, as written by
- * colimoe_route, or NULL to rebuild them in the workspace.  flags: one of
- * colimoe_forward_flags.  The fp32 path gives each token bit-identical
- * results whether it runs alone or batched with others.  Errors: E_ARG,
- * E_SHAPE, E_NOT_LOADED, E_WORKSPACE, E_HIP. */
+/* The experts of one layer for T tokens: residual[T][d] += MoE(x) under the
+ * given routing.  Each routed expert is the three adjacent matrices of [A] §2
+ * (gate, up, down; y = Wd (SiLU(Wg x) * (Wu x))), the shared expert runs for
+ * every token with weight 1 ([D] §3), and the outputs are added in ascending
+ * expert id, then the shared expert.  Batched tokens read each distinct
+ * expert from HBM once per call ([A] §2, batch-union); at batch 1 the
+ * weights are dequantised to fp32-class arithmetic, for many tokens per
+ * expert the grouped bf16 matrix-core path applies ([D] §4, highlight 4).
+ * Device pointers: x [T][d] fp32; idx [T][k] int32 and w [T][k] fp32 are
+ * inputs, so a caller may force a routing; residual [T][d] fp32, updated in
+ * place.  u: union lists for this idx, as written by colimoe_route, or NULL
+ * to rebuild them in the workspace.  flags: one of colimoe_forward_flags
+ * (no silent change of path, [A] §4: a flag the shapes do not allow is
+ * E_SHAPE).  The fp32-class paths give each token bit-identical results
+ * whether it runs alone or batched with others.  Errors: E_ARG, E_SHAPE,
+ * E_NOT_LOADED, E_WORKSPACE, E_HIP. */
 COLIMOE_API int colimoe_forward(colimoe_ctx *ctx, int32_t layer, const float *x, int32_t T, const int32_t *idx,
                     const float *w, const colimoe_union *u, float *residual, uint32_t flags);
 

@@ -402,11 +402,15 @@ static int ensure_resident(colimoe_ctx *ctx, int32_t layer, const int32_t *idx, 
   }
   std::sort(need.begin(), need.end());
   need.erase(std::unique(need.begin(), need.end()), need.end());
-  int free_slots = 0;
-  for (int i = 0; i < C.n_slots; ++i) free_slots += !C.fixed[i];
-  if ((int)need.size() > free_slots) return COLIMOE_E_WORKSPACE;
-  const uint64_t now = ++C.stamp;
   int32_t *map = &C.slot_of[(size_t)layer * (E + 1)];
+  // the call's experts that must sit in evictable slots: the misses, and the
+  // hits that already sit in one (a pinned expert's slot is not evictable and
+  // is not counted)
+  int free_slots = 0, want_free = 0;
+  for (int i = 0; i < C.n_slots; ++i) free_slots += !C.fixed[i];
+  for (int e : need) want_free += map[e] < 0 || !C.fixed[map[e]];
+  if (want_free > free_slots) return COLIMOE_E_WORKSPACE;
+  const uint64_t now = ++C.stamp;
   for (int e : need) C.uses[(size_t)layer * (E + 1) + e] += 1;
   for (int e : need)
     if (map[e] >= 0) {

@@ -708,20 +708,35 @@ __global__ __launch_bounds__(64 * NWMAX) void k_down_wide(LayerDev L, Dims D, co
 // accumulated in fp32 along the row.  The weights are the canonical
 // two's-complement nibbles, read as they are.
 
+// Group exponent: the smallest E with max|v| < 2^E (at least -100), and the
+// group's scale 2^(E-22).  mb is the bit pattern of max|v|, taken as an
+// integer maximum over the |v| patterns, so a NaN or an infinity in the
+// group wins it.  Such a group gets a NaN scale (every output it enters is
+// NaN, as on the fp32 path: no silent change of the result) and its values
+// are encoded as zeros (fin = false), so no non-finite value reaches the
+// integer conversion.
+__device__ __forceinline__ int fxp_exponent(uint32_t mb, float &scale, bool &fin) {
+  fin = mb < 0x7F800000u;
+  const float mx = bits_f(fin ? mb : 0u);
+  int E = mx > 0.0f ? ilogbf(mx) + 1 : 0;
+  E = E < -100 ? -100 : E;
+  scale = fin ? ldexpf(1.0f, E - 22) : __builtin_nanf("");
+  return E;
+}
+
 // Encodes 16 values; words[2k + w] holds digit plane k of columns 8w..8w+7.
 __device__ __forceinline__ void quant16(const float *v, uint32_t *words, float &scale) {
-  float m = 0.0f;
+  uint32_t mb = 0u;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
-  int E = m > 0.0f ? ilogbf(m) + 1 : 0;  // m < 2^E
-  E = E < -100 ? -100 : E;
+  for (int i = 0; i < 16; ++i) mb = max(mb, f_bits(fabsf(v[i])));
+  bool fin;
+  const int E = fxp_exponent(mb, scale, fin);
   const float up = ldexpf(1.0f, 22 - E);
-  scale = ldexpf(1.0f, E - 22);
 #pragma unroll
   for (int k = 0; k < 12; ++k) words[k] = 0u;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const uint32_t B = (uint32_t)((int)__builtin_rintf(v[i] * up) + 0x888888);
+    const uint32_t B = (uint32_t)((int)__builtin_rintf((fin ? v[i] : 0.0f) * up) + 0x888888);
 #pragma unroll
     for (int k = 0; k < 6; ++k) words[2 * k + (i >> 3)] |= (((B >> (4 * k)) & 15u) ^ 8u) << (4 * (i & 7));
   }
@@ -953,14 +968,14 @@ __global__ __launch_bounds__(256 * WPT) void k_gateup_tok(LayerDev L, Dims D, Un
       mb = max(mb, dpp<kRowRor4>(mb));
       mb = max(mb, dpp<kRowRor2>(mb));
       mb = max(mb, dpp<kRowRor1>(mb));
-      const float mx = bits_f(mb);
-      int E = mx > 0.0f ? ilogbf(mx) + 1 : 0;
-      E = E < -100 ? -100 : E;
+      float sc;
+      bool fin;
+      const int E = fxp_exponent(mb, sc, fin);
       if (m < mc) {
-        const uint32_t B = (uint32_t)((int)__builtin_rintf(v * ldexpf(1.0f, 22 - E)) + 0x888888);
+        const uint32_t B = (uint32_t)((int)__builtin_rintf((fin ? v : 0.0f) * ldexpf(1.0f, 22 - E)) + 0x888888);
 #pragma unroll
         for (int k = 0; k < 6; ++k) atomicOr(&hw[m][2 * k + (i >> 3)], (((B >> (4 * k)) & 15u) ^ 8u) << (4 * (i & 7)));
-        if (i == 0) hsc[m] = ldexpf(1.0f, E - 22);
+        if (i == 0) hsc[m] = sc;
       }
     }
     __syncthreads();
@@ -1043,13 +1058,13 @@ __global__ __launch_bounds__(256 * NS) void k_gateup_one(LayerDev L, Dims D, Uni
     mb = max(mb, dpp<kRowRor4>(mb));
     mb = max(mb, dpp<kRowRor2>(mb));
     mb = max(mb, dpp<kRowRor1>(mb));
-    const float mx = bits_f(mb);
-    int E = mx > 0.0f ? ilogbf(mx) + 1 : 0;
-    E = E < -100 ? -100 : E;
-    const uint32_t B = (uint32_t)((int)__builtin_rintf(hval * ldexpf(1.0f, 22 - E)) + 0x888888);
+    float sc;
+    bool fin;
+    const int E = fxp_exponent(mb, sc, fin);
+    const uint32_t B = (uint32_t)((int)__builtin_rintf((fin ? hval : 0.0f) * ldexpf(1.0f, 22 - E)) + 0x888888);
 #pragma unroll
     for (int k = 0; k < 6; ++k) atomicOr(&hw[2 * k + (i >> 3)], (((B >> (4 * k)) & 15u) ^ 8u) << (4 * (i & 7)));
-    if (i == 0) hsc = ldexpf(1.0f, E - 22);
+    if (i == 0) hsc = sc;
   }
   __syncthreads();
   if (threadIdx.x < 12) {
@@ -1133,13 +1148,13 @@ __global__ __launch_bounds__(256 * NS) __attribute__((amdgpu_waves_per_eu(6))) v
       mb = max(mb, dpp<kRowRor4>(mb));
       mb = max(mb, dpp<kRowRor2>(mb));
       mb = max(mb, dpp<kRowRor1>(mb));
-      const float mx = bits_f(mb);
-      int E = mx > 0.0f ? ilogbf(mx) + 1 : 0;
-      E = E < -100 ? -100 : E;
-      const uint32_t B = (uint32_t)((int)__builtin_rintf(hval * ldexpf(1.0f, 22 - E)) + 0x888888);
+      float sc;
+      bool fin;
+      const int E = fxp_exponent(mb, sc, fin);
+      const uint32_t B = (uint32_t)((int)__builtin_rintf((fin ? hval : 0.0f) * ldexpf(1.0f, 22 - E)) + 0x888888);
 #pragma unroll
       for (int k = 0; k < 6; ++k) atomicOr(&hw[m][2 * k + (i >> 3)], (((B >> (4 * k)) & 15u) ^ 8u) << (4 * (i & 7)));
-      if (i == 0) hsc[m] = ldexpf(1.0f, E - 22);
+      if (i == 0) hsc[m] = sc;
     }
     __syncthreads();
     if ((int)threadIdx.x < mc * 12) {

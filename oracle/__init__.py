@@ -33,44 +33,65 @@ def build(force: bool = True) -> str:
     return _LIB
 
 
+def _configure(L):
+    i32 = ctypes.c_int
+    L.oracle_set_bits.argtypes = [i32]
+    L.oracle_nibble.restype = i32
+    L.oracle_nibble.argtypes = [ctypes.c_uint8, i32]
+    L.oracle_half.restype = ctypes.c_double
+    L.oracle_half.argtypes = [ctypes.c_uint16]
+    L.oracle_weight.restype = ctypes.c_double
+    L.oracle_weight.argtypes = [_vp, _vp, i32, i32, i32, i32]
+    L.oracle_dequant.argtypes = [_vp, _vp, i32, i32, _vp]
+    L.oracle_matvec.argtypes = [_vp, _vp, i32, i32, _vp, _vp, _vp]
+    L.oracle_expert_bytes.restype = ctypes.c_size_t
+    L.oracle_expert_bytes.argtypes = [i32, i32]
+    L.oracle_silu.restype = ctypes.c_double
+    L.oracle_silu.argtypes = [ctypes.c_double]
+    L.oracle_expert.argtypes = [_vp, i32, i32, _vp, _vp, _vp, _vp, _vp, _vp]
+    L.oracle_router.argtypes = [_vp, _vp, _vp, i32, i32, _vp]
+    L.oracle_topk_sort.argtypes = [_vp, i32, i32, _vp]
+    L.oracle_topk_select.argtypes = [_vp, i32, i32, _vp]
+    L.oracle_softmax_selected.argtypes = [_vp, i32, _vp, i32, _vp]
+    L.oracle_union.restype = i32
+    L.oracle_union.argtypes = [_vp, i32, i32, i32, _vp, _vp, _vp, _vp, _vp]
+    L.oracle_rmsnorm.argtypes = [_vp, i32, ctypes.c_double, _vp]
+    L.oracle_moe_token.restype = i32
+    L.oracle_moe_token.argtypes = [_vp, i32, i32, i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+    L.oracle_route_token.restype = i32
+    L.oracle_route_token.argtypes = [_vp, _vp, _vp, i32, i32, i32, _vp, _vp, _vp]
+    L.oracle_expert_top_p.argtypes = [_vp, i32, i32, ctypes.c_double, _vp, _vp]
+    L.oracle_expert_top_p.restype = i32
+    return L
+
+
 def lib():
     global _lib
     if _lib is None:
         if not os.path.exists(_LIB):
             build(force=False)
-        L = ctypes.CDLL(_LIB)
-        i32 = ctypes.c_int
-        L.oracle_set_mutation.argtypes = [i32]
-        L.oracle_set_bits.argtypes = [i32]
-        L.oracle_get_mutation.restype = i32
-        L.oracle_nibble.restype = i32
-        L.oracle_nibble.argtypes = [ctypes.c_uint8, i32]
-        L.oracle_half.restype = ctypes.c_double
-        L.oracle_half.argtypes = [ctypes.c_uint16]
-        L.oracle_weight.restype = ctypes.c_double
-        L.oracle_weight.argtypes = [_vp, _vp, i32, i32, i32, i32]
-        L.oracle_dequant.argtypes = [_vp, _vp, i32, i32, _vp]
-        L.oracle_matvec.argtypes = [_vp, _vp, i32, i32, _vp, _vp, _vp]
-        L.oracle_expert_bytes.restype = ctypes.c_size_t
-        L.oracle_expert_bytes.argtypes = [i32, i32]
-        L.oracle_silu.restype = ctypes.c_double
-        L.oracle_silu.argtypes = [ctypes.c_double]
-        L.oracle_expert.argtypes = [_vp, i32, i32, _vp, _vp, _vp, _vp, _vp, _vp]
-        L.oracle_router.argtypes = [_vp, _vp, _vp, i32, i32, _vp]
-        L.oracle_topk_sort.argtypes = [_vp, i32, i32, _vp]
-        L.oracle_topk_select.argtypes = [_vp, i32, i32, _vp]
-        L.oracle_softmax_selected.argtypes = [_vp, i32, _vp, i32, _vp]
-        L.oracle_union.restype = i32
-        L.oracle_union.argtypes = [_vp, i32, i32, i32, _vp, _vp, _vp, _vp, _vp]
-        L.oracle_rmsnorm.argtypes = [_vp, i32, ctypes.c_double, _vp]
-        L.oracle_moe_token.restype = i32
-        L.oracle_moe_token.argtypes = [_vp, i32, i32, i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
-        L.oracle_route_token.restype = i32
-        L.oracle_route_token.argtypes = [_vp, _vp, _vp, i32, i32, i32, _vp, _vp, _vp]
-        L.oracle_expert_top_p.argtypes = [_vp, i32, i32, ctypes.c_double, _vp, _vp]
-        L.oracle_expert_top_p.restype = i32
-        _lib = L
+        _lib = _configure(ctypes.CDLL(_LIB))
     return _lib
+
+
+class variant:
+    """Context in which every function below calls another build of the
+    oracle's source (a library at ``path`` exporting the same functions).
+    The pin-sensitivity test uses it to run the pins against copies of the
+    oracle with one mistake planted."""
+
+    def __init__(self, path: str):
+        self.path = path
+
+    def __enter__(self):
+        global _lib
+        self._saved = lib()
+        _lib = _configure(ctypes.CDLL(self.path))
+        return self
+
+    def __exit__(self, *exc):
+        global _lib
+        _lib = self._saved
 
 
 def _c(a, dtype):
@@ -90,10 +111,6 @@ class container_bits:
 
     def __exit__(self, *exc):
         lib().oracle_set_bits(4)
-
-
-def set_mutation(m: int) -> None:
-    lib().oracle_set_mutation(int(m))
 
 
 # ------------------------------------------------------------------ pieces
@@ -287,4 +304,75 @@ def moe_layer(X, d: int, f: int, experts: Dict[int, np.ndarray], shared, idx, w,
     l1 = np.empty_like(X)
     for t in range(X.shape[0]):
         out[t], l1[t] = moe_token(X[t], d, f, experts, shared, idx[t], w[t], R[t], E)
+    return out, l1
+
+
+def _dense_expert_rows(blob: np.ndarray, d: int, f: int, Xe: np.ndarray):
+    """One expert applied to the m tokens in Xe [m][d]: y [m][d] and
+    yabs[t][r] = sum_c |Wd[r][c] h_t[c]|.  The three matrices are decoded once
+    by the oracle's own dequantisation (exact q*s in fp64); the products are
+    fp64 matrix products (a library routine)."""
+    (gn, gs), (un, us), (dn, ds) = blob_sections(blob, d, f)
+    Wg = dequant(gn, gs, f, d)
+    G = Xe @ Wg.T
+    del Wg
+    Wu = dequant(un, us, f, d)
+    Uu = Xe @ Wu.T
+    del Wu
+    H = G / (1.0 + np.exp(-G)) * Uu  # SiLU(g) * u, SiLU(z) = z / (1 + e^-z)
+    Wd = dequant(dn, ds, d, f)
+    Y = H @ Wd.T
+    Yabs = np.abs(H) @ np.abs(Wd).T  # |Wd[r][c] h[c]| = |Wd[r][c]| |h[c]|
+    return Y, Yabs
+
+
+def moe_layer_grouped(X, d: int, f: int, blob_of, shared, idx, w, residual=None, threads: int = 0):
+    """The same layer as ``moe_layer`` for many tokens, grouped by expert.
+
+    Each distinct expert in idx (and the shared expert) is dequantised once and
+    applied to all tokens routed to it with fp64 matrix products, so a
+    2048-token prefill-shaped call is checked in seconds instead of minutes.
+    out[t] = residual[t] + sum_j w[t][j] y_{idx[t][j]}(x_t) + y_shared(x_t), and
+    l1 the per-output L1 norm of the products, exactly as ``moe_token`` defines
+    them; only the fp64 summation order differs from its sequential sums.
+    blob_of(e) returns expert e's canonical blob; slots with idx -1 add nothing.
+    Experts run on ``threads`` worker threads (default: the process's CPUs)."""
+    from concurrent.futures import ThreadPoolExecutor
+    X = np.atleast_2d(np.asarray(X, dtype=np.float64))
+    idx = np.asarray(idx)
+    w = np.asarray(w, dtype=np.float64)
+    T = X.shape[0]
+    R = X if residual is None else np.atleast_2d(np.asarray(residual, dtype=np.float64))
+    out = R.copy()
+    l1 = np.abs(R)
+    groups = {}
+    for t in range(T):
+        for j in range(idx.shape[1]):
+            e = int(idx[t, j])
+            if e >= 0:
+                groups.setdefault(e, []).append((t, j))
+    jobs = [(e, groups[e]) for e in sorted(groups)]
+    if shared is not None:
+        jobs.append((-1, [(t, -1) for t in range(T)]))
+
+    def run(job):
+        e, pairs = job
+        blob = shared if e < 0 else blob_of(e)
+        toks = np.array([t for t, _ in pairs])
+        Y, Ya = _dense_expert_rows(np.ascontiguousarray(blob, dtype=np.uint8), d, f, X[toks])
+        return e, pairs, Y, Ya
+
+    from threadpoolctl import threadpool_limits
+    n = threads or len(os.sched_getaffinity(0))
+    # one library thread per worker: the workers already fill the cores
+    with threadpool_limits(1), ThreadPoolExecutor(max_workers=max(1, n)) as pool:
+        # largest groups first, so the long ones do not start last
+        order = sorted(range(len(jobs)), key=lambda i: -len(jobs[i][1]))
+        res = dict(zip(order, pool.map(run, [jobs[i] for i in order])))
+        for i in range(len(jobs)):
+            e, pairs, Y, Ya = res[i]
+            for i, (t, j) in enumerate(pairs):
+                g = 1.0 if j < 0 else w[t, j]
+                out[t] += g * Y[i]
+                l1[t] += abs(g) * Ya[i]
     return out, l1

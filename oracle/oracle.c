@@ -48,11 +48,6 @@
 static int g_bits = 4;
 void oracle_set_bits(int bits) { g_bits = bits == 8 ? 8 : 4; }
 
-/* Planted-mistake switch for the pin-sensitivity test (0 = the definition). */
-static int g_mutation = 0;
-void oracle_set_mutation(int m) { g_mutation = m; }
-int oracle_get_mutation(void) { return g_mutation; }
-
 /* ---------------------------------------------------------------- decoding */
 
 /* O1: one int4 element.  Reading: byte i of a row holds element 2i in its low
@@ -60,8 +55,6 @@ int oracle_get_mutation(void) { return g_mutation; }
  * complement integer in [-8, 7] with no zero-point. */
 int oracle_nibble(uint8_t byte, int high) {
   int n = high ? (byte >> 4) & 15 : byte & 15;
-  if (g_mutation == 1) n = high ? byte & 15 : (byte >> 4) & 15; /* swapped order */
-  if (g_mutation == 2) return n - 8;                               /* offset binary */
   return n >= 8 ? n - 16 : n;
 }
 
@@ -95,7 +88,6 @@ double oracle_weight(const uint8_t *nib, const uint8_t *sc, int rows, int cols, 
     q = oracle_nibble(b, c & 1);
   }
   int g = c / GS;
-  if (g_mutation == 3) g = (r / GS) % (cols / GS); /* groups along the wrong axis */
   double s = oracle_half(rd16(sc + 2 * ((size_t)r * (size_t)(cols / GS) + (size_t)g)));
   return (double)q * s;
 }
@@ -150,7 +142,6 @@ size_t oracle_expert_bytes(int d, int f) {
 
 /* SiLU(z) = z * sigmoid(z) = z / (1 + e^-z). */
 double oracle_silu(double z) {
-  if (g_mutation == 7) return z / (1.0 + exp(z));
   return z / (1.0 + exp(-z));
 }
 
@@ -182,7 +173,7 @@ void oracle_router(const float *R, const float *bias, const double *x, int E, in
   for (int e = 0; e < E; ++e) {
     double acc = 0.0;
     for (int c = 0; c < d; ++c) acc += (double)R[(size_t)e * d + c] * x[c];
-    if (bias && g_mutation != 8) acc += (double)bias[e];
+    if (bias) acc += (double)bias[e];
     l[e] = acc;
   }
 }
@@ -192,7 +183,7 @@ void oracle_router(const float *R, const float *bias, const double *x, int E, in
 static const double *g_sort_l;
 static int before(int a, int b, const double *l) {
   if (l[a] != l[b]) return l[a] > l[b];
-  return g_mutation == 6 ? a > b : a < b;
+  return a < b;
 }
 static int cmp_sort(const void *pa, const void *pb) {
   int a = *(const int *)pa, b = *(const int *)pb;
@@ -228,12 +219,7 @@ void oracle_topk_select(const double *l, int E, int k, int32_t *idx) {
  * renormalisation or scaling beyond that).  w_j = e^(l_j - m) / sum_i e^(l_i - m). */
 void oracle_softmax_selected(const double *l, int E, const int32_t *idx, int k, double *w) {
   double m = -INFINITY, s = 0.0;
-  if (g_mutation == 5) { /* softmax over all experts, then pick */
-    for (int e = 0; e < E; ++e) m = fmax(m, l[e]);
-    for (int e = 0; e < E; ++e) s += exp(l[e] - m);
-    for (int j = 0; j < k; ++j) w[j] = exp(l[idx[j]] - m) / s;
-    return;
-  }
+  (void)E;
   for (int j = 0; j < k; ++j) m = fmax(m, l[idx[j]]);
   for (int j = 0; j < k; ++j) s += exp(l[idx[j]] - m);
   for (int j = 0; j < k; ++j) w[j] = exp(l[idx[j]] - m) / s;
@@ -255,13 +241,6 @@ int oracle_expert_top_p(const double *l, int E, int k, double p, int32_t *idx, d
       cum += w[m];
       ++m;
     }
-  }
-  if (g_mutation == 9) { /* kept weights left as they were (no softmax over the kept) */
-    for (int j = m; j < k; ++j) {
-      idx[j] = -1;
-      w[j] = 0.0;
-    }
-    return m;
   }
   oracle_softmax_selected(l, E, idx, m, w);
   for (int j = m; j < k; ++j) {
@@ -340,7 +319,7 @@ int oracle_moe_token(const double *x, int d, int f, int k, const uint8_t *const 
       if (l1) l1[r] += fabs(w[j]) * ya[r];
     }
   }
-  if (shared && g_mutation != 4) {
+  if (shared) {
     oracle_expert(shared, d, f, x, NULL, NULL, NULL, y, ya);
     for (int r = 0; r < d; ++r) {
       out[r] += y[r];

@@ -252,3 +252,40 @@ def test_one_token_kernel_variants(w):
         assert np.array_equal(a["out"][0].view(np.uint32), batch["out"][t].view(np.uint32)), t
         assert np.array_equal(a["idx"][0], batch["idx"][t])
     print(w.name, "worst ratio", batch["ratio"])
+
+
+@pytest.mark.parametrize("flags", [FXP, FP32, 2], ids=["fxp", "fp32", "bf16"])
+@pytest.mark.parametrize("T", [1, 3])
+@pytest.mark.parametrize("bad", ["nan", "inf"])
+def test_non_finite_inputs_propagate(flags, T, bad):
+    """One NaN or one infinity in a token's activations makes every output of
+    that token non-finite on every arithmetic path (the fixed-point encoding
+    gives the affected group a NaN scale instead of a finite digit pattern;
+    [A] §4: precision never changes silently).  The other tokens are
+    untouched: their bits equal those of a call without the bad value."""
+    w = RAGGED3
+    ctx = _ctx(w, max_tokens=3)
+    P.load_layer(ctx, w, 0)
+    X = synth.activations(w, stream=11)[:T].copy()
+    rng = np.random.default_rng(5)
+    idx = torch.from_numpy(np.stack([rng.permutation(w.E)[:w.k] for _ in range(T)]).astype(np.int32)).cuda()
+    wts = torch.full((T, w.k), 1.0 / w.k, dtype=torch.float32, device="cuda")
+
+    def run(Xh):
+        x = torch.from_numpy(np.ascontiguousarray(Xh)).cuda()
+        res = x.clone()
+        ctx.forward(0, x, idx, wts, None, res, flags)
+        ctx.sync()
+        return res.cpu().numpy()
+
+    clean = run(X)
+    assert np.all(np.isfinite(clean))
+    Xb = X.copy()
+    Xb[T - 1, 1000] = np.nan if bad == "nan" else np.inf
+    out = run(Xb)
+    # the residual keeps the token's own input; every other output is non-finite
+    mask = np.ones(w.d, bool)
+    mask[1000] = False
+    assert not np.any(np.isfinite(out[T - 1][mask])), "finite outputs from a %s input" % bad
+    if T > 1:
+        assert np.array_equal(out[:T - 1].view(np.uint32), clean[:T - 1].view(np.uint32))

@@ -2,9 +2,10 @@
 
 Each check below compares the oracle with a value fixed by a definition, a
 library routine, a closed form, an invariant, brute force, an exact sum or a
-size the colibrì pages print.  ``test_planted_mistakes_are_caught`` plants
-plausible mistakes in the oracle (on the CPU) and requires each to fail at
-least one pin.
+size the colibrì pages print.  ``test_planted_mistakes_are_caught`` builds
+copies of the oracle with one plausible mistake planted in each
+(``tests/_mutants.py``, on the CPU) and requires each copy to fail at least
+one pin.
 """
 import math
 import os
@@ -16,7 +17,7 @@ from scipy.special import expit, softmax
 
 import oracle
 import synth
-from tests import _dense
+from tests import _dense, _mutants
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 TINY = synth.WORKLOADS["tiny"]
@@ -26,9 +27,7 @@ TINY = synth.WORKLOADS["tiny"]
 def _built():
     oracle.build(force=False)
     synth.build(force=False)
-    oracle.set_mutation(0)
     yield
-    oracle.set_mutation(0)
 
 
 def _tiny_inputs(layer=0):
@@ -374,6 +373,32 @@ def test_tiny_layer_bruteforce():
     pin_tiny_layer_bruteforce()
 
 
+def pin_grouped_layer():
+    """The grouped form (each expert dequantised once, fp64 matrix products
+    over its tokens) against the per-token definition, which the pins above
+    fix: same outputs and L1 norms up to fp64 summation order, on a routing
+    with ragged groups, a dropped slot, a shared expert and a separate
+    residual."""
+    w = synth.Workload(name="grouped_pin", d=192, f=128, E=12, k=3, T=30, n_shared=1, zipf=1.1,
+                       seed=synth.BASE_SEED + 77)
+    blobs = synth.expert_blobs(w, 0, 0, w.E)
+    shared = synth.shared_blob(w, 0)
+    X = synth.activations(w, stream=0).astype(np.float64)
+    rng = np.random.default_rng(77)
+    idx = np.stack([rng.permutation(w.E)[:w.k] for _ in range(w.T)]).astype(np.int32)
+    idx[4, 2] = -1
+    wts = rng.uniform(0.1, 1.0, size=(w.T, w.k))
+    res = rng.normal(size=X.shape)
+    ref, ref_l1 = oracle.moe_layer(X, w.d, w.f, {e: blobs[e] for e in range(w.E)}, shared, idx, wts, res, E=w.E)
+    out, l1 = oracle.moe_layer_grouped(X, w.d, w.f, lambda e: blobs[e], shared, idx, wts, res, threads=3)
+    assert np.all(np.abs(out - ref) <= 1e-12 * ref_l1)
+    assert np.allclose(l1, ref_l1, rtol=1e-12, atol=0)
+
+
+def test_grouped_layer():
+    pin_grouped_layer()
+
+
 def pin_l1_norm():
     blobs, R, x = _tiny_inputs()
     xd = x[0].astype(np.float64)
@@ -565,22 +590,16 @@ def test_page_sizes():
 
 PINS = [pin_nibble_table, pin_dequant_matches_numpy, pin_matvec_closed_forms, pin_router, pin_topk,
         pin_softmax, pin_silu, pin_expert_dense, pin_onehot_gate, pin_dense_all_experts,
-        pin_tiny_layer_bruteforce, pin_expert_top_p]
-MUTATIONS = {1: "nibble order swapped", 2: "offset-binary decode", 3: "scale groups along rows",
-             4: "shared expert dropped", 5: "softmax over all experts", 6: "ties to the higher index",
-             7: "SiLU sign", 8: "router bias dropped", 9: "top-p keeps the top-k weights of the kept experts"}
+        pin_tiny_layer_bruteforce, pin_expert_top_p, pin_grouped_layer]
 
 
-@pytest.mark.parametrize("m", sorted(MUTATIONS))
-def test_planted_mistakes_are_caught(m):
-    oracle.set_mutation(m)
-    try:
+@pytest.mark.parametrize("name", sorted(_mutants.MUTANTS))
+def test_planted_mistakes_are_caught(name):
+    with oracle.variant(_mutants.build(name)):
         failed = []
         for pin in PINS:
             try:
                 pin()
             except AssertionError:
                 failed.append(pin.__name__)
-        assert failed, "mutation %d (%s) passed every pin" % (m, MUTATIONS[m])
-    finally:
-        oracle.set_mutation(0)
+    assert failed, "mutant %r passed every pin" % name
