@@ -287,6 +287,34 @@ COLIMOE_API int colimoe_set_expert_top_p(colimoe_ctx *ctx, float p);
 COLIMOE_API int colimoe_route_forward(colimoe_ctx *ctx, int32_t layer, const float *x, int32_t T, int32_t *idx, float *w,
                           const colimoe_union *u, float *residual, uint32_t flags);
 
+/* For callers that cannot allocate device memory or hand over a workspace:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The same computation, arguments and results as
+ * colimoe_route_forward (bit for bit), but every scratch buffer the kernels
+ * use (logits, union lists when u is NULL, fixed-point encodings, h, y, error
+ * word) lives in a fixed device array inside the library, 32 MiB
+ * (COLIMOE_STATIC_SCRATCH_BYTES) per device, held by each device the library
+ * runs on until the process ends; the context's own workspace is neither
+ * needed nor touched.  The call allocates nothing, neither device nor host
+ * memory, and creates no events (kernel timing is skipped for it).
+ * The array is looked up once per device by colimoe_create, with that device
+ * current.
+ * Limit: a call whose workspace at this T exceeds the array returns
+ * E_WORKSPACE with no effect (at d = 6144, f = 2048, E = 256, k = 8 and a
+ * shared expert, calls of up to 63 tokens fit).
+ * Sharing: every call on one device uses that device's one array, which
+ * keeps the last call's contents (the call clears what must start at zero).
+ * Calls that overlap in time on one device (different streams, threads or
+ * contexts) race on the array and give undefined results: serialise them.
+ * A rejected routing would be reported by the next colimoe_sync, as for the
+ * other calls.  Errors: E_ARG, E_SHAPE, E_NOT_LOADED, E_WORKSPACE (this T
+ * needs more than the array), E_HIP (the lookup at colimoe_create failed, or
+ * a launch failed). */
+#define COLIMOE_STATIC_SCRATCH_BYTES ((size_t)32 << 20)
+COLIMOE_API int colimoe_route_forward_static(colimoe_ctx *ctx, int32_t layer, const float *x, int32_t T,
+                                             int32_t *idx, float *w, const colimoe_union *u, float *residual,
+                                             uint32_t flags);
+
 /* x_out[t] = r[t] / sqrt(mean(r[t]^2) + eps), unit weight, fp32 (device
  * pointers, [T][d], 16-byte aligned); lets a stack of layers run without
  * leaving the GPU.  Errors: E_ARG, E_SHAPE, E_HIP. */

@@ -28,6 +28,7 @@ COLIMOE_FWD_FP32 = 1
 COLIMOE_FWD_BF16_MFMA = 2
 COLIMOE_FWD_FXP = 3
 COLIMOE_CFG_INT8 = 1
+COLIMOE_STATIC_SCRATCH_BYTES = 32 << 20
 
 EXPORTED = [
     "colimoe_create", "colimoe_destroy", "colimoe_set_stream", "colimoe_expert_bytes", "colimoe_layer_bytes",
@@ -35,7 +36,7 @@ EXPORTED = [
     "colimoe_union_build", "colimoe_forward", "colimoe_route_forward", "colimoe_rmsnorm_route_forward", "colimoe_rmsnorm", "colimoe_debug_expert", "colimoe_sync", "colimoe_status_str",
     "colimoe_timing_enable", "colimoe_timing_read", "colimoe_set_expert_top_p", "colimoe_expert_cache_bytes",
     "colimoe_host_layer_bytes", "colimoe_set_expert_cache", "colimoe_load_experts_host", "colimoe_cache_stats",
-    "colimoe_cache_repin",
+    "colimoe_cache_repin", "colimoe_route_forward_static",
 ]
 
 
@@ -110,6 +111,8 @@ def lib() -> ctypes.CDLL:
         L.colimoe_forward.restype = ctypes.c_int
         L.colimoe_route_forward.argtypes = [vp, i32, vp, i32, vp, vp, ctypes.POINTER(colimoe_union), vp, u32]
         L.colimoe_route_forward.restype = ctypes.c_int
+        L.colimoe_route_forward_static.argtypes = [vp, i32, vp, i32, vp, vp, ctypes.POINTER(colimoe_union), vp, u32]
+        L.colimoe_route_forward_static.restype = ctypes.c_int
         L.colimoe_rmsnorm_route_forward.argtypes = [vp, i32, vp, i32, ctypes.c_float, vp, vp, vp,
                                                     ctypes.POINTER(colimoe_union), u32]
         L.colimoe_rmsnorm_route_forward.restype = ctypes.c_int
@@ -253,6 +256,13 @@ def colimoe_route_forward(ctx, layer: int, x: int, T: int, idx: int, w: int, uni
     rc = lib().colimoe_route_forward(ctx, layer, x, T, idx, w, ctypes.byref(union) if union is not None else None,
                                      residual, flags)
     return _check("colimoe_route_forward", rc) if check else rc
+
+
+def colimoe_route_forward_static(ctx, layer: int, x: int, T: int, idx: int, w: int, union: Optional[colimoe_union],
+                                 residual: int, flags: int = COLIMOE_FWD_AUTO, check: bool = True) -> int:
+    rc = lib().colimoe_route_forward_static(ctx, layer, x, T, idx, w,
+                                            ctypes.byref(union) if union is not None else None, residual, flags)
+    return _check("colimoe_route_forward_static", rc) if check else rc
 
 
 def colimoe_rmsnorm_route_forward(ctx, layer: int, r: int, T: int, eps: float, x_out: int, idx: int, w: int,

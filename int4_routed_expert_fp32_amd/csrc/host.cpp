@@ -44,6 +44,7 @@ struct colimoe_ctx {
   } cache;
   uint8_t *ws;
   size_t ws_bytes;
+  bool static_used;  // colimoe_route_forward_static has run on this context
   float top_p;  // adaptive expert top-p of one-token routing (1: off)
   Workspace wl;
   ExpertLayout el;
@@ -589,6 +590,11 @@ int colimoe_create(const colimoe_config *cfg, void *hip_stream, colimoe_ctx **ou
   c->host_store.assign(cfg->n_layers, nullptr);
   c->ws = nullptr;
   c->ws_bytes = 0;
+  c->static_used = false;
+  // The static scratch's address on this device, looked up once per device
+  // while it is current.  A failure here only disables
+  // colimoe_route_forward_static (it then returns E_HIP).
+  (void)static_scratch_init(dev);
   c->top_p = 1.0f;
   c->wl = workspace_layout(cfg->d, cfg->f, cfg->n_experts, cfg->top_k, cfg->n_shared, cfg->max_tokens);
   c->el = expert_layout(cfg->d, cfg->f);
@@ -958,6 +964,48 @@ int colimoe_route_forward(colimoe_ctx *ctx, int32_t layer, const float *x, int32
   return forward_impl(ctx, layer, x, T, idx, w, uu, residual, path, encode && T <= kRouteSplitMaxT);
 }
 
+int colimoe_route_forward_static(colimoe_ctx *ctx, int32_t layer, const float *x, int32_t T, int32_t *idx,
+                                 float *w, const colimoe_union *u, float *residual, uint32_t flags) {
+  if (!ctx) return COLIMOE_E_ARG;
+  if (layer < 0 || layer >= ctx->cfg.n_layers) return COLIMOE_E_SHAPE;
+  if (T < 0 || T > ctx->cfg.max_tokens) return COLIMOE_E_SHAPE;
+  if (!ctx->loaded[layer]) return COLIMOE_E_NOT_LOADED;
+  if (flags > COLIMOE_FWD_FXP) return COLIMOE_E_ARG;
+  if (T == 0) return COLIMOE_OK;
+  if (!x || !idx || !w || !residual || !aligned(x, 16) || !aligned(idx, 4) || !aligned(w, 4) ||
+      !aligned(residual, 16))
+    return COLIMOE_E_ARG;
+  if (u && !union_ok(u)) return COLIMOE_E_ARG;
+  const int path = select_path(ctx, T, flags);
+  if (path < 0) return path;
+  // the workspace this call needs, laid out for its own T
+  const Workspace wl =
+      workspace_layout(ctx->cfg.d, ctx->cfg.f, ctx->cfg.n_experts, ctx->cfg.top_k, ctx->cfg.n_shared, T);
+  if (wl.bytes > kStaticScratchBytes) return COLIMOE_E_WORKSPACE;
+  uint8_t *scr = static_scratch(ctx->device);
+  if (!scr) return COLIMOE_E_HIP;  // the address lookup at colimoe_create failed
+  // The same launches as colimoe_route_forward, with the scratch standing in
+  // for the context's workspace; timing is off (its events are created on
+  // demand), and everything is put back before returning.
+  uint8_t *const ws = ctx->ws;
+  const size_t ws_bytes = ctx->ws_bytes;
+  const Workspace saved = ctx->wl;
+  const bool timing = ctx->timing;
+  ctx->ws = scr;
+  ctx->ws_bytes = kStaticScratchBytes;
+  ctx->wl = wl;
+  ctx->timing = false;
+  ctx->static_used = true;
+  // the error word must start at zero; the scratch keeps the last call's contents
+  int rc = hip_status(launch_zero_words((uint32_t *)(scr + wl.err), 1, ctx->stream));
+  if (!rc) rc = colimoe_route_forward(ctx, layer, x, T, idx, w, u, residual, flags);
+  ctx->ws = ws;
+  ctx->ws_bytes = ws_bytes;
+  ctx->wl = saved;
+  ctx->timing = timing;
+  return rc;
+}
+
 int colimoe_rmsnorm_route_forward(colimoe_ctx *ctx, int32_t layer, float *r, int32_t T, float eps, float *x_out,
                                   int32_t *idx, float *w, const colimoe_union *u, uint32_t flags) {
   int rc = check_call(ctx, layer, T);
@@ -1068,14 +1116,21 @@ int colimoe_timing_read(colimoe_ctx *ctx, const char *name, double *total_ms, in
 int colimoe_sync(colimoe_ctx *ctx) {
   if (!ctx) return COLIMOE_E_ARG;
   if (hipStreamSynchronize(ctx->stream) != hipSuccess) return COLIMOE_E_HIP;
-  if (!ctx->ws) return COLIMOE_OK;
-  int32_t err = 0;
-  if (hipMemcpy(&err, ctx->ws + ctx->wl.err, 4, hipMemcpyDeviceToHost) != hipSuccess) return COLIMOE_E_HIP;
-  if (err) {
-    if (hipMemset(ctx->ws + ctx->wl.err, 0, 4) != hipSuccess) return COLIMOE_E_HIP;
-    return COLIMOE_E_ARG;
+  // the error word of the workspace, and of the static scratch once used
+  // (the error word sits at offset 0 of every workspace layout)
+  uint8_t *words[2] = {ctx->ws ? ctx->ws + ctx->wl.err : nullptr,
+                       ctx->static_used ? static_scratch(ctx->device) : nullptr};
+  int rc = COLIMOE_OK;
+  for (uint8_t *p : words) {
+    if (!p) continue;
+    int32_t err = 0;
+    if (hipMemcpy(&err, p, 4, hipMemcpyDeviceToHost) != hipSuccess) return COLIMOE_E_HIP;
+    if (err) {
+      if (hipMemset(p, 0, 4) != hipSuccess) return COLIMOE_E_HIP;
+      rc = COLIMOE_E_ARG;
+    }
   }
-  return COLIMOE_OK;
+  return rc;
 }
 
 }  // extern "C"

@@ -168,6 +168,17 @@ hipError_t launch_gateup_mfma(const LayerDev &L, const Dims &D, const uint16_t *
 hipError_t launch_down_mfma(const LayerDev &L, const Dims &D, const uint16_t *hb, const int4 *list,
                             const int32_t *count, int max_entries, float *y, hipStream_t s);
 hipError_t launch_rmsnorm(const float *r, int T, int d, float eps, float *x, hipStream_t s);
+// Zeroes n 32-bit words with a kernel (not a memset node, so the call can sit
+// in a captured graph).
+hipError_t launch_zero_words(uint32_t *p, int n, hipStream_t s);
+
+// Static device scratch of the allocation-free entry point (kernels.hip).
+constexpr size_t kStaticScratchBytes = (size_t)32 << 20;
+// Looks up the scratch array's address on `device`, which must be current;
+// once per device, later calls return at once.
+hipError_t static_scratch_init(int device);
+// The address on `device`, or null before static_scratch_init succeeded there.
+uint8_t *static_scratch(int device);
 // int8 container, one token (fp32 dequantisation): h [rows][f] and y
 // [rows][d] fp32 in the rows of the fixed-point path; the combine follows in
 // launch_combine.

@@ -12,6 +12,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -2197,6 +2199,54 @@ hipError_t launch_forward_i8(const LayerDev &L, const Dims &D, const float *x, c
   const int slots = D.k + D.n_shared;
   k_gateup_i8<<<dim3((D.f + 3) / 4, slots), 256, 0, s>>>(L, D, x, U, h);
   k_down_i8<<<dim3((D.d + 3) / 4, slots), 256, 0, s>>>(L, D, h, U, y);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------- static scratch
+// Device scratch of colimoe_route_forward_static, for callers that cannot
+// allocate: a fixed array in the library's code object, one copy per device
+// the library runs on, held until the process ends.  Host code never uses
+// the array's name as an address (on the host it names a stand-in, not
+// device memory): static_scratch_init() asks the runtime for the array's
+// address on the current device once, and every launch gets that address.
+
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+uint8_t *g_scratch_addr[kMaxDevices];  // the array's address on each device, or null
+}  // namespace
+
+hipError_t static_scratch_init(int device) {
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_addr[device]) return hipSuccess;
+  int cur = -1;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return e;
+  if (cur != device) return hipErrorInvalidDevice;  // the device must be current
+  void *ptr = nullptr;
+  e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return e;
+  g_scratch_addr[device] = (uint8_t *)ptr;
+  return hipSuccess;
+}
+
+uint8_t *static_scratch(int device) {
+  if (device < 0 || device >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  return g_scratch_addr[device];
+}
+
+__global__ void k_zero_words(uint32_t *__restrict__ p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+hipError_t launch_zero_words(uint32_t *p, int n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  k_zero_words<<<(n + 255) / 256, 256, 0, s>>>(p, n);
   return hipGetLastError();
 }
 
