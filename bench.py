@@ -45,8 +45,8 @@ def parse():
                     help="arithmetic path of the headline (auto: fixed-point activations at these shapes)")
     ap.add_argument("--no-compare", action="store_true", help="skip timing the other arithmetic path")
     ap.add_argument("--no-top-p", action="store_true", help="skip the adaptive expert top-p line of the decode workload")
-    ap.add_argument("--only", choices=("all", "decode", "stack32", "union16", "verify", "prefill2048", "tiered",
-                                       "int8"),
+    ap.add_argument("--only", choices=("all", "decode", "tiny", "stack32", "union16", "verify", "prefill2048",
+                                       "tiered", "int8"),
                     default="all",
                     help="run one workload only (the headline line needs decode)")
     return ap.parse_args()
@@ -56,11 +56,26 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def hipcc_version():
+    import subprocess
+    try:
+        r = subprocess.run([os.environ.get("HIPCC", "/opt/rocm/bin/hipcc"), "--version"], capture_output=True,
+                           text=True, timeout=60)
+        return r.stdout.strip()
+    except (OSError, subprocess.SubprocessError):
+        return "unknown"
+
+
 def kernel_source_sha():
+    """Hash of what decides the decode kernels' code: their sources, the build
+    script (compiler flags) and the compiler's version."""
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
         with open(os.path.join(ROOT, "int4_routed_expert_fp32_amd", "csrc", name), "rb") as f:
             h.update(f.read())
+    with open(os.path.join(ROOT, "int4_routed_expert_fp32_amd", "_build.py"), "rb") as f:
+        h.update(f.read())
+    h.update(hipcc_version().encode())
     return h.hexdigest()
 
 
@@ -80,6 +95,60 @@ def measured_traffic(kernel):
     if not k or rec.get("source_sha256") != kernel_source_sha():
         return None
     return int(k["fetch_bytes"] + k["write_bytes"])
+
+
+def host_protocol():
+    """Facts of the measurement protocol that need no GPU: host CPU, ROCm,
+    source identity, command.  Gathered before the GPU is initialised (the
+    tools run as child processes)."""
+    import platform
+    import subprocess
+    info = {"command": " ".join([os.path.basename(sys.executable)] + sys.argv), "host": platform.node()}
+    try:
+        with open("/proc/cpuinfo") as f:
+            models = [l.split(":", 1)[1].strip() for l in f if l.startswith("model name")]
+        info["cpu_model"] = models[0] if models else "unknown"
+        info["cpu_threads_online"] = len(models)
+    except OSError:
+        info["cpu_model"] = "unknown"
+    info["cpu_affinity"] = len(os.sched_getaffinity(0))
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            info["rocm"] = f.read().strip()
+    except OSError:
+        info["rocm"] = "unknown"
+    try:
+        r = subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"], capture_output=True, text=True, timeout=30)
+        info["git_commit"] = r.stdout.strip() if r.returncode == 0 else "unavailable (tree without .git)"
+    except (OSError, subprocess.SubprocessError):
+        info["git_commit"] = "unavailable"
+    h = hashlib.sha256()
+    for sub in ("include", os.path.join("int4_routed_expert_fp32_amd", "csrc")):
+        d = os.path.join(ROOT, sub)
+        for name in sorted(os.listdir(d)):
+            with open(os.path.join(d, name), "rb") as f:
+                h.update(name.encode() + f.read())
+    with open(os.path.abspath(__file__), "rb") as f:
+        h.update(f.read())
+    info["source_sha256"] = h.hexdigest()
+    try:
+        r = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=60)
+        for line in r.stdout.splitlines():
+            if "Max Clock Freq" in line and "gfx" in info.get("_last_agent", ""):
+                info["gpu_max_clock_mhz"] = int(line.split(":")[1].split("(")[0].strip())
+                break
+            if line.strip().startswith("Name:") and "gfx" in line:
+                info["_last_agent"] = line
+    except (OSError, subprocess.SubprocessError, ValueError):
+        pass
+    info.pop("_last_agent", None)
+    return info
+
+
+def gpu_protocol(torch, dev):
+    p = torch.cuda.get_device_properties(dev)
+    return {"gpu": p.name, "arch": getattr(p, "gcnArchName", "unknown"), "compute_units": p.multi_processor_count,
+            "hbm_bytes": p.total_memory, "torch": torch.__version__, "hip_runtime": torch.version.hip}
 
 
 def calibration_copy(torch, dev):
@@ -134,6 +203,44 @@ def event_time(torch, stream, run):
     return ev0.elapsed_time(ev1)  # ms
 
 
+def windowed_time(torch, stream, run, lo, hi, n_win=5):
+    """Times steps lo..hi-1 (run(a, b) enqueues steps a..b-1) in n_win equal
+    consecutive sub-windows, events between them and no host synchronisation
+    inside: (ms per step over all of them, [ms per step of each window])."""
+    bounds = [lo + (hi - lo) * i // n_win for i in range(n_win + 1)]
+    evs = [torch.cuda.Event(enable_timing=True) for _ in bounds]
+    torch.cuda.synchronize()
+    evs[0].record(stream)
+    for i in range(n_win):
+        run(bounds[i], bounds[i + 1])
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = [evs[i].elapsed_time(evs[i + 1]) / max(bounds[i + 1] - bounds[i], 1) for i in range(n_win)]
+    return evs[0].elapsed_time(evs[-1]) / (hi - lo), per
+
+
+def graph_time(torch, ctx, run, reps=3):
+    """ms per replay of `run` captured into one HIP graph (the context's calls
+    are enqueued on the capture stream while capturing, then the stream is
+    put back)."""
+    cap = torch.cuda.Stream()
+    old = ctx.stream
+    torch.cuda.synchronize()
+    ctx.set_stream(cap)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        run()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(cap):
+        g.replay()
+        torch.cuda.synchronize()
+        ms = event_time(torch, cap, lambda: [g.replay() for _ in range(reps)]) / reps
+    ctx.set_stream(old)
+    del g
+    torch.cuda.synchronize()
+    return ms
+
+
 def load_ring(ctx, synth, w, n, tag):
     t0 = time.time()
     for i in range(n):
@@ -167,9 +274,15 @@ def bench_decode(args, torch, np, synth, cm, MoeContext, dev, stream):
     head = flag_of[args.path]
     steps(head, 0, args.warmup)()
     ctx.sync()
-    ms = event_time(torch, stream, steps(head, args.warmup, n)) / args.steps
+    # exactly `steps` timed steps, in five consecutive sub-windows
+    ms, win = windowed_time(torch, stream, lambda a, b: steps(head, a, b)(), args.warmup, n)
     ctx.sync()
     kern = per_kernel(cm, ctx, steps(head, args.warmup, n))
+    # the same steps captured into one HIP graph and replayed
+    gms = graph_time(torch, ctx, steps(head, args.warmup, n)) / args.steps
+    timing = {"median_window_us": round(1000 * sorted(win)[len(win) // 2], 3),
+              "window_us": [round(1000 * v, 3) for v in win],
+              "graph_replay_us_per_token": round(1000 * gms, 3)}
     topp = None
     if not args.no_top_p:
         # adaptive expert top-p at the pages' value (p = 0.7): time per token and
@@ -199,7 +312,7 @@ def bench_decode(args, torch, np, synth, cm, MoeContext, dev, stream):
     ctx.close()
     del ctx, X, res
     torch.cuda.empty_cache()
-    return w, ms, kern, other, topp
+    return w, ms, kern, other, topp, timing
 
 
 def bench_stack32(args, torch, np, synth, cm, MoeContext, dev, stream):
@@ -234,6 +347,7 @@ def bench_stack32(args, torch, np, synth, cm, MoeContext, dev, stream):
     ms = event_time(torch, stream, lambda: [token(i) for i in range(warm, warm + ntok)]) / ntok
     ctx.sync()
     kern = per_kernel(cm, ctx, lambda: [token(i) for i in range(warm, warm + 4)])
+    gms = graph_time(torch, ctx, lambda: [token(i) for i in range(warm, warm + ntok)]) / ntok
     ctx.close()
     del ctx, X0, r, x
     torch.cuda.empty_cache()
@@ -244,7 +358,38 @@ def bench_stack32(args, torch, np, synth, cm, MoeContext, dev, stream):
             "us_per_token": round(1000 * ms, 2), "tokens_per_s": round(1000.0 / ms, 1),
             "us_per_layer": round(1000 * ms / w.n_layers, 3), "int4_bytes_per_token": bytes_tok,
             "int4_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "tokens_timed": ntok,
+            "graph_replay_us_per_token": round(1000 * gms, 2),
+            "graph_replay_hbm_frac": round(bytes_tok / (gms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "kernels": {k: round(v["avg_us"], 3) for k, v in kern.items()}}
+
+
+def bench_tiny(args, torch, np, synth, cm, MoeContext, dev, stream):
+    """The tiny layer (d=256 f=128 E=16 top-2, no shared expert), one token per
+    call: latency-bound, its weights stay in the caches."""
+    w = synth.WORKLOADS["tiny"]
+    ctx = MoeContext(w.d, w.f, w.E, w.k, n_layers=1, n_shared=w.n_shared, max_tokens=1)
+    load_ring(ctx, synth, w, 1, "tiny")
+    n, warm = 400, 40
+    X = torch.from_numpy(synth.activations(w.with_(T=n), stream=13)).to(dev)
+    res = X.clone()
+    idx = torch.empty((n, w.k), dtype=torch.int32, device=dev)
+    wts = torch.empty((n, w.k), dtype=torch.float32, device=dev)
+    U = ctx.new_union(1)
+
+    def run(a, b):
+        for i in range(a, b):
+            cm.colimoe_route_forward(ctx.ctx, 0, X[i].data_ptr(), 1, idx[i].data_ptr(), wts[i].data_ptr(), U.abi(),
+                                     res[i].data_ptr(), cm.COLIMOE_FWD_AUTO)
+
+    run(0, warm)
+    ctx.sync()
+    ms, win = windowed_time(torch, stream, run, warm, n)
+    gms = graph_time(torch, ctx, lambda: run(warm, n)) / (n - warm)
+    ctx.close()
+    del ctx, X, res
+    return {"workload": "tiny MoE layer d=256 f=128 E=16 top-2, no shared expert, 1 token (fp32 path)",
+            "us_per_call": round(1000 * ms, 3), "median_window_us": round(1000 * sorted(win)[2], 3),
+            "graph_replay_us_per_call": round(1000 * gms, 3), "calls_timed": n - warm}
 
 
 def bench_union16(args, torch, np, synth, cm, MoeContext, dev, stream):
@@ -492,8 +637,10 @@ def main():
     import int4_routed_expert_fp32_amd as cm
     from int4_routed_expert_fp32_amd.runtime import MoeContext
 
+    proto = host_protocol()  # before the GPU is initialised
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    proto.update(gpu_protocol(torch, dev))
     stream = torch.cuda.current_stream(dev)
     calibration_copy(torch, dev)
     ceiling = stream_ceiling(torch, dev, stream)
@@ -501,7 +648,7 @@ def main():
     common = (args, torch, np, synth, cm, MoeContext, dev, stream)
 
     extra = {}
-    for name, fn in (("stack32", bench_stack32), ("union16", bench_union16), ("verify", bench_verify),
+    for name, fn in (("tiny", bench_tiny), ("stack32", bench_stack32), ("union16", bench_union16), ("verify", bench_verify),
                      ("prefill2048", bench_prefill), ("tiered", bench_tiered), ("int8", bench_int8)):
         if args.only in ("all", name):
             extra[name] = fn(*common)
@@ -510,7 +657,7 @@ def main():
         print(json.dumps(extra), flush=True)
         return
 
-    w, ms_step, kern, other, topp = bench_decode(*common)
+    w, ms_step, kern, other, topp, timing = bench_decode(*common)
     be = w.expert_bytes
     gu_bytes = 2 * (w.d * w.f // 2 + 2 * w.d * w.f // 64)     # gate+up int4 + fp16 scales of one expert
     dn_bytes = be - gu_bytes
@@ -544,6 +691,12 @@ def main():
         "data": "synthetic (seeded int4 gs64 experts, fp16 scales, N(0,1) activations)",
         "config": {"workload": "decode MoE layer d=6144 f=2048 E=256 top-8 + 1 shared, 1 token",
                    "layer_ring": args.ring},
+        "protocol": dict(proto, seed=w.seed, cache_state="experts resident in HBM; %d independently generated "
+                         "layer instances cycled (%.1f GB between reuses of one layer's weights)" % (
+                             args.ring, (args.ring - 1) * (w.E + w.n_shared) * w.expert_bytes / 1e9),
+                         timed="%d steps after %d warmup steps, HIP events on the stream, in 5 consecutive "
+                               "sub-windows" % (args.steps, args.warmup)),
+        "timing": timing,
         "tokens_per_s": round(1e6 / us_token, 1),
         "int4_bytes_per_token": int4_bytes,
         "int4_gbs": round(gbs, 1),
@@ -562,35 +715,73 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(w, budget_s):
-    """The oracle (route + forward, fp64) on a bounded sample of decode tokens."""
+def _omp_threads(n=None):
+    """OpenMP threads the oracle's parallel regions use: sets them when n is
+    given (on this thread), returns the current setting."""
+    import ctypes
+    try:
+        gomp = ctypes.CDLL("libgomp.so.1")
+    except OSError:
+        return None
+    if n is not None:
+        gomp.omp_set_num_threads(int(n))
+    return int(gomp.omp_get_max_threads())
+
+
+def _oracle_tokens(w, budget_s, max_tokens=64):
+    """us per token of the oracle (route + forward, fp64) on decode-shaped
+    tokens of layer instance 0, within about budget_s seconds of oracle time."""
     import numpy as np
 
     import oracle
     import synth
-    oracle.build(force=False)
-    L = 0
-    R = synth.router(w, L)
-    shared = synth.shared_blob(w, L)
-    X = synth.activations(w.with_(T=64), stream=11)
+    R = synth.router(w, 0)
+    b = synth.bias(w, 0)
+    shared = synth.shared_blob(w, 0) if w.n_shared else None
+    X = synth.activations(w.with_(T=max_tokens), stream=11)
     done, t_cpu = 0, 0.0
     blobs = {}
     while done < X.shape[0] and t_cpu < budget_s:
         x = X[done].astype(np.float64)
         t = time.perf_counter()
-        l, idx, wt = oracle.route_token(R, None, x, w.k)
+        l, idx, wt = oracle.route_token(R, b, x, w.k)
         t_cpu += time.perf_counter() - t
         for e in idx:  # input generation is not part of the timed work
             if int(e) not in blobs:
-                blobs[int(e)] = synth.expert_blobs(w, L, int(e), int(e) + 1)[0].copy()
+                blobs[int(e)] = synth.expert_blobs(w, 0, int(e), int(e) + 1)[0].copy()
         t = time.perf_counter()
         oracle.moe_token(x, w.d, w.f, {int(e): blobs[int(e)] for e in idx}, shared, idx, wt, x, w.E)
         t_cpu += time.perf_counter() - t
         done += 1
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    return {"value": round(1e6 * t_cpu / done, 1), "unit": "us/token", "cores": threads, "kind": "oracle",
+    return 1e6 * t_cpu / done, done, t_cpu
+
+
+def cpu_baseline(w, budget_s):
+    """The oracle (route + forward, fp64) on a bounded sample of decode tokens,
+    on the process's cores; then on one core, for the decode and the tiny
+    layer."""
+    import oracle
+    import synth
+    oracle.build(force=False)
+    cores = len(os.sched_getaffinity(0))
+    threads = _omp_threads()
+    us, done, t_cpu = _oracle_tokens(w, budget_s)
+    prev = _omp_threads(1)
+    one = {}
+    for name, ww, budget in (("decode", w, max(4.0, budget_s / 3)), ("tiny", synth.WORKLOADS["tiny"], 1.0)):
+        u1, d1, t1 = _oracle_tokens(ww, budget)
+        one[name] = {"us_per_token": round(u1, 1), "tokens": d1, "seconds": round(t1, 2)}
+    _omp_threads(threads if threads else prev)
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "unknown")
+    except OSError:
+        pass
+    return {"value": round(us, 1), "unit": "us/token", "cores": threads or cores, "kind": "oracle",
             "sample": "%d decode tokens of the same layer shape (layer instance 0), route + 8 routed + shared "
-                      "expert in fp64, %.1f s" % (done, t_cpu)}
+                      "expert in fp64, %.1f s" % (done, t_cpu),
+            "cpu_model": model, "affinity_cores": cores, "omp_threads": threads, "one_core": one}
 
 
 if __name__ == "__main__":
