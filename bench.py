@@ -471,79 +471,90 @@ def bench_verify(args, torch, np, synth, cm, MoeContext, dev, stream):
 
 def bench_tiered(args, torch, np, synth, cm, MoeContext, dev, stream):
     """Tiered placement: the first 4 layers of the stacked-decode recipe kept in
-    pinned host memory, served through an HBM cache of 256 expert slots (a
-    quarter of their 1024 routed experts); one token at a time through the 4
-    layers.  Each layer call copies its routing to the host and streams the
-    missing experts over PCIe, so the time is wall-clock time."""
+    pinned host memory, served through an HBM cache of 256 expert slots (64
+    per layer: a quarter of each layer's 256 routed experts); one token at a
+    time through the 4 layers.  Each layer call copies its routing to the host
+    and streams the missing experts over PCIe, so the time is wall-clock time.
+    Every configuration starts from a fresh cache, is warmed with the same 32
+    tokens and timed on the same 32 other tokens: per-layer LRU alone; with the
+    next layer's router run one layer ahead, prefetching the first `depth`
+    experts of its prediction; and with the learned pin (each layer's most
+    used experts pinned after the warm-up) or automatic repinning on top."""
     w = synth.WORKLOADS["stack32"].with_(n_layers=4)
     slots = 256
-    ctx = MoeContext(w.d, w.f, w.E, w.k, n_layers=w.n_layers, n_shared=w.n_shared, max_tokens=1)
-    ctx.set_expert_cache(slots)
+    per_layer = slots // w.n_layers
+    n_pin = per_layer - w.n_shared - w.k
+    ntok, warm = 32, 32
+    X_warm = torch.from_numpy(synth.activations(w.with_(T=warm), stream=5)).to(dev)
+    X_time = torch.from_numpy(synth.activations(w.with_(T=ntok), stream=6)).to(dev)
+    blobs = [(synth.router(w, l), synth.bias(w, l), synth.expert_blobs(w, l, 0, w.E), synth.shared_blob(w, l))
+             for l in range(w.n_layers)]
+
+    def config(depth, pin=False, autorepin=0):
+        ctx = MoeContext(w.d, w.f, w.E, w.k, n_layers=w.n_layers, n_shared=w.n_shared, max_tokens=1)
+        ctx.set_expert_cache(slots)
+        for l in range(w.n_layers):
+            ctx.load_layer_host(l, *blobs[l])
+        ctx.cache_set_prefetch(depth)
+        if autorepin:
+            ctx.cache_set_autorepin(autorepin, n_pin)
+        idx = torch.empty((w.n_layers, w.k), dtype=torch.int32, device=dev)
+        wts = torch.empty((w.n_layers, w.k), dtype=torch.float32, device=dev)
+        U = ctx.new_union(1)
+
+        def run(X0):
+            r = X0.clone()
+            x = torch.empty_like(X0)
+            a = ctx.cache_info()
+            t = time.perf_counter()
+            for i in range(X0.shape[0]):
+                cm.colimoe_route_forward(ctx.ctx, 0, X0[i].data_ptr(), 1, idx[0].data_ptr(), wts[0].data_ptr(),
+                                         U.abi(), r[i].data_ptr(), cm.COLIMOE_FWD_AUTO)
+                for l in range(1, w.n_layers):
+                    cm.colimoe_rmsnorm_route_forward(ctx.ctx, l, r[i].data_ptr(), 1, 1e-6, x[i].data_ptr(),
+                                                     idx[l].data_ptr(), wts[l].data_ptr(), U.abi(),
+                                                     cm.COLIMOE_FWD_AUTO)
+            ctx.sync()
+            return time.perf_counter() - t, a, ctx.cache_info()
+
+        run(X_warm)
+        if pin:
+            ctx.cache_repin(n_pin)
+        dt, a, b = run(X_time)
+        ctx.close()
+        n = X_time.shape[0]
+        hits, misses = b.hits - a.hits, b.misses - a.misses
+        out = {"us_per_token": round(1e6 * dt / n, 1), "us_per_layer": round(1e6 * dt / n / w.n_layers, 1),
+               "tokens_per_s": round(n / dt, 2), "hit_rate": round(hits / max(hits + misses, 1), 4),
+               "misses_per_token": round(misses / n, 2), "pcie_gbs": round(misses * w.expert_bytes / dt / 1e9, 1)}
+        pr = b.predicted - a.predicted
+        if pr:
+            pf = b.prefetched - a.prefetched
+            out.update({"prediction_hit_rate": round((b.predicted_hits - a.predicted_hits) / pr, 4),
+                        "prefetched_per_token": round(pf / n, 2),
+                        "prefetched_used_per_token": round((b.prefetched_used - a.prefetched_used) / n, 2)})
+        return out
+
     t0 = time.time()
-    for l in range(w.n_layers):
-        ctx.load_layer_host(l, synth.router(w, l), synth.bias(w, l), synth.expert_blobs(w, l, 0, w.E),
-                            synth.shared_blob(w, l))
-    log("tiered: loaded %d host-resident layers (%.1f s)" % (w.n_layers, time.time() - t0))
-    ntok, warm = 32, 8
-    X0 = torch.from_numpy(synth.activations(w.with_(T=ntok + warm), stream=5)).to(dev)
-    r = X0.clone()
-    x = torch.empty_like(X0)
-    idx = torch.empty((w.n_layers, w.k), dtype=torch.int32, device=dev)
-    wts = torch.empty((w.n_layers, w.k), dtype=torch.float32, device=dev)
-    U = ctx.new_union(1)
-
-    def token(i):
-        cm.colimoe_route_forward(ctx.ctx, 0, X0[i].data_ptr(), 1, idx[0].data_ptr(), wts[0].data_ptr(), U.abi(),
-                                 r[i].data_ptr(), cm.COLIMOE_FWD_AUTO)
-        for l in range(1, w.n_layers):
-            cm.colimoe_rmsnorm_route_forward(ctx.ctx, l, r[i].data_ptr(), 1, 1e-6, x[i].data_ptr(), idx[l].data_ptr(),
-                                             wts[l].data_ptr(), U.abi(), cm.COLIMOE_FWD_AUTO)
-
-    for i in range(warm):
-        token(i)
-    ctx.sync()
-    h0, m0, _ = ctx.cache_stats()
-    t = time.perf_counter()
-    for i in range(warm, warm + ntok):
-        token(i)
-    ctx.sync()
-    dt = time.perf_counter() - t
-    h1, m1, _ = ctx.cache_stats()
-    # learned pinning: the 3/4 of the slots the run so far used most stay put
-    ctx.cache_repin(3 * slots // 4)
-    X1 = torch.from_numpy(synth.activations(w.with_(T=ntok), stream=6)).to(dev)
-    r1 = X1.clone()
-    x1 = torch.empty_like(X1)
-
-    def token1(i):
-        cm.colimoe_route_forward(ctx.ctx, 0, X1[i].data_ptr(), 1, idx[0].data_ptr(), wts[0].data_ptr(), U.abi(),
-                                 r1[i].data_ptr(), cm.COLIMOE_FWD_AUTO)
-        for l in range(1, w.n_layers):
-            cm.colimoe_rmsnorm_route_forward(ctx.ctx, l, r1[i].data_ptr(), 1, 1e-6, x1[i].data_ptr(),
-                                             idx[l].data_ptr(), wts[l].data_ptr(), U.abi(), cm.COLIMOE_FWD_AUTO)
-
-    t = time.perf_counter()
-    for i in range(ntok):
-        token1(i)
-    ctx.sync()
-    dt1 = time.perf_counter() - t
-    h2, m2, _ = ctx.cache_stats()
-    ctx.close()
-    del ctx, X0, r, x, X1, r1, x1
+    res = {"lru": config(0)}
+    for depth in (1, 2, 4, w.k):
+        res["prefetch%d" % depth] = config(depth)
+    best = min((1, 2, 4, w.k), key=lambda d: res["prefetch%d" % d]["us_per_token"])
+    res["learned_pin"] = config(0, pin=True)
+    res["learned_pin_prefetch%d" % best] = config(best, pin=True)
+    res["autorepin8_prefetch%d" % best] = config(best, autorepin=8)
+    log("tiered: %d configurations in %.1f s" % (len(res), time.time() - t0))
+    top = res["learned_pin_prefetch%d" % best]
+    del X_warm, X_time, blobs
     torch.cuda.empty_cache()
-    ph, pm = h2 - h1, m2 - m1
-    pinned = {"pinned": 3 * slots // 4, "us_per_token": round(1e6 * dt1 / ntok, 1),
-              "hit_rate": round(ph / max(ph + pm, 1), 4), "misses_per_token": round(pm / ntok, 2)}
-    hits, misses = h1 - h0, m1 - m0
     return {"workload": "tiered placement: 4 layers of the stacked-decode recipe (d=6144 f=2048 E=256 top-8 + shared, "
                         "Zipf(1.1) bias, RMSNorm between) with routed experts in pinned host memory (%.1f GB), an HBM "
-                        "cache of %d expert slots (%.1f GB), 1 token" % (w.n_layers * w.E * w.expert_bytes / 1e9, slots,
-                                                                         slots * w.expert_bytes / 1e9),
-            "us_per_token": round(1e6 * dt / ntok, 1), "us_per_layer": round(1e6 * dt / ntok / w.n_layers, 1),
-            "tokens_per_s": round(ntok / dt, 2), "hit_rate": round(hits / max(hits + misses, 1), 4),
-            "misses_per_token": round(misses / ntok, 2),
-            "pcie_gbs": round(misses * w.expert_bytes / dt / 1e9, 1), "tokens_timed": ntok,
-            "after_repin": pinned}
+                        "cache of %d expert slots (%.1f GB, %d per layer), 1 token; each configuration from a fresh "
+                        "cache, warmed on the same %d tokens, timed on the same %d others" % (
+                            w.n_layers * w.E * w.expert_bytes / 1e9, slots, slots * w.expert_bytes / 1e9,
+                            per_layer, warm, ntok),
+            "configs": res, "pinned_per_layer": n_pin, "best_prefetch_depth": best,
+            "us_per_token": top["us_per_token"], "hit_rate": top["hit_rate"]}
 
 
 def bench_int8(args, torch, np, synth, cm, MoeContext, dev, stream):

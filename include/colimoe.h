@@ -178,52 +178,105 @@ COLIMOE_API int colimoe_load_experts(colimoe_ctx *ctx, int32_t layer, const coli
 
 /* Tiered placement for models whose experts do not all fit in HBM ([A] §2:
  * parameters are data moved between tiers by how often routing asks for them,
- * with a per-layer LRU cache; [D] §3: the routed experts stay on disk and are
- * read on demand into an LRU cache; here host RAM over PCIe plays the disk and
- * HBM the RAM).
+ * with a per-layer LRU cache, a learned hot set saved between runs, and the
+ * next layer's router run one layer ahead; [D] §3: the routed experts stay on
+ * disk and are read on demand into an LRU cache; [D] key tuning parameters:
+ * --repin N re-places the hot experts every N tokens.  Here host RAM over
+ * PCIe plays the disk and HBM the RAM).
  *
  * colimoe_expert_cache_bytes: device bytes of an expert cache of n_slots
- * slots (slot maps of every layer, then the slots); 0 for a bad config or
- * n_slots < 1.  colimoe_host_layer_bytes: device bytes of a host-resident
- * layer (router and bias only).
+ * slots (slot maps of every layer, a prediction scratch, then the slots); 0
+ * for a bad config or n_slots < 1.  colimoe_host_layer_bytes: device bytes of
+ * a host-resident layer (router and bias only).
  *
  * colimoe_set_expert_cache: the caller-owned device buffer (256-byte aligned)
  * the cache lives in, before any host-resident layer is loaded (E_STATE once
- * one is).  Errors: E_ARG, E_STATE, E_WORKSPACE (room for less than one
- * slot), E_HIP.
+ * one is).  The slots are split evenly among the context's n_layers layers:
+ * layer l owns slots_per_layer = n_slots / n_layers of them, with its own
+ * least-recently-used order, so a layer's calls never evict another layer's
+ * experts (a partition of a layer resident in HBM stays unused).  Resets all
+ * counters and usage histograms.  Creates the two streams (default priority)
+ * and the events the prefetch uses.  Errors: E_ARG, E_STATE, E_WORKSPACE
+ * (room for less than one slot), E_HIP.
  *
  * colimoe_load_experts_host: as colimoe_load_experts, but the routed experts
  * are repacked into pinned host memory owned by the context (freed by
  * colimoe_destroy or when the layer is loaded again); router and bias go to
- * dev_dst (colimoe_host_layer_bytes); the shared expert takes a cache slot of
- * its own for the layer's lifetime.  A forward on such a layer first copies
- * the routing to the host (this synchronises the stream), brings each missing
- * expert into the least recently used slot the call does not need, and then
- * runs the same kernels, reading every expert from the cache: results are
- * bit-identical to the layer loaded with colimoe_load_experts.  A call whose
- * routing names more distinct experts than there are free slots returns
+ * dev_dst (colimoe_host_layer_bytes); the shared expert takes the first slot
+ * of the layer's partition for the layer's lifetime.  A forward on such a
+ * layer first copies the routing to the host (this synchronises the stream),
+ * adds the routing to the layer's usage histogram (tokens routed to each
+ * expert), brings each missing expert into the least recently used
+ * evictable slot of the layer's partition that the call does not need, and
+ * then runs the same kernels, reading every expert from the cache: results
+ * are bit-identical to the layer loaded with colimoe_load_experts.  A call
+ * whose routing needs more evictable slots than the partition has returns
  * E_WORKSPACE.  colimoe_debug_expert on such a layer returns E_STATE.
- * Errors: E_ARG, E_SHAPE, E_STATE (no cache), E_WORKSPACE (cache too small for
- * the shared expert and one token's experts), E_HIP.
+ * Errors: E_ARG, E_SHAPE, E_STATE (no cache), E_WORKSPACE (slots_per_layer <
+ * n_shared + top_k: no room for one token's experts), E_HIP.
+ *
+ * colimoe_cache_set_prefetch: one-layer-ahead prediction ([A] §2).  With
+ * depth > 0, a forward call of up to 16 tokens on host-resident layer l whose
+ * next layer l + 1 is host-resident also runs layer l + 1's router and top-k
+ * on the call's input x (the router "one layer ahead"), on the cache's side
+ * stream while layer l's kernels run; the host waits for that prediction
+ * only, then starts copying, over PCIe on the cache's copy stream, the first
+ * `depth` experts of each token's predicted top-k (its largest predicted
+ * logits) that are absent from layer l + 1's partition.  A later call reading
+ * or evicting such a slot waits for its copy only.  depth = 0 (the default)
+ * turns prediction off; 1 <= depth <= top_k.  Prediction changes which experts
+ * are in the cache, never the results.  Errors: E_ARG (depth out of range),
+ * E_STATE (no cache).
  *
  * colimoe_cache_repin: learned pinning ([A] §2: the engine records which
- * experts the workload routes to and pins the hottest; [D] key tuning
- * parameters, --repin N: the hot experts are re-placed every N tokens).  The cache counts, per host-resident layer and
- * expert, the calls that needed it; this call pins the n experts counted most
- * often (ties to the lower layer, then the lower id) in the cache, loading
- * the absent ones, and unpins the rest; pinned experts are never evicted.
- * Synchronises the stream.  Errors: E_ARG, E_STATE (no cache), E_WORKSPACE
- * (n leaves fewer free slots than one token's k experts), E_HIP.
+ * experts the workload routes to and pins the hottest).  For every
+ * host-resident layer, pins the n experts of its usage histogram with the
+ * most tokens (ties to the lower id) in its partition, loading the absent
+ * ones, and unpins the rest; pinned experts are never evicted.  Synchronises
+ * the stream.  Errors: E_ARG, E_STATE (no cache), E_WORKSPACE (n > slots_per_layer
+ * - n_shared - top_k: one token's experts must still fit), E_HIP.
  *
- * colimoe_cache_stats: experts found in the cache and brought in since the
- * cache was set, and its number of slots.  Errors: E_ARG. */
+ * colimoe_cache_set_autorepin: repins a layer by itself ([D] key tuning
+ * parameters, --repin N): every every_tokens tokens a host-resident layer has
+ * served, its forward call first repins it with n (capped at slots_per_layer
+ * - n_shared - top_k).  every_tokens = 0 turns it off (the default).
+ * Errors: E_ARG, E_STATE (no cache), E_WORKSPACE (n too large).
+ *
+ * colimoe_cache_usage: the usage histogram of one layer (E counts: tokens
+ * routed to each expert since the cache was set or the histogram loaded).
+ * colimoe_cache_usage_save / _load: the histograms of all layers to / from a
+ * file (the learned hot set kept between runs): 8 bytes "COLIUSE1", int32
+ * n_layers, int32 E, then n_layers * E uint32 counts, little-endian.  Load
+ * replaces the counts (a repin then pins by them).  Errors: E_ARG (null,
+ * unreadable or unwritable file, not a usage file, truncated), E_SHAPE (the
+ * file's layers or experts differ), E_STATE (no cache).
+ *
+ * colimoe_cache_stats: experts found in the cache and brought in on demand
+ * since the cache was set, and its number of slots.  colimoe_cache_get_info:
+ * those and the prediction figures: predicted = routed experts of calls that
+ * had a prediction, predicted_hits = how many of them its full top-k named
+ * (their ratio is the prediction hit rate); prefetched = experts copied ahead, and
+ * prefetched_used = how many of those a call then needed; slots,
+ * slots_per_layer, pinned (slots holding pinned experts).  Errors: E_ARG. */
+typedef struct colimoe_cache_info {
+  int64_t hits, misses;
+  int64_t predicted, predicted_hits;
+  int64_t prefetched, prefetched_used;
+  int32_t slots, slots_per_layer, pinned;
+} colimoe_cache_info;
 COLIMOE_API size_t colimoe_expert_cache_bytes(const colimoe_config *cfg, int32_t n_slots);
 COLIMOE_API size_t colimoe_host_layer_bytes(const colimoe_config *cfg);
 COLIMOE_API int colimoe_set_expert_cache(colimoe_ctx *ctx, void *dev, size_t bytes);
 COLIMOE_API int colimoe_load_experts_host(colimoe_ctx *ctx, int32_t layer, const colimoe_layer_src *src, void *dev_dst,
                               size_t dev_bytes);
+COLIMOE_API int colimoe_cache_set_prefetch(colimoe_ctx *ctx, int32_t depth);
 COLIMOE_API int colimoe_cache_repin(colimoe_ctx *ctx, int32_t n);
+COLIMOE_API int colimoe_cache_set_autorepin(colimoe_ctx *ctx, int32_t every_tokens, int32_t n);
+COLIMOE_API int colimoe_cache_usage(colimoe_ctx *ctx, int32_t layer, uint32_t *counts);
+COLIMOE_API int colimoe_cache_usage_save(colimoe_ctx *ctx, const char *path);
+COLIMOE_API int colimoe_cache_usage_load(colimoe_ctx *ctx, const char *path);
 COLIMOE_API int colimoe_cache_stats(colimoe_ctx *ctx, int64_t *hits, int64_t *misses, int32_t *slots);
+COLIMOE_API int colimoe_cache_get_info(colimoe_ctx *ctx, colimoe_cache_info *out);
 
 /* Route T tokens ([A] §1 background: a router picks 8 of the 256 experts of
  * a layer per token; [A] §4: routing is never changed silently, so the

@@ -36,7 +36,8 @@ EXPORTED = [
     "colimoe_union_build", "colimoe_forward", "colimoe_route_forward", "colimoe_rmsnorm_route_forward", "colimoe_rmsnorm", "colimoe_debug_expert", "colimoe_sync", "colimoe_status_str",
     "colimoe_timing_enable", "colimoe_timing_read", "colimoe_set_expert_top_p", "colimoe_expert_cache_bytes",
     "colimoe_host_layer_bytes", "colimoe_set_expert_cache", "colimoe_load_experts_host", "colimoe_cache_stats",
-    "colimoe_cache_repin", "colimoe_route_forward_static",
+    "colimoe_cache_repin", "colimoe_route_forward_static", "colimoe_cache_set_prefetch", "colimoe_cache_set_autorepin",
+    "colimoe_cache_usage", "colimoe_cache_usage_save", "colimoe_cache_usage_load", "colimoe_cache_get_info",
 ]
 
 
@@ -54,6 +55,12 @@ class colimoe_layer_src(ctypes.Structure):
 class colimoe_union(ctypes.Structure):
     _fields_ = [("n_unique", ctypes.c_void_p), ("ids", ctypes.c_void_p), ("offsets", ctypes.c_void_p),
                 ("pair_token", ctypes.c_void_p), ("pair_slot", ctypes.c_void_p), ("pair_of", ctypes.c_void_p)]
+
+
+class colimoe_cache_info(ctypes.Structure):
+    _fields_ = [("hits", ctypes.c_int64), ("misses", ctypes.c_int64), ("predicted", ctypes.c_int64),
+                ("predicted_hits", ctypes.c_int64), ("prefetched", ctypes.c_int64), ("prefetched_used", ctypes.c_int64),
+                ("slots", ctypes.c_int32), ("slots_per_layer", ctypes.c_int32), ("pinned", ctypes.c_int32)]
 
 
 class ColimoeError(RuntimeError):
@@ -103,6 +110,18 @@ def lib() -> ctypes.CDLL:
         L.colimoe_cache_stats.restype = ctypes.c_int
         L.colimoe_cache_repin.argtypes = [vp, i32]
         L.colimoe_cache_repin.restype = ctypes.c_int
+        L.colimoe_cache_set_prefetch.argtypes = [vp, i32]
+        L.colimoe_cache_set_prefetch.restype = ctypes.c_int
+        L.colimoe_cache_set_autorepin.argtypes = [vp, i32, i32]
+        L.colimoe_cache_set_autorepin.restype = ctypes.c_int
+        L.colimoe_cache_usage.argtypes = [vp, i32, vp]
+        L.colimoe_cache_usage.restype = ctypes.c_int
+        L.colimoe_cache_usage_save.argtypes = [vp, ctypes.c_char_p]
+        L.colimoe_cache_usage_save.restype = ctypes.c_int
+        L.colimoe_cache_usage_load.argtypes = [vp, ctypes.c_char_p]
+        L.colimoe_cache_usage_load.restype = ctypes.c_int
+        L.colimoe_cache_get_info.argtypes = [vp, ctypes.POINTER(colimoe_cache_info)]
+        L.colimoe_cache_get_info.restype = ctypes.c_int
         L.colimoe_route.argtypes = [vp, i32, vp, i32, vp, vp, ctypes.POINTER(colimoe_union), vp]
         L.colimoe_route.restype = ctypes.c_int
         L.colimoe_union_build.argtypes = [vp, vp, i32, ctypes.POINTER(colimoe_union)]
@@ -218,6 +237,38 @@ def colimoe_set_expert_cache(ctx, dev_ptr: int, nbytes: int, check: bool = True)
 def colimoe_cache_repin(ctx, n: int, check: bool = True) -> int:
     rc = lib().colimoe_cache_repin(ctx, n)
     return _check("colimoe_cache_repin", rc) if check else rc
+
+
+def colimoe_cache_set_prefetch(ctx, depth: int, check: bool = True) -> int:
+    rc = lib().colimoe_cache_set_prefetch(ctx, int(depth))
+    return _check("colimoe_cache_set_prefetch", rc) if check else rc
+
+
+def colimoe_cache_set_autorepin(ctx, every_tokens: int, n: int, check: bool = True) -> int:
+    rc = lib().colimoe_cache_set_autorepin(ctx, every_tokens, n)
+    return _check("colimoe_cache_set_autorepin", rc) if check else rc
+
+
+def colimoe_cache_usage(ctx, layer: int, counts_ptr: int, check: bool = True) -> int:
+    """Writes the layer's E usage counts (uint32) to host memory at counts_ptr."""
+    rc = lib().colimoe_cache_usage(ctx, layer, counts_ptr)
+    return _check("colimoe_cache_usage", rc) if check else rc
+
+
+def colimoe_cache_usage_save(ctx, path: str, check: bool = True) -> int:
+    rc = lib().colimoe_cache_usage_save(ctx, path.encode())
+    return _check("colimoe_cache_usage_save", rc) if check else rc
+
+
+def colimoe_cache_usage_load(ctx, path: str, check: bool = True) -> int:
+    rc = lib().colimoe_cache_usage_load(ctx, path.encode())
+    return _check("colimoe_cache_usage_load", rc) if check else rc
+
+
+def colimoe_cache_get_info(ctx) -> colimoe_cache_info:
+    info = colimoe_cache_info()
+    _check("colimoe_cache_get_info", lib().colimoe_cache_get_info(ctx, ctypes.byref(info)))
+    return info
 
 
 def colimoe_cache_stats(ctx):

@@ -7,7 +7,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libcolimoe.so")
-SOURCES = [os.path.join(CSRC, "host.cpp"), os.path.join(CSRC, "kernels.hip"), os.path.join(CSRC, "kernels_mfma.hip")]
+SOURCES = [os.path.join(CSRC, "host.cpp"), os.path.join(CSRC, "cache.cpp"), os.path.join(CSRC, "kernels.hip"),
+           os.path.join(CSRC, "kernels_mfma.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

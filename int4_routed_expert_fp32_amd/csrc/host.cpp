@@ -13,55 +13,10 @@
 #include <thread>
 #include <vector>
 
-#include "../../include/colimoe.h"
-#include "internal.h"
+#include "context.h"
 
 using namespace colimoe;
 
-struct colimoe_ctx {
-  colimoe_config cfg;
-  hipStream_t stream;
-  int device;
-  std::vector<LayerDev> layers;
-  std::vector<char> loaded;
-  // Tiered placement: routed experts of host-resident layers live in pinned
-  // host memory (device layout) and move into an HBM cache of fixed slots on
-  // demand, least recently used out.
-  std::vector<uint8_t *> host_store;  // per layer: E * expert bytes, or null
-  struct Cache {
-    uint8_t *slots = nullptr;      // device: n_slots * expert bytes
-    int32_t *dev_maps = nullptr;   // device: [n_layers][E + 1] slot of each expert
-    int32_t *stage = nullptr;      // pinned host copy of the maps as uploaded
-    int32_t *idx_host = nullptr;   // pinned host: a call's routing
-    int n_slots = 0;
-    std::vector<int32_t> slot_of;  // [n_layers][E + 1]: slot or -1
-    std::vector<int64_t> tag;      // per slot: layer * (E + 1) + expert, or -1
-    std::vector<uint64_t> used;    // per slot: call stamp of the last use
-    std::vector<char> fixed;       // per slot: 1 holds a shared expert, 2 a pinned expert (neither evicted)
-    std::vector<uint32_t> uses;    // [n_layers][E + 1]: calls that needed each expert
-    uint64_t stamp = 0;
-    int64_t hits = 0, misses = 0;
-  } cache;
-  uint8_t *ws;
-  size_t ws_bytes;
-  bool static_used;  // colimoe_route_forward_static has run on this context
-  float top_p;  // adaptive expert top-p of one-token routing (1: off)
-  Workspace wl;
-  ExpertLayout el;
-  uint8_t *staging[2];  // pinned host buffers for the loader
-  size_t staging_bytes;
-  // kernel timing
-  bool timing;
-  std::vector<hipEvent_t> ev_pool;
-  size_t ev_used;
-  struct Rec {
-    int kid;
-    hipEvent_t a, b;
-  };
-  std::vector<Rec> recs;
-  double tot_ms[16];
-  long long cnt[16];
-};
 
 namespace {
 // "route": the fused route kernel, or the router GEMV/GEMM when top-k runs apart.
@@ -112,10 +67,7 @@ int drain_timing(colimoe_ctx *c) {
 }
 }  // namespace
 
-namespace {
-
-constexpr size_t kAlign = 256;
-inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+namespace colimoe {
 
 bool cfg_ok(const colimoe_config *c) {
   if (!c) return false;
@@ -141,12 +93,6 @@ size_t router_bytes(const colimoe_config *c) {
   return align_up((size_t)c->n_experts * c->d * 4, kAlign) + align_up((size_t)c->n_experts * 4, kAlign);
 }
 
-bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
-
-int hip_status(hipError_t e) { return e == hipSuccess ? COLIMOE_OK : COLIMOE_E_HIP; }
-
-LayerDev layer_of(colimoe_ctx *ctx, int layer) { return ctx->layers[layer]; }
-
 Dims dims_of(const colimoe_ctx *ctx, int T) {
   Dims D;
   D.d = ctx->cfg.d;
@@ -157,6 +103,12 @@ Dims dims_of(const colimoe_ctx *ctx, int T) {
   D.n_shared = ctx->cfg.n_shared;
   return D;
 }
+
+}  // namespace colimoe
+
+namespace {
+
+LayerDev layer_of(colimoe_ctx *ctx, int layer) { return ctx->layers[layer]; }
 
 UnionDev ws_union(colimoe_ctx *ctx) {
   UnionDev U;
@@ -196,6 +148,10 @@ int check_call(colimoe_ctx *ctx, int32_t layer, int32_t T) {
   return COLIMOE_OK;
 }
 
+}  // namespace
+
+namespace colimoe {
+
 // ---------------------------------------------------------------- repacking
 // Canonical blob -> device layout (internal.h): gate/up rows interleaved in
 // tiles of 4+4, nibbles of a tile stored step-major, scales regrouped per
@@ -203,7 +159,7 @@ int check_call(colimoe_ctx *ctx, int32_t layer, int32_t T) {
 
 // Copies one canonical row of K nibbles into tile row r of tile `tile` of a
 // device matrix (step-major tiles).
-inline void put_row(uint8_t *dst_nib, const uint8_t *src_row, int tile, int r, int K) {
+static inline void put_row(uint8_t *dst_nib, const uint8_t *src_row, int tile, int r, int K) {
   const int C = K / kChunk;
   for (int c0 = 0; c0 < C; c0 += 64) {
     const int width = std::min(64, C - c0);
@@ -259,10 +215,6 @@ void repack_many(const uint8_t *const *srcs, uint8_t *dst, int n, size_t be, int
     });
   for (auto &x : th) x.join();
 }
-
-}  // namespace
-
-namespace colimoe {
 
 Workspace workspace_layout(int d, int f, int E, int k, int n_shared, int max_tokens) {
   Workspace W;
@@ -379,98 +331,12 @@ static int route_impl(colimoe_ctx *ctx, int32_t layer, const float *x, int32_t T
 
 // Expert work and combine.  x_encoded: the workspace already holds the
 // fixed-point encoding of this x (written by the route kernel).
-// Tiered placement: makes every expert of routing idx [T][k] (device) of a
-// host-resident layer present in the HBM cache.  Copies the routing to the
-// host (synchronising the stream, so no earlier kernel still reads a slot),
-// counts hits, brings each missing expert in over PCIe into the slot used
-// least recently (never one this call needs, never a shared expert's), and
-// uploads the layer's slot map.  A map entry of an expert not in the cache
-// points at the layer's shared-expert slot, so every address a kernel forms
-// stays inside the cache.  E_WORKSPACE if the call needs more experts than
-// the cache has slots for.
-static int ensure_resident(colimoe_ctx *ctx, int32_t layer, const int32_t *idx, int32_t T) {
-  colimoe_ctx::Cache &C = ctx->cache;
-  const int E = ctx->cfg.n_experts, k = ctx->cfg.top_k;
-  const size_t be = ctx->el.bytes;
-  hipStream_t s = ctx->stream;
-  if (hipMemcpyAsync(C.idx_host, idx, (size_t)T * k * 4, hipMemcpyDeviceToHost, s) != hipSuccess ||
-      hipStreamSynchronize(s) != hipSuccess)
-    return COLIMOE_E_HIP;
-  std::vector<int> need;
-  for (int i = 0; i < T * k; ++i) {
-    const int e = C.idx_host[i];
-    if (e >= 0 && e < E) need.push_back(e);
-  }
-  std::sort(need.begin(), need.end());
-  need.erase(std::unique(need.begin(), need.end()), need.end());
-  int32_t *map = &C.slot_of[(size_t)layer * (E + 1)];
-  // the call's experts that must sit in evictable slots: the misses, and the
-  // hits that already sit in one (a pinned expert's slot is not evictable and
-  // is not counted)
-  int free_slots = 0, want_free = 0;
-  for (int i = 0; i < C.n_slots; ++i) free_slots += !C.fixed[i];
-  for (int e : need) want_free += map[e] < 0 || !C.fixed[map[e]];
-  if (want_free > free_slots) return COLIMOE_E_WORKSPACE;
-  const uint64_t now = ++C.stamp;
-  for (int e : need) C.uses[(size_t)layer * (E + 1) + e] += 1;
-  for (int e : need)
-    if (map[e] >= 0) {
-      C.used[map[e]] = now;
-      ++C.hits;
-    }
-  for (int e : need) {
-    if (map[e] >= 0) continue;
-    int victim = -1;
-    for (int i = 0; i < C.n_slots; ++i)
-      if (!C.fixed[i] && C.used[i] != now && (victim < 0 || C.used[i] < C.used[victim])) victim = i;
-    if (victim < 0) return COLIMOE_E_WORKSPACE;
-    if (C.tag[victim] >= 0) C.slot_of[(size_t)C.tag[victim]] = -1;
-    if (hipMemcpyAsync(C.slots + (size_t)victim * be, ctx->host_store[layer] + (size_t)e * be, be,
-                       hipMemcpyHostToDevice, s) != hipSuccess)
-      return COLIMOE_E_HIP;
-    C.tag[victim] = (int64_t)layer * (E + 1) + e;
-    C.used[victim] = now;
-    map[e] = victim;
-    ++C.misses;
-  }
-  int32_t *st = C.stage + (size_t)layer * (E + 1);
-  const int dummy = map[E] >= 0 ? map[E] : 0;
-  for (int e = 0; e <= E; ++e) st[e] = map[e] >= 0 ? map[e] : dummy;
-  return hip_status(hipMemcpyAsync(C.dev_maps + (size_t)layer * (E + 1), st, (size_t)(E + 1) * 4,
-                                   hipMemcpyHostToDevice, s));
-}
-
-// Forgets a layer's place in the expert cache (its routed experts and its
-// shared-expert slot) and frees its host store.
-static void cache_drop_layer(colimoe_ctx *ctx, int32_t layer) {
-  colimoe_ctx::Cache &C = ctx->cache;
-  const int E = ctx->cfg.n_experts;
-  for (int i = 0; i < C.n_slots; ++i)
-    if (C.tag[i] >= 0 && C.tag[i] / (E + 1) == layer) {
-      C.tag[i] = -1;
-      C.used[i] = 0;
-      C.fixed[i] = 0;
-    }
-  if (!C.slot_of.empty())
-    for (int e = 0; e <= E; ++e) {
-      C.slot_of[(size_t)layer * (E + 1) + e] = -1;
-      C.uses[(size_t)layer * (E + 1) + e] = 0;
-    }
-  if (ctx->host_store[layer]) {
-    (void)hipHostFree(ctx->host_store[layer]);
-    ctx->host_store[layer] = nullptr;
-  }
-}
-
-static int forward_impl(colimoe_ctx *ctx, int32_t layer, const float *x, int32_t T, const int32_t *idx, const float *w,
+static int forward_kernels(colimoe_ctx *ctx, int32_t layer, const float *x, int32_t T, const int32_t *idx, const float *w,
                  const colimoe_union *u, float *residual, int path, bool x_encoded) {
   const Dims D = dims_of(ctx, T);
   const LayerDev L = layer_of(ctx, layer);
   hipStream_t s = ctx->stream;
-  if (ctx->host_store[layer]) {
-    const int rc = ensure_resident(ctx, layer, idx, T);
-    if (rc) return rc;
-  }
+
   UnionDev U;
   if (u) {
     U = to_dev(u);
@@ -544,6 +410,24 @@ static int forward_impl(colimoe_ctx *ctx, int32_t layer, const float *x, int32_t
   return COLIMOE_OK;
 }
 
+// On a host-resident layer the call's experts are first made present in the
+// HBM cache; then, with prefetch on, the next layer's router starts on x (one
+// layer ahead) beside this layer's kernels, and its predicted experts start
+// moving into the cache once the prediction is in.
+static int forward_impl(colimoe_ctx *ctx, int32_t layer, const float *x, int32_t T, const int32_t *idx, const float *w,
+                        const colimoe_union *u, float *residual, int path, bool x_encoded) {
+  int predicting = 0;
+  if (ctx->host_store[layer]) {
+    const int rc = cache_ensure_resident(ctx, layer, idx, T);
+    if (rc) return rc;
+    predicting = cache_predict_start(ctx, layer, x, T);
+    if (predicting < 0) return predicting;
+  }
+  const int rc = forward_kernels(ctx, layer, x, T, idx, w, u, residual, path, x_encoded);
+  const int rp = predicting ? cache_prefetch_issue(ctx, layer, T) : COLIMOE_OK;
+  return rc ? rc : rp;
+}
+
 extern "C" {
 
 const char *colimoe_status_str(int s) {
@@ -613,10 +497,7 @@ int colimoe_create(const colimoe_config *cfg, void *hip_stream, colimoe_ctx **ou
 
 void colimoe_destroy(colimoe_ctx *ctx) {
   if (!ctx) return;
-  for (uint8_t *h : ctx->host_store)
-    if (h) (void)hipHostFree(h);
-  if (ctx->cache.stage) (void)hipHostFree(ctx->cache.stage);
-  if (ctx->cache.idx_host) (void)hipHostFree(ctx->cache.idx_host);
+  cache_release(ctx);
   for (int i = 0; i < 2; ++i)
     if (ctx->staging[i]) (void)hipHostFree(ctx->staging[i]);
   for (hipEvent_t e : ctx->ev_pool) (void)hipEventDestroy(e);
@@ -714,196 +595,6 @@ int colimoe_load_experts(colimoe_ctx *ctx, int32_t layer, const colimoe_layer_sr
   if (rc != COLIMOE_OK) return rc;
   ctx->layers[layer] = LayerDev{router, bias, experts, be, nullptr};
   ctx->loaded[layer] = 1;
-  return COLIMOE_OK;
-}
-
-size_t colimoe_host_layer_bytes(const colimoe_config *cfg) {
-  if (!cfg_ok(cfg)) return 0;
-  return router_bytes(cfg);
-}
-
-size_t colimoe_expert_cache_bytes(const colimoe_config *cfg, int32_t n_slots) {
-  if (!cfg_ok(cfg) || n_slots < 1) return 0;
-  return align_up((size_t)cfg->n_layers * (cfg->n_experts + 1) * 4, kAlign) +
-         (size_t)n_slots * cfg_expert_bytes(cfg);
-}
-
-int colimoe_set_expert_cache(colimoe_ctx *ctx, void *dev, size_t bytes) {
-  if (!ctx || !dev || !aligned(dev, kAlign)) return COLIMOE_E_ARG;
-  for (uint8_t *h : ctx->host_store)
-    if (h) return COLIMOE_E_STATE;  // the cache cannot move under host-resident layers
-  const colimoe_config *c = &ctx->cfg;
-  const size_t maps = align_up((size_t)c->n_layers * (c->n_experts + 1) * 4, kAlign);
-  const size_t be = ctx->el.bytes;
-  if (bytes < maps + be) return COLIMOE_E_WORKSPACE;
-  colimoe_ctx::Cache &C = ctx->cache;
-  if (!C.stage && hipHostMalloc((void **)&C.stage, (size_t)c->n_layers * (c->n_experts + 1) * 4,
-                                hipHostMallocDefault) != hipSuccess)
-    return COLIMOE_E_HIP;
-  if (!C.idx_host && hipHostMalloc((void **)&C.idx_host, (size_t)c->max_tokens * c->top_k * 4,
-                                   hipHostMallocDefault) != hipSuccess)
-    return COLIMOE_E_HIP;
-  C.dev_maps = (int32_t *)dev;
-  C.slots = (uint8_t *)dev + maps;
-  C.n_slots = (int)std::min<size_t>((bytes - maps) / be, (size_t)1 << 30);
-  C.slot_of.assign((size_t)c->n_layers * (c->n_experts + 1), -1);
-  C.tag.assign(C.n_slots, -1);
-  C.used.assign(C.n_slots, 0);
-  C.fixed.assign(C.n_slots, 0);
-  C.uses.assign((size_t)c->n_layers * (c->n_experts + 1), 0);
-  C.stamp = 0;
-  C.hits = C.misses = 0;
-  return COLIMOE_OK;
-}
-
-int colimoe_load_experts_host(colimoe_ctx *ctx, int32_t layer, const colimoe_layer_src *src, void *dev_dst,
-                              size_t dev_bytes) {
-  if (!ctx || !src || !dev_dst || !src->router || !src->experts) return COLIMOE_E_ARG;
-  const colimoe_config *c = &ctx->cfg;
-  if (layer < 0 || layer >= c->n_layers) return COLIMOE_E_SHAPE;
-  if ((c->n_shared == 1) != (src->shared != nullptr)) return COLIMOE_E_ARG;
-  if (!aligned(dev_dst, kAlign)) return COLIMOE_E_ARG;
-  if (dev_bytes < router_bytes(c)) return COLIMOE_E_SHAPE;
-  colimoe_ctx::Cache &C = ctx->cache;
-  if (!C.slots) return COLIMOE_E_STATE;  // colimoe_set_expert_cache first
-  const int E = c->n_experts;
-  const size_t be = ctx->el.bytes;
-  hipStream_t s = ctx->stream;
-  ctx->loaded[layer] = 0;
-  cache_drop_layer(ctx, layer);
-  // the shared expert takes a slot of its own for as long as the layer lives
-  int sslot = -1;
-  if (c->n_shared) {
-    for (int i = 0; i < C.n_slots && sslot < 0; ++i)
-      if (!C.fixed[i] && C.tag[i] < 0) sslot = i;  // an empty slot, else the least recently used
-    if (sslot < 0)
-      for (int i = 0; i < C.n_slots; ++i)
-        if (!C.fixed[i] && (sslot < 0 || C.used[i] < C.used[sslot])) sslot = i;
-    if (sslot < 0) return COLIMOE_E_WORKSPACE;
-    int free_after = 0;
-    for (int i = 0; i < C.n_slots; ++i) free_after += !C.fixed[i] && i != sslot;
-    if (free_after < c->top_k) return COLIMOE_E_WORKSPACE;  // room for one token's experts
-  }
-  float *router = (float *)dev_dst;
-  float *bias = (float *)((uint8_t *)dev_dst + align_up((size_t)E * c->d * 4, kAlign));
-  if (hipMemcpyAsync(router, src->router, (size_t)E * c->d * 4, hipMemcpyHostToDevice, s) != hipSuccess)
-    return COLIMOE_E_HIP;
-  if (src->bias) {
-    if (hipMemcpyAsync(bias, src->bias, (size_t)E * 4, hipMemcpyHostToDevice, s) != hipSuccess) return COLIMOE_E_HIP;
-  } else if (hipMemsetAsync(bias, 0, (size_t)E * 4, s) != hipSuccess) {
-    return COLIMOE_E_HIP;
-  }
-  uint8_t *store = nullptr;
-  if (hipHostMalloc((void **)&store, (size_t)E * be, hipHostMallocDefault) != hipSuccess) return COLIMOE_E_HIP;
-  std::vector<const uint8_t *> srcs(E);
-  for (int e = 0; e < E; ++e) srcs[e] = src->experts + (size_t)e * be;
-  if (c->flags & COLIMOE_CFG_INT8)
-    copy_many(srcs.data(), store, E, be);
-  else
-    repack_many(srcs.data(), store, E, be, c->d, c->f);
-  int32_t *map = &C.slot_of[(size_t)layer * (E + 1)];
-  if (c->n_shared) {
-    uint8_t *tmp = nullptr;
-    if (hipHostMalloc((void **)&tmp, be, hipHostMallocDefault) != hipSuccess) {
-      (void)hipHostFree(store);
-      return COLIMOE_E_HIP;
-    }
-    if (c->flags & COLIMOE_CFG_INT8)
-      memcpy(tmp, src->shared, be);
-    else
-      repack_expert(src->shared, tmp, c->d, c->f);
-    if (C.tag[sslot] >= 0) C.slot_of[(size_t)C.tag[sslot]] = -1;
-    const bool ok = hipMemcpyAsync(C.slots + (size_t)sslot * be, tmp, be, hipMemcpyHostToDevice, s) == hipSuccess &&
-                    hipStreamSynchronize(s) == hipSuccess;
-    (void)hipHostFree(tmp);
-    if (!ok) {
-      (void)hipHostFree(store);
-      return COLIMOE_E_HIP;
-    }
-    C.tag[sslot] = (int64_t)layer * (E + 1) + E;
-    C.fixed[sslot] = 1;
-    map[E] = sslot;
-  }
-  // until a call brings experts in, every entry points at a valid slot
-  int32_t *st = C.stage + (size_t)layer * (E + 1);
-  const int dummy = map[E] >= 0 ? map[E] : 0;
-  for (int e = 0; e <= E; ++e) st[e] = map[e] >= 0 ? map[e] : dummy;
-  if (hipMemcpyAsync(C.dev_maps + (size_t)layer * (E + 1), st, (size_t)(E + 1) * 4, hipMemcpyHostToDevice, s) !=
-          hipSuccess ||
-      hipStreamSynchronize(s) != hipSuccess) {
-    (void)hipHostFree(store);
-    return COLIMOE_E_HIP;
-  }
-  ctx->host_store[layer] = store;
-  ctx->layers[layer] = LayerDev{router, bias, C.slots, be, C.dev_maps + (size_t)layer * (E + 1)};
-  ctx->loaded[layer] = 1;
-  return COLIMOE_OK;
-}
-
-int colimoe_cache_repin(colimoe_ctx *ctx, int32_t n) {
-  if (!ctx || n < 0) return COLIMOE_E_ARG;
-  colimoe_ctx::Cache &C = ctx->cache;
-  if (!C.slots) return COLIMOE_E_STATE;
-  const int E = ctx->cfg.n_experts, k = ctx->cfg.top_k;
-  const size_t be = ctx->el.bytes;
-  hipStream_t s = ctx->stream;
-  int open_slots = 0;  // slots not holding a shared expert
-  for (int i = 0; i < C.n_slots; ++i) open_slots += C.fixed[i] != 1;
-  if (n > open_slots - k) return COLIMOE_E_WORKSPACE;  // one token's experts must still fit
-  // the n routed experts of host-resident layers used most often (ties: lower layer, lower id)
-  std::vector<int64_t> cand;
-  for (int l = 0; l < ctx->cfg.n_layers; ++l)
-    if (ctx->host_store[l])
-      for (int e = 0; e < E; ++e)
-        if (C.uses[(size_t)l * (E + 1) + e]) cand.push_back((int64_t)l * (E + 1) + e);
-  std::stable_sort(cand.begin(), cand.end(), [&](int64_t a, int64_t b) { return C.uses[a] > C.uses[b]; });
-  if ((int)cand.size() > n) cand.resize(n);
-  if (hipStreamSynchronize(s) != hipSuccess) return COLIMOE_E_HIP;  // no kernel still reads a slot
-  for (int i = 0; i < C.n_slots; ++i)
-    if (C.fixed[i] == 2) C.fixed[i] = 0;
-  std::vector<char> want(C.slot_of.size(), 0);
-  for (int64_t t : cand) want[t] = 1;
-  for (int64_t t : cand)  // those already present keep their slot
-    if (C.slot_of[t] >= 0) C.fixed[C.slot_of[t]] = 2;
-  std::vector<char> dirty(ctx->cfg.n_layers, 0);
-  for (int64_t t : cand) {
-    if (C.slot_of[t] >= 0) continue;
-    int victim = -1;
-    for (int i = 0; i < C.n_slots; ++i)
-      if (!C.fixed[i] && (victim < 0 || C.used[i] < C.used[victim])) victim = i;
-    if (victim < 0) return COLIMOE_E_WORKSPACE;
-    if (C.tag[victim] >= 0) {
-      C.slot_of[(size_t)C.tag[victim]] = -1;
-      dirty[C.tag[victim] / (E + 1)] = 1;
-    }
-    const int l = (int)(t / (E + 1)), e = (int)(t % (E + 1));
-    if (hipMemcpyAsync(C.slots + (size_t)victim * be, ctx->host_store[l] + (size_t)e * be, be,
-                       hipMemcpyHostToDevice, s) != hipSuccess)
-      return COLIMOE_E_HIP;
-    C.tag[victim] = t;
-    C.used[victim] = C.stamp;
-    C.fixed[victim] = 2;
-    C.slot_of[t] = victim;
-    dirty[l] = 1;
-  }
-  for (int l = 0; l < ctx->cfg.n_layers; ++l) {
-    if (!dirty[l]) continue;
-    const int32_t *map = &C.slot_of[(size_t)l * (E + 1)];
-    int32_t *st = C.stage + (size_t)l * (E + 1);
-    const int dummy = map[E] >= 0 ? map[E] : 0;
-    for (int e = 0; e <= E; ++e) st[e] = map[e] >= 0 ? map[e] : dummy;
-    if (hipMemcpyAsync(C.dev_maps + (size_t)l * (E + 1), st, (size_t)(E + 1) * 4, hipMemcpyHostToDevice, s) !=
-        hipSuccess)
-      return COLIMOE_E_HIP;
-  }
-  return hip_status(hipStreamSynchronize(s));
-}
-
-int colimoe_cache_stats(colimoe_ctx *ctx, int64_t *hits, int64_t *misses, int32_t *slots) {
-  if (!ctx || !hits || !misses || !slots) return COLIMOE_E_ARG;
-  *hits = ctx->cache.hits;
-  *misses = ctx->cache.misses;
-  *slots = ctx->cache.n_slots;
   return COLIMOE_OK;
 }
 

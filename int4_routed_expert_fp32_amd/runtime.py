@@ -13,7 +13,9 @@ from typing import Dict, Optional
 import numpy as np
 import torch
 
-from . import (COLIMOE_FWD_AUTO, colimoe_cache_repin, colimoe_cache_stats, colimoe_create, colimoe_debug_expert, colimoe_destroy,
+from . import (COLIMOE_FWD_AUTO, colimoe_cache_get_info, colimoe_cache_repin, colimoe_cache_set_autorepin,
+               colimoe_cache_set_prefetch, colimoe_cache_stats, colimoe_cache_usage, colimoe_cache_usage_load,
+               colimoe_cache_usage_save, colimoe_create, colimoe_debug_expert, colimoe_destroy,
                colimoe_expert_cache_bytes, colimoe_forward, colimoe_host_layer_bytes, colimoe_load_experts_host,
                colimoe_set_expert_cache, colimoe_set_expert_top_p,
                colimoe_layer_bytes, colimoe_load_experts, colimoe_rmsnorm, colimoe_rmsnorm_route_forward, colimoe_route,
@@ -138,6 +140,27 @@ class MoeContext:
 
     def cache_repin(self, n: int) -> None:
         colimoe_cache_repin(self.ctx, n)
+
+    def cache_info(self):
+        return colimoe_cache_get_info(self.ctx)
+
+    def cache_set_prefetch(self, depth: int) -> None:
+        """Prefetch the first `depth` experts of each token's predicted routing (0: off)."""
+        colimoe_cache_set_prefetch(self.ctx, depth)
+
+    def cache_set_autorepin(self, every_tokens: int, n: int) -> None:
+        colimoe_cache_set_autorepin(self.ctx, every_tokens, n)
+
+    def cache_usage(self, layer: int) -> np.ndarray:
+        out = np.zeros(self.E, dtype=np.uint32)
+        colimoe_cache_usage(self.ctx, layer, out.ctypes.data)
+        return out
+
+    def cache_usage_save(self, path: str) -> None:
+        colimoe_cache_usage_save(self.ctx, path)
+
+    def cache_usage_load(self, path: str) -> None:
+        colimoe_cache_usage_load(self.ctx, path)
 
     def new_union(self, T: int) -> UnionTensors:
         tk = T * self.k

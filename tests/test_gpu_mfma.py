@@ -130,14 +130,16 @@ def test_prefill2048_parity():
 
 
 def test_mfma_block_class_boundaries():
-    """A forced routing that gives experts 1, 32, 33, 128, 129, 160 and 257
-    rows: M-blocks at both edges of the one-M-tile class (<= 32 rows) and of
-    the 128-row blocks, through the bf16 path, against the oracle under the
-    same routing."""
-    w = synth.Workload(name="mfma_edges", d=384, f=256, E=24, k=4, T=257, n_shared=1, seed=synth.BASE_SEED + 204)
-    counts = {0: 32, 1: 33, 2: 128, 3: 129, 4: 160, 5: 1, 6: 257}
+    """A forced routing that gives experts 1, 32, 33, 128, 129, 160, 256, 257,
+    288 and 289 rows: M-blocks at both edges of the one-M-tile class (<= 32
+    rows), of the 256-row blocks (a 257-row expert leaves a one-row block, a
+    288-row one a 32-row block, a 289-row one a 33-row block), and blocks of
+    every M-tile count from 2 to 8, through the bf16 path, against the oracle
+    under the same routing."""
+    w = synth.Workload(name="mfma_edges", d=384, f=256, E=24, k=4, T=512, n_shared=1, seed=synth.BASE_SEED + 204)
+    counts = {0: 32, 1: 33, 2: 128, 3: 129, 4: 160, 5: 1, 6: 257, 7: 256, 8: 288, 9: 289, 10: 70, 11: 200}
     rest = w.T * w.k - sum(counts.values())
-    others = list(range(7, w.E))
+    others = list(range(12, w.E))
     for i, e in enumerate(others):
         counts[e] = rest // len(others) + (1 if i < rest % len(others) else 0)
     pairs = [e for e in sorted(counts) for _ in range(counts[e])]
