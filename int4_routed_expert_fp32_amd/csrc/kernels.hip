@@ -519,16 +519,23 @@ __device__ __forceinline__ void load_step(const uint8_t *__restrict__ nib, const
   for (int r = 0; r < kTileRows; ++r) W[r] = *(const uint4 *)(nib + chunk_offset(tile, K, c, r));
 }
 
-// acc[r] = fma(s_r, chunk dot, acc[r]) for the 8 rows of a step, one token.
+// acc[r] = fma(s_r, chunk dot, acc[r]) for the 8 rows of a step, the
+// chunk's 32 activations in xv.
+__device__ __forceinline__ void step_accumulate_xv(const uint4 (&W)[kTileRows], const uint4 &S, const float4 (&xv)[8],
+                                                   float (&acc)[kTileRows]) {
+  const float nsx = neg8_sum(xv);
+#pragma unroll
+  for (int r = 0; r < kTileRows; ++r) acc[r] = __builtin_fmaf(tile_scale(S, r), chunk_dot(W[r], xv, nsx), acc[r]);
+}
+
+// The same for one token's activation row xrow, chunk c.
 __device__ __forceinline__ void step_accumulate(const uint4 (&W)[kTileRows], const uint4 &S,
                                                 const float *__restrict__ xrow, int c, float (&acc)[kTileRows]) {
   float4 xv[8];
   const float4 *src = (const float4 *)(xrow + (size_t)kChunk * c);
 #pragma unroll
   for (int v = 0; v < 8; ++v) xv[v] = src[v];
-  const float nsx = neg8_sum(xv);
-#pragma unroll
-  for (int r = 0; r < kTileRows; ++r) acc[r] = __builtin_fmaf(tile_scale(S, r), chunk_dot(W[r], xv, nsx), acc[r]);
+  step_accumulate_xv(W, S, xv, acc);
 }
 
 // Gate/up for K = d >= 2048: a block of NW = ceil(d/2048) waves per work item
@@ -594,6 +601,141 @@ __global__ __launch_bounds__(512) void k_gateup_wide(LayerDev L, Dims D, const f
         }
       }
       __syncthreads();
+    }
+  }
+}
+
+// The fp32 dequantisation path's one-token pair of kernels ([D] §4
+// highlight 4: f32 at batch 1).  Their h rows use a chunk-interleaved
+// layout: element 32c + 4v + i of a row (chunk c, float4 v of the chunk) is
+// stored at (v C + c) 4 + i, C = f / 32, so that the down kernel's lane c
+// reads float4 v of its chunk in one coalesced load per v (a plain row
+// would give every lane its own 128-byte line).  The layout is private to
+// the pair: no other kernel reads or writes it.
+__device__ __forceinline__ size_t h_ilv(int col, int C) {
+  return (size_t)((((col & 31) >> 2) * C + (col >> 5)) * 4 + (col & 3));
+}
+
+// Gate/up: a block of 4 waves per (slot, 4 TPW tiles); wave w takes tiles
+// TPW w .. TPW w + TPW - 1, each tile's NS steps (d <= 8192) one after the
+// other, the next step's weights loading while the current step computes.
+// x is staged once per block in LDS, 36 floats per 32-float chunk so that a
+// wave's 16-byte reads of one float4 of 64 chunks fall in distinct banks,
+// with each chunk's neg8_sum in the pad.  Per h row the operations are
+// those of k_gateup_wide (the lane's chunk, fma(scale, chunk_dot, 0), the
+// fixed 8-row tree, the steps added in order, SiLU(g) * u): the bits are
+// those of the batched fp32 kernels.
+constexpr int kXPad = 36;      // LDS floats per 32-activation chunk
+constexpr int kF32DecTPW = 1;  // tiles per wave
+template <int NS, int TPW>
+__global__ __launch_bounds__(256) void k_gateup_f32_dec(LayerDev L, Dims D, const float *__restrict__ x, UnionDev U,
+                                                        float *__restrict__ h) {
+  __shared__ __attribute__((aligned(16))) float xl[NS * 64 * kXPad];
+  __shared__ int slot_s[2];  // expert, output row
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int C = D.d / kChunk, groups = D.f / (16 * TPW);
+  const int s = blockIdx.x / groups, grp = blockIdx.x - s * groups;
+  if (threadIdx.x == 0) {
+    const int nu = clamp_nu(U.n_unique, D);
+    int e = -1, p0 = 0, p1 = 0;
+    if (s < nu || (s == nu && D.n_shared)) {
+      if (!resolve_slot(D, U, nu, s, e, p0, p1) || p1 <= p0) e = -1;
+    }
+    slot_s[0] = e;
+    slot_s[1] = s < nu ? p0 : D.T * D.k;
+  }
+  __syncthreads();
+  const int e = slot_s[0], orow = slot_s[1];
+  if (e < 0) return;  // block-uniform
+  const ExpertLayout EL = expert_layout(D.d, D.f);
+  const uint8_t *base = expert_base(L, e);
+  // weights through buffer loads (the lane's offset in a VGPR, the rest in
+  // the scalar offset); a lane past the row end reads the row's last chunk
+  // and its sums are replaced by 0
+  const __amdgpu_buffer_rsrc_t rn = wave_rsrc(base + EL.gu_nib, (uint32_t)(EL.gu_sc - EL.gu_nib));
+  const __amdgpu_buffer_rsrc_t rs = wave_rsrc(base + EL.gu_sc, (uint32_t)(EL.dn_nib - EL.gu_sc));
+  const int tile0 = grp * 4 * TPW + wave * TPW;
+  constexpr int kItems = NS * TPW;
+  uint4 Wb[2][kTileRows], Sb[2];
+  auto issue = [&](int it, uint4(&W)[kTileRows], uint4 &S) {
+    const int ti = tile0 + it / NS, st = it % NS;
+    const int width = C - 64 * st < 64 ? C - 64 * st : 64;
+    const int cl = lane < width ? lane : width - 1;
+    const int tb = ti * kTileRows * (D.d / 2) + st * (kTileRows * 64 * 16);
+#pragma unroll
+    for (int r = 0; r < kTileRows; ++r) {
+      const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(rn, cl * 16, tb + r * width * 16, 0);
+      W[r] = make_uint4(t.x, t.y, t.z, t.w);
+    }
+    const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(rs, (cl >> 1) * 16, (ti * (D.d / kGroup) + 32 * st) * 16, 0);
+    S = make_uint4(t.x, t.y, t.z, t.w);
+  };
+  issue(0, Wb[0], Sb[0]);
+  // x into LDS; each float4's sum, then the chunk's 8 sums in neg8_sum's
+  // tree (the 8 float4s of a chunk sit in 8 consecutive lanes; a + b is
+  // b + a exactly, so the shifted partners give the same sums)
+  for (int q = threadIdx.x; q < C * 8; q += blockDim.x) {
+    const float4 xq = ((const float4 *)x)[q];
+    *(float4 *)&xl[(q >> 3) * kXPad + (q & 7) * 4] = xq;
+    float v = (xq.x + xq.y) + (xq.z + xq.w);
+    v = v + bits_f(dpp<kRowShr1>(f_bits(v)));
+    v = v + bits_f(dpp<kRowShr2>(f_bits(v)));
+    v = v + bits_f(dpp<kRowShr4>(f_bits(v)));
+    if ((q & 7) == 7) xl[(q >> 3) * kXPad + 32] = -8.0f * v;
+  }
+  __syncthreads();
+  float tot = 0.0f;
+#pragma unroll
+  for (int it = 0; it < kItems; ++it) {
+    if (it + 1 < kItems) issue(it + 1, Wb[(it + 1) & 1], Sb[(it + 1) & 1]);
+    const uint4(&W)[kTileRows] = Wb[it & 1];
+    const uint4 &S = Sb[it & 1];
+    const int ti = tile0 + it / NS, st = it % NS;
+    const int width = C - 64 * st < 64 ? C - 64 * st : 64;
+    const bool live = lane < width;
+    const float *xc = &xl[(64 * st + (live ? lane : width - 1)) * kXPad];
+    // chunk_dot of the 8 rows, a word's 8 columns at a time: per row the
+    // same two chains (even columns from -8 sum x, odd from 0), same order
+    float alo[kTileRows], ahi[kTileRows];
+    const float nsx = xc[32];
+#pragma unroll
+    for (int r = 0; r < kTileRows; ++r) {
+      alo[r] = nsx;
+      ahi[r] = 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float4 xa = *(const float4 *)&xc[8 * i], xb = *(const float4 *)&xc[8 * i + 4];
+#pragma unroll
+      for (int r = 0; r < kTileRows; ++r) {
+        const uint32_t wi = (i == 0 ? W[r].x : i == 1 ? W[r].y : i == 2 ? W[r].z : W[r].w) ^ 0x88888888u;
+        uint32_t lo = wi & 0x0F0F0F0Fu, hi = wi & 0xF0F0F0F0u;
+        asm("" : "+v"(lo), "+v"(hi));
+        alo[r] = __builtin_fmaf((float)(lo & 0xFFu), xa.x, alo[r]);
+        alo[r] = __builtin_fmaf((float)((lo >> 8) & 0xFFu), xa.z, alo[r]);
+        alo[r] = __builtin_fmaf((float)((lo >> 16) & 0xFFu), xb.x, alo[r]);
+        alo[r] = __builtin_fmaf((float)(lo >> 24), xb.z, alo[r]);
+        ahi[r] = __builtin_fmaf((float)(hi & 0xFFu), xa.y, ahi[r]);
+        ahi[r] = __builtin_fmaf((float)((hi >> 8) & 0xFFu), xa.w, ahi[r]);
+        ahi[r] = __builtin_fmaf((float)((hi >> 16) & 0xFFu), xb.y, ahi[r]);
+        ahi[r] = __builtin_fmaf((float)(hi >> 24), xb.w, ahi[r]);
+      }
+      // the word's sums are due here: one word's masks and activations
+      // live at a time
+#pragma unroll
+      for (int r = 0; r < kTileRows; ++r) asm volatile("" : "+v"(alo[r]), "+v"(ahi[r]));
+    }
+    float acc[kTileRows];
+#pragma unroll
+    for (int r = 0; r < kTileRows; ++r)
+      acc[r] = live ? __builtin_fmaf(tile_scale(S, r), __builtin_fmaf(ahi[r], 0.0625f, alo[r]), 0.0f) : 0.0f;
+    const float v = reduce8_rows(acc);  // row r of this step at lane 8r + 7
+    tot = st == 0 ? v : tot + v;
+    if (st == NS - 1) {
+      // gate row r (lane 8r + 7) meets up row r + 4 (lane 8r + 39)
+      const float u = bits_f(xor32(f_bits(tot)));
+      if ((lane & 7) == 7 && lane < 32)
+        h[(size_t)orow * D.f + h_ilv(ti * 4 + (lane >> 3), D.f / kChunk)] = silu_f(tot) * u;
     }
   }
 }
@@ -1482,6 +1624,105 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(6))) void 
 }
 
 
+// Down projection and combine of the fp32 one-token pair: a block per 8-row
+// output tile, one wave per slot (up to kDecMaxSlots), few enough registers
+// that a decode call's blocks are resident together.  Per (row, slot) the
+// operations are those of k_down_wide (the lane's chunks in order,
+// fma(scale, chunk_dot, acc), the fixed 8-row tree), and the combine adds
+// the routed experts in ascending pair order with their gate weights, then
+// the shared expert, as combine_tile does: the bits are those of the fused
+// k_down_wide.  h rows come in the pair's interleaved layout (h_ilv).
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(7))) void k_down_f32_dec(
+    LayerDev L, Dims D, const float *__restrict__ h, UnionDev U, const float *__restrict__ w,
+    float *__restrict__ residual) {
+  __shared__ float vb[kDecMaxSlots][kTileRows];
+  __shared__ int ok_s[kDecMaxSlots];
+  __shared__ float wsl_s[kDecMaxSlots];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int ti = blockIdx.x, C = D.f / kChunk;
+  const int nu = clamp_nu(U.n_unique, D);
+  const int slots = nu + D.n_shared;
+  const ExpertLayout EL = expert_layout(D.d, D.f);
+  float rin = 0.0f;
+  if (wave == 0 && lane < kTileRows) rin = residual[(size_t)ti * kTileRows + lane];
+  if (wave < slots) {
+    int e, p0, p1;
+    const bool ok = resolve_slot(D, U, nu, wave, e, p0, p1) && p1 > p0;
+    if (lane == 0) {
+      float g = 1.0f;
+      if (wave < nu) {
+        int js = U.pair_slot[p0];
+        js = js < 0 ? 0 : (js >= D.k ? D.k - 1 : js);  // caller-supplied lists stay in bounds
+        g = w[js];
+      }
+      wsl_s[wave] = g;
+      ok_s[wave] = ok;
+    }
+    // buffer loads: the lane's offset in a VGPR, the rest in the scalar
+    // offset; a lane past the row end reads a valid chunk (the row's last)
+    // and keeps its sums unchanged
+    const uint8_t *base = expert_base(L, ok ? e : 0);
+    const __amdgpu_buffer_rsrc_t rn = wave_rsrc(base + EL.dn_nib, (uint32_t)(EL.dn_sc - EL.dn_nib));
+    const __amdgpu_buffer_rsrc_t rs = wave_rsrc(base + EL.dn_sc, (uint32_t)(EL.bytes - EL.dn_sc));
+    const __amdgpu_buffer_rsrc_t rh =
+        wave_rsrc(h + (size_t)(wave < nu ? p0 : D.T * D.k) * D.f, (uint32_t)D.f * 4u);
+    float acc[kTileRows];
+#pragma unroll
+    for (int r = 0; r < kTileRows; ++r) acc[r] = 0.0f;
+    for (int j = 0; 64 * j < C; ++j) {
+      const int width = C - 64 * j < 64 ? C - 64 * j : 64;
+      const bool live = lane < width;
+      const int cl = live ? lane : width - 1;
+      const int tb = ti * kTileRows * (D.f / 2) + j * (kTileRows * 64 * 16);
+      const u32x4 Sv =
+          __builtin_amdgcn_raw_buffer_load_b128(rs, (cl >> 1) * 16, (ti * (D.f / kGroup) + 32 * j) * 16, 0);
+      const uint4 S = make_uint4(Sv.x, Sv.y, Sv.z, Sv.w);
+      float4 xv[8];
+#pragma unroll
+      for (int v = 0; v < 8; ++v) {
+        const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(rh, cl * 16, (v * C + 64 * j) * 16, 0);
+        // (elements by index: hipcc turns __builtin_bit_cast of a vector
+        // element .y/.z/.w into element 0)
+        xv[v] = make_float4(bits_f(t[0]), bits_f(t[1]), bits_f(t[2]), bits_f(t[3]));
+      }
+      // the tile's rows in two halves of 4, the second half's weights
+      // loaded after the first half's sums: the activations, one half's
+      // weights and the sums fit the register budget of 3 blocks per CU
+      float a[kTileRows];
+      float nsx = 0.0f;
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        uint4 W[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(rn, cl * 16, tb + (4 * hf + r) * width * 16, 0);
+          W[r] = make_uint4(t.x, t.y, t.z, t.w);
+        }
+        if (hf == 0) nsx = neg8_sum(xv);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int rr = 4 * hf + r;
+          a[rr] = __builtin_fmaf(tile_scale(S, rr), chunk_dot(W[r], xv, nsx), acc[rr]);
+          asm volatile("" : "+v"(a[rr]));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int r = 0; r < kTileRows; ++r) acc[r] = live ? a[r] : acc[r];
+    }
+    const float v = reduce8_rows(acc);
+    if ((lane & 7) == 7) vb[wave][lane >> 3] = v;
+  }
+  __syncthreads();
+  if (wave == 0 && lane < kTileRows) {
+    float out = rin;
+    for (int sl = 0; sl < nu; ++sl)
+      if (ok_s[sl]) out = __builtin_fmaf(wsl_s[sl], vb[sl][lane], out);
+    if (D.n_shared && ok_s[nu]) out = out + vb[nu][lane];
+    residual[(size_t)ti * kTileRows + lane] = out;
+  }
+}
+
 // ------------------------------------------------------- int8 container
 // Experts stored as int8 gs64 (one two's-complement byte per weight, the
 // canonical blob layout [gate q][gate s][up q][up s][down q][down s], rows
@@ -2166,6 +2407,33 @@ hipError_t launch_down_tok(const LayerDev &L, const Dims &D, const UnionDev &U, 
     else
       down_tok_launch<2, false>(wpt, grid, lds, s, L, D, U, hq, hs, y);
   }
+  return hipGetLastError();
+}
+
+bool f32_dec_supported(const Dims &D) {
+  const int NS = (D.d / kChunk + 63) / 64;
+  return D.T == 1 && wide(D.d) && NS <= 4 && D.f % (16 * kF32DecTPW) == 0 && down_fusable(D) &&
+         D.k + D.n_shared <= kDecMaxSlots;
+}
+
+hipError_t launch_gateup_f32_dec(const LayerDev &L, const Dims &D, const float *x, const UnionDev &U, float *h,
+                                 hipStream_t s) {
+  if (!f32_dec_supported(D)) return hipErrorInvalidValue;
+  const int NS = (D.d / kChunk + 63) / 64;
+  const int grid = slots_max(D) * (D.f / (16 * kF32DecTPW));
+  switch (NS) {
+    case 1: k_gateup_f32_dec<1, kF32DecTPW><<<grid, 256, 0, s>>>(L, D, x, U, h); break;
+    case 2: k_gateup_f32_dec<2, kF32DecTPW><<<grid, 256, 0, s>>>(L, D, x, U, h); break;
+    case 3: k_gateup_f32_dec<3, kF32DecTPW><<<grid, 256, 0, s>>>(L, D, x, U, h); break;
+    default: k_gateup_f32_dec<4, kF32DecTPW><<<grid, 256, 0, s>>>(L, D, x, U, h); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_down_f32_dec(const LayerDev &L, const Dims &D, const float *h, const UnionDev &U, const float *w,
+                               float *residual, hipStream_t s) {
+  if (!f32_dec_supported(D)) return hipErrorInvalidValue;
+  k_down_f32_dec<<<D.d / kTileRows, 64 * (D.k + D.n_shared), 0, s>>>(L, D, h, U, w, residual);
   return hipGetLastError();
 }
 

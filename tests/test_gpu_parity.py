@@ -224,9 +224,10 @@ def test_forced_routing_onehot_gate():
 
 
 # One-token shapes that reach the other kernel variants: two steps per row with
-# a partial second one (d = f = 2112: the streaming down kernel), 17 slots
-# (k = 16 + shared: more slots than one block of slot-waves holds), and
-# d > 8192 (the general fixed-point kernels).
+# a partial second one (d = f = 2112: the streaming down kernel, and the lanes
+# past the row end of the fp32 one-token pair), 17 slots (k = 16 + shared:
+# more slots than one block of slot-waves holds), and d > 8192 (the general
+# fixed-point and fp32 kernels).
 DEC_SHAPES = [
     synth.Workload(name="dec_2step", d=2112, f=2112, E=40, k=3, T=3, n_shared=1, zipf=1.1,
                    seed=synth.BASE_SEED + 104),
@@ -235,19 +236,20 @@ DEC_SHAPES = [
 ]
 
 
+@pytest.mark.parametrize("flags", [FXP, FP32], ids=["fxp", "fp32"])
 @pytest.mark.parametrize("w", DEC_SHAPES, ids=lambda w: w.name)
-def test_one_token_kernel_variants(w):
+def test_one_token_kernel_variants(w, flags):
     """Each token alone (one call and route + forward) matches the oracle, the
     two call forms agree bit for bit, and both equal the batched call."""
     ctx = _ctx(w)
     P.load_layer(ctx, w, 0)
     ora = P.OracleLayer(w, 0)
     X = synth.activations(w, stream=4)
-    batch = P.layer_parity(ctx, w, 0, X, ora, flags=FXP)
+    batch = P.layer_parity(ctx, w, 0, X, ora, flags=flags)
     for t in range(w.T):
         x1 = X[t:t + 1]
-        a = P.layer_parity(ctx, w, 0, x1, ora, flags=FXP, one_call=True)
-        b = P.layer_parity(ctx, w, 0, x1, ora, flags=FXP)
+        a = P.layer_parity(ctx, w, 0, x1, ora, flags=flags, one_call=True)
+        b = P.layer_parity(ctx, w, 0, x1, ora, flags=flags)
         assert np.array_equal(a["out"].view(np.uint32), b["out"].view(np.uint32)), t
         assert np.array_equal(a["out"][0].view(np.uint32), batch["out"][t].view(np.uint32)), t
         assert np.array_equal(a["idx"][0], batch["idx"][t])
