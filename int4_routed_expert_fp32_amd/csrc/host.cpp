@@ -287,9 +287,11 @@ static colimoe_union ws_union_abi(colimoe_ctx *ctx) {
 }
 
 // Router, top-k and (if u) union lists; `encode` also writes the fixed-point
-// encoding of x into the workspace when the route runs as one kernel.
+// encoding of x into the workspace when the route runs as one kernel, and
+// `shared_early` (one token) runs the shared expert's fixed-point gate/up in
+// the top-k launch.
 static int route_impl(colimoe_ctx *ctx, int32_t layer, const float *x, int32_t T, int32_t *idx, float *w,
-               const colimoe_union *u, float *logits, bool encode) {
+               const colimoe_union *u, float *logits, bool encode, bool shared_early = false) {
   const Dims D = dims_of(ctx, T);
   const LayerDev L = layer_of(ctx, layer);
   float *lg = logits ? logits : (float *)(ctx->ws + ctx->wl.logits);
@@ -306,7 +308,14 @@ static int route_impl(colimoe_ctx *ctx, int32_t layer, const float *x, int32_t T
     if (D.T == 1) {
       KTimer kt(ctx, K_TOPK);
       const UnionDev U = u ? to_dev(u) : UnionDev{};
-      if (launch_topk_union1(lg, D, idx, w, u ? &U : nullptr, ctx->top_p, s) != hipSuccess) return COLIMOE_E_HIP;
+      if (shared_early) {
+        if (launch_topk_shared1(lg, D, idx, w, u ? &U : nullptr, ctx->top_p, L, (uint32_t *)(ctx->ws + ctx->wl.xq),
+                                (float *)(ctx->ws + ctx->wl.xs), (uint32_t *)(ctx->ws + ctx->wl.hq),
+                                (float *)(ctx->ws + ctx->wl.hs), s) != hipSuccess)
+          return COLIMOE_E_HIP;
+      } else if (launch_topk_union1(lg, D, idx, w, u ? &U : nullptr, ctx->top_p, s) != hipSuccess) {
+        return COLIMOE_E_HIP;
+      }
       return COLIMOE_OK;
     }
     if (u) {  // up to 16 tokens: top-k and the union lists in one launch
@@ -330,9 +339,10 @@ static int route_impl(colimoe_ctx *ctx, int32_t layer, const float *x, int32_t T
 }
 
 // Expert work and combine.  x_encoded: the workspace already holds the
-// fixed-point encoding of this x (written by the route kernel).
+// fixed-point encoding of this x (written by the route kernel); shared_done:
+// also the shared expert's h encoding (written by the top-k launch).
 static int forward_kernels(colimoe_ctx *ctx, int32_t layer, const float *x, int32_t T, const int32_t *idx, const float *w,
-                 const colimoe_union *u, float *residual, int path, bool x_encoded) {
+                 const colimoe_union *u, float *residual, int path, bool x_encoded, bool shared_done) {
   const Dims D = dims_of(ctx, T);
   const LayerDev L = layer_of(ctx, layer);
   hipStream_t s = ctx->stream;
@@ -382,7 +392,7 @@ static int forward_kernels(colimoe_ctx *ctx, int32_t layer, const float *x, int3
     }
     {
       KTimer kt(ctx, K_GATEUP);
-      if (launch_gateup_tok(L, D, U, w, xq, xs, hq, hs, wslot, s) != hipSuccess) return COLIMOE_E_HIP;
+      if (launch_gateup_tok(L, D, U, w, xq, xs, hq, hs, wslot, shared_done, s) != hipSuccess) return COLIMOE_E_HIP;
     }
     if (down_dec_supported(D)) {
       KTimer kt(ctx, K_DOWN);
@@ -424,7 +434,7 @@ static int forward_kernels(colimoe_ctx *ctx, int32_t layer, const float *x, int3
 // layer ahead) beside this layer's kernels, and its predicted experts start
 // moving into the cache once the prediction is in.
 static int forward_impl(colimoe_ctx *ctx, int32_t layer, const float *x, int32_t T, const int32_t *idx, const float *w,
-                        const colimoe_union *u, float *residual, int path, bool x_encoded) {
+                        const colimoe_union *u, float *residual, int path, bool x_encoded, bool shared_done = false) {
   int predicting = 0;
   if (ctx->host_store[layer]) {
     const int rc = cache_ensure_resident(ctx, layer, idx, T);
@@ -432,7 +442,7 @@ static int forward_impl(colimoe_ctx *ctx, int32_t layer, const float *x, int32_t
     predicting = cache_predict_start(ctx, layer, x, T);
     if (predicting < 0) return predicting;
   }
-  const int rc = forward_kernels(ctx, layer, x, T, idx, w, u, residual, path, x_encoded);
+  const int rc = forward_kernels(ctx, layer, x, T, idx, w, u, residual, path, x_encoded, shared_done);
   const int rp = predicting ? cache_prefetch_issue(ctx, layer, T) : COLIMOE_OK;
   return rc ? rc : rp;
 }
@@ -659,9 +669,12 @@ int colimoe_route_forward(colimoe_ctx *ctx, int32_t layer, const float *x, int32
   const colimoe_union *uu = u ? u : &uw;
   const bool encode = path == PATH_FXP;
   const Dims D = dims_of(ctx, T);
-  rc = route_impl(ctx, layer, x, T, idx, w, uu, nullptr, encode);
+  // one token on an HBM-resident layer: the shared expert's gate/up rides in
+  // the top-k launch
+  const bool early = encode && !ctx->host_store[layer] && shared_early_supported(D);
+  rc = route_impl(ctx, layer, x, T, idx, w, uu, nullptr, encode, early);
   if (rc) return rc;
-  return forward_impl(ctx, layer, x, T, idx, w, uu, residual, path, encode && T <= kRouteSplitMaxT);
+  return forward_impl(ctx, layer, x, T, idx, w, uu, residual, path, encode && T <= kRouteSplitMaxT, early);
 }
 
 int colimoe_route_forward_static(colimoe_ctx *ctx, int32_t layer, const float *x, int32_t T, int32_t *idx,
@@ -737,13 +750,21 @@ int colimoe_rmsnorm_route_forward(colimoe_ctx *ctx, int32_t layer, float *r, int
                            (float *)(ctx->ws + ctx->wl.xs), ctx->stream) != hipSuccess)
       return COLIMOE_E_HIP;
   }
+  const bool early = !ctx->host_store[layer] && shared_early_supported(D);
   {
     KTimer kt(ctx, K_TOPK);
     const UnionDev U = to_dev(uu);
-    if (launch_topk_union1((float *)(ctx->ws + ctx->wl.logits), D, idx, w, &U, ctx->top_p, ctx->stream) != hipSuccess)
+    float *lg = (float *)(ctx->ws + ctx->wl.logits);
+    if (early) {
+      if (launch_topk_shared1(lg, D, idx, w, &U, ctx->top_p, L, (uint32_t *)(ctx->ws + ctx->wl.xq),
+                              (float *)(ctx->ws + ctx->wl.xs), (uint32_t *)(ctx->ws + ctx->wl.hq),
+                              (float *)(ctx->ws + ctx->wl.hs), ctx->stream) != hipSuccess)
+        return COLIMOE_E_HIP;
+    } else if (launch_topk_union1(lg, D, idx, w, &U, ctx->top_p, ctx->stream) != hipSuccess) {
       return COLIMOE_E_HIP;
+    }
   }
-  return forward_impl(ctx, layer, x_out, T, idx, w, uu, r, path, true);
+  return forward_impl(ctx, layer, x_out, T, idx, w, uu, r, path, true, early);
 }
 
 int colimoe_rmsnorm(colimoe_ctx *ctx, const float *r, int32_t T, float eps, float *x_out) {

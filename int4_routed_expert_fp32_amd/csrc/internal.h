@@ -118,6 +118,13 @@ hipError_t launch_router_norm(const LayerDev &L, const Dims &D, const float *r, 
                               uint32_t *xq, float *xs, hipStream_t s);
 // Top-k of one token and, if U, its union lists (T == 1); top_p < 1 applies
 // adaptive expert top-p (dropped slots: id -1, weight 0, pair_of -1).
+// One token: the top-k and union lists of launch_topk_union1 and, in the same
+// launch, the shared expert's fixed-point gate/up from the encoding xq/xs
+// (into hq/hs row T*k, as launch_gateup_tok writes it).
+bool shared_early_supported(const Dims &D);
+hipError_t launch_topk_shared1(const float *logits, const Dims &D, int32_t *idx, float *w, const UnionDev *U,
+                               float top_p, const LayerDev &L, const uint32_t *xq, const float *xs, uint32_t *hq,
+                               float *hs, hipStream_t s);
 hipError_t launch_topk_union1(const float *logits, const Dims &D, int32_t *idx, float *w, const UnionDev *U,
                               float top_p, hipStream_t s);
 hipError_t launch_topk(const float *logits, const Dims &D, int32_t *idx, float *w, hipStream_t s);
@@ -143,8 +150,10 @@ hipError_t launch_xquant(const float *x, int T, int K, uint32_t *xq, float *xs, 
 // Fixed-point gate/up for any T (one wave per tile and step, weights loaded
 // once per call, tokens in chunks of 16); writes h's encoding to hq/hs and, for
 // T == 1, each slot's gate weight (from w) to wslot[k + shared].
+// skip_shared (one token, shared_early_supported): the shared expert's h is
+// already there (launch_topk_shared1).
 hipError_t launch_gateup_tok(const LayerDev &L, const Dims &D, const UnionDev &U, const float *w, const uint32_t *xq,
-                             const float *xs, uint32_t *hq, float *hs, float *wslot, hipStream_t s);
+                             const float *xs, uint32_t *hq, float *hs, float *wslot, bool skip_shared, hipStream_t s);
 // Fixed-point down for any T: y [T*k + T*shared][d] fp32 (combine in k_combine).
 hipError_t launch_down_tok(const LayerDev &L, const Dims &D, const UnionDev &U, const uint32_t *hq, const float *hs,
                            float *y, hipStream_t s);

@@ -1137,44 +1137,20 @@ __global__ __launch_bounds__(256 * WPT) void k_gateup_tok(LayerDev L, Dims D, Un
 
 // Gate/up for one token, up to 4 steps per row (d <= 8192): one wave per
 // (tile, step), the same operations as k_gateup_tok with a single token, in
-// a lean form that keeps two blocks resident per CU.
+// a lean form that keeps two blocks resident per CU.  One block: 16 h rows
+// (4 tiles, quad qd) of expert e into output row orow.
 template <int NS>
-__global__ __launch_bounds__(256 * NS) void k_gateup_one(LayerDev L, Dims D, UnionDev U, const float *__restrict__ w,
-                                                         const uint32_t *__restrict__ xq,
-                                                         const float *__restrict__ xs, uint32_t *__restrict__ hq,
-                                                         float *__restrict__ hs, float *__restrict__ wslot) {
+__device__ __forceinline__ void gateup_one_quad(const LayerDev &L, const Dims &D, int e, int orow, int qd,
+                                                const uint32_t *__restrict__ xq, const float *__restrict__ xs,
+                                                uint32_t *__restrict__ hq, float *__restrict__ hs) {
   __shared__ float red[4][NS][kTileRows];
-  __shared__ int slot_s[2];  // expert, output row
-  __shared__ float hv[16];
   __shared__ uint32_t hw[12];
   __shared__ float hsc;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int C = D.d / kChunk, quads = D.f / 16;
-  const int s = blockIdx.x / quads, qd = blockIdx.x - s * quads;
+  const int C = D.d / kChunk;
   const int tt = wave / NS, st = wave - tt * NS;
   const int ti = qd * 4 + tt, c = lane + 64 * st;
   if (threadIdx.x < 12) hw[threadIdx.x] = 0u;
-  if (threadIdx.x == 0) {
-    const int nu = clamp_nu(U.n_unique, D);
-    int e = -1, p0 = 0, p1 = 0;
-    if (s < nu || (s == nu && D.n_shared)) {
-      if (!resolve_slot(D, U, nu, s, e, p0, p1) || p1 <= p0) e = -1;
-    }
-    slot_s[0] = e;
-    slot_s[1] = s < nu ? p0 : D.k;
-    if (qd == 0 && e >= 0) {
-      float f = 1.0f;
-      if (s < nu) {
-        int js = U.pair_slot[p0];
-        js = js < 0 ? 0 : (js >= D.k ? D.k - 1 : js);  // caller-supplied lists stay in bounds
-        f = w[js];
-      }
-      wslot[s] = f;
-    }
-  }
-  __syncthreads();
-  const int e = slot_s[0], orow = slot_s[1];
-  if (e < 0) return;  // block-uniform
   const ExpertLayout EL = expert_layout(D.d, D.f);
   const uint8_t *base = expert_base(L, e);
   float acc[kTileRows];
@@ -1217,7 +1193,42 @@ __global__ __launch_bounds__(256 * NS) void k_gateup_one(LayerDev L, Dims D, Uni
   }
 }
 
-// Gate/up for a few tokens per expert (up to 16 per call), the form of
+// Routed slots (and, unless skip_shared, the shared expert after them): a
+// block per (slot, quad); the first quad of a routed slot records the slot's
+// gate weight in wslot.
+template <int NS>
+__global__ __launch_bounds__(256 * NS) void k_gateup_one(LayerDev L, Dims D, UnionDev U, const float *__restrict__ w,
+                                                         const uint32_t *__restrict__ xq,
+                                                         const float *__restrict__ xs, uint32_t *__restrict__ hq,
+                                                         float *__restrict__ hs, float *__restrict__ wslot,
+                                                         int skip_shared) {
+  __shared__ int slot_s[2];  // expert, output row
+  const int quads = D.f / 16;
+  const int s = blockIdx.x / quads, qd = blockIdx.x - s * quads;
+  if (threadIdx.x == 0) {
+    const int nu = clamp_nu(U.n_unique, D);
+    int e = -1, p0 = 0, p1 = 0;
+    if (s < nu || (s == nu && D.n_shared && !skip_shared)) {
+      if (!resolve_slot(D, U, nu, s, e, p0, p1) || p1 <= p0) e = -1;
+    }
+    slot_s[0] = e;
+    slot_s[1] = s < nu ? p0 : D.k;
+    if (qd == 0 && e >= 0) {
+      float f = 1.0f;
+      if (s < nu) {
+        int js = U.pair_slot[p0];
+        js = js < 0 ? 0 : (js >= D.k ? D.k - 1 : js);  // caller-supplied lists stay in bounds
+        f = w[js];
+      }
+      wslot[s] = f;
+    }
+  }
+  __syncthreads();
+  const int e = slot_s[0], orow = slot_s[1];
+  if (e < 0) return;  // block-uniform
+  gateup_one_quad<NS>(L, D, e, orow, qd, xq, xs, hq, hs);
+}
+
 // k_gateup_one with the slot's tokens looped kFewT at a time: every wave loads
 // its (tile, step) weights once and applies them to each token in turn; per
 // token the operations are those of k_gateup_tok and k_gateup_one, so the
@@ -1550,6 +1561,29 @@ __global__ __launch_bounds__(64) void k_topk_union1(const float *__restrict__ lo
   topk_token<PER>(logits, D, 0, idx, wout, ids, top_p);
   wave_lds_sync();
   if (with_union) union_one_token(ids, D, U);
+}
+
+// Top-k of one token plus its union lists (block 0, as k_topk_union1), and
+// beside it the shared expert's gate/up (blocks 1..f/16, one quad each, as
+// k_gateup_one): the shared expert does not depend on the routing, so its
+// weights stream while the selection runs.
+template <int PER, int NS>
+__global__ __launch_bounds__(256 * NS) void k_topk_shared1(const float *__restrict__ logits, Dims D,
+                                                           int32_t *__restrict__ idx, float *__restrict__ wout,
+                                                           UnionDev U, int with_union, float top_p, LayerDev L,
+                                                           const uint32_t *__restrict__ xq,
+                                                           const float *__restrict__ xs, uint32_t *__restrict__ hq,
+                                                           float *__restrict__ hs) {
+  __shared__ int32_t ids[16];
+  if (blockIdx.x == 0) {
+    if (threadIdx.x < 64) {
+      topk_token<PER>(logits, D, 0, idx, wout, ids, top_p);
+      wave_lds_sync();
+      if (with_union) union_one_token(ids, D, U);
+    }
+    return;
+  }
+  gateup_one_quad<NS>(L, D, D.E, D.T * D.k, (int)blockIdx.x - 1, xq, xs, hq, hs);
 }
 
 // Down + combine for one token when a down row is one step (f <= 2048): a
@@ -2104,6 +2138,40 @@ hipError_t launch_topk_union1(const float *logits, const Dims &D, int32_t *idx, 
   return hipGetLastError();
 }
 
+bool shared_early_supported(const Dims &D) {
+  const int NS = (D.d / kChunk + 63) / 64;
+  return D.T == 1 && D.n_shared == 1 && NS <= 4 && D.f % 16 == 0;
+}
+
+template <int PER>
+static void topk_shared1_launch(int NS, int grid, hipStream_t s, const float *logits, const Dims &D, int32_t *idx,
+                                float *w, const UnionDev &u, int wu, float top_p, const LayerDev &L,
+                                const uint32_t *xq, const float *xs, uint32_t *hq, float *hs) {
+  switch (NS) {
+    case 1: k_topk_shared1<PER, 1><<<grid, 256, 0, s>>>(logits, D, idx, w, u, wu, top_p, L, xq, xs, hq, hs); break;
+    case 2: k_topk_shared1<PER, 2><<<grid, 512, 0, s>>>(logits, D, idx, w, u, wu, top_p, L, xq, xs, hq, hs); break;
+    case 3: k_topk_shared1<PER, 3><<<grid, 768, 0, s>>>(logits, D, idx, w, u, wu, top_p, L, xq, xs, hq, hs); break;
+    default: k_topk_shared1<PER, 4><<<grid, 1024, 0, s>>>(logits, D, idx, w, u, wu, top_p, L, xq, xs, hq, hs); break;
+  }
+}
+
+hipError_t launch_topk_shared1(const float *logits, const Dims &D, int32_t *idx, float *w, const UnionDev *U,
+                               float top_p, const LayerDev &L, const uint32_t *xq, const float *xs, uint32_t *hq,
+                               float *hs, hipStream_t s) {
+  if (!shared_early_supported(D)) return hipErrorInvalidValue;
+  const UnionDev u = U ? *U : UnionDev{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
+  const int wu = U ? 1 : 0;
+  const int NS = (D.d / kChunk + 63) / 64, grid = 1 + D.f / 16;
+  switch (topk_per(D.E)) {
+    case 1: topk_shared1_launch<1>(NS, grid, s, logits, D, idx, w, u, wu, top_p, L, xq, xs, hq, hs); break;
+    case 2: topk_shared1_launch<2>(NS, grid, s, logits, D, idx, w, u, wu, top_p, L, xq, xs, hq, hs); break;
+    case 4: topk_shared1_launch<4>(NS, grid, s, logits, D, idx, w, u, wu, top_p, L, xq, xs, hq, hs); break;
+    case 8: topk_shared1_launch<8>(NS, grid, s, logits, D, idx, w, u, wu, top_p, L, xq, xs, hq, hs); break;
+    default: topk_shared1_launch<16>(NS, grid, s, logits, D, idx, w, u, wu, top_p, L, xq, xs, hq, hs); break;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_topk(const float *logits, const Dims &D, int32_t *idx, float *w, hipStream_t s) {
   if (D.T <= 0) return hipSuccess;
   dim3 g((D.T + 3) / 4), b(256);
@@ -2357,7 +2425,7 @@ static void down_tok_launch(int wpt, int grid, size_t lds, hipStream_t s, const 
 }
 
 hipError_t launch_gateup_tok(const LayerDev &L, const Dims &D, const UnionDev &U, const float *w, const uint32_t *xq,
-                             const float *xs, uint32_t *hq, float *hs, float *wslot, hipStream_t s) {
+                             const float *xs, uint32_t *hq, float *hs, float *wslot, bool skip_shared, hipStream_t s) {
   if (D.T <= 0) return hipSuccess;
   const int NS = (D.d / kChunk + 63) / 64, wpt = NS < 4 ? NS : 4;
   const int slots = (D.T * D.k < D.E ? D.T * D.k : D.E) + D.n_shared;
@@ -2366,10 +2434,10 @@ hipError_t launch_gateup_tok(const LayerDev &L, const Dims &D, const UnionDev &U
   if (D.T == 1) {
     if (NS <= 4) {
       switch (NS) {
-        case 1: k_gateup_one<1><<<grid, 256, 0, s>>>(L, D, U, w, xq, xs, hq, hs, wslot); break;
-        case 2: k_gateup_one<2><<<grid, 512, 0, s>>>(L, D, U, w, xq, xs, hq, hs, wslot); break;
-        case 3: k_gateup_one<3><<<grid, 768, 0, s>>>(L, D, U, w, xq, xs, hq, hs, wslot); break;
-        default: k_gateup_one<4><<<grid, 1024, 0, s>>>(L, D, U, w, xq, xs, hq, hs, wslot); break;
+        case 1: k_gateup_one<1><<<grid, 256, 0, s>>>(L, D, U, w, xq, xs, hq, hs, wslot, skip_shared ? 1 : 0); break;
+        case 2: k_gateup_one<2><<<grid, 512, 0, s>>>(L, D, U, w, xq, xs, hq, hs, wslot, skip_shared ? 1 : 0); break;
+        case 3: k_gateup_one<3><<<grid, 768, 0, s>>>(L, D, U, w, xq, xs, hq, hs, wslot, skip_shared ? 1 : 0); break;
+        default: k_gateup_one<4><<<grid, 1024, 0, s>>>(L, D, U, w, xq, xs, hq, hs, wslot, skip_shared ? 1 : 0); break;
       }
     } else
       gateup_tok_launch<2, true>(wpt, grid, lds, s, L, D, U, w, xq, xs, hq, hs, wslot);
