@@ -673,14 +673,17 @@ def main():
     gu_bytes = 2 * (w.d * w.f // 2 + 2 * w.d * w.f // 64)     # gate+up int4 + fp16 scales of one expert
     dn_bytes = be - gu_bytes
     experts_touched = w.k + w.n_shared                         # T = 1: k distinct routed + shared
+    # the fixed-point one-token path runs the shared expert's gate/up in the
+    # top-k launch: the gate/up launch reads the k routed experts only
+    gu_experts = w.k if args.path != "fp32" else experts_touched
     int4_bytes = experts_touched * be
     us_token = 1000.0 * ms_step
     gbs = int4_bytes / (ms_step * 1e-3) / 1e9
-    gu_gbs = experts_touched * gu_bytes / (kern["gateup"]["avg_us"] * 1e-6) / 1e9
+    gu_gbs = gu_experts * gu_bytes / (kern["gateup"]["avg_us"] * 1e-6) / 1e9
     dn_gbs = experts_touched * dn_bytes / (kern["down"]["avg_us"] * 1e-6) / 1e9
     roofline = dict(bound="hbm", kernel=DECODE_GATEUP_KERNEL, achieved=round(gu_gbs, 1), peak=HBM_PEAK_GBS,
                     unit="GB/s", frac=round(gu_gbs / HBM_PEAK_GBS, 4), traffic=measured_traffic(DECODE_GATEUP_KERNEL),
-                    bytes_per_launch=experts_touched * gu_bytes, avg_launch_us=round(kern["gateup"]["avg_us"], 3))
+                    bytes_per_launch=gu_experts * gu_bytes, avg_launch_us=round(kern["gateup"]["avg_us"], 3))
 
     cpu = None
     if not args.no_cpu_baseline:
