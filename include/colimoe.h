@@ -292,9 +292,10 @@ COLIMOE_API int colimoe_route(colimoe_ctx *ctx, int32_t layer, const float *x, i
                   const colimoe_union *u, float *logits);
 
 /* Batch-union scheduler on its own ([A] §2, batch-union): builds the union
- * lists of a routing idx [T][k] (device) into u.  A routing with an expert
- * id outside [0, E) or an expert twice in one token yields n_unique = 0 and
- * makes the next colimoe_sync return E_ARG.  Errors: E_ARG, E_SHAPE,
+ * lists of a routing idx [T][k] (device) into u.  An id of -1 marks a slot
+ * dropped by expert top-p: it gets no pair (pair_of -1).  A routing with any
+ * other id outside [0, E) or an expert twice in one token yields n_unique = 0
+ * and makes the next colimoe_sync return E_ARG.  Errors: E_ARG, E_SHAPE,
  * E_WORKSPACE, E_HIP. */
 COLIMOE_API int colimoe_union_build(colimoe_ctx *ctx, const int32_t *idx, int32_t T, const colimoe_union *u);
 
@@ -307,9 +308,10 @@ COLIMOE_API int colimoe_union_build(colimoe_ctx *ctx, const int32_t *idx, int32_
  * weights are dequantised to fp32-class arithmetic, for many tokens per
  * expert the grouped bf16 matrix-core path applies ([D] §4, highlight 4).
  * Device pointers: x [T][d] fp32; idx [T][k] int32 and w [T][k] fp32 are
- * inputs, so a caller may force a routing; residual [T][d] fp32, updated in
- * place.  u: union lists for this idx, as written by colimoe_route, or NULL
- * to rebuild them in the workspace.  flags: one of colimoe_forward_flags
+ * inputs, so a caller may force a routing (an id of -1 is a dropped slot,
+ * as expert top-p writes it); residual [T][d] fp32, updated in place.  u:
+ * union lists for this idx, as written by colimoe_route, or NULL to rebuild
+ * them in the workspace.  flags: one of colimoe_forward_flags
  * (no silent change of path, [A] §4: a flag the shapes do not allow is
  * E_SHAPE).  The fp32-class paths give each token bit-identical results
  * whether it runs alone or batched with others.  Errors: E_ARG, E_SHAPE,
@@ -317,19 +319,17 @@ COLIMOE_API int colimoe_union_build(colimoe_ctx *ctx, const int32_t *idx, int32_
 COLIMOE_API int colimoe_forward(colimoe_ctx *ctx, int32_t layer, const float *x, int32_t T, const int32_t *idx,
                     const float *w, const colimoe_union *u, float *residual, uint32_t flags);
 
-/* Adaptive expert top-p for one-token routing ([D] key tuning parameters,
- * "topp=0.7": an adaptive expert top-p that reads 30-40% fewer experts; [D]
- * §4: top-p decides which experts are read).  With p < 1, colimoe_route,
- * colimoe_route_forward and colimoe_rmsnorm_route_forward with T == 1 keep,
- * of the k selected experts in top-k order, the shortest prefix whose gate
- * weights (softmax over the k) sum to at least p (at least the first one);
- * the kept experts get the softmax over their own logits, and a dropped slot
- * gets idx -1 and weight 0 (pair_of -1 in the union lists, which list the
- * kept experts only), so the layer reads the kept experts and the shared
- * expert only.  p = 1 (the default) is plain top-k.  The setting stays until
- * changed.  A routing with dropped slots is passed to colimoe_forward with
- * the union lists colimoe_route wrote (the lists cannot be rebuilt from an
- * idx holding -1).  Calls with T > 1 while p < 1 return E_SHAPE.  Errors:
+/* Adaptive expert top-p ([D] key tuning parameters, "topp=0.7": an adaptive
+ * expert top-p that reads 30-40% fewer experts; [D] §4: top-p decides which
+ * experts are read).  With p < 1, colimoe_route, colimoe_route_forward and
+ * colimoe_rmsnorm_route_forward keep, for each token, of the k selected
+ * experts in top-k order, the shortest prefix whose gate weights (softmax
+ * over the k) sum to at least p (at least the first one); the kept experts
+ * get the softmax over their own logits, and a dropped slot gets idx -1 and
+ * weight 0 (pair_of -1 in the union lists, which list the kept experts
+ * only), so the layer reads the kept experts and the shared expert only.  A
+ * token's result does not depend on the other tokens of the call.  p = 1
+ * (the default) is plain top-k.  The setting stays until changed.  Errors:
  * E_ARG (null ctx, p not in (0, 1]). */
 COLIMOE_API int colimoe_set_expert_top_p(colimoe_ctx *ctx, float p);
 

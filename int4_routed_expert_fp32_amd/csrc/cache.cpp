@@ -234,7 +234,7 @@ int cache_predict_start(colimoe_ctx *ctx, int l, const float *x, int T) {
   // and the prediction runs beside this layer's expert kernels
   const Dims D = dims_of(ctx, T);
   if (launch_router_split(ctx->layers[nl], D, x, C.pred_logits, nullptr, nullptr, C.side) != hipSuccess ||
-      launch_topk(C.pred_logits, D, C.pred_idx, C.pred_w, C.side) != hipSuccess ||
+      launch_topk(C.pred_logits, D, C.pred_idx, C.pred_w, 1.0f, C.side) != hipSuccess ||
       hipMemcpyAsync(C.pred_host, C.pred_idx, (size_t)T * ctx->cfg.top_k * 4, hipMemcpyDeviceToHost, C.side) !=
           hipSuccess)
     return COLIMOE_E_HIP;

@@ -297,7 +297,6 @@ static int route_impl(colimoe_ctx *ctx, int32_t layer, const float *x, int32_t T
   float *lg = logits ? logits : (float *)(ctx->ws + ctx->wl.logits);
   hipStream_t s = ctx->stream;
   int32_t *err = (int32_t *)(ctx->ws + ctx->wl.err);
-  if (ctx->top_p < 1.0f && D.T != 1) return COLIMOE_E_SHAPE;  // expert top-p: one-token calls only
   if (D.T <= kRouteSplitMaxT) {
     {
       KTimer kt(ctx, K_ROUTE);
@@ -320,7 +319,7 @@ static int route_impl(colimoe_ctx *ctx, int32_t layer, const float *x, int32_t T
     }
     if (u) {  // up to 16 tokens: top-k and the union lists in one launch
       KTimer kt(ctx, K_TOPK);
-      if (launch_topk_union(lg, D, idx, w, to_dev(u), err, s) != hipSuccess) return COLIMOE_E_HIP;
+      if (launch_topk_union(lg, D, idx, w, to_dev(u), err, ctx->top_p, s) != hipSuccess) return COLIMOE_E_HIP;
       return COLIMOE_OK;
     }
   } else {
@@ -329,7 +328,7 @@ static int route_impl(colimoe_ctx *ctx, int32_t layer, const float *x, int32_t T
   }
   {
     KTimer kt(ctx, K_TOPK);
-    if (launch_topk(lg, D, idx, w, s) != hipSuccess) return COLIMOE_E_HIP;
+    if (launch_topk(lg, D, idx, w, ctx->top_p, s) != hipSuccess) return COLIMOE_E_HIP;
   }
   if (u) {
     KTimer kt(ctx, K_UNION);
@@ -728,7 +727,6 @@ int colimoe_rmsnorm_route_forward(colimoe_ctx *ctx, int32_t layer, float *r, int
   if (T == 0) return COLIMOE_OK;
   if (!r || !x_out || !idx || !w || !aligned(r, 16) || !aligned(x_out, 16) || !aligned(idx, 4) || !aligned(w, 4))
     return COLIMOE_E_ARG;
-  if (ctx->top_p < 1.0f && T != 1) return COLIMOE_E_SHAPE;  // expert top-p: one-token calls only
   if (u && !union_ok(u)) return COLIMOE_E_ARG;
   const int path = select_path(ctx, T, flags);
   if (path < 0) return path;

@@ -127,12 +127,12 @@ hipError_t launch_topk_shared1(const float *logits, const Dims &D, int32_t *idx,
                                float *hs, hipStream_t s);
 hipError_t launch_topk_union1(const float *logits, const Dims &D, int32_t *idx, float *w, const UnionDev *U,
                               float top_p, hipStream_t s);
-hipError_t launch_topk(const float *logits, const Dims &D, int32_t *idx, float *w, hipStream_t s);
+hipError_t launch_topk(const float *logits, const Dims &D, int32_t *idx, float *w, float top_p, hipStream_t s);
 hipError_t launch_union(const int32_t *idx, const Dims &D, const UnionDev &U, int32_t *err, hipStream_t s);
 // Top-k of 1..16 tokens and their union lists in one launch (the results of
 // launch_topk followed by launch_union).
 hipError_t launch_topk_union(const float *logits, const Dims &D, int32_t *idx, float *w, const UnionDev &U,
-                             int32_t *err, hipStream_t s);
+                             int32_t *err, float top_p, hipStream_t s);
 hipError_t launch_gateup(const LayerDev &L, const Dims &D, const float *x, const UnionDev &U, float *h,
                          hipStream_t s);
 hipError_t launch_debug_gateup(const LayerDev &L, const Dims &D, const float *x, const UnionDev &U, float *h,

@@ -241,9 +241,9 @@ __device__ __forceinline__ void topk_token(const float *__restrict__ l, const Di
 
 template <int PER>
 __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ logits, Dims D, int32_t *__restrict__ idx,
-                                              float *__restrict__ wout) {
+                                              float *__restrict__ wout, float top_p) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t < D.T) topk_token<PER>(logits + (size_t)t * D.E, D, t, idx, wout, nullptr);
+  if (t < D.T) topk_token<PER>(logits + (size_t)t * D.E, D, t, idx, wout, nullptr, top_p);
 }
 
 // -------------------------------------------------------------------- union
@@ -254,6 +254,11 @@ __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ logits, 
 // range, or an expert twice in one token) produce an empty union and set *err.
 // idx may point to LDS (the top-k's copy of the routing, up to 16 tokens).
 // LDS: masks[E] u64 (8-byte aligned), counts[E], running[E], one flag.
+
+// An expert id of -1 in a routing marks a slot dropped by expert top-p: it
+// gets no pair (pair_of -1) and is not read; any other id outside [0, E) is
+// an invalid routing.
+constexpr int kDropped = -1;
 
 __host__ __device__ inline size_t union_lds_bytes(int E) { return (size_t)E * 8 + (size_t)(2 * E + 1) * 4; }
 
@@ -279,6 +284,7 @@ __device__ void union_wave(const int32_t *__restrict__ idx, const Dims &D, const
   for (int t = lane; t < T; t += 64) {
     for (int j = 0; j < k; ++j) {
       const int e = idx[(size_t)t * k + j];
+      if (e == kDropped) continue;
       bool ok = e >= 0 && e < E;
       for (int i = 0; i < j && ok; ++i) ok = idx[(size_t)t * k + i] != e;
       if (!ok)
@@ -334,26 +340,29 @@ __device__ void union_wave(const int32_t *__restrict__ idx, const Dims &D, const
     unsigned long long mm[16];
     int rr[16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j)
-      if (act && j < k) {
-        ee[j] = idx[(size_t)t * k + j];
-        atomicOr(&masks[ee[j]], 1ull << lane);
-      }
+    for (int j = 0; j < 16; ++j) {
+      ee[j] = act && j < k ? idx[(size_t)t * k + j] : kDropped;
+      if (ee[j] != kDropped) atomicOr(&masks[ee[j]], 1ull << lane);
+    }
     wave_lds_sync();
 #pragma unroll
-    for (int j = 0; j < 16; ++j)
-      if (act && j < k) {
+    for (int j = 0; j < 16; ++j) {
+      rr[j] = -1;
+      if (ee[j] != kDropped) {
         mm[j] = masks[ee[j]];
         rr[j] = __popcll(mm[j] & ((1ull << lane) - 1ull));
         const int p = running[ee[j]] + rr[j];
         U.pair_token[p] = t;
         U.pair_slot[p] = j;
         U.pair_of[(size_t)t * k + j] = p;
+      } else if (act && j < k) {
+        U.pair_of[(size_t)t * k + j] = -1;
       }
+    }
     wave_lds_sync();
 #pragma unroll
     for (int j = 0; j < 16; ++j)
-      if (act && j < k && rr[j] == 0) {
+      if (rr[j] == 0) {
         running[ee[j]] += __popcll(mm[j]);
         masks[ee[j]] = 0ull;
       }
@@ -400,6 +409,7 @@ __global__ __launch_bounds__(1024) void k_union_multi(const int32_t *__restrict_
   for (int t = t_lo + lane; t < t_hi; t += 64) {
     for (int j = 0; j < k; ++j) {
       const int e = idx[(size_t)t * k + j];
+      if (e == kDropped) continue;
       bool ok = e >= 0 && e < E;
       for (int i = 0; i < j && ok; ++i) ok = idx[(size_t)t * k + i] != e;
       if (!ok)
@@ -471,26 +481,29 @@ __global__ __launch_bounds__(1024) void k_union_multi(const int32_t *__restrict_
     unsigned long long mm[16];
     int rr[16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j)
-      if (act && j < k) {
-        ee[j] = idx[(size_t)t * k + j];
-        atomicOr(&mymask[ee[j]], 1ull << lane);
-      }
+    for (int j = 0; j < 16; ++j) {
+      ee[j] = act && j < k ? idx[(size_t)t * k + j] : kDropped;
+      if (ee[j] != kDropped) atomicOr(&mymask[ee[j]], 1ull << lane);
+    }
     wave_lds_sync();
 #pragma unroll
-    for (int j = 0; j < 16; ++j)
-      if (act && j < k) {
+    for (int j = 0; j < 16; ++j) {
+      rr[j] = -1;
+      if (ee[j] != kDropped) {
         mm[j] = mymask[ee[j]];
         rr[j] = __popcll(mm[j] & ((1ull << lane) - 1ull));
         const int p = mycount[ee[j]] + rr[j];
         U.pair_token[p] = t;
         U.pair_slot[p] = j;
         U.pair_of[(size_t)t * k + j] = p;
+      } else if (act && j < k) {
+        U.pair_of[(size_t)t * k + j] = -1;
       }
+    }
     wave_lds_sync();
 #pragma unroll
     for (int j = 0; j < 16; ++j)
-      if (act && j < k && rr[j] == 0) {
+      if (rr[j] == 0) {
         mycount[ee[j]] += __popcll(mm[j]);
         mymask[ee[j]] = 0ull;
       }
@@ -2172,15 +2185,15 @@ hipError_t launch_topk_shared1(const float *logits, const Dims &D, int32_t *idx,
   return hipGetLastError();
 }
 
-hipError_t launch_topk(const float *logits, const Dims &D, int32_t *idx, float *w, hipStream_t s) {
+hipError_t launch_topk(const float *logits, const Dims &D, int32_t *idx, float *w, float top_p, hipStream_t s) {
   if (D.T <= 0) return hipSuccess;
   dim3 g((D.T + 3) / 4), b(256);
   switch (topk_per(D.E)) {
-    case 1: k_topk<1><<<g, b, 0, s>>>(logits, D, idx, w); break;
-    case 2: k_topk<2><<<g, b, 0, s>>>(logits, D, idx, w); break;
-    case 4: k_topk<4><<<g, b, 0, s>>>(logits, D, idx, w); break;
-    case 8: k_topk<8><<<g, b, 0, s>>>(logits, D, idx, w); break;
-    default: k_topk<16><<<g, b, 0, s>>>(logits, D, idx, w); break;
+    case 1: k_topk<1><<<g, b, 0, s>>>(logits, D, idx, w, top_p); break;
+    case 2: k_topk<2><<<g, b, 0, s>>>(logits, D, idx, w, top_p); break;
+    case 4: k_topk<4><<<g, b, 0, s>>>(logits, D, idx, w, top_p); break;
+    case 8: k_topk<8><<<g, b, 0, s>>>(logits, D, idx, w, top_p); break;
+    default: k_topk<16><<<g, b, 0, s>>>(logits, D, idx, w, top_p); break;
   }
   return hipGetLastError();
 }
@@ -2195,12 +2208,13 @@ __device__ void union_small(const int32_t *__restrict__ idx, const Dims &D, cons
   const bool act = lane < P;
   const int e = act ? idx[lane] : 0;
   const int t = act ? lane / D.k : 0, j = act ? lane - t * D.k : 0;
-  bool ok = !act || (e >= 0 && e < D.E);
+  const bool live = act && e != kDropped;  // a slot dropped by expert top-p has no pair
+  bool ok = !live || (e >= 0 && e < D.E);
   // distinct within the token: compare with the ids of slots 0..j-1 of the
   // same token, taken from the lanes that hold them
   for (int q = 0; q + 1 < D.k; ++q) {
     const int eq = __shfl(e, t * D.k + q, 64);
-    if (q < j && eq == e) ok = false;
+    if (live && q < j && eq == e) ok = false;
   }
   if (__ballot(!ok)) {
     if (lane == 0) {
@@ -2210,9 +2224,9 @@ __device__ void union_small(const int32_t *__restrict__ idx, const Dims &D, cons
     }
     return;
   }
-  const int key = act ? e * D.T + t : 0x7FFFFFFF;  // (expert, token), unique per pair
+  const int key = live ? e * D.T + t : 0x7FFFFFFF;  // (expert, token), unique per pair
   int rank = 0;
-  bool first = act;
+  bool first = live;
   for (int q = 0; q < P; ++q) {
     const int kq = __shfl(key, q, 64), eq = __shfl(e, q, 64);
     rank += kq < key;
@@ -2221,7 +2235,8 @@ __device__ void union_small(const int32_t *__restrict__ idx, const Dims &D, cons
   const unsigned long long fm = __ballot(first);
   int below = 0;  // distinct experts smaller than e
   for (int q = 0; q < P; ++q) below += ((fm >> q) & 1ull) && __shfl(e, q, 64) < e;
-  if (act) {
+  const int kept = __popcll(__ballot(live));
+  if (live) {
     U.pair_token[rank] = t;
     U.pair_slot[rank] = j;
     U.pair_of[lane] = rank;
@@ -2229,11 +2244,13 @@ __device__ void union_small(const int32_t *__restrict__ idx, const Dims &D, cons
       U.ids[below] = e;
       U.offsets[below] = rank;
     }
+  } else if (act) {
+    U.pair_of[lane] = -1;
   }
   if (lane == 0) {
     const int n = __popcll(fm);
     *U.n_unique = n;
-    U.offsets[n] = P;
+    U.offsets[n] = kept;
   }
 }
 
@@ -2243,11 +2260,11 @@ __device__ void union_small(const int32_t *__restrict__ idx, const Dims &D, cons
 template <int PER>
 __global__ __launch_bounds__(1024) void k_topk_union(const float *__restrict__ logits, Dims D,
                                                      int32_t *__restrict__ idx, float *__restrict__ wout, UnionDev U,
-                                                     int32_t *__restrict__ err) {
+                                                     int32_t *__restrict__ err, float top_p) {
   extern __shared__ unsigned long long masks[];
   __shared__ int32_t sids[kRouteSplitMaxT * 16];  // the call's routing (T <= 16, k <= 16) for the union
   const int t = threadIdx.x >> 6;
-  if (t < D.T) topk_token<PER>(logits + (size_t)t * D.E, D, t, idx, wout, sids);
+  if (t < D.T) topk_token<PER>(logits + (size_t)t * D.E, D, t, idx, wout, sids, top_p);
   __syncthreads();
   if (threadIdx.x < 64) {
     if (D.T * D.k <= 64)
@@ -2258,16 +2275,16 @@ __global__ __launch_bounds__(1024) void k_topk_union(const float *__restrict__ l
 }
 
 hipError_t launch_topk_union(const float *logits, const Dims &D, int32_t *idx, float *w, const UnionDev &U,
-                             int32_t *err, hipStream_t s) {
+                             int32_t *err, float top_p, hipStream_t s) {
   if (D.T < 1 || D.T > kRouteSplitMaxT) return hipErrorInvalidValue;
   const int b = 64 * D.T;
   const size_t lds = union_lds_bytes(D.E);
   switch (topk_per(D.E)) {
-    case 1: k_topk_union<1><<<1, b, lds, s>>>(logits, D, idx, w, U, err); break;
-    case 2: k_topk_union<2><<<1, b, lds, s>>>(logits, D, idx, w, U, err); break;
-    case 4: k_topk_union<4><<<1, b, lds, s>>>(logits, D, idx, w, U, err); break;
-    case 8: k_topk_union<8><<<1, b, lds, s>>>(logits, D, idx, w, U, err); break;
-    default: k_topk_union<16><<<1, b, lds, s>>>(logits, D, idx, w, U, err); break;
+    case 1: k_topk_union<1><<<1, b, lds, s>>>(logits, D, idx, w, U, err, top_p); break;
+    case 2: k_topk_union<2><<<1, b, lds, s>>>(logits, D, idx, w, U, err, top_p); break;
+    case 4: k_topk_union<4><<<1, b, lds, s>>>(logits, D, idx, w, U, err, top_p); break;
+    case 8: k_topk_union<8><<<1, b, lds, s>>>(logits, D, idx, w, U, err, top_p); break;
+    default: k_topk_union<16><<<1, b, lds, s>>>(logits, D, idx, w, U, err, top_p); break;
   }
   return hipGetLastError();
 }

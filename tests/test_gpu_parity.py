@@ -91,30 +91,45 @@ def test_union_lists_exact(T, E, k):
     w = synth.Workload(name="u", d=256, f=128, E=E, k=k, T=T, n_shared=0)
     ctx = _ctx(w)
     rng = np.random.default_rng(T * 1000 + E + k)
-    for trial in range(3):
+    for trial in range(4):
         idx = _rand_routing(rng, T, E, k)
         if trial == 1:
             idx[:] = idx[0]  # identical tokens: U = k
+        if trial == 3:
+            idx[rng.random(idx.shape) < 0.3] = -1  # slots dropped by expert top-p: no pair
         U = ctx.new_union(T)
         ctx.union_build(torch.from_numpy(idx).cuda(), U)
         ctx.sync()
         g = U.to_host()
         o = oracle.union(idx, E)
         assert g["n_unique"] == o["n_unique"]
-        for key in ("ids", "offsets", "pair_token", "pair_slot", "pair_of"):
+        for key in ("ids", "offsets", "pair_of"):
             assert np.array_equal(g[key], o[key]), key
+        n = int(o["offsets"][-1])  # pairs listed (dropped slots have none)
+        for key in ("pair_token", "pair_slot"):
+            assert np.array_equal(g[key][:n], o[key][:n]), key
 
 
 def test_invalid_routing_is_reported():
+    """An id outside [0, E) other than -1, or an expert twice in one token, is
+    an invalid routing: empty lists and E_ARG at the next sync.  -1 is a
+    dropped slot (expert top-p), not an error, also twice in one token."""
     w = TINY
     ctx = _ctx(w, max_tokens=2)
     U = ctx.new_union(2)
     for bad in (np.array([[0, 16], [1, 2]], np.int32), np.array([[3, 3], [1, 2]], np.int32),
-                np.array([[-1, 2], [1, 2]], np.int32)):
+                np.array([[-2, 2], [1, 2]], np.int32)):
         ctx.union_build(torch.from_numpy(bad).cuda(), U)
         assert ctx.sync(check=False) == -1
         assert int(U.n_unique.item()) == 0
     assert ctx.sync(check=False) == 0
+    for ok in (np.array([[-1, 2], [1, 2]], np.int32), np.array([[-1, -1], [5, -1]], np.int32)):
+        ctx.union_build(torch.from_numpy(ok).cuda(), U)
+        assert ctx.sync(check=False) == 0
+        g, o = U.to_host(), oracle.union(ok, w.E)
+        assert g["n_unique"] == o["n_unique"]
+        for key in ("ids", "offsets", "pair_of"):
+            assert np.array_equal(g[key], o[key]), key
 
 
 @pytest.mark.parametrize("w", [TINY, RAGGED, RAGGED2, RAGGED3], ids=lambda w: w.name)

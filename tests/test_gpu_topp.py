@@ -1,4 +1,6 @@
-"""Adaptive expert top-p on one-token calls, against the oracle.
+"""Adaptive expert top-p, against the oracle: one-token calls, batched calls
+(whose tokens must carry the bits of the same token alone) and a
+prefill-shaped call on the matrix-core path.
 
 Rule (the oracle's): of the k experts in top-k order, keep the shortest prefix
 whose gate weights (softmax over the k) reach p, re-weighted by the softmax
@@ -140,16 +142,125 @@ def test_topp_rejections():
     P.load_layer(ctx, w, 0)
     for bad in (0.0, -0.5, 1.5, math.nan):
         assert cm.colimoe_set_expert_top_p(ctx.ctx, bad, check=False) == cm.COLIMOE_E_ARG
-    ctx.set_expert_top_p(0.6)
-    x = torch.from_numpy(synth.activations(w.with_(T=2), stream=34)).cuda()
-    idx = torch.empty((2, w.k), dtype=torch.int32, device="cuda")
-    wt = torch.empty((2, w.k), dtype=torch.float32, device="cuda")
-    res = x.clone()
-    rc = cm.colimoe_route_forward(ctx.ctx, 0, x.data_ptr(), 2, idx.data_ptr(), wt.data_ptr(), None, res.data_ptr(),
-                                  0, check=False)
-    assert rc == cm.COLIMOE_E_SHAPE
+    ctx.close()
+
+
+def check_topp_batch(w, ora, X, gidx, gw, union, p):
+    """Every token's kept prefix and weights (the rule of check_topp_token),
+    the union lists of the whole routing against the oracle's; returns the
+    oracle's outputs and L1 norms under the GPU's routing, and the kept counts."""
+    L, oidx, ow = ora.route(X)
+    T = X.shape[0]
+    wref = np.zeros((T, w.k))
+    kept = []
+    for t in range(T):
+        m = int(np.sum(gidx[t] >= 0))
+        assert m >= 1 and np.all(gidx[t, :m] >= 0) and np.all(gidx[t, m:] == -1), gidx[t]
+        assert np.array_equal(gidx[t, :m], oidx[t, :m]), (t, gidx[t], oidx[t])
+        _, _, mo = oracle.expert_top_p(L[t], oidx[t], ow[t], p)
+        if m != mo:
+            cum = float(np.sum(ow[t, :min(m, mo)]))
+            assert abs(cum - p) < 1e-5, "token %d kept %d, oracle %d, boundary mass %.9f" % (t, m, mo, cum)
+        wref[t, :m] = oracle.softmax_selected(L[t], gidx[t, :m])
+        kept.append(m)
+    P.assert_close(gw, wref, rel=1e-4, what="top-p gate weights")
+    assert np.all(gw[gidx < 0] == 0.0)
+    ou = oracle.union(gidx, w.E)
+    assert union["n_unique"] == ou["n_unique"]
+    n = int(np.sum(gidx >= 0))
+    for key in ("ids", "offsets", "pair_of"):
+        assert np.array_equal(union[key], ou[key]), key
+    for key in ("pair_token", "pair_slot"):
+        assert np.array_equal(union[key][:n], ou[key][:n]), key
+    out, l1 = ora.forward(X, gidx, wref)
+    return out, l1, kept
+
+
+# Batched calls with expert top-p: up to 16 tokens (top-k and lists in one
+# launch; 24 pairs ranked in one wave, 128 through the per-expert lane
+# masks), 40 tokens (the matrix-core router, the general top-k and union
+# kernels), each on both fp32-class paths.  Every token's row of the batch
+# must carry the bits of the same token forwarded alone under its routing,
+# and up to 16 tokens also those of the token routed alone.
+BATCH_T = [3, 16, 40]
+
+
+@pytest.fixture(scope="module")
+def u16():
+    w = synth.WORKLOADS["union16"].with_(T=max(BATCH_T))
+    ctx = _ctx(w, max_tokens=w.T)
+    P.load_layer(ctx, w, 0)
+    yield ctx, P.OracleLayer(w, 0), w
+    ctx.close()
+
+
+@pytest.mark.parametrize("flags", [FXP, FP32], ids=["fxp", "fp32"])
+@pytest.mark.parametrize("T", BATCH_T)
+def test_topp_batched_matches_one_token(u16, T, flags):
+    ctx, ora, w = u16
+    X = synth.activations(w, stream=36)[:T]
+    ctx.set_expert_top_p(P_PAGES)
+    try:
+        xt = torch.from_numpy(np.ascontiguousarray(X)).cuda()
+        U = ctx.new_union(T)
+        res = xt.clone()
+        idx, wt = ctx.route_forward(0, xt, U, res, flags)
+        ctx.sync()
+        gidx, gw, gout = idx.cpu().numpy(), wt.cpu().numpy(), res.cpu().numpy()
+        out, _, kept = check_topp_batch(w, ora, X.astype(np.float64), gidx, gw, U.to_host(), P_PAGES)
+        ratio = P.assert_close(gout, out, what="top-p batched layer output")
+        print("T=%d: experts kept per token %s (mean %.2f of %d), unique %d, worst ratio %.3g" % (
+            T, kept, np.mean(kept), w.k, U.to_host()["n_unique"], ratio))
+        assert min(kept) < w.k
+        # forward with the lists rebuilt from idx (dropped slots are -1): the same bits
+        res2 = xt.clone()
+        ctx.forward(0, xt, idx, wt, None, res2, flags)
+        ctx.sync()
+        assert np.array_equal(res2.cpu().numpy().view(np.uint32), gout.view(np.uint32))
+        for t in range(T):
+            x1 = xt[t:t + 1].contiguous()
+            # the token's routing row alone through colimoe_forward: the bits
+            # of its row in the batch
+            r1 = x1.clone()
+            ctx.forward(0, x1, idx[t:t + 1].contiguous(), wt[t:t + 1].contiguous(), None, r1, flags)
+            ctx.sync()
+            assert np.array_equal(r1.cpu().numpy()[0].view(np.uint32), gout[t].view(np.uint32)), t
+            if T <= 16:
+                # up to 16 tokens the router sums every logit as one token's
+                # does, so routing the token alone gives the same bits again
+                U1 = ctx.new_union(1)
+                r2 = x1.clone()
+                i1, w1 = ctx.route_forward(0, x1, U1, r2, flags)
+                ctx.sync()
+                assert np.array_equal(i1.cpu().numpy()[0], gidx[t]), t
+                assert np.array_equal(w1.cpu().numpy()[0].view(np.uint32), gw[t].view(np.uint32)), t
+                assert np.array_equal(r2.cpu().numpy()[0].view(np.uint32), gout[t].view(np.uint32)), t
+    finally:
+        ctx.set_expert_top_p(1.0)
+
+
+def test_topp_prefill_shape_mfma():
+    """A prefill-shaped call (T k >= 64 E: the bf16 matrix-core path) with
+    expert top-p: routing, weights and union lists as above, outputs within
+    the bf16 bound 2e-2 N_r."""
+    w = synth.Workload(name="mfma_a", d=384, f=256, E=24, k=4, T=400, n_shared=1, zipf=1.1,
+                       seed=synth.BASE_SEED + 201)
+    ctx = _ctx(w, max_tokens=w.T)
+    P.load_layer(ctx, w, 0)
+    ora = P.OracleLayer(w, 0)
+    ctx.set_expert_top_p(P_PAGES)
+    X = synth.activations(w, stream=37)
+    xt = torch.from_numpy(X).cuda()
+    U = ctx.new_union(w.T)
+    res = xt.clone()
+    idx, wt = ctx.route_forward(0, xt, U, res, 2)
     ctx.sync()
-    assert torch.equal(res, x)  # a rejected call has no effect
+    gidx, gw, gout = idx.cpu().numpy(), wt.cpu().numpy(), res.cpu().numpy()
+    out, l1, kept = check_topp_batch(w, ora, X.astype(np.float64), gidx, gw, U.to_host(), P_PAGES)
+    ratio = float(np.max(np.abs(gout.astype(np.float64) - out) / (2e-2 * l1)))
+    print("mfma top-p: mean kept %.2f of %d, worst bf16 ratio %.3g" % (np.mean(kept), w.k, ratio))
+    assert ratio <= 1.0
+    assert min(kept) < w.k
     ctx.close()
 
 
