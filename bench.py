@@ -430,7 +430,8 @@ def bench_union16(args, torch, np, synth, cm, MoeContext, dev, stream):
 
 def bench_verify(args, torch, np, synth, cm, MoeContext, dev, stream):
     """T = 1..4 draft positions per call (batch-union recipe): the cost of each
-    extra position in time and in expert bytes."""
+    extra position in time and in expert bytes, with plain top-k and with the
+    pages' expert top-p 0.7 (fewer experts read per position)."""
     w4 = synth.WORKLOADS["verify4"]
     ring = 4
     ctx = MoeContext(w4.d, w4.f, w4.E, w4.k, n_layers=ring, n_shared=w4.n_shared, max_tokens=w4.T)
@@ -438,31 +439,36 @@ def bench_verify(args, torch, np, synth, cm, MoeContext, dev, stream):
     nb, warm = 48, 4
     out = {"workload": "multi-position verify: T = 1..4 positions per call (pairwise correlation 0.6, Zipf(1.1) "
                        "bias), d=6144 f=2048 E=256 top-8 + shared", "per_T": {}}
-    for T in (1, 2, 3, 4):
-        w = w4.with_(T=T)
-        Xs = [torch.from_numpy(synth.activations(w, stream=300 + b)).to(dev) for b in range(nb + warm)]
-        res = [x.clone() for x in Xs]
-        idx = torch.empty((T, w.k), dtype=torch.int32, device=dev)
-        wts = torch.empty((T, w.k), dtype=torch.float32, device=dev)
-        unions = [ctx.new_union(T) for _ in range(nb + warm)]
+    # plain top-k, then the pages' expert top-p 0.7 on the same calls
+    for p, key in ((1.0, "per_T"), (0.7, "per_T_top_p_0.7")):
+        out.setdefault(key, {})
+        ctx.set_expert_top_p(p)
+        for T in (1, 2, 3, 4):
+            w = w4.with_(T=T)
+            Xs = [torch.from_numpy(synth.activations(w, stream=300 + b)).to(dev) for b in range(nb + warm)]
+            res = [x.clone() for x in Xs]
+            idx = torch.empty((T, w.k), dtype=torch.int32, device=dev)
+            wts = torch.empty((T, w.k), dtype=torch.float32, device=dev)
+            unions = [ctx.new_union(T) for _ in range(nb + warm)]
 
-        def call(b):
-            cm.colimoe_route_forward(ctx.ctx, b % ring, Xs[b].data_ptr(), T, idx.data_ptr(), wts.data_ptr(),
-                                     unions[b].abi(), res[b].data_ptr(), cm.COLIMOE_FWD_AUTO)
+            def call(b):
+                cm.colimoe_route_forward(ctx.ctx, b % ring, Xs[b].data_ptr(), T, idx.data_ptr(), wts.data_ptr(),
+                                         unions[b].abi(), res[b].data_ptr(), cm.COLIMOE_FWD_AUTO)
 
-        for b in range(warm):
-            call(b)
-        ctx.sync()
-        ms = event_time(torch, stream, lambda: [call(b) for b in range(warm, warm + nb)]) / nb
-        ctx.sync()
-        kern = per_kernel(cm, ctx, lambda: [call(b) for b in range(warm, warm + nb)])
-        nus = [int(unions[b].n_unique.item()) for b in range(warm, warm + nb)]
-        bytes_call = (float(np.mean(nus)) + w.n_shared) * w.expert_bytes
-        out["per_T"][T] = {"us_per_call": round(1000 * ms, 2), "us_per_position": round(1000 * ms / T, 2),
+            for b in range(warm):
+                call(b)
+            ctx.sync()
+            ms = event_time(torch, stream, lambda: [call(b) for b in range(warm, warm + nb)]) / nb
+            ctx.sync()
+            kern = per_kernel(cm, ctx, lambda: [call(b) for b in range(warm, warm + nb)])
+            nus = [int(unions[b].n_unique.item()) for b in range(warm, warm + nb)]
+            bytes_call = (float(np.mean(nus)) + w.n_shared) * w.expert_bytes
+            out[key][T] = {"us_per_call": round(1000 * ms, 2), "us_per_position": round(1000 * ms / T, 2),
                            "unique_experts_mean": round(float(np.mean(nus)), 2), "int4_bytes_per_call": int(bytes_call),
                            "int4_gbs": round(bytes_call / (ms * 1e-3) / 1e9, 1),
                            "kernels": {k: round(v["avg_us"], 3) for k, v in kern.items()}}
-        del Xs, res, unions
+            del Xs, res, unions
+    ctx.set_expert_top_p(1.0)
     ctx.close()
     del ctx
     torch.cuda.empty_cache()
