@@ -96,9 +96,11 @@ enum colimoe_config_flags {
                            lost too much precision there): the canonical blob
                            layout with one two's-complement byte per weight
                            (colimoe_expert_bytes() = 3*d*f*(1 + 2/64)).
-                           Forward calls take T == 1 on the fp32 path (AUTO or
-                           FP32: dequantisation to fp32, fp32 accumulation);
-                           other T or paths return E_SHAPE */
+                           Forward calls take any T on the fp32 path (AUTO or
+                           FP32: dequantisation to fp32, fp32 accumulation;
+                           each unique expert read once per call, a token's
+                           bits independent of the others); the fixed-point
+                           and bf16 paths return E_SHAPE */
 };
 
 typedef struct colimoe_config {

@@ -262,8 +262,8 @@ enum { PATH_FP32 = 0, PATH_FXP = 1, PATH_MFMA = 2, PATH_I8 = 3 };
 // least 2048), else fp32 dequantisation.
 static int select_path(colimoe_ctx *ctx, int T, uint32_t flags) {
   const Dims D = dims_of(ctx, T);
-  if (ctx->cfg.flags & COLIMOE_CFG_INT8) {  // int8 experts: one-token calls, fp32 dequantisation
-    if (T != 1 || (flags != COLIMOE_FWD_AUTO && flags != COLIMOE_FWD_FP32)) return COLIMOE_E_SHAPE;
+  if (ctx->cfg.flags & COLIMOE_CFG_INT8) {  // int8 experts: fp32 dequantisation, any T
+    if (flags != COLIMOE_FWD_AUTO && flags != COLIMOE_FWD_FP32) return COLIMOE_E_SHAPE;
     return PATH_I8;
   }
   if (flags == COLIMOE_FWD_BF16_MFMA) return PATH_MFMA;

@@ -1773,14 +1773,18 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(7))) void 
 // ------------------------------------------------------- int8 container
 // Experts stored as int8 gs64 (one two's-complement byte per weight, the
 // canonical blob layout [gate q][gate s][up q][up s][down q][down s], rows
-// row-major) for one-token calls: the pages keep the MTP head in int8
-// because int4 lost too much precision there ([P] lessons on record; [D] §4
-// highlight 2).  One wave per output row; a lane takes 16-column chunks
-// (one 16-byte load) lane, lane + 64, ...; each byte is flipped to offset
-// binary n = q + 128 (XOR 0x80) and converted, and -128 * (sum of the
-// chunk's activations) starts the chunk's sum, so sum n x - 128 sum x =
-// sum q x; times the group scale, accumulated in fp32; the wave's partials
-// are summed by the fixed tree of wave_sum.
+// row-major): the pages keep the MTP head in int8 because int4 lost too much
+// precision there ([P] lessons on record; [D] §4 highlight 2).  One wave per
+// output row of one unique-expert slot; a lane takes 16-column chunks (one
+// 16-byte load) lane, lane + 64, ...; each byte is flipped to offset binary
+// n = q + 128 (XOR 0x80) and converted, and -128 * (sum of the chunk's
+// activations) starts the chunk's sum, so sum n x - 128 sum x = sum q x;
+// times the group scale, accumulated in fp32; the wave's partials are summed
+// by the fixed tree of wave_sum.  The slot's tokens are taken kI8Tok at a
+// time, each chunk's weights loaded once for all of them (the batch-union
+// read of [A] §2); per token the operations do not depend on the others, so
+// a token's bits are those of the token alone.
+constexpr int kI8Tok = 4;
 
 // Sum over 16 columns of (n_i - 128) x_i for the 16 bytes of w and x[0..15].
 __device__ __forceinline__ float chunk_dot_i8(const uint4 &w, const float4 (&xv)[4]) {
@@ -1814,8 +1818,10 @@ __device__ __forceinline__ bool slot_i8(const Dims &D, const UnionDev &U, int s,
   return true;
 }
 
-// h[orow][j] = SiLU(gate_j . x) * (up_j . x); grid (f/4, slots), 4 waves a block.
-__global__ __launch_bounds__(256) void k_gateup_i8(LayerDev L, Dims D, const float *__restrict__ x, UnionDev U,
+// One token: h[orow][j] = SiLU(gate_j . x) * (up_j . x); grid (f/4, slots),
+// 4 waves a block (the per-token operations of k_gateup_i8, without the
+// token loop).
+__global__ __launch_bounds__(256) void k_gateup_i8_one(LayerDev L, Dims D, const float *__restrict__ x, UnionDev U,
                                                    float *__restrict__ h) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int j = blockIdx.x * 4 + wave;
@@ -1838,8 +1844,8 @@ __global__ __launch_bounds__(256) void k_gateup_i8(LayerDev L, Dims D, const flo
   if (lane == 0) h[(size_t)orow * D.f + j] = silu_f(g) * u;
 }
 
-// y[orow][r] = down_r . h[orow]; grid (d/4, slots), 4 waves a block.
-__global__ __launch_bounds__(256) void k_down_i8(LayerDev L, Dims D, const float *__restrict__ h, UnionDev U,
+// One token: y[orow][r] = down_r . h[orow]; grid (d/4, slots), 4 waves a block.
+__global__ __launch_bounds__(256) void k_down_i8_one(LayerDev L, Dims D, const float *__restrict__ h, UnionDev U,
                                                  float *__restrict__ y) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r = blockIdx.x * 4 + wave;
@@ -1859,6 +1865,99 @@ __global__ __launch_bounds__(256) void k_down_i8(LayerDev L, Dims D, const float
   }
   const float v = wave_sum(acc);
   if (lane == 0) y[(size_t)orow * D.d + r] = v;
+}
+
+// h[orow][j] = SiLU(gate_j . x_t) * (up_j . x_t) for every pair (t, orow) of
+// slot blockIdx.y; grid (f/4, slots), 4 waves a block.
+__global__ __launch_bounds__(256) void k_gateup_i8(LayerDev L, Dims D, const float *__restrict__ x, UnionDev U,
+                                                   float *__restrict__ h) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int j = blockIdx.x * 4 + wave, s = blockIdx.y;
+  const int nu = clamp_nu(U.n_unique, D);
+  int e, p0, p1;
+  if (j >= D.f || s > nu || (s == nu && !D.n_shared) || !resolve_slot(D, U, nu, s, e, p0, p1)) return;
+  const size_t w = (size_t)D.d * D.f, ns = w / kGroup * 2;
+  const uint8_t *base = expert_base(L, e);
+  const uint8_t *gq = base + (size_t)j * D.d, *uq = base + w + ns + (size_t)j * D.d;
+  const uint8_t *gs = base + w + (size_t)j * (D.d / kGroup) * 2, *us = base + 2 * w + ns + (size_t)j * (D.d / kGroup) * 2;
+  for (int pg = p0; pg < p1; pg += kI8Tok) {
+    const int mc = min(kI8Tok, p1 - pg);
+    int tm[kI8Tok], om[kI8Tok];
+    float ag[kI8Tok], au[kI8Tok];
+#pragma unroll
+    for (int m = 0; m < kI8Tok; ++m) {
+      tm[m] = 0;
+      om[m] = -1;
+      if (m < mc) slot_token(D, U, nu, s, pg + m, tm[m], om[m]);
+      ag[m] = 0.0f;
+      au[m] = 0.0f;
+    }
+    for (int c = lane; c < D.d / 16; c += 64) {
+      const uint4 wg = *(const uint4 *)(gq + 16 * (size_t)c), wu = *(const uint4 *)(uq + 16 * (size_t)c);
+      const float sg = half_at(gs, c >> 2), su = half_at(us, c >> 2);
+#pragma unroll
+      for (int m = 0; m < kI8Tok; ++m)
+        if (m < mc) {
+          float4 xv[4];
+          const float *xr = x + (size_t)tm[m] * D.d;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) xv[i] = *(const float4 *)(xr + 16 * (size_t)c + 4 * i);
+          ag[m] = __builtin_fmaf(sg, chunk_dot_i8(wg, xv), ag[m]);
+          au[m] = __builtin_fmaf(su, chunk_dot_i8(wu, xv), au[m]);
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < kI8Tok; ++m)
+      if (m < mc) {
+        const float g = wave_sum(ag[m]), u = wave_sum(au[m]);
+        if (lane == 0 && om[m] >= 0) h[(size_t)om[m] * D.f + j] = silu_f(g) * u;
+      }
+  }
+}
+
+// y[orow][r] = down_r . h[orow] for every pair of slot blockIdx.y; grid
+// (d/4, slots), 4 waves a block.
+__global__ __launch_bounds__(256) void k_down_i8(LayerDev L, Dims D, const float *__restrict__ h, UnionDev U,
+                                                 float *__restrict__ y) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + wave, s = blockIdx.y;
+  const int nu = clamp_nu(U.n_unique, D);
+  int e, p0, p1;
+  if (r >= D.d || s > nu || (s == nu && !D.n_shared) || !resolve_slot(D, U, nu, s, e, p0, p1)) return;
+  const size_t w = (size_t)D.d * D.f, ns = w / kGroup * 2;
+  const uint8_t *base = expert_base(L, e) + 2 * (w + ns);
+  const uint8_t *dq = base + (size_t)r * D.f, *ds = base + w + (size_t)r * (D.f / kGroup) * 2;
+  for (int pg = p0; pg < p1; pg += kI8Tok) {
+    const int mc = min(kI8Tok, p1 - pg);
+    int om[kI8Tok];
+    float acc[kI8Tok];
+#pragma unroll
+    for (int m = 0; m < kI8Tok; ++m) {
+      int t = 0;
+      om[m] = -1;
+      if (m < mc) slot_token(D, U, nu, s, pg + m, t, om[m]);
+      acc[m] = 0.0f;
+    }
+    for (int c = lane; c < D.f / 16; c += 64) {
+      const uint4 wd = *(const uint4 *)(dq + 16 * (size_t)c);
+      const float sd = half_at(ds, c >> 2);
+#pragma unroll
+      for (int m = 0; m < kI8Tok; ++m)
+        if (m < mc && om[m] >= 0) {
+          float4 hv[4];
+          const float *hr = h + (size_t)om[m] * D.f;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) hv[i] = *(const float4 *)(hr + 16 * (size_t)c + 4 * i);
+          acc[m] = __builtin_fmaf(sd, chunk_dot_i8(wd, hv), acc[m]);
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < kI8Tok; ++m)
+      if (m < mc) {
+        const float v = wave_sum(acc[m]);
+        if (lane == 0 && om[m] >= 0) y[(size_t)om[m] * D.d + r] = v;
+      }
+  }
 }
 
 // ------------------------------------------------- narrow shapes (K < 2048)
@@ -2548,10 +2647,15 @@ hipError_t launch_rmsnorm(const float *r, int T, int d, float eps, float *x, hip
 
 hipError_t launch_forward_i8(const LayerDev &L, const Dims &D, const float *x, const UnionDev &U, float *h, float *y,
                              hipStream_t s) {
-  if (D.T != 1) return hipErrorInvalidValue;
-  const int slots = D.k + D.n_shared;
-  k_gateup_i8<<<dim3((D.f + 3) / 4, slots), 256, 0, s>>>(L, D, x, U, h);
-  k_down_i8<<<dim3((D.d + 3) / 4, slots), 256, 0, s>>>(L, D, h, U, y);
+  if (D.T <= 0) return hipSuccess;
+  const int slots = slots_max(D);
+  if (D.T == 1) {
+    k_gateup_i8_one<<<dim3((D.f + 3) / 4, slots), 256, 0, s>>>(L, D, x, U, h);
+    k_down_i8_one<<<dim3((D.d + 3) / 4, slots), 256, 0, s>>>(L, D, h, U, y);
+  } else {
+    k_gateup_i8<<<dim3((D.f + 3) / 4, slots), 256, 0, s>>>(L, D, x, U, h);
+    k_down_i8<<<dim3((D.d + 3) / 4, slots), 256, 0, s>>>(L, D, h, U, y);
+  }
   return hipGetLastError();
 }
 

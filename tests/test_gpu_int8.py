@@ -1,7 +1,8 @@
-"""int8 gs64 expert container (COLIMOE_CFG_INT8): one-token calls against the
-oracle reading the same int8 blobs.  Bound per output: the fp32 path's
-|gpu - oracle| <= 1e-3 (1 + |oracle|); routing, gate weights and union lists
-as on the int4 path.  Calls the int8 container does not serve are refused.
+"""int8 gs64 expert container (COLIMOE_CFG_INT8): one-token and batched
+calls against the oracle reading the same int8 blobs.  Bound per output: the
+fp32 path's |gpu - oracle| <= 1e-3 (1 + |oracle|); routing, gate weights and
+union lists as on the int4 path; a batched token carries the bits of the
+token alone.  Paths the int8 container does not serve are refused.
 """
 import numpy as np
 import pytest
@@ -20,7 +21,7 @@ RAGGED8 = synth.Workload(name="ragged8", d=320, f=192, E=37, k=3, T=3, n_shared=
                          seed=synth.BASE_SEED + 402)
 
 
-def _ctx(w, max_tokens=2):
+def _ctx(w, max_tokens=4):
     import int4_routed_expert_fp32_amd as cm
     from int4_routed_expert_fp32_amd.runtime import MoeContext
     print("context", w.name, w.d, w.f, w.E, w.k, "int8", flush=True)
@@ -52,6 +53,28 @@ def test_int8_layer_parity(w):
     ctx.close()
 
 
+# Batched int8 calls: the slot's tokens four at a time (T = 3 in one group,
+# 6 and 16 across groups; union16's correlated positions share experts)
+U8 = synth.Workload(name="u8", d=6144, f=2048, E=32, k=8, T=16, n_shared=1, zipf=1.1, rho=0.6, bits=8,
+                    seed=synth.BASE_SEED + 403)
+
+
+@pytest.mark.parametrize("w,T", [(RAGGED8, 3), (U8, 6), (U8, 16)], ids=["ragged8-3", "u8-6", "u8-16"])
+def test_int8_batched_parity_and_identity(w, T):
+    ctx = _ctx(w, max_tokens=T)
+    P.load_layer(ctx, w, 0)
+    ora = P.OracleLayer(w, 0)
+    X = synth.activations(w.with_(T=T), stream=53)
+    with oracle.container_bits(8):
+        r = P.layer_parity(ctx, w.with_(T=T), 0, X, ora)
+        print("%s T=%d: unique experts %d, worst ratio %.3g" % (w.name, T, r["union"]["n_unique"], r["ratio"]))
+        for t in range(T):
+            a = P.layer_parity(ctx, w, 0, X[t:t + 1], ora, one_call=True)
+            assert np.array_equal(a["idx"][0], r["idx"][t])
+            assert np.array_equal(a["out"][0].view(np.uint32), r["out"][t].view(np.uint32)), t
+    ctx.close()
+
+
 def test_int8_refusals():
     import int4_routed_expert_fp32_amd as cm
     w = TINY8
@@ -62,9 +85,7 @@ def test_int8_refusals():
     idx[:, 1] = 1
     wt = torch.full((2, w.k), 0.5, dtype=torch.float32, device="cuda")
     res = x.clone()
-    # more than one token, or a path other than the fp32 one
-    assert cm.colimoe_forward(ctx.ctx, 0, x.data_ptr(), 2, idx.data_ptr(), wt.data_ptr(), None, res.data_ptr(), 0,
-                              check=False) == cm.COLIMOE_E_SHAPE
+    # a path other than the fp32 one
     for flags in (cm.COLIMOE_FWD_FXP, cm.COLIMOE_FWD_BF16_MFMA):
         assert cm.colimoe_forward(ctx.ctx, 0, x.data_ptr(), 1, idx.data_ptr(), wt.data_ptr(), None, res.data_ptr(),
                                   flags, check=False) == cm.COLIMOE_E_SHAPE
