@@ -15,8 +15,9 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 FXP = 3
-# decode-sized experts (fixed-point path; 1 token and batch-union shapes) on
-# a smaller expert count, and the tiny layer (fp32 path)
+# decode-sized experts (fixed-point path, 1 token and batch-union shapes, and
+# the fp32 path's one-token pair) on a smaller expert count, and the tiny
+# layer (fp32 path)
 WIDE = synth.Workload(name="static_wide", d=6144, f=2048, E=32, k=8, T=16, n_shared=1, zipf=1.1, rho=0.6,
                       seed=synth.BASE_SEED + 401)
 TINY = synth.WORKLOADS["tiny"]
@@ -55,8 +56,9 @@ def _run(fn, ctx_handle, X, with_union, flags):
     return out
 
 
-@pytest.mark.parametrize("w,flags,sizes", [(WIDE, FXP, (16, 1)), (WIDE, FXP, (5, 2)), (TINY, 1, (3, 1))],
-                         ids=["wide-16-then-1", "wide-5-then-2", "tiny"])
+@pytest.mark.parametrize("w,flags,sizes", [(WIDE, FXP, (16, 1)), (WIDE, FXP, (5, 2)), (WIDE, 1, (3, 1)),
+                                           (TINY, 1, (3, 1))],
+                         ids=["wide-16-then-1", "wide-5-then-2", "wide-fp32-3-then-1", "tiny"])
 def test_static_matches_route_forward(w, flags, sizes):
     import int4_routed_expert_fp32_amd as cm
     ctx, bare = _ctx(w, max_tokens=max(sizes), workspace=False)
