@@ -12,6 +12,7 @@ namespace colimoe {
 // uint4 class type is copied through memory, which keeps staged data off
 // registers).
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // Buffer resource over `bytes` bytes at p (p wave-uniform): loads through it
 // take a per-lane offset plus a scalar offset, and loads past the end read 0.

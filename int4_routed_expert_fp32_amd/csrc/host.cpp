@@ -403,13 +403,14 @@ static int forward_kernels(colimoe_ctx *ctx, int32_t layer, const float *x, int3
       if (launch_down_tok(L, D, U, hq, hs, y, s) != hipSuccess) return COLIMOE_E_HIP;
     }
   } else if (fused && f32_dec_supported(D)) {
+    float *hsum = (float *)(ctx->ws + ctx->wl.hs);
     {
       KTimer kt(ctx, K_GATEUP);
-      if (launch_gateup_f32_dec(L, D, x, U, h, s) != hipSuccess) return COLIMOE_E_HIP;
+      if (launch_gateup_f32_dec(L, D, x, U, h, hsum, s) != hipSuccess) return COLIMOE_E_HIP;
     }
     {
       KTimer kt(ctx, K_DOWN);
-      if (launch_down_f32_dec(L, D, h, U, w, residual, s) != hipSuccess) return COLIMOE_E_HIP;
+      if (launch_down_f32_dec(L, D, h, hsum, U, w, residual, s) != hipSuccess) return COLIMOE_E_HIP;
     }
   } else {
     {

@@ -164,13 +164,14 @@ hipError_t launch_down_dec(const LayerDev &L, const Dims &D, const uint32_t *hq,
                            const float *wslot, float *residual, hipStream_t s);
 // The fp32 dequantisation path for one token (d <= 8192, f a multiple of 16,
 // down fusable, k + shared <= 16): gate/up writes h in a layout of its own
-// that only launch_down_f32_dec reads; down adds the combined output to
-// residual.  Bits equal to launch_gateup + fused launch_down.
+// that only launch_down_f32_dec reads, with h's sums over 16 columns in
+// hsum ([rows][f/16]); down adds the combined output to residual.  Bits
+// equal to launch_gateup + fused launch_down.
 bool f32_dec_supported(const Dims &D);
 hipError_t launch_gateup_f32_dec(const LayerDev &L, const Dims &D, const float *x, const UnionDev &U, float *h,
-                                 hipStream_t s);
-hipError_t launch_down_f32_dec(const LayerDev &L, const Dims &D, const float *h, const UnionDev &U, const float *w,
-                               float *residual, hipStream_t s);
+                                 float *hsum, hipStream_t s);
+hipError_t launch_down_f32_dec(const LayerDev &L, const Dims &D, const float *h, const float *hsum, const UnionDev &U,
+                               const float *w, float *residual, hipStream_t s);
 // Router for many tokens on the matrix cores (fp32), with S = router_splits(d)
 // K-slices whose partials (part: [S][T][E]) are summed in slice order.
 int router_splits(int d);

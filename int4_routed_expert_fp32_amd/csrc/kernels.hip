@@ -642,8 +642,9 @@ constexpr int kXPad = 36;      // LDS floats per 32-activation chunk
 constexpr int kF32DecTPW = 1;  // tiles per wave
 template <int NS, int TPW>
 __global__ __launch_bounds__(256) void k_gateup_f32_dec(LayerDev L, Dims D, const float *__restrict__ x, UnionDev U,
-                                                        float *__restrict__ h) {
+                                                        float *__restrict__ h, float *__restrict__ hsum) {
   __shared__ __attribute__((aligned(16))) float xl[NS * 64 * kXPad];
+  __shared__ float s4[4];    // each wave's float4 sum of h
   __shared__ int slot_s[2];  // expert, output row
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int C = D.d / kChunk, groups = D.f / (16 * TPW);
@@ -747,10 +748,16 @@ __global__ __launch_bounds__(256) void k_gateup_f32_dec(LayerDev L, Dims D, cons
     if (st == NS - 1) {
       // gate row r (lane 8r + 7) meets up row r + 4 (lane 8r + 39)
       const float u = bits_f(xor32(f_bits(tot)));
-      if ((lane & 7) == 7 && lane < 32)
-        h[(size_t)orow * D.f + h_ilv(ti * 4 + (lane >> 3), D.f / kChunk)] = silu_f(tot) * u;
+      const float hv = silu_f(tot) * u;
+      if ((lane & 7) == 7 && lane < 32) h[(size_t)orow * D.f + h_ilv(ti * 4 + (lane >> 3), D.f / kChunk)] = hv;
+      // the sum of this float4 of h, in neg8_sum's order
+      const float a = __shfl(hv, 7, 64), b = __shfl(hv, 15, 64), c = __shfl(hv, 23, 64), d = __shfl(hv, 31, 64);
+      if (lane == 0) s4[wave] = (a + b) + (c + d);
     }
   }
+  // the block's 4 float4s are half a 32-column chunk: its first-level sum
+  __syncthreads();
+  if (threadIdx.x == 0) hsum[(size_t)orow * (D.f / 16) + grp] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
 }
 
 // A7 for one 8-row output tile, y of every pair in LDS: per token and row,
@@ -1678,10 +1685,13 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(6))) void 
 // fma(scale, chunk_dot, acc), the fixed 8-row tree), and the combine adds
 // the routed experts in ascending pair order with their gate weights, then
 // the shared expert, as combine_tile does: the bits are those of the fused
-// k_down_wide.  h rows come in the pair's interleaved layout (h_ilv).
+// k_down_wide.  h rows come in the pair's interleaved layout (h_ilv), with
+// the two half-chunk sums the gate/up kernel formed in neg8_sum's order
+// (hsum), so chunk_dot can run a word's 8 columns at a time for all 8 rows
+// with only those columns' activations in registers.
 __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(7))) void k_down_f32_dec(
-    LayerDev L, Dims D, const float *__restrict__ h, UnionDev U, const float *__restrict__ w,
-    float *__restrict__ residual) {
+    LayerDev L, Dims D, const float *__restrict__ h, const float *__restrict__ hsum, UnionDev U,
+    const float *__restrict__ w, float *__restrict__ residual) {
   __shared__ float vb[kDecMaxSlots][kTileRows];
   __shared__ int ok_s[kDecMaxSlots];
   __shared__ float wsl_s[kDecMaxSlots];
@@ -1708,11 +1718,12 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(7))) void 
     // buffer loads: the lane's offset in a VGPR, the rest in the scalar
     // offset; a lane past the row end reads a valid chunk (the row's last)
     // and keeps its sums unchanged
+    const int hrow = wave < nu ? p0 : D.T * D.k;
     const uint8_t *base = expert_base(L, ok ? e : 0);
     const __amdgpu_buffer_rsrc_t rn = wave_rsrc(base + EL.dn_nib, (uint32_t)(EL.dn_sc - EL.dn_nib));
     const __amdgpu_buffer_rsrc_t rs = wave_rsrc(base + EL.dn_sc, (uint32_t)(EL.bytes - EL.dn_sc));
-    const __amdgpu_buffer_rsrc_t rh =
-        wave_rsrc(h + (size_t)(wave < nu ? p0 : D.T * D.k) * D.f, (uint32_t)D.f * 4u);
+    const __amdgpu_buffer_rsrc_t rh = wave_rsrc(h + (size_t)hrow * D.f, (uint32_t)D.f * 4u);
+    const __amdgpu_buffer_rsrc_t rq = wave_rsrc(hsum + (size_t)hrow * (D.f / 16), (uint32_t)D.f / 4u);
     float acc[kTileRows];
 #pragma unroll
     for (int r = 0; r < kTileRows; ++r) acc[r] = 0.0f;
@@ -1721,41 +1732,56 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(7))) void 
       const bool live = lane < width;
       const int cl = live ? lane : width - 1;
       const int tb = ti * kTileRows * (D.f / 2) + j * (kTileRows * 64 * 16);
+      uint4 W[kTileRows];
+#pragma unroll
+      for (int r = 0; r < kTileRows; ++r) {
+        const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(rn, cl * 16, tb + r * width * 16, 0);
+        W[r] = make_uint4(t.x, t.y, t.z, t.w);
+      }
       const u32x4 Sv =
           __builtin_amdgcn_raw_buffer_load_b128(rs, (cl >> 1) * 16, (ti * (D.f / kGroup) + 32 * j) * 16, 0);
       const uint4 S = make_uint4(Sv.x, Sv.y, Sv.z, Sv.w);
-      float4 xv[8];
+      // -8 sum of the chunk's 32 activations: the two halves in order
+      const u32x2 hq2 = __builtin_amdgcn_raw_buffer_load_b64(rq, cl * 8, 64 * j * 8, 0);
+      const float nsx = -8.0f * (bits_f(hq2[0]) + bits_f(hq2[1]));
+      float alo[kTileRows], ahi[kTileRows];
 #pragma unroll
-      for (int v = 0; v < 8; ++v) {
-        const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(rh, cl * 16, (v * C + 64 * j) * 16, 0);
+      for (int r = 0; r < kTileRows; ++r) {
+        alo[r] = nsx;
+        ahi[r] = 0.0f;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
         // (elements by index: hipcc turns __builtin_bit_cast of a vector
         // element .y/.z/.w into element 0)
-        xv[v] = make_float4(bits_f(t[0]), bits_f(t[1]), bits_f(t[2]), bits_f(t[3]));
-      }
-      // the tile's rows in two halves of 4, the second half's weights
-      // loaded after the first half's sums: the activations, one half's
-      // weights and the sums fit the register budget of 3 blocks per CU
-      float a[kTileRows];
-      float nsx = 0.0f;
+        const u32x4 ta = __builtin_amdgcn_raw_buffer_load_b128(rh, cl * 16, ((2 * i) * C + 64 * j) * 16, 0);
+        const u32x4 tb2 = __builtin_amdgcn_raw_buffer_load_b128(rh, cl * 16, ((2 * i + 1) * C + 64 * j) * 16, 0);
+        const float4 xa = make_float4(bits_f(ta[0]), bits_f(ta[1]), bits_f(ta[2]), bits_f(ta[3]));
+        const float4 xb = make_float4(bits_f(tb2[0]), bits_f(tb2[1]), bits_f(tb2[2]), bits_f(tb2[3]));
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        uint4 W[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(rn, cl * 16, tb + (4 * hf + r) * width * 16, 0);
-          W[r] = make_uint4(t.x, t.y, t.z, t.w);
+        for (int r = 0; r < kTileRows; ++r) {
+          const uint32_t wi = (i == 0 ? W[r].x : i == 1 ? W[r].y : i == 2 ? W[r].z : W[r].w) ^ 0x88888888u;
+          uint32_t lo = wi & 0x0F0F0F0Fu, hi = wi & 0xF0F0F0F0u;
+          asm("" : "+v"(lo), "+v"(hi));
+          alo[r] = __builtin_fmaf((float)(lo & 0xFFu), xa.x, alo[r]);
+          alo[r] = __builtin_fmaf((float)((lo >> 8) & 0xFFu), xa.z, alo[r]);
+          alo[r] = __builtin_fmaf((float)((lo >> 16) & 0xFFu), xb.x, alo[r]);
+          alo[r] = __builtin_fmaf((float)(lo >> 24), xb.z, alo[r]);
+          ahi[r] = __builtin_fmaf((float)(hi & 0xFFu), xa.y, ahi[r]);
+          ahi[r] = __builtin_fmaf((float)((hi >> 8) & 0xFFu), xa.w, ahi[r]);
+          ahi[r] = __builtin_fmaf((float)((hi >> 16) & 0xFFu), xb.y, ahi[r]);
+          ahi[r] = __builtin_fmaf((float)(hi >> 24), xb.w, ahi[r]);
         }
-        if (hf == 0) nsx = neg8_sum(xv);
+        // the word's sums are due here: one word's masks and activations
+        // live at a time
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int rr = 4 * hf + r;
-          a[rr] = __builtin_fmaf(tile_scale(S, rr), chunk_dot(W[r], xv, nsx), acc[rr]);
-          asm volatile("" : "+v"(a[rr]));
-        }
-        __builtin_amdgcn_sched_barrier(0);
+        for (int r = 0; r < kTileRows; ++r) asm volatile("" : "+v"(alo[r]), "+v"(ahi[r]));
       }
 #pragma unroll
-      for (int r = 0; r < kTileRows; ++r) acc[r] = live ? a[r] : acc[r];
+      for (int r = 0; r < kTileRows; ++r) {
+        const float a = __builtin_fmaf(tile_scale(S, r), __builtin_fmaf(ahi[r], 0.0625f, alo[r]), acc[r]);
+        acc[r] = live ? a : acc[r];
+      }
     }
     const float v = reduce8_rows(acc);
     if ((lane & 7) == 7) vb[wave][lane >> 3] = v;
@@ -2601,23 +2627,23 @@ bool f32_dec_supported(const Dims &D) {
 }
 
 hipError_t launch_gateup_f32_dec(const LayerDev &L, const Dims &D, const float *x, const UnionDev &U, float *h,
-                                 hipStream_t s) {
+                                 float *hsum, hipStream_t s) {
   if (!f32_dec_supported(D)) return hipErrorInvalidValue;
   const int NS = (D.d / kChunk + 63) / 64;
   const int grid = slots_max(D) * (D.f / (16 * kF32DecTPW));
   switch (NS) {
-    case 1: k_gateup_f32_dec<1, kF32DecTPW><<<grid, 256, 0, s>>>(L, D, x, U, h); break;
-    case 2: k_gateup_f32_dec<2, kF32DecTPW><<<grid, 256, 0, s>>>(L, D, x, U, h); break;
-    case 3: k_gateup_f32_dec<3, kF32DecTPW><<<grid, 256, 0, s>>>(L, D, x, U, h); break;
-    default: k_gateup_f32_dec<4, kF32DecTPW><<<grid, 256, 0, s>>>(L, D, x, U, h); break;
+    case 1: k_gateup_f32_dec<1, kF32DecTPW><<<grid, 256, 0, s>>>(L, D, x, U, h, hsum); break;
+    case 2: k_gateup_f32_dec<2, kF32DecTPW><<<grid, 256, 0, s>>>(L, D, x, U, h, hsum); break;
+    case 3: k_gateup_f32_dec<3, kF32DecTPW><<<grid, 256, 0, s>>>(L, D, x, U, h, hsum); break;
+    default: k_gateup_f32_dec<4, kF32DecTPW><<<grid, 256, 0, s>>>(L, D, x, U, h, hsum); break;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_down_f32_dec(const LayerDev &L, const Dims &D, const float *h, const UnionDev &U, const float *w,
-                               float *residual, hipStream_t s) {
+hipError_t launch_down_f32_dec(const LayerDev &L, const Dims &D, const float *h, const float *hsum, const UnionDev &U,
+                               const float *w, float *residual, hipStream_t s) {
   if (!f32_dec_supported(D)) return hipErrorInvalidValue;
-  k_down_f32_dec<<<D.d / kTileRows, 64 * (D.k + D.n_shared), 0, s>>>(L, D, h, U, w, residual);
+  k_down_f32_dec<<<D.d / kTileRows, 64 * (D.k + D.n_shared), 0, s>>>(L, D, h, hsum, U, w, residual);
   return hipGetLastError();
 }
 
