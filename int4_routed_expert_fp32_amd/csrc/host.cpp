@@ -356,10 +356,14 @@ static int forward_kernels(colimoe_ctx *ctx, int32_t layer, const float *x, int3
   }
   float *h = (float *)(ctx->ws + ctx->wl.h);
   float *y = (float *)(ctx->ws + ctx->wl.y);
-  const bool fused = path == PATH_FP32 && down_fusable(D);
+  const bool fused = (path == PATH_FP32 && down_fusable(D)) || (path == PATH_I8 && i8_dec_supported(D));
   if (path == PATH_I8) {
     KTimer kt(ctx, K_GATEUP);
-    if (launch_forward_i8(L, D, x, U, h, y, s) != hipSuccess) return COLIMOE_E_HIP;
+    if (fused) {
+      if (launch_forward_i8_dec(L, D, x, U, h, w, residual, s) != hipSuccess) return COLIMOE_E_HIP;
+    } else if (launch_forward_i8(L, D, x, U, h, y, s) != hipSuccess) {
+      return COLIMOE_E_HIP;
+    }
   } else if (path == PATH_MFMA) {
     int4 *list = (int4 *)(ctx->ws + ctx->wl.mblk);
     int32_t *mcount = (int32_t *)(ctx->ws + ctx->wl.mcount);

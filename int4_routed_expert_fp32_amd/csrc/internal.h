@@ -203,6 +203,12 @@ uint8_t *static_scratch(int device);
 // launch_combine.
 hipError_t launch_forward_i8(const LayerDev &L, const Dims &D, const float *x, const UnionDev &U, float *h, float *y,
                              hipStream_t s);
+// int8 container, one token (d <= 8192, f <= 2048, k + shared <= 16): the same
+// results with the combine into `residual` in the down kernel (w: the gate
+// weights).
+bool i8_dec_supported(const Dims &D);
+hipError_t launch_forward_i8_dec(const LayerDev &L, const Dims &D, const float *x, const UnionDev &U, float *h,
+                                 const float *w, float *residual, hipStream_t s);
 // Bytes of one expert in the int8 container (the canonical layout).
 inline size_t expert_bytes_i8(int d, int f) {
   const size_t w = (size_t)d * (size_t)f;

@@ -1893,6 +1893,129 @@ __global__ __launch_bounds__(256) void k_down_i8_one(LayerDev L, Dims D, const f
   if (lane == 0) y[(size_t)orow * D.d + r] = v;
 }
 
+// The one-token int8 kernels of a decode call.  Per row they perform the
+// operations of k_gateup_i8_one and k_down_i8_one (lane l takes chunks l,
+// l + 64, ... in order, fma(scale, chunk_dot_i8, acc), the wave_sum tree), so
+// the bits are those of the batched int8 kernels; what changes is how many
+// loads a wave has in flight.  Gate/up: a wave per h output issues all NI
+// chunks of its gate and up rows before the arithmetic (a lane past the row
+// end loads the row's last chunk and adds nothing).  Down: a block per
+// kI8Rows output rows (8: every block reads all slots' h rows, so taller
+// tiles read h fewer times), a wave per slot issuing its NI chunks of every
+// row at once; wave 0 then folds the slot outputs into the residual in the order of
+// k_combine (routed experts in pair order, each times its gate weight, then
+// the shared expert).
+constexpr int kI8Rows = 8;
+template <int NI>
+__global__ __launch_bounds__(256) void k_gateup_i8_dec(LayerDev L, Dims D, const float *__restrict__ x, UnionDev U,
+                                                       float *__restrict__ h) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int j = blockIdx.x * 4 + wave;
+  int e, orow;
+  if (j >= D.f || !slot_i8(D, U, blockIdx.y, e, orow)) return;
+  const size_t w = (size_t)D.d * D.f, ns = w / kGroup * 2;
+  const uint8_t *base = expert_base(L, e);
+  const uint8_t *gq = base + (size_t)j * D.d, *uq = base + w + ns + (size_t)j * D.d;
+  const uint8_t *gs = base + w + (size_t)j * (D.d / kGroup) * 2, *us = base + 2 * w + ns + (size_t)j * (D.d / kGroup) * 2;
+  const int C = D.d / 16;
+  uint4 Wg[NI], Wu[NI];
+  float sg[NI], su[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int c = lane + 64 * i, cl = c < C ? c : C - 1;
+    Wg[i] = *(const uint4 *)(gq + 16 * (size_t)cl);
+    Wu[i] = *(const uint4 *)(uq + 16 * (size_t)cl);
+    sg[i] = half_at(gs, cl >> 2);
+    su[i] = half_at(us, cl >> 2);
+  }
+  float ag = 0.0f, au = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int c = lane + 64 * i;
+    if (c < C) {
+      float4 xv[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) xv[k] = *(const float4 *)(x + 16 * (size_t)c + 4 * k);
+      ag = __builtin_fmaf(sg[i], chunk_dot_i8(Wg[i], xv), ag);
+      au = __builtin_fmaf(su[i], chunk_dot_i8(Wu[i], xv), au);
+    }
+  }
+  const float g = wave_sum(ag), u = wave_sum(au);
+  if (lane == 0) h[(size_t)orow * D.f + j] = silu_f(g) * u;
+}
+
+template <int NI>
+__global__ __launch_bounds__(64 * kDecMaxSlots) void k_down_i8_dec(LayerDev L, Dims D, const float *__restrict__ h,
+                                                                UnionDev U, const float *__restrict__ w,
+                                                                float *__restrict__ residual) {
+  __shared__ float vb[kDecMaxSlots][kI8Rows];
+  __shared__ int ok_s[kDecMaxSlots];
+  __shared__ float wsl_s[kDecMaxSlots];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r0 = blockIdx.x * kI8Rows;
+  const int nu = clamp_nu(U.n_unique, D);
+  const int slots = nu + D.n_shared;
+  float rin = 0.0f;
+  if (wave == 0 && lane < kI8Rows) rin = residual[r0 + lane];
+  if (wave < slots) {
+    int e, p0, p1;
+    const bool ok = resolve_slot(D, U, nu, wave, e, p0, p1) && p1 > p0;
+    if (lane == 0) {
+      float g = 1.0f;
+      if (wave < nu) {
+        int js = U.pair_slot[p0];
+        js = js < 0 ? 0 : (js >= D.k ? D.k - 1 : js);  // caller-supplied lists stay in bounds
+        g = w[js];
+      }
+      wsl_s[wave] = g;
+      ok_s[wave] = ok;
+    }
+    const size_t wsz = (size_t)D.d * D.f, ns = wsz / kGroup * 2;
+    const uint8_t *dq = expert_base(L, ok ? e : 0) + 2 * (wsz + ns);
+    const uint8_t *ds = dq + wsz;
+    const float *hr = h + (size_t)(wave < nu ? p0 : D.T * D.k) * D.f;
+    const int C = D.f / 16;
+    uint4 W[kI8Rows][NI];
+    float sc[kI8Rows][NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int c = lane + 64 * i, cl = c < C ? c : C - 1;
+#pragma unroll
+      for (int r = 0; r < kI8Rows; ++r) {
+        W[r][i] = *(const uint4 *)(dq + (size_t)(r0 + r) * D.f + 16 * (size_t)cl);
+        sc[r][i] = half_at(ds + (size_t)(r0 + r) * (D.f / kGroup) * 2, cl >> 2);
+      }
+    }
+    float acc[kI8Rows];
+#pragma unroll
+    for (int r = 0; r < kI8Rows; ++r) acc[r] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int c = lane + 64 * i;
+      if (c < C) {
+        float4 hv[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) hv[k] = *(const float4 *)(hr + 16 * (size_t)c + 4 * k);
+#pragma unroll
+        for (int r = 0; r < kI8Rows; ++r) acc[r] = __builtin_fmaf(sc[r][i], chunk_dot_i8(W[r][i], hv), acc[r]);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < kI8Rows; ++r) {
+      const float v = wave_sum(acc[r]);
+      if (lane == 0) vb[wave][r] = v;
+    }
+  }
+  __syncthreads();
+  if (wave == 0 && lane < kI8Rows) {
+    float out = rin;
+    for (int sl = 0; sl < nu; ++sl)
+      if (ok_s[sl]) out = __builtin_fmaf(wsl_s[sl], vb[sl][lane], out);
+    if (D.n_shared && ok_s[nu]) out = out + vb[nu][lane];
+    residual[r0 + lane] = out;
+  }
+}
+
 // h[orow][j] = SiLU(gate_j . x_t) * (up_j . x_t) for every pair (t, orow) of
 // slot blockIdx.y; grid (f/4, slots), 4 waves a block.
 __global__ __launch_bounds__(256) void k_gateup_i8(LayerDev L, Dims D, const float *__restrict__ x, UnionDev U,
@@ -2668,6 +2791,33 @@ hipError_t launch_combine(const Dims &D, const float *w, const UnionDev &U, cons
 hipError_t launch_rmsnorm(const float *r, int T, int d, float eps, float *x, hipStream_t s) {
   if (T <= 0) return hipSuccess;
   k_rmsnorm<<<T, 512, 0, s>>>(r, d, eps, x);
+  return hipGetLastError();
+}
+
+bool i8_dec_supported(const Dims &D) {
+  const int gi = (D.d / 16 + 63) / 64, di = (D.f / 16 + 63) / 64;
+  return D.T == 1 && D.d % kI8Rows == 0 && gi <= 8 && di <= 2 && D.k + D.n_shared <= kDecMaxSlots;
+}
+
+hipError_t launch_forward_i8_dec(const LayerDev &L, const Dims &D, const float *x, const UnionDev &U, float *h,
+                                 const float *w, float *residual, hipStream_t s) {
+  if (!i8_dec_supported(D)) return hipErrorInvalidValue;
+  const dim3 gg((D.f + 3) / 4, slots_max(D));
+  switch ((D.d / 16 + 63) / 64) {
+    case 1: k_gateup_i8_dec<1><<<gg, 256, 0, s>>>(L, D, x, U, h); break;
+    case 2: k_gateup_i8_dec<2><<<gg, 256, 0, s>>>(L, D, x, U, h); break;
+    case 3: k_gateup_i8_dec<3><<<gg, 256, 0, s>>>(L, D, x, U, h); break;
+    case 4: k_gateup_i8_dec<4><<<gg, 256, 0, s>>>(L, D, x, U, h); break;
+    case 5: k_gateup_i8_dec<5><<<gg, 256, 0, s>>>(L, D, x, U, h); break;
+    case 6: k_gateup_i8_dec<6><<<gg, 256, 0, s>>>(L, D, x, U, h); break;
+    case 7: k_gateup_i8_dec<7><<<gg, 256, 0, s>>>(L, D, x, U, h); break;
+    default: k_gateup_i8_dec<8><<<gg, 256, 0, s>>>(L, D, x, U, h); break;
+  }
+  const int threads = 64 * (D.k + D.n_shared);
+  if ((D.f / 16 + 63) / 64 == 1)
+    k_down_i8_dec<1><<<D.d / kI8Rows, threads, 0, s>>>(L, D, h, U, w, residual);
+  else
+    k_down_i8_dec<2><<<D.d / kI8Rows, threads, 0, s>>>(L, D, h, U, w, residual);
   return hipGetLastError();
 }
 
