@@ -19,6 +19,10 @@ DEC8 = synth.Workload(name="dec8", d=6144, f=2048, E=32, k=8, T=3, n_shared=1, z
                       seed=synth.BASE_SEED + 401)
 RAGGED8 = synth.Workload(name="ragged8", d=320, f=192, E=37, k=3, T=3, n_shared=1, bits=8,
                          seed=synth.BASE_SEED + 402)
+# beyond the one-token kernels that fuse the combine (d > 8192, f > 2048): the
+# one-token calls take the general one-token kernels and the combine kernel
+WIDE8 = synth.Workload(name="wide8", d=8256, f=2112, E=5, k=2, T=3, n_shared=1, bits=8,
+                       seed=synth.BASE_SEED + 404)
 
 
 def _ctx(w, max_tokens=4):
@@ -35,7 +39,7 @@ def _builds():
     synth.build(force=False)
 
 
-@pytest.mark.parametrize("w", [TINY8, RAGGED8, DEC8], ids=lambda w: w.name)
+@pytest.mark.parametrize("w", [TINY8, RAGGED8, DEC8, WIDE8], ids=lambda w: w.name)
 def test_int8_layer_parity(w):
     ctx = _ctx(w)
     P.load_layer(ctx, w, 0)
@@ -59,7 +63,8 @@ U8 = synth.Workload(name="u8", d=6144, f=2048, E=32, k=8, T=16, n_shared=1, zipf
                     seed=synth.BASE_SEED + 403)
 
 
-@pytest.mark.parametrize("w,T", [(RAGGED8, 3), (U8, 6), (U8, 16)], ids=["ragged8-3", "u8-6", "u8-16"])
+@pytest.mark.parametrize("w,T", [(RAGGED8, 3), (U8, 6), (U8, 16), (WIDE8, 3)],
+                         ids=["ragged8-3", "u8-6", "u8-16", "wide8-3"])
 def test_int8_batched_parity_and_identity(w, T):
     ctx = _ctx(w, max_tokens=T)
     P.load_layer(ctx, w, 0)
