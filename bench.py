@@ -691,9 +691,11 @@ def main():
                     unit="GB/s", frac=round(gu_gbs / HBM_PEAK_GBS, 4), traffic=measured_traffic(DECODE_GATEUP_KERNEL),
                     bytes_per_launch=gu_experts * gu_bytes, avg_launch_us=round(kern["gateup"]["avg_us"], 3))
 
-    cpu = None
+    cpu, parity = None, None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, args.cpu_seconds)
+        samples = []
+        cpu = cpu_baseline(w, args.cpu_seconds, keep=samples)
+        parity = parity_verdict(torch, np, synth, cm, MoeContext, dev, w, samples)
 
     out = {
         "metric": "MoE-layer decode us/token + int4 expert-weight GB/s vs HBM peak",
@@ -730,6 +732,7 @@ def main():
         "expert_top_p": topp,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "parity": parity,
         "workloads": extra,
     }
     print(json.dumps(out), flush=True)
@@ -748,9 +751,13 @@ def _omp_threads(n=None):
     return int(gomp.omp_get_max_threads())
 
 
-def _oracle_tokens(w, budget_s, max_tokens=64):
+ORACLE_STREAM = 11  # activation stream of the oracle's sample tokens
+
+
+def _oracle_tokens(w, budget_s, max_tokens=64, keep=None):
     """us per token of the oracle (route + forward, fp64) on decode-shaped
-    tokens of layer instance 0, within about budget_s seconds of oracle time."""
+    tokens of layer instance 0, within about budget_s seconds of oracle time;
+    `keep` (a list) receives (token, logits, idx, out) of every token done."""
     import numpy as np
 
     import oracle
@@ -758,7 +765,7 @@ def _oracle_tokens(w, budget_s, max_tokens=64):
     R = synth.router(w, 0)
     b = synth.bias(w, 0)
     shared = synth.shared_blob(w, 0) if w.n_shared else None
-    X = synth.activations(w.with_(T=max_tokens), stream=11)
+    X = synth.activations(w.with_(T=max_tokens), stream=ORACLE_STREAM)
     done, t_cpu = 0, 0.0
     blobs = {}
     while done < X.shape[0] and t_cpu < budget_s:
@@ -770,22 +777,25 @@ def _oracle_tokens(w, budget_s, max_tokens=64):
             if int(e) not in blobs:
                 blobs[int(e)] = synth.expert_blobs(w, 0, int(e), int(e) + 1)[0].copy()
         t = time.perf_counter()
-        oracle.moe_token(x, w.d, w.f, {int(e): blobs[int(e)] for e in idx}, shared, idx, wt, x, w.E)
+        out, _ = oracle.moe_token(x, w.d, w.f, {int(e): blobs[int(e)] for e in idx}, shared, idx, wt, x, w.E)
         t_cpu += time.perf_counter() - t
+        if keep is not None:
+            keep.append((done, l, idx.copy(), out))
         done += 1
     return 1e6 * t_cpu / done, done, t_cpu
 
 
-def cpu_baseline(w, budget_s):
+def cpu_baseline(w, budget_s, keep=None):
     """The oracle (route + forward, fp64) on a bounded sample of decode tokens,
     on the process's cores; then on one core, for the decode and the tiny
-    layer."""
+    layer.  `keep` receives the sample's oracle results (for the parity
+    verdict)."""
     import oracle
     import synth
     oracle.build(force=False)
     cores = len(os.sched_getaffinity(0))
     threads = _omp_threads()
-    us, done, t_cpu = _oracle_tokens(w, budget_s)
+    us, done, t_cpu = _oracle_tokens(w, budget_s, keep=keep)
     prev = _omp_threads(1)
     one = {}
     for name, ww, budget in (("decode", w, max(4.0, budget_s / 3)), ("tiny", synth.WORKLOADS["tiny"], 1.0)):
@@ -802,6 +812,48 @@ def cpu_baseline(w, budget_s):
             "sample": "%d decode tokens of the same layer shape (layer instance 0), route + 8 routed + shared "
                       "expert in fp64, %.1f s" % (done, t_cpu),
             "cpu_model": model, "affinity_cores": cores, "omp_threads": threads, "one_core": one}
+
+
+def parity_verdict(torch, np, synth, cm, MoeContext, dev, w, samples):
+    """The library on the oracle sample's tokens (layer instance 0, residual =
+    x, one call each, both fp32-class paths) against the oracle's outputs:
+    worst |gpu - oracle| / (1e-3 (1 + |oracle|)) per path, tokens whose k-th
+    and (k+1)-th oracle logits lie within 1e-5 (near-ties, where another
+    routing is also correct), and routings that differ elsewhere."""
+    ctx = MoeContext(w.d, w.f, w.E, w.k, n_layers=1, n_shared=w.n_shared, max_tokens=1)
+    ctx.load_layer(0, synth.router(w, 0), synth.bias(w, 0), synth.expert_blobs(w, 0, 0, w.E),
+                   synth.shared_blob(w, 0) if w.n_shared else None)
+    X = synth.activations(w.with_(T=max(t for t, _, _, _ in samples) + 1), stream=ORACLE_STREAM)
+    idx = torch.empty((1, w.k), dtype=torch.int32, device=dev)
+    wt = torch.empty((1, w.k), dtype=torch.float32, device=dev)
+    out = {"tokens": len(samples), "bound": "|gpu - oracle| <= 1e-3 (1 + |oracle|) per output",
+           "oracle": "fp64, the cpu_baseline sample's tokens on layer instance 0, residual = x"}
+    near = 0
+    for t, l, _, _ in samples:
+        ls = np.sort(l)[::-1]
+        near += int(ls[w.k - 1] - ls[w.k] < 1e-5)
+    out["near_ties"] = near
+    for name, flag in (("fxp", cm.COLIMOE_FWD_FXP), ("fp32", cm.COLIMOE_FWD_FP32)):
+        worst, differ, compared = 0.0, 0, 0
+        for t, l, oidx, oout in samples:
+            x = torch.from_numpy(X[t:t + 1]).to(dev)
+            res = x.clone()
+            cm.colimoe_route_forward(ctx.ctx, 0, x.data_ptr(), 1, idx.data_ptr(), wt.data_ptr(), None, res.data_ptr(),
+                                     flag)
+            ctx.sync()
+            if set(idx.cpu().numpy()[0].tolist()) != set(oidx.tolist()):
+                ls = np.sort(l)[::-1]
+                differ += int(not ls[w.k - 1] - ls[w.k] < 1e-5)
+                continue
+            g = res.cpu().numpy()[0].astype(np.float64)
+            worst = max(worst, float(np.max(np.abs(g - oout) / (1e-3 * (1.0 + np.abs(oout))))))
+            compared += 1
+        out[name] = {"worst_ratio_to_bound": round(worst, 4), "tokens_compared": compared,
+                     "routing_mismatches": differ}
+    ctx.close()
+    del ctx
+    torch.cuda.empty_cache()
+    return out
 
 
 if __name__ == "__main__":
