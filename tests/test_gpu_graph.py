@@ -41,9 +41,39 @@ def _step(c, x0, r, xn, idx, wts, U, flags, T):
                                          wts[l].data_ptr(), U[l].abi(), flags)
 
 
-@pytest.mark.parametrize("flags,T", [(FXP, 1), (FP32, 1), (FXP, 3)], ids=["fxp-T1", "fp32-T1", "fxp-T3"])
-def test_graph_replays_match_eager(ctx, flags, T):
+@pytest.mark.parametrize("flags,T,top_p", [(FXP, 1, 1.0), (FP32, 1, 1.0), (FXP, 3, 1.0), (FXP, 1, 0.7)],
+                         ids=["fxp-T1", "fp32-T1", "fxp-T3", "fxp-T1-top-p-0.7"])
+def test_graph_replays_match_eager(ctx, flags, T, top_p):
     c, cap = ctx
+    c.set_expert_top_p(top_p)
+    try:
+        _replays_match_eager(c, cap, W, flags, T)
+    finally:
+        c.set_expert_top_p(1.0)
+
+
+# int8 experts: the one-token int8 kernels (combine in the down kernel)
+W8 = synth.Workload(name="graph8", d=1024, f=512, E=32, k=4, T=1, n_shared=1, zipf=1.1, bits=8,
+                    seed=synth.BASE_SEED + 502)
+
+
+def test_graph_replays_match_eager_int8():
+    import int4_routed_expert_fp32_amd as cm
+    from int4_routed_expert_fp32_amd.runtime import MoeContext
+    print("graph int8: %d layers d=%d f=%d E=%d" % (LAYERS, W8.d, W8.f, W8.E), flush=True)
+    cap = torch.cuda.Stream()
+    c = MoeContext(W8.d, W8.f, W8.E, W8.k, n_layers=LAYERS, n_shared=1, max_tokens=1, stream=cap,
+                   cfg_flags=cm.COLIMOE_CFG_INT8)
+    try:
+        for l in range(LAYERS):
+            c.load_layer(l, synth.router(W8, l), synth.bias(W8, l), synth.expert_blobs(W8, l, 0, W8.E),
+                         synth.shared_blob(W8, l))
+        _replays_match_eager(c, cap, W8, 0, 1)
+    finally:
+        c.close()
+
+
+def _replays_match_eager(c, cap, W, flags, T):
     X = torch.from_numpy(synth.activations(W.with_(T=T), stream=7 + T)).cuda()
     r = X.clone()
     xn = torch.empty_like(X)
@@ -82,4 +112,4 @@ def test_graph_replays_match_eager(ctx, flags, T):
             _step(c, X, tmp, torch.empty_like(X), torch.empty_like(idx), torch.empty_like(wts),
                   [c.new_union(T) for _ in range(LAYERS)], flags, T)
         c.sync()
-    print("graph %s T=%d: 4 replays bit-identical" % ("fxp" if flags == FXP else "fp32", T))
+    print("graph %s T=%d: 4 replays bit-identical" % (W.name, T))
