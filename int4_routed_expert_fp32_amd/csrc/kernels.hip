@@ -2694,9 +2694,10 @@ hipError_t launch_gateup_tok(const LayerDev &L, const Dims &D, const UnionDev &U
   if (D.T <= 0) return hipSuccess;
   const int NS = (D.d / kChunk + 63) / 64, wpt = NS < 4 ? NS : 4;
   const int slots = (D.T * D.k < D.E ? D.T * D.k : D.E) + D.n_shared;
-  const int grid = slots * (D.f / 16);
+  int grid = slots * (D.f / 16);
   const size_t lds = tok_lds(D.d);
   if (D.T == 1) {
+    if (skip_shared && NS <= 4) grid -= D.n_shared * (D.f / 16);  // the shared expert's blocks would only exit
     if (NS <= 4) {
       switch (NS) {
         case 1: k_gateup_one<1><<<grid, 256, 0, s>>>(L, D, U, w, xq, xs, hq, hs, wslot, skip_shared ? 1 : 0); break;
