@@ -944,14 +944,19 @@ __device__ __forceinline__ void load_digits(const uint32_t *__restrict__ q, cons
   xs[1] = sv.y;
 }
 
+__device__ __forceinline__ void fxp_apply(const uint4 (&W)[kTileRows], const uint4 &S, const uint32_t (&dg)[kDigitWords],
+                                          const float (&xs)[2], float (&acc)[kTileRows]) {
+#pragma unroll
+  for (int r = 0; r < kTileRows; ++r) acc[r] = fxp_chunk(W[r], dg, xs, tile_scale(S, r), acc[r]);
+}
+
 __device__ __forceinline__ void fxp_step(const uint4 (&W)[kTileRows], const uint4 &S, const uint32_t *__restrict__ q,
                                          const float *__restrict__ qs, int row, int K, int c,
                                          float (&acc)[kTileRows]) {
   uint32_t dg[kDigitWords];
   float xs[2];
   load_digits(q, qs, row, K, c, dg, xs);
-#pragma unroll
-  for (int r = 0; r < kTileRows; ++r) acc[r] = fxp_chunk(W[r], dg, xs, tile_scale(S, r), acc[r]);
+  fxp_apply(W, S, dg, xs, acc);
 }
 
 // Encodes T rows of x (K columns each) for the gate/up kernel; one lane per
@@ -1179,7 +1184,15 @@ __device__ __forceinline__ void gateup_one_quad(const LayerDev &L, const Dims &D
   if (c < C) {
     uint4 W[kTileRows], S;
     load_step(base + EL.gu_nib, base + EL.gu_sc, ti, D.d, c, W, S);
-    fxp_step(W, S, xq, xs, 0, D.d, c, acc);
+    uint32_t dg[kDigitWords];
+    float dsc[2];
+    load_digits(xq, xs, 0, D.d, c, dg, dsc);
+    // loads issued: from here the wave outranks waves of newer blocks still
+    // issuing theirs, so blocks whose data has arrived finish and retire
+    // sooner (measured: gate/up 0.2-0.4 us faster; the same in the down
+    // kernel was slower)
+    __builtin_amdgcn_s_setprio(2);
+    fxp_apply(W, S, dg, dsc, acc);
   }
   const float v = reduce8_rows(acc);
   if ((lane & 7) == 7) red[tt][st][lane >> 3] = v;
