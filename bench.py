@@ -643,7 +643,7 @@ def bench_prefill(args, torch, np, synth, cm, MoeContext, dev, stream):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (requested --gpus %d)" % args.gpus,
+        print("bench.py measures one GPU: the library has no multi-GPU path (requested --gpus %d)" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
 
@@ -695,7 +695,7 @@ def main():
     if not args.no_cpu_baseline:
         samples = []
         cpu = cpu_baseline(w, args.cpu_seconds, keep=samples)
-        parity = parity_verdict(torch, np, synth, cm, MoeContext, dev, w, samples)
+        parity = parity_check(torch, np, synth, cm, MoeContext, dev, w, samples)
 
     out = {
         "metric": "MoE-layer decode us/token + int4 expert-weight GB/s vs HBM peak",
@@ -789,7 +789,7 @@ def cpu_baseline(w, budget_s, keep=None):
     """The oracle (route + forward, fp64) on a bounded sample of decode tokens,
     on the process's cores; then on one core, for the decode and the tiny
     layer.  `keep` receives the sample's oracle results (for the parity
-    verdict)."""
+    check)."""
     import oracle
     import synth
     oracle.build(force=False)
@@ -814,7 +814,7 @@ def cpu_baseline(w, budget_s, keep=None):
             "cpu_model": model, "affinity_cores": cores, "omp_threads": threads, "one_core": one}
 
 
-def parity_verdict(torch, np, synth, cm, MoeContext, dev, w, samples):
+def parity_check(torch, np, synth, cm, MoeContext, dev, w, samples):
     """The library on the oracle sample's tokens (layer instance 0, residual =
     x, one call each, both fp32-class paths) against the oracle's outputs:
     worst |gpu - oracle| / (1e-3 (1 + |oracle|)) per path, tokens whose k-th
