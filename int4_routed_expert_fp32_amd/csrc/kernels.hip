@@ -1915,9 +1915,9 @@ __global__ __launch_bounds__(256) void k_down_i8_one(LayerDev L, Dims D, const f
 // end loads the row's last chunk and adds nothing).  Down: a block per
 // kI8Rows output rows (8: every block reads all slots' h rows, so taller
 // tiles read h fewer times), a wave per slot issuing its NI chunks of every
-// row at once; wave 0 then folds the slot outputs into the residual in the order of
-// k_combine (routed experts in pair order, each times its gate weight, then
-// the shared expert).
+// row at once; wave 0 then folds the slot outputs into the residual in the
+// order of k_combine (routed experts in pair order, each times its gate
+// weight, then the shared expert).
 constexpr int kI8Rows = 8;
 template <int NI>
 __global__ __launch_bounds__(256) void k_gateup_i8_dec(LayerDev L, Dims D, const float *__restrict__ x, UnionDev U,
