@@ -23,6 +23,10 @@ RAGGED = synth.Workload(name="ragged", d=320, f=192, E=37, k=3, T=5, n_shared=1,
                         seed=synth.BASE_SEED + 101)
 # d/32 = 66: two chunk steps per row, the second one partial
 RAGGED2 = synth.Workload(name="ragged2", d=2112, f=128, E=20, k=4, T=3, n_shared=0, seed=synth.BASE_SEED + 102)
+# narrow rows of 33-63 chunks (d/32 = 46, f/32 = 34: 64 lanes per row in the
+# narrow kernels), more experts than the one-launch small path takes
+RAGGED4 = synth.Workload(name="ragged4", d=1472, f=1088, E=80, k=4, T=4, n_shared=1, zipf=1.1,
+                         seed=synth.BASE_SEED + 104)
 # wide in both d and f (fixed-point path) with partial steps in both GEMVs
 RAGGED3 = synth.Workload(name="ragged3", d=2112, f=2112, E=24, k=3, T=4, n_shared=1, zipf=1.1, rho=0.5,
                          seed=synth.BASE_SEED + 103)
@@ -132,7 +136,7 @@ def test_invalid_routing_is_reported():
             assert np.array_equal(g[key], o[key]), key
 
 
-@pytest.mark.parametrize("w", [TINY, RAGGED, RAGGED2, RAGGED3], ids=lambda w: w.name)
+@pytest.mark.parametrize("w", [TINY, RAGGED, RAGGED2, RAGGED3, RAGGED4], ids=lambda w: w.name)
 def test_layer_parity_small(w):
     ctx = _ctx(w)
     P.load_layer(ctx, w, 0)
@@ -144,6 +148,10 @@ def test_layer_parity_small(w):
         r3 = P.layer_parity(ctx, w, 0, X, ora, one_call=True)
         assert np.array_equal(r3["out"].view(np.uint32), r["out"].view(np.uint32))
         print("ragged3 fp32 path worst ratio", r2["ratio"])
+    if w is RAGGED4:  # every token alone (one call) gives its row of the batch
+        for t in range(w.T):
+            a = P.layer_parity(ctx, w, 0, X[t:t + 1], ora, one_call=True)
+            assert np.array_equal(a["out"][0].view(np.uint32), r["out"][t].view(np.uint32)), t
     print(w.name, "worst ratio", r["ratio"], "near-tie tokens", r["differ"])
     # union lists from route equal the oracle's union of the GPU routing
     o = oracle.union(r["idx"], w.E)
