@@ -673,13 +673,6 @@ int colimoe_route_forward(colimoe_ctx *ctx, int32_t layer, const float *x, int32
   const colimoe_union *uu = u ? u : &uw;
   const bool encode = path == PATH_FXP;
   const Dims D = dims_of(ctx, T);
-  if (path == PATH_FP32 && !ctx->host_store[layer] && layer_small_supported(D)) {  // the whole layer in one launch
-    KTimer kt(ctx, K_GATEUP);
-    if (launch_layer_small(layer_of(ctx, layer), D, x, idx, w, to_dev(uu), ctx->top_p, (float *)(ctx->ws + ctx->wl.h),
-                           (float *)(ctx->ws + ctx->wl.y), residual, ctx->stream) != hipSuccess)
-      return COLIMOE_E_HIP;
-    return COLIMOE_OK;
-  }
   // one token on an HBM-resident layer: the shared expert's gate/up rides in
   // the top-k launch
   const bool early = encode && !ctx->host_store[layer] && shared_early_supported(D);

@@ -172,14 +172,6 @@ hipError_t launch_gateup_f32_dec(const LayerDev &L, const Dims &D, const float *
                                  float *hsum, hipStream_t s);
 hipError_t launch_down_f32_dec(const LayerDev &L, const Dims &D, const float *h, const float *hsum, const UnionDev &U,
                                const float *w, float *residual, hipStream_t s);
-// One token, small shapes (E <= 64, d and f < 2048, k + shared <= 16), fp32
-// path: router, top-k (idx, w), union lists into U, gate/up, down and combine
-// into residual in one launch (h, y: workspace rows); results equal to
-// launch_router_split + launch_topk_union1 + launch_gateup + launch_down +
-// launch_combine.
-bool layer_small_supported(const Dims &D);
-hipError_t launch_layer_small(const LayerDev &L, const Dims &D, const float *x, int32_t *idx, float *w,
-                              const UnionDev &U, float top_p, float *h, float *y, float *residual, hipStream_t s);
 // Router for many tokens on the matrix cores (fp32), with S = router_splits(d)
 // K-slices whose partials (part: [S][T][E]) are summed in slice order.
 int router_splits(int d);

@@ -2125,8 +2125,8 @@ __global__ __launch_bounds__(256) void k_down_i8(LayerDev L, Dims D, const float
 // ------------------------------------------------- narrow shapes (K < 2048)
 // Rows shorter than 64 chunks: LPR lanes per row (a power of two >= K/32,
 // one chunk per lane), 64/LPR rows side by side in a wave, one wave per
-// (slot, 8-row tile).  Same
-// arithmetic per chunk; reductions by a fixed butterfly within LPR lanes.
+// (slot, 8-row tile).  Same arithmetic per chunk; reductions by a fixed
+// butterfly within LPR lanes.
 
 template <int LPR>
 struct NarrowShape {
@@ -2186,19 +2186,18 @@ __device__ __forceinline__ void narrow_reduce(const float *acc, float *rows) {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// The narrow gate/up items (slot, 4 h rows) first, first + stride, ..., one
-// wave each; rows: the wave's 8 floats of LDS.
 template <int LPR, int MT>
-__device__ __forceinline__ void gateup_narrow_items(const LayerDev &L, const Dims &D, const float *__restrict__ x,
-                                                    const UnionDev &U, float *__restrict__ h, float *__restrict__ gdbg,
-                                                    float *__restrict__ udbg, int first, int stride, float *rows) {
+__global__ __launch_bounds__(256) void k_gateup_narrow(LayerDev L, Dims D, const float *__restrict__ x, UnionDev U,
+                                                       float *__restrict__ h, float *__restrict__ gdbg,
+                                                       float *__restrict__ udbg) {
   using NS = NarrowShape<LPR>;
-  const int lane = threadIdx.x & 63;
+  __shared__ float rows_lds[4][kTileRows];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int tiles = D.f / 4;
   const int nu = clamp_nu(U.n_unique, D);
   const int active = (nu + D.n_shared) * tiles;
   const ExpertLayout EL = expert_layout(D.d, D.f);
-  for (int item = first; item < active; item += stride) {
+  for (int item = blockIdx.x * 4 + wave; item < active; item += gridDim.x * 4) {
     const int s = item / tiles, ti = item - s * tiles;
     int e, p0, p1;
     if (!resolve_slot(D, U, nu, s, e, p0, p1)) continue;
@@ -2218,9 +2217,9 @@ __device__ __forceinline__ void gateup_narrow_items(const LayerDev &L, const Dim
 #pragma unroll
       for (int m = 0; m < MT; ++m)
         if (m < mcount) {
-          narrow_reduce<LPR>(acc[m], rows);
+          narrow_reduce<LPR>(acc[m], rows_lds[wave]);
           if (lane < 4 && orows[m] >= 0) {
-            const float g = rows[lane], u = rows[lane + 4];
+            const float g = rows_lds[wave][lane], u = rows_lds[wave][lane + 4];
             const size_t o = (size_t)orows[m] * D.f + (size_t)ti * 4 + lane;
             h[o] = silu_f(g) * u;
             if (gdbg) {
@@ -2234,26 +2233,16 @@ __device__ __forceinline__ void gateup_narrow_items(const LayerDev &L, const Dim
 }
 
 template <int LPR, int MT>
-__global__ __launch_bounds__(256) void k_gateup_narrow(LayerDev L, Dims D, const float *__restrict__ x, UnionDev U,
-                                                       float *__restrict__ h, float *__restrict__ gdbg,
-                                                       float *__restrict__ udbg) {
-  __shared__ float rows_lds[4][kTileRows];
-  const int wave = threadIdx.x >> 6;
-  gateup_narrow_items<LPR, MT>(L, D, x, U, h, gdbg, udbg, blockIdx.x * 4 + wave, gridDim.x * 4, rows_lds[wave]);
-}
-
-// The narrow down items (slot, 8 output rows) first, first + stride, ...
-template <int LPR, int MT>
-__device__ __forceinline__ void down_narrow_items(const LayerDev &L, const Dims &D, const float *__restrict__ h,
-                                                  const UnionDev &U, float *__restrict__ y, int first, int stride,
-                                                  float *rows) {
+__global__ __launch_bounds__(256) void k_down_narrow(LayerDev L, Dims D, const float *__restrict__ h, UnionDev U,
+                                                     float *__restrict__ y) {
   using NS = NarrowShape<LPR>;
-  const int lane = threadIdx.x & 63;
+  __shared__ float rows_lds[4][kTileRows];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int tiles = D.d / kTileRows;
   const int nu = clamp_nu(U.n_unique, D);
   const int active = (nu + D.n_shared) * tiles;
   const ExpertLayout EL = expert_layout(D.d, D.f);
-  for (int item = first; item < active; item += stride) {
+  for (int item = blockIdx.x * 4 + wave; item < active; item += gridDim.x * 4) {
     const int s = item / tiles, ti = item - s * tiles;
     int e, p0, p1;
     if (!resolve_slot(D, U, nu, s, e, p0, p1)) continue;
@@ -2268,19 +2257,11 @@ __device__ __forceinline__ void down_narrow_items(const LayerDev &L, const Dims 
 #pragma unroll
       for (int m = 0; m < MT; ++m)
         if (m < mcount) {
-          narrow_reduce<LPR>(acc[m], rows);
-          if (lane < kTileRows) y[(size_t)orows[m] * D.d + (size_t)ti * kTileRows + lane] = rows[lane];
+          narrow_reduce<LPR>(acc[m], rows_lds[wave]);
+          if (lane < kTileRows) y[(size_t)orows[m] * D.d + (size_t)ti * kTileRows + lane] = rows_lds[wave][lane];
         }
     }
   }
-}
-
-template <int LPR, int MT>
-__global__ __launch_bounds__(256) void k_down_narrow(LayerDev L, Dims D, const float *__restrict__ h, UnionDev U,
-                                                     float *__restrict__ y) {
-  __shared__ float rows_lds[4][kTileRows];
-  const int wave = threadIdx.x >> 6;
-  down_narrow_items<LPR, MT>(L, D, h, U, y, blockIdx.x * 4 + wave, gridDim.x * 4, rows_lds[wave]);
 }
 
 // ------------------------------------------------------------------ combine
@@ -2288,37 +2269,42 @@ __global__ __launch_bounds__(256) void k_down_narrow(LayerDev L, Dims D, const f
 // shared expert's y (weight 1).  Fixed order, no atomics: a token's result
 // is the same whether it runs alone or batched, fused or not.
 
-// The order of token t's routed outputs (pair positions ascending, i.e.
-// experts ascending) with their gate weights, and their count; run by the 64
-// threads of one wave.
-__device__ __forceinline__ void combine_order(const Dims &D, const float *__restrict__ w, const UnionDev &U, int t,
-                                              int *order, float *wt, int *nsel) {
+__global__ __launch_bounds__(256) void k_combine(Dims D, const float *__restrict__ w, UnionDev U,
+                                                 const float *__restrict__ y, float *__restrict__ residual) {
+  // Block (column slice, token): 256 threads x 4 columns.  A token's pairs sit
+  // in ascending expert order in the union lists, so visiting its slots by
+  // increasing pair index visits experts ascending; the order is ranked into
+  // LDS by every block of the token.
+  __shared__ int order[16];
+  __shared__ float wt[16];
+  __shared__ int nsel;
+  const int t = blockIdx.y;
+  if (t >= D.T) return;
   const int nu = clamp_nu(U.n_unique, D);
   const int tk = D.T * D.k;
-  const int j = threadIdx.x & 63;
-  int p = 0x7FFFFFFF;
-  if (nu > 0 && j < D.k) {
-    p = U.pair_of[(size_t)t * D.k + j];
-    if (p < 0 || p >= tk) p = 0x7FFFFFFF;
+  if (threadIdx.x < 64) {
+    const int j = threadIdx.x;
+    int p = 0x7FFFFFFF;
+    if (nu > 0 && j < D.k) {
+      p = U.pair_of[(size_t)t * D.k + j];
+      if (p < 0 || p >= tk) p = 0x7FFFFFFF;
+    }
+    int rank = 0, valid = 0;
+    for (int i = 0; i < D.k; ++i) {
+      const int q = __shfl(p, i, 64);
+      rank += (q < p) || (q == p && i < j);
+      valid += q < tk;
+    }
+    if (j < D.k && p < tk) {
+      order[rank] = p;
+      wt[rank] = w[(size_t)t * D.k + j];
+    }
+    if (j == 0) nsel = valid;
   }
-  int rank = 0, valid = 0;
-  for (int i = 0; i < D.k; ++i) {
-    const int q = __shfl(p, i, 64);
-    rank += (q < p) || (q == p && i < j);
-    valid += q < tk;
-  }
-  if (j < D.k && p < tk) {
-    order[rank] = p;
-    wt[rank] = w[(size_t)t * D.k + j];
-  }
-  if (j == 0) *nsel = valid;
-}
-
-// Columns 4 c4 .. 4 c4 + 3 of token t's residual: the n routed outputs in
-// `order`, each times its weight, then the shared expert's output.
-__device__ __forceinline__ void combine_col(const Dims &D, const float *__restrict__ y, float *__restrict__ residual,
-                                            int t, int c4, const int *order, const float *wt, int n) {
-  const int d4 = D.d / 4, tk = D.T * D.k;
+  __syncthreads();
+  const int n = nsel;
+  const int d4 = D.d / 4, c4 = blockIdx.x * 256 + threadIdx.x;
+  if (c4 >= d4) return;
   float4 *rp = (float4 *)residual + (size_t)t * d4 + c4;
   const float4 *y4 = (const float4 *)y;
   float4 acc = *rp;
@@ -2347,82 +2333,6 @@ __device__ __forceinline__ void combine_col(const Dims &D, const float *__restri
     acc.w = acc.w + sh.w;
   }
   *rp = acc;
-}
-
-__global__ __launch_bounds__(256) void k_combine(Dims D, const float *__restrict__ w, UnionDev U,
-                                                 const float *__restrict__ y, float *__restrict__ residual) {
-  // Block (column slice, token): 256 threads x 4 columns.  A token's pairs sit
-  // in ascending expert order in the union lists, so visiting its slots by
-  // increasing pair index visits experts ascending; the order is ranked into
-  // LDS by every block of the token.
-  __shared__ int order[16];
-  __shared__ float wt[16];
-  __shared__ int nsel;
-  const int t = blockIdx.y;
-  if (t >= D.T) return;
-  if (threadIdx.x < 64) combine_order(D, w, U, t, order, wt, &nsel);
-  __syncthreads();
-  const int c4 = blockIdx.x * 256 + threadIdx.x;
-  if (c4 < D.d / 4) combine_col(D, y, residual, t, c4, order, wt, nsel);
-}
-
-// A whole one-token layer of small shapes in one block of 4 waves: the
-// router (each expert row's columns over the 4 waves, as k_router_split), the
-// top-k and the union lists (as k_topk_union1, from the logits in LDS), the
-// narrow gate/up and down items (one wave per item, as k_gateup_narrow and
-// k_down_narrow) and the combine (as k_combine), the phases separated by the
-// block barrier.  Per value the operations are those of the separate kernels,
-// so the bits are theirs; the call is one launch instead of five, for layers
-// whose whole work is a few microseconds of one CU.
-constexpr int kSmallMaxE = 64;
-template <int LPRG, int LPRD>
-__global__ __launch_bounds__(256) void k_layer_small(LayerDev L, Dims D, const float *__restrict__ x,
-                                                     int32_t *__restrict__ idx, float *__restrict__ w, UnionDev U,
-                                                     float top_p, float *__restrict__ h, float *__restrict__ y,
-                                                     float *__restrict__ residual) {
-  __shared__ float part[kSmallMaxE][4];
-  __shared__ float lg[kSmallMaxE];
-  __shared__ int32_t ids[16];
-  __shared__ float rows_lds[4][kTileRows];
-  __shared__ int order[16];
-  __shared__ float wt[16];
-  __shared__ int nsel;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  // A1
-  const int q4 = D.d / 4;
-  for (int e = 0; e < D.E; ++e) {
-    const float *row = L.router + (size_t)e * D.d + (size_t)wave * q4;
-    float4 r[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int c = 4 * lane + 256 * i;
-      r[i] = c < q4 ? *(const float4 *)(row + c) : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-    router_tokens<1>(r, x, D, wave, lane, q4, &part[e]);
-  }
-  __syncthreads();
-  if ((int)threadIdx.x < D.E) {
-    const int e = threadIdx.x;
-    lg[e] = ((part[e][0] + part[e][1]) + part[e][2]) + part[e][3] + L.bias[e];
-  }
-  __syncthreads();
-  // A2, A3
-  if (wave == 0) {
-    topk_token<1>(lg, D, 0, idx, w, ids, top_p);
-    wave_lds_sync();
-    union_one_token(ids, D, U);
-  }
-  __syncthreads();
-  // A4, A6 (the shared expert is the last slot)
-  gateup_narrow_items<LPRG, 1>(L, D, x, U, h, nullptr, nullptr, wave, 4, rows_lds[wave]);
-  __syncthreads();
-  // A5
-  down_narrow_items<LPRD, 1>(L, D, h, U, y, wave, 4, rows_lds[wave]);
-  __syncthreads();
-  // A7
-  if (wave == 0) combine_order(D, w, U, 0, order, wt, &nsel);
-  __syncthreads();
-  for (int c4 = threadIdx.x; c4 < D.d / 4; c4 += 256) combine_col(D, y, residual, 0, c4, order, wt, nsel);
 }
 
 // ------------------------------------------------------------------ rmsnorm
@@ -2660,38 +2570,6 @@ static bool wide(int K) { return K / kChunk >= 64; }
 static int narrow_lpr(int K) {
   const int C = K / kChunk;
   return C > 32 ? 64 : C > 16 ? 32 : C > 8 ? 16 : C > 4 ? 8 : C > 2 ? 4 : 2;
-}
-
-bool layer_small_supported(const Dims &D) {
-  return D.T == 1 && D.E <= kSmallMaxE && !wide(D.d) && !wide(D.f) && D.k + D.n_shared <= 16;
-}
-
-template <int LPRG>
-static void layer_small_launch(int lprd, hipStream_t s, const LayerDev &L, const Dims &D, const float *x, int32_t *idx,
-                               float *w, const UnionDev &U, float top_p, float *h, float *y, float *residual) {
-  switch (lprd) {
-    case 2: k_layer_small<LPRG, 2><<<1, 256, 0, s>>>(L, D, x, idx, w, U, top_p, h, y, residual); break;
-    case 4: k_layer_small<LPRG, 4><<<1, 256, 0, s>>>(L, D, x, idx, w, U, top_p, h, y, residual); break;
-    case 8: k_layer_small<LPRG, 8><<<1, 256, 0, s>>>(L, D, x, idx, w, U, top_p, h, y, residual); break;
-    case 16: k_layer_small<LPRG, 16><<<1, 256, 0, s>>>(L, D, x, idx, w, U, top_p, h, y, residual); break;
-    case 32: k_layer_small<LPRG, 32><<<1, 256, 0, s>>>(L, D, x, idx, w, U, top_p, h, y, residual); break;
-    default: k_layer_small<LPRG, 64><<<1, 256, 0, s>>>(L, D, x, idx, w, U, top_p, h, y, residual); break;
-  }
-}
-
-hipError_t launch_layer_small(const LayerDev &L, const Dims &D, const float *x, int32_t *idx, float *w,
-                              const UnionDev &U, float top_p, float *h, float *y, float *residual, hipStream_t s) {
-  if (!layer_small_supported(D)) return hipErrorInvalidValue;
-  const int lprd = narrow_lpr(D.f);
-  switch (narrow_lpr(D.d)) {
-    case 2: layer_small_launch<2>(lprd, s, L, D, x, idx, w, U, top_p, h, y, residual); break;
-    case 4: layer_small_launch<4>(lprd, s, L, D, x, idx, w, U, top_p, h, y, residual); break;
-    case 8: layer_small_launch<8>(lprd, s, L, D, x, idx, w, U, top_p, h, y, residual); break;
-    case 16: layer_small_launch<16>(lprd, s, L, D, x, idx, w, U, top_p, h, y, residual); break;
-    case 32: layer_small_launch<32>(lprd, s, L, D, x, idx, w, U, top_p, h, y, residual); break;
-    default: layer_small_launch<64>(lprd, s, L, D, x, idx, w, U, top_p, h, y, residual); break;
-  }
-  return hipGetLastError();
 }
 
 static int grid_cap(long long blocks, int cap) { return (int)(blocks < 1 ? 1 : blocks > cap ? cap : blocks); }

@@ -1,9 +1,10 @@
-"""Small layers in one launch: a one-token call whose layer is small (at most
-64 experts, d and f below 2048, k + shared <= 16) runs router, top-k, union
-lists, gate/up, down and combine in one block (k_layer_small).  Its results
-must be the bits of the separate kernels: route + forward of the same token,
-and the token's row of a batched call; and within the fp32 bound of the
-oracle ([A] §1-§2: 8-of-256 routing and the expert FFN, here at small sizes).
+"""Small layers (d and f below 2048: the narrow kernels, LPR lanes per row)
+through the one-call entry point (route_forward) of a one-token call: its
+results must be the bits of route + forward of the same token and of the
+token's row in a batched call, and within the fp32 bound of the oracle ([A]
+§1-§2: 8-of-256 routing and the expert FFN, here at small sizes), at top-k
+and top-p.  Rows of 33 to 63 chunks (1024 < K < 2048) take 64 lanes per row:
+with 32 lanes the chunks from 32 on were dropped.
 """
 import numpy as np
 import pytest
@@ -18,9 +19,9 @@ pytestmark = pytest.mark.gpu
 TINY = synth.WORKLOADS["tiny"].with_(T=6)
 RAGGED = synth.Workload(name="small_ragged", d=320, f=192, E=37, k=3, T=5, n_shared=1, zipf=1.1, rho=0.3,
                         seed=synth.BASE_SEED + 701)
-# the largest shape the one-launch path takes: 64 experts, d and f one chunk
-# group below the wide kernels, 15 routed + shared slots
-EDGE = synth.Workload(name="small_edge", d=1984, f=1984, E=64, k=15, T=3, n_shared=1, zipf=1.1,
+# 64 experts, 15 routed + shared slots, d one chunk below the wide kernels
+# and f = 38 chunks: both projections at 64 lanes per row
+EDGE = synth.Workload(name="small_edge", d=1984, f=1216, E=64, k=15, T=3, n_shared=1, zipf=1.1,
                       seed=synth.BASE_SEED + 702)
 
 
@@ -44,7 +45,7 @@ def _bits(a):
 
 @pytest.mark.parametrize("w", [TINY, RAGGED, EDGE], ids=lambda w: w.name)
 @pytest.mark.parametrize("top_p", [1.0, 0.7], ids=["top-k", "top-p-0.7"])
-def test_one_launch_layer(w, top_p):
+def test_small_layer_one_call(w, top_p):
     ctx = _ctx(w)
     try:
         ctx.set_expert_top_p(top_p)
@@ -56,8 +57,8 @@ def test_one_launch_layer(w, top_p):
         for t in range(w.T):
             x1 = X[t:t + 1]
             if top_p == 1.0:
-                a = P.layer_parity(ctx, w, 0, x1, ora, one_call=True)  # the one-launch path
-                b = P.layer_parity(ctx, w, 0, x1, ora)  # route + forward: the separate kernels
+                a = P.layer_parity(ctx, w, 0, x1, ora, one_call=True)  # route_forward
+                b = P.layer_parity(ctx, w, 0, x1, ora)  # route, then forward
                 worst = max(worst, a["ratio"])
                 assert np.array_equal(a["idx"], batch["idx"][t:t + 1]), t
                 assert np.array_equal(_bits(a["out"][0]), _bits(batch["out"][t])), t
@@ -84,7 +85,7 @@ def test_one_launch_layer(w, top_p):
             assert np.array_equal(_bits(a["out"]), _bits(b["out"])), t
             for key in ("ids", "offsets", "pair_token", "pair_slot", "pair_of"):
                 assert np.array_equal(a["union"][key], b["union"][key]), (t, key)
-        print("%s top_p %.1f: %d tokens bit-identical to the separate kernels, worst ratio %.3g" % (
+        print("%s top_p %.1f: %d tokens bit-identical to route + forward, worst ratio %.3g" % (
             w.name, top_p, w.T, worst))
     finally:
         ctx.set_expert_top_p(1.0)
