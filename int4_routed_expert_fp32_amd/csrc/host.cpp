@@ -395,11 +395,16 @@ static int forward_kernels(colimoe_ctx *ctx, int32_t layer, const float *x, int3
     }
     {
       KTimer kt(ctx, K_GATEUP);
-      if (launch_gateup_tok(L, D, U, w, xq, xs, hq, hs, wslot, shared_done, s) != hipSuccess) return COLIMOE_E_HIP;
+      if (launch_gateup_tok(L, D, U, idx, w, xq, xs, hq, hs, wslot, shared_done, s) != hipSuccess) return COLIMOE_E_HIP;
     }
     if (down_dec_supported(D)) {
       KTimer kt(ctx, K_DOWN);
       if (launch_down_dec(L, D, hq, hs, U, wslot, residual, s) != hipSuccess) return COLIMOE_E_HIP;
+      return COLIMOE_OK;  // combine done in the kernel
+    }
+    if (down_dec_tok_supported(D)) {
+      KTimer kt(ctx, K_DOWN);
+      if (launch_down_dec_tok(L, D, hq, hs, U, idx, w, residual, s) != hipSuccess) return COLIMOE_E_HIP;
       return COLIMOE_OK;  // combine done in the kernel
     }
     {

@@ -152,14 +152,23 @@ hipError_t launch_xquant(const float *x, int T, int K, uint32_t *xq, float *xs, 
 // T == 1, each slot's gate weight (from w) to wslot[k + shared].
 // skip_shared (one token, shared_early_supported): the shared expert's h is
 // already there (launch_topk_shared1).
-hipError_t launch_gateup_tok(const LayerDev &L, const Dims &D, const UnionDev &U, const float *w, const uint32_t *xq,
-                             const float *xs, uint32_t *hq, float *hs, float *wslot, bool skip_shared, hipStream_t s);
+hipError_t launch_gateup_tok(const LayerDev &L, const Dims &D, const UnionDev &U, const int32_t *idx, const float *w,
+                             const uint32_t *xq, const float *xs, uint32_t *hq, float *hs, float *wslot,
+                             bool skip_shared, hipStream_t s);
 // Fixed-point down for any T: y [T*k + T*shared][d] fp32 (combine in k_combine).
 hipError_t launch_down_tok(const LayerDev &L, const Dims &D, const UnionDev &U, const uint32_t *hq, const float *hs,
                            float *y, hipStream_t s);
 // Down + combine for one token when a down row is one step (f <= 2048) and
 // k + shared <= 16 slots; slot gate weights from wslot.
 bool down_dec_supported(const Dims &D);
+// Down + combine for 2-4 tokens when a down row is one step (f <= 2048) and
+// k + shared <= 16: a block per (token, output tile); the token's expert ids
+// from idx, its gate weights from w; combine into the residual as
+// launch_combine does.
+bool down_dec_tok_supported(const Dims &D);
+hipError_t launch_down_dec_tok(const LayerDev &L, const Dims &D, const uint32_t *hq, const float *hs,
+                               const UnionDev &U, const int32_t *idx, const float *w, float *residual,
+                               hipStream_t s);
 hipError_t launch_down_dec(const LayerDev &L, const Dims &D, const uint32_t *hq, const float *hs, const UnionDev &U,
                            const float *wslot, float *residual, hipStream_t s);
 // The fp32 dequantisation path for one token (d <= 8192, f a multiple of 16,

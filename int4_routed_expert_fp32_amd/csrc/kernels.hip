@@ -1165,7 +1165,7 @@ __global__ __launch_bounds__(256 * WPT) void k_gateup_tok(LayerDev L, Dims D, Un
 // a lean form that keeps two blocks resident per CU.  One block: 16 h rows
 // (4 tiles, quad qd) of expert e into output row orow.
 template <int NS>
-__device__ __forceinline__ void gateup_one_quad(const LayerDev &L, const Dims &D, int e, int orow, int qd,
+__device__ __forceinline__ void gateup_one_quad(const LayerDev &L, const Dims &D, int e, int orow, int qd, int xrow,
                                                 const uint32_t *__restrict__ xq, const float *__restrict__ xs,
                                                 uint32_t *__restrict__ hq, float *__restrict__ hs) {
   __shared__ float red[4][NS][kTileRows];
@@ -1186,7 +1186,7 @@ __device__ __forceinline__ void gateup_one_quad(const LayerDev &L, const Dims &D
     load_step(base + EL.gu_nib, base + EL.gu_sc, ti, D.d, c, W, S);
     uint32_t dg[kDigitWords];
     float dsc[2];
-    load_digits(xq, xs, 0, D.d, c, dg, dsc);
+    load_digits(xq, xs, xrow, D.d, c, dg, dsc);
     // loads issued: from here the wave outranks waves of newer blocks still
     // issuing theirs, so blocks whose data has arrived finish and retire
     // sooner (measured: gate/up 0.2-0.4 us faster; the same in the down
@@ -1259,14 +1259,62 @@ __global__ __launch_bounds__(256 * NS) void k_gateup_one(LayerDev L, Dims D, Uni
   __syncthreads();
   const int e = slot_s[0], orow = slot_s[1];
   if (e < 0) return;  // block-uniform
-  gateup_one_quad<NS>(L, D, e, orow, qd, xq, xs, hq, hs);
+  gateup_one_quad<NS>(L, D, e, orow, qd, 0, xq, xs, hq, hs);
 }
 
 // k_gateup_one with the slot's tokens looped kFewT at a time: every wave loads
 // its (tile, step) weights once and applies them to each token in turn; per
 // token the operations are those of k_gateup_tok and k_gateup_one, so the
 // bits do not depend on the batch.
+// 2-16 tokens: a block per (pair, quad), the one-token block code on the
+// pair's token, so each token's h has the bits of the token alone.  Items are
+// (quad, pair) with the pair fastest; the block ids are remapped so that each
+// XCD takes one contiguous range of items, which puts the pairs of one expert
+// (consecutive in the union lists) and quad on one L2 at about the same time:
+// the weights come from HBM once and the other pairs' reads hit that L2.  A
+// routed pair's expert is idx[token][top-k position]; pairs past the list's
+// count (dropped by expert top-p) and the shared expert's rows past T exit.
+template <int NS>
+__global__ __launch_bounds__(256 * NS) void k_gateup_pairs(LayerDev L, Dims D, UnionDev U,
+                                                           const int32_t *__restrict__ idx,
+                                                           const uint32_t *__restrict__ xq,
+                                                           const float *__restrict__ xs, uint32_t *__restrict__ hq,
+                                                           float *__restrict__ hs, int n_items) {
+  __shared__ int pr_s[3];  // expert, token, output row
+  const int per = (int)gridDim.x / 8;
+  const int item = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+  if (item >= n_items) return;  // block-uniform
+  const int tk = D.T * D.k, P = tk + D.T * D.n_shared;
+  const int qd = item / P, p = item - qd * P;
+  if (threadIdx.x == 0) {
+    int e = -1, t = 0;
+    if (p < tk) {
+      const int nu = clamp_nu(U.n_unique, D);
+      int np = U.offsets[nu];
+      np = np < 0 ? 0 : (np > tk ? tk : np);
+      t = U.pair_token[p];
+      const int j = U.pair_slot[p];
+      if (p < np && t >= 0 && t < D.T && j >= 0 && j < D.k) {
+        e = idx[(size_t)t * D.k + j];
+        if (e < 0 || e >= D.E) e = -1;
+      }
+    } else {
+      t = p - tk;
+      e = D.E;
+    }
+    pr_s[0] = e;
+    pr_s[1] = t;
+    pr_s[2] = p;
+  }
+  __syncthreads();
+  const int e = pr_s[0];
+  if (e < 0) return;  // block-uniform
+  gateup_one_quad<NS>(L, D, e, pr_s[2], qd, pr_s[1], xq, xs, hq, hs);
+}
+
 constexpr int kFewT = 4;
+constexpr int kPairsMaxT = 16;   // tokens up to which gate/up runs per pair
+constexpr int kDownTokMaxT = 4;  // tokens up to which down runs per token (with the combine)
 
 template <int NS>
 __global__ __launch_bounds__(256 * NS) __attribute__((amdgpu_waves_per_eu(6))) void k_gateup_few(LayerDev L, Dims D, UnionDev U,
@@ -1616,7 +1664,7 @@ __global__ __launch_bounds__(256 * NS) void k_topk_shared1(const float *__restri
     }
     return;
   }
-  gateup_one_quad<NS>(L, D, D.E, D.T * D.k, (int)blockIdx.x - 1, xq, xs, hq, hs);
+  gateup_one_quad<NS>(L, D, D.E, D.T * D.k, (int)blockIdx.x - 1, 0, xq, xs, hq, hs);
 }
 
 // Down + combine for one token when a down row is one step (f <= 2048): a
@@ -1632,6 +1680,39 @@ __global__ __launch_bounds__(256 * NS) void k_topk_shared1(const float *__restri
 // is replaced by 0), so no load sits behind a branch.
 constexpr int kDecMaxSlots = 16;  // slots of the one-token down kernel (one wave each)
 
+// One wave of the one-step down kernels: the 8 rows of output tile ti of
+// expert e (when ok) against h row hrow, reduced by the fixed tree into
+// out[0..8).  Every lane computes (a lane past the row end reads a valid
+// chunk and its result is replaced by 0), so no load sits behind a branch.
+__device__ __forceinline__ void dec_down_wave(const LayerDev &L, const Dims &D, bool ok, int e, int ti, int hrow,
+                                              const uint32_t *__restrict__ hq, const float *__restrict__ hs,
+                                              float *out) {
+  const int lane = threadIdx.x & 63, C = D.f / kChunk;
+  const ExpertLayout EL = expert_layout(D.d, D.f);
+  const uint8_t *base = expert_base(L, ok ? e : 0);
+  const __amdgpu_buffer_rsrc_t rn = wave_rsrc(base + EL.dn_nib, (uint32_t)(EL.dn_sc - EL.dn_nib));
+  const __amdgpu_buffer_rsrc_t rs = wave_rsrc(base + EL.dn_sc, (uint32_t)(EL.bytes - EL.dn_sc));
+  const int cl = lane < C ? lane : C - 1;
+  // chunk_offset with one step per row: tile, then row r at r * C * 16 bytes
+  const int tb = ti * kTileRows * (D.f / 2);
+  u32x4 W[kTileRows];
+#pragma unroll
+  for (int r = 0; r < kTileRows; ++r) W[r] = __builtin_amdgcn_raw_buffer_load_b128(rn, cl * 16, tb + r * C * 16, 0);
+  const u32x4 Sv = __builtin_amdgcn_raw_buffer_load_b128(rs, (cl >> 1) * 16, ti * (D.f / kGroup) * 16, 0);
+  uint32_t dg[kDigitWords];
+  float dsc[2];
+  load_digits(hq, hs, hrow, D.f, cl, dg, dsc);
+  const uint4 S = make_uint4(Sv.x, Sv.y, Sv.z, Sv.w);
+  float acc[kTileRows];
+#pragma unroll
+  for (int rr = 0; rr < kTileRows; ++rr) {
+    const float a = fxp_chunk(make_uint4(W[rr].x, W[rr].y, W[rr].z, W[rr].w), dg, dsc, tile_scale(S, rr), 0.0f);
+    acc[rr] = (ok && lane < C) ? a : 0.0f;
+  }
+  const float v = reduce8_rows(acc);
+  if ((lane & 7) == 7) out[lane >> 3] = v;
+}
+
 __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(6))) void k_down_dec1(
     LayerDev L, Dims D, const uint32_t *__restrict__ hq, const float *__restrict__ hs, UnionDev U,
     const float *__restrict__ wslot, float *__restrict__ residual) {
@@ -1639,10 +1720,9 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(6))) void 
   __shared__ int ok_s[16];
   __shared__ float wsl_s[16];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int ti = blockIdx.x, C = D.f / kChunk;
+  const int ti = blockIdx.x;
   const int nu = clamp_nu(U.n_unique, D);
   const int slots = nu + D.n_shared;
-  const ExpertLayout EL = expert_layout(D.d, D.f);
   // the combine's inputs (slot gate weights, the residual tile) are fetched
   // by wave 0 before its weights, so they are in hand after the barrier
   float wl = 0.0f, rin = 0.0f;
@@ -1653,28 +1733,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(6))) void 
   if (wave < slots) {
     int e, p0, p1;
     const bool ok = resolve_slot(D, U, nu, wave, e, p0, p1) && p1 > p0;
-    const uint8_t *base = expert_base(L, ok ? e : 0);
-    const __amdgpu_buffer_rsrc_t rn = wave_rsrc(base + EL.dn_nib, (uint32_t)(EL.dn_sc - EL.dn_nib));
-    const __amdgpu_buffer_rsrc_t rs = wave_rsrc(base + EL.dn_sc, (uint32_t)(EL.bytes - EL.dn_sc));
-    const int cl = lane < C ? lane : C - 1;
-    // chunk_offset with one step per row: tile, then row r at r * C * 16 bytes
-    const int tb = ti * kTileRows * (D.f / 2);
-    u32x4 W[kTileRows];
-#pragma unroll
-    for (int r = 0; r < kTileRows; ++r) W[r] = __builtin_amdgcn_raw_buffer_load_b128(rn, cl * 16, tb + r * C * 16, 0);
-    const u32x4 Sv = __builtin_amdgcn_raw_buffer_load_b128(rs, (cl >> 1) * 16, ti * (D.f / kGroup) * 16, 0);
-    uint32_t dg[kDigitWords];
-    float dsc[2];
-    load_digits(hq, hs, wave < nu ? p0 : D.T * D.k, D.f, cl, dg, dsc);
-    const uint4 S = make_uint4(Sv.x, Sv.y, Sv.z, Sv.w);
-    float acc[kTileRows];
-#pragma unroll
-    for (int rr = 0; rr < kTileRows; ++rr) {
-      const float a = fxp_chunk(make_uint4(W[rr].x, W[rr].y, W[rr].z, W[rr].w), dg, dsc, tile_scale(S, rr), 0.0f);
-      acc[rr] = (ok && lane < C) ? a : 0.0f;
-    }
-    const float v = reduce8_rows(acc);
-    if ((lane & 7) == 7) vb[wave][lane >> 3] = v;
+    dec_down_wave(L, D, ok, e, ti, wave < nu ? p0 : D.T * D.k, hq, hs, vb[wave]);
     if (lane == 0) ok_s[wave] = ok;
   }
   if (wave == 0 && lane < kDecMaxSlots) wsl_s[lane] = wl;
@@ -1690,6 +1749,80 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(6))) void 
   }
 }
 
+
+// Down + combine for 2-4 tokens when a down row is one step: a block per
+// (token, 8-row output tile), one wave per top-k position of the token (the
+// pair's h row, its expert from idx) plus the shared expert, the wave code of
+// k_down_dec1; wave 0 then folds the outputs into the token's residual in
+// pair order with the gate weights, then the shared expert's, as k_combine
+// does.  Items are (tile, token) with the token fastest, the block ids
+// remapped so each XCD takes one contiguous range: the tokens of one tile
+// read the same expert rows through one L2.
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(6))) void k_down_dec_tok(
+    LayerDev L, Dims D, const uint32_t *__restrict__ hq, const float *__restrict__ hs, UnionDev U,
+    const int32_t *__restrict__ idx, const float *__restrict__ w, float *__restrict__ residual, int n_items) {
+  __shared__ float vb[kDecMaxSlots][kTileRows];
+  __shared__ int ok_s[kDecMaxSlots], order_s[kDecMaxSlots], nsel_s;
+  __shared__ float wsl_s[kDecMaxSlots];
+  const int per = (int)gridDim.x / 8;
+  const int item = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+  if (item >= n_items) return;  // block-uniform
+  const int ti = item / D.T, t = item - ti * D.T;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int tk = D.T * D.k;
+  const int nu = clamp_nu(U.n_unique, D);
+  float rin = 0.0f;
+  if (wave == 0) {
+    // the token's pair positions ranked: the combine's order (experts
+    // ascending), with each position's gate weight
+    int p = 0x7FFFFFFF;
+    float wv = 0.0f;
+    if (nu > 0 && lane < D.k) {
+      p = U.pair_of[(size_t)t * D.k + lane];
+      if (p < 0 || p >= tk) p = 0x7FFFFFFF;
+      wv = w[(size_t)t * D.k + lane];
+    }
+    int rank = 0, valid = 0;
+    for (int i = 0; i < D.k; ++i) {
+      const int q = __shfl(p, i, 64);
+      rank += (q < p) || (q == p && i < lane);
+      valid += q < tk;
+    }
+    if (lane < D.k && p < tk) order_s[rank] = lane;
+    if (lane < kDecMaxSlots) wsl_s[lane] = wv;
+    if (lane == 0) nsel_s = valid;
+    rin = residual[(size_t)t * D.d + (size_t)ti * kTileRows + (lane & 7)];
+  }
+  if (wave < D.k + D.n_shared) {
+    bool ok;
+    int e, hrow;
+    if (wave < D.k) {
+      const int p = nu > 0 ? U.pair_of[(size_t)t * D.k + wave] : -1;
+      e = idx[(size_t)t * D.k + wave];
+      ok = p >= 0 && p < tk && e >= 0 && e < D.E;
+      hrow = ok ? p : 0;
+    } else {
+      ok = true;
+      e = D.E;
+      hrow = tk + t;
+    }
+    // a position dropped by expert top-p loads nothing (the test is the same
+    // for every lane of the wave)
+    if (__builtin_amdgcn_readfirstlane((int)ok)) dec_down_wave(L, D, true, e, ti, hrow, hq, hs, vb[wave]);
+    if (lane == 0) ok_s[wave] = ok;
+  }
+  __syncthreads();
+  if (wave == 0 && lane < kTileRows) {
+    float out = rin;
+    const int n = nsel_s;
+    for (int r = 0; r < n; ++r) {
+      const int j = order_s[r];
+      if (ok_s[j]) out = __builtin_fmaf(wsl_s[j], vb[j][lane], out);
+    }
+    if (D.n_shared) out = out + vb[D.k][lane];
+    residual[(size_t)t * D.d + (size_t)ti * kTileRows + lane] = out;
+  }
+}
 
 // Down projection and combine of the fp32 one-token pair: a block per 8-row
 // output tile, one wave per slot (up to kDecMaxSlots), few enough registers
@@ -2707,8 +2840,9 @@ static void down_tok_launch(int wpt, int grid, size_t lds, hipStream_t s, const 
   }
 }
 
-hipError_t launch_gateup_tok(const LayerDev &L, const Dims &D, const UnionDev &U, const float *w, const uint32_t *xq,
-                             const float *xs, uint32_t *hq, float *hs, float *wslot, bool skip_shared, hipStream_t s) {
+hipError_t launch_gateup_tok(const LayerDev &L, const Dims &D, const UnionDev &U, const int32_t *idx, const float *w,
+                             const uint32_t *xq, const float *xs, uint32_t *hq, float *hs, float *wslot,
+                             bool skip_shared, hipStream_t s) {
   if (D.T <= 0) return hipSuccess;
   const int NS = (D.d / kChunk + 63) / 64, wpt = NS < 4 ? NS : 4;
   const int slots = (D.T * D.k < D.E ? D.T * D.k : D.E) + D.n_shared;
@@ -2725,6 +2859,15 @@ hipError_t launch_gateup_tok(const LayerDev &L, const Dims &D, const UnionDev &U
       }
     } else
       gateup_tok_launch<2, true>(wpt, grid, lds, s, L, D, U, w, xq, xs, hq, hs, wslot);
+  } else if (NS <= 4 && D.T <= kPairsMaxT) {
+    const int items = (D.T * D.k + D.T * D.n_shared) * (D.f / 16);
+    const int pgrid = 8 * ((items + 7) / 8);
+    switch (NS) {
+      case 1: k_gateup_pairs<1><<<pgrid, 256, 0, s>>>(L, D, U, idx, xq, xs, hq, hs, items); break;
+      case 2: k_gateup_pairs<2><<<pgrid, 512, 0, s>>>(L, D, U, idx, xq, xs, hq, hs, items); break;
+      case 3: k_gateup_pairs<3><<<pgrid, 768, 0, s>>>(L, D, U, idx, xq, xs, hq, hs, items); break;
+      default: k_gateup_pairs<4><<<pgrid, 1024, 0, s>>>(L, D, U, idx, xq, xs, hq, hs, items); break;
+    }
   } else if (NS <= 4 && D.T <= kRouteSplitMaxT) {
     switch (NS) {
       case 1: k_gateup_few<1><<<grid, 256, 0, s>>>(L, D, U, xq, xs, hq, hs); break;
@@ -2791,6 +2934,20 @@ hipError_t launch_down_f32_dec(const LayerDev &L, const Dims &D, const float *h,
 
 bool down_dec_supported(const Dims &D) {
   return D.T == 1 && (D.f / kChunk + 63) / 64 == 1 && D.k + D.n_shared <= kDecMaxSlots;
+}
+
+bool down_dec_tok_supported(const Dims &D) {
+  return D.T >= 2 && D.T <= kDownTokMaxT && (D.f / kChunk + 63) / 64 == 1 && D.k + D.n_shared <= kDecMaxSlots;
+}
+
+hipError_t launch_down_dec_tok(const LayerDev &L, const Dims &D, const uint32_t *hq, const float *hs,
+                               const UnionDev &U, const int32_t *idx, const float *w, float *residual,
+                               hipStream_t s) {
+  if (!down_dec_tok_supported(D)) return hipErrorInvalidValue;
+  const int items = D.T * (D.d / kTileRows);
+  k_down_dec_tok<<<8 * ((items + 7) / 8), 64 * (D.k + D.n_shared), 0, s>>>(L, D, hq, hs, U, idx, w, residual,
+                                                                            items);
+  return hipGetLastError();
 }
 
 hipError_t launch_down_dec(const LayerDev &L, const Dims &D, const uint32_t *hq, const float *hs, const UnionDev &U,
