@@ -1262,10 +1262,6 @@ __global__ __launch_bounds__(256 * NS) void k_gateup_one(LayerDev L, Dims D, Uni
   gateup_one_quad<NS>(L, D, e, orow, qd, 0, xq, xs, hq, hs);
 }
 
-// k_gateup_one with the slot's tokens looped kFewT at a time: every wave loads
-// its (tile, step) weights once and applies them to each token in turn; per
-// token the operations are those of k_gateup_tok and k_gateup_one, so the
-// bits do not depend on the batch.
 // 2-16 tokens: a block per (pair, quad), the one-token block code on the
 // pair's token, so each token's h has the bits of the token alone.  Items are
 // (quad, pair) with the pair fastest; the block ids are remapped so that each
@@ -1312,98 +1308,8 @@ __global__ __launch_bounds__(256 * NS) void k_gateup_pairs(LayerDev L, Dims D, U
   gateup_one_quad<NS>(L, D, e, pr_s[2], qd, pr_s[1], xq, xs, hq, hs);
 }
 
-constexpr int kFewT = 4;
 constexpr int kPairsMaxT = 16;   // tokens up to which gate/up runs per pair
 constexpr int kDownTokMaxT = 4;  // tokens up to which down runs per token (with the combine)
-
-template <int NS>
-__global__ __launch_bounds__(256 * NS) __attribute__((amdgpu_waves_per_eu(6))) void k_gateup_few(LayerDev L, Dims D, UnionDev U,
-                                                         const uint32_t *__restrict__ xq,
-                                                         const float *__restrict__ xs, uint32_t *__restrict__ hq,
-                                                         float *__restrict__ hs) {
-  __shared__ float red[kFewT][4][NS][kTileRows];
-  __shared__ int slot_s[4];  // expert, p0, p1, nu
-  __shared__ int tok_s[kFewT], orow_s[kFewT];
-  __shared__ uint32_t hw[kFewT][12];
-  __shared__ float hsc[kFewT];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int C = D.d / kChunk, quads = D.f / 16;
-  const int s = blockIdx.x / quads, qd = blockIdx.x - s * quads;
-  const int tt = wave / NS, st = wave - tt * NS;
-  const int ti = qd * 4 + tt, c = lane + 64 * st;
-  if (threadIdx.x == 0) {
-    const int nu = clamp_nu(U.n_unique, D);
-    int e = -1, p0 = 0, p1 = 0;
-    if (s < nu || (s == nu && D.n_shared)) {
-      if (!resolve_slot(D, U, nu, s, e, p0, p1) || p1 <= p0) e = -1;
-    }
-    slot_s[0] = e;
-    slot_s[1] = p0;
-    slot_s[2] = p1;
-    slot_s[3] = nu;
-  }
-  __syncthreads();
-  const int e = slot_s[0], p0 = slot_s[1], p1 = slot_s[2], nu = slot_s[3];
-  if (e < 0) return;  // block-uniform
-  const ExpertLayout EL = expert_layout(D.d, D.f);
-  const uint8_t *base = expert_base(L, e);
-  uint4 W[kTileRows], S;
-  if (c < C) load_step(base + EL.gu_nib, base + EL.gu_sc, ti, D.d, c, W, S);
-  for (int pg = p0; pg < p1; pg += kFewT) {
-    const int mc = min(kFewT, p1 - pg);
-    if ((int)threadIdx.x < mc) {
-      int t, orow;
-      slot_token(D, U, nu, s, pg + threadIdx.x, t, orow);
-      tok_s[threadIdx.x] = t;
-      orow_s[threadIdx.x] = orow;
-    }
-    if ((int)threadIdx.x < kFewT * 12) hw[threadIdx.x / 12][threadIdx.x % 12] = 0u;
-    __syncthreads();
-    for (int m = 0; m < mc; ++m) {
-      float acc[kTileRows];
-#pragma unroll
-      for (int r = 0; r < kTileRows; ++r) acc[r] = 0.0f;
-      if (c < C) fxp_step(W, S, xq, xs, tok_s[m], D.d, c, acc);
-      const float v = reduce8_rows(acc);
-      if ((lane & 7) == 7) red[m][tt][st][lane >> 3] = v;
-    }
-    __syncthreads();
-    // h for (token m, h row i): tile i/4, gate row i%4, up row i%4 + 4; each
-    // token's 16 values sit in one 16-lane row for the encoding
-    if ((int)threadIdx.x < mc * 16) {
-      const int m = threadIdx.x >> 4, i = threadIdx.x & 15, t4 = i >> 2, r = i & 3;
-      float g = red[m][t4][0][r], u = red[m][t4][0][r + 4];
-#pragma unroll
-      for (int j = 1; j < NS; ++j) {
-        g = g + red[m][t4][j][r];
-        u = u + red[m][t4][j][r + 4];
-      }
-      const float hval = silu_f(g) * u;
-      uint32_t mb = f_bits(fabsf(hval));
-      mb = max(mb, dpp<kRowRor8>(mb));
-      mb = max(mb, dpp<kRowRor4>(mb));
-      mb = max(mb, dpp<kRowRor2>(mb));
-      mb = max(mb, dpp<kRowRor1>(mb));
-      float sc;
-      bool fin;
-      const int E = fxp_exponent(mb, sc, fin);
-      const uint32_t B = (uint32_t)((int)__builtin_rintf((fin ? hval : 0.0f) * ldexpf(1.0f, 22 - E)) + 0x888888);
-#pragma unroll
-      for (int k = 0; k < 6; ++k) atomicOr(&hw[m][2 * k + (i >> 3)], (((B >> (4 * k)) & 15u) ^ 8u) << (4 * (i & 7)));
-      if (i == 0) hsc[m] = sc;
-    }
-    __syncthreads();
-    if ((int)threadIdx.x < mc * 12) {
-      const int m = threadIdx.x / 12, wd = threadIdx.x - m * 12;
-      const int orow = orow_s[m];
-      if (orow >= 0) {
-        hq[((size_t)orow * (D.f / kChunk) + (qd >> 1)) * kDigitWords + (qd & 1) * 12 + wd] = hw[m][wd];
-        if (wd == 0) hs[(size_t)orow * (D.f / 16) + qd] = hsc[m];
-      }
-    }
-    __syncthreads();
-  }
-}
 
 // Down: block = (slot, 4 output tiles = 32 rows); y[output row of the pair]
 // for each of the slot's pairs (the shared expert: rows T*k + t).  The
@@ -2867,13 +2773,6 @@ hipError_t launch_gateup_tok(const LayerDev &L, const Dims &D, const UnionDev &U
       case 2: k_gateup_pairs<2><<<pgrid, 512, 0, s>>>(L, D, U, idx, xq, xs, hq, hs, items); break;
       case 3: k_gateup_pairs<3><<<pgrid, 768, 0, s>>>(L, D, U, idx, xq, xs, hq, hs, items); break;
       default: k_gateup_pairs<4><<<pgrid, 1024, 0, s>>>(L, D, U, idx, xq, xs, hq, hs, items); break;
-    }
-  } else if (NS <= 4 && D.T <= kRouteSplitMaxT) {
-    switch (NS) {
-      case 1: k_gateup_few<1><<<grid, 256, 0, s>>>(L, D, U, xq, xs, hq, hs); break;
-      case 2: k_gateup_few<2><<<grid, 512, 0, s>>>(L, D, U, xq, xs, hq, hs); break;
-      case 3: k_gateup_few<3><<<grid, 768, 0, s>>>(L, D, U, xq, xs, hq, hs); break;
-      default: k_gateup_few<4><<<grid, 1024, 0, s>>>(L, D, U, xq, xs, hq, hs); break;
     }
   } else {
     if (NS <= 4)
