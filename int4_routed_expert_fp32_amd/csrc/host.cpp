@@ -356,7 +356,8 @@ static int forward_kernels(colimoe_ctx *ctx, int32_t layer, const float *x, int3
   }
   float *h = (float *)(ctx->ws + ctx->wl.h);
   float *y = (float *)(ctx->ws + ctx->wl.y);
-  const bool fused = (path == PATH_FP32 && down_fusable(D)) || (path == PATH_I8 && i8_dec_supported(D));
+  const bool fused = (path == PATH_FP32 && (down_fusable(D) || narrow_dec_supported(D))) ||
+                     (path == PATH_I8 && i8_dec_supported(D));
   if (path == PATH_I8) {
     KTimer kt(ctx, K_GATEUP);
     if (fused) {

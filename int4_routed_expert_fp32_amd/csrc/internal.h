@@ -138,6 +138,9 @@ hipError_t launch_gateup(const LayerDev &L, const Dims &D, const float *x, const
 hipError_t launch_debug_gateup(const LayerDev &L, const Dims &D, const float *x, const UnionDev &U, float *h,
                                float *g, float *u, hipStream_t s);
 bool down_fusable(const Dims &D);
+// One token on the narrow shapes (f < 2048) with k + shared <= 16: launch_down
+// with fused set runs down and combine in one kernel.
+bool narrow_dec_supported(const Dims &D);
 // fused: y stays in LDS and the combine into `residual` happens in the same
 // kernel; otherwise y is written to global memory for launch_combine.
 hipError_t launch_down(const LayerDev &L, const Dims &D, const float *h, const UnionDev &U, float *y,

@@ -2303,6 +2303,62 @@ __global__ __launch_bounds__(256) void k_down_narrow(LayerDev L, Dims D, const f
   }
 }
 
+// Down + combine for one token on the narrow shapes (f < 2048): a block per
+// 8-row output tile, one wave per slot (up to kDecMaxSlots) with the
+// operations of k_down_narrow (narrow_tile, narrow_reduce) on the slot's h
+// row; wave 0 folds the slots' rows into the residual as k_combine does
+// (routed slots in pair order, which for one token is slot order, with their
+// gate weights, then the shared expert).
+template <int LPR>
+__global__ __launch_bounds__(64 * kDecMaxSlots) void k_down_narrow_dec1(LayerDev L, Dims D,
+                                                                        const float *__restrict__ h, UnionDev U,
+                                                                        const float *__restrict__ w,
+                                                                        float *__restrict__ residual) {
+  using NS = NarrowShape<LPR>;
+  __shared__ float vb[kDecMaxSlots][kTileRows];
+  __shared__ int ok_s[kDecMaxSlots];
+  __shared__ float wsl_s[kDecMaxSlots];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int ti = blockIdx.x;
+  const int nu = clamp_nu(U.n_unique, D);
+  const int slots = nu + D.n_shared;
+  float rin = 0.0f;
+  if (wave == 0) {
+    // slot lane's gate weight: its one pair's top-k position (pair = slot)
+    float wv = 0.0f;
+    if (lane < nu) {
+      int js = U.pair_slot[lane];
+      js = js < 0 ? 0 : (js >= D.k ? D.k - 1 : js);  // caller-supplied lists stay in bounds
+      wv = w[js];
+    }
+    if (lane < kDecMaxSlots) wsl_s[lane] = wv;
+    rin = residual[(size_t)ti * kTileRows + (lane & 7)];
+  }
+  if (wave < slots) {
+    int e, p0, p1;
+    const bool ok = resolve_slot(D, U, nu, wave, e, p0, p1) && p1 > p0;
+    if (__builtin_amdgcn_readfirstlane((int)ok)) {
+      const ExpertLayout EL = expert_layout(D.d, D.f);
+      const uint8_t *base = expert_base(L, e);
+      const int xrow[1] = {wave < nu ? p0 : D.T * D.k};
+      float acc[1][NS::RPG];
+      narrow_tile<LPR, 1>(base + EL.dn_nib, base + EL.dn_sc, ti, D.f, h, (size_t)D.f, xrow, 1, acc);
+      narrow_reduce<LPR>(acc[0], vb[wave]);
+    }
+    if (lane == 0) ok_s[wave] = ok;
+  }
+  __syncthreads();
+  if (wave == 0 && lane < kTileRows) {
+    float out = rin;
+    for (int sl = 0; sl < slots; ++sl) {
+      if (!ok_s[sl]) continue;
+      const float v = vb[sl][lane];
+      out = sl < nu ? __builtin_fmaf(wsl_s[sl], v, out) : out + v;
+    }
+    residual[(size_t)ti * kTileRows + lane] = out;
+  }
+}
+
 // ------------------------------------------------------------------ combine
 // A7: r[t] += sum over the token's experts in ascending id of w * y, then the
 // shared expert's y (weight 1).  Fixed order, no atomics: a token's result
@@ -2672,6 +2728,8 @@ static size_t fused_rows(const Dims &D) { return (size_t)D.T * D.k + (size_t)D.T
 
 bool down_fusable(const Dims &D) { return wide(D.f) && fused_rows(D) * kTileRows * 4 <= kFusedLdsMax; }
 
+bool narrow_dec_supported(const Dims &D) { return D.T == 1 && !wide(D.f) && slots_max(D) <= kDecMaxSlots; }
+
 hipError_t launch_down(const LayerDev &L, const Dims &D, const float *h, const UnionDev &U, float *y,
                        const float *w, float *residual, bool fused, hipStream_t s) {
   if (D.T <= 0) return hipSuccess;
@@ -2693,6 +2751,16 @@ hipError_t launch_down(const LayerDev &L, const Dims &D, const float *h, const U
         k_down_wide<1, false, 9><<<grid, block, 0, s>>>(L, D, h, U, y, w, residual);
       else
         k_down_wide<8, false, 8><<<grid, block, 0, s>>>(L, D, h, U, y, w, residual);
+    }
+  } else if (fused) {  // one token (narrow_dec_supported)
+    const dim3 grid(D.d / kTileRows), block(64 * slots_max(D));
+    switch (narrow_lpr(D.f)) {
+      case 64: k_down_narrow_dec1<64><<<grid, block, 0, s>>>(L, D, h, U, w, residual); break;
+      case 32: k_down_narrow_dec1<32><<<grid, block, 0, s>>>(L, D, h, U, w, residual); break;
+      case 16: k_down_narrow_dec1<16><<<grid, block, 0, s>>>(L, D, h, U, w, residual); break;
+      case 8: k_down_narrow_dec1<8><<<grid, block, 0, s>>>(L, D, h, U, w, residual); break;
+      case 4: k_down_narrow_dec1<4><<<grid, block, 0, s>>>(L, D, h, U, w, residual); break;
+      default: k_down_narrow_dec1<2><<<grid, block, 0, s>>>(L, D, h, U, w, residual); break;
     }
   } else {
     const long long items = (long long)slots_max(D) * (D.d / kTileRows);
