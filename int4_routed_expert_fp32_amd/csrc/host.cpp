@@ -297,6 +297,13 @@ static int route_impl(colimoe_ctx *ctx, int32_t layer, const float *x, int32_t T
   float *lg = logits ? logits : (float *)(ctx->ws + ctx->wl.logits);
   hipStream_t s = ctx->stream;
   int32_t *err = (int32_t *)(ctx->ws + ctx->wl.err);
+  if (D.T == 1 && !encode && !shared_early && route_one_small_supported(D)) {
+    KTimer kt(ctx, K_ROUTE);
+    const UnionDev U = u ? to_dev(u) : UnionDev{};
+    if (launch_route_one_small(L, D, x, lg, idx, w, u ? &U : nullptr, ctx->top_p, s) != hipSuccess)
+      return COLIMOE_E_HIP;
+    return COLIMOE_OK;
+  }
   if (D.T <= kRouteSplitMaxT) {
     {
       KTimer kt(ctx, K_ROUTE);

@@ -125,6 +125,11 @@ bool shared_early_supported(const Dims &D);
 hipError_t launch_topk_shared1(const float *logits, const Dims &D, int32_t *idx, float *w, const UnionDev *U,
                                float top_p, const LayerDev &L, const uint32_t *xq, const float *xs, uint32_t *hq,
                                float *hs, hipStream_t s);
+// Router, top-k and (if U) union lists of one token in one launch, for E <= 32
+// and d <= 2048 (the logits, selection and lists of the separate kernels).
+bool route_one_small_supported(const Dims &D);
+hipError_t launch_route_one_small(const LayerDev &L, const Dims &D, const float *x, float *logits, int32_t *idx,
+                                  float *w, const UnionDev *U, float top_p, hipStream_t s);
 hipError_t launch_topk_union1(const float *logits, const Dims &D, int32_t *idx, float *w, const UnionDev *U,
                               float top_p, hipStream_t s);
 hipError_t launch_topk(const float *logits, const Dims &D, int32_t *idx, float *w, float top_p, hipStream_t s);

@@ -1550,6 +1550,77 @@ __global__ __launch_bounds__(64) void k_topk_union1(const float *__restrict__ lo
   if (with_union) union_one_token(ids, D, U);
 }
 
+// Router, top-k and union lists of one token in one block, for small routers
+// (E <= 32, d <= 2048; at 64 experts the one block's row loads cost more than
+// the launch it saves).  Wave group g (4 waves) takes rows g, g + 4, ...,
+// wave w of the group the quarter of the columns k_router_split gives it;
+// every row's loads are issued before any arithmetic, then per row the fmas
+// in router_tokens<1>'s order, the wave sum and the 4 partial sums added in
+// wave order: the logits are k_router_split's bits.  Wave 0 then selects as
+// k_topk_union1 does.
+constexpr int kRouteOneMaxE = 32;
+template <int NF, int PER>
+__global__ __launch_bounds__(1024) void k_route_one_small(LayerDev L, Dims D, const float *__restrict__ x,
+                                                          float *__restrict__ logits, int32_t *__restrict__ idx,
+                                                          float *__restrict__ wout, UnionDev U, int with_union,
+                                                          float top_p) {
+  constexpr int RB = kRouteOneMaxE / 4;  // rows per wave group at most
+  __shared__ float part[kRouteOneMaxE][4];
+  __shared__ float lg[kRouteOneMaxE];
+  __shared__ int32_t ids[16];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int g4 = wave >> 2, w4 = wave & 3, q4 = D.d / 4;
+  float4 xv[NF], rr[RB][NF];
+#pragma unroll
+  for (int i = 0; i < NF; ++i) {
+    const int c = 4 * lane + 256 * i;
+    xv[i] = c < q4 ? *(const float4 *)(x + (size_t)w4 * q4 + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+#pragma unroll
+  for (int b = 0; b < RB; ++b) {
+    const int e = g4 + 4 * b;
+    const float *row = L.router + (size_t)(e < D.E ? e : 0) * D.d + (size_t)w4 * q4;
+#pragma unroll
+    for (int i = 0; i < NF; ++i) {
+      const int c = 4 * lane + 256 * i;
+      rr[b][i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (e < D.E && c < q4) rr[b][i] = *(const float4 *)(row + c);  // rows past E load nothing
+    }
+  }
+#pragma unroll
+  for (int b = 0; b < RB; ++b) {
+    const int e = g4 + 4 * b;
+    if (e < D.E) {  // wave-uniform
+      float acc = 0.0f;
+#pragma unroll
+      for (int i = 0; i < NF; ++i) {
+        const int c = 4 * lane + 256 * i;
+        if (c < q4) {
+          acc = __builtin_fmaf(rr[b][i].x, xv[i].x, acc);
+          acc = __builtin_fmaf(rr[b][i].y, xv[i].y, acc);
+          acc = __builtin_fmaf(rr[b][i].z, xv[i].z, acc);
+          acc = __builtin_fmaf(rr[b][i].w, xv[i].w, acc);
+        }
+      }
+      const float v = wave_sum(acc);
+      if (lane == 0) part[e][w4] = v;
+    }
+  }
+  __syncthreads();
+  if ((int)threadIdx.x < D.E) {
+    const int e = threadIdx.x;
+    const float v = ((part[e][0] + part[e][1]) + part[e][2]) + part[e][3] + L.bias[e];
+    lg[e] = v;
+    logits[e] = v;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    topk_token<PER>(lg, D, 0, idx, wout, ids, top_p);
+    wave_lds_sync();
+    if (with_union) union_one_token(ids, D, U);
+  }
+}
+
 // Top-k of one token plus its union lists (block 0, as k_topk_union1), and
 // beside it the shared expert's gate/up (blocks 1..f/16, one quad each, as
 // k_gateup_one): the shared expert does not depend on the routing, so its
@@ -2505,6 +2576,24 @@ hipError_t launch_topk_union1(const float *logits, const Dims &D, int32_t *idx, 
     case 8: k_topk_union1<8><<<1, 64, 0, s>>>(logits, D, idx, w, u, wu, top_p); break;
     default: k_topk_union1<16><<<1, 64, 0, s>>>(logits, D, idx, w, u, wu, top_p); break;
   }
+  return hipGetLastError();
+}
+
+bool route_one_small_supported(const Dims &D) {
+  const int nf = (D.d / 4 + 255) / 256;
+  return D.T == 1 && D.E <= kRouteOneMaxE && nf <= 2;
+}
+
+hipError_t launch_route_one_small(const LayerDev &L, const Dims &D, const float *x, float *logits, int32_t *idx,
+                                  float *w, const UnionDev *U, float top_p, hipStream_t s) {
+  if (!route_one_small_supported(D)) return hipErrorInvalidValue;
+  const UnionDev u = U ? *U : UnionDev{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
+  const int wu = U ? 1 : 0;
+  // E <= 32: one top-k key per lane (topk_per(E) = 1)
+  if ((D.d / 4 + 255) / 256 == 1)
+    k_route_one_small<1, 1><<<1, 1024, 0, s>>>(L, D, x, logits, idx, w, u, wu, top_p);
+  else
+    k_route_one_small<2, 1><<<1, 1024, 0, s>>>(L, D, x, logits, idx, w, u, wu, top_p);
   return hipGetLastError();
 }
 

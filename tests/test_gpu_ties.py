@@ -136,3 +136,73 @@ def test_duplicated_router_rows_go_to_the_lower_index(ctx_and_layers, T, form):
         blobs = {e: ex[e] for e in EXPECT}
         out, _ = oracle.moe_layer(X, W.d, W.f, blobs, sh, idx, wref, E=W.E)
         P.assert_close(res.cpu().numpy(), out, what="layer output")
+
+
+# The same cases on a small router (E <= 32, d <= 2048): one-token calls route
+# and select in one block there.
+WS = synth.Workload(name="ties_small", d=512, f=128, E=24, k=4, T=1, n_shared=1, seed=synth.BASE_SEED + 302)
+G1S = [20, 3]            # bias +10: the two largest logits
+G2S = [22, 10, 5, 6, 15]  # bias +5: the tied group cut at the 4th place keeps 5 and 6
+EXPECT_S = [3, 20, 5, 6]
+FORMS_S = ["route", "route_forward", "route_no_union"]
+
+
+@pytest.fixture(scope="module")
+def small_ctx():
+    from int4_routed_expert_fp32_amd.runtime import MoeContext
+    oracle.build(force=False)
+    synth.build(force=False)
+    print("ties: context d=%d f=%d E=%d k=%d" % (WS.d, WS.f, WS.E, WS.k), flush=True)
+    ctx = MoeContext(WS.d, WS.f, WS.E, WS.k, n_layers=2, n_shared=WS.n_shared, max_tokens=1)
+    ex = synth.expert_blobs(WS, 0, 0, WS.E)
+    sh = synth.shared_blob(WS, 0)
+    R0 = synth.router(WS, 0)
+    ctx.load_layer(0, R0, None, ex, sh)
+    R1 = R0.copy()
+    b1 = np.zeros(WS.E, np.float32)
+    for e in G1S:
+        R1[e] = R0[G1S[1]]
+        b1[e] = 10.0
+    for e in G2S:
+        R1[e] = R0[G2S[3]]
+        b1[e] = 5.0
+    ctx.load_layer(1, R1, b1, ex, sh)
+    yield ctx, R1, b1, ex, sh
+    ctx.close()
+
+
+@pytest.mark.parametrize("form", FORMS_S)
+@pytest.mark.parametrize("zero", ["+0", "-0"])
+def test_small_router_zero_logits(small_ctx, form, zero):
+    ctx = small_ctx[0]
+    X = np.full((1, WS.d), 0.0 if zero == "+0" else -0.0, np.float32)
+    idx, w, lg, union = _route(ctx, 0, X, form)
+    if lg is not None:
+        assert np.all(lg == 0.0)
+    assert np.array_equal(idx, np.arange(WS.k, dtype=np.int32)[None, :]), idx
+    assert np.array_equal(w.view(np.uint32), np.full((1, WS.k), np.float32(1.0 / WS.k)).view(np.uint32)), w
+    if union is not None:
+        o = oracle.union(idx, WS.E)
+        for key in ("ids", "offsets", "pair_token", "pair_slot", "pair_of"):
+            assert np.array_equal(union[key], o[key]), key
+
+
+@pytest.mark.parametrize("form", FORMS_S)
+def test_small_router_duplicated_rows(small_ctx, form):
+    ctx, R1, b1, ex, sh = small_ctx
+    X = synth.activations(WS, stream=5)[:1]
+    idx, w, lg, union = _route(ctx, 1, X, form)
+    L, oidx, ow = oracle.route(R1, b1, X.astype(np.float64), WS.k)
+    assert np.array_equal(oidx[0], np.array(EXPECT_S, np.int32)), "oracle: " + str(oidx[0])
+    assert np.array_equal(idx, oidx), "GPU %s vs oracle %s" % (idx[0], oidx[0])
+    if lg is not None:
+        for grp in (G1S, G2S):
+            assert np.all(lg[:, grp] == lg[:, grp[:1]])
+        P.assert_close(lg, L, rel=1e-4, what="logits")
+    wref = np.stack([oracle.softmax_selected(L[0], idx[0])])
+    P.assert_close(w, wref, rel=1e-4, what="gate weights")
+    assert w[0, 0] == w[0, 1] and np.all(w[0, 2:] == w[0, 2])
+    if union is not None:
+        o = oracle.union(idx, WS.E)
+        for key in ("ids", "offsets", "pair_token", "pair_slot", "pair_of"):
+            assert np.array_equal(union[key], o[key]), key
