@@ -288,8 +288,8 @@ static colimoe_union ws_union_abi(colimoe_ctx *ctx) {
 
 // Router, top-k and (if u) union lists; `encode` also writes the fixed-point
 // encoding of x into the workspace when the route runs as one kernel, and
-// `shared_early` (one token) runs the shared expert's fixed-point gate/up in
-// the top-k launch.
+// `shared_early` (up to 4 tokens) runs the shared expert's fixed-point
+// gate/up in the top-k launch.
 static int route_impl(colimoe_ctx *ctx, int32_t layer, const float *x, int32_t T, int32_t *idx, float *w,
                const colimoe_union *u, float *logits, bool encode, bool shared_early = false) {
   const Dims D = dims_of(ctx, T);
@@ -326,7 +326,14 @@ static int route_impl(colimoe_ctx *ctx, int32_t layer, const float *x, int32_t T
     }
     if (u) {  // up to 16 tokens: top-k and the union lists in one launch
       KTimer kt(ctx, K_TOPK);
-      if (launch_topk_union(lg, D, idx, w, to_dev(u), err, ctx->top_p, s) != hipSuccess) return COLIMOE_E_HIP;
+      if (shared_early) {
+        if (launch_topk_union_shared(lg, D, idx, w, to_dev(u), err, ctx->top_p, L, (uint32_t *)(ctx->ws + ctx->wl.xq),
+                                     (float *)(ctx->ws + ctx->wl.xs), (uint32_t *)(ctx->ws + ctx->wl.hq),
+                                     (float *)(ctx->ws + ctx->wl.hs), s) != hipSuccess)
+          return COLIMOE_E_HIP;
+      } else if (launch_topk_union(lg, D, idx, w, to_dev(u), err, ctx->top_p, s) != hipSuccess) {
+        return COLIMOE_E_HIP;
+      }
       return COLIMOE_OK;
     }
   } else {
@@ -686,9 +693,10 @@ int colimoe_route_forward(colimoe_ctx *ctx, int32_t layer, const float *x, int32
   const colimoe_union *uu = u ? u : &uw;
   const bool encode = path == PATH_FXP;
   const Dims D = dims_of(ctx, T);
-  // one token on an HBM-resident layer: the shared expert's gate/up rides in
-  // the top-k launch
-  const bool early = encode && !ctx->host_store[layer] && shared_early_supported(D);
+  // up to 4 tokens on an HBM-resident layer: the shared expert's gate/up
+  // rides in the top-k launch
+  const bool early =
+      encode && !ctx->host_store[layer] && (shared_early_supported(D) || shared_early_multi_supported(D));
   rc = route_impl(ctx, layer, x, T, idx, w, uu, nullptr, encode, early);
   if (rc) return rc;
   return forward_impl(ctx, layer, x, T, idx, w, uu, residual, path, encode && T <= kRouteSplitMaxT, early);

@@ -130,6 +130,13 @@ hipError_t launch_topk_shared1(const float *logits, const Dims &D, int32_t *idx,
 bool route_one_small_supported(const Dims &D);
 hipError_t launch_route_one_small(const LayerDev &L, const Dims &D, const float *x, float *logits, int32_t *idx,
                                   float *w, const UnionDev *U, float top_p, hipStream_t s);
+// 2-4 tokens with union lists: launch_topk_union, and the shared expert's
+// fixed-point gate/up for every token in the same launch (h rows T*k + t, as
+// launch_gateup_tok writes them).
+bool shared_early_multi_supported(const Dims &D);
+hipError_t launch_topk_union_shared(const float *logits, const Dims &D, int32_t *idx, float *w, const UnionDev &U,
+                                    int32_t *err, float top_p, const LayerDev &L, const uint32_t *xq,
+                                    const float *xs, uint32_t *hq, float *hs, hipStream_t s);
 hipError_t launch_topk_union1(const float *logits, const Dims &D, int32_t *idx, float *w, const UnionDev *U,
                               float top_p, hipStream_t s);
 hipError_t launch_topk(const float *logits, const Dims &D, int32_t *idx, float *w, float top_p, hipStream_t s);

@@ -1280,7 +1280,7 @@ __global__ __launch_bounds__(256 * NS) void k_gateup_pairs(LayerDev L, Dims D, U
   const int per = (int)gridDim.x / 8;
   const int item = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
   if (item >= n_items) return;  // block-uniform
-  const int tk = D.T * D.k, P = tk + D.T * D.n_shared;
+  const int tk = D.T * D.k, P = n_items / (D.f / 16);  // pairs per quad: tk, plus T shared rows unless done
   const int qd = item / P, p = item - qd * P;
   if (threadIdx.x == 0) {
     int e = -1, t = 0;
@@ -1310,6 +1310,10 @@ __global__ __launch_bounds__(256 * NS) void k_gateup_pairs(LayerDev L, Dims D, U
 
 constexpr int kPairsMaxT = 16;   // tokens up to which gate/up runs per pair
 constexpr int kDownTokMaxT = 4;  // tokens up to which down runs per token (with the combine)
+// tokens up to which the shared gate/up rides in the top-k launch (at 16 the
+// shared expert's 16 token rows outlast the selection: +25 us of top-k launch
+// for -15 us of gate/up)
+constexpr int kSharedEarlyMaxT = 4;
 
 // Down: block = (slot, 4 output tiles = 32 rows); y[output row of the pair]
 // for each of the slot's pairs (the shared expert: rows T*k + t).  The
@@ -2720,6 +2724,76 @@ __global__ __launch_bounds__(1024) void k_topk_union(const float *__restrict__ l
   }
 }
 
+// As k_topk_union (block 0), and beside it the shared expert's gate/up for
+// every token (blocks 1.., one (quad, token) item each, the one-token block
+// code): the shared expert does not depend on the routing, so its weights
+// stream while the selection runs.  Items are quad-major with XCD-contiguous
+// ranges, as in k_gateup_pairs, so the tokens of one quad share an L2.
+template <int PER, int NS>
+__global__ __launch_bounds__(1024) void k_topk_union_shared(const float *__restrict__ logits, Dims D,
+                                                            int32_t *__restrict__ idx, float *__restrict__ wout,
+                                                            UnionDev U, int32_t *__restrict__ err, float top_p,
+                                                            LayerDev L, const uint32_t *__restrict__ xq,
+                                                            const float *__restrict__ xs, uint32_t *__restrict__ hq,
+                                                            float *__restrict__ hs) {
+  extern __shared__ unsigned long long masks[];
+  __shared__ int32_t sids[kRouteSplitMaxT * 16];
+  if (blockIdx.x > 0) {
+    if ((int)threadIdx.x >= 256 * NS) return;  // waves past the block code's
+    const int b = (int)blockIdx.x - 1, per = ((int)gridDim.x - 1) / 8;
+    const int item = (b % 8) * per + b / 8;
+    if (item >= D.T * (D.f / 16)) return;  // block-uniform
+    const int qd = item / D.T, t = item - qd * D.T;
+    gateup_one_quad<NS>(L, D, D.E, D.T * D.k + t, qd, t, xq, xs, hq, hs);
+    return;
+  }
+  const int t = threadIdx.x >> 6;
+  if (t < D.T) topk_token<PER>(logits + (size_t)t * D.E, D, t, idx, wout, sids, top_p);
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    if (D.T * D.k <= 64)
+      union_small(sids, D, U, err);
+    else
+      union_wave(sids, D, U, err, masks);
+  }
+}
+
+bool shared_early_multi_supported(const Dims &D) {
+  const int NS = (D.d / kChunk + 63) / 64;
+  return D.T >= 2 && D.T <= kSharedEarlyMaxT && D.n_shared == 1 && NS <= 4 && D.f % 16 == 0;
+}
+
+template <int PER>
+static void topk_union_shared_launch(int NS, int grid, int block, size_t lds, hipStream_t s, const float *logits,
+                                     const Dims &D, int32_t *idx, float *w, const UnionDev &U, int32_t *err,
+                                     float top_p, const LayerDev &L, const uint32_t *xq, const float *xs,
+                                     uint32_t *hq, float *hs) {
+  switch (NS) {
+    case 1: k_topk_union_shared<PER, 1><<<grid, block, lds, s>>>(logits, D, idx, w, U, err, top_p, L, xq, xs, hq, hs); break;
+    case 2: k_topk_union_shared<PER, 2><<<grid, block, lds, s>>>(logits, D, idx, w, U, err, top_p, L, xq, xs, hq, hs); break;
+    case 3: k_topk_union_shared<PER, 3><<<grid, block, lds, s>>>(logits, D, idx, w, U, err, top_p, L, xq, xs, hq, hs); break;
+    default: k_topk_union_shared<PER, 4><<<grid, block, lds, s>>>(logits, D, idx, w, U, err, top_p, L, xq, xs, hq, hs); break;
+  }
+}
+
+hipError_t launch_topk_union_shared(const float *logits, const Dims &D, int32_t *idx, float *w, const UnionDev &U,
+                                    int32_t *err, float top_p, const LayerDev &L, const uint32_t *xq,
+                                    const float *xs, uint32_t *hq, float *hs, hipStream_t s) {
+  if (!shared_early_multi_supported(D)) return hipErrorInvalidValue;
+  const int NS = (D.d / kChunk + 63) / 64;
+  const int block = 64 * D.T > 256 * NS ? 64 * D.T : 256 * NS;
+  const int grid = 1 + 8 * ((D.T * (D.f / 16) + 7) / 8);
+  const size_t lds = union_lds_bytes(D.E);
+  switch (topk_per(D.E)) {
+    case 1: topk_union_shared_launch<1>(NS, grid, block, lds, s, logits, D, idx, w, U, err, top_p, L, xq, xs, hq, hs); break;
+    case 2: topk_union_shared_launch<2>(NS, grid, block, lds, s, logits, D, idx, w, U, err, top_p, L, xq, xs, hq, hs); break;
+    case 4: topk_union_shared_launch<4>(NS, grid, block, lds, s, logits, D, idx, w, U, err, top_p, L, xq, xs, hq, hs); break;
+    case 8: topk_union_shared_launch<8>(NS, grid, block, lds, s, logits, D, idx, w, U, err, top_p, L, xq, xs, hq, hs); break;
+    default: topk_union_shared_launch<16>(NS, grid, block, lds, s, logits, D, idx, w, U, err, top_p, L, xq, xs, hq, hs); break;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_topk_union(const float *logits, const Dims &D, int32_t *idx, float *w, const UnionDev &U,
                              int32_t *err, float top_p, hipStream_t s) {
   if (D.T < 1 || D.T > kRouteSplitMaxT) return hipErrorInvalidValue;
@@ -2923,7 +2997,8 @@ hipError_t launch_gateup_tok(const LayerDev &L, const Dims &D, const UnionDev &U
     } else
       gateup_tok_launch<2, true>(wpt, grid, lds, s, L, D, U, w, xq, xs, hq, hs, wslot);
   } else if (NS <= 4 && D.T <= kPairsMaxT) {
-    const int items = (D.T * D.k + D.T * D.n_shared) * (D.f / 16);
+    // with skip_shared the shared expert's rows are already there
+    const int items = (D.T * D.k + (skip_shared ? 0 : D.T * D.n_shared)) * (D.f / 16);
     const int pgrid = 8 * ((items + 7) / 8);
     switch (NS) {
       case 1: k_gateup_pairs<1><<<pgrid, 256, 0, s>>>(L, D, U, idx, xq, xs, hq, hs, items); break;
