@@ -388,11 +388,11 @@ static int forward_kernels(colimoe_ctx *ctx, int32_t layer, const float *x, int3
     {
       KTimer kt(ctx, K_ENCODE);
       if (launch_mblocks(D, U, list, mcount, me, s) != hipSuccess) return COLIMOE_E_HIP;
-      if (launch_gather_bf16(x, D, U, xb, s) != hipSuccess) return COLIMOE_E_HIP;
+      if (launch_gather_bf16(x, D, xb, s) != hipSuccess) return COLIMOE_E_HIP;
     }
     {
       KTimer kt(ctx, K_GATEUP);
-      if (launch_gateup_mfma(L, D, xb, list, mcount, me, hb, s) != hipSuccess) return COLIMOE_E_HIP;
+      if (launch_gateup_mfma(L, D, xb, U, list, mcount, me, hb, s) != hipSuccess) return COLIMOE_E_HIP;
     }
     {
       KTimer kt(ctx, K_DOWN);

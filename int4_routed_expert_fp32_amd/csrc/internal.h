@@ -205,9 +205,12 @@ hipError_t launch_router_mfma(const LayerDev &L, const Dims &D, const float *x, 
 int mfma_max_entries(int T, int k, int E, int n_shared);
 hipError_t launch_mblocks(const Dims &D, const UnionDev &U, int4 *list, int32_t *count, int max_entries,
                           hipStream_t s);
-hipError_t launch_gather_bf16(const float *x, const Dims &D, const UnionDev &U, uint16_t *xb, hipStream_t s);
-hipError_t launch_gateup_mfma(const LayerDev &L, const Dims &D, const uint16_t *xb, const int4 *list,
-                              const int32_t *count, int max_entries, uint16_t *hb, hipStream_t s);
+// xb [T][d] = bf16(x), one row per token.
+hipError_t launch_gather_bf16(const float *x, const Dims &D, uint16_t *xb, hipStream_t s);
+// A rows of the gate/up GEMM: pair p reads xb[pair_token[p]], shared row T*k + t
+// reads xb[t].
+hipError_t launch_gateup_mfma(const LayerDev &L, const Dims &D, const uint16_t *xb, const UnionDev &U,
+                              const int4 *list, const int32_t *count, int max_entries, uint16_t *hb, hipStream_t s);
 hipError_t launch_down_mfma(const LayerDev &L, const Dims &D, const uint16_t *hb, const int4 *list,
                             const int32_t *count, int max_entries, float *y, hipStream_t s);
 hipError_t launch_rmsnorm(const float *r, int T, int d, float eps, float *x, hipStream_t s);

@@ -136,25 +136,17 @@ __global__ __launch_bounds__(64) void k_mblocks(Dims D, UnionDev U, int4 *__rest
   }
 }
 
-// ------------------------------------------------------- activation gather
-// Row r of xb = bf16(x[token of row r]): rows [0, T*k) follow the pair order of
-// the union lists, rows T*k + t hold token t for the shared expert.
-__global__ __launch_bounds__(256) void k_gather_bf16(const float *__restrict__ x, Dims D, UnionDev U,
+// ---------------------------------------------------- activations in bf16
+// Row t of xb = bf16(x[t]), one row per token; the gate/up GEMM reads a
+// pair's row through the pair's token (the union lists' pair_token; rows
+// T*k + t of the shared expert are token t).
+__global__ __launch_bounds__(256) void k_gather_bf16(const float *__restrict__ x, Dims D,
                                                      uint16_t *__restrict__ xb) {
-  const int tk = D.T * D.k;
-  const int rows = tk + (D.n_shared > 0 ? D.T : 0);
-  for (int row = blockIdx.x; row < rows; row += gridDim.x) {
-    int t = row < tk ? U.pair_token[row] : row - tk;
-    const bool ok = t >= 0 && t < D.T;
-    if (!ok) t = 0;
+  for (int t = blockIdx.x; t < D.T; t += gridDim.x) {
     const float *src = x + (size_t)t * D.d;
-    uint16_t *dst = xb + (size_t)row * D.d;
+    uint16_t *dst = xb + (size_t)t * D.d;
     for (int c = 8 * threadIdx.x; c < D.d; c += 8 * 256) {
-      float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
-      if (ok) {
-        a = *(const float4 *)(src + c);
-        b = *(const float4 *)(src + c + 4);
-      }
+      const float4 a = *(const float4 *)(src + c), b = *(const float4 *)(src + c + 4);
       uint4 o;
       o.x = (uint32_t)bf16_bits(a.x) | ((uint32_t)bf16_bits(a.y) << 16);
       o.y = (uint32_t)bf16_bits(a.z) | ((uint32_t)bf16_bits(a.w) << 16);
@@ -254,6 +246,7 @@ __device__ __forceinline__ void gemm_group(const unsigned char *cur, const WStag
 
 template <bool GATEUP, int NMT>
 __global__ __launch_bounds__(256, NMT == 1 ? 3 : 2) void k_gemm_mfma(LayerDev L, Dims D, const uint16_t *__restrict__ A,
+                                                      const int32_t *__restrict__ pair_token,
                                                       const int4 *__restrict__ list,
                                                       const int32_t *__restrict__ count, int max_entries,
                                                       uint16_t *__restrict__ hb, float *__restrict__ y) {
@@ -297,7 +290,13 @@ __global__ __launch_bounds__(256, NMT == 1 ? 3 : 2) void k_gemm_mfma(LayerDev L,
     it.sc0 = scb + (size_t)it.tile0 * G * 8 + it.r;
     it.sc1 = scb + (size_t)it.tile1 * G * 8 + it.r;
     const bool lok = lrow < rc;
-    const u32x4 *asrc = (const u32x4 *)(A + (size_t)(row0 + (lok ? lrow : 0)) * K + 8 * NMT * lpart);
+    int arow = row0 + (lok ? lrow : 0);
+    if (GATEUP) {  // A = x in bf16, one row per token: the row's token
+      const int tk = D.T * D.k;
+      arow = arow < tk ? pair_token[arow] : arow - tk;
+      arow = arow >= 0 && arow < D.T ? arow : 0;  // a row of caller-supplied lists' bad token: never combined
+    }
+    const u32x4 *asrc = (const u32x4 *)(A + (size_t)arow * K + 8 * NMT * lpart);
     unsigned char *adst = As + lrow * kArowBytes + 16 * NMT * lpart;
 
     f32x16 acc[NMT][2];
@@ -466,10 +465,9 @@ hipError_t launch_mblocks(const Dims &D, const UnionDev &U, int4 *list, int32_t 
   return hipGetLastError();
 }
 
-hipError_t launch_gather_bf16(const float *x, const Dims &D, const UnionDev &U, uint16_t *xb, hipStream_t s) {
-  const int rows = D.T * D.k + (D.n_shared > 0 ? D.T : 0);
-  if (rows <= 0) return hipSuccess;
-  k_gather_bf16<<<rows < 8192 ? rows : 8192, 256, 0, s>>>(x, D, U, xb);
+hipError_t launch_gather_bf16(const float *x, const Dims &D, uint16_t *xb, hipStream_t s) {
+  if (D.T <= 0) return hipSuccess;
+  k_gather_bf16<<<D.T < 8192 ? D.T : 8192, 256, 0, s>>>(x, D, xb);
   return hipGetLastError();
 }
 
@@ -484,14 +482,14 @@ static int mfma_grid(int max_entries, int ntiles, int per_cu) {
 
 // M-blocks of one M-tile (list[0..count[0])) and of up to four
 // (list[max_entries..], count[1]), one kernel each.
-hipError_t launch_gateup_mfma(const LayerDev &L, const Dims &D, const uint16_t *xb, const int4 *list,
-                              const int32_t *count, int max_entries, uint16_t *hb, hipStream_t s) {
+hipError_t launch_gateup_mfma(const LayerDev &L, const Dims &D, const uint16_t *xb, const UnionDev &U,
+                              const int4 *list, const int32_t *count, int max_entries, uint16_t *hb, hipStream_t s) {
   if (D.T <= 0) return hipSuccess;
   const int ntiles = (2 * D.f + kNT - 1) / kNT;
-  k_gemm_mfma<true, 1><<<mfma_grid(max_entries, ntiles, 3), 256, 0, s>>>(L, D, xb, list, count, max_entries, hb,
-                                                                          nullptr);
-  k_gemm_mfma<true, 4><<<mfma_grid(max_entries, ntiles, 2), 256, 0, s>>>(L, D, xb, list + max_entries, count + 1,
+  k_gemm_mfma<true, 1><<<mfma_grid(max_entries, ntiles, 3), 256, 0, s>>>(L, D, xb, U.pair_token, list, count,
                                                                           max_entries, hb, nullptr);
+  k_gemm_mfma<true, 4><<<mfma_grid(max_entries, ntiles, 2), 256, 0, s>>>(L, D, xb, U.pair_token, list + max_entries,
+                                                                          count + 1, max_entries, hb, nullptr);
   return hipGetLastError();
 }
 
@@ -499,10 +497,10 @@ hipError_t launch_down_mfma(const LayerDev &L, const Dims &D, const uint16_t *hb
                             const int32_t *count, int max_entries, float *y, hipStream_t s) {
   if (D.T <= 0) return hipSuccess;
   const int ntiles = (D.d + kNT - 1) / kNT;
-  k_gemm_mfma<false, 1><<<mfma_grid(max_entries, ntiles, 3), 256, 0, s>>>(L, D, hb, list, count, max_entries,
-                                                                           nullptr, y);
-  k_gemm_mfma<false, 4><<<mfma_grid(max_entries, ntiles, 2), 256, 0, s>>>(L, D, hb, list + max_entries, count + 1,
+  k_gemm_mfma<false, 1><<<mfma_grid(max_entries, ntiles, 3), 256, 0, s>>>(L, D, hb, nullptr, list, count,
                                                                            max_entries, nullptr, y);
+  k_gemm_mfma<false, 4><<<mfma_grid(max_entries, ntiles, 2), 256, 0, s>>>(L, D, hb, nullptr, list + max_entries,
+                                                                           count + 1, max_entries, nullptr, y);
   return hipGetLastError();
 }
 
