@@ -1269,7 +1269,8 @@ __global__ __launch_bounds__(256 * NS) void k_gateup_one(LayerDev L, Dims D, Uni
 // (consecutive in the union lists) and quad on one L2 at about the same time:
 // the weights come from HBM once and the other pairs' reads hit that L2.  A
 // routed pair's expert is idx[token][top-k position]; pairs past the list's
-// count (dropped by expert top-p) and the shared expert's rows past T exit.
+// count (dropped by expert top-p) exit.  The items hold the shared expert's T
+// rows after the routed pairs, unless the top-k launch has written them.
 template <int NS>
 __global__ __launch_bounds__(256 * NS) void k_gateup_pairs(LayerDev L, Dims D, UnionDev U,
                                                            const int32_t *__restrict__ idx,
@@ -1737,8 +1738,8 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(6))) void 
 // k_down_dec1; wave 0 then folds the outputs into the token's residual in
 // pair order with the gate weights, then the shared expert's, as k_combine
 // does.  Items are (tile, token) with the token fastest, the block ids
-// remapped so each XCD takes one contiguous range: the tokens of one tile
-// read the same expert rows through one L2.
+// remapped so each XCD takes one contiguous range: tokens of one tile that
+// share an expert read its rows through one L2.
 __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(6))) void k_down_dec_tok(
     LayerDev L, Dims D, const uint32_t *__restrict__ hq, const float *__restrict__ hs, UnionDev U,
     const int32_t *__restrict__ idx, const float *__restrict__ w, float *__restrict__ residual, int n_items) {
