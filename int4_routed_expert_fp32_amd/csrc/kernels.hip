@@ -407,11 +407,19 @@ __global__ __launch_bounds__(1024) void k_union_multi(const int32_t *__restrict_
   const int t_lo = min(T, wave * seg), t_hi = min(T, t_lo + seg);
   int32_t *mycount = segc + (size_t)wave * E;
   for (int t = t_lo + lane; t < t_hi; t += 64) {
-    for (int j = 0; j < k; ++j) {
-      const int e = idx[(size_t)t * k + j];
-      if (e == kDropped) continue;
+    // the token's k ids in registers first (one round of loads), then the
+    // checks: distinct and in range
+    int ee[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) ee[j] = j < k ? idx[(size_t)t * k + j] : kDropped;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int e = ee[j];
+      if (j >= k || e == kDropped) continue;
       bool ok = e >= 0 && e < E;
-      for (int i = 0; i < j && ok; ++i) ok = idx[(size_t)t * k + i] != e;
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (i < j) ok = ok && ee[i] != e;
       if (!ok)
         bad = 1;
       else
