@@ -282,11 +282,18 @@ __device__ void union_wave(const int32_t *__restrict__ idx, const Dims &D, const
   }
   wave_lds_sync();
   for (int t = lane; t < T; t += 64) {
-    for (int j = 0; j < k; ++j) {
-      const int e = idx[(size_t)t * k + j];
-      if (e == kDropped) continue;
+    // the token's k ids first (one round of loads), then the checks
+    int ee[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) ee[j] = j < k ? idx[(size_t)t * k + j] : kDropped;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int e = ee[j];
+      if (j >= k || e == kDropped) continue;
       bool ok = e >= 0 && e < E;
-      for (int i = 0; i < j && ok; ++i) ok = idx[(size_t)t * k + i] != e;
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (i < j) ok = ok && ee[i] != e;
       if (!ok)
         bad = 1;
       else
