@@ -436,6 +436,10 @@ static int forward_kernels(colimoe_ctx *ctx, int32_t layer, const float *x, int3
       KTimer kt(ctx, K_DOWN);
       if (launch_down_f32_dec(L, D, h, hsum, U, w, residual, s) != hipSuccess) return COLIMOE_E_HIP;
     }
+  } else if (fused && f32_dec_tok_supported(D)) {
+    KTimer kt(ctx, K_GATEUP);  // gate/up and down with the combine (two launches)
+    if (launch_f32_dec_tok(L, D, x, U, idx, w, h, (float *)(ctx->ws + ctx->wl.hs), residual, s) != hipSuccess)
+      return COLIMOE_E_HIP;
   } else {
     {
       KTimer kt(ctx, K_GATEUP);

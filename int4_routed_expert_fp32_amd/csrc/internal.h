@@ -196,6 +196,12 @@ hipError_t launch_gateup_f32_dec(const LayerDev &L, const Dims &D, const float *
                                  float *hsum, hipStream_t s);
 hipError_t launch_down_f32_dec(const LayerDev &L, const Dims &D, const float *h, const float *hsum, const UnionDev &U,
                                const float *w, float *residual, hipStream_t s);
+// The fp32 pair for 2-4 tokens (wide d and f, k + shared <= 16): gate/up per
+// (pair, group), then down and combine per (token, tile) into the residual.
+bool f32_dec_tok_supported(const Dims &D);
+hipError_t launch_f32_dec_tok(const LayerDev &L, const Dims &D, const float *x, const UnionDev &U,
+                              const int32_t *idx, const float *w, float *h, float *hsum, float *residual,
+                              hipStream_t s);
 // Router for many tokens on the matrix cores (fp32), with S = router_splits(d)
 // K-slices whose partials (part: [S][T][E]) are summed in slice order.
 int router_splits(int d);

@@ -655,27 +655,64 @@ __device__ __forceinline__ size_t h_ilv(int col, int C) {
 // those of the batched fp32 kernels.
 constexpr int kXPad = 36;      // LDS floats per 32-activation chunk
 constexpr int kF32DecTPW = 1;  // tiles per wave
-template <int NS, int TPW>
+// PAIRS (2-4 tokens): a block per (pair, group) instead of (slot, group), on
+// the pair's token, items ordered and spread over the XCDs as in
+// k_gateup_pairs; h rows are the pairs' (routed pair p, shared T*k + t).
+template <int NS, int TPW, bool PAIRS>
 __global__ __launch_bounds__(256) void k_gateup_f32_dec(LayerDev L, Dims D, const float *__restrict__ x, UnionDev U,
-                                                        float *__restrict__ h, float *__restrict__ hsum) {
+                                                        float *__restrict__ h, float *__restrict__ hsum,
+                                                        const int32_t *__restrict__ idx, int n_items) {
   __shared__ __attribute__((aligned(16))) float xl[NS * 64 * kXPad];
   __shared__ float s4[4];    // each wave's float4 sum of h
-  __shared__ int slot_s[2];  // expert, output row
+  __shared__ int slot_s[3];  // expert, output row, token
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int C = D.d / kChunk, groups = D.f / (16 * TPW);
-  const int s = blockIdx.x / groups, grp = blockIdx.x - s * groups;
-  if (threadIdx.x == 0) {
-    const int nu = clamp_nu(U.n_unique, D);
-    int e = -1, p0 = 0, p1 = 0;
-    if (s < nu || (s == nu && D.n_shared)) {
-      if (!resolve_slot(D, U, nu, s, e, p0, p1) || p1 <= p0) e = -1;
+  int grp;
+  if (PAIRS) {
+    const int per = (int)gridDim.x / 8;
+    const int item = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+    if (item >= n_items) return;  // block-uniform
+    const int tk = D.T * D.k, P = tk + D.T * D.n_shared;
+    grp = item / P;
+    const int p = item - grp * P;
+    if (threadIdx.x == 0) {
+      int e = -1, t = 0;
+      if (p < tk) {
+        const int nu = clamp_nu(U.n_unique, D);
+        int np = U.offsets[nu];
+        np = np < 0 ? 0 : (np > tk ? tk : np);
+        t = U.pair_token[p];
+        const int j = U.pair_slot[p];
+        if (p < np && t >= 0 && t < D.T && j >= 0 && j < D.k) {
+          e = idx[(size_t)t * D.k + j];
+          if (e < 0 || e >= D.E) e = -1;
+        }
+      } else {
+        t = p - tk;
+        e = D.E;
+      }
+      slot_s[0] = e;
+      slot_s[1] = p;
+      slot_s[2] = t;
     }
-    slot_s[0] = e;
-    slot_s[1] = s < nu ? p0 : D.T * D.k;
+  } else {
+    const int s = blockIdx.x / groups;
+    grp = blockIdx.x - s * groups;
+    if (threadIdx.x == 0) {
+      const int nu = clamp_nu(U.n_unique, D);
+      int e = -1, p0 = 0, p1 = 0;
+      if (s < nu || (s == nu && D.n_shared)) {
+        if (!resolve_slot(D, U, nu, s, e, p0, p1) || p1 <= p0) e = -1;
+      }
+      slot_s[0] = e;
+      slot_s[1] = s < nu ? p0 : D.T * D.k;
+      slot_s[2] = 0;
+    }
   }
   __syncthreads();
   const int e = slot_s[0], orow = slot_s[1];
   if (e < 0) return;  // block-uniform
+  x += (size_t)slot_s[2] * D.d;
   const ExpertLayout EL = expert_layout(D.d, D.f);
   const uint8_t *base = expert_base(L, e);
   // weights through buffer loads (the lane's offset in a VGPR, the rest in
@@ -1326,6 +1363,7 @@ __global__ __launch_bounds__(256 * NS) void k_gateup_pairs(LayerDev L, Dims D, U
 
 constexpr int kPairsMaxT = 16;   // tokens up to which gate/up runs per pair
 constexpr int kDownTokMaxT = 4;  // tokens up to which down runs per token (with the combine)
+constexpr int kF32TokMaxT = 16;  // the same for the fp32 pair
 // tokens up to which the shared gate/up rides in the top-k launch (at 16 the
 // shared expert's 16 token rows outlast the selection: +25 us of top-k launch
 // for -15 us of gate/up)
@@ -1832,6 +1870,85 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(6))) void 
 // the two half-chunk sums the gate/up kernel formed in neg8_sum's order
 // (hsum), so chunk_dot can run a word's 8 columns at a time for all 8 rows
 // with only those columns' activations in registers.
+// One wave of the fp32 one-token down kernels: the 8 rows of output tile ti
+// of expert e (when ok) against h row hrow (the pair's interleaved layout,
+// with its chunk sums in hsum), reduced by the fixed tree into out[0..8).
+__device__ __forceinline__ void f32_down_wave(const LayerDev &L, const Dims &D, bool ok, int e, int ti, int hrow,
+                                              const float *__restrict__ h, const float *__restrict__ hsum,
+                                              float *out) {
+  const int lane = threadIdx.x & 63, C = D.f / kChunk;
+  const ExpertLayout EL = expert_layout(D.d, D.f);
+  // buffer loads: the lane's offset in a VGPR, the rest in the scalar
+  // offset; a lane past the row end reads a valid chunk (the row's last)
+  // and keeps its sums unchanged
+  const uint8_t *base = expert_base(L, ok ? e : 0);
+  const __amdgpu_buffer_rsrc_t rn = wave_rsrc(base + EL.dn_nib, (uint32_t)(EL.dn_sc - EL.dn_nib));
+  const __amdgpu_buffer_rsrc_t rs = wave_rsrc(base + EL.dn_sc, (uint32_t)(EL.bytes - EL.dn_sc));
+  const __amdgpu_buffer_rsrc_t rh = wave_rsrc(h + (size_t)hrow * D.f, (uint32_t)D.f * 4u);
+  const __amdgpu_buffer_rsrc_t rq = wave_rsrc(hsum + (size_t)hrow * (D.f / 16), (uint32_t)D.f / 4u);
+  float acc[kTileRows];
+#pragma unroll
+  for (int r = 0; r < kTileRows; ++r) acc[r] = 0.0f;
+  for (int j = 0; 64 * j < C; ++j) {
+    const int width = C - 64 * j < 64 ? C - 64 * j : 64;
+    const bool live = lane < width;
+    const int cl = live ? lane : width - 1;
+    const int tb = ti * kTileRows * (D.f / 2) + j * (kTileRows * 64 * 16);
+    uint4 W[kTileRows];
+#pragma unroll
+    for (int r = 0; r < kTileRows; ++r) {
+      const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(rn, cl * 16, tb + r * width * 16, 0);
+      W[r] = make_uint4(t.x, t.y, t.z, t.w);
+    }
+    const u32x4 Sv =
+        __builtin_amdgcn_raw_buffer_load_b128(rs, (cl >> 1) * 16, (ti * (D.f / kGroup) + 32 * j) * 16, 0);
+    const uint4 S = make_uint4(Sv.x, Sv.y, Sv.z, Sv.w);
+    // -8 sum of the chunk's 32 activations: the two halves in order
+    const u32x2 hq2 = __builtin_amdgcn_raw_buffer_load_b64(rq, cl * 8, 64 * j * 8, 0);
+    const float nsx = -8.0f * (bits_f(hq2[0]) + bits_f(hq2[1]));
+    float alo[kTileRows], ahi[kTileRows];
+#pragma unroll
+    for (int r = 0; r < kTileRows; ++r) {
+      alo[r] = nsx;
+      ahi[r] = 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      // (elements by index: hipcc turns __builtin_bit_cast of a vector
+      // element .y/.z/.w into element 0)
+      const u32x4 ta = __builtin_amdgcn_raw_buffer_load_b128(rh, cl * 16, ((2 * i) * C + 64 * j) * 16, 0);
+      const u32x4 tb2 = __builtin_amdgcn_raw_buffer_load_b128(rh, cl * 16, ((2 * i + 1) * C + 64 * j) * 16, 0);
+      const float4 xa = make_float4(bits_f(ta[0]), bits_f(ta[1]), bits_f(ta[2]), bits_f(ta[3]));
+      const float4 xb = make_float4(bits_f(tb2[0]), bits_f(tb2[1]), bits_f(tb2[2]), bits_f(tb2[3]));
+#pragma unroll
+      for (int r = 0; r < kTileRows; ++r) {
+        const uint32_t wi = (i == 0 ? W[r].x : i == 1 ? W[r].y : i == 2 ? W[r].z : W[r].w) ^ 0x88888888u;
+        uint32_t lo = wi & 0x0F0F0F0Fu, hi = wi & 0xF0F0F0F0u;
+        asm("" : "+v"(lo), "+v"(hi));
+        alo[r] = __builtin_fmaf((float)(lo & 0xFFu), xa.x, alo[r]);
+        alo[r] = __builtin_fmaf((float)((lo >> 8) & 0xFFu), xa.z, alo[r]);
+        alo[r] = __builtin_fmaf((float)((lo >> 16) & 0xFFu), xb.x, alo[r]);
+        alo[r] = __builtin_fmaf((float)(lo >> 24), xb.z, alo[r]);
+        ahi[r] = __builtin_fmaf((float)(hi & 0xFFu), xa.y, ahi[r]);
+        ahi[r] = __builtin_fmaf((float)((hi >> 8) & 0xFFu), xa.w, ahi[r]);
+        ahi[r] = __builtin_fmaf((float)((hi >> 16) & 0xFFu), xb.y, ahi[r]);
+        ahi[r] = __builtin_fmaf((float)(hi >> 24), xb.w, ahi[r]);
+      }
+      // the word's sums are due here: one word's masks and activations
+      // live at a time
+#pragma unroll
+      for (int r = 0; r < kTileRows; ++r) asm volatile("" : "+v"(alo[r]), "+v"(ahi[r]));
+    }
+#pragma unroll
+    for (int r = 0; r < kTileRows; ++r) {
+      const float a = __builtin_fmaf(tile_scale(S, r), __builtin_fmaf(ahi[r], 0.0625f, alo[r]), acc[r]);
+      acc[r] = live ? a : acc[r];
+    }
+  }
+  const float v = reduce8_rows(acc);
+  if ((lane & 7) == 7) out[lane >> 3] = v;
+}
+
 __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(7))) void k_down_f32_dec(
     LayerDev L, Dims D, const float *__restrict__ h, const float *__restrict__ hsum, UnionDev U,
     const float *__restrict__ w, float *__restrict__ residual) {
@@ -1839,10 +1956,9 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(7))) void 
   __shared__ int ok_s[kDecMaxSlots];
   __shared__ float wsl_s[kDecMaxSlots];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int ti = blockIdx.x, C = D.f / kChunk;
+  const int ti = blockIdx.x;
   const int nu = clamp_nu(U.n_unique, D);
   const int slots = nu + D.n_shared;
-  const ExpertLayout EL = expert_layout(D.d, D.f);
   float rin = 0.0f;
   if (wave == 0 && lane < kTileRows) rin = residual[(size_t)ti * kTileRows + lane];
   if (wave < slots) {
@@ -1858,76 +1974,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(7))) void 
       wsl_s[wave] = g;
       ok_s[wave] = ok;
     }
-    // buffer loads: the lane's offset in a VGPR, the rest in the scalar
-    // offset; a lane past the row end reads a valid chunk (the row's last)
-    // and keeps its sums unchanged
-    const int hrow = wave < nu ? p0 : D.T * D.k;
-    const uint8_t *base = expert_base(L, ok ? e : 0);
-    const __amdgpu_buffer_rsrc_t rn = wave_rsrc(base + EL.dn_nib, (uint32_t)(EL.dn_sc - EL.dn_nib));
-    const __amdgpu_buffer_rsrc_t rs = wave_rsrc(base + EL.dn_sc, (uint32_t)(EL.bytes - EL.dn_sc));
-    const __amdgpu_buffer_rsrc_t rh = wave_rsrc(h + (size_t)hrow * D.f, (uint32_t)D.f * 4u);
-    const __amdgpu_buffer_rsrc_t rq = wave_rsrc(hsum + (size_t)hrow * (D.f / 16), (uint32_t)D.f / 4u);
-    float acc[kTileRows];
-#pragma unroll
-    for (int r = 0; r < kTileRows; ++r) acc[r] = 0.0f;
-    for (int j = 0; 64 * j < C; ++j) {
-      const int width = C - 64 * j < 64 ? C - 64 * j : 64;
-      const bool live = lane < width;
-      const int cl = live ? lane : width - 1;
-      const int tb = ti * kTileRows * (D.f / 2) + j * (kTileRows * 64 * 16);
-      uint4 W[kTileRows];
-#pragma unroll
-      for (int r = 0; r < kTileRows; ++r) {
-        const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(rn, cl * 16, tb + r * width * 16, 0);
-        W[r] = make_uint4(t.x, t.y, t.z, t.w);
-      }
-      const u32x4 Sv =
-          __builtin_amdgcn_raw_buffer_load_b128(rs, (cl >> 1) * 16, (ti * (D.f / kGroup) + 32 * j) * 16, 0);
-      const uint4 S = make_uint4(Sv.x, Sv.y, Sv.z, Sv.w);
-      // -8 sum of the chunk's 32 activations: the two halves in order
-      const u32x2 hq2 = __builtin_amdgcn_raw_buffer_load_b64(rq, cl * 8, 64 * j * 8, 0);
-      const float nsx = -8.0f * (bits_f(hq2[0]) + bits_f(hq2[1]));
-      float alo[kTileRows], ahi[kTileRows];
-#pragma unroll
-      for (int r = 0; r < kTileRows; ++r) {
-        alo[r] = nsx;
-        ahi[r] = 0.0f;
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        // (elements by index: hipcc turns __builtin_bit_cast of a vector
-        // element .y/.z/.w into element 0)
-        const u32x4 ta = __builtin_amdgcn_raw_buffer_load_b128(rh, cl * 16, ((2 * i) * C + 64 * j) * 16, 0);
-        const u32x4 tb2 = __builtin_amdgcn_raw_buffer_load_b128(rh, cl * 16, ((2 * i + 1) * C + 64 * j) * 16, 0);
-        const float4 xa = make_float4(bits_f(ta[0]), bits_f(ta[1]), bits_f(ta[2]), bits_f(ta[3]));
-        const float4 xb = make_float4(bits_f(tb2[0]), bits_f(tb2[1]), bits_f(tb2[2]), bits_f(tb2[3]));
-#pragma unroll
-        for (int r = 0; r < kTileRows; ++r) {
-          const uint32_t wi = (i == 0 ? W[r].x : i == 1 ? W[r].y : i == 2 ? W[r].z : W[r].w) ^ 0x88888888u;
-          uint32_t lo = wi & 0x0F0F0F0Fu, hi = wi & 0xF0F0F0F0u;
-          asm("" : "+v"(lo), "+v"(hi));
-          alo[r] = __builtin_fmaf((float)(lo & 0xFFu), xa.x, alo[r]);
-          alo[r] = __builtin_fmaf((float)((lo >> 8) & 0xFFu), xa.z, alo[r]);
-          alo[r] = __builtin_fmaf((float)((lo >> 16) & 0xFFu), xb.x, alo[r]);
-          alo[r] = __builtin_fmaf((float)(lo >> 24), xb.z, alo[r]);
-          ahi[r] = __builtin_fmaf((float)(hi & 0xFFu), xa.y, ahi[r]);
-          ahi[r] = __builtin_fmaf((float)((hi >> 8) & 0xFFu), xa.w, ahi[r]);
-          ahi[r] = __builtin_fmaf((float)((hi >> 16) & 0xFFu), xb.y, ahi[r]);
-          ahi[r] = __builtin_fmaf((float)(hi >> 24), xb.w, ahi[r]);
-        }
-        // the word's sums are due here: one word's masks and activations
-        // live at a time
-#pragma unroll
-        for (int r = 0; r < kTileRows; ++r) asm volatile("" : "+v"(alo[r]), "+v"(ahi[r]));
-      }
-#pragma unroll
-      for (int r = 0; r < kTileRows; ++r) {
-        const float a = __builtin_fmaf(tile_scale(S, r), __builtin_fmaf(ahi[r], 0.0625f, alo[r]), acc[r]);
-        acc[r] = live ? a : acc[r];
-      }
-    }
-    const float v = reduce8_rows(acc);
-    if ((lane & 7) == 7) vb[wave][lane >> 3] = v;
+    f32_down_wave(L, D, ok, e, ti, wave < nu ? p0 : D.T * D.k, h, hsum, vb[wave]);
   }
   __syncthreads();
   if (wave == 0 && lane < kTileRows) {
@@ -1936,6 +1983,74 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(7))) void 
       if (ok_s[sl]) out = __builtin_fmaf(wsl_s[sl], vb[sl][lane], out);
     if (D.n_shared && ok_s[nu]) out = out + vb[nu][lane];
     residual[(size_t)ti * kTileRows + lane] = out;
+  }
+}
+
+// The fp32 pair for 2-4 tokens: down + combine per (token, 8-row output
+// tile), one wave per top-k position of the token (the pair's h row, its
+// expert from idx) plus the shared expert, the wave code of k_down_f32_dec;
+// wave 0 folds into the token's residual in pair order as k_combine does.
+// Items and block ids as in k_down_dec_tok.
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(7))) void k_down_f32_tok(
+    LayerDev L, Dims D, const float *__restrict__ h, const float *__restrict__ hsum, UnionDev U,
+    const int32_t *__restrict__ idx, const float *__restrict__ w, float *__restrict__ residual, int n_items) {
+  __shared__ float vb[kDecMaxSlots][kTileRows];
+  __shared__ int ok_s[kDecMaxSlots], order_s[kDecMaxSlots], nsel_s;
+  __shared__ float wsl_s[kDecMaxSlots];
+  const int per = (int)gridDim.x / 8;
+  const int item = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+  if (item >= n_items) return;  // block-uniform
+  const int ti = item / D.T, t = item - ti * D.T;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int tk = D.T * D.k;
+  const int nu = clamp_nu(U.n_unique, D);
+  float rin = 0.0f;
+  if (wave == 0) {
+    int p = 0x7FFFFFFF;
+    float wv = 0.0f;
+    if (nu > 0 && lane < D.k) {
+      p = U.pair_of[(size_t)t * D.k + lane];
+      if (p < 0 || p >= tk) p = 0x7FFFFFFF;
+      wv = w[(size_t)t * D.k + lane];
+    }
+    int rank = 0, valid = 0;
+    for (int i = 0; i < D.k; ++i) {
+      const int q = __shfl(p, i, 64);
+      rank += (q < p) || (q == p && i < lane);
+      valid += q < tk;
+    }
+    if (lane < D.k && p < tk) order_s[rank] = lane;
+    if (lane < kDecMaxSlots) wsl_s[lane] = wv;
+    if (lane == 0) nsel_s = valid;
+    rin = residual[(size_t)t * D.d + (size_t)ti * kTileRows + (lane & 7)];
+  }
+  if (wave < D.k + D.n_shared) {
+    bool ok;
+    int e, hrow;
+    if (wave < D.k) {
+      const int p = nu > 0 ? U.pair_of[(size_t)t * D.k + wave] : -1;
+      e = idx[(size_t)t * D.k + wave];
+      ok = p >= 0 && p < tk && e >= 0 && e < D.E;
+      hrow = ok ? p : 0;
+    } else {
+      ok = true;
+      e = D.E;
+      hrow = tk + t;
+    }
+    // a position dropped by expert top-p loads nothing
+    if (__builtin_amdgcn_readfirstlane((int)ok)) f32_down_wave(L, D, true, e, ti, hrow, h, hsum, vb[wave]);
+    if (lane == 0) ok_s[wave] = ok;
+  }
+  __syncthreads();
+  if (wave == 0 && lane < kTileRows) {
+    float out = rin;
+    const int n = nsel_s;
+    for (int r = 0; r < n; ++r) {
+      const int j = order_s[r];
+      if (ok_s[j]) out = __builtin_fmaf(wsl_s[j], vb[j][lane], out);
+    }
+    if (D.n_shared) out = out + vb[D.k][lane];
+    residual[(size_t)t * D.d + (size_t)ti * kTileRows + lane] = out;
   }
 }
 
@@ -3064,11 +3179,36 @@ hipError_t launch_gateup_f32_dec(const LayerDev &L, const Dims &D, const float *
   const int NS = (D.d / kChunk + 63) / 64;
   const int grid = slots_max(D) * (D.f / (16 * kF32DecTPW));
   switch (NS) {
-    case 1: k_gateup_f32_dec<1, kF32DecTPW><<<grid, 256, 0, s>>>(L, D, x, U, h, hsum); break;
-    case 2: k_gateup_f32_dec<2, kF32DecTPW><<<grid, 256, 0, s>>>(L, D, x, U, h, hsum); break;
-    case 3: k_gateup_f32_dec<3, kF32DecTPW><<<grid, 256, 0, s>>>(L, D, x, U, h, hsum); break;
-    default: k_gateup_f32_dec<4, kF32DecTPW><<<grid, 256, 0, s>>>(L, D, x, U, h, hsum); break;
+    case 1: k_gateup_f32_dec<1, kF32DecTPW, false><<<grid, 256, 0, s>>>(L, D, x, U, h, hsum, nullptr, 0); break;
+    case 2: k_gateup_f32_dec<2, kF32DecTPW, false><<<grid, 256, 0, s>>>(L, D, x, U, h, hsum, nullptr, 0); break;
+    case 3: k_gateup_f32_dec<3, kF32DecTPW, false><<<grid, 256, 0, s>>>(L, D, x, U, h, hsum, nullptr, 0); break;
+    default: k_gateup_f32_dec<4, kF32DecTPW, false><<<grid, 256, 0, s>>>(L, D, x, U, h, hsum, nullptr, 0); break;
   }
+  return hipGetLastError();
+}
+
+bool f32_dec_tok_supported(const Dims &D) {
+  const int NS = (D.d / kChunk + 63) / 64;
+  return D.T >= 2 && D.T <= kF32TokMaxT && wide(D.d) && NS <= 4 && D.f % (16 * kF32DecTPW) == 0 &&
+         down_fusable(D) && D.k + D.n_shared <= kDecMaxSlots;
+}
+
+hipError_t launch_f32_dec_tok(const LayerDev &L, const Dims &D, const float *x, const UnionDev &U,
+                              const int32_t *idx, const float *w, float *h, float *hsum, float *residual,
+                              hipStream_t s) {
+  if (!f32_dec_tok_supported(D)) return hipErrorInvalidValue;
+  const int NS = (D.d / kChunk + 63) / 64;
+  const int gitems = (D.T * D.k + D.T * D.n_shared) * (D.f / (16 * kF32DecTPW));
+  const int ggrid = 8 * ((gitems + 7) / 8);
+  switch (NS) {
+    case 1: k_gateup_f32_dec<1, kF32DecTPW, true><<<ggrid, 256, 0, s>>>(L, D, x, U, h, hsum, idx, gitems); break;
+    case 2: k_gateup_f32_dec<2, kF32DecTPW, true><<<ggrid, 256, 0, s>>>(L, D, x, U, h, hsum, idx, gitems); break;
+    case 3: k_gateup_f32_dec<3, kF32DecTPW, true><<<ggrid, 256, 0, s>>>(L, D, x, U, h, hsum, idx, gitems); break;
+    default: k_gateup_f32_dec<4, kF32DecTPW, true><<<ggrid, 256, 0, s>>>(L, D, x, U, h, hsum, idx, gitems); break;
+  }
+  const int ditems = D.T * (D.d / kTileRows);
+  k_down_f32_tok<<<8 * ((ditems + 7) / 8), 64 * (D.k + D.n_shared), 0, s>>>(L, D, h, hsum, U, idx, w, residual,
+                                                                            ditems);
   return hipGetLastError();
 }
 
