@@ -371,11 +371,13 @@ static int forward_kernels(colimoe_ctx *ctx, int32_t layer, const float *x, int3
   float *h = (float *)(ctx->ws + ctx->wl.h);
   float *y = (float *)(ctx->ws + ctx->wl.y);
   const bool fused = (path == PATH_FP32 && (down_fusable(D) || narrow_dec_supported(D))) ||
-                     (path == PATH_I8 && i8_dec_supported(D));
+                     (path == PATH_I8 && (i8_dec_supported(D) || i8_tok_supported(D)));
   if (path == PATH_I8) {
     KTimer kt(ctx, K_GATEUP);
-    if (fused) {
+    if (fused && D.T == 1) {
       if (launch_forward_i8_dec(L, D, x, U, h, w, residual, s) != hipSuccess) return COLIMOE_E_HIP;
+    } else if (fused) {
+      if (launch_forward_i8_tok(L, D, x, U, idx, h, w, residual, s) != hipSuccess) return COLIMOE_E_HIP;
     } else if (launch_forward_i8(L, D, x, U, h, y, s) != hipSuccess) {
       return COLIMOE_E_HIP;
     }

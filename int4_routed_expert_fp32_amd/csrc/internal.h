@@ -242,6 +242,11 @@ hipError_t launch_forward_i8(const LayerDev &L, const Dims &D, const float *x, c
 bool i8_dec_supported(const Dims &D);
 hipError_t launch_forward_i8_dec(const LayerDev &L, const Dims &D, const float *x, const UnionDev &U, float *h,
                                  const float *w, float *residual, hipStream_t s);
+// The int8 container for 2-16 tokens (as i8_dec_supported otherwise): gate/up
+// per (4 h outputs, pair), then down and combine per (token, 8 rows).
+bool i8_tok_supported(const Dims &D);
+hipError_t launch_forward_i8_tok(const LayerDev &L, const Dims &D, const float *x, const UnionDev &U,
+                                 const int32_t *idx, float *h, const float *w, float *residual, hipStream_t s);
 // Bytes of one expert in the int8 container (the canonical layout).
 inline size_t expert_bytes_i8(int d, int f) {
   const size_t w = (size_t)d * (size_t)f;

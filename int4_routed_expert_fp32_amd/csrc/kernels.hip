@@ -2164,13 +2164,46 @@ __global__ __launch_bounds__(256) void k_down_i8_one(LayerDev L, Dims D, const f
 // order of k_combine (routed experts in pair order, each times its gate
 // weight, then the shared expert).
 constexpr int kI8Rows = 8;
-template <int NI>
+template <int NI, bool PAIRS>
 __global__ __launch_bounds__(256) void k_gateup_i8_dec(LayerDev L, Dims D, const float *__restrict__ x, UnionDev U,
-                                                       float *__restrict__ h) {
+                                                       float *__restrict__ h, const int32_t *__restrict__ idx,
+                                                       int n_items) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int j = blockIdx.x * 4 + wave;
-  int e, orow;
-  if (j >= D.f || !slot_i8(D, U, blockIdx.y, e, orow)) return;
+  int j, e, orow;
+  if (PAIRS) {
+    // 2-16 tokens: items (4 h outputs, pair) with the pair fastest, spread
+    // over the XCDs in contiguous ranges as in k_gateup_pairs; the pair's
+    // token and expert as there (every lane resolves the same pair)
+    const int per = (int)gridDim.x / 8;
+    const int item = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+    if (item >= n_items) return;
+    const int tk = D.T * D.k, P = tk + D.T * D.n_shared;
+    const int jg = item / P, p = item - jg * P;
+    j = jg * 4 + wave;
+    if (j >= D.f) return;
+    int t = 0;
+    e = -1;
+    if (p < tk) {
+      const int nu = clamp_nu(U.n_unique, D);
+      int np = U.offsets[nu];
+      np = np < 0 ? 0 : (np > tk ? tk : np);
+      t = U.pair_token[p];
+      const int js = U.pair_slot[p];
+      if (p < np && t >= 0 && t < D.T && js >= 0 && js < D.k) {
+        e = idx[(size_t)t * D.k + js];
+        if (e < 0 || e >= D.E) e = -1;
+      }
+    } else {
+      t = p - tk;
+      e = D.E;
+    }
+    if (e < 0) return;
+    orow = p;
+    x += (size_t)t * D.d;
+  } else {
+    j = blockIdx.x * 4 + wave;
+    if (j >= D.f || !slot_i8(D, U, blockIdx.y, e, orow)) return;
+  }
   const size_t w = (size_t)D.d * D.f, ns = w / kGroup * 2;
   const uint8_t *base = expert_base(L, e);
   const uint8_t *gq = base + (size_t)j * D.d, *uq = base + w + ns + (size_t)j * D.d;
@@ -2202,6 +2235,50 @@ __global__ __launch_bounds__(256) void k_gateup_i8_dec(LayerDev L, Dims D, const
   if (lane == 0) h[(size_t)orow * D.f + j] = silu_f(g) * u;
 }
 
+// One wave of the int8 one-token down kernels: rows r0..r0+7 of expert e's
+// down matrix against h row hrow, lane l taking chunks l, l + 64, ... in
+// order, fma(scale, chunk_dot_i8, acc), the wave_sum tree; into out[0..8).
+template <int NI>
+__device__ __forceinline__ void i8_down_wave(const LayerDev &L, const Dims &D, int e, int r0, int hrow,
+                                             const float *__restrict__ h, float *out) {
+  const int lane = threadIdx.x & 63;
+  const size_t wsz = (size_t)D.d * D.f, ns = wsz / kGroup * 2;
+  const uint8_t *dq = expert_base(L, e) + 2 * (wsz + ns);
+  const uint8_t *ds = dq + wsz;
+  const float *hr = h + (size_t)hrow * D.f;
+  const int C = D.f / 16;
+  uint4 W[kI8Rows][NI];
+  float sc[kI8Rows][NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int c = lane + 64 * i, cl = c < C ? c : C - 1;
+#pragma unroll
+    for (int r = 0; r < kI8Rows; ++r) {
+      W[r][i] = *(const uint4 *)(dq + (size_t)(r0 + r) * D.f + 16 * (size_t)cl);
+      sc[r][i] = half_at(ds + (size_t)(r0 + r) * (D.f / kGroup) * 2, cl >> 2);
+    }
+  }
+  float acc[kI8Rows];
+#pragma unroll
+  for (int r = 0; r < kI8Rows; ++r) acc[r] = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int c = lane + 64 * i;
+    if (c < C) {
+      float4 hv[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) hv[k] = *(const float4 *)(hr + 16 * (size_t)c + 4 * k);
+#pragma unroll
+      for (int r = 0; r < kI8Rows; ++r) acc[r] = __builtin_fmaf(sc[r][i], chunk_dot_i8(W[r][i], hv), acc[r]);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < kI8Rows; ++r) {
+    const float v = wave_sum(acc[r]);
+    if (lane == 0) out[r] = v;
+  }
+}
+
 template <int NI>
 __global__ __launch_bounds__(64 * kDecMaxSlots) void k_down_i8_dec(LayerDev L, Dims D, const float *__restrict__ h,
                                                                 UnionDev U, const float *__restrict__ w,
@@ -2228,41 +2305,7 @@ __global__ __launch_bounds__(64 * kDecMaxSlots) void k_down_i8_dec(LayerDev L, D
       wsl_s[wave] = g;
       ok_s[wave] = ok;
     }
-    const size_t wsz = (size_t)D.d * D.f, ns = wsz / kGroup * 2;
-    const uint8_t *dq = expert_base(L, ok ? e : 0) + 2 * (wsz + ns);
-    const uint8_t *ds = dq + wsz;
-    const float *hr = h + (size_t)(wave < nu ? p0 : D.T * D.k) * D.f;
-    const int C = D.f / 16;
-    uint4 W[kI8Rows][NI];
-    float sc[kI8Rows][NI];
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int c = lane + 64 * i, cl = c < C ? c : C - 1;
-#pragma unroll
-      for (int r = 0; r < kI8Rows; ++r) {
-        W[r][i] = *(const uint4 *)(dq + (size_t)(r0 + r) * D.f + 16 * (size_t)cl);
-        sc[r][i] = half_at(ds + (size_t)(r0 + r) * (D.f / kGroup) * 2, cl >> 2);
-      }
-    }
-    float acc[kI8Rows];
-#pragma unroll
-    for (int r = 0; r < kI8Rows; ++r) acc[r] = 0.0f;
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int c = lane + 64 * i;
-      if (c < C) {
-        float4 hv[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) hv[k] = *(const float4 *)(hr + 16 * (size_t)c + 4 * k);
-#pragma unroll
-        for (int r = 0; r < kI8Rows; ++r) acc[r] = __builtin_fmaf(sc[r][i], chunk_dot_i8(W[r][i], hv), acc[r]);
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < kI8Rows; ++r) {
-      const float v = wave_sum(acc[r]);
-      if (lane == 0) vb[wave][r] = v;
-    }
+    i8_down_wave<NI>(L, D, ok ? e : 0, r0, wave < nu ? p0 : D.T * D.k, h, vb[wave]);
   }
   __syncthreads();
   if (wave == 0 && lane < kI8Rows) {
@@ -2271,6 +2314,76 @@ __global__ __launch_bounds__(64 * kDecMaxSlots) void k_down_i8_dec(LayerDev L, D
       if (ok_s[sl]) out = __builtin_fmaf(wsl_s[sl], vb[sl][lane], out);
     if (D.n_shared && ok_s[nu]) out = out + vb[nu][lane];
     residual[r0 + lane] = out;
+  }
+}
+
+// The int8 pair for 2-16 tokens: down + combine per (token, 8 output rows),
+// one wave per top-k position of the token (the pair's h row, its expert from
+// idx) plus the shared expert, the wave code of k_down_i8_dec; wave 0 folds
+// into the token's residual in pair order as k_combine does.  Items and
+// block ids as in k_down_dec_tok.
+template <int NI>
+__global__ __launch_bounds__(64 * kDecMaxSlots) void k_down_i8_tok(LayerDev L, Dims D, const float *__restrict__ h,
+                                                                UnionDev U, const int32_t *__restrict__ idx,
+                                                                const float *__restrict__ w,
+                                                                float *__restrict__ residual, int n_items) {
+  __shared__ float vb[kDecMaxSlots][kI8Rows];
+  __shared__ int ok_s[kDecMaxSlots], order_s[kDecMaxSlots], nsel_s;
+  __shared__ float wsl_s[kDecMaxSlots];
+  const int per = (int)gridDim.x / 8;
+  const int item = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+  if (item >= n_items) return;  // block-uniform
+  const int rb = item / D.T, t = item - rb * D.T, r0 = rb * kI8Rows;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int tk = D.T * D.k;
+  const int nu = clamp_nu(U.n_unique, D);
+  float rin = 0.0f;
+  if (wave == 0) {
+    int p = 0x7FFFFFFF;
+    float wv = 0.0f;
+    if (nu > 0 && lane < D.k) {
+      p = U.pair_of[(size_t)t * D.k + lane];
+      if (p < 0 || p >= tk) p = 0x7FFFFFFF;
+      wv = w[(size_t)t * D.k + lane];
+    }
+    int rank = 0, valid = 0;
+    for (int i = 0; i < D.k; ++i) {
+      const int q = __shfl(p, i, 64);
+      rank += (q < p) || (q == p && i < lane);
+      valid += q < tk;
+    }
+    if (lane < D.k && p < tk) order_s[rank] = lane;
+    if (lane < kDecMaxSlots) wsl_s[lane] = wv;
+    if (lane == 0) nsel_s = valid;
+    rin = residual[(size_t)t * D.d + r0 + (lane & 7)];
+  }
+  if (wave < D.k + D.n_shared) {
+    bool ok;
+    int e, hrow;
+    if (wave < D.k) {
+      const int p = nu > 0 ? U.pair_of[(size_t)t * D.k + wave] : -1;
+      e = idx[(size_t)t * D.k + wave];
+      ok = p >= 0 && p < tk && e >= 0 && e < D.E;
+      hrow = ok ? p : 0;
+    } else {
+      ok = true;
+      e = D.E;
+      hrow = tk + t;
+    }
+    // a position dropped by expert top-p loads nothing
+    if (__builtin_amdgcn_readfirstlane((int)ok)) i8_down_wave<NI>(L, D, e, r0, hrow, h, vb[wave]);
+    if (lane == 0) ok_s[wave] = ok;
+  }
+  __syncthreads();
+  if (wave == 0 && lane < kI8Rows) {
+    float out = rin;
+    const int n = nsel_s;
+    for (int r = 0; r < n; ++r) {
+      const int jj = order_s[r];
+      if (ok_s[jj]) out = __builtin_fmaf(wsl_s[jj], vb[jj][lane], out);
+    }
+    if (D.n_shared) out = out + vb[D.k][lane];
+    residual[(size_t)t * D.d + r0 + lane] = out;
   }
 }
 
@@ -3267,20 +3380,50 @@ hipError_t launch_forward_i8_dec(const LayerDev &L, const Dims &D, const float *
   if (!i8_dec_supported(D)) return hipErrorInvalidValue;
   const dim3 gg((D.f + 3) / 4, slots_max(D));
   switch ((D.d / 16 + 63) / 64) {
-    case 1: k_gateup_i8_dec<1><<<gg, 256, 0, s>>>(L, D, x, U, h); break;
-    case 2: k_gateup_i8_dec<2><<<gg, 256, 0, s>>>(L, D, x, U, h); break;
-    case 3: k_gateup_i8_dec<3><<<gg, 256, 0, s>>>(L, D, x, U, h); break;
-    case 4: k_gateup_i8_dec<4><<<gg, 256, 0, s>>>(L, D, x, U, h); break;
-    case 5: k_gateup_i8_dec<5><<<gg, 256, 0, s>>>(L, D, x, U, h); break;
-    case 6: k_gateup_i8_dec<6><<<gg, 256, 0, s>>>(L, D, x, U, h); break;
-    case 7: k_gateup_i8_dec<7><<<gg, 256, 0, s>>>(L, D, x, U, h); break;
-    default: k_gateup_i8_dec<8><<<gg, 256, 0, s>>>(L, D, x, U, h); break;
+    case 1: k_gateup_i8_dec<1, false><<<gg, 256, 0, s>>>(L, D, x, U, h, nullptr, 0); break;
+    case 2: k_gateup_i8_dec<2, false><<<gg, 256, 0, s>>>(L, D, x, U, h, nullptr, 0); break;
+    case 3: k_gateup_i8_dec<3, false><<<gg, 256, 0, s>>>(L, D, x, U, h, nullptr, 0); break;
+    case 4: k_gateup_i8_dec<4, false><<<gg, 256, 0, s>>>(L, D, x, U, h, nullptr, 0); break;
+    case 5: k_gateup_i8_dec<5, false><<<gg, 256, 0, s>>>(L, D, x, U, h, nullptr, 0); break;
+    case 6: k_gateup_i8_dec<6, false><<<gg, 256, 0, s>>>(L, D, x, U, h, nullptr, 0); break;
+    case 7: k_gateup_i8_dec<7, false><<<gg, 256, 0, s>>>(L, D, x, U, h, nullptr, 0); break;
+    default: k_gateup_i8_dec<8, false><<<gg, 256, 0, s>>>(L, D, x, U, h, nullptr, 0); break;
   }
   const int threads = 64 * (D.k + D.n_shared);
   if ((D.f / 16 + 63) / 64 == 1)
     k_down_i8_dec<1><<<D.d / kI8Rows, threads, 0, s>>>(L, D, h, U, w, residual);
   else
     k_down_i8_dec<2><<<D.d / kI8Rows, threads, 0, s>>>(L, D, h, U, w, residual);
+  return hipGetLastError();
+}
+
+bool i8_tok_supported(const Dims &D) {
+  const int gi = (D.d / 16 + 63) / 64, di = (D.f / 16 + 63) / 64;
+  return D.T >= 2 && D.T <= kPairsMaxT && D.d % kI8Rows == 0 && gi <= 8 && di <= 2 &&
+         D.k + D.n_shared <= kDecMaxSlots;
+}
+
+hipError_t launch_forward_i8_tok(const LayerDev &L, const Dims &D, const float *x, const UnionDev &U,
+                                 const int32_t *idx, float *h, const float *w, float *residual, hipStream_t s) {
+  if (!i8_tok_supported(D)) return hipErrorInvalidValue;
+  const int gitems = (D.T * D.k + D.T * D.n_shared) * ((D.f + 3) / 4);
+  const int gg = 8 * ((gitems + 7) / 8);
+  switch ((D.d / 16 + 63) / 64) {
+    case 1: k_gateup_i8_dec<1, true><<<gg, 256, 0, s>>>(L, D, x, U, h, idx, gitems); break;
+    case 2: k_gateup_i8_dec<2, true><<<gg, 256, 0, s>>>(L, D, x, U, h, idx, gitems); break;
+    case 3: k_gateup_i8_dec<3, true><<<gg, 256, 0, s>>>(L, D, x, U, h, idx, gitems); break;
+    case 4: k_gateup_i8_dec<4, true><<<gg, 256, 0, s>>>(L, D, x, U, h, idx, gitems); break;
+    case 5: k_gateup_i8_dec<5, true><<<gg, 256, 0, s>>>(L, D, x, U, h, idx, gitems); break;
+    case 6: k_gateup_i8_dec<6, true><<<gg, 256, 0, s>>>(L, D, x, U, h, idx, gitems); break;
+    case 7: k_gateup_i8_dec<7, true><<<gg, 256, 0, s>>>(L, D, x, U, h, idx, gitems); break;
+    default: k_gateup_i8_dec<8, true><<<gg, 256, 0, s>>>(L, D, x, U, h, idx, gitems); break;
+  }
+  const int ditems = D.T * (D.d / kI8Rows);
+  const int dg = 8 * ((ditems + 7) / 8), threads = 64 * (D.k + D.n_shared);
+  if ((D.f / 16 + 63) / 64 == 1)
+    k_down_i8_tok<1><<<dg, threads, 0, s>>>(L, D, h, U, idx, w, residual, ditems);
+  else
+    k_down_i8_tok<2><<<dg, threads, 0, s>>>(L, D, h, U, idx, w, residual, ditems);
   return hipGetLastError();
 }
 
