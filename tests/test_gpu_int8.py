@@ -101,3 +101,41 @@ def test_int8_refusals():
     ctx.sync()
     assert torch.equal(res, x)  # refused calls have no effect
     ctx.close()
+
+
+@pytest.mark.parametrize("T", [3, 16])
+def test_int8_topp_batched_matches_one_token(T):
+    """Expert top-p 0.7 on int8 experts, 3 and 16 tokens in one call: routing,
+    weights, union lists and outputs as the oracle gives them (reading the
+    same int8 blobs), and every token's row = the token routed and forwarded
+    alone, bit for bit (dropped slots load nothing on either path)."""
+    from tests.test_gpu_topp import check_topp_batch
+    w = U8.with_(T=T)
+    ctx = _ctx(w, max_tokens=T)
+    P.load_layer(ctx, w, 0)
+    ora = P.OracleLayer(w, 0)
+    X = synth.activations(w, stream=57)
+    ctx.set_expert_top_p(0.7)
+    try:
+        xt = torch.from_numpy(np.ascontiguousarray(X)).cuda()
+        U = ctx.new_union(T)
+        res = xt.clone()
+        idx, wt = ctx.route_forward(0, xt, U, res)
+        ctx.sync()
+        gidx, gw, gout = idx.cpu().numpy(), wt.cpu().numpy(), res.cpu().numpy()
+        with oracle.container_bits(8):
+            out, _, kept = check_topp_batch(w, ora, X.astype(np.float64), gidx, gw, U.to_host(), 0.7)
+        ratio = P.assert_close(gout, out, what="int8 top-p batched output")
+        print("int8 top-p T=%d: kept %s, worst ratio %.3g" % (T, kept, ratio))
+        assert min(kept) < w.k
+        for t in range(T):
+            x1 = xt[t:t + 1].contiguous()
+            r1 = x1.clone()
+            i1, w1 = ctx.route_forward(0, x1, ctx.new_union(1), r1)
+            ctx.sync()
+            assert np.array_equal(i1.cpu().numpy()[0], gidx[t]), t
+            assert np.array_equal(w1.cpu().numpy()[0].view(np.uint32), gw[t].view(np.uint32)), t
+            assert np.array_equal(r1.cpu().numpy()[0].view(np.uint32), gout[t].view(np.uint32)), t
+    finally:
+        ctx.set_expert_top_p(1.0)
+        ctx.close()
