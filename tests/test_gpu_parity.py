@@ -30,6 +30,10 @@ RAGGED4 = synth.Workload(name="ragged4", d=1472, f=1088, E=80, k=4, T=4, n_share
 # wide in both d and f (fixed-point path) with partial steps in both GEMVs
 RAGGED3 = synth.Workload(name="ragged3", d=2112, f=2112, E=24, k=3, T=4, n_shared=1, zipf=1.1, rho=0.5,
                          seed=synth.BASE_SEED + 103)
+# wide, no shared expert, odd k: the few-token kernels' pair grids and token
+# blocks without the shared rows
+RAGGED5 = synth.Workload(name="ragged5", d=2112, f=2112, E=30, k=5, T=3, n_shared=0, zipf=1.1, rho=0.5,
+                         seed=synth.BASE_SEED + 107)
 FP32, FXP = 1, 3
 
 
@@ -136,7 +140,7 @@ def test_invalid_routing_is_reported():
             assert np.array_equal(g[key], o[key]), key
 
 
-@pytest.mark.parametrize("w", [TINY, RAGGED, RAGGED2, RAGGED3, RAGGED4], ids=lambda w: w.name)
+@pytest.mark.parametrize("w", [TINY, RAGGED, RAGGED2, RAGGED3, RAGGED4, RAGGED5], ids=lambda w: w.name)
 def test_layer_parity_small(w):
     ctx = _ctx(w)
     P.load_layer(ctx, w, 0)
@@ -152,6 +156,13 @@ def test_layer_parity_small(w):
         for t in range(w.T):
             a = P.layer_parity(ctx, w, 0, X[t:t + 1], ora, one_call=True)
             assert np.array_equal(a["out"][0].view(np.uint32), r["out"][t].view(np.uint32)), t
+    if w is RAGGED5:  # both paths, one call, and every token alone = its row of the batch
+        for flags in (FXP, FP32):
+            b = P.layer_parity(ctx, w, 0, X, ora, flags=flags, one_call=True)
+            for t in range(w.T):
+                a = P.layer_parity(ctx, w, 0, X[t:t + 1], ora, flags=flags, one_call=True)
+                assert np.array_equal(a["out"][0].view(np.uint32), b["out"][t].view(np.uint32)), (flags, t)
+            print("ragged5 flags", flags, "worst ratio", b["ratio"])
     print(w.name, "worst ratio", r["ratio"], "near-tie tokens", r["differ"])
     # union lists from route equal the oracle's union of the GPU routing
     o = oracle.union(r["idx"], w.E)
