@@ -57,14 +57,14 @@ def test_int8_layer_parity(w):
     ctx.close()
 
 
-# Batched int8 calls: the slot's tokens four at a time (T = 3 in one group,
-# 6 and 16 across groups; union16's correlated positions share experts)
+# Batched int8 calls (2-16 tokens: per pair; the tiny layer has no shared
+# expert; union16's correlated positions share experts)
 U8 = synth.Workload(name="u8", d=6144, f=2048, E=32, k=8, T=16, n_shared=1, zipf=1.1, rho=0.6, bits=8,
                     seed=synth.BASE_SEED + 403)
 
 
-@pytest.mark.parametrize("w,T", [(RAGGED8, 3), (U8, 6), (U8, 16), (WIDE8, 3)],
-                         ids=["ragged8-3", "u8-6", "u8-16", "wide8-3"])
+@pytest.mark.parametrize("w,T", [(TINY8, 4), (RAGGED8, 3), (U8, 6), (U8, 16), (WIDE8, 3)],
+                         ids=["tiny8-4", "ragged8-3", "u8-6", "u8-16", "wide8-3"])
 def test_int8_batched_parity_and_identity(w, T):
     ctx = _ctx(w, max_tokens=T)
     P.load_layer(ctx, w, 0)
